@@ -1,0 +1,95 @@
+"""CPU: the oracle against its pins, and planted oracle mistakes against the pins."""
+import numpy as np
+import pytest
+
+import oracle.hkv_oracle as orc
+from tests import oracle_pins as pins
+
+
+@pytest.mark.parametrize("name,fn", pins.ALL_PINS, ids=[n for n, _ in pins.ALL_PINS])
+def test_pin(name, fn):
+    fn(orc, np.random.default_rng(1234))
+
+
+def _m_scale_128(x):
+    x = np.asarray(x)
+    return np.float32(float(np.max(np.abs(x.astype(np.float64)))) / 128.0) if x.size else np.float32(0)
+
+
+def _m_round_half_up(x, s):
+    if float(s) == 0.0:
+        return np.zeros(np.asarray(x).shape, np.int8)
+    quot = (np.asarray(x).astype(np.float64) / np.float64(s)).astype(np.float32).astype(np.float64)
+    return np.clip(np.floor(quot + 0.5), -127, 127).astype(np.int8)
+
+
+def _m_no_fp32_quotient(x, s):
+    if float(s) == 0.0:
+        return np.zeros(np.asarray(x).shape, np.int8)
+    return np.clip(np.rint(np.asarray(x).astype(np.float64) / np.float64(s)), -127, 127).astype(np.int8)
+
+
+def _m_split_first_hot(n, hot):
+    # hot = the FIRST tokens instead of the most recent ones: split sizes are the same, so the
+    # planted mistake is the position of the hot rows; emulate it by reversing the history
+    return min(n, hot), n - min(n, hot)
+
+
+def _mutant_build_state_first_hot(k_hist, v_hist, hot, block):
+    st = _REAL["build_state"](k_hist[::-1].copy(), v_hist[::-1].copy(), hot, block)
+    return st
+
+
+def _m_attend_no_sqrt(q, keys, vals):
+    z = keys @ q
+    e = np.exp(z - z.max())
+    return (e @ vals) / e.sum(), float(z.max() + np.log(e.sum()))
+
+
+def _m_attend_sign(q, keys, vals):
+    z = -(keys @ q) / np.sqrt(q.shape[0])
+    e = np.exp(z - z.max())
+    return (e @ vals) / e.sum(), float(z.max() + np.log(e.sum()))
+
+
+def _m_window_global(c, n_valid, block):
+    e = np.exp(c - c.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def _m_cosine_no_knorm(q, state):
+    q64 = np.asarray(q, np.float16).astype(np.float64)
+    g = q64.shape[0] // state.hot_k.shape[1]
+    out = np.zeros((state.hot_k.shape[1], state.n_cold))
+    for h in range(out.shape[0]):
+        ck, _ = orc.cold_kv(state, h)
+        for hq in range(h * g, (h + 1) * g):
+            out[h] += ck @ q64[hq] / np.linalg.norm(q64[hq])
+        out[h] /= g
+    return out
+
+
+_REAL = {"build_state": orc.build_state}
+
+MUTANTS = [
+    ("scale_divides_by_128", "block_scale", _m_scale_128),
+    ("round_half_up", "quantize_codes", _m_round_half_up),
+    ("quotient_not_rounded_to_fp32", "quantize_codes", _m_no_fp32_quotient),
+    ("hot_zone_is_first_tokens", "build_state", _mutant_build_state_first_hot),
+    ("logits_missing_inv_sqrt_d", "attend", _m_attend_no_sqrt),
+    ("logit_sign_flipped", "attend", _m_attend_sign),
+    ("softmax_over_all_tokens_not_windows", "window_softmax", _m_window_global),
+    ("cosine_missing_key_norm", "token_scores", _m_cosine_no_knorm),
+]
+
+
+@pytest.mark.parametrize("name,attr,fn", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(monkeypatch, name, attr, fn):
+    monkeypatch.setattr(orc, attr, fn)
+    caught = []
+    for pin_name, pin in pins.ALL_PINS:
+        try:
+            pin(orc, np.random.default_rng(1234))
+        except (AssertionError, ValueError, IndexError):
+            caught.append(pin_name)
+    assert caught, f"no pin caught the planted mistake {name}"
