@@ -1,0 +1,264 @@
+/*
+ * hkv.h -- C ABI of libhkv: hybrid FP16-hot / INT8-cold KV cache and
+ * single-token decode attention on AMD Instinct MI355X (gfx950).
+ *
+ * Sources, cited by short title and section:
+ *   "Hybrid KV Cache page": DeepSeek V4 hybrid KV Cache inference
+ *       optimisation: hands-on analysis (tqpw.cn news 44343).
+ *   "KV Cache reuse page": KV Cache reuse: the key to LLM-inference memory
+ *       and throughput (yfxerp.com news 372023), HySparse part.
+ *   "V4 architecture page": DeepSeek V4 architecture: MoE dynamic loading and
+ *       hierarchical KV cache (xxmr.cn news 3419).
+ *
+ * The cache (Hybrid KV Cache page, 2.1 and 3.2): the most recent
+ * `hot_tokens` tokens of every sequence stay in FP16 ("hot zone", K and V
+ * interleaved per token); older tokens live in `block_size`-token cold blocks
+ * stored as INT8 with one fp32 scale per (block, kv-head, K|V), reached
+ * through a 16-byte block header holding the physical block id and the
+ * valid-token count.  Quantisation: s = fl32(max|x| / 127), code =
+ * clamp(rint(fl32(x / s)), -127, 127) with round-half-to-even; a partially
+ * filled last block always holds the codes of its current valid tokens (its
+ * FP16 originals are kept in a per-sequence tail shadow so that the block can
+ * be re-quantised when its scale grows).
+ *
+ * Conventions for every entry point:
+ *   - The caller owns every buffer and the stream.  Device buffers are passed
+ *     as raw device pointers (e.g. from torch tensors); arrays documented as
+ *     "host" are plain host memory read during the call.
+ *   - All validation is host-side and synchronous and happens before any HIP
+ *     call; on an error nothing is launched and no buffer is touched.
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream);
+ *     results are valid after the stream is synchronised.  Calls on the same
+ *     cache must be ordered on one stream; different caches are independent.
+ *   - A handle is immutable after hkv_create except for its optional timing
+ *     state (hkv_timing_*); a handle must not be used from two host threads at
+ *     once while timing is enabled.
+ */
+#ifndef HKV_H_
+#define HKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct hkv_ctx* hkv_handle;
+
+/* Status codes.  Invalid parameters are reported synchronously at the call,
+ * the host-side counterpart of the launch-time CUDA_ERROR_INVALID_VALUE the
+ * Hybrid KV Cache page (3.1, 5.1) describes for bad hot_tokens/block_size. */
+typedef enum {
+  HKV_OK = 0,
+  HKV_ERR_INVALID_VALUE = -1, /* a parameter breaks the protocol rules or a shape/count is out of range */
+  HKV_ERR_UNSUPPORTED = -2,   /* valid per the protocol but not built (see hkv_create) */
+  HKV_ERR_NULL_POINTER = -3,  /* a required pointer is NULL */
+  HKV_ERR_CAPACITY = -4,      /* an append would exceed max_blocks_per_seq or num_phys_blocks */
+  HKV_ERR_WORKSPACE = -5,     /* workspace pointer NULL or smaller than hkv_workspace_bytes */
+  HKV_ERR_HIP = -6,           /* a HIP runtime call or kernel launch failed */
+  HKV_ERR_ALIGNMENT = -7      /* a buffer is not aligned as documented */
+} hkv_status;
+
+/* One cold block header, 16 bytes (Hybrid KV Cache page 3.2: each
+ * block_header element is 16 bytes; V4 architecture page 2.2: a cold page
+ * entry is a physical address plus a valid length).  The per-head scales do
+ * not fit in 16 bytes, so they live in the `scales` array indexed by
+ * phys_block.
+ *   phys_block     caller-assigned physical block id in [0, num_phys_blocks)
+ *                  for every logical block the sequence may reach; the
+ *                  library never changes it.
+ *   n_valid        tokens stored in the block (written by hkv_append).
+ *   logical_block  index of the block in its sequence (written by hkv_append).
+ *   flags          reserved, written as 0. */
+typedef struct {
+  int32_t phys_block;
+  int32_t n_valid;
+  int32_t logical_block;
+  uint32_t flags;
+} hkv_block_header;
+
+/* Cache descriptor: pointers to caller-owned buffers, sized with
+ * hkv_cache_sizes.  Layouts (H = n_kv_heads, d = head_dim, T = hot_tokens,
+ * S = block_size, P = num_phys_blocks):
+ *   hot      fp16 [batch][H][T][2][d]; ring slot = token position mod T;
+ *            K then V of one token adjacent ("interleaved per token").
+ *            Base 512-byte aligned (Hybrid KV Cache page 3.2).
+ *   tail     fp16 [batch][H][2][S][d]; FP16 originals of each sequence's
+ *            partially filled last cold block (row-major [token][channel]).
+ *   cold     int8 [P][H][2][S*d]; one 8 KiB (S=64, d=128) tile per
+ *            (physical block, kv-head, K|V).  K tiles are stored as 16-byte
+ *            channel chunks: byte (t, c) at ((c/16)*S + t)*16 + c%16.  V tiles
+ *            are stored as 16-token column chunks: byte (t, c) at
+ *            ((t/16)*d + c)*16 + t%16.  Rows t >= n_valid hold code 0.
+ *   scales   fp32 [P][H][2]  (K scale, V scale).
+ *   headers  hkv_block_header [batch][max_blocks_per_seq].
+ *   seq_len_dev   int32 [batch] device: tokens cached per sequence.
+ *   seq_len_host  int32 [batch] host mirror of seq_len_dev, used to plan
+ *            launches and check capacity; hkv_append updates both.
+ * A new cache is all zero except headers[].phys_block; every buffer except
+ * hot must be 16-byte aligned. */
+typedef struct {
+  int32_t batch;
+  int32_t max_blocks_per_seq;
+  int32_t num_phys_blocks;
+  void* hot;
+  void* tail;
+  int8_t* cold;
+  float* scales;
+  hkv_block_header* headers;
+  int32_t* seq_len_dev;
+  int32_t* seq_len_host;
+} hkv_cache_desc;
+
+/* Bytes of every cache buffer, for one configuration (see hkv_cache_sizes). */
+typedef struct {
+  size_t hot;
+  size_t tail;
+  size_t cold;
+  size_t scales;
+  size_t headers;
+  size_t seq_len;
+  int32_t max_blocks_per_seq;
+  int32_t num_phys_blocks;
+} hkv_cache_sizes_t;
+
+/* Create a handle for one layer's cache protocol (Hybrid KV Cache page 3.1:
+ * the hybrid_v2 protocol has three required fields hot_tokens,
+ * quantization_bits, block_size; 4.2 reads them with defaults 32 / 8 / 64).
+ *   HKV_ERR_INVALID_VALUE: hot_tokens not in {16, 32, 64, 128} (5.1 assert),
+ *     block_size <= 0 or block_size % 8 != 0 (3.1, 5.1), quant_bits not in
+ *     {0, 4, 8} (3.1 allows 4 and 8; 5.2 uses 0 for an FP16 cold zone),
+ *     n_kv_heads < 1 or head_dim < 1.
+ *   HKV_ERR_UNSUPPORTED: protocol-valid values this library does not build:
+ *     quant_bits != 8, block_size != 64, head_dim not in {64, 128}.
+ *   HKV_ERR_NULL_POINTER: out is NULL.
+ * On success *out owns a small host object released by hkv_destroy. */
+hkv_status hkv_create(int n_kv_heads, int head_dim, int hot_tokens, int block_size, int quant_bits,
+                      hkv_handle* out);
+
+/* Release a handle (NULL is accepted). Pending events of the timing state are
+ * waited for.  Buffers are the caller's and are not touched. */
+hkv_status hkv_destroy(hkv_handle h);
+
+/* Buffer sizes for `batch` sequences of at most `max_tokens_per_seq` tokens
+ * each and a pool of `num_phys_blocks` cold blocks (0 = batch *
+ * max_blocks_per_seq, a dense pool).  max_blocks_per_seq =
+ * ceil(max(0, max_tokens_per_seq - hot_tokens) / block_size).
+ * HKV_ERR_INVALID_VALUE for negative counts or batch < 1. */
+hkv_status hkv_cache_sizes(hkv_handle h, int batch, int64_t max_tokens_per_seq, int64_t num_phys_blocks,
+                           hkv_cache_sizes_t* out);
+
+/* Header-table size of one sequence (Hybrid KV Cache page 5.4: blocks =
+ * ceil(tokens / block_size), about 16 bytes per block): *n_blocks =
+ * ceil(max(0, total_tokens - hot_tokens) / block_size), *bytes = 16 *
+ * *n_blocks.  Validates hot_tokens and block_size with the rules of
+ * hkv_create but needs no handle, so protocol-valid block sizes that are not
+ * built (e.g. 256) can be sized. */
+hkv_status hkv_header_table_bytes(int hot_tokens, int block_size, int64_t total_tokens, int64_t* n_blocks,
+                                  size_t* bytes);
+
+/* Workspace bytes needed by hkv_decode_attn (dense and sparse) and
+ * hkv_topk_select on this cache with n_q_heads query heads and a top-K
+ * budget k_sel (0 if top-K is not used).  The bound holds for every length
+ * up to the cache's capacity, so one allocation serves all later calls.
+ * HKV_ERR_INVALID_VALUE if n_q_heads is not a positive multiple of
+ * n_kv_heads or k_sel is outside [0, 512]. */
+hkv_status hkv_workspace_bytes(hkv_handle h, const hkv_cache_desc* c, int n_q_heads, int k_sel, size_t* bytes);
+
+/* Append n_new_host[b] new tokens to every sequence b (0 allowed) and move
+ * the tokens that leave the hot zone into cold blocks (Hybrid KV Cache page
+ * 2.1: hot = the most recent hot_tokens tokens in full FP16, cold = older
+ * tokens as INT8 with a block-wise scale; 4.2: quantise the non-hot part).
+ *   k_new, v_new  device fp16 [batch][max_n_new][n_kv_heads][head_dim]; row
+ *                 i < n_new_host[b] of sequence b is token seq_len[b] + i.
+ *   n_new_host    host int32 [batch], each in [0, max_n_new].
+ * Every cold block touched by the append is (re-)quantised from its FP16
+ * values; headers get n_valid/logical_block; the hot ring, tail shadow,
+ * seq_len_dev and seq_len_host are updated.  The result does not depend on
+ * how a token stream is split into appends.
+ *   HKV_ERR_CAPACITY: some sequence would need more than max_blocks_per_seq
+ *     cold blocks.  HKV_ERR_INVALID_VALUE: max_n_new < 0, a count outside
+ *     [0, max_n_new] or a negative seq_len_host entry.
+ * Physical ids outside [0, num_phys_blocks) are skipped by the kernels, never
+ * written through. */
+hkv_status hkv_append(hkv_handle h, const hkv_cache_desc* c, const void* k_new, const void* v_new,
+                      const int32_t* n_new_host, int max_n_new, hipStream_t stream);
+
+/* Single-token decode attention for every sequence:
+ *   out[b][hq] = softmax(q[b][hq] . K^T / sqrt(d)) . V
+ * over the FP16 hot tokens and the dequantised cold tokens of kv-head
+ * hq / (n_q_heads / n_kv_heads), with one softmax over both zones (the
+ * Hybrid KV Cache page 4.2 computes the hot part with FlashAttention-2 and
+ * dequantises cold blocks lazily; a joint softmax replaces its concatenation
+ * of the two outputs).  Split-K partials are merged with a log-sum-exp
+ * combine.
+ *   q        device fp16 [batch][n_q_heads][head_dim].
+ *   sel_idx  NULL for dense decode, or device int32 [batch][n_kv_heads][k_sel]
+ *            of selected cold-token indices (as written by
+ *            hkv_topk_select; -1 entries and out-of-range entries are
+ *            ignored, duplicates count twice): attention then covers the
+ *            hot zone plus exactly these cold tokens (KV Cache reuse page 2:
+ *            only the selected tokens are loaded).
+ *   k_sel    entries per (sequence, kv-head) of sel_idx, 1..512 when sel_idx
+ *            is given, ignored otherwise.
+ *   out      device fp16 [batch][n_q_heads][head_dim] (round to nearest even).
+ *   lse      NULL or device fp32 [batch][n_q_heads]: natural-log
+ *            log-sum-exp of the scaled logits q.k/sqrt(d).
+ *   workspace/ws_bytes  device scratch of at least hkv_workspace_bytes.
+ * HKV_ERR_INVALID_VALUE: a sequence with seq_len_host == 0, n_q_heads not a
+ * multiple of n_kv_heads, k_sel out of range.  HKV_ERR_UNSUPPORTED: a
+ * GQA group size other than 1, 2, 4 or 8. */
+hkv_status hkv_decode_attn(hkv_handle h, const hkv_cache_desc* c, const void* q, int n_q_heads,
+                           const int32_t* sel_idx, int k_sel, void* out, float* lse, void* workspace,
+                           size_t ws_bytes, hipStream_t stream);
+
+/* HySparse-style top-K selection per (sequence, kv-head) over the cold
+ * tokens (KV Cache reuse page 2 and 2.1):
+ *   c_t = mean over the kv-head's query heads of cos(q_hq, k_t) in fp32
+ *         (cos := 0 for a zero norm; the learned projection is taken as the
+ *         identity; cosine is invariant to the block scale, so INT8 codes are
+ *         scored directly),
+ *   p_t = softmax of c inside each 64-token window (= cold block, valid
+ *         tokens only),
+ *   out_idx[b][h] = the k largest p (ties to the lower token index), in
+ *         ascending token order, padded with -1 when fewer than k cold tokens
+ *         exist (the page's fixed max_K = 512 with masked padding).
+ *   k        1..512.  out_idx device int32 [batch][n_kv_heads][k].
+ * HKV_ERR_UNSUPPORTED: block_size other than 64 (windows are cold blocks). */
+hkv_status hkv_topk_select(hkv_handle h, const hkv_cache_desc* c, const void* q, int n_q_heads, int k,
+                           int32_t* out_idx, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Static, human-readable text for a status code. */
+const char* hkv_status_string(hkv_status st);
+
+/* Text describing the most recent HKV_ERR_HIP returned on the calling thread
+ * (which HIP call failed and its hipError_t name); "" if none.  The pointer
+ * stays valid until the next failing call on the same thread. */
+const char* hkv_last_error_detail(void);
+
+/* Kernel timing (profiling aid).  When enabled on a handle, every kernel the
+ * handle launches is launched with a start/stop hipEvent pair recorded by the
+ * dispatch itself (hipExtLaunchKernelGGL), so the measured interval is the
+ * kernel's own execution on `stream`.  hkv_timing_read waits for the pending
+ * events of one kernel kind and returns their summed milliseconds and count
+ * (and clears them when reset != 0). */
+typedef enum {
+  HKV_KERNEL_APPEND_QUANT = 0,
+  HKV_KERNEL_APPEND_RING = 1,
+  HKV_KERNEL_DECODE_PARTIAL = 2,
+  HKV_KERNEL_DECODE_COMBINE = 3,
+  HKV_KERNEL_TOPK_SCORE = 4,
+  HKV_KERNEL_TOPK_SELECT = 5,
+  HKV_KERNEL_DECODE_GATHER = 6,
+  HKV_KERNEL_KINDS = 7
+} hkv_kernel_kind;
+
+hkv_status hkv_timing_enable(hkv_handle h, int enable);
+hkv_status hkv_timing_read(hkv_handle h, int kind, double* total_ms, int64_t* count, int reset);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HKV_H_ */

@@ -1,0 +1,416 @@
+// Host side of the libhkv C ABI: protocol validation, size queries, launch
+// planning (from the host seq_len mirror) and kernel timing.
+//
+// Protocol rules (Hybrid KV Cache page, 3.1 and 5.1): hot_tokens is a power of
+// two in {16, 32, 64, 128}; block_size is a positive multiple of 8;
+// quantization_bits is 4 or 8 (5.2 adds 0 = FP16 cold zone).  The pages
+// describe a launch-time CUDA_ERROR_INVALID_VALUE for violations; here every
+// check runs on the host before any HIP call.
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "hkv.h"
+#include "hkv_internal.h"
+
+struct hkv_ctx {
+  int H, D, T, S, bits;
+  bool timing = false;
+  struct Pending {
+    int kind;
+    hipEvent_t start, stop;
+  };
+  std::vector<Pending> pending;
+  std::vector<hipEvent_t> free_events;
+  double total_ms[HKV_KERNEL_KINDS] = {};
+  int64_t count[HKV_KERNEL_KINDS] = {};
+};
+
+namespace {
+
+using hkv::LaunchCtx;
+
+// Target workgroups per decode/top-K launch: 4 per CU on 256 CUs, 16 waves/CU.
+constexpr int kTargetWorkgroups = 1024;
+constexpr int kMaxSplits = 512;
+
+bool valid_protocol(int hot_tokens, int block_size) {
+  const bool hot_ok = hot_tokens == 16 || hot_tokens == 32 || hot_tokens == 64 || hot_tokens == 128;
+  return hot_ok && block_size > 0 && block_size % 8 == 0;
+}
+
+int64_t cold_blocks(int64_t tokens, int T, int S) {
+  const int64_t n_cold = std::max<int64_t>(0, tokens - T);
+  return (n_cold + S - 1) / S;
+}
+
+// Split plan: units per split is a multiple of the 4 waves of a workgroup and
+// the grid aims at kTargetWorkgroups; a split count never exceeds kMaxSplits.
+struct SplitPlan {
+  int nsplit;
+  int per_split;
+};
+SplitPlan plan_splits(int64_t bh, int64_t units) {
+  units = std::max<int64_t>(1, units);
+  int64_t target = std::max<int64_t>(1, (kTargetWorkgroups + bh - 1) / bh);
+  int64_t per = hkv::kWaves * ((units + hkv::kWaves * target - 1) / (hkv::kWaves * target));
+  int64_t ns = (units + per - 1) / per;
+  if (ns > kMaxSplits) {
+    per = hkv::kWaves * ((units + hkv::kWaves * kMaxSplits - 1) / (hkv::kWaves * kMaxSplits));
+    ns = (units + per - 1) / per;
+  }
+  return {static_cast<int>(ns), static_cast<int>(per)};
+}
+
+// Upper bound of the split count over every unit count in [1, units_cap]: a
+// plan has at most `target` splits (units_per_split >= units / target) and at
+// most ceil(units / 4) splits (units_per_split >= 4), capped by kMaxSplits.
+int max_splits(int64_t bh, int64_t units_cap) {
+  const int64_t target = std::max<int64_t>(1, (kTargetWorkgroups + bh - 1) / bh);
+  int64_t ns = std::min<int64_t>(std::min<int64_t>(target, kMaxSplits), (std::max<int64_t>(1, units_cap) + 3) / 4);
+  return static_cast<int>(std::max<int64_t>(1, ns));
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+hkv_status check_desc(const hkv_ctx* h, const hkv_cache_desc* c) {
+  if (!h || !c) return HKV_ERR_NULL_POINTER;
+  if (!c->hot || !c->tail || !c->cold || !c->scales || !c->headers || !c->seq_len_dev || !c->seq_len_host)
+    return HKV_ERR_NULL_POINTER;
+  if (c->batch < 1 || c->max_blocks_per_seq < 0 || c->num_phys_blocks < 0) return HKV_ERR_INVALID_VALUE;
+  if (reinterpret_cast<uintptr_t>(c->hot) % 512 != 0) return HKV_ERR_ALIGNMENT;
+  const void* ptrs[] = {c->tail, c->cold, c->scales, c->headers, c->seq_len_dev};
+  for (const void* p : ptrs)
+    if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return HKV_ERR_ALIGNMENT;
+  for (int b = 0; b < c->batch; ++b)
+    if (c->seq_len_host[b] < 0) return HKV_ERR_INVALID_VALUE;
+  return HKV_OK;
+}
+
+hkv::CacheView view_of(const hkv_ctx* h, const hkv_cache_desc* c) {
+  hkv::CacheView v;
+  v.B = c->batch;
+  v.H = h->H;
+  v.D = h->D;
+  v.T = h->T;
+  v.S = h->S;
+  v.max_blocks = c->max_blocks_per_seq;
+  v.num_phys = c->num_phys_blocks;
+  v.hot = static_cast<_Float16*>(c->hot);
+  v.tail = static_cast<_Float16*>(c->tail);
+  v.cold = c->cold;
+  v.scales = c->scales;
+  v.headers = c->headers;
+  v.seq_len = c->seq_len_dev;
+  return v;
+}
+
+size_t partials_bytes(const hkv_ctx* h, const hkv_cache_desc* c, int G, int k_sel) {
+  const int64_t bh = static_cast<int64_t>(c->batch) * h->H;
+  const int64_t dense_units = 1 + c->max_blocks_per_seq;
+  int ns = max_splits(bh, dense_units);
+  if (k_sel > 0) ns = std::max(ns, max_splits(bh, 1 + (k_sel + 63) / 64));
+  return static_cast<size_t>(bh) * ns * G * (h->D + 2) * sizeof(float);
+}
+
+size_t topk_bytes(const hkv_ctx* h, const hkv_cache_desc* c) {
+  return static_cast<size_t>(c->batch) * h->H * c->max_blocks_per_seq * h->S * sizeof(float);
+}
+
+LaunchCtx make_ctx(hkv_ctx* h, hipStream_t s, int kind) {
+  LaunchCtx ctx{s, nullptr, nullptr};
+  if (!h->timing) return ctx;
+  hipEvent_t ev[2];
+  for (hipEvent_t& e : ev) {
+    if (!h->free_events.empty()) {
+      e = h->free_events.back();
+      h->free_events.pop_back();
+    } else if (hipEventCreate(&e) != hipSuccess) {
+      return ctx;  // timing degrades to "not recorded", the launch still happens
+    }
+  }
+  ctx.start = ev[0];
+  ctx.stop = ev[1];
+  h->pending.push_back({kind, ev[0], ev[1]});
+  return ctx;
+}
+
+thread_local char g_detail[256] = "";
+
+// Map a HIP failure to HKV_ERR_HIP and remember what failed for hkv_last_error_detail.
+hkv_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return HKV_OK;
+  snprintf(g_detail, sizeof(g_detail), "%s: %s (%s)", where, hipGetErrorName(e), hipGetErrorString(e));
+  return HKV_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+hkv_status hkv_create(int n_kv_heads, int head_dim, int hot_tokens, int block_size, int quant_bits,
+                      hkv_handle* out) {
+  if (!out) return HKV_ERR_NULL_POINTER;
+  *out = nullptr;
+  if (n_kv_heads < 1 || head_dim < 1) return HKV_ERR_INVALID_VALUE;
+  if (!valid_protocol(hot_tokens, block_size)) return HKV_ERR_INVALID_VALUE;
+  if (quant_bits != 0 && quant_bits != 4 && quant_bits != 8) return HKV_ERR_INVALID_VALUE;
+  if (quant_bits != 8 || block_size != hkv::kBlockSize || (head_dim != 64 && head_dim != 128))
+    return HKV_ERR_UNSUPPORTED;
+  hkv_ctx* h = new (std::nothrow) hkv_ctx;
+  if (!h) return HKV_ERR_INVALID_VALUE;
+  h->H = n_kv_heads;
+  h->D = head_dim;
+  h->T = hot_tokens;
+  h->S = block_size;
+  h->bits = quant_bits;
+  *out = h;
+  return HKV_OK;
+}
+
+hkv_status hkv_destroy(hkv_handle h) {
+  if (!h) return HKV_OK;
+  for (auto& p : h->pending) {
+    (void)hipEventSynchronize(p.stop);
+    (void)hipEventDestroy(p.start);
+    (void)hipEventDestroy(p.stop);
+  }
+  for (hipEvent_t e : h->free_events) (void)hipEventDestroy(e);
+  delete h;
+  return HKV_OK;
+}
+
+hkv_status hkv_cache_sizes(hkv_handle h, int batch, int64_t max_tokens_per_seq, int64_t num_phys_blocks,
+                           hkv_cache_sizes_t* out) {
+  if (!h || !out) return HKV_ERR_NULL_POINTER;
+  if (batch < 1 || max_tokens_per_seq < 0 || num_phys_blocks < 0) return HKV_ERR_INVALID_VALUE;
+  const int64_t mb = cold_blocks(max_tokens_per_seq, h->T, h->S);
+  if (mb > INT32_MAX) return HKV_ERR_INVALID_VALUE;
+  const int64_t P = num_phys_blocks ? num_phys_blocks : mb * batch;
+  if (P > INT32_MAX) return HKV_ERR_INVALID_VALUE;
+  out->hot = static_cast<size_t>(batch) * h->H * h->T * 2 * h->D * 2;
+  out->tail = static_cast<size_t>(batch) * h->H * 2 * h->S * h->D * 2;
+  out->cold = static_cast<size_t>(P) * h->H * 2 * h->S * h->D;
+  out->scales = static_cast<size_t>(P) * h->H * 2 * sizeof(float);
+  out->headers = static_cast<size_t>(batch) * mb * sizeof(hkv_block_header);
+  out->seq_len = static_cast<size_t>(batch) * sizeof(int32_t);
+  out->max_blocks_per_seq = static_cast<int32_t>(mb);
+  out->num_phys_blocks = static_cast<int32_t>(P);
+  return HKV_OK;
+}
+
+hkv_status hkv_header_table_bytes(int hot_tokens, int block_size, int64_t total_tokens, int64_t* n_blocks,
+                                  size_t* bytes) {
+  if (!n_blocks || !bytes) return HKV_ERR_NULL_POINTER;
+  if (!valid_protocol(hot_tokens, block_size) || total_tokens < 0) return HKV_ERR_INVALID_VALUE;
+  *n_blocks = cold_blocks(total_tokens, hot_tokens, block_size);
+  *bytes = static_cast<size_t>(*n_blocks) * sizeof(hkv_block_header);
+  return HKV_OK;
+}
+
+hkv_status hkv_workspace_bytes(hkv_handle h, const hkv_cache_desc* c, int n_q_heads, int k_sel, size_t* bytes) {
+  if (!h || !c || !bytes) return HKV_ERR_NULL_POINTER;
+  if (c->batch < 1 || c->max_blocks_per_seq < 0) return HKV_ERR_INVALID_VALUE;
+  if (n_q_heads < 1 || n_q_heads % h->H != 0) return HKV_ERR_INVALID_VALUE;
+  if (k_sel < 0 || k_sel > hkv::kMaxTopK) return HKV_ERR_INVALID_VALUE;
+  const int G = n_q_heads / h->H;
+  size_t ws = align_up(partials_bytes(h, c, G, k_sel), 256);
+  if (k_sel > 0) ws = std::max(ws, align_up(topk_bytes(h, c), 256));
+  *bytes = std::max<size_t>(ws, 256);
+  return HKV_OK;
+}
+
+hkv_status hkv_append(hkv_handle h, const hkv_cache_desc* c, const void* k_new, const void* v_new,
+                      const int32_t* n_new_host, int max_n_new, hipStream_t stream) {
+  hkv_status st = check_desc(h, c);
+  if (st != HKV_OK) return st;
+  if (!n_new_host) return HKV_ERR_NULL_POINTER;
+  if (max_n_new < 0) return HKV_ERR_INVALID_VALUE;
+  bool any = false;
+  for (int b = 0; b < c->batch; ++b) {
+    const int nn = n_new_host[b];
+    if (nn < 0 || nn > max_n_new) return HKV_ERR_INVALID_VALUE;
+    const int64_t n1 = static_cast<int64_t>(c->seq_len_host[b]) + nn;
+    if (n1 > INT32_MAX) return HKV_ERR_CAPACITY;
+    if (cold_blocks(n1, h->T, h->S) > c->max_blocks_per_seq) return HKV_ERR_CAPACITY;
+    if (nn > 0) any = true;
+  }
+  if (!any) return HKV_OK;
+  if (!k_new || !v_new) return HKV_ERR_NULL_POINTER;
+  if (reinterpret_cast<uintptr_t>(k_new) % 16 != 0 || reinterpret_cast<uintptr_t>(v_new) % 16 != 0)
+    return HKV_ERR_ALIGNMENT;
+
+  hkv::AppendParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.c = view_of(h, c);
+  p.k_new = static_cast<const _Float16*>(k_new);
+  p.v_new = static_cast<const _Float16*>(v_new);
+  p.max_n_new = max_n_new;
+  for (int b0 = 0; b0 < c->batch; b0 += hkv::kAppendChunk) {
+    const int ns = std::min(hkv::kAppendChunk, c->batch - b0);
+    int touched = 0;
+    bool chunk_any = false;
+    for (int i = 0; i < ns; ++i) {
+      const int b = b0 + i;
+      const int nn = n_new_host[b];
+      p.n_new[i] = nn;
+      if (nn == 0) continue;
+      chunk_any = true;
+      const int64_t n0 = c->seq_len_host[b], n1 = n0 + nn;
+      const int64_t cold0 = std::max<int64_t>(0, n0 - h->T), cold1 = std::max<int64_t>(0, n1 - h->T);
+      if (cold1 > cold0) touched = std::max<int>(touched, static_cast<int>((cold1 + h->S - 1) / h->S - cold0 / h->S));
+    }
+    if (!chunk_any) continue;
+    p.b0 = b0;
+    p.n_seq = ns;
+    p.touched_max = touched;
+    LaunchCtx qctx = make_ctx(h, stream, HKV_KERNEL_APPEND_QUANT);
+    LaunchCtx rctx = make_ctx(h, stream, HKV_KERNEL_APPEND_RING);
+    if (touched == 0 && qctx.start) {  // nothing to quantise: release the unused event pair
+      h->free_events.push_back(qctx.start);
+      h->free_events.push_back(qctx.stop);
+      h->pending.erase(h->pending.end() - 2);
+      qctx.start = qctx.stop = nullptr;
+    }
+    hipError_t e = hkv::launch_append(p, qctx, rctx);
+    if (e != hipSuccess) return hip_status(e, "hkv_append launch");
+  }
+  for (int b = 0; b < c->batch; ++b) c->seq_len_host[b] += n_new_host[b];
+  return HKV_OK;
+}
+
+hkv_status hkv_decode_attn(hkv_handle h, const hkv_cache_desc* c, const void* q, int n_q_heads,
+                           const int32_t* sel_idx, int k_sel, void* out, float* lse, void* workspace,
+                           size_t ws_bytes, hipStream_t stream) {
+  hkv_status st = check_desc(h, c);
+  if (st != HKV_OK) return st;
+  if (!q || !out) return HKV_ERR_NULL_POINTER;
+  if (n_q_heads < 1 || n_q_heads % h->H != 0) return HKV_ERR_INVALID_VALUE;
+  const int G = n_q_heads / h->H;
+  if (sel_idx && (k_sel < 1 || k_sel > hkv::kMaxTopK)) return HKV_ERR_INVALID_VALUE;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return HKV_ERR_UNSUPPORTED;
+  int64_t units_max = 1;
+  for (int b = 0; b < c->batch; ++b) {
+    const int n = c->seq_len_host[b];
+    if (n == 0) return HKV_ERR_INVALID_VALUE;
+    const int64_t nblk = cold_blocks(n, h->T, h->S);
+    const int64_t cold_units = sel_idx ? (nblk > 0 ? (k_sel + 63) / 64 : 0) : nblk;
+    units_max = std::max(units_max, 1 + cold_units);
+  }
+  size_t need = 0;
+  if (hkv_workspace_bytes(h, c, n_q_heads, sel_idx ? k_sel : 0, &need) != HKV_OK) return HKV_ERR_INVALID_VALUE;
+  if (!workspace || ws_bytes < need) return HKV_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0 || reinterpret_cast<uintptr_t>(q) % 16 != 0)
+    return HKV_ERR_ALIGNMENT;
+
+  hkv::DecodeParams p;
+  p.c = view_of(h, c);
+  p.G = G;
+  p.q = static_cast<const _Float16*>(q);
+  p.sel = sel_idx;
+  p.k_sel = sel_idx ? k_sel : 0;
+  p.partials = static_cast<float*>(workspace);
+  const SplitPlan sp = plan_splits(static_cast<int64_t>(c->batch) * h->H, units_max);
+  p.nsplit = sp.nsplit;
+  p.units_per_split = sp.per_split;
+  p.qscale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(h->D)));
+  p.out = static_cast<_Float16*>(out);
+  p.lse = lse;
+  LaunchCtx a = make_ctx(h, stream, sel_idx ? HKV_KERNEL_DECODE_GATHER : HKV_KERNEL_DECODE_PARTIAL);
+  LaunchCtx b = make_ctx(h, stream, HKV_KERNEL_DECODE_COMBINE);
+  return hip_status(hkv::launch_decode(p, a, b), "hkv_decode_attn launch");
+}
+
+hkv_status hkv_topk_select(hkv_handle h, const hkv_cache_desc* c, const void* q, int n_q_heads, int k,
+                           int32_t* out_idx, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  hkv_status st = check_desc(h, c);
+  if (st != HKV_OK) return st;
+  if (!q || !out_idx) return HKV_ERR_NULL_POINTER;
+  if (n_q_heads < 1 || n_q_heads % h->H != 0) return HKV_ERR_INVALID_VALUE;
+  if (k < 1 || k > hkv::kMaxTopK) return HKV_ERR_INVALID_VALUE;
+  const int G = n_q_heads / h->H;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return HKV_ERR_UNSUPPORTED;
+  if (h->S != hkv::kBlockSize) return HKV_ERR_UNSUPPORTED;
+  size_t need = 0;
+  if (hkv_workspace_bytes(h, c, n_q_heads, k, &need) != HKV_OK) return HKV_ERR_INVALID_VALUE;
+  if (!workspace || ws_bytes < need) return HKV_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0 || reinterpret_cast<uintptr_t>(q) % 16 != 0)
+    return HKV_ERR_ALIGNMENT;
+  int64_t blk_max = 1;
+  for (int b = 0; b < c->batch; ++b) blk_max = std::max(blk_max, cold_blocks(c->seq_len_host[b], h->T, h->S));
+
+  hkv::TopkParams p;
+  p.c = view_of(h, c);
+  p.G = G;
+  p.q = static_cast<const _Float16*>(q);
+  p.prob = static_cast<float*>(workspace);
+  const SplitPlan sp = plan_splits(static_cast<int64_t>(c->batch) * h->H, blk_max);
+  p.nsplit = sp.nsplit;
+  p.units_per_split = sp.per_split;
+  p.k = k;
+  p.out_idx = out_idx;
+  LaunchCtx a = make_ctx(h, stream, HKV_KERNEL_TOPK_SCORE);
+  LaunchCtx b = make_ctx(h, stream, HKV_KERNEL_TOPK_SELECT);
+  return hip_status(hkv::launch_topk(p, a, b), "hkv_topk_select launch");
+}
+
+const char* hkv_last_error_detail(void) { return g_detail; }
+
+const char* hkv_status_string(hkv_status st) {
+  switch (st) {
+    case HKV_OK: return "ok";
+    case HKV_ERR_INVALID_VALUE: return "invalid value";
+    case HKV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case HKV_ERR_NULL_POINTER: return "null pointer";
+    case HKV_ERR_CAPACITY: return "cache capacity exceeded";
+    case HKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case HKV_ERR_HIP: return "HIP runtime error";
+    case HKV_ERR_ALIGNMENT: return "misaligned buffer";
+  }
+  return "unknown status";
+}
+
+hkv_status hkv_timing_enable(hkv_handle h, int enable) {
+  if (!h) return HKV_ERR_NULL_POINTER;
+  h->timing = enable != 0;
+  return HKV_OK;
+}
+
+hkv_status hkv_timing_read(hkv_handle h, int kind, double* total_ms, int64_t* count, int reset) {
+  if (!h || !total_ms || !count) return HKV_ERR_NULL_POINTER;
+  if (kind < 0 || kind >= HKV_KERNEL_KINDS) return HKV_ERR_INVALID_VALUE;
+  std::vector<hkv_ctx::Pending> keep;
+  keep.reserve(h->pending.size());
+  for (auto& p : h->pending) {
+    if (p.kind != kind) {
+      keep.push_back(p);
+      continue;
+    }
+    hipError_t e = hipEventSynchronize(p.stop);
+    if (e != hipSuccess) return hip_status(e, "hkv_timing_read sync");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, p.start, p.stop);
+    if (e != hipSuccess) return hip_status(e, "hkv_timing_read elapsed");
+    h->total_ms[kind] += ms;
+    h->count[kind] += 1;
+    h->free_events.push_back(p.start);
+    h->free_events.push_back(p.stop);
+  }
+  h->pending.swap(keep);
+  *total_ms = h->total_ms[kind];
+  *count = h->count[kind];
+  if (reset) {
+    h->total_ms[kind] = 0.0;
+    h->count[kind] = 0;
+  }
+  return HKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// Internal launch interface of libhkv: parameter blocks passed by value to the
+// gfx950 kernels and the host-side launch wrappers.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hkv.h"
+
+namespace hkv {
+
+constexpr int kBlockSize = 64;      // tokens per cold block (the only built value)
+constexpr int kThreads = 256;       // 4 wave64 per workgroup for the streaming kernels
+constexpr int kWaves = kThreads / 64;
+constexpr int kAppendChunk = 256;   // sequences whose append counts travel in one kernel-argument block
+constexpr int kMaxTopK = 512;       // fixed top-K budget of the sparse path
+
+// Per-launch timing: when start/stop are non-null the dispatch records them.
+struct LaunchCtx {
+  hipStream_t stream;
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+
+struct CacheView {
+  int B, H, D, T, S;
+  int max_blocks, num_phys;
+  _Float16* hot;       // [B][H][T][2][D]
+  _Float16* tail;      // [B][H][2][S][D]
+  int8_t* cold;        // [P][H][2][S*D]
+  float* scales;       // [P][H][2]
+  hkv_block_header* headers;  // [B][max_blocks]
+  int32_t* seq_len;    // [B]
+};
+
+struct AppendParams {
+  CacheView c;
+  const _Float16* k_new;   // [B][max_n_new][H][D]
+  const _Float16* v_new;
+  int max_n_new;
+  int b0;                  // first sequence of this launch
+  int n_seq;               // sequences in this launch (<= kAppendChunk)
+  int touched_max;         // grid extent over touched cold blocks per sequence
+  int32_t n_new[kAppendChunk];
+};
+
+struct DecodeParams {
+  CacheView c;
+  int G;                   // query heads per kv-head
+  const _Float16* q;       // [B][H*G][D]
+  const int32_t* sel;      // sparse mode: [B][H][k_sel]; nullptr for dense
+  int k_sel;
+  float* partials;         // [B][H][nsplit][G][D + 2]  (m in log2 units, l, acc[D])
+  int nsplit;              // splits per (sequence, kv-head)
+  int units_per_split;     // units handled per split (multiple of kWaves)
+  float qscale;            // log2(e) / sqrt(D)
+  _Float16* out;           // [B][H*G][D]
+  float* lse;              // [B][H*G] or nullptr
+};
+
+struct TopkParams {
+  CacheView c;
+  int G;
+  const _Float16* q;       // [B][H*G][D]
+  float* prob;             // [B][H][max_blocks*S] window probabilities
+  int nsplit;
+  int units_per_split;
+  int k;
+  int32_t* out_idx;        // [B][H][k]
+};
+
+hipError_t launch_append(const AppendParams& p, const LaunchCtx& quant_ctx, const LaunchCtx& ring_ctx);
+hipError_t launch_decode(const DecodeParams& p, const LaunchCtx& part_ctx, const LaunchCtx& comb_ctx);
+hipError_t launch_topk(const TopkParams& p, const LaunchCtx& score_ctx, const LaunchCtx& sel_ctx);
+
+}  // namespace hkv

@@ -1,0 +1,247 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C-ABI.
+
+Bit-exact: INT8 codes, fp32 scales, block headers, hot ring and tail contents.
+Within tolerance (max |d| <= 4e-3, mean |d| <= 5e-4 against fp64): the fp16
+attention output.  Top-K: index sets equal outside near-ties of the K-th
+window probability (|p - tau| <= 1e-5).
+"""
+import numpy as np
+import pytest
+
+import oracle.hkv_oracle as orc
+import workloads as wl
+from tests import gpu_helpers as gh
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode(cache, q_np, lse=True, sel=None, k_sel=0):
+    torch = gh.torch_mod()
+    q = gh.upload(q_np)
+    out = torch.empty_like(q)
+    lse_t = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device) if lse else None
+    cache.decode(q, out=out, lse=lse_t, sel_idx=sel, k_sel=k_sel)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), (lse_t.cpu().numpy() if lse else None)
+
+
+def _oracle_states(w, lens, seqs=None):
+    seqs = list(range(len(lens))) if seqs is None else seqs
+    out = []
+    for b, n in zip(seqs, lens):
+        k, v = gh.history(w, b, n)
+        out.append(orc.build_state(k, v, w.hot_tokens, w.block_size))
+    return out
+
+
+# ------------------------------------------------------------------ tiny: every output, every byte
+def test_tiny_config_parity():
+    w = wl.WORKLOADS["tiny"]
+    gh.log(f"tiny: B={w.batch} H={w.n_kv_heads} Hq={w.n_q_heads} d={w.head_dim} n={w.context}")
+    cache = gh.make_cache(w, w.context)
+    gh.fill(cache, w, [w.context])
+    states = _oracle_states(w, [w.context])
+    gh.check_state(cache, states)
+    q = wl.queries(w)
+    out, lse = _decode(cache, q)
+    o_ref, l_ref = orc.decode(q[0], states[0])
+    gh.compare_out(out[0], o_ref, "tiny out")
+    gh.compare_lse(lse[0], l_ref, "tiny")
+
+
+@pytest.mark.parametrize("n", [1, 5, 31, 32, 33, 95, 96, 97, 160, 161, 300])
+def test_small_lengths_ragged_tail(n):
+    """Empty/partial cold zones, exact block boundaries and ragged partial blocks."""
+    w = wl.WORKLOADS["tiny"]
+    cache = gh.make_cache(w, 400)
+    gh.fill(cache, w, [n])
+    states = _oracle_states(w, [n])
+    gh.check_state(cache, states)
+    q = wl.queries(w, step=n)
+    out, lse = _decode(cache, q)
+    o_ref, l_ref = orc.decode(q[0], states[0])
+    gh.compare_out(out[0], o_ref, f"n={n}")
+    gh.compare_lse(lse[0], l_ref, f"n={n}")
+
+
+def test_append_chunking_invariance():
+    """One bulk append, single-token appends and random chunks give identical bytes and outputs."""
+    torch = gh.torch_mod()
+    w = wl.WORKLOADS["tiny"]
+    n = 350
+    rng = np.random.default_rng(5)
+    caches = []
+    for mode in ("bulk", "single", "random"):
+        cache = gh.make_cache(w, 400)
+        if mode == "bulk":
+            gh.fill(cache, w, [n])
+        elif mode == "single":
+            for p in range(n):
+                gh.fill(cache, w, [p + 1], start=[p])
+        else:
+            p = 0
+            while p < n:
+                step = int(min(n - p, rng.integers(1, 90)))
+                gh.fill(cache, w, [p + step], start=[p])
+                p += step
+        caches.append(cache)
+    ref = caches[0]
+    for c in caches[1:]:
+        assert torch.equal(ref.cold, c.cold)
+        assert torch.equal(ref.scales, c.scales)
+        assert torch.equal(ref.headers, c.headers)
+        assert torch.equal(ref.hot, c.hot)
+    q = wl.queries(w, step=7)
+    outs = [_decode(c, q)[0] for c in caches]
+    assert all(np.array_equal(outs[0].view(np.uint16), o.view(np.uint16)) for o in outs[1:])
+    gh.check_state(ref, _oracle_states(w, [n]))
+
+
+# ------------------------------------------------------------------ Llama-3-8B-shaped layer, full size
+def test_llama8b_config_parity():
+    w = wl.WORKLOADS["llama8b"]
+    gh.log(f"llama8b: B={w.batch} n={w.context} (K outliers x{w.outlier_scale})")
+    cache = gh.make_cache(w, w.context + 64)
+    gh.fill(cache, w, [w.context] * w.batch)
+    states = _oracle_states(w, [w.context] * w.batch)
+    gh.check_state(cache, states)
+    q = wl.queries(w)
+    out, lse = _decode(cache, q)
+    o_ref = np.stack([orc.decode(q[b], states[b])[0] for b in range(w.batch)])
+    l_ref = np.stack([orc.decode(q[b], states[b])[1] for b in range(w.batch)])
+    gh.compare_out(out, o_ref, "llama8b out")
+    gh.compare_lse(lse, l_ref, "llama8b")
+    # one more decode step: append one token to every sequence (spill into the half block), decode again
+    gh.fill(cache, w, [w.context + 1] * w.batch, start=[w.context] * w.batch)
+    states = _oracle_states(w, [w.context + 1] * w.batch)
+    gh.check_state(cache, states)
+    q = wl.queries(w, step=1)
+    out, _ = _decode(cache, q)
+    o_ref = np.stack([orc.decode(q[b], states[b])[0] for b in range(w.batch)])
+    gh.compare_out(out, o_ref, "llama8b step 1")
+
+
+def test_decode_deterministic_and_permutation_invariant():
+    """Two runs are bitwise equal; a different physical placement changes no output bit."""
+    w = wl.WORKLOADS["llama8b"]
+    n = 1000
+    lens = [n] * 4
+    mb = -(-(n + 10 - 32) // 64)
+    a = gh.make_cache(w, n + 10, batch=4)
+    perm = np.random.default_rng(3).permutation(4 * mb).reshape(4, mb)
+    b = gh.make_cache(w, n + 10, batch=4, phys_ids=perm)
+    gh.fill(a, w, lens)
+    gh.fill(b, w, lens)
+    q = wl.queries(w)[:4]
+    o1, l1 = _decode(a, q)
+    o2, l2 = _decode(a, q)
+    o3, l3 = _decode(b, q)
+    assert np.array_equal(o1.view(np.uint16), o2.view(np.uint16)) and np.array_equal(l1, l2)
+    assert np.array_equal(o1.view(np.uint16), o3.view(np.uint16)) and np.array_equal(l1, l3)
+
+
+# ------------------------------------------------------------------ ragged paged batch
+def test_ragged_config_parity():
+    w = wl.WORKLOADS["ragged"]
+    lens = [int(x) for x in wl.lengths(w)]
+    cap = max(lens) + w.steps + 64
+    mb = -(-(cap - w.hot_tokens) // w.block_size)
+    n_phys = w.batch * mb
+    perm = wl.block_permutation(w, n_phys).reshape(w.batch, mb)
+    gh.log(f"ragged: B={w.batch} lens {min(lens)}..{max(lens)} phys={n_phys} steps={w.steps}")
+    cache = gh.make_cache(w, cap, phys_ids=perm)
+    gh.fill(cache, w, lens)
+    states = _oracle_states(w, lens)
+    gh.check_state(cache, states)
+    watch = [0, 1, int(np.argmax(lens)), int(np.argmin(lens))]
+    for step in range(w.steps):
+        cur = [n + step for n in lens]
+        gh.fill(cache, w, [n + 1 for n in cur], start=cur)
+        q = wl.queries(w, step=step)
+        out, lse = _decode(cache, q)
+        full = step in (0, w.steps - 1)
+        seqs = list(range(w.batch)) if full else watch
+        st = _oracle_states(w, [cur[b] + 1 for b in seqs], seqs)
+        if full:
+            gh.check_state(cache, st, seqs)
+        o_ref = np.stack([orc.decode(q[b], s)[0] for b, s in zip(seqs, st)])
+        gh.compare_out(out[seqs], o_ref, f"ragged step {step}")
+
+
+# ------------------------------------------------------------------ long context, sampled
+def test_long_config_parity_sampled():
+    w = wl.WORKLOADS["long"]
+    n = w.context
+    gh.log(f"long: B={w.batch} n={n}")
+    cache = gh.make_cache(w, n)
+    gh.fill(cache, w, [n] * w.batch, chunk=8192)
+    q = wl.queries(w)
+    out, lse = _decode(cache, q)
+    for b in (0, w.batch - 1):
+        st = _oracle_states(w, [n], [b])[0]
+        o_ref, l_ref = orc.decode(q[b], st)
+        gh.compare_out(out[b], o_ref, f"long seq {b}")
+        gh.compare_lse(lse[b], l_ref, f"long seq {b}")
+        # codes of a sample of blocks, bit-exact
+        hdr = cache.header_array()
+        for j in (0, 1, 1000, st.n_blocks - 2, st.n_blocks - 1):
+            phys = int(hdr[b, j, 0])
+            got = cache.cold_codes_of([phys])[0]
+            nv = int(st.n_valid[j])
+            assert np.array_equal(got[:, :, :nv], st.codes[j][:, :, :nv]), (b, j)
+
+
+# ------------------------------------------------------------------ top-K and sparse decode
+@pytest.mark.parametrize("n,k", [(32 + 100, 128), (32 + 300, 50), (32 + 64 * 9 + 17, 100), (20, 16)])
+def test_topk_small(n, k):
+    w = wl.WORKLOADS["tiny"]
+    cache = gh.make_cache(w, n + 64)
+    gh.fill(cache, w, [n])
+    st = _oracle_states(w, [n])[0]
+    q = wl.queries(w, step=3)
+    idx = cache.topk(gh.upload(q), k)
+    gh.torch_mod().cuda.synchronize()
+    got = idx.cpu().numpy()
+    want, p, tau = orc.topk_select(q[0], st, k)
+    for h in range(w.n_kv_heads):
+        gh.compare_topk(got[0, h], want[h], p[h], tau[h], st.n_cold, k, f"n={n} k={k} h={h}")
+    if st.n_cold > 0:
+        out, lse = _decode(cache, q, sel=idx, k_sel=k)
+        o_ref, l_ref = orc.sparse_decode(q[0], st, got[0])
+        gh.compare_out(out[0], o_ref, "sparse")
+        gh.compare_lse(lse[0], l_ref, "sparse")
+
+
+def test_topk_ties_prefer_lower_index():
+    """Identical keys tie exactly in fp32 too: the lowest token indices must be chosen."""
+    torch = gh.torch_mod()
+    import int8_kv_cache_hkv_amd as hkv
+    H, D, n = 2, 64, 32 + 64 * 4
+    cache = hkv.HybridKVCache(H, D, 1, n)
+    k = np.ones((1, n, H, D), dtype=np.float16)
+    cache.append(gh.upload(k), gh.upload(k))
+    q = np.ones((1, 2 * H, D), dtype=np.float16)
+    idx = cache.topk(gh.upload(q), 10)
+    torch.cuda.synchronize()
+    assert idx.cpu().numpy()[0].tolist() == [list(range(10))] * H
+
+
+def test_topk_config_parity_sampled():
+    w = wl.WORKLOADS["topk"]
+    n = w.context
+    gh.log(f"topk: B={w.batch} n={n} K={w.k_sel}")
+    cache = gh.make_cache(w, n)
+    gh.fill(cache, w, [n] * w.batch, chunk=8192)
+    q = wl.queries(w)
+    qd = gh.upload(q)
+    idx = cache.topk(qd, w.k_sel)
+    out, lse = _decode(cache, q, sel=idx, k_sel=w.k_sel)
+    got = idx.cpu().numpy()
+    for b in (0, 7, w.batch - 1):
+        st = _oracle_states(w, [n], [b])[0]
+        want, p, tau = orc.topk_select(q[b], st, w.k_sel)
+        for h in range(w.n_kv_heads):
+            gh.compare_topk(got[b, h], want[h], p[h], tau[h], st.n_cold, w.k_sel, f"topk b={b} h={h}")
+        o_ref, l_ref = orc.sparse_decode(q[b], st, got[b])
+        gh.compare_out(out[b], o_ref, f"sparse b={b}")
+        gh.compare_lse(lse[b], l_ref, f"sparse b={b}")
