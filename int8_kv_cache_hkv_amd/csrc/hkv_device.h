@@ -8,6 +8,10 @@
 
 namespace hkv {
 
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -74,6 +78,54 @@ __device__ __forceinline__ SeqGeom seq_geom(int n, int T, int S) {
 // Byte offset of the (phys, head, K|V) tile inside the cold pool.
 __device__ __forceinline__ size_t tile_offset(int phys, int h, int kv, int H, int S, int D) {
   return ((static_cast<size_t>(phys) * H + h) * 2 + kv) * static_cast<size_t>(S) * D;
+}
+
+// ---------------------------------------------------------------- MFMA / DPP helpers
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Max over the 64 lanes, result in every lane: DPP inside rows of 16, then two lane swaps.
+__device__ __forceinline__ float wave_max_dpp(float x) {
+  x = fmaxf(x, dpp_mov<0xB1>(x));    // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_mov<0x4E>(x));    // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_mov<0x141>(x));   // row_half_mirror
+  x = fmaxf(x, dpp_mov<0x140>(x));   // row_mirror
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+// Sum over the 64 lanes, result in every lane (same pattern as wave_max_dpp).
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+  x += dpp_mov<0xB1>(x);
+  x += dpp_mov<0x4E>(x);
+  x += dpp_mov<0x141>(x);
+  x += dpp_mov<0x140>(x);
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Four signed int8 codes (one word) to four exact fp16 values: bias the bytes to
+// c + 128, place each under the fp16 exponent of 1024 (0x64xx = 1024 + byte),
+// subtract 1152.  Every step is exact.
+__device__ __forceinline__ half4_t codes_to_half4(uint32_t w) {
+  const uint32_t u = w ^ 0x80808080u;
+  const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
+  const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+  const half2_t off = {static_cast<_Float16>(1152.0f), static_cast<_Float16>(1152.0f)};
+  const half2_t a = __builtin_bit_cast(half2_t, lo) - off;
+  const half2_t b = __builtin_bit_cast(half2_t, hi) - off;
+  return half4_t{a.x, a.y, b.x, b.y};
+}
+
+__device__ __forceinline__ float4_t mfma_qk(half4_t a, half4_t b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float4_t mfma_pv(float a, float b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
 }
 
 }  // namespace hkv

@@ -8,7 +8,9 @@
 //
 //   topk_score_kernel   one wave per cold block (window): lane t scores token
 //                       t as the mean over the kv-head's G query heads of
-//                       cos(q, code_t) (the block scale cancels in a cosine),
+//                       cos(q, code_t) (the block scale cancels in a cosine);
+//                       q.code comes from v_mfma_f32_4x4x4f16 on exact fp16
+//                       copies (lane = token), |code|^2 from an integer dot4;
 //                       then the wave does the window softmax and stores p.
 //   topk_select_kernel  one 1024-thread workgroup per (sequence, kv-head):
 //                       4-pass 8-bit radix select of the K-th largest p (as
@@ -28,10 +30,12 @@ constexpr float kNegInfT = -__builtin_inff();
 constexpr int kSelThreads = 1024;
 
 template <int D, int G>
-__global__ __launch_bounds__(kThreads) void topk_score_kernel(TopkParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void topk_score_kernel(TopkParams p) {
   constexpr int S = kBlockSize;
-  __shared__ float qs[G][D];
-  __shared__ float qn[G];
+  constexpr int NQ = (G + 3) / 4;          // groups of 4 query heads (MFMA rows)
+  constexpr int QROW = D + 8;              // padded fp16 query row
+  __shared__ _Float16 qh[NQ][4][QROW];
+  __shared__ float qinv[4 * NQ];           // 1 / |q_g| (0 for a zero query or a padding row)
   const CacheView& c = p.c;
   const int H = c.H;
   const int split = blockIdx.x % p.nsplit;
@@ -40,19 +44,19 @@ __global__ __launch_bounds__(kThreads) void topk_score_kernel(TopkParams p) {
   const int b = bh / H;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const _Float16* qg = p.q + (static_cast<size_t>(b) * H * G + static_cast<size_t>(h) * G) * D;
-  for (int i = tid; i < G * D; i += kThreads) qs[i / D][i % D] = static_cast<float>(qg[i]);
-  __syncthreads();
-  if (w < G) {  // query norms (fp32)
-    float s2 = 0.f;
-    for (int d = lane; d < D; d += 64) s2 = fmaf(qs[w][d], qs[w][d], s2);
-    s2 = wave_sum(s2);
-    if (lane == 0) qn[w] = __builtin_sqrtf(s2);
+  for (int i = tid; i < 4 * NQ * D; i += kThreads) {
+    const int g = i / D, d = i % D;
+    qh[g / 4][g % 4][d] = g < G ? qg[g * D + d] : static_cast<_Float16>(0.f);
   }
-  for (int g = kWaves + w; g < G; g += kWaves) {  // G > 4
+  __syncthreads();
+  for (int g = w; g < 4 * NQ; g += kWaves) {  // query norms in fp32
     float s2 = 0.f;
-    for (int d = lane; d < D; d += 64) s2 = fmaf(qs[g][d], qs[g][d], s2);
+    for (int d = lane; d < D; d += 64) {
+      const float x = static_cast<float>(qh[g / 4][g % 4][d]);
+      s2 = fmaf(x, x, s2);
+    }
     s2 = wave_sum(s2);
-    if (lane == 0) qn[g] = __builtin_sqrtf(s2);
+    if (lane == 0) qinv[g] = (g < G && s2 > 0.f) ? 1.f / __builtin_sqrtf(s2) : 0.f;
   }
   __syncthreads();
 
@@ -68,40 +72,41 @@ __global__ __launch_bounds__(kThreads) void topk_score_kernel(TopkParams p) {
       if (phys < 0 || phys >= c.num_phys) continue;
       const int nv = min(S, sg.n_cold - j * S);
       const uint4* tk = reinterpret_cast<const uint4*>(c.cold + tile_offset(phys, h, 0, H, S, D));
-      asm volatile("" ::: "memory");  // re-read q from LDS per block instead of pinning G x D VGPRs
-      float dot[G];
+      uint4 kr[D / 16];
 #pragma unroll
-      for (int g = 0; g < G; ++g) dot[g] = 0.f;
+      for (int ch = 0; ch < D / 16; ++ch) kr[ch] = tk[ch * S + lane];
+      asm volatile("" ::: "memory");
+      // dot(q_g, code_t) for the lane's token t (MFMA, exact products) and |code_t|^2 (integer dot4)
+      float4_t s[NQ];
+#pragma unroll
+      for (int quad = 0; quad < NQ; ++quad) s[quad] = float4_t{0.f, 0.f, 0.f, 0.f};
       int n2 = 0;
 #pragma unroll
       for (int ch = 0; ch < D / 16; ++ch) {
-        const uint4 kw = tk[ch * S + lane];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t wd = word_of(kw, i);
+        for (int wd = 0; wd < 4; ++wd) {
+          const uint32_t word = word_of(kr[ch], wd);
+          n2 = __builtin_amdgcn_sdot4(static_cast<int>(word), static_cast<int>(word), n2, false);
+          const half4_t bk = codes_to_half4(word);
+          const int k0 = ch * 16 + wd * 4;
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int code = static_cast<int8_t>(static_cast<uint8_t>(wd >> (8 * k)));
-            const float kf = static_cast<float>(code);
-            n2 += code * code;  // exact integer |code|^2
-#pragma unroll
-            for (int g = 0; g < G; ++g) dot[g] = fmaf(qs[g][ch * 16 + i * 4 + k], kf, dot[g]);
-          }
+          for (int quad = 0; quad < NQ; ++quad)
+            s[quad] = mfma_qk(*reinterpret_cast<const half4_t*>(&qh[quad][lane & 3][k0]), bk, s[quad]);
         }
       }
-      const float kn = __builtin_sqrtf(static_cast<float>(n2));
+      // c_t = mean over the G query heads of cos(q_g, code_t); cosine is scale-free, so codes suffice
+      const float kinv = n2 > 0 ? 1.f / __builtin_sqrtf(static_cast<float>(n2)) : 0.f;
       float csum = 0.f;
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float den = qn[g] * kn;
-        csum += den > 0.f ? dot[g] / den : 0.f;
-      }
+      for (int quad = 0; quad < NQ; ++quad)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) csum += s[quad][r] * qinv[4 * quad + r];
       const bool valid = lane < nv;
-      const float cs = valid ? csum / static_cast<float>(G) : kNegInfT;
+      const float cs = valid ? (csum * kinv) / static_cast<float>(G) : kNegInfT;
       // softmax inside the window (= this block's valid tokens)
-      const float mx = wave_max(cs);
+      const float mx = wave_max_dpp(cs);
       const float e = valid ? exp2_approx((cs - mx) * kLog2e) : 0.f;
-      const float es = wave_sum(e);
+      const float es = wave_sum_dpp(e);
       if (valid) prob[static_cast<size_t>(j) * S + lane] = e / es;
     }
   }
