@@ -163,6 +163,9 @@ hkv_status hkv_header_table_bytes(int hot_tokens, int block_size, int64_t total_
  * hkv_topk_select on this cache with n_q_heads query heads and a top-K
  * budget k_sel (0 if top-K is not used).  The bound holds for every length
  * up to the cache's capacity, so one allocation serves all later calls.
+ * The workspace must be zero-filled before its first use: its first bytes
+ * hold per-(sequence, kv-head) arrival counters that every call leaves at
+ * zero again.  Calls that share a workspace must be ordered on one stream.
  * HKV_ERR_INVALID_VALUE if n_q_heads is not a positive multiple of
  * n_kv_heads or k_sel is outside [0, 512]. */
 hkv_status hkv_workspace_bytes(hkv_handle h, const hkv_cache_desc* c, int n_q_heads, int k_sel, size_t* bytes);
@@ -245,14 +248,13 @@ const char* hkv_last_error_detail(void);
  * events of one kernel kind and returns their summed milliseconds and count
  * (and clears them when reset != 0). */
 typedef enum {
-  HKV_KERNEL_APPEND_QUANT = 0,
-  HKV_KERNEL_APPEND_RING = 1,
-  HKV_KERNEL_DECODE_PARTIAL = 2,
-  HKV_KERNEL_DECODE_COMBINE = 3,
+  HKV_KERNEL_APPEND = 0,        /* append/quantise (single-pass or first of two) */
+  HKV_KERNEL_APPEND_RING = 1,   /* second pass of a multi-block append */
+  HKV_KERNEL_DECODE = 2,        /* dense decode (splits + hot zone + combine, one launch) */
+  HKV_KERNEL_DECODE_SPARSE = 3, /* sparse decode over selected tokens, one launch */
   HKV_KERNEL_TOPK_SCORE = 4,
   HKV_KERNEL_TOPK_SELECT = 5,
-  HKV_KERNEL_DECODE_GATHER = 6,
-  HKV_KERNEL_KINDS = 7
+  HKV_KERNEL_KINDS = 6
 } hkv_kernel_kind;
 
 hkv_status hkv_timing_enable(hkv_handle h, int enable);

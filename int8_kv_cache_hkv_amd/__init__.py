@@ -24,8 +24,7 @@ LIB_PATH = os.path.join(_PKG, "libhkv.so")
 HKV_OK = 0
 STATUS_NAMES = {0: "HKV_OK", -1: "HKV_ERR_INVALID_VALUE", -2: "HKV_ERR_UNSUPPORTED", -3: "HKV_ERR_NULL_POINTER",
                 -4: "HKV_ERR_CAPACITY", -5: "HKV_ERR_WORKSPACE", -6: "HKV_ERR_HIP", -7: "HKV_ERR_ALIGNMENT"}
-KERNELS = {"append_quant": 0, "append_ring": 1, "decode_partial": 2, "decode_combine": 3,
-           "topk_score": 4, "topk_select": 5, "decode_gather": 6}
+KERNELS = {"append": 0, "append_ring": 1, "decode": 2, "decode_sparse": 3, "topk_score": 4, "topk_select": 5}
 EXPORTS = ["hkv_create", "hkv_destroy", "hkv_cache_sizes", "hkv_header_table_bytes", "hkv_workspace_bytes",
            "hkv_append", "hkv_decode_attn", "hkv_topk_select", "hkv_status_string", "hkv_timing_enable",
            "hkv_timing_read", "hkv_last_error_detail"]

@@ -9,7 +9,8 @@
 // an append touches is re-quantised from FP16 (older tokens of a partial block
 // come from the per-sequence tail shadow).
 //
-// Two launches, in stream order:
+// Two launches, in stream order (multi-block appends; the single-pass
+// append_step_kernel below serves appends that touch at most two blocks):
 //   append_quant_kernel  one workgroup per (sequence, touched block, kv-head):
 //                        gathers the block's FP16 rows (tail shadow, hot ring,
 //                        new tokens), reduces max|x|, divides and rounds, and
@@ -215,6 +216,207 @@ __global__ __launch_bounds__(kThreads) void append_ring_kernel(AppendParams p) {
   if (tid == 0) c.seq_len[b] = n1;
 }
 
+// Single-pass append, one workgroup per (sequence, kv-head), for appends that
+// touch at most a couple of cold blocks per sequence (a decode step touches
+// one).  Everything one kv-head of one sequence owns (its touched tiles, tail
+// shadow rows and hot-ring slots) is handled by one workgroup in program
+// order, so no second launch is needed; the cached length comes from the host
+// mirror (kernel argument), so no workgroup reads seq_len while another
+// publishes it.
+//
+// Block scale reuse: s = fl32(m / 127) is monotonic and injective on fp16
+// maxima, so when fl32(m_new / 127) <= s_old for the rows being added, the
+// block maximum and scale are unchanged and the old rows keep their codes;
+// only the new rows are coded.  Otherwise the whole block is re-quantised
+// from its FP16 rows.  Both paths give the codes a full re-quantisation gives.
+template <int D>
+__global__ __launch_bounds__(kThreads) void append_step_kernel(AppendParams p) {
+  constexpr int S = kBlockSize;
+  constexpr int TPT = kThreads / S;     // threads per token row
+  constexpr int CPT = D / TPT;          // channels per thread
+  constexpr int LDS_ROW = D + 16;
+  constexpr int VPR = D / 8;            // 16-byte vectors per fp16 row
+  __shared__ __align__(16) int8_t stage[S * LDS_ROW];
+  __shared__ float red[kWaves];
+
+  const CacheView& c = p.c;
+  const int H = c.H, T = c.T;
+  const int h = blockIdx.x % H;
+  const int bl = blockIdx.x / H;
+  if (bl >= p.n_seq) return;
+  const int b = p.b0 + bl;
+  const int nn = p.n_new[bl];
+  if (nn <= 0) return;
+  const int n0 = p.n0[bl];
+  const int n1 = n0 + nn;
+  const int cold0 = n0 > T ? n0 - T : 0;
+  const int cold1 = n1 > T ? n1 - T : 0;
+  const int tid = threadIdx.x;
+  const int t = tid / TPT, part = tid % TPT;
+  const size_t bh = static_cast<size_t>(b) * H + h;
+
+  auto row_ptr = [&](int pos, int kv) -> const _Float16* {
+    if (pos < n0) return c.hot + ((bh * T + (pos % T)) * 2 + kv) * D;
+    return (kv ? p.v_new : p.k_new) + ((static_cast<size_t>(b) * p.max_n_new + (pos - n0)) * H + h) * D;
+  };
+  auto block_max = [&](float m) -> float {
+    m = wave_max(m);
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) r = fmaxf(r, red[w]);
+    __syncthreads();
+    return r;
+  };
+
+  for (int j = cold0 / S; j * S < cold1; ++j) {
+    if (j >= c.max_blocks) break;
+    hkv_block_header* hdr = c.headers + static_cast<size_t>(b) * c.max_blocks + j;
+    const int phys = hdr->phys_block;
+    if (phys < 0 || phys >= c.num_phys) continue;
+    const int v_old = j * S < cold0 ? cold0 - j * S : 0;   // rows already coded, FP16 in the tail shadow
+    const int v_new = min(S, cold1 - j * S);
+    for (int kv = 0; kv < 2; ++kv) {
+      float x[CPT];
+      const bool is_new = t >= v_old && t < v_new;
+      if (is_new) {
+        const uint4* r4 = reinterpret_cast<const uint4*>(row_ptr(j * S + t, kv) + part * CPT);
+#pragma unroll
+        for (int v = 0; v < CPT / 8; ++v) {
+          const uint4 wv = r4[v];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x[v * 8 + 2 * i] = half_lo(word_of(wv, i));
+            x[v * 8 + 2 * i + 1] = half_hi(word_of(wv, i));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) x[i] = 0.f;
+      }
+      float m = 0.f;
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) m = fmaxf(m, fabsf(x[i]));
+      const float m_new = block_max(m);
+      float* sp = c.scales + (static_cast<size_t>(phys) * H + h) * 2 + kv;
+      int8_t* tile = c.cold + tile_offset(phys, h, kv, H, S, D);
+      const float s_old = v_old > 0 ? *sp : 0.f;
+      if (v_old > 0 && m_new / 127.0f <= s_old) {
+        // ---- scale unchanged: code only the new rows, in place
+        if (is_new) {
+          int8_t q8[CPT];
+#pragma unroll
+          for (int i = 0; i < CPT; ++i)
+            q8[i] = s_old > 0.f ? static_cast<int8_t>(fminf(127.f, fmaxf(-127.f, __builtin_rintf(x[i] / s_old)))) : 0;
+          if (kv == 0) {
+#pragma unroll
+            for (int ch = 0; ch < CPT / 16; ++ch) {
+              const int dc = (part * CPT) / 16 + ch;
+              uint32_t wv[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                wv[i] = (static_cast<uint32_t>(static_cast<uint8_t>(q8[ch * 16 + 4 * i])) |
+                         (static_cast<uint32_t>(static_cast<uint8_t>(q8[ch * 16 + 4 * i + 1])) << 8) |
+                         (static_cast<uint32_t>(static_cast<uint8_t>(q8[ch * 16 + 4 * i + 2])) << 16) |
+                         (static_cast<uint32_t>(static_cast<uint8_t>(q8[ch * 16 + 4 * i + 3])) << 24));
+              reinterpret_cast<uint4*>(tile)[dc * S + t] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) tile[((t / 16) * D + part * CPT + i) * 16 + (t % 16)] = q8[i];
+          }
+        }
+        continue;
+      }
+      // ---- (re-)quantise the whole block: old rows come back from the tail shadow
+      if (t < v_old) {
+        const uint4* r4 = reinterpret_cast<const uint4*>(c.tail + ((bh * 2 + kv) * S + t) * D + part * CPT);
+#pragma unroll
+        for (int v = 0; v < CPT / 8; ++v) {
+          const uint4 wv = r4[v];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x[v * 8 + 2 * i] = half_lo(word_of(wv, i));
+            x[v * 8 + 2 * i + 1] = half_hi(word_of(wv, i));
+          }
+        }
+      }
+      float mo = 0.f;
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) mo = fmaxf(mo, fabsf(x[i]));
+      const float mblk = v_old > 0 ? fmaxf(m_new, block_max(mo)) : m_new;
+      const float s = mblk / 127.0f;
+      int8_t* srow = stage + t * LDS_ROW + part * CPT;
+#pragma unroll
+      for (int i = 0; i < CPT; i += 4) {
+        uint32_t packed = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          float qv = 0.f;
+          if (s > 0.f) qv = fminf(127.f, fmaxf(-127.f, __builtin_rintf(x[i + k] / s)));
+          packed |= (static_cast<uint32_t>(static_cast<int>(qv)) & 0xffu) << (8 * k);
+        }
+        *reinterpret_cast<uint32_t*>(srow + i) = packed;
+      }
+      __syncthreads();
+      constexpr int NVEC = S * D / 16;
+      for (int vi = tid; vi < NVEC; vi += kThreads) {
+        uint4 out;
+        if (kv == 0) {
+          const int dc = vi / S, tt = vi % S;
+          out = *reinterpret_cast<const uint4*>(stage + tt * LDS_ROW + dc * 16);
+        } else {
+          const int tc = vi / D, cc = vi % D;
+          uint32_t wv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            uint32_t acc = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              acc |= static_cast<uint32_t>(static_cast<uint8_t>(stage[(tc * 16 + i * 4 + k) * LDS_ROW + cc])) << (8 * k);
+            wv[i] = acc;
+          }
+          out = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        }
+        reinterpret_cast<uint4*>(tile)[vi] = out;
+      }
+      if (tid == 0) *sp = s;
+      __syncthreads();
+    }
+    if (h == 0 && tid == 0) {
+      hdr->n_valid = v_new;
+      hdr->logical_block = j;
+      hdr->flags = 0u;
+    }
+  }
+  __syncthreads();  // every read of the tail shadow and of spilled ring slots is done
+  // FP16 shadow of the new partial last block (rows already there stay)
+  const int jf = cold1 / S;
+  if ((cold1 % S) != 0) {
+    const int lo = max(jf * S, cold0), hi = cold1;
+    for (int it = tid; it < (hi - lo) * 2 * VPR; it += kThreads) {
+      const int v = it % VPR;
+      const int kv = (it / VPR) % 2;
+      const int pos = lo + it / (2 * VPR);
+      reinterpret_cast<uint4*>(c.tail + ((bh * 2 + kv) * S + (pos - jf * S)) * D)[v] =
+          reinterpret_cast<const uint4*>(row_ptr(pos, kv))[v];
+    }
+  }
+  __syncthreads();  // ring slots read above are overwritten below
+  {
+    const int lo = max(n0, n1 - T), hi = n1;
+    for (int it = tid; it < (hi - lo) * 2 * VPR; it += kThreads) {
+      const int v = it % VPR;
+      const int kv = (it / VPR) % 2;
+      const int pos = lo + it / (2 * VPR);
+      reinterpret_cast<uint4*>(c.hot + ((bh * T + (pos % T)) * 2 + kv) * D)[v] =
+          reinterpret_cast<const uint4*>(row_ptr(pos, kv))[v];
+    }
+  }
+  if (h == 0 && tid == 0) c.seq_len[b] = n1;
+}
+
 template <typename K>
 hipError_t launch1(K kernel, int grid, const AppendParams& p, const LaunchCtx& ctx) {
   if (grid <= 0) return hipSuccess;
@@ -231,6 +433,10 @@ hipError_t launch1(K kernel, int grid, const AppendParams& p, const LaunchCtx& c
 using namespace detail;
 
 hipError_t launch_append(const AppendParams& p, const LaunchCtx& quant_ctx, const LaunchCtx& ring_ctx) {
+  if (p.single_pass) {
+    return p.c.D == 128 ? launch1(append_step_kernel<128>, p.n_seq * p.c.H, p, quant_ctx)
+                        : launch1(append_step_kernel<64>, p.n_seq * p.c.H, p, quant_ctx);
+  }
   const int qgrid = p.touched_max > 0 ? p.n_seq * p.touched_max * p.c.H : 0;
   hipError_t e;
   if (p.c.D == 128) {

@@ -37,7 +37,8 @@ namespace hkv {
 namespace detail {
 
 constexpr float kNegInf = -__builtin_inff();
-constexpr int kCombineThreads = 128;  // >= head_dim and >= hot_tokens (both at most 128)
+constexpr int kHotChunk = 32;         // hot-zone slots staged through LDS at a time
+constexpr int kMaxSplitsDev = kMaxSplits;
 
 template <int D, int G>
 struct Cfg {
@@ -55,6 +56,16 @@ struct DecodeSmem {
   float wm[kWaves][4 * C::NQ];
   float wl[kWaves][4 * C::NQ];
   float wacc[kWaves][4 * C::NQ][D];
+  long long voff[kWaves][64];              // sparse mode: byte offset of each selected token's V column
+};
+
+template <int D, int G>
+struct HotSmem {
+  float q[G][D];
+  float acc[G][D];
+  float z[G][kHotChunk];                   // logits, then weights, of the current chunk
+  float m[G], l[G], alpha[G];
+  _Float16 kv[kHotChunk * (2 * D + 8)];     // staged [K|V] rows of the current chunk (padded)
 };
 
 template <int D, int G>
@@ -177,12 +188,16 @@ __device__ void cold_block_unit(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const
   wave_lds_sync();
 }
 
-// Sparse unit: up to 64 selected cold tokens, one gathered row per lane.
+// Sparse unit: up to 64 selected cold tokens, one gathered row per lane.  For
+// PV, lane c needs the value code of every selected token at channel c: the
+// tokens' V-tile offsets go through LDS and the byte loads of 16 tokens are
+// issued together, so the unit pays four memory latencies, not 64.
 template <int D, int G>
 __device__ void gather_unit(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const CacheView& c, const int32_t* sel_bh,
                             int k_sel, int b, int h, int chunk, int n_cold, float qscale, int w, int lane) {
   using C = Cfg<D, G>;
   constexpr int S = kBlockSize;
+  constexpr int TB = 16;  // tokens whose value bytes are loaded together
   const int e = chunk * 64 + lane;
   const int idx = e < k_sel ? sel_bh[e] : -1;
   int phys = -1;
@@ -204,52 +219,66 @@ __device__ void gather_unit(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const Cac
 #pragma unroll
     for (int ch = 0; ch < D / 16; ++ch) kr[ch] = make_uint4(0, 0, 0, 0);
   }
+  // byte offset of (token, channel 0) in the cold pool, or -1 for a masked lane
+  sm.voff[w][lane] = valid ? static_cast<long long>(tile_offset(phys, h, 1, c.H, S, D)) + (t / 16) * D * 16 + (t % 16)
+                           : -1ll;
   float4_t s[C::NQ];
   qk_codes<D, G>(kr, sm, lane, s);
   softmax_unit<D, G>(st, sm, s, valid, sK * qscale, sV, w, lane);
   const int cnt = min(64, k_sel - chunk * 64);
-  for (int t0 = 0; t0 < cnt; t0 += 4) {
-    float4_t pa[C::NQ];
+  for (int tb = 0; tb < cnt; tb += TB) {
+    float vf[TB][C::NDL];
 #pragma unroll
-    for (int quad = 0; quad < C::NQ; ++quad) pa[quad] = *reinterpret_cast<const float4_t*>(&sm.pw[w][quad][lane & 3][t0]);
+    for (int k = 0; k < TB; ++k) {
+      const long long off = sm.voff[w][tb + k];  // uniform across the wave
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      // token t0 + k of this run (uniform across the wave); a masked token has p = 0 and reads nothing
-      const int i2 = t0 + k;
-      const int idx2 = i2 < cnt ? sel_bh[chunk * 64 + i2] : -1;
-      int phys2 = -1;
-      if (idx2 >= 0 && idx2 < n_cold && idx2 / S < c.max_blocks)
-        phys2 = c.headers[static_cast<size_t>(b) * c.max_blocks + idx2 / S].phys_block;
-      const bool ok = phys2 >= 0 && phys2 < c.num_phys;
-      const int8_t* vt = ok ? c.cold + tile_offset(phys2, h, 1, c.H, S, D) + ((idx2 % S) / 16) * D * 16 + (idx2 % 16)
-                            : nullptr;
+      for (int ps = 0; ps < C::NDL; ++ps)
+        vf[k][ps] = off >= 0 ? static_cast<float>(c.cold[off + (64 * ps + lane) * 16]) : 0.f;
+    }
 #pragma unroll
-      for (int ps = 0; ps < C::NDL; ++ps) {
-        const float vf = ok ? static_cast<float>(vt[(64 * ps + lane) * 16]) : 0.f;
+    for (int t0 = 0; t0 < TB; t0 += 4) {
+      float4_t pa[C::NQ];
 #pragma unroll
-        for (int quad = 0; quad < C::NQ; ++quad) st.acc[quad][ps][k & 1] = mfma_pv(pa[quad][k], vf, st.acc[quad][ps][k & 1]);
-      }
+      for (int quad = 0; quad < C::NQ; ++quad)
+        pa[quad] = *reinterpret_cast<const float4_t*>(&sm.pw[w][quad][lane & 3][tb + t0]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int ps = 0; ps < C::NDL; ++ps)
+#pragma unroll
+          for (int quad = 0; quad < C::NQ; ++quad)
+            st.acc[quad][ps][k & 1] = mfma_pv(pa[quad][k], vf[t0 + k][ps], st.acc[quad][ps][k & 1]);
     }
   }
   wave_lds_sync();
 }
 
+// Partials are exchanged between workgroups that may sit on different XCDs
+// (each with its own L2).  They are written and read with agent-scope relaxed
+// atomic accesses (device-coherent sc1 loads/stores), so publishing them needs
+// only a wait for the stores to complete, not an L2-wide writeback.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Partial record of one split: m (base-2 log units), l, acc[D] for each of the G query heads.
+template <int D>
+__device__ __forceinline__ float* partial_ptr(const DecodeParams& p, int bh, int split, int g) {
+  return p.partials + ((static_cast<size_t>(bh) * (p.nsplit + 1) + split) * p.G + g) * (D + 2);
+}
+
+// ---- cold split: stream its units, merge the 4 waves, write the partial
 template <int D, int G, bool SPARSE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void decode_partial_kernel(DecodeParams p) {
+__device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, int h, int bh, int split) {
   using C = Cfg<D, G>;
   constexpr int S = kBlockSize;
   constexpr int NG = 4 * C::NQ;
-  __shared__ DecodeSmem<D, G> sm;
   const CacheView& c = p.c;
-  const int H = c.H;
-  const int split = blockIdx.x % p.nsplit;
-  const int bh = blockIdx.x / p.nsplit;
-  const int h = bh % H;
-  const int b = bh / H;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-
-  // query rows of this kv-head's group as fp16 (exact copies), zero rows past G
-  const _Float16* qg = p.q + (static_cast<size_t>(b) * H * G + static_cast<size_t>(h) * G) * D;
+  const _Float16* qg = p.q + (static_cast<size_t>(b) * c.H * G + static_cast<size_t>(h) * G) * D;
   for (int i = tid; i < NG * D; i += kThreads) {
     const int g = i / D, d = i % D;
     sm.qh[g / 4][g % 4][d] = g < G ? qg[g * D + d] : static_cast<_Float16>(0.f);
@@ -258,7 +287,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 
   const SeqGeom sg = seq_geom(c.seq_len[b], c.T, S);
   const int units = sg.n_cold > 0 ? (SPARSE ? cdiv(p.k_sel, 64) : sg.n_blk) : 0;
-  const int32_t* sel_bh = SPARSE ? p.sel + (static_cast<size_t>(b) * H + h) * p.k_sel : nullptr;
+  const int32_t* sel_bh = SPARSE ? p.sel + static_cast<size_t>(bh) * p.k_sel : nullptr;
 
   WaveState<D, G> st;
 #pragma unroll
@@ -282,7 +311,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       }
     }
   }
-  // ---- merge the 4 waves: lane holds out[4quad + r][64 pass + lane]
+  // merge the 4 waves: lane holds out[4quad + r][64 pass + lane]
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     const float lsum = wave_sum(st.l[g]);
@@ -298,7 +327,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 #pragma unroll
       for (int r = 0; r < 4; ++r) sm.wacc[w][4 * quad + r][64 * ps + lane] = st.acc[quad][ps][0][r] + st.acc[quad][ps][1][r];
   __syncthreads();
-  float* part = p.partials + (static_cast<size_t>(bh) * p.nsplit + split) * G * (D + 2);
   for (int idx = tid; idx < G * D; idx += kThreads) {
     const int g = idx / D, d = idx % D;
     float M = kNegInf;
@@ -314,92 +342,159 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         A += f * sm.wacc[ww][g][d];
       }
     }
-    float* pg = part + g * (D + 2);
-    pg[2 + d] = A;
+    float* pg = partial_ptr<D>(p, bh, split, g);
+    store_coherent(pg + 2 + d, A);
     if (d == 0) {
-      pg[0] = M;
-      pg[1] = L;
+      store_coherent(pg, M);
+      store_coherent(pg + 1, L);
     }
   }
 }
 
-// Hot zone + combine, one workgroup per (sequence, query head).  The FP16 hot
-// zone (Hybrid KV Cache page 2.1: the most recent tokens in full precision) is
-// attended here in fp32: thread t scores slot t, thread d accumulates channel
-// d.  Its (m, l, acc) is then merged with the cold splits' partials by the
-// log-sum-exp rule: M = max m_s, L = sum e^(m_s - M) l_s, out = sum e^(m_s - M)
-// acc_s / L.
-template <int D>
-__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeParams p) {
-  __shared__ float qf[D];
-  __shared__ float ph[kCombineThreads];
-  __shared__ float red[kCombineThreads / 64];
+// ---- hot split: the FP16 ring (Hybrid KV Cache page 2.1: the most recent
+// tokens in full precision), attended in fp32.  Chunks of kHotChunk slots are
+// staged through LDS with coalesced loads; thread (g, t) scores slot t for
+// query head g, thread (g, d) accumulates channel d.
+template <int D, int G>
+__device__ void hot_split(const DecodeParams& p, HotSmem<D, G>& hm, int b, int h, int bh) {
+  constexpr int ROW = 2 * D + 8;          // padded fp16 [K|V] row
+  constexpr int VPR = 2 * D / 8;          // 16-byte vectors per row
   const CacheView& c = p.c;
-  const int Hq = c.H * p.G;
-  const int b = blockIdx.x / Hq;
-  const int hq = blockIdx.x % Hq;
-  const int h = hq / p.G, g = hq % p.G;
   const int tid = threadIdx.x;
-  for (int d = tid; d < D; d += kCombineThreads) qf[d] = static_cast<float>(p.q[(static_cast<size_t>(b) * Hq + hq) * D + d]);
-  __syncthreads();
+  const _Float16* qg = p.q + (static_cast<size_t>(b) * c.H * G + static_cast<size_t>(h) * G) * D;
+  for (int i = tid; i < G * D; i += kThreads) hm.q[i / D][i % D] = static_cast<float>(qg[i]);
+  for (int g = tid; g < G; g += kThreads) {
+    hm.m[g] = kNegInf;
+    hm.l[g] = 0.f;
+  }
+  for (int i = tid; i < G * D; i += kThreads) hm.acc[i / D][i % D] = 0.f;
   const SeqGeom sg = seq_geom(c.seq_len[b], c.T, kBlockSize);
-  const _Float16* hot_bh = c.hot + (static_cast<size_t>(b) * c.H + h) * c.T * 2 * D;
-  // ---- hot logits (base 2): slot t < n_hot (ring slots hold positions mod T; order is irrelevant)
-  float z = kNegInf;
-  if (tid < sg.n_hot) {
-    const uint4* krow = reinterpret_cast<const uint4*>(hot_bh + static_cast<size_t>(tid) * 2 * D);
-    float acc = 0.f;
-#pragma unroll
-    for (int v = 0; v < D / 8; ++v) {
-      const uint4 kw = krow[v];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t wd = word_of(kw, i);
-        acc = fmaf(qf[v * 8 + 2 * i], half_lo(wd), acc);
-        acc = fmaf(qf[v * 8 + 2 * i + 1], half_hi(wd), acc);
+  const _Float16* hot_bh = c.hot + static_cast<size_t>(bh) * c.T * 2 * D;
+  __syncthreads();
+  for (int base = 0; base < sg.n_hot; base += kHotChunk) {
+    const int cnt = min(kHotChunk, sg.n_hot - base);
+    const uint4* src = reinterpret_cast<const uint4*>(hot_bh + static_cast<size_t>(base) * 2 * D);
+    for (int i = tid; i < cnt * VPR; i += kThreads)
+      *reinterpret_cast<uint4*>(&hm.kv[(i / VPR) * ROW + (i % VPR) * 8]) = src[i];
+    __syncthreads();
+    // logits (base 2)
+    for (int i = tid; i < G * kHotChunk; i += kThreads) {
+      const int g = i / kHotChunk, t = i % kHotChunk;
+      float z = kNegInf;
+      if (t < cnt) {
+        float acc = 0.f;
+        const _Float16* kr = &hm.kv[t * ROW];
+#pragma unroll 8
+        for (int d = 0; d < D; ++d) acc = fmaf(hm.q[g][d], static_cast<float>(kr[d]), acc);
+        z = acc * p.qscale;
       }
+      hm.z[g][t] = z;
     }
-    z = acc * p.qscale;
+    __syncthreads();
+    // online softmax per query head (one thread each: at most 8 heads x 32 slots)
+    for (int g = tid; g < G; g += kThreads) {
+      float mb = kNegInf;
+      for (int t = 0; t < cnt; ++t) mb = fmaxf(mb, hm.z[g][t]);
+      const float mn = fmaxf(hm.m[g], mb);
+      const float alpha = exp2_approx(hm.m[g] - mn);
+      float ls = 0.f;
+      for (int t = 0; t < kHotChunk; ++t) {
+        const float pt = t < cnt ? exp2_approx(hm.z[g][t] - mn) : 0.f;
+        hm.z[g][t] = pt;
+        ls += pt;
+      }
+      hm.l[g] = hm.l[g] * alpha + ls;
+      hm.m[g] = mn;
+      hm.alpha[g] = alpha;
+    }
+    __syncthreads();
+    for (int i = tid; i < G * D; i += kThreads) {
+      const int g = i / D, d = i % D;
+      float a = hm.acc[g][d] * hm.alpha[g];
+      for (int t = 0; t < cnt; ++t) a = fmaf(hm.z[g][t], static_cast<float>(hm.kv[t * ROW + D + d]), a);
+      hm.acc[g][d] = a;
+    }
+    __syncthreads();
   }
-  float mh = wave_max(z);
-  if ((tid & 63) == 0) red[tid >> 6] = mh;
-  __syncthreads();
-  mh = red[0];
-#pragma unroll
-  for (int i = 1; i < kCombineThreads / 64; ++i) mh = fmaxf(mh, red[i]);
-  __syncthreads();
-  const float pt = tid < sg.n_hot ? exp2_approx(z - mh) : 0.f;
-  ph[tid] = pt;
-  float lh = wave_sum(pt);
-  if ((tid & 63) == 0) red[tid >> 6] = lh;
-  __syncthreads();
-  lh = 0.f;
-#pragma unroll
-  for (int i = 0; i < kCombineThreads / 64; ++i) lh += red[i];
-  // ---- merge with the cold partials
-  const size_t stride = static_cast<size_t>(p.G) * (D + 2);
-  const float* base = p.partials + ((static_cast<size_t>(b) * c.H + h) * p.nsplit) * stride + g * (D + 2);
-  float M = mh;
-  for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, base[s * stride]);
-  for (int d = tid; d < D; d += kCombineThreads) {
-    float A = 0.f, L = 0.f;
-    if (mh != kNegInf) {
-      float ah = 0.f;
-      for (int t = 0; t < sg.n_hot; ++t) ah = fmaf(ph[t], static_cast<float>(hot_bh[(static_cast<size_t>(t) * 2 + 1) * D + d]), ah);
-      const float f = exp2_approx(mh - M);
-      A = f * ah;
-      L = f * lh;
+  for (int i = tid; i < G * D; i += kThreads) {
+    const int g = i / D, d = i % D;
+    float* pg = partial_ptr<D>(p, bh, p.nsplit, g);
+    store_coherent(pg + 2 + d, hm.acc[g][d]);
+    if (d == 0) {
+      store_coherent(pg, hm.m[g]);
+      store_coherent(pg + 1, hm.l[g]);
     }
-    for (int s = 0; s < p.nsplit; ++s) {
-      const float ms = base[s * stride];
-      if (ms == kNegInf) continue;
-      const float f = exp2_approx(ms - M);
-      L += f * base[s * stride + 1];
-      A += f * base[s * stride + 2 + d];
-    }
-    p.out[(static_cast<size_t>(b) * Hq + hq) * D + d] = static_cast<_Float16>(A / L);
-    if (d == 0 && p.lse) p.lse[static_cast<size_t>(b) * Hq + hq] = (M + __builtin_log2f(L)) * kLn2;
   }
+}
+
+// One launch per decode call: B*H*(nsplit + 1) workgroups; for each (sequence,
+// kv-head) nsplit cold splits and one hot split write partials, and the last
+// of them to arrive merges all nsplit + 1 partials with the log-sum-exp rule
+// (M = max m_s, L = sum e^(m_s - M) l_s, out = sum e^(m_s - M) acc_s / L) and
+// writes the fp16 output.  Arrival is counted with a device-scope atomic in
+// the workspace, which the merging workgroup resets to zero.
+template <int D, int G, bool SPARSE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G > 4 ? 2 : 3))) void decode_kernel(DecodeParams p) {
+  __shared__ union Smem {
+    DecodeSmem<D, G> cold;
+    HotSmem<D, G> hot;
+  } sm;
+  __shared__ int s_last;
+  __shared__ float sm_w[kMaxSplitsDev + 1][G];   // m_s, then e^(m_s - M)
+  __shared__ float sm_l[kMaxSplitsDev + 1][G];
+  __shared__ float sm_M[G], sm_L[G];
+  const CacheView& c = p.c;
+  const int split = blockIdx.x % (p.nsplit + 1);
+  const int bh = blockIdx.x / (p.nsplit + 1);
+  const int h = bh % c.H;
+  const int b = bh / c.H;
+  const int tid = threadIdx.x;
+  if (split < p.nsplit) {
+    cold_split<D, G, SPARSE>(p, sm.cold, b, h, bh, split);
+  } else {
+    hot_split<D, G>(p, sm.hot, b, h, bh);
+  }
+  // ---- arrival: wait until this workgroup's partial stores are complete, count, and let the
+  // last workgroup merge
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(&p.counters[bh], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             static_cast<unsigned>(p.nsplit);
+  __syncthreads();
+  if (!s_last) return;
+  // weights e^(m_s - M) per (split, head) through LDS: one round of loads for all m_s and l_s
+  const int NS = p.nsplit + 1;
+  for (int i = tid; i < NS * G; i += kThreads) {
+    const float* pg = partial_ptr<D>(p, bh, i / G, i % G);
+    sm_w[i / G][i % G] = load_coherent(pg);
+    sm_l[i / G][i % G] = load_coherent(pg + 1);
+  }
+  __syncthreads();
+  for (int g = tid; g < G; g += kThreads) {
+    float M = kNegInf;
+    for (int s2 = 0; s2 < NS; ++s2) M = fmaxf(M, sm_w[s2][g]);
+    float L = 0.f;
+    for (int s2 = 0; s2 < NS; ++s2) {
+      const float f = sm_w[s2][g] == kNegInf ? 0.f : exp2_approx(sm_w[s2][g] - M);
+      sm_w[s2][g] = f;
+      L += f * sm_l[s2][g];
+    }
+    sm_M[g] = M;
+    sm_L[g] = L;
+  }
+  __syncthreads();
+  const int Hq = c.H * G;
+  for (int i = tid; i < G * D; i += kThreads) {
+    const int g = i / D, d = i % D;
+    float A = 0.f;
+#pragma unroll 8
+    for (int s2 = 0; s2 < NS; ++s2) A = fmaf(sm_w[s2][g], load_coherent(partial_ptr<D>(p, bh, s2, g) + 2 + d), A);
+    const int hq = h * G + g;
+    p.out[(static_cast<size_t>(b) * Hq + hq) * D + d] = static_cast<_Float16>(A / sm_L[g]);
+    if (d == 0 && p.lse) p.lse[static_cast<size_t>(b) * Hq + hq] = (sm_M[g] + __builtin_log2f(sm_L[g])) * kLn2;
+  }
+  if (tid == 0) __hip_atomic_store(&p.counters[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <typename K>
@@ -414,21 +509,19 @@ hipError_t launch_k(K kernel, int grid, int block, const DecodeParams& p, const 
 }
 
 template <int D, int G>
-hipError_t launch_dg(const DecodeParams& p, const LaunchCtx& part_ctx, const LaunchCtx& comb_ctx) {
-  const int grid = p.c.B * p.c.H * p.nsplit;
-  hipError_t e = p.sel ? launch_k(decode_partial_kernel<D, G, true>, grid, kThreads, p, part_ctx)
-                       : launch_k(decode_partial_kernel<D, G, false>, grid, kThreads, p, part_ctx);
-  if (e != hipSuccess) return e;
-  return launch_k(decode_combine_kernel<D>, p.c.B * p.c.H * p.G, kCombineThreads, p, comb_ctx);
+hipError_t launch_dg(const DecodeParams& p, const LaunchCtx& ctx) {
+  const int grid = p.c.B * p.c.H * (p.nsplit + 1);
+  return p.sel ? launch_k(decode_kernel<D, G, true>, grid, kThreads, p, ctx)
+               : launch_k(decode_kernel<D, G, false>, grid, kThreads, p, ctx);
 }
 
 template <int D>
-hipError_t launch_d(const DecodeParams& p, const LaunchCtx& a, const LaunchCtx& b) {
+hipError_t launch_d(const DecodeParams& p, const LaunchCtx& a) {
   switch (p.G) {
-    case 1: return launch_dg<D, 1>(p, a, b);
-    case 2: return launch_dg<D, 2>(p, a, b);
-    case 4: return launch_dg<D, 4>(p, a, b);
-    case 8: return launch_dg<D, 8>(p, a, b);
+    case 1: return launch_dg<D, 1>(p, a);
+    case 2: return launch_dg<D, 2>(p, a);
+    case 4: return launch_dg<D, 4>(p, a);
+    case 8: return launch_dg<D, 8>(p, a);
     default: return hipErrorInvalidValue;
   }
 }
@@ -437,8 +530,8 @@ hipError_t launch_d(const DecodeParams& p, const LaunchCtx& a, const LaunchCtx& 
 
 using namespace detail;
 
-hipError_t launch_decode(const DecodeParams& p, const LaunchCtx& part_ctx, const LaunchCtx& comb_ctx) {
-  return p.c.D == 128 ? launch_d<128>(p, part_ctx, comb_ctx) : launch_d<64>(p, part_ctx, comb_ctx);
+hipError_t launch_decode(const DecodeParams& p, const LaunchCtx& ctx) {
+  return p.c.D == 128 ? launch_d<128>(p, ctx) : launch_d<64>(p, ctx);
 }
 
 }  // namespace hkv

@@ -39,7 +39,7 @@ using hkv::LaunchCtx;
 
 // Target workgroups per decode/top-K launch: 4 per CU on 256 CUs, 16 waves/CU.
 constexpr int kTargetWorkgroups = 1024;
-constexpr int kMaxSplits = 512;
+using hkv::kMaxSplits;
 
 bool valid_protocol(int hot_tokens, int block_size) {
   const bool hot_ok = hot_tokens == 16 || hot_tokens == 32 || hot_tokens == 64 || hot_tokens == 128;
@@ -112,13 +112,16 @@ hkv::CacheView view_of(const hkv_ctx* h, const hkv_cache_desc* c) {
   return v;
 }
 
+// Decode workspace: partials [B][H][nsplit + 1][G][D + 2] fp32, then one arrival
+// counter per (sequence, kv-head).
 size_t partials_bytes(const hkv_ctx* h, const hkv_cache_desc* c, int G, int k_sel) {
   const int64_t bh = static_cast<int64_t>(c->batch) * h->H;
-  const int64_t dense_units = 1 + c->max_blocks_per_seq;
-  int ns = max_splits(bh, dense_units);
-  if (k_sel > 0) ns = std::max(ns, max_splits(bh, 1 + (k_sel + 63) / 64));
-  return static_cast<size_t>(bh) * ns * G * (h->D + 2) * sizeof(float);
+  int ns = max_splits(bh, std::max<int64_t>(1, c->max_blocks_per_seq));
+  if (k_sel > 0) ns = std::max(ns, max_splits(bh, (k_sel + 63) / 64));
+  return static_cast<size_t>(bh) * (ns + 1) * G * (h->D + 2) * sizeof(float);
 }
+
+size_t counters_bytes(const hkv_cache_desc* c, int H) { return static_cast<size_t>(c->batch) * H * sizeof(unsigned); }
 
 size_t topk_bytes(const hkv_ctx* h, const hkv_cache_desc* c) {
   return static_cast<size_t>(c->batch) * h->H * c->max_blocks_per_seq * h->S * sizeof(float);
@@ -221,8 +224,9 @@ hkv_status hkv_workspace_bytes(hkv_handle h, const hkv_cache_desc* c, int n_q_he
   if (n_q_heads < 1 || n_q_heads % h->H != 0) return HKV_ERR_INVALID_VALUE;
   if (k_sel < 0 || k_sel > hkv::kMaxTopK) return HKV_ERR_INVALID_VALUE;
   const int G = n_q_heads / h->H;
-  size_t ws = align_up(partials_bytes(h, c, G, k_sel), 256);
-  if (k_sel > 0) ws = std::max(ws, align_up(topk_bytes(h, c), 256));
+  // the counters sit at the front so that their offset does not depend on the state
+  size_t ws = align_up(counters_bytes(c, h->H), 256) + align_up(partials_bytes(h, c, G, k_sel), 256);
+  if (k_sel > 0) ws = std::max(ws, align_up(counters_bytes(c, h->H), 256) + align_up(topk_bytes(h, c), 256));
   *bytes = std::max<size_t>(ws, 256);
   return HKV_OK;
 }
@@ -261,6 +265,7 @@ hkv_status hkv_append(hkv_handle h, const hkv_cache_desc* c, const void* k_new, 
       const int b = b0 + i;
       const int nn = n_new_host[b];
       p.n_new[i] = nn;
+      p.n0[i] = c->seq_len_host[b];
       if (nn == 0) continue;
       chunk_any = true;
       const int64_t n0 = c->seq_len_host[b], n1 = n0 + nn;
@@ -271,9 +276,10 @@ hkv_status hkv_append(hkv_handle h, const hkv_cache_desc* c, const void* k_new, 
     p.b0 = b0;
     p.n_seq = ns;
     p.touched_max = touched;
-    LaunchCtx qctx = make_ctx(h, stream, HKV_KERNEL_APPEND_QUANT);
-    LaunchCtx rctx = make_ctx(h, stream, HKV_KERNEL_APPEND_RING);
-    if (touched == 0 && qctx.start) {  // nothing to quantise: release the unused event pair
+    p.single_pass = touched <= hkv::kSinglePassMaxBlocks ? 1 : 0;
+    LaunchCtx qctx = make_ctx(h, stream, HKV_KERNEL_APPEND);
+    LaunchCtx rctx = p.single_pass ? LaunchCtx{stream, nullptr, nullptr} : make_ctx(h, stream, HKV_KERNEL_APPEND_RING);
+    if (touched == 0 && !p.single_pass && qctx.start) {  // nothing to quantise: release the unused event pair
       h->free_events.push_back(qctx.start);
       h->free_events.push_back(qctx.stop);
       h->pending.erase(h->pending.end() - 2);
@@ -302,7 +308,7 @@ hkv_status hkv_decode_attn(hkv_handle h, const hkv_cache_desc* c, const void* q,
     if (n == 0) return HKV_ERR_INVALID_VALUE;
     const int64_t nblk = cold_blocks(n, h->T, h->S);
     const int64_t cold_units = sel_idx ? (nblk > 0 ? (k_sel + 63) / 64 : 0) : nblk;
-    units_max = std::max(units_max, 1 + cold_units);
+    units_max = std::max(units_max, cold_units);
   }
   size_t need = 0;
   if (hkv_workspace_bytes(h, c, n_q_heads, sel_idx ? k_sel : 0, &need) != HKV_OK) return HKV_ERR_INVALID_VALUE;
@@ -316,16 +322,16 @@ hkv_status hkv_decode_attn(hkv_handle h, const hkv_cache_desc* c, const void* q,
   p.q = static_cast<const _Float16*>(q);
   p.sel = sel_idx;
   p.k_sel = sel_idx ? k_sel : 0;
-  p.partials = static_cast<float*>(workspace);
+  p.counters = static_cast<unsigned*>(workspace);
+  p.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(counters_bytes(c, h->H), 256));
   const SplitPlan sp = plan_splits(static_cast<int64_t>(c->batch) * h->H, units_max);
   p.nsplit = sp.nsplit;
   p.units_per_split = sp.per_split;
   p.qscale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(h->D)));
   p.out = static_cast<_Float16*>(out);
   p.lse = lse;
-  LaunchCtx a = make_ctx(h, stream, sel_idx ? HKV_KERNEL_DECODE_GATHER : HKV_KERNEL_DECODE_PARTIAL);
-  LaunchCtx b = make_ctx(h, stream, HKV_KERNEL_DECODE_COMBINE);
-  return hip_status(hkv::launch_decode(p, a, b), "hkv_decode_attn launch");
+  LaunchCtx a = make_ctx(h, stream, sel_idx ? HKV_KERNEL_DECODE_SPARSE : HKV_KERNEL_DECODE);
+  return hip_status(hkv::launch_decode(p, a), "hkv_decode_attn launch");
 }
 
 hkv_status hkv_topk_select(hkv_handle h, const hkv_cache_desc* c, const void* q, int n_q_heads, int k,
@@ -350,7 +356,7 @@ hkv_status hkv_topk_select(hkv_handle h, const hkv_cache_desc* c, const void* q,
   p.c = view_of(h, c);
   p.G = G;
   p.q = static_cast<const _Float16*>(q);
-  p.prob = static_cast<float*>(workspace);
+  p.prob = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(counters_bytes(c, h->H), 256));
   const SplitPlan sp = plan_splits(static_cast<int64_t>(c->batch) * h->H, blk_max);
   p.nsplit = sp.nsplit;
   p.units_per_split = sp.per_split;

@@ -13,7 +13,9 @@ constexpr int kBlockSize = 64;      // tokens per cold block (the only built val
 constexpr int kThreads = 256;       // 4 wave64 per workgroup for the streaming kernels
 constexpr int kWaves = kThreads / 64;
 constexpr int kAppendChunk = 256;   // sequences whose append counts travel in one kernel-argument block
+constexpr int kSinglePassMaxBlocks = 2;  // appends touching at most this many blocks per sequence use one launch
 constexpr int kMaxTopK = 512;       // fixed top-K budget of the sparse path
+constexpr int kMaxSplits = 128;     // cold splits per (sequence, kv-head) at most
 
 // Per-launch timing: when start/stop are non-null the dispatch records them.
 struct LaunchCtx {
@@ -41,7 +43,9 @@ struct AppendParams {
   int b0;                  // first sequence of this launch
   int n_seq;               // sequences in this launch (<= kAppendChunk)
   int touched_max;         // grid extent over touched cold blocks per sequence
+  int single_pass;         // 1: append_step_kernel (lengths from n0[]), 0: two-pass kernels
   int32_t n_new[kAppendChunk];
+  int32_t n0[kAppendChunk];  // cached length before the append (host mirror)
 };
 
 struct DecodeParams {
@@ -50,8 +54,9 @@ struct DecodeParams {
   const _Float16* q;       // [B][H*G][D]
   const int32_t* sel;      // sparse mode: [B][H][k_sel]; nullptr for dense
   int k_sel;
-  float* partials;         // [B][H][nsplit][G][D + 2]  (m in log2 units, l, acc[D])
-  int nsplit;              // splits per (sequence, kv-head)
+  float* partials;         // [B][H][nsplit + 1][G][D + 2]  (m in log2 units, l, acc[D]); last = hot zone
+  unsigned* counters;      // [B*H] arrival counters, zero between calls
+  int nsplit;              // cold splits per (sequence, kv-head)
   int units_per_split;     // units handled per split (multiple of kWaves)
   float qscale;            // log2(e) / sqrt(D)
   _Float16* out;           // [B][H*G][D]
@@ -70,7 +75,7 @@ struct TopkParams {
 };
 
 hipError_t launch_append(const AppendParams& p, const LaunchCtx& quant_ctx, const LaunchCtx& ring_ctx);
-hipError_t launch_decode(const DecodeParams& p, const LaunchCtx& part_ctx, const LaunchCtx& comb_ctx);
+hipError_t launch_decode(const DecodeParams& p, const LaunchCtx& ctx);
 hipError_t launch_topk(const TopkParams& p, const LaunchCtx& score_ctx, const LaunchCtx& sel_ctx);
 
 }  // namespace hkv
