@@ -237,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void append_step_kernel(AppendParams p) {
   constexpr int LDS_ROW = D + 16;
   constexpr int VPR = D / 8;            // 16-byte vectors per fp16 row
   __shared__ __align__(16) int8_t stage[S * LDS_ROW];
-  __shared__ float red[kWaves];
+  __shared__ float red[kWaves], red2[kWaves];
 
   const CacheView& c = p.c;
   const int H = c.H, T = c.T;
@@ -259,56 +259,75 @@ __global__ __launch_bounds__(kThreads) void append_step_kernel(AppendParams p) {
     if (pos < n0) return c.hot + ((bh * T + (pos % T)) * 2 + kv) * D;
     return (kv ? p.v_new : p.k_new) + ((static_cast<size_t>(b) * p.max_n_new + (pos - n0)) * H + h) * D;
   };
-  auto block_max = [&](float m) -> float {
-    m = wave_max(m);
-    if ((tid & 63) == 0) red[tid >> 6] = m;
+  auto block_max2 = [&](float& m0, float& m1) {
+    m0 = wave_max(m0);
+    m1 = wave_max(m1);
+    if ((tid & 63) == 0) {
+      red[tid >> 6] = m0;
+      red2[tid >> 6] = m1;
+    }
     __syncthreads();
-    float r = red[0];
+    float r0 = red[0], r1 = red2[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) r = fmaxf(r, red[w]);
+    for (int w = 1; w < kWaves; ++w) {
+      r0 = fmaxf(r0, red[w]);
+      r1 = fmaxf(r1, red2[w]);
+    }
     __syncthreads();
-    return r;
+    m0 = r0;
+    m1 = r1;
+  };
+  auto load_row = [&](const _Float16* row, float (&x)[CPT]) {
+    const uint4* r4 = reinterpret_cast<const uint4*>(row + part * CPT);
+#pragma unroll
+    for (int v = 0; v < CPT / 8; ++v) {
+      const uint4 wv = r4[v];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[v * 8 + 2 * i] = half_lo(word_of(wv, i));
+        x[v * 8 + 2 * i + 1] = half_hi(word_of(wv, i));
+      }
+    }
   };
 
   for (int j = cold0 / S; j * S < cold1; ++j) {
     if (j >= c.max_blocks) break;
-    hkv_block_header* hdr = c.headers + static_cast<size_t>(b) * c.max_blocks + j;
-    const int phys = hdr->phys_block;
-    if (phys < 0 || phys >= c.num_phys) continue;
     const int v_old = j * S < cold0 ? cold0 - j * S : 0;   // rows already coded, FP16 in the tail shadow
     const int v_new = min(S, cold1 - j * S);
+    const bool is_new = t >= v_old && t < v_new;
+    // the new K and V rows do not depend on the block's physical id: load them together with the header
+    float x[2][CPT];
+#pragma unroll
     for (int kv = 0; kv < 2; ++kv) {
-      float x[CPT];
-      const bool is_new = t >= v_old && t < v_new;
       if (is_new) {
-        const uint4* r4 = reinterpret_cast<const uint4*>(row_ptr(j * S + t, kv) + part * CPT);
-#pragma unroll
-        for (int v = 0; v < CPT / 8; ++v) {
-          const uint4 wv = r4[v];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            x[v * 8 + 2 * i] = half_lo(word_of(wv, i));
-            x[v * 8 + 2 * i + 1] = half_hi(word_of(wv, i));
-          }
-        }
+        load_row(row_ptr(j * S + t, kv), x[kv]);
       } else {
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) x[i] = 0.f;
+        for (int i = 0; i < CPT; ++i) x[kv][i] = 0.f;
       }
-      float m = 0.f;
+    }
+    hkv_block_header* hdr = c.headers + static_cast<size_t>(b) * c.max_blocks + j;
+    const int phys = hdr->phys_block;
+    float mnew[2] = {0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < CPT; ++i) m = fmaxf(m, fabsf(x[i]));
-      const float m_new = block_max(m);
-      float* sp = c.scales + (static_cast<size_t>(phys) * H + h) * 2 + kv;
+    for (int kv = 0; kv < 2; ++kv)
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) mnew[kv] = fmaxf(mnew[kv], fabsf(x[kv][i]));
+    block_max2(mnew[0], mnew[1]);
+    if (phys < 0 || phys >= c.num_phys) continue;
+    float* sp = c.scales + (static_cast<size_t>(phys) * H + h) * 2;
+    const float s_old[2] = {v_old > 0 ? sp[0] : 0.f, v_old > 0 ? sp[1] : 0.f};
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv) {  // unrolled: x[kv] must stay in registers
       int8_t* tile = c.cold + tile_offset(phys, h, kv, H, S, D);
-      const float s_old = v_old > 0 ? *sp : 0.f;
-      if (v_old > 0 && m_new / 127.0f <= s_old) {
+      if (v_old > 0 && mnew[kv] / 127.0f <= s_old[kv]) {
         // ---- scale unchanged: code only the new rows, in place
+        const float so = s_old[kv];
         if (is_new) {
           int8_t q8[CPT];
 #pragma unroll
           for (int i = 0; i < CPT; ++i)
-            q8[i] = s_old > 0.f ? static_cast<int8_t>(fminf(127.f, fmaxf(-127.f, __builtin_rintf(x[i] / s_old)))) : 0;
+            q8[i] = so > 0.f ? static_cast<int8_t>(fminf(127.f, fmaxf(-127.f, __builtin_rintf(x[kv][i] / so)))) : 0;
           if (kv == 0) {
 #pragma unroll
             for (int ch = 0; ch < CPT / 16; ++ch) {
@@ -330,22 +349,15 @@ __global__ __launch_bounds__(kThreads) void append_step_kernel(AppendParams p) {
         continue;
       }
       // ---- (re-)quantise the whole block: old rows come back from the tail shadow
-      if (t < v_old) {
-        const uint4* r4 = reinterpret_cast<const uint4*>(c.tail + ((bh * 2 + kv) * S + t) * D + part * CPT);
+      float mblk = mnew[kv];
+      if (v_old > 0) {
+        if (t < v_old) load_row(c.tail + ((bh * 2 + kv) * S + t) * D, x[kv]);
+        float mo = 0.f, dummy = 0.f;
 #pragma unroll
-        for (int v = 0; v < CPT / 8; ++v) {
-          const uint4 wv = r4[v];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            x[v * 8 + 2 * i] = half_lo(word_of(wv, i));
-            x[v * 8 + 2 * i + 1] = half_hi(word_of(wv, i));
-          }
-        }
+        for (int i = 0; i < CPT; ++i) mo = fmaxf(mo, fabsf(x[kv][i]));
+        block_max2(mo, dummy);
+        mblk = fmaxf(mblk, mo);
       }
-      float mo = 0.f;
-#pragma unroll
-      for (int i = 0; i < CPT; ++i) mo = fmaxf(mo, fabsf(x[i]));
-      const float mblk = v_old > 0 ? fmaxf(m_new, block_max(mo)) : m_new;
       const float s = mblk / 127.0f;
       int8_t* srow = stage + t * LDS_ROW + part * CPT;
 #pragma unroll
@@ -354,7 +366,7 @@ __global__ __launch_bounds__(kThreads) void append_step_kernel(AppendParams p) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           float qv = 0.f;
-          if (s > 0.f) qv = fminf(127.f, fmaxf(-127.f, __builtin_rintf(x[i + k] / s)));
+          if (s > 0.f) qv = fminf(127.f, fmaxf(-127.f, __builtin_rintf(x[kv][i + k] / s)));
           packed |= (static_cast<uint32_t>(static_cast<int>(qv)) & 0xffu) << (8 * k);
         }
         *reinterpret_cast<uint32_t*>(srow + i) = packed;
@@ -381,7 +393,7 @@ __global__ __launch_bounds__(kThreads) void append_step_kernel(AppendParams p) {
         }
         reinterpret_cast<uint4*>(tile)[vi] = out;
       }
-      if (tid == 0) *sp = s;
+      if (tid == 0) sp[kv] = s;
       __syncthreads();
     }
     if (h == 0 && tid == 0) {

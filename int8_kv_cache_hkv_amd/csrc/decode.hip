@@ -38,7 +38,6 @@ namespace detail {
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kHotChunk = 32;         // hot-zone slots staged through LDS at a time
-constexpr int kMaxSplitsDev = kMaxSplits;
 
 template <int D, int G>
 struct Cfg {
@@ -61,10 +60,11 @@ struct DecodeSmem {
 
 template <int D, int G>
 struct HotSmem {
-  float q[G][D];
+  using C = Cfg<D, G>;
+  _Float16 qh[C::NQ][4][C::QROW];          // query rows (fp16), zero rows past G
   float acc[G][D];
-  float z[G][kHotChunk];                   // logits, then weights, of the current chunk
-  float m[G], l[G], alpha[G];
+  float z[4 * C::NQ][kHotChunk];           // softmax weights of the current chunk (rows stay 0 past cnt)
+  float m[4 * C::NQ], l[4 * C::NQ], alpha[4 * C::NQ];
   _Float16 kv[kHotChunk * (2 * D + 8)];     // staged [K|V] rows of the current chunk (padded)
 };
 
@@ -144,8 +144,9 @@ __device__ __forceinline__ void qk_codes(const uint4 (&kr)[D / 16], const Decode
                                          float4_t (&s)[Cfg<D, G>::NQ]) {
   using C = Cfg<D, G>;
   asm volatile("" ::: "memory");  // re-read the query operand from LDS for every unit
+  float4_t s2[C::NQ];  // second accumulator chain: halves the dependent MFMA chain
 #pragma unroll
-  for (int quad = 0; quad < C::NQ; ++quad) s[quad] = float4_t{0.f, 0.f, 0.f, 0.f};
+  for (int quad = 0; quad < C::NQ; ++quad) s[quad] = s2[quad] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ch = 0; ch < D / 16; ++ch) {
     asm volatile("" ::: "memory");  // bound how far the query-operand LDS reads are hoisted
@@ -154,19 +155,25 @@ __device__ __forceinline__ void qk_codes(const uint4 (&kr)[D / 16], const Decode
       const half4_t b = codes_to_half4(word_of(kr[ch], wd));
       const int k0 = ch * 16 + wd * 4;
 #pragma unroll
-      for (int quad = 0; quad < C::NQ; ++quad) s[quad] = mfma_qk(q_operand(sm, quad, lane, k0), b, s[quad]);
+      for (int quad = 0; quad < C::NQ; ++quad) {
+        if (wd & 1) s2[quad] = mfma_qk(q_operand(sm, quad, lane, k0), b, s2[quad]);
+        else s[quad] = mfma_qk(q_operand(sm, quad, lane, k0), b, s[quad]);
+      }
     }
   }
+#pragma unroll
+  for (int quad = 0; quad < C::NQ; ++quad) s[quad] += s2[quad];
 }
 
 // Dense cold block j.
 template <int D, int G>
 __device__ void cold_block_unit(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const CacheView& c, int b, int h, int j,
-                                int n_cold, float qscale, int w, int lane) {
+                                int phys_hint, int n_cold, float qscale, int w, int lane) {
   using C = Cfg<D, G>;
   constexpr int S = kBlockSize;
   if (j >= c.max_blocks) return;
-  const int phys = c.headers[static_cast<size_t>(b) * c.max_blocks + j].phys_block;
+  // phys_hint: the header already read for this block (-2: not read yet)
+  const int phys = phys_hint != -2 ? phys_hint : c.headers[static_cast<size_t>(b) * c.max_blocks + j].phys_block;
   if (phys < 0 || phys >= c.num_phys) return;
   const int nv = min(S, n_cold - j * S);
   const float sK = c.scales[(static_cast<size_t>(phys) * c.H + h) * 2 + 0];
@@ -175,12 +182,12 @@ __device__ void cold_block_unit(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const
   const uint4* tv = reinterpret_cast<const uint4*>(c.cold + tile_offset(phys, h, 1, c.H, S, D));
   uint4 kr[D / 16];
 #pragma unroll
-  for (int ch = 0; ch < D / 16; ++ch) kr[ch] = tk[ch * S + lane];
+  for (int ch = 0; ch < D / 16; ++ch) kr[ch] = load_stream(tk + ch * S + lane);
   uint4 vr[C::NDL][4];
 #pragma unroll
   for (int ps = 0; ps < C::NDL; ++ps)
 #pragma unroll
-    for (int tc = 0; tc < 4; ++tc) vr[ps][tc] = tv[tc * D + 64 * ps + lane];
+    for (int tc = 0; tc < 4; ++tc) vr[ps][tc] = load_stream(tv + tc * D + 64 * ps + lane);
   float4_t s[C::NQ];
   qk_codes<D, G>(kr, sm, lane, s);
   softmax_unit<D, G>(st, sm, s, lane < nv, sK * qscale, sV, w, lane);
@@ -270,6 +277,19 @@ __device__ __forceinline__ float* partial_ptr(const DecodeParams& p, int bh, int
   return p.partials + ((static_cast<size_t>(bh) * (p.nsplit + 1) + split) * p.G + g) * (D + 2);
 }
 
+// Query rows of one kv-head's group into LDS as fp16 (exact), 16 bytes per
+// thread in one round; rows past G are zero.
+template <int D, int G>
+__device__ __forceinline__ void copy_query(const _Float16* qg, _Float16 (*qh)[4][Cfg<D, G>::QROW], int tid) {
+  using C = Cfg<D, G>;
+  constexpr int VPR = D / 8;
+  for (int i = tid; i < 4 * C::NQ * VPR; i += kThreads) {
+    const int g = i / VPR, v = i % VPR;
+    const uint4 val = g < G ? reinterpret_cast<const uint4*>(qg + static_cast<size_t>(g) * D)[v] : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(&qh[g / 4][g % 4][v * 8]) = val;
+  }
+}
+
 // ---- cold split: stream its units, merge the 4 waves, write the partial
 template <int D, int G, bool SPARSE>
 __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, int h, int bh, int split) {
@@ -278,14 +298,14 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
   constexpr int NG = 4 * C::NQ;
   const CacheView& c = p.c;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const _Float16* qg = p.q + (static_cast<size_t>(b) * c.H * G + static_cast<size_t>(h) * G) * D;
-  for (int i = tid; i < NG * D; i += kThreads) {
-    const int g = i / D, d = i % D;
-    sm.qh[g / 4][g % 4][d] = g < G ? qg[g * D + d] : static_cast<_Float16>(0.f);
-  }
+  // issue the length and this wave's first header read together with the query copy
+  const int n_seq = c.seq_len[b];
+  const int u0 = split * p.units_per_split + w;
+  const int phys0 = (!SPARSE && u0 < c.max_blocks) ? c.headers[static_cast<size_t>(b) * c.max_blocks + u0].phys_block : -1;
+  copy_query<D, G>(p.q + (static_cast<size_t>(b) * c.H * G + static_cast<size_t>(h) * G) * D, sm.qh, tid);
   __syncthreads();
 
-  const SeqGeom sg = seq_geom(c.seq_len[b], c.T, S);
+  const SeqGeom sg = seq_geom(n_seq, c.T, S);
   const int units = sg.n_cold > 0 ? (SPARSE ? cdiv(p.k_sel, 64) : sg.n_blk) : 0;
   const int32_t* sel_bh = SPARSE ? p.sel + static_cast<size_t>(bh) * p.k_sel : nullptr;
 
@@ -307,7 +327,7 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
       if (SPARSE) {
         gather_unit<D, G>(st, sm, c, sel_bh, p.k_sel, b, h, u, sg.n_cold, p.qscale, w, lane);
       } else {
-        cold_block_unit<D, G>(st, sm, c, b, h, u, sg.n_cold, p.qscale, w, lane);
+        cold_block_unit<D, G>(st, sm, c, b, h, u, u == u0 ? phys0 : -2, sg.n_cold, p.qscale, w, lane);
       }
     }
   }
@@ -352,70 +372,91 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
 }
 
 // ---- hot split: the FP16 ring (Hybrid KV Cache page 2.1: the most recent
-// tokens in full precision), attended in fp32.  Chunks of kHotChunk slots are
-// staged through LDS with coalesced loads; thread (g, t) scores slot t for
-// query head g, thread (g, d) accumulates channel d.
+// tokens in full precision).  Chunks of kHotChunk slots are staged through LDS
+// with coalesced loads; wave 0 computes the logits with the same MFMA as the
+// cold blocks (lane = slot, fp16 K rows are already MFMA operands) and the
+// softmax weights; all four waves then accumulate thread (g, d) = sum_t p v.
 template <int D, int G>
 __device__ void hot_split(const DecodeParams& p, HotSmem<D, G>& hm, int b, int h, int bh) {
+  using C = Cfg<D, G>;
+  constexpr int NG = 4 * C::NQ;
   constexpr int ROW = 2 * D + 8;          // padded fp16 [K|V] row
   constexpr int VPR = 2 * D / 8;          // 16-byte vectors per row
   const CacheView& c = p.c;
-  const int tid = threadIdx.x;
-  const _Float16* qg = p.q + (static_cast<size_t>(b) * c.H * G + static_cast<size_t>(h) * G) * D;
-  for (int i = tid; i < G * D; i += kThreads) hm.q[i / D][i % D] = static_cast<float>(qg[i]);
-  for (int g = tid; g < G; g += kThreads) {
-    hm.m[g] = kNegInf;
-    hm.l[g] = 0.f;
-  }
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int n_seq = c.seq_len[b];
+  copy_query<D, G>(p.q + (static_cast<size_t>(b) * c.H * G + static_cast<size_t>(h) * G) * D, hm.qh, tid);
   for (int i = tid; i < G * D; i += kThreads) hm.acc[i / D][i % D] = 0.f;
-  const SeqGeom sg = seq_geom(c.seq_len[b], c.T, kBlockSize);
+  const SeqGeom sg = seq_geom(n_seq, c.T, kBlockSize);
   const _Float16* hot_bh = c.hot + static_cast<size_t>(bh) * c.T * 2 * D;
-  __syncthreads();
+  float m[NG], l[NG];  // wave 0's running softmax state (wave-uniform)
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    m[g] = kNegInf;
+    l[g] = 0.f;
+  }
   for (int base = 0; base < sg.n_hot; base += kHotChunk) {
     const int cnt = min(kHotChunk, sg.n_hot - base);
     const uint4* src = reinterpret_cast<const uint4*>(hot_bh + static_cast<size_t>(base) * 2 * D);
-    for (int i = tid; i < cnt * VPR; i += kThreads)
-      *reinterpret_cast<uint4*>(&hm.kv[(i / VPR) * ROW + (i % VPR) * 8]) = src[i];
-    __syncthreads();
-    // logits (base 2)
-    for (int i = tid; i < G * kHotChunk; i += kThreads) {
-      const int g = i / kHotChunk, t = i % kHotChunk;
-      float z = kNegInf;
-      if (t < cnt) {
-        float acc = 0.f;
-        const _Float16* kr = &hm.kv[t * ROW];
-#pragma unroll 8
-        for (int d = 0; d < D; ++d) acc = fmaf(hm.q[g][d], static_cast<float>(kr[d]), acc);
-        z = acc * p.qscale;
-      }
-      hm.z[g][t] = z;
+    constexpr int NV = (kHotChunk * VPR + kThreads - 1) / kThreads;
+    uint4 buf[NV];  // all of the chunk's loads in flight together
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int i = tid + k * kThreads;
+      buf[k] = i < cnt * VPR ? src[i] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int i = tid + k * kThreads;
+      if (i < kHotChunk * VPR) *reinterpret_cast<uint4*>(&hm.kv[(i / VPR) * ROW + (i % VPR) * 8]) = buf[k];
     }
     __syncthreads();
-    // online softmax per query head (one thread each: at most 8 heads x 32 slots)
-    for (int g = tid; g < G; g += kThreads) {
-      float mb = kNegInf;
-      for (int t = 0; t < cnt; ++t) mb = fmaxf(mb, hm.z[g][t]);
-      const float mn = fmaxf(hm.m[g], mb);
-      const float alpha = exp2_approx(hm.m[g] - mn);
-      float ls = 0.f;
-      for (int t = 0; t < kHotChunk; ++t) {
-        const float pt = t < cnt ? exp2_approx(hm.z[g][t] - mn) : 0.f;
-        hm.z[g][t] = pt;
-        ls += pt;
+    if (w == 0) {
+      const bool valid = lane < cnt;
+      const _Float16* kr = &hm.kv[(valid ? lane : 0) * ROW];
+      float4_t s[C::NQ];
+#pragma unroll
+      for (int quad = 0; quad < C::NQ; ++quad) s[quad] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+      for (int k0 = 0; k0 < D; k0 += 4) {
+        const half4_t bk = *reinterpret_cast<const half4_t*>(kr + k0);
+#pragma unroll
+        for (int quad = 0; quad < C::NQ; ++quad)
+          s[quad] = mfma_qk(*reinterpret_cast<const half4_t*>(&hm.qh[quad][lane & 3][k0]), bk, s[quad]);
       }
-      hm.l[g] = hm.l[g] * alpha + ls;
-      hm.m[g] = mn;
-      hm.alpha[g] = alpha;
+#pragma unroll
+      for (int quad = 0; quad < C::NQ; ++quad) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int g = 4 * quad + r;
+          const float z = valid ? s[quad][r] * p.qscale : kNegInf;
+          const float mn = fmaxf(m[g], wave_max_dpp(z));
+          const float alpha = exp2_approx(m[g] - mn);
+          const float pt = valid ? exp2_approx(z - mn) : 0.f;
+          l[g] = l[g] * alpha + wave_sum_dpp(pt);
+          m[g] = mn;
+          if (lane < kHotChunk) hm.z[g][lane] = pt;
+          if (lane == 0) hm.alpha[g] = alpha;
+        }
+      }
     }
     __syncthreads();
     for (int i = tid; i < G * D; i += kThreads) {
       const int g = i / D, d = i % D;
       float a = hm.acc[g][d] * hm.alpha[g];
-      for (int t = 0; t < cnt; ++t) a = fmaf(hm.z[g][t], static_cast<float>(hm.kv[t * ROW + D + d]), a);
+      for (int t = 0; t < cnt; ++t) a = fmaf(hm.z[g][t], static_cast<float>(hm.kv[t * ROW + D + d]), a);  // rows past cnt are not staged
       hm.acc[g][d] = a;
     }
     __syncthreads();
   }
+  if (w == 0 && lane == 0) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      hm.m[g] = m[g];
+      hm.l[g] = l[g];
+    }
+  }
+  __syncthreads();
   for (int i = tid; i < G * D; i += kThreads) {
     const int g = i / D, d = i % D;
     float* pg = partial_ptr<D>(p, bh, p.nsplit, g);
@@ -440,9 +481,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G > 4 
     HotSmem<D, G> hot;
   } sm;
   __shared__ int s_last;
-  __shared__ float sm_w[kMaxSplitsDev + 1][G];   // m_s, then e^(m_s - M)
-  __shared__ float sm_l[kMaxSplitsDev + 1][G];
-  __shared__ float sm_M[G], sm_L[G];
+  __shared__ float mw[kMaxSplits + 1][G];   // m_s, then e^(m_s - M)
+  __shared__ float ml[kMaxSplits + 1][G];
+  __shared__ float mM[G], mL[G];
   const CacheView& c = p.c;
   const int split = blockIdx.x % (p.nsplit + 1);
   const int bh = blockIdx.x / (p.nsplit + 1);
@@ -463,36 +504,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G > 4 
              static_cast<unsigned>(p.nsplit);
   __syncthreads();
   if (!s_last) return;
-  // weights e^(m_s - M) per (split, head) through LDS: one round of loads for all m_s and l_s
+  // merge: (1) every m_s, l_s into LDS in one round and the weights e^(m_s - M);
+  // (2) each thread's accumulator columns, 16 splits' loads in flight at a time
   const int NS = p.nsplit + 1;
   for (int i = tid; i < NS * G; i += kThreads) {
     const float* pg = partial_ptr<D>(p, bh, i / G, i % G);
-    sm_w[i / G][i % G] = load_coherent(pg);
-    sm_l[i / G][i % G] = load_coherent(pg + 1);
+    mw[i / G][i % G] = load_coherent(pg);
+    ml[i / G][i % G] = load_coherent(pg + 1);
   }
   __syncthreads();
   for (int g = tid; g < G; g += kThreads) {
     float M = kNegInf;
-    for (int s2 = 0; s2 < NS; ++s2) M = fmaxf(M, sm_w[s2][g]);
+    for (int s2 = 0; s2 < NS; ++s2) M = fmaxf(M, mw[s2][g]);
     float L = 0.f;
     for (int s2 = 0; s2 < NS; ++s2) {
-      const float f = sm_w[s2][g] == kNegInf ? 0.f : exp2_approx(sm_w[s2][g] - M);
-      sm_w[s2][g] = f;
-      L += f * sm_l[s2][g];
+      const float f = mw[s2][g] == kNegInf ? 0.f : exp2_approx(mw[s2][g] - M);
+      mw[s2][g] = f;
+      L = fmaf(f, ml[s2][g], L);
     }
-    sm_M[g] = M;
-    sm_L[g] = L;
+    mM[g] = M;
+    mL[g] = L;
   }
   __syncthreads();
   const int Hq = c.H * G;
   for (int i = tid; i < G * D; i += kThreads) {
     const int g = i / D, d = i % D;
     float A = 0.f;
-#pragma unroll 8
-    for (int s2 = 0; s2 < NS; ++s2) A = fmaf(sm_w[s2][g], load_coherent(partial_ptr<D>(p, bh, s2, g) + 2 + d), A);
+    for (int s0 = 0; s0 < NS; s0 += 16) {
+      float av[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) av[k] = s0 + k < NS ? load_coherent(partial_ptr<D>(p, bh, s0 + k, g) + 2 + d) : 0.f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        if (s0 + k < NS) A = fmaf(mw[s0 + k][g], av[k], A);
+    }
     const int hq = h * G + g;
-    p.out[(static_cast<size_t>(b) * Hq + hq) * D + d] = static_cast<_Float16>(A / sm_L[g]);
-    if (d == 0 && p.lse) p.lse[static_cast<size_t>(b) * Hq + hq] = (sm_M[g] + __builtin_log2f(sm_L[g])) * kLn2;
+    p.out[(static_cast<size_t>(b) * Hq + hq) * D + d] = static_cast<_Float16>(A / mL[g]);
+    if (d == 0 && p.lse) p.lse[static_cast<size_t>(b) * Hq + hq] = (mM[g] + __builtin_log2f(mL[g])) * kLn2;
   }
   if (tid == 0) __hip_atomic_store(&p.counters[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

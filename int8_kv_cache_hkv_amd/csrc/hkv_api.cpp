@@ -59,7 +59,9 @@ struct SplitPlan {
 };
 SplitPlan plan_splits(int64_t bh, int64_t units) {
   units = std::max<int64_t>(1, units);
-  int64_t target = std::max<int64_t>(1, (kTargetWorkgroups + bh - 1) / bh);
+  // all of a launch's workgroups (cold splits + one hot workgroup per (sequence, kv-head)) should be
+  // resident at once: a straggler that starts late delays the merge of its (sequence, kv-head)
+  int64_t target = std::max<int64_t>(1, kTargetWorkgroups / bh - 1);
   int64_t per = hkv::kWaves * ((units + hkv::kWaves * target - 1) / (hkv::kWaves * target));
   int64_t ns = (units + per - 1) / per;
   if (ns > kMaxSplits) {
@@ -73,7 +75,7 @@ SplitPlan plan_splits(int64_t bh, int64_t units) {
 // plan has at most `target` splits (units_per_split >= units / target) and at
 // most ceil(units / 4) splits (units_per_split >= 4), capped by kMaxSplits.
 int max_splits(int64_t bh, int64_t units_cap) {
-  const int64_t target = std::max<int64_t>(1, (kTargetWorkgroups + bh - 1) / bh);
+  const int64_t target = std::max<int64_t>(1, kTargetWorkgroups / bh - 1);
   int64_t ns = std::min<int64_t>(std::min<int64_t>(target, kMaxSplits), (std::max<int64_t>(1, units_cap) + 3) / 4);
   return static_cast<int>(std::max<int64_t>(1, ns));
 }

@@ -62,6 +62,17 @@ __device__ __forceinline__ float half_hi(uint32_t w) {
 
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// Streaming 16-byte load of cold-tile data that is read once per call: the
+// non-temporal hint keeps it from displacing reused lines in the caches
+// (measured on MI355X: the decode access pattern reads 6.8 TB/s with it, 6.1
+// without).
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Sequence geometry derived from the cached length.
 struct SeqGeom {
   int n, n_hot, n_cold, n_blk;
@@ -86,26 +97,28 @@ __device__ __forceinline__ float dpp_mov(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
-// Max over the 64 lanes, result in every lane: DPP inside rows of 16, then two lane swaps.
+__device__ __forceinline__ float readlane_f(float x, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+
+// Max over the 64 lanes, wave-uniform result: DPP inside rows of 16 lanes, then
+// the four row results are read as scalars (no LDS round trip).
 __device__ __forceinline__ float wave_max_dpp(float x) {
   x = fmaxf(x, dpp_mov<0xB1>(x));    // quad_perm [1,0,3,2]
   x = fmaxf(x, dpp_mov<0x4E>(x));    // quad_perm [2,3,0,1]
   x = fmaxf(x, dpp_mov<0x141>(x));   // row_half_mirror
   x = fmaxf(x, dpp_mov<0x140>(x));   // row_mirror
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  return fmaxf(fmaxf(readlane_f(x, 0), readlane_f(x, 16)), fmaxf(readlane_f(x, 32), readlane_f(x, 48)));
 }
 
-// Sum over the 64 lanes, result in every lane (same pattern as wave_max_dpp).
+// Sum over the 64 lanes, wave-uniform result (same pattern as wave_max_dpp;
+// fixed order, so deterministic).
 __device__ __forceinline__ float wave_sum_dpp(float x) {
   x += dpp_mov<0xB1>(x);
   x += dpp_mov<0x4E>(x);
   x += dpp_mov<0x141>(x);
   x += dpp_mov<0x140>(x);
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  return (readlane_f(x, 0) + readlane_f(x, 16)) + (readlane_f(x, 32) + readlane_f(x, 48));
 }
 
 // Four signed int8 codes (one word) to four exact fp16 values: bias the bytes to

@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       const uint4* tk = reinterpret_cast<const uint4*>(c.cold + tile_offset(phys, h, 0, H, S, D));
       uint4 kr[D / 16];
 #pragma unroll
-      for (int ch = 0; ch < D / 16; ++ch) kr[ch] = tk[ch * S + lane];
+      for (int ch = 0; ch < D / 16; ++ch) kr[ch] = load_stream(tk + ch * S + lane);
       asm volatile("" ::: "memory");
       // dot(q_g, code_t) for the lane's token t (MFMA, exact products) and |code_t|^2 (integer dot4)
       float4_t s[NQ];
