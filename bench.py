@@ -76,7 +76,7 @@ def run_leg(hkv, torch, w, n0, steps, warmup, R, label, do_append=True):
     """Rotating-instance append+decode loop; returns timing and byte counts."""
     import workloads as wl
     H, Hq, d = w.n_kv_heads, w.n_q_heads, w.head_dim
-    uses = -(-(steps + warmup + 2 * R) // R) + 1
+    uses = -(-(2 * steps + warmup) // R) + 1
     cap = n0 + uses + 1
     log(f"{label}: {R} instances of B={w.batch} n0={n0} (cap {cap}), generating inputs")
     insts = [Inst(hkv, w, cap) for _ in range(R)]
@@ -121,36 +121,27 @@ def run_leg(hkv, torch, w, n0, steps, warmup, R, label, do_append=True):
             raise hkv.HKVError(st, "hkv_decode_attn")
         return lens[r]
 
+    def step_bytes_of(n):
+        db = w.batch * decode_bytes(n, H, Hq, d)
+        return db, db + (w.batch * append_bytes(1, H, d) if do_append else 0)
+
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    # plain timed pass (no per-kernel events), used for the step rate
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    n_plain = min(steps, R * 2)
-    e0.record()
-    for i in range(warmup, warmup + n_plain):
-        step(i)
-    e1.record()
-    torch.cuda.synchronize()
-    plain_ms = e0.elapsed_time(e1) / n_plain
-    warmup += n_plain
-    for it in insts:
-        hkv.hkv_timing_enable(it.c.handle, True)
+    # timed pass: exactly `steps` steps, no per-kernel events, bracketed by device synchronisation
     step_bytes = 0
-    kern_bytes = 0
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    e0.record()
     for i in range(warmup, warmup + steps):
-        n = step(i)
-        db = w.batch * decode_bytes(n, H, Hq, d)
-        step_bytes += db + (w.batch * append_bytes(1, H, d) if do_append else 0)
-        kern_bytes += db
-    e1.record()
+        step_bytes += step_bytes_of(step(i))[1]
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ev_ms = e0.elapsed_time(e1)
+    # second pass of the same length with dispatch-recorded events, for per-kernel durations
+    for it in insts:
+        hkv.hkv_timing_enable(it.c.handle, True)
+    kern_bytes = 0
+    for i in range(warmup + steps, warmup + 2 * steps):
+        kern_bytes += step_bytes_of(step(i))[0]
+    torch.cuda.synchronize()
     kms = {}
     for kname in ("append", "append_ring", "decode"):
         tot, cnt = 0.0, 0
@@ -162,14 +153,13 @@ def run_leg(hkv, torch, w, n0, steps, warmup, R, label, do_append=True):
     for it in insts:
         hkv.hkv_timing_enable(it.c.handle, False)
         it.c.close()
-    ms = ev_ms / steps
+    ms = wall * 1e3 / steps
     res = {
         "ms_per_step": ms,
-        "ms_per_step_without_kernel_events": plain_ms,
-        "wall_ms_per_step": wall * 1e3 / steps,
         "gbs": step_bytes / steps / (ms * 1e-3) / 1e9,
         "bytes_per_step": step_bytes / steps,
         "kernel_ms": {k: v[0] for k, v in kms.items()},
+        "kernel_launches": {k: v[1] for k, v in kms.items()},
         "kernel_bytes": kern_bytes / steps,
     }
     return res
@@ -257,17 +247,21 @@ def sparse_leg(hkv, torch, steps):
         c.topk(q, k, out_idx=idx, workspace=ws)
         c.decode(q, out=out, sel_idx=idx, k_sel=k, workspace=ws)
     torch.cuda.synchronize()
-    for c in insts:
-        hkv.hkv_timing_enable(c.handle, True)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(steps):
+    def sparse_step(i):
         c = insts[i % 2]
         c.topk(q, k, out_idx=idx, workspace=ws)
         c.decode(q, out=out, sel_idx=idx, k_sel=k, workspace=ws)
-    e1.record()
+
+    t0 = time.perf_counter()
+    for i in range(steps):
+        sparse_step(i)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    for c in insts:
+        hkv.hkv_timing_enable(c.handle, True)
+    for i in range(steps):
+        sparse_step(i)
+    torch.cuda.synchronize()
     km = {}
     for kname in ("topk_score", "topk_select", "decode_sparse"):
         tot, cnt = 0.0, 0
@@ -285,6 +279,18 @@ def sparse_leg(hkv, torch, steps):
             "topk_score_gbs": score_b / (km["topk_score"] * 1e-3) / 1e9 if km["topk_score"] else None}
 
 
+def copy_calibration(torch, mib=256, reps=4):
+    """A plain elementwise copy of a known size (reads and writes `mib` MiB per launch).  Hardware
+    counters of this launch calibrate the FETCH_SIZE / WRITE_SIZE readings of the decode kernel."""
+    x = torch.ones(mib << 19, dtype=torch.float16, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    return {"kernel": "torch.neg (elementwise fp16)", "bytes_read": mib << 20, "bytes_written": mib << 20,
+            "launches": reps}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -294,6 +300,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the long-context and sparse legs")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a known-size copy kernel (for hardware-counter traffic calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (this build runs the decode "
@@ -334,7 +342,6 @@ def main():
         "head_queries_per_s": round(w.batch * Hq / (ms * 1e-3), 1),
         "bytes_per_step": int(main_leg["bytes_per_step"]),
         "kernel_ms": main_leg["kernel_ms"],
-        "ms_per_step_without_kernel_events": round(main_leg["ms_per_step_without_kernel_events"], 5),
         "roofline": {"kernel": "decode_kernel", "bound": "hbm",
                      "achieved": round(achieved, 1) if achieved else None, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None, "traffic": None,
@@ -344,6 +351,8 @@ def main():
     if not args.no_extra:
         res["long"] = long_leg(hkv, torch, 16)
         res["sparse"] = sparse_leg(hkv, torch, 20)
+    if args.copy_calibration:
+        res["copy_calibration"] = copy_calibration(torch)
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
