@@ -15,7 +15,7 @@ SOURCES = ["append.hip", "decode.hip", "topk.hip", "hkv_api.cpp"]
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
     "-fhip-fp32-correctly-rounded-divide-sqrt",   # IEEE fp32 division for the quantiser
-    "-fno-fast-math", "-ffp-contract=fast",
+    "-fno-fast-math", "-ffp-contract=fast", "-fno-strict-aliasing",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]

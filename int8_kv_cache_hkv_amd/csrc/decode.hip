@@ -8,26 +8,34 @@
 // Work decomposition.  For each (sequence, kv-head) the cold tokens are split
 // into "units": unit j is cold block j (dense mode) or the j-th run of 64
 // selected cold tokens (sparse mode, KV Cache reuse page 2: only the selected
-// tokens are loaded).  The FP16 hot zone is attended by decode_combine.
-// A workgroup of 4 waves owns one split = a run of units_per_split units
-// (round-robin over runs when a sequence has more units than the grid
-// covers); each wave streams every 4th unit of the run and keeps an fp32
-// online softmax (m, l, acc) for the G query heads of the kv-head; the 4
-// waves are merged in LDS into one partial per split, and decode_combine
-// attends the hot zone and merges it with the splits.
+// tokens are loaded).  A workgroup of 4 waves owns one split = a run of
+// units_per_split units (round-robin over runs when a sequence has more units
+// than the grid covers); each wave streams every 4th unit of the run and keeps
+// an fp32 online softmax (m, l, acc) for the G query heads of the kv-head; the
+// 4 waves are merged in LDS into one partial per split.  One more workgroup
+// per (sequence, kv-head) attends the FP16 hot zone, and the last workgroup to
+// finish merges all partials.
 //
-// Per unit of 64 tokens a wave does:
-//   QK  v_mfma_f32_4x4x4f16: B operand = 4 channels of the lane's own token
-//       (lane = token), A operand = 4 channels of query row lane%4 (from LDS),
-//       so lane t ends with the logits of token t for 4 query heads.  INT8
-//       codes become exact fp16 values with a byte permute + packed subtract.
-//   PV  v_mfma_f32_4x4x1f32 (fp32 inputs, no rounding of p): B operand = the
-//       value code of token t at the lane's channel, A operand = p of token t
-//       for query row lane%4 (from LDS, with the block's V scale folded in), so
-//       lane c accumulates out[g][c] for 4 query heads.
+// Per unit of 64 tokens a wave does (all on v_mfma_f32_4x4x4f16):
+//   QK  B operand = 4 channels of the lane's own token (lane = token), A
+//       operand = 4 channels of query row lane%4 (from LDS), so lane t ends
+//       with the logits of token t for 4 query heads.
+//   PV  B operand = the value codes of 4 consecutive tokens at the lane's
+//       channel (lane = channel), A operand = the weights of those tokens for
+//       query row lane%4 (from LDS), so lane c accumulates out[g][c].
+// INT8 codes enter the MFMAs as the exact fp16 values code + 1152 (a byte
+// permute under the fp16 exponent of 1024; no subtraction), and the offset is
+// removed from the finished sums: 1152 * sum(q) from each logit, 1152 *
+// sum(weights) from the value accumulator.  Weights are p = 2^(z - block max)
+// in [0, 1], split into hi + lo fp16 halves (about 22 significant bits) and
+// accumulated per block; the block's V scale and its online-softmax factor are
+// applied once per block in fp32.
 // Cold tiles are laid out so that one coalesced 16-byte load per lane lands
 // exactly these operands: lane t gets 16 channels of token t from a K tile,
-// lane c gets 16 tokens of channel c from a V tile.
+// lane c gets 16 tokens of channel c from a V tile.  Dense units are software
+// pipelined: the next unit's K tile is requested as soon as the QK products of
+// the current one are done, its V tile as soon as the PV products are, so a
+// wave always has one unit's loads in flight.
 #include <hip/hip_ext.h>
 
 #include "hkv_device.h"
@@ -38,42 +46,53 @@ namespace detail {
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kHotChunk = 32;         // hot-zone slots staged through LDS at a time
+constexpr int kMergeChunk = 16;       // partials whose loads are in flight together in the merge
 
 template <int D, int G>
 struct Cfg {
   static constexpr int NQ = (G + 3) / 4;   // groups of 4 query heads (MFMA rows)
+  static constexpr int NG = 4 * NQ;        // query rows including zero padding
   static constexpr int NDL = D / 64;       // channel passes of 64 lanes
   static constexpr int QROW = D + 8;       // padded fp16 query row in LDS (spreads the 4 rows over banks)
-  static constexpr int PROW = 64 + 4;      // padded fp32 weight row in LDS
+  static constexpr int PROW = 16 * 8 + 8;  // fp16 weight row: 16 groups of {hi[4], lo[4]}, padded
 };
 
 template <int D, int G>
 struct DecodeSmem {
   using C = Cfg<D, G>;
-  _Float16 qh[C::NQ][4][C::QROW];          // query rows (fp16, exact), zero rows past G
-  float pw[kWaves][C::NQ][4][C::PROW];     // per-wave weights p[g][token] of the current unit
-  float wm[kWaves][4 * C::NQ];
-  float wl[kWaves][4 * C::NQ];
-  float wacc[kWaves][4 * C::NQ][D];
-  long long voff[kWaves][64];              // sparse mode: byte offset of each selected token's V column
+  alignas(16) _Float16 qh[C::NQ][4][C::QROW];        // query rows (fp16, exact), zero rows past G
+  alignas(16) _Float16 pw[kWaves][C::NQ][4][C::PROW]; // per-wave weights of the current unit (hi/lo)
+  float wm[kWaves][C::NG];
+  float wl[kWaves][C::NG];
+  alignas(16) float wacc[kWaves][C::NG][D];
+  long long voff[kWaves][64];                         // sparse mode: byte offset of each selected token's V column
 };
 
 template <int D, int G>
 struct HotSmem {
   using C = Cfg<D, G>;
-  _Float16 qh[C::NQ][4][C::QROW];          // query rows (fp16), zero rows past G
+  alignas(16) _Float16 qh[C::NQ][4][C::QROW];          // query rows (fp16), zero rows past G
   float acc[G][D];
-  float z[4 * C::NQ][kHotChunk];           // softmax weights of the current chunk (rows stay 0 past cnt)
-  float m[4 * C::NQ], l[4 * C::NQ], alpha[4 * C::NQ];
-  _Float16 kv[kHotChunk * (2 * D + 8)];     // staged [K|V] rows of the current chunk (padded)
+  float z[C::NG][kHotChunk];               // softmax weights of the current chunk (rows stay 0 past cnt)
+  float m[C::NG], l[C::NG], alpha[C::NG];
+  alignas(16) _Float16 kv[kHotChunk * (2 * D + 8)];     // staged [K|V] rows of the current chunk (padded)
+};
+
+// Per-block PV sums: one MFMA chain per (query quad, channel pass); the hi and lo
+// weight halves accumulate into the same chain.
+template <int D, int G>
+struct BlockAcc {
+  float4_t v[Cfg<D, G>::NQ][Cfg<D, G>::NDL];
 };
 
 template <int D, int G>
 struct WaveState {
   using C = Cfg<D, G>;
-  float m[4 * C::NQ];                      // running max of base-2 logits (wave-uniform)
-  float l[4 * C::NQ];                      // lane-partial sum of p
-  float4_t acc[C::NQ][C::NDL][2];          // [quad][pass][token parity]: out[4quad + r][64 pass + lane]
+  float m[C::NG];                          // running max of base-2 logits (wave-uniform)
+  float l[C::NG];                          // lane-partial sum of softmax weights
+  float pb[C::NG];                         // lane-partial sum of weight * V scale (removes the code offset)
+  float qb[C::NG];                         // 1152 * sum_k q[g][k] (wave-uniform)
+  float4_t acc[C::NQ][C::NDL];             // out[4quad + r][64 pass + lane] (with the code offset)
 };
 
 template <int D, int G>
@@ -81,64 +100,99 @@ __device__ __forceinline__ half4_t q_operand(const DecodeSmem<D, G>& sm, int qua
   return *reinterpret_cast<const half4_t*>(&sm.qh[quad][lane & 3][k0]);
 }
 
-// Online-softmax update for one unit: s[quad][r] are this lane's raw logits for
-// query rows 4quad + r; `scale` turns them into base-2 logits; masked lanes give
-// p = 0.  Leaves p * vscale in pw (PV operand), rescales the accumulators.
-template <int D, int G>
+// Online-softmax update for one unit.  s[quad][r]: this lane's logit sums for
+// query row 4quad + r with biased key codes; `scale` (per lane) turns
+// s - qb into a base-2 logit; masked lanes give weight 0.  Per query row the
+// block max mb is taken first, the weight is w = 2^(z - mb) * vw (vw <= 1 per
+// lane, the lane's V scale relative to vcoef), stored to LDS as hi/lo fp16 for
+// the PV MFMAs, and the row's fold factors are returned: alpha rescales the
+// old accumulator, coef multiplies this block's PV sum.
+template <int D, int G, bool PER_LANE_V>
 __device__ __forceinline__ void softmax_unit(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const float4_t (&s)[Cfg<D, G>::NQ],
-                                             bool valid, float scale, float vscale, int w, int lane) {
+                                             bool valid, float scale, float vw, float vcoef,
+                                             float (&alpha)[Cfg<D, G>::NG], float (&coef)[Cfg<D, G>::NG], int w, int lane) {
   using C = Cfg<D, G>;
 #pragma unroll
   for (int quad = 0; quad < C::NQ; ++quad) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int g = 4 * quad + r;
-      const float z = valid ? s[quad][r] * scale : kNegInf;
+      const float z = valid ? (s[quad][r] - st.qb[g]) * scale : kNegInf;
       const float mb = wave_max_dpp(z);
+      const bool none = mb == kNegInf;  // every lane masked: state unchanged
       const float mn = fmaxf(st.m[g], mb);
-      const bool none = mn == kNegInf;  // all lanes masked (sparse padding): state unchanged
-      const float alpha = none ? 1.f : exp2_approx(st.m[g] - mn);
-      const float p = none ? 0.f : exp2_approx(z - mn);
-      st.l[g] = st.l[g] * alpha + p;
+      const float a = none ? 1.f : exp2_approx(st.m[g] - mn);
+      const float be = none ? 0.f : exp2_approx(mb - mn);
+      const float pp = none ? 0.f : exp2_approx(z - mb);
+      const float wv = PER_LANE_V ? pp * vw : pp;
+      const float cf = be * vcoef;
+      st.l[g] = fmaf(st.l[g], a, be * pp);
+      st.pb[g] = fmaf(st.pb[g], a, cf * wv);
       st.m[g] = mn;
-      sm.pw[w][quad][r][lane] = p * vscale;
-#pragma unroll
-      for (int ps = 0; ps < C::NDL; ++ps) {
-        st.acc[quad][ps][0][r] *= alpha;
-        st.acc[quad][ps][1][r] *= alpha;
-      }
+      alpha[g] = a;
+      coef[g] = cf;
+      const _Float16 hi = static_cast<_Float16>(wv);
+      const _Float16 lo = static_cast<_Float16>(wv - static_cast<float>(hi));
+      _Float16* row = &sm.pw[w][quad][r][(lane >> 2) * 8 + (lane & 3)];
+      row[0] = hi;
+      row[4] = lo;
     }
   }
   wave_lds_sync();
 }
 
-// PV over the 64 tokens of a unit whose value codes are lane-resident:
-// vr[pass][tc] holds tokens 16tc..16tc+15 of channel 64 pass + lane.
+// PV products of four tokens t0..t0+3 into the block accumulators: vw[ps] is
+// the word holding their value codes at channel 64 ps + lane.
 template <int D, int G>
-__device__ __forceinline__ void pv_codes(WaveState<D, G>& st, const DecodeSmem<D, G>& sm, const uint4 (&vr)[Cfg<D, G>::NDL][4],
-                                         int w, int lane) {
+__device__ __forceinline__ void pv_step(BlockAcc<D, G>& blk, const DecodeSmem<D, G>& sm,
+                                        const uint32_t (&vw)[Cfg<D, G>::NDL], int t0, int w, int lane) {
   using C = Cfg<D, G>;
+  half4_t ph[C::NQ], pl[C::NQ];
 #pragma unroll
-  for (int t0 = 0; t0 < 64; t0 += 4) {
-    asm volatile("" ::: "memory");  // convert codes 4 tokens at a time (bounds live VGPRs)
-    float4_t pa[C::NQ];
-#pragma unroll
-    for (int quad = 0; quad < C::NQ; ++quad) pa[quad] = *reinterpret_cast<const float4_t*>(&sm.pw[w][quad][lane & 3][t0]);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int t = t0 + k;
-#pragma unroll
-      for (int ps = 0; ps < C::NDL; ++ps) {
-        const float vf = sbyte(word_of(vr[ps][t / 16], (t % 16) / 4), t % 4);
-#pragma unroll
-        for (int quad = 0; quad < C::NQ; ++quad) st.acc[quad][ps][t & 1] = mfma_pv(pa[quad][k], vf, st.acc[quad][ps][t & 1]);
-      }
-    }
+  for (int quad = 0; quad < C::NQ; ++quad) {
+    const half4_t* pr = reinterpret_cast<const half4_t*>(&sm.pw[w][quad][lane & 3][(t0 >> 2) * 8]);
+    ph[quad] = pr[0];
+    pl[quad] = pr[1];
   }
+  half4_t bv[C::NDL];
+#pragma unroll
+  for (int ps = 0; ps < C::NDL; ++ps) bv[ps] = codes_to_biased_half4(vw[ps]);
+#pragma unroll
+  for (int quad = 0; quad < C::NQ; ++quad)
+#pragma unroll
+    for (int ps = 0; ps < C::NDL; ++ps) blk.v[quad][ps] = mfma_qk(ph[quad], bv[ps], blk.v[quad][ps]);
+#pragma unroll
+  for (int quad = 0; quad < C::NQ; ++quad)
+#pragma unroll
+    for (int ps = 0; ps < C::NDL; ++ps) blk.v[quad][ps] = mfma_qk(pl[quad], bv[ps], blk.v[quad][ps]);
 }
 
-// ---------------------------------------------------------------- units
-// Logits of the lane's K row (D/16 chunks of 16 int8 codes) for every query row.
+template <int D, int G>
+__device__ __forceinline__ void zero_blk(BlockAcc<D, G>& blk) {
+  using C = Cfg<D, G>;
+#pragma unroll
+  for (int quad = 0; quad < C::NQ; ++quad)
+#pragma unroll
+    for (int ps = 0; ps < C::NDL; ++ps) blk.v[quad][ps] = float4_t{0.f, 0.f, 0.f, 0.f};
+}
+
+// acc = acc * alpha + coef * block sum, per query row.
+template <int D, int G>
+__device__ __forceinline__ void fold_block(WaveState<D, G>& st, const BlockAcc<D, G>& blk,
+                                           const float (&alpha)[Cfg<D, G>::NG], const float (&coef)[Cfg<D, G>::NG]) {
+  using C = Cfg<D, G>;
+#pragma unroll
+  for (int quad = 0; quad < C::NQ; ++quad)
+#pragma unroll
+    for (int ps = 0; ps < C::NDL; ++ps)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int g = 4 * quad + r;
+        st.acc[quad][ps][r] = fmaf(coef[g], blk.v[quad][ps][r], st.acc[quad][ps][r] * alpha[g]);
+      }
+}
+
+// Logit sums of the lane's K row (D/16 chunks of 16 int8 codes, biased) for every query row.
 template <int D, int G>
 __device__ __forceinline__ void qk_codes(const uint4 (&kr)[D / 16], const DecodeSmem<D, G>& sm, int lane,
                                          float4_t (&s)[Cfg<D, G>::NQ]) {
@@ -152,7 +206,7 @@ __device__ __forceinline__ void qk_codes(const uint4 (&kr)[D / 16], const Decode
     asm volatile("" ::: "memory");  // bound how far the query-operand LDS reads are hoisted
 #pragma unroll
     for (int wd = 0; wd < 4; ++wd) {
-      const half4_t b = codes_to_half4(word_of(kr[ch], wd));
+      const half4_t b = codes_to_biased_half4(word_of(kr[ch], wd));
       const int k0 = ch * 16 + wd * 4;
 #pragma unroll
       for (int quad = 0; quad < C::NQ; ++quad) {
@@ -163,42 +217,158 @@ __device__ __forceinline__ void qk_codes(const uint4 (&kr)[D / 16], const Decode
   }
 #pragma unroll
   for (int quad = 0; quad < C::NQ; ++quad) s[quad] += s2[quad];
+  asm volatile("" ::: "memory");
 }
 
-// Dense cold block j.
+// ---------------------------------------------------------------- dense units
+// One dense unit's tiles in registers.
+template <int D>
+struct Tiles {
+  uint4 kr[D / 16];     // lane t: chunk ch = codes 16ch..16ch+15 of token t
+  uint4 vr[D / 64][4];  // lane c: [pass][tc] = tokens 16tc..16tc+15 of channel 64 pass + lane
+};
+// Physical block of cold block j of sequence b, or -1 when the header is out of range.
+__device__ __forceinline__ int dense_phys(const CacheView& c, int b, int j) {
+  if (j >= c.max_blocks) return -1;
+  const int ph = c.headers[static_cast<size_t>(b) * c.max_blocks + j].phys_block;
+  return (ph >= 0 && ph < c.num_phys) ? ph : -1;
+}
+
+// Buffer resource over one block's K and V tiles of one kv-head (2*S*D
+// contiguous bytes, K first): the tile loads take a uniform descriptor plus a
+// 32-bit lane offset, and the hardware range check returns 0 past the end.
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const CacheView& c, int phys, int h) {
+  const int8_t* base = c.cold + tile_offset(phys, h, 0, c.H, kBlockSize, D);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(base), 0, 2 * kBlockSize * D, kBufferDword3);
+}
+
+// Request the K tile (lane t: 16 codes of token t per chunk).
+template <int D>
+__device__ __forceinline__ void issue_k(Tiles<D>& t, __amdgpu_buffer_rsrc_t r, int lane) {
+  constexpr int S = kBlockSize;
+  const uint32_t lo = static_cast<uint32_t>(lane) * 16u;
+#pragma unroll
+  for (int ch = 0; ch < D / 16; ++ch) t.kr[ch] = load_stream_buf(r, lo + ch * S * 16);
+}
+
+// Request the two scales (K, V) and the V tile (lane c: 16 tokens of channel c
+// per load).  The scales travel with the V tile: they are requested after the
+// previous unit's softmax has used the register pair.
+template <int D>
+__device__ __forceinline__ void issue_v(Tiles<D>& t, float2& sc, __amdgpu_buffer_rsrc_t r, const CacheView& c,
+                                        int phys, int h, int lane) {
+  constexpr int S = kBlockSize;
+  sc = *reinterpret_cast<const float2*>(c.scales + (static_cast<size_t>(phys) * c.H + h) * 2);
+  const uint32_t lo = static_cast<uint32_t>(lane) * 16u;
+#pragma unroll
+  for (int ps = 0; ps < D / 64; ++ps)
+#pragma unroll
+    for (int tc = 0; tc < 4; ++tc) t.vr[ps][tc] = load_stream_buf(r, lo + S * D + (tc * D + 64 * ps) * 16);
+}
+
+// PV over a dense unit whose value codes are lane-resident: vr[pass][tc] holds
+// tokens 16tc..16tc+15 of channel 64 pass + lane.
 template <int D, int G>
-__device__ void cold_block_unit(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const CacheView& c, int b, int h, int j,
-                                int phys_hint, int n_cold, float qscale, int w, int lane) {
+__device__ __forceinline__ void pv_dense(BlockAcc<D, G>& blk, const DecodeSmem<D, G>& sm,
+                                         const uint4 (&vr)[Cfg<D, G>::NDL][4], int w, int lane) {
+  using C = Cfg<D, G>;
+  zero_blk<D, G>(blk);
+#pragma unroll
+  for (int t0 = 0; t0 < 64; t0 += 4) {
+    asm volatile("" ::: "memory");  // read the weights 4 tokens at a time (bounds live VGPRs)
+    uint32_t vw[C::NDL];
+#pragma unroll
+    for (int ps = 0; ps < C::NDL; ++ps) vw[ps] = word_of(vr[ps][t0 / 16], (t0 % 16) / 4);
+    pv_step<D, G>(blk, sm, vw, t0, w, lane);
+  }
+  asm volatile("" ::: "memory");
+}
+
+// A wave's walk over its dense units: runs of CU = units_per_split units start
+// at split * CU and repeat every nsplit * CU; inside a run the wave takes every
+// 4th unit, CU / 4 of them.  Unit k of the walk (k = 0, 1, ...):
+__device__ __forceinline__ int walk_unit(int k, int split, int nsplit, int CU, int w) {
+  const int KR = CU / kWaves;
+  const int run = k / KR;
+  return (split + run * nsplit) * CU + w + kWaves * (k - run * KR);
+}
+
+// Physical blocks of walk units kb .. kb + 63, one per lane (-1 past the header
+// table or for an out-of-range id): one coalesced load serves 64 units, and
+// the walk reads them with readlane, so no header load waits inside the loop.
+__device__ __forceinline__ int header_batch(const CacheView& c, int b, int kb, int split, int nsplit, int CU, int w,
+                                            int lane) {
+  return dense_phys(c, b, walk_unit(kb + lane, split, nsplit, CU, w));
+}
+
+// The walk itself.  K and V of the unit after the current one are requested
+// while the current one is being computed.  t/phys_u/sc hold the first unit
+// (already requested by the caller), hb the header batch of walk units 0..63.
+template <int D, int G>
+__device__ void dense_units(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const DecodeParams& p, int b, int h, int split,
+                            int units, int n_cold, int w, int lane, Tiles<D>& t, int phys_u, float2 sc, int hb) {
   using C = Cfg<D, G>;
   constexpr int S = kBlockSize;
-  if (j >= c.max_blocks) return;
-  // phys_hint: the header already read for this block (-2: not read yet)
-  const int phys = phys_hint != -2 ? phys_hint : c.headers[static_cast<size_t>(b) * c.max_blocks + j].phys_block;
-  if (phys < 0 || phys >= c.num_phys) return;
-  const int nv = min(S, n_cold - j * S);
-  const float sK = c.scales[(static_cast<size_t>(phys) * c.H + h) * 2 + 0];
-  const float sV = c.scales[(static_cast<size_t>(phys) * c.H + h) * 2 + 1];
-  const uint4* tk = reinterpret_cast<const uint4*>(c.cold + tile_offset(phys, h, 0, c.H, S, D));
-  const uint4* tv = reinterpret_cast<const uint4*>(c.cold + tile_offset(phys, h, 1, c.H, S, D));
-  uint4 kr[D / 16];
-#pragma unroll
-  for (int ch = 0; ch < D / 16; ++ch) kr[ch] = load_stream(tk + ch * S + lane);
-  uint4 vr[C::NDL][4];
-#pragma unroll
-  for (int ps = 0; ps < C::NDL; ++ps)
-#pragma unroll
-    for (int tc = 0; tc < 4; ++tc) vr[ps][tc] = load_stream(tv + tc * D + 64 * ps + lane);
-  float4_t s[C::NQ];
-  qk_codes<D, G>(kr, sm, lane, s);
-  softmax_unit<D, G>(st, sm, s, lane < nv, sK * qscale, sV, w, lane);
-  pv_codes<D, G>(st, sm, vr, w, lane);
-  wave_lds_sync();
+  const CacheView& c = p.c;
+  const int CU = p.units_per_split;
+  const int stride = p.nsplit * CU;
+  int run0 = split * CU;
+  int run_end = min(units, run0 + CU);
+  int u = run0 + w < units ? run0 + w : -1;
+  // next unit of this wave after x (x is the most recent unit handed out)
+  auto advance = [&](int x) -> int {
+    int nx = x + kWaves;
+    if (nx < run_end) return nx;
+    run0 += stride;
+    run_end = min(units, run0 + CU);
+    nx = run0 + w;
+    return nx < units ? nx : -1;
+  };
+  int kb = 0;  // walk index of lane 0 of the header batch
+  auto phys_of = [&](int k) -> int {
+    if (k - kb >= 64) {
+      kb = k;
+      hb = header_batch(c, b, kb, split, p.nsplit, CU, w, lane);
+    }
+    return __builtin_amdgcn_readlane(hb, k - kb);
+  };
+  int k = 0;
+  int un = u >= 0 ? advance(u) : -1;
+  int phys_n = un >= 0 ? phys_of(k + 1) : -1;
+  while (u >= 0) {
+    const int nv = phys_u >= 0 ? min(S, n_cold - u * S) : 0;
+    float4_t s[C::NQ];
+    qk_codes<D, G>(t.kr, sm, lane, s);
+    __amdgpu_buffer_rsrc_t rn;
+    if (phys_n >= 0) {
+      rn = tile_rsrc<D>(c, phys_n, h);
+      issue_k<D>(t, rn, lane);
+    }
+    float alpha[C::NG], coef[C::NG];
+    softmax_unit<D, G, false>(st, sm, s, lane < nv, sc.x * p.qscale, 1.f, sc.y, alpha, coef, w, lane);
+    BlockAcc<D, G> blk;
+    pv_dense<D, G>(blk, sm, t.vr, w, lane);
+    if (phys_n >= 0) issue_v<D>(t, sc, rn, c, phys_n, h, lane);
+    fold_block<D, G>(st, blk, alpha, coef);
+    wave_lds_sync();  // this unit's weight reads are done before the next unit's writes
+    u = un;
+    phys_u = phys_n;
+    ++k;
+    if (u >= 0) {
+      un = advance(u);
+      phys_n = un >= 0 ? phys_of(k + 1) : -1;
+    }
+  }
 }
 
-// Sparse unit: up to 64 selected cold tokens, one gathered row per lane.  For
-// PV, lane c needs the value code of every selected token at channel c: the
-// tokens' V-tile offsets go through LDS and the byte loads of 16 tokens are
-// issued together, so the unit pays four memory latencies, not 64.
+// ---------------------------------------------------------------- sparse units
+// Up to 64 selected cold tokens, one gathered row per lane.  For PV, lane c
+// needs the value code of every selected token at channel c: the tokens'
+// V-tile offsets go through LDS and the byte loads of 16 tokens are issued
+// together, so the unit pays four memory latencies, not 64.  Each token has
+// its own block scales: the logit scale is per lane, and the value weight is
+// taken relative to the largest V scale of the unit (vcoef).
 template <int D, int G>
 __device__ void gather_unit(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const CacheView& c, const int32_t* sel_bh,
                             int k_sel, int b, int h, int chunk, int n_cold, float qscale, int w, int lane) {
@@ -214,11 +384,10 @@ __device__ void gather_unit(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const Cac
   }
   const bool valid = phys >= 0 && phys < c.num_phys;
   const int t = valid ? idx % S : 0;
-  float sK = 0.f, sV = 0.f;
+  float2 sc = make_float2(0.f, 0.f);
   uint4 kr[D / 16];
   if (valid) {
-    sK = c.scales[(static_cast<size_t>(phys) * c.H + h) * 2 + 0];
-    sV = c.scales[(static_cast<size_t>(phys) * c.H + h) * 2 + 1];
+    sc = *reinterpret_cast<const float2*>(c.scales + (static_cast<size_t>(phys) * c.H + h) * 2);
     const uint4* tk = reinterpret_cast<const uint4*>(c.cold + tile_offset(phys, h, 0, c.H, S, D));
 #pragma unroll
     for (int ch = 0; ch < D / 16; ++ch) kr[ch] = tk[ch * S + t];
@@ -231,47 +400,54 @@ __device__ void gather_unit(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const Cac
                            : -1ll;
   float4_t s[C::NQ];
   qk_codes<D, G>(kr, sm, lane, s);
-  softmax_unit<D, G>(st, sm, s, valid, sK * qscale, sV, w, lane);
+  const float vmax = wave_max_dpp(sc.y);
+  const float vw = vmax > 0.f ? sc.y * __builtin_amdgcn_rcpf(vmax) : 0.f;
+  float alpha[C::NG], coef[C::NG];
+  softmax_unit<D, G, true>(st, sm, s, valid, sc.x * qscale, vw, vmax, alpha, coef, w, lane);
+  BlockAcc<D, G> blk;
+  zero_blk<D, G>(blk);
   const int cnt = min(64, k_sel - chunk * 64);
   for (int tb = 0; tb < cnt; tb += TB) {
-    float vf[TB][C::NDL];
+    uint32_t vb[TB][C::NDL];
 #pragma unroll
     for (int k = 0; k < TB; ++k) {
       const long long off = sm.voff[w][tb + k];  // uniform across the wave
 #pragma unroll
       for (int ps = 0; ps < C::NDL; ++ps)
-        vf[k][ps] = off >= 0 ? static_cast<float>(c.cold[off + (64 * ps + lane) * 16]) : 0.f;
+        vb[k][ps] = off >= 0 ? static_cast<uint32_t>(reinterpret_cast<const uint8_t*>(c.cold)[off + (64 * ps + lane) * 16]) : 0u;
     }
 #pragma unroll
     for (int t0 = 0; t0 < TB; t0 += 4) {
-      float4_t pa[C::NQ];
+      uint32_t vw4[C::NDL];
 #pragma unroll
-      for (int quad = 0; quad < C::NQ; ++quad)
-        pa[quad] = *reinterpret_cast<const float4_t*>(&sm.pw[w][quad][lane & 3][tb + t0]);
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-#pragma unroll
-        for (int ps = 0; ps < C::NDL; ++ps)
-#pragma unroll
-          for (int quad = 0; quad < C::NQ; ++quad)
-            st.acc[quad][ps][k & 1] = mfma_pv(pa[quad][k], vf[t0 + k][ps], st.acc[quad][ps][k & 1]);
+      for (int ps = 0; ps < C::NDL; ++ps)
+        vw4[ps] = vb[t0][ps] | (vb[t0 + 1][ps] << 8) | (vb[t0 + 2][ps] << 16) | (vb[t0 + 3][ps] << 24);
+      pv_step<D, G>(blk, sm, vw4, tb + t0, w, lane);
     }
   }
+  fold_block<D, G>(st, blk, alpha, coef);
   wave_lds_sync();
 }
 
 // Partials are exchanged between workgroups that may sit on different XCDs
 // (each with its own L2).  They are written and read with agent-scope relaxed
-// atomic accesses (device-coherent sc1 loads/stores), so publishing them needs
-// only a wait for the stores to complete, not an L2-wide writeback.
-__device__ __forceinline__ void store_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// atomic accesses (device-coherent sc1 loads/stores, 8 bytes each), so
+// publishing them needs only a wait for the stores to complete, not an
+// L2-wide writeback.
+__device__ __forceinline__ void store_coherent2(float* p, float a, float b) {
+  const uint64_t v = static_cast<uint64_t>(__builtin_bit_cast(uint32_t, a)) |
+                     (static_cast<uint64_t>(__builtin_bit_cast(uint32_t, b)) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float load_coherent(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ float2 load_coherent2(const float* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__builtin_bit_cast(float, static_cast<uint32_t>(v)),
+                     __builtin_bit_cast(float, static_cast<uint32_t>(v >> 32)));
 }
 
-// Partial record of one split: m (base-2 log units), l, acc[D] for each of the G query heads.
+// Partial record of one split: m (base-2 log units), l, acc[D] for each of the
+// G query heads; records are 8-byte aligned (D + 2 is even).
 template <int D>
 __device__ __forceinline__ float* partial_ptr(const DecodeParams& p, int bh, int split, int g) {
   return p.partials + ((static_cast<size_t>(bh) * (p.nsplit + 1) + split) * p.G + g) * (D + 2);
@@ -295,13 +471,25 @@ template <int D, int G, bool SPARSE>
 __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, int h, int bh, int split) {
   using C = Cfg<D, G>;
   constexpr int S = kBlockSize;
-  constexpr int NG = 4 * C::NQ;
+  constexpr int NG = C::NG;
   const CacheView& c = p.c;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  // issue the length and this wave's first header read together with the query copy
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // the length, this wave's first header and (dense) its first tiles are requested together
+  // with the query copy; the tiles are used only if the unit exists
   const int n_seq = c.seq_len[b];
-  const int u0 = split * p.units_per_split + w;
-  const int phys0 = (!SPARSE && u0 < c.max_blocks) ? c.headers[static_cast<size_t>(b) * c.max_blocks + u0].phys_block : -1;
+  Tiles<D> t0;
+  float2 sc0 = make_float2(0.f, 0.f);
+  int phys0 = -1, hb = -1;
+  if (!SPARSE) {
+    hb = header_batch(c, b, 0, split, p.nsplit, p.units_per_split, w, lane);
+    phys0 = __builtin_amdgcn_readlane(hb, 0);
+    if (phys0 >= 0) {
+      const __amdgpu_buffer_rsrc_t r0 = tile_rsrc<D>(c, phys0, h);
+      issue_k<D>(t0, r0, lane);
+      issue_v<D>(t0, sc0, r0, c, phys0, h, lane);
+    }
+  }
   copy_query<D, G>(p.q + (static_cast<size_t>(b) * c.H * G + static_cast<size_t>(h) * G) * D, sm.qh, tid);
   __syncthreads();
 
@@ -314,27 +502,33 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
   for (int g = 0; g < NG; ++g) {
     st.m[g] = kNegInf;
     st.l[g] = 0.f;
+    st.pb[g] = 0.f;
+    float qs = 0.f;
+#pragma unroll
+    for (int k = lane; k < D; k += 64) qs += static_cast<float>(sm.qh[g / 4][g % 4][k]);
+    st.qb[g] = kCodeBias * wave_sum_dpp(qs);
   }
 #pragma unroll
   for (int quad = 0; quad < C::NQ; ++quad)
 #pragma unroll
-    for (int ps = 0; ps < C::NDL; ++ps) st.acc[quad][ps][0] = st.acc[quad][ps][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int ps = 0; ps < C::NDL; ++ps) st.acc[quad][ps] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int CU = p.units_per_split;
-  for (int run = split; run * CU < units; run += p.nsplit) {
-    const int u_end = min(units, (run + 1) * CU);
-    for (int u = run * CU + w; u < u_end; u += kWaves) {
-      if (SPARSE) {
+  if (SPARSE) {
+    const int CU = p.units_per_split;
+    for (int run = split; run * CU < units; run += p.nsplit) {
+      const int u_end = min(units, (run + 1) * CU);
+      for (int u = run * CU + w; u < u_end; u += kWaves)
         gather_unit<D, G>(st, sm, c, sel_bh, p.k_sel, b, h, u, sg.n_cold, p.qscale, w, lane);
-      } else {
-        cold_block_unit<D, G>(st, sm, c, b, h, u, u == u0 ? phys0 : -2, sg.n_cold, p.qscale, w, lane);
-      }
     }
+  } else {
+    dense_units<D, G>(st, sm, p, b, h, split, units, sg.n_cold, w, lane, t0, phys0, sc0, hb);
   }
-  // merge the 4 waves: lane holds out[4quad + r][64 pass + lane]
+  // merge the 4 waves: lane holds out[4quad + r][64 pass + lane] + 1152 * pb
+  float bias[NG];
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
-    const float lsum = wave_sum(st.l[g]);
+    const float lsum = wave_sum_dpp(st.l[g]);
+    bias[g] = kCodeBias * wave_sum_dpp(st.pb[g]);
     if (lane == 0) {
       sm.wm[w][g] = st.m[g];
       sm.wl[w][g] = lsum;
@@ -345,29 +539,28 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
 #pragma unroll
     for (int ps = 0; ps < C::NDL; ++ps)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm.wacc[w][4 * quad + r][64 * ps + lane] = st.acc[quad][ps][0][r] + st.acc[quad][ps][1][r];
+      for (int r = 0; r < 4; ++r) sm.wacc[w][4 * quad + r][64 * ps + lane] = st.acc[quad][ps][r] - bias[4 * quad + r];
   __syncthreads();
-  for (int idx = tid; idx < G * D; idx += kThreads) {
-    const int g = idx / D, d = idx % D;
+  for (int idx = tid; idx < G * (D / 2); idx += kThreads) {
+    const int g = idx / (D / 2), d = 2 * (idx % (D / 2));
     float M = kNegInf;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm.wm[ww][g]);
-    float L = 0.f, A = 0.f;
+    float L = 0.f, A0 = 0.f, A1 = 0.f;
     if (M != kNegInf) {
 #pragma unroll
       for (int ww = 0; ww < kWaves; ++ww) {
         if (sm.wm[ww][g] == kNegInf) continue;
         const float f = exp2_approx(sm.wm[ww][g] - M);
-        L += f * sm.wl[ww][g];
-        A += f * sm.wacc[ww][g][d];
+        const float2 a = *reinterpret_cast<const float2*>(&sm.wacc[ww][g][d]);
+        L = fmaf(f, sm.wl[ww][g], L);
+        A0 = fmaf(f, a.x, A0);
+        A1 = fmaf(f, a.y, A1);
       }
     }
     float* pg = partial_ptr<D>(p, bh, split, g);
-    store_coherent(pg + 2 + d, A);
-    if (d == 0) {
-      store_coherent(pg, M);
-      store_coherent(pg + 1, L);
-    }
+    store_coherent2(pg + 2 + d, A0, A1);
+    if (d == 0) store_coherent2(pg, M, L);
   }
 }
 
@@ -457,14 +650,11 @@ __device__ void hot_split(const DecodeParams& p, HotSmem<D, G>& hm, int b, int h
     }
   }
   __syncthreads();
-  for (int i = tid; i < G * D; i += kThreads) {
-    const int g = i / D, d = i % D;
+  for (int i = tid; i < G * (D / 2); i += kThreads) {
+    const int g = i / (D / 2), d = 2 * (i % (D / 2));
     float* pg = partial_ptr<D>(p, bh, p.nsplit, g);
-    store_coherent(pg + 2 + d, hm.acc[g][d]);
-    if (d == 0) {
-      store_coherent(pg, hm.m[g]);
-      store_coherent(pg + 1, hm.l[g]);
-    }
+    store_coherent2(pg + 2 + d, hm.acc[g][d], hm.acc[g][d + 1]);
+    if (d == 0) store_coherent2(pg, hm.m[g], hm.l[g]);
   }
 }
 
@@ -473,17 +663,16 @@ __device__ void hot_split(const DecodeParams& p, HotSmem<D, G>& hm, int b, int h
 // of them to arrive merges all nsplit + 1 partials with the log-sum-exp rule
 // (M = max m_s, L = sum e^(m_s - M) l_s, out = sum e^(m_s - M) acc_s / L) and
 // writes the fp16 output.  Arrival is counted with a device-scope atomic in
-// the workspace, which the merging workgroup resets to zero.
+// the workspace, which the merging workgroup resets to zero.  The merge runs
+// online over groups of kMergeChunk partials whose loads are all in flight
+// together; thread i owns two adjacent output columns of one query head.
 template <int D, int G, bool SPARSE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G > 4 ? 2 : 3))) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G > 4 ? 2 : 4))) void decode_kernel(DecodeParams p) {
   __shared__ union Smem {
     DecodeSmem<D, G> cold;
     HotSmem<D, G> hot;
   } sm;
   __shared__ int s_last;
-  __shared__ float mw[kMaxSplits + 1][G];   // m_s, then e^(m_s - M)
-  __shared__ float ml[kMaxSplits + 1][G];
-  __shared__ float mM[G], mL[G];
   const CacheView& c = p.c;
   const int split = blockIdx.x % (p.nsplit + 1);
   const int bh = blockIdx.x / (p.nsplit + 1);
@@ -504,43 +693,49 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G > 4 
              static_cast<unsigned>(p.nsplit);
   __syncthreads();
   if (!s_last) return;
-  // merge: (1) every m_s, l_s into LDS in one round and the weights e^(m_s - M);
-  // (2) each thread's accumulator columns, 16 splits' loads in flight at a time
   const int NS = p.nsplit + 1;
-  for (int i = tid; i < NS * G; i += kThreads) {
-    const float* pg = partial_ptr<D>(p, bh, i / G, i % G);
-    mw[i / G][i % G] = load_coherent(pg);
-    ml[i / G][i % G] = load_coherent(pg + 1);
-  }
-  __syncthreads();
-  for (int g = tid; g < G; g += kThreads) {
-    float M = kNegInf;
-    for (int s2 = 0; s2 < NS; ++s2) M = fmaxf(M, mw[s2][g]);
-    float L = 0.f;
-    for (int s2 = 0; s2 < NS; ++s2) {
-      const float f = mw[s2][g] == kNegInf ? 0.f : exp2_approx(mw[s2][g] - M);
-      mw[s2][g] = f;
-      L = fmaf(f, ml[s2][g], L);
-    }
-    mM[g] = M;
-    mL[g] = L;
-  }
-  __syncthreads();
   const int Hq = c.H * G;
-  for (int i = tid; i < G * D; i += kThreads) {
-    const int g = i / D, d = i % D;
-    float A = 0.f;
-    for (int s0 = 0; s0 < NS; s0 += 16) {
-      float av[16];
+  constexpr int REC = G * (D + 2);  // floats per split record of one (sequence, kv-head)
+  const float* base_bh = p.partials + static_cast<size_t>(bh) * NS * REC;
+  for (int idx = tid; idx < G * (D / 2); idx += kThreads) {
+    const int g = idx / (D / 2), d = 2 * (idx % (D / 2));
+    const int off_ml = g * (D + 2), off_a = off_ml + 2 + d;  // per lane; the split offset is uniform
+    float M = kNegInf, L = 0.f, A0 = 0.f, A1 = 0.f;
+    for (int s0 = 0; s0 < NS; s0 += kMergeChunk) {
+      float2 ml[kMergeChunk], av[kMergeChunk];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) av[k] = s0 + k < NS ? load_coherent(partial_ptr<D>(p, bh, s0 + k, g) + 2 + d) : 0.f;
+      for (int k = 0; k < kMergeChunk; ++k) {
+        if (s0 + k < NS) {
+          const float* rec = base_bh + (s0 + k) * REC;
+          ml[k] = load_coherent2(rec + off_ml);
+          av[k] = load_coherent2(rec + off_a);
+        } else {
+          ml[k] = make_float2(kNegInf, 0.f);
+          av[k] = make_float2(0.f, 0.f);
+        }
+      }
+      float cm = kNegInf;
 #pragma unroll
-      for (int k = 0; k < 16; ++k)
-        if (s0 + k < NS) A = fmaf(mw[s0 + k][g], av[k], A);
+      for (int k = 0; k < kMergeChunk; ++k) cm = fmaxf(cm, ml[k].x);
+      const float Mn = fmaxf(M, cm);
+      if (Mn == kNegInf) continue;
+      const float sc = exp2_approx(M - Mn);  // 0 while M is still -inf
+      L *= sc;
+      A0 *= sc;
+      A1 *= sc;
+#pragma unroll
+      for (int k = 0; k < kMergeChunk; ++k) {
+        const float f = ml[k].x == kNegInf ? 0.f : exp2_approx(ml[k].x - Mn);
+        L = fmaf(f, ml[k].y, L);
+        A0 = fmaf(f, av[k].x, A0);
+        A1 = fmaf(f, av[k].y, A1);
+      }
+      M = Mn;
     }
     const int hq = h * G + g;
-    p.out[(static_cast<size_t>(b) * Hq + hq) * D + d] = static_cast<_Float16>(A / mL[g]);
-    if (d == 0 && p.lse) p.lse[static_cast<size_t>(b) * Hq + hq] = (mM[g] + __builtin_log2f(mL[g])) * kLn2;
+    const half2_t o = {static_cast<_Float16>(A0 / L), static_cast<_Float16>(A1 / L)};
+    *reinterpret_cast<half2_t*>(&p.out[(static_cast<size_t>(b) * Hq + hq) * D + d]) = o;
+    if (d == 0 && p.lse) p.lse[static_cast<size_t>(b) * Hq + hq] = (M + __builtin_log2f(L)) * kLn2;
   }
   if (tid == 0) __hip_atomic_store(&p.counters[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

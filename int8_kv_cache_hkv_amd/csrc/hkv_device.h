@@ -73,6 +73,17 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Fourth descriptor word of a raw buffer resource on gfx9-family GPUs (32-bit
+// data format, no swizzle).
+constexpr int kBufferDword3 = 0x00020000;
+
+// Streaming 16-byte buffer load (non-temporal, like load_stream) at byte
+// offset `off` of the resource.
+__device__ __forceinline__ uint4 load_stream_buf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 2 /* nt */);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Sequence geometry derived from the cached length.
 struct SeqGeom {
   int n, n_hot, n_cold, n_blk;
@@ -133,6 +144,19 @@ __device__ __forceinline__ half4_t codes_to_half4(uint32_t w) {
   const half2_t b = __builtin_bit_cast(half2_t, hi) - off;
   return half4_t{a.x, a.y, b.x, b.y};
 }
+
+// Four signed int8 codes (one word) to the four exact fp16 values code + 1152:
+// the same byte placement as codes_to_half4 without the final subtraction.
+// Callers remove the 1152 offset from the finished dot products.
+__device__ __forceinline__ half4_t codes_to_biased_half4(uint32_t w) {
+  const uint32_t u = w ^ 0x80808080u;
+  const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
+  const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+  const half2_t a = __builtin_bit_cast(half2_t, lo);
+  const half2_t b = __builtin_bit_cast(half2_t, hi);
+  return half4_t{a.x, a.y, b.x, b.y};
+}
+constexpr float kCodeBias = 1152.0f;
 
 __device__ __forceinline__ float4_t mfma_qk(half4_t a, half4_t b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c, 0, 0, 0);
