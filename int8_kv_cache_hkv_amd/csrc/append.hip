@@ -22,6 +22,8 @@
 //                        the slots they replace), then publishes seq_len.
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 #include "hkv_device.h"
 
 namespace hkv {
@@ -217,37 +219,54 @@ __global__ __launch_bounds__(kThreads) void append_ring_kernel(AppendParams p) {
 }
 
 // Single-pass append, one workgroup per (sequence, kv-head), for appends that
-// touch at most a couple of cold blocks per sequence (a decode step touches
-// one).  Everything one kv-head of one sequence owns (its touched tiles, tail
-// shadow rows and hot-ring slots) is handled by one workgroup in program
-// order, so no second launch is needed; the cached length comes from the host
-// mirror (kernel argument), so no workgroup reads seq_len while another
-// publishes it.
+// touch at most two cold blocks per sequence (a decode step touches one).
+// Everything one kv-head of one sequence owns (its touched tiles, tail shadow
+// rows and hot-ring slots) is handled by one workgroup, so no second launch is
+// needed; the cached length comes from the host mirror (kernel argument), so
+// no workgroup reads seq_len while another publishes it.
 //
-// Block scale reuse: s = fl32(m / 127) is monotonic and injective on fp16
-// maxima, so when fl32(m_new / 127) <= s_old for the rows being added, the
-// block maximum and scale are unchanged and the old rows keep their codes;
-// only the new rows are coded.  Otherwise the whole block is re-quantised
-// from its FP16 rows.  Both paths give the codes a full re-quantisation gives.
+// One round of loads: every row the append needs (the spilled or new FP16 rows
+// of the touched blocks, the old rows of a partial block from the tail
+// shadow, the new tokens that stay hot) and the block headers are requested
+// together at the start; nothing else is read.  In particular the old scale of
+// a partial block is not loaded: its rows are the block's only rows, and
+// s = fl32(m / 127) is monotonic and injective on fp16 maxima, so the stored
+// scale is always fl32(m_old / 127) with m_old = max|x| over the tail-shadow
+// rows.  When the new rows satisfy m_new <= m_old the block's maximum and scale
+// are unchanged and only the new rows are coded (the old ones keep their
+// codes); otherwise the whole block is re-quantised from its FP16 rows.  Both
+// paths give the codes a full re-quantisation gives.
 template <int D>
 __global__ __launch_bounds__(kThreads) void append_step_kernel(AppendParams p) {
   constexpr int S = kBlockSize;
   constexpr int TPT = kThreads / S;     // threads per token row
   constexpr int CPT = D / TPT;          // channels per thread
+  constexpr int NV = CPT / 8;           // 16-byte vectors per thread and row
   constexpr int LDS_ROW = D + 16;
   constexpr int VPR = D / 8;            // 16-byte vectors per fp16 row
+  constexpr int RING_V = 4;             // ring vectors per thread held in registers
   __shared__ __align__(16) int8_t stage[S * LDS_ROW];
-  __shared__ float red[kWaves], red2[kWaves];
+  __shared__ float red[6][kWaves];
 
-  const CacheView& c = p.c;
-  const int H = c.H, T = c.T;
-  const int h = blockIdx.x % H;
-  const int bl = blockIdx.x / H;
-  if (bl >= p.n_seq) return;
+  // grid (kv-head, sequence of this launch): no index depends on a kernel argument, so every
+  // argument the kernel uses is read in one round of scalar loads, before any branch
+  const int h = blockIdx.x;
+  const int bl = blockIdx.y;
+  const CacheView c = p.c;
+  const _Float16* const k_new = p.k_new;
+  const _Float16* const v_new = p.v_new;
+  const int max_n_new = p.max_n_new;
   const int b = p.b0 + bl;
   const int nn = p.n_new[bl];
-  if (nn <= 0) return;
   const int n0 = p.n0[bl];
+  const int n_seq = p.n_seq;
+  // consume every argument here: their scalar loads are issued together and waited for once,
+  // instead of being sunk one by one behind the branches below
+  asm volatile("" ::"s"(c.hot), "s"(c.tail), "s"(c.cold), "s"(c.scales), "s"(c.headers), "s"(c.seq_len),
+               "s"(k_new), "s"(v_new), "s"(max_n_new), "s"(b), "s"(nn), "s"(n0), "s"(n_seq), "s"(c.H), "s"(c.T),
+               "s"(c.max_blocks), "s"(c.num_phys));
+  if (bl >= n_seq || nn <= 0) return;
+  const int H = c.H, T = c.T;
   const int n1 = n0 + nn;
   const int cold0 = n0 > T ? n0 - T : 0;
   const int cold1 = n1 > T ? n1 - T : 0;
@@ -257,120 +276,152 @@ __global__ __launch_bounds__(kThreads) void append_step_kernel(AppendParams p) {
 
   auto row_ptr = [&](int pos, int kv) -> const _Float16* {
     if (pos < n0) return c.hot + ((bh * T + (pos % T)) * 2 + kv) * D;
-    return (kv ? p.v_new : p.k_new) + ((static_cast<size_t>(b) * p.max_n_new + (pos - n0)) * H + h) * D;
+    return (kv ? v_new : k_new) + ((static_cast<size_t>(b) * max_n_new + (pos - n0)) * H + h) * D;
   };
-  auto block_max2 = [&](float& m0, float& m1) {
-    m0 = wave_max(m0);
-    m1 = wave_max(m1);
-    if ((tid & 63) == 0) {
-      red[tid >> 6] = m0;
-      red2[tid >> 6] = m1;
-    }
-    __syncthreads();
-    float r0 = red[0], r1 = red2[0];
+  // row slices are ext-vector values (u32x4_t), never structs: selects between them stay in registers
+  auto load_slice = [&](const _Float16* row, u32x4_t (&x)[NV]) {
+    const u32x4_t* r4 = reinterpret_cast<const u32x4_t*>(row + part * CPT);
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) {
-      r0 = fmaxf(r0, red[w]);
-      r1 = fmaxf(r1, red2[w]);
-    }
-    __syncthreads();
-    m0 = r0;
-    m1 = r1;
+    for (int v = 0; v < NV; ++v) x[v] = r4[v];
   };
-  auto load_row = [&](const _Float16* row, float (&x)[CPT]) {
-    const uint4* r4 = reinterpret_cast<const uint4*>(row + part * CPT);
+  auto zero_slice = [&](u32x4_t (&x)[NV]) {
 #pragma unroll
-    for (int v = 0; v < CPT / 8; ++v) {
-      const uint4 wv = r4[v];
+    for (int v = 0; v < NV; ++v) x[v] = u32x4_t{0u, 0u, 0u, 0u};
+  };
+  auto slice_max = [&](const u32x4_t (&x)[NV]) -> float {
+    float m = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[v * 8 + 2 * i] = half_lo(word_of(wv, i));
-        x[v * 8 + 2 * i + 1] = half_hi(word_of(wv, i));
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(half_lo(x[v][i])), fabsf(half_hi(x[v][i]))));
+    return m;
+  };
+  // codes of one row slice with scale s (IEEE division, round half to even, clamp)
+  auto code_slice = [&](const u32x4_t (&x)[NV], float s, uint32_t (&q)[CPT / 4]) {
+#pragma unroll
+    for (int i = 0; i < CPT / 4; ++i) {
+      uint32_t packed = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int e = 4 * i + k;
+        const uint32_t wd = x[e / 8][(e % 8) / 2];
+        const float xv = (e & 1) ? half_hi(wd) : half_lo(wd);
+        float qv = 0.f;
+        if (s > 0.f) qv = fminf(127.f, fmaxf(-127.f, __builtin_rintf(xv / s)));
+        packed |= (static_cast<uint32_t>(static_cast<int>(qv)) & 0xffu) << (8 * k);
       }
+      q[i] = packed;
     }
   };
 
-  for (int j = cold0 / S; j * S < cold1; ++j) {
-    if (j >= c.max_blocks) break;
-    const int v_old = j * S < cold0 ? cold0 - j * S : 0;   // rows already coded, FP16 in the tail shadow
-    const int v_new = min(S, cold1 - j * S);
-    const bool is_new = t >= v_old && t < v_new;
-    // the new K and V rows do not depend on the block's physical id: load them together with the header
-    float x[2][CPT];
+  // ---- the touched blocks (at most two)
+  const int j0 = cold0 / S;
+  const int jl = cold1 > cold0 ? (cold1 - 1) / S : j0 - 1;  // last touched block
+  const int nblk = jl >= j0 ? min(jl - j0 + 1, 2) : 0;
+  const int v_old = cold0 - j0 * S;                         // coded rows of block j0 (tail shadow)
+  int phys[2] = {-1, -1};  // raw header values; checked against [0, num_phys) where used
+  u32x4_t xo[2][NV];      // old rows of block j0, K and V
+  u32x4_t xn[2][2][NV];   // new rows of the touched blocks, [block][K|V]
+  // the block index q is a compile-time constant in every use (keeps the row slices in registers)
+  using Q0 = std::integral_constant<int, 0>;
+  using Q1 = std::integral_constant<int, 1>;
+  auto load_block = [&](auto qc) {
+    constexpr int q = decltype(qc)::value;
+    const int j = j0 + q;
+    const int lo = q == 0 ? v_old : 0;
+    const int hi = q < nblk ? min(S, cold1 - j * S) : 0;
 #pragma unroll
     for (int kv = 0; kv < 2; ++kv) {
-      if (is_new) {
-        load_row(row_ptr(j * S + t, kv), x[kv]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) x[kv][i] = 0.f;
-      }
+      if (t >= lo && t < hi) load_slice(row_ptr(j * S + t, kv), xn[q][kv]);
+      else zero_slice(xn[q][kv]);
     }
-    hkv_block_header* hdr = c.headers + static_cast<size_t>(b) * c.max_blocks + j;
-    const int phys = hdr->phys_block;
-    float mnew[2] = {0.f, 0.f};
+  };
+  load_block(Q0{});
+  load_block(Q1{});
 #pragma unroll
-    for (int kv = 0; kv < 2; ++kv)
+  for (int kv = 0; kv < 2; ++kv) {
+    if (nblk > 0 && t < v_old) load_slice(c.tail + ((bh * 2 + kv) * S + t) * D, xo[kv]);
+    else zero_slice(xo[kv]);
+  }
+  // the new tokens that stay hot (ring slots pos mod T), held in registers until the spilled
+  // slots they replace have been read
+  const int rlo = max(n0, n1 - T);
+  const int ritems = (n1 - rlo) * 2 * VPR;
+  u32x4_t rv[RING_V];
 #pragma unroll
-      for (int i = 0; i < CPT; ++i) mnew[kv] = fmaxf(mnew[kv], fabsf(x[kv][i]));
-    block_max2(mnew[0], mnew[1]);
-    if (phys < 0 || phys >= c.num_phys) continue;
-    float* sp = c.scales + (static_cast<size_t>(phys) * H + h) * 2;
-    const float s_old[2] = {v_old > 0 ? sp[0] : 0.f, v_old > 0 ? sp[1] : 0.f};
+  for (int k = 0; k < RING_V; ++k) {
+    // unconditional load from a clamped (valid) item: no divergent branch around it; only items
+    // below ritems are stored (ritems >= 2 * VPR since nn >= 1)
+    const int it = min(tid + k * kThreads, ritems - 1);
+    const int v = it % VPR, kv = (it / VPR) % 2, pos = rlo + it / (2 * VPR);
+    rv[k] = reinterpret_cast<const u32x4_t*>(row_ptr(pos, kv))[v];
+  }
+  // headers last: none of the row loads above waits for them
 #pragma unroll
-    for (int kv = 0; kv < 2; ++kv) {  // unrolled: x[kv] must stay in registers
-      int8_t* tile = c.cold + tile_offset(phys, h, kv, H, S, D);
-      if (v_old > 0 && mnew[kv] / 127.0f <= s_old[kv]) {
-        // ---- scale unchanged: code only the new rows, in place
-        const float so = s_old[kv];
+  for (int q = 0; q < 2; ++q)
+    if (q < nblk && j0 + q < c.max_blocks) phys[q] = c.headers[static_cast<size_t>(b) * c.max_blocks + j0 + q].phys_block;
+
+  // ---- block maxima (one reduction round for all six values)
+  float mx[6] = {slice_max(xo[0]), slice_max(xo[1]), slice_max(xn[0][0]), slice_max(xn[0][1]),
+                 slice_max(xn[1][0]), slice_max(xn[1][1])};
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    mx[i] = wave_max_dpp(mx[i]);  // DPP + readlane: no LDS round trips
+    if ((tid & 63) == 0) red[i][tid >> 6] = mx[i];
+  }
+  __syncthreads();  // also: every load above has completed, so spilled slots may be overwritten
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    float r = red[i][0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) r = fmaxf(r, red[i][w]);
+    mx[i] = r;
+  }
+
+  // ---- codes of the touched blocks
+  auto code_block = [&](auto qc) {
+    constexpr int q = decltype(qc)::value;
+    if (q >= nblk) return;
+    const int j = j0 + q;
+    const int vo = q == 0 ? v_old : 0;
+    const int vn = min(S, cold1 - j * S);
+    const bool is_new = t >= vo && t < vn;
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv) {  // unrolled: the slices stay in registers
+      const float m_old = q == 0 ? mx[kv] : 0.f;
+      const float m_new = mx[2 + 2 * q + kv];
+      if (phys[q] < 0 || phys[q] >= c.num_phys) continue;
+      int8_t* tile = c.cold + tile_offset(phys[q], h, kv, H, S, D);
+      if (vo > 0 && m_new <= m_old) {
+        // ---- maximum unchanged: code only the new rows, in place
         if (is_new) {
-          int8_t q8[CPT];
-#pragma unroll
-          for (int i = 0; i < CPT; ++i)
-            q8[i] = so > 0.f ? static_cast<int8_t>(fminf(127.f, fmaxf(-127.f, __builtin_rintf(x[kv][i] / so)))) : 0;
+          const float so = m_old / 127.0f;
+          uint32_t qw[CPT / 4];
+          code_slice(xn[q][kv], so, qw);
           if (kv == 0) {
 #pragma unroll
             for (int ch = 0; ch < CPT / 16; ++ch) {
               const int dc = (part * CPT) / 16 + ch;
-              uint32_t wv[4];
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-                wv[i] = (static_cast<uint32_t>(static_cast<uint8_t>(q8[ch * 16 + 4 * i])) |
-                         (static_cast<uint32_t>(static_cast<uint8_t>(q8[ch * 16 + 4 * i + 1])) << 8) |
-                         (static_cast<uint32_t>(static_cast<uint8_t>(q8[ch * 16 + 4 * i + 2])) << 16) |
-                         (static_cast<uint32_t>(static_cast<uint8_t>(q8[ch * 16 + 4 * i + 3])) << 24));
-              reinterpret_cast<uint4*>(tile)[dc * S + t] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+              reinterpret_cast<uint4*>(tile)[dc * S + t] = make_uint4(qw[4 * ch], qw[4 * ch + 1], qw[4 * ch + 2], qw[4 * ch + 3]);
             }
           } else {
 #pragma unroll
-            for (int i = 0; i < CPT; ++i) tile[((t / 16) * D + part * CPT + i) * 16 + (t % 16)] = q8[i];
+            for (int i = 0; i < CPT; ++i)
+              tile[((t / 16) * D + part * CPT + i) * 16 + (t % 16)] = static_cast<int8_t>(qw[i / 4] >> (8 * (i % 4)));
           }
         }
         continue;
       }
-      // ---- (re-)quantise the whole block: old rows come back from the tail shadow
-      float mblk = mnew[kv];
-      if (v_old > 0) {
-        if (t < v_old) load_row(c.tail + ((bh * 2 + kv) * S + t) * D, x[kv]);
-        float mo = 0.f, dummy = 0.f;
+      // ---- (re-)quantise the whole block: old rows from the tail shadow, new rows as loaded
+      const float s = fmaxf(m_old, m_new) / 127.0f;
+      u32x4_t xs[NV];
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) mo = fmaxf(mo, fabsf(x[kv][i]));
-        block_max2(mo, dummy);
-        mblk = fmaxf(mblk, mo);
-      }
-      const float s = mblk / 127.0f;
-      int8_t* srow = stage + t * LDS_ROW + part * CPT;
+      for (int v = 0; v < NV; ++v) xs[v] = t < vo ? xo[kv][v] : xn[q][kv][v];  // element-wise: no indexed arrays
+      uint32_t qw[CPT / 4];
+      code_slice(xs, s, qw);
+      uint32_t* srow = reinterpret_cast<uint32_t*>(stage + t * LDS_ROW + part * CPT);
 #pragma unroll
-      for (int i = 0; i < CPT; i += 4) {
-        uint32_t packed = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          float qv = 0.f;
-          if (s > 0.f) qv = fminf(127.f, fmaxf(-127.f, __builtin_rintf(x[kv][i + k] / s)));
-          packed |= (static_cast<uint32_t>(static_cast<int>(qv)) & 0xffu) << (8 * k);
-        }
-        *reinterpret_cast<uint32_t*>(srow + i) = packed;
-      }
+      for (int i = 0; i < CPT / 4; ++i) srow[i] = qw[i];
       __syncthreads();
       constexpr int NVEC = S * D / 16;
       for (int vi = tid; vi < NVEC; vi += kThreads) {
@@ -393,38 +444,47 @@ __global__ __launch_bounds__(kThreads) void append_step_kernel(AppendParams p) {
         }
         reinterpret_cast<uint4*>(tile)[vi] = out;
       }
-      if (tid == 0) sp[kv] = s;
-      __syncthreads();
+      if (tid == 0) c.scales[(static_cast<size_t>(phys[q]) * H + h) * 2 + kv] = s;
+      __syncthreads();  // stage is reused
     }
-    if (h == 0 && tid == 0) {
-      hdr->n_valid = v_new;
+    if (h == 0 && tid == 0 && j < c.max_blocks) {
+      hkv_block_header* hdr = c.headers + static_cast<size_t>(b) * c.max_blocks + j;
+      hdr->n_valid = vn;
       hdr->logical_block = j;
       hdr->flags = 0u;
     }
-  }
-  __syncthreads();  // every read of the tail shadow and of spilled ring slots is done
-  // FP16 shadow of the new partial last block (rows already there stay)
-  const int jf = cold1 / S;
-  if ((cold1 % S) != 0) {
-    const int lo = max(jf * S, cold0), hi = cold1;
-    for (int it = tid; it < (hi - lo) * 2 * VPR; it += kThreads) {
-      const int v = it % VPR;
-      const int kv = (it / VPR) % 2;
-      const int pos = lo + it / (2 * VPR);
-      reinterpret_cast<uint4*>(c.tail + ((bh * 2 + kv) * S + (pos - jf * S)) * D)[v] =
-          reinterpret_cast<const uint4*>(row_ptr(pos, kv))[v];
+  };
+  code_block(Q0{});
+  code_block(Q1{});
+
+  // ---- FP16 shadow of the new partial last block: its new rows, from registers
+  if ((cold1 % S) != 0 && nblk > 0) {
+    const int q = jl - j0;  // the partial block is the last touched one
+    const int vo = q == 0 ? v_old : 0;
+    const int vn = cold1 - jl * S;
+    if (t >= vo && t < vn) {
+#pragma unroll
+      for (int kv = 0; kv < 2; ++kv) {
+        u32x4_t* dst = reinterpret_cast<u32x4_t*>(c.tail + ((bh * 2 + kv) * S + t) * D + part * CPT);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) dst[v] = q == 0 ? xn[0][kv][v] : xn[1][kv][v];
+      }
     }
   }
-  __syncthreads();  // ring slots read above are overwritten below
-  {
-    const int lo = max(n0, n1 - T), hi = n1;
-    for (int it = tid; it < (hi - lo) * 2 * VPR; it += kThreads) {
-      const int v = it % VPR;
-      const int kv = (it / VPR) % 2;
-      const int pos = lo + it / (2 * VPR);
-      reinterpret_cast<uint4*>(c.hot + ((bh * T + (pos % T)) * 2 + kv) * D)[v] =
-          reinterpret_cast<const uint4*>(row_ptr(pos, kv))[v];
+  // ---- new tokens that stay hot: ring slot pos mod T (every read of the slots they replace
+  // happened before the barrier above)
+#pragma unroll
+  for (int k = 0; k < RING_V; ++k) {
+    const int it = tid + k * kThreads;
+    if (it < ritems) {
+      const int v = it % VPR, kv = (it / VPR) % 2, pos = rlo + it / (2 * VPR);
+      reinterpret_cast<u32x4_t*>(c.hot + ((bh * T + (pos % T)) * 2 + kv) * D)[v] = rv[k];
     }
+  }
+  for (int it = tid + RING_V * kThreads; it < ritems; it += kThreads) {  // hot zones larger than the registers
+    const int v = it % VPR, kv = (it / VPR) % 2, pos = rlo + it / (2 * VPR);
+    reinterpret_cast<uint4*>(c.hot + ((bh * T + (pos % T)) * 2 + kv) * D)[v] =
+        reinterpret_cast<const uint4*>(row_ptr(pos, kv))[v];
   }
   if (h == 0 && tid == 0) c.seq_len[b] = n1;
 }
@@ -440,14 +500,26 @@ hipError_t launch1(K kernel, int grid, const AppendParams& p, const LaunchCtx& c
   return hipGetLastError();
 }
 
+template <typename K>
+hipError_t launch_grid(K kernel, dim3 grid, const AppendParams& p, const LaunchCtx& ctx) {
+  if (grid.x == 0 || grid.y == 0) return hipSuccess;
+  if (ctx.start) {
+    hipExtLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, ctx.stream, ctx.start, ctx.stop, 0, p);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, ctx.stream, p);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace detail
 
 using namespace detail;
 
 hipError_t launch_append(const AppendParams& p, const LaunchCtx& quant_ctx, const LaunchCtx& ring_ctx) {
   if (p.single_pass) {
-    return p.c.D == 128 ? launch1(append_step_kernel<128>, p.n_seq * p.c.H, p, quant_ctx)
-                        : launch1(append_step_kernel<64>, p.n_seq * p.c.H, p, quant_ctx);
+    const dim3 grid(p.c.H, p.n_seq);  // (kv-head, sequence)
+    return p.c.D == 128 ? launch_grid(append_step_kernel<128>, grid, p, quant_ctx)
+                        : launch_grid(append_step_kernel<64>, grid, p, quant_ctx);
   }
   const int qgrid = p.touched_max > 0 ? p.n_seq * p.touched_max * p.c.H : 0;
   hipError_t e;

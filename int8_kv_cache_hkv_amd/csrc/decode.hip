@@ -237,10 +237,18 @@ __device__ __forceinline__ int dense_phys(const CacheView& c, int b, int j) {
 // Buffer resource over one block's K and V tiles of one kv-head (2*S*D
 // contiguous bytes, K first): the tile loads take a uniform descriptor plus a
 // 32-bit lane offset, and the hardware range check returns 0 past the end.
+// phys < 0 gives an empty descriptor: the loads return 0 and touch no memory.
 template <int D>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const CacheView& c, int phys, int h) {
-  const int8_t* base = c.cold + tile_offset(phys, h, 0, c.H, kBlockSize, D);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(base), 0, 2 * kBlockSize * D, kBufferDword3);
+  const bool ok = phys >= 0;
+  const int8_t* base = c.cold + tile_offset(ok ? phys : 0, h, 0, c.H, kBlockSize, D);
+  return make_rsrc(base, ok ? 2u * kBlockSize * D : 0u);
+}
+
+// Descriptor over the whole scales array [num_phys][H][2]: an out-of-range
+// (phys, h) reads 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t scales_rsrc(const CacheView& c) {
+  return make_rsrc(c.scales, static_cast<uint32_t>(c.num_phys) * c.H * 8u);
 }
 
 // Request the K tile (lane t: 16 codes of token t per chunk).
@@ -256,10 +264,15 @@ __device__ __forceinline__ void issue_k(Tiles<D>& t, __amdgpu_buffer_rsrc_t r, i
 // per load).  The scales travel with the V tile: they are requested after the
 // previous unit's softmax has used the register pair.
 template <int D>
-__device__ __forceinline__ void issue_v(Tiles<D>& t, float2& sc, __amdgpu_buffer_rsrc_t r, const CacheView& c,
-                                        int phys, int h, int lane) {
+__device__ __forceinline__ void issue_v(Tiles<D>& t, float2& sc, __amdgpu_buffer_rsrc_t r,
+                                        __amdgpu_buffer_rsrc_t rs, int phys, int H, int h, int lane) {
   constexpr int S = kBlockSize;
-  sc = *reinterpret_cast<const float2*>(c.scales + (static_cast<size_t>(phys) * c.H + h) * 2);
+  // per-lane offset (kept out of scalar registers: no wait right after the load); phys < 0 reads 0
+  const int so = static_cast<int>(opaque_index(static_cast<uint32_t>((phys * H + h) * 8)));
+  // two 32-bit loads (the 64-bit buffer-load builtin can come out as a single dword load)
+  const int o = phys < 0 ? -8 : so;
+  sc = make_float2(__builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, o, 0, 0)),
+                   __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, o, 4, 0)));
   const uint32_t lo = static_cast<uint32_t>(lane) * 16u;
 #pragma unroll
   for (int ps = 0; ps < D / 64; ++ps)
@@ -299,7 +312,13 @@ __device__ __forceinline__ int walk_unit(int k, int split, int nsplit, int CU, i
 // the walk reads them with readlane, so no header load waits inside the loop.
 __device__ __forceinline__ int header_batch(const CacheView& c, int b, int kb, int split, int nsplit, int CU, int w,
                                             int lane) {
-  return dense_phys(c, b, walk_unit(kb + lane, split, nsplit, CU, w));
+  asm volatile("" : "+s"(CU));  // keeps the division by CU / 4 here (rarely executed), not hoisted and kept live
+  const int j = walk_unit(kb + lane, split, nsplit, CU, w);
+  const __amdgpu_buffer_rsrc_t rh =
+      make_rsrc(c.headers + static_cast<size_t>(b) * c.max_blocks, static_cast<uint32_t>(c.max_blocks) * 16u);
+  const bool in_table = j < c.max_blocks;
+  const int ph = __builtin_amdgcn_raw_buffer_load_b32(rh, in_table ? j * 16 : -1, 0, 0);  // phys_block at offset 0
+  return (in_table && ph >= 0 && ph < c.num_phys) ? ph : -1;
 }
 
 // The walk itself.  K and V of the unit after the current one are requested
@@ -333,6 +352,7 @@ __device__ void dense_units(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const Dec
     }
     return __builtin_amdgcn_readlane(hb, k - kb);
   };
+  const __amdgpu_buffer_rsrc_t rs = scales_rsrc(c);
   int k = 0;
   int un = u >= 0 ? advance(u) : -1;
   int phys_n = un >= 0 ? phys_of(k + 1) : -1;
@@ -340,16 +360,13 @@ __device__ void dense_units(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const Dec
     const int nv = phys_u >= 0 ? min(S, n_cold - u * S) : 0;
     float4_t s[C::NQ];
     qk_codes<D, G>(t.kr, sm, lane, s);
-    __amdgpu_buffer_rsrc_t rn;
-    if (phys_n >= 0) {
-      rn = tile_rsrc<D>(c, phys_n, h);
-      issue_k<D>(t, rn, lane);
-    }
+    const __amdgpu_buffer_rsrc_t rn = tile_rsrc<D>(c, phys_n, h);  // empty when there is no next unit
+    issue_k<D>(t, rn, lane);
     float alpha[C::NG], coef[C::NG];
     softmax_unit<D, G, false>(st, sm, s, lane < nv, sc.x * p.qscale, 1.f, sc.y, alpha, coef, w, lane);
     BlockAcc<D, G> blk;
     pv_dense<D, G>(blk, sm, t.vr, w, lane);
-    if (phys_n >= 0) issue_v<D>(t, sc, rn, c, phys_n, h, lane);
+    issue_v<D>(t, sc, rn, rs, phys_n, c.H, h, lane);
     fold_block<D, G>(st, blk, alpha, coef);
     wave_lds_sync();  // this unit's weight reads are done before the next unit's writes
     u = un;
@@ -477,23 +494,41 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   // the length, this wave's first header and (dense) its first tiles are requested together
   // with the query copy; the tiles are used only if the unit exists
-  const int n_seq = c.seq_len[b];
+  // first memory round: the query rows, the length and this wave's header batch; the first
+  // unit's tiles follow as soon as its physical block id is known
+  constexpr int QITEMS = 4 * C::NQ * (D / 8);  // 16-byte query vectors (rows past G are zero)
+  constexpr int QPT = (QITEMS + kThreads - 1) / kThreads;
+  const _Float16* qg = p.q + (static_cast<size_t>(b) * c.H * G + static_cast<size_t>(h) * G) * D;
+  u32x4_t qv[QPT];
+#pragma unroll
+  for (int k = 0; k < QPT; ++k) {  // unconditional loads (clamped item), zero outside the rows
+    const int i = tid + k * kThreads;
+    const int g = i / (D / 8);
+    const bool ok = i < QITEMS && g < G;
+    const u32x4_t v = reinterpret_cast<const u32x4_t*>(qg)[ok ? i : 0];
+    qv[k] = ok ? v : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  // needed only after the barrier: kept in a vector register, waited for there (issued before the
+  // tiles, so that wait does not include them)
+  const int n_seq_lane = c.seq_len[opaque_index(b)];
   Tiles<D> t0;
   float2 sc0 = make_float2(0.f, 0.f);
   int phys0 = -1, hb = -1;
   if (!SPARSE) {
     hb = header_batch(c, b, 0, split, p.nsplit, p.units_per_split, w, lane);
     phys0 = __builtin_amdgcn_readlane(hb, 0);
-    if (phys0 >= 0) {
-      const __amdgpu_buffer_rsrc_t r0 = tile_rsrc<D>(c, phys0, h);
-      issue_k<D>(t0, r0, lane);
-      issue_v<D>(t0, sc0, r0, c, phys0, h, lane);
-    }
+    const __amdgpu_buffer_rsrc_t r0 = tile_rsrc<D>(c, phys0, h);
+    issue_k<D>(t0, r0, lane);
+    issue_v<D>(t0, sc0, r0, scales_rsrc(c), phys0, c.H, h, lane);
   }
-  copy_query<D, G>(p.q + (static_cast<size_t>(b) * c.H * G + static_cast<size_t>(h) * G) * D, sm.qh, tid);
+#pragma unroll
+  for (int k = 0; k < QPT; ++k) {
+    const int i = tid + k * kThreads;
+    if (i < QITEMS) *reinterpret_cast<u32x4_t*>(&sm.qh[i / (D / 8) / 4][i / (D / 8) % 4][(i % (D / 8)) * 8]) = qv[k];
+  }
   __syncthreads();
 
-  const SeqGeom sg = seq_geom(n_seq, c.T, S);
+  const SeqGeom sg = seq_geom(__builtin_amdgcn_readfirstlane(n_seq_lane), c.T, S);
   const int units = sg.n_cold > 0 ? (SPARSE ? cdiv(p.k_sel, 64) : sg.n_blk) : 0;
   const int32_t* sel_bh = SPARSE ? p.sel + static_cast<size_t>(bh) * p.k_sel : nullptr;
 
@@ -658,7 +693,7 @@ __device__ void hot_split(const DecodeParams& p, HotSmem<D, G>& hm, int b, int h
   }
 }
 
-// One launch per decode call: B*H*(nsplit + 1) workgroups; for each (sequence,
+// One launch per decode call: (nsplit + 1) x H x B workgroups; for each (sequence,
 // kv-head) nsplit cold splits and one hot split write partials, and the last
 // of them to arrive merges all nsplit + 1 partials with the log-sum-exp rule
 // (M = max m_s, L = sum e^(m_s - M) l_s, out = sum e^(m_s - M) acc_s / L) and
@@ -673,11 +708,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G > 4 
     HotSmem<D, G> hot;
   } sm;
   __shared__ int s_last;
+  // grid (split, kv-head, sequence): no index depends on a kernel argument, and every argument the
+  // kernel uses is consumed here, so its scalar loads are issued together and waited for once
+  asm volatile("" ::"s"(p.c.H), "s"(p.c.T), "s"(p.c.max_blocks), "s"(p.c.num_phys), "s"(p.c.hot), "s"(p.c.cold),
+               "s"(p.c.scales), "s"(p.c.headers), "s"(p.c.seq_len), "s"(p.q), "s"(p.sel), "s"(p.k_sel),
+               "s"(p.partials), "s"(p.counters), "s"(p.nsplit), "s"(p.units_per_split), "s"(p.qscale));
   const CacheView& c = p.c;
-  const int split = blockIdx.x % (p.nsplit + 1);
-  const int bh = blockIdx.x / (p.nsplit + 1);
-  const int h = bh % c.H;
-  const int b = bh / c.H;
+  const int split = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int bh = b * c.H + h;
   const int tid = threadIdx.x;
   if (split < p.nsplit) {
     cold_split<D, G, SPARSE>(p, sm.cold, b, h, bh, split);
@@ -741,8 +781,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G > 4 
 }
 
 template <typename K>
-hipError_t launch_k(K kernel, int grid, int block, const DecodeParams& p, const LaunchCtx& ctx) {
-  if (grid <= 0) return hipSuccess;
+hipError_t launch_k(K kernel, dim3 grid, int block, const DecodeParams& p, const LaunchCtx& ctx) {
+  if (grid.x == 0 || grid.y == 0 || grid.z == 0) return hipSuccess;
   if (ctx.start) {
     hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(block), 0, ctx.stream, ctx.start, ctx.stop, 0, p);
   } else {
@@ -753,7 +793,7 @@ hipError_t launch_k(K kernel, int grid, int block, const DecodeParams& p, const 
 
 template <int D, int G>
 hipError_t launch_dg(const DecodeParams& p, const LaunchCtx& ctx) {
-  const int grid = p.c.B * p.c.H * (p.nsplit + 1);
+  const dim3 grid(p.nsplit + 1, p.c.H, p.c.B);  // (split, kv-head, sequence)
   return p.sel ? launch_k(decode_kernel<D, G, true>, grid, kThreads, p, ctx)
                : launch_k(decode_kernel<D, G, false>, grid, kThreads, p, ctx);
 }

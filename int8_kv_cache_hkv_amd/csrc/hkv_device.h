@@ -63,6 +63,7 @@ __device__ __forceinline__ float half_hi(uint32_t w) {
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
 // Streaming 16-byte load of cold-tile data that is read once per call: the
 // non-temporal hint keeps it from displacing reused lines in the caches
@@ -73,14 +74,30 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// An index the compiler must treat as per-lane: a load through it stays a
+// vector-register value instead of being turned into a scalar right after the
+// load (which would make the wave wait for it there).  Used for uniform values
+// that are needed only much later.
+__device__ __forceinline__ size_t opaque_index(size_t i) {
+  asm volatile("" : "+v"(i));
+  return i;
+}
+
 // Fourth descriptor word of a raw buffer resource on gfx9-family GPUs (32-bit
 // data format, no swizzle).
 constexpr int kBufferDword3 = 0x00020000;
 
+// Raw buffer resource over `bytes` bytes at `base` (bytes = 0: every load
+// returns 0 without a memory access, so a load can be issued unconditionally).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kBufferDword3);
+}
+
 // Streaming 16-byte buffer load (non-temporal, like load_stream) at byte
 // offset `off` of the resource.
 __device__ __forceinline__ uint4 load_stream_buf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 2 /* nt */);
+  // bit_cast, not a conversion: an implicit conversion from the builtin's vector type may splat
+  const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 2 /* nt */));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
