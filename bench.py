@@ -72,8 +72,9 @@ class Inst:
         self.desc_ref = ctypes.byref(self.c.desc)
 
 
-def run_leg(hkv, torch, w, n0, steps, warmup, R, label, do_append=True):
-    """Rotating-instance append+decode loop; returns timing and byte counts."""
+def run_leg(hkv, torch, w, n0, steps, warmup, R, label, do_append=True, fused=True):
+    """Rotating-instance append+decode loop (one hkv_append_decode launch per step, or hkv_append then
+    hkv_decode_attn when fused is False); returns timing and byte counts."""
     import workloads as wl
     H, Hq, d = w.n_kv_heads, w.n_q_heads, w.head_dim
     uses = -(-(2 * steps + warmup) // R) + 1
@@ -108,6 +109,15 @@ def run_leg(hkv, torch, w, n0, steps, warmup, R, label, do_append=True):
     def step(i):
         r = i % R
         it = insts[r]
+        if do_append and fused:
+            u = use_count[r]
+            st = lib.hkv_append_decode(it.c.handle, it.desc_ref, newk[u].data_ptr(), newv[u].data_ptr(),
+                                       qs[i % NQ].data_ptr(), Hq, out.data_ptr(), None, ws_ptr, ws_len, stream)
+            if st:
+                raise hkv.HKVError(st, "hkv_append_decode")
+            use_count[r] += 1
+            lens[r] += 1
+            return lens[r]
         if do_append:
             u = use_count[r]
             st = lib.hkv_append(it.c.handle, it.desc_ref, newk[u].data_ptr(), newv[u].data_ptr(), ones_ptr, 1, stream)
@@ -140,10 +150,11 @@ def run_leg(hkv, torch, w, n0, steps, warmup, R, label, do_append=True):
         hkv.hkv_timing_enable(it.c.handle, True)
     kern_bytes = 0
     for i in range(warmup + steps, warmup + 2 * steps):
-        kern_bytes += step_bytes_of(step(i))[0]
+        # the fused kernel moves the append's bytes too; the plain decode kernel only the decode's
+        kern_bytes += step_bytes_of(step(i))[1 if (fused and do_append) else 0]
     torch.cuda.synchronize()
     kms = {}
-    for kname in ("append", "append_ring", "decode"):
+    for kname in ("append", "append_ring", "decode", "append_decode"):
         tot, cnt = 0.0, 0
         for it in insts:
             a, b = hkv.hkv_timing_read(it.c.handle, kname, reset=True)
@@ -218,8 +229,9 @@ def long_leg(hkv, torch, steps):
     r = run_leg(hkv, torch, w, w.context - 1, steps, 3, 2, "long")
     H, Hq, d = w.n_kv_heads, w.n_q_heads, w.head_dim
     kb = r["kernel_bytes"]
-    kms = r["kernel_ms"]["decode"]
-    return {"workload": "long: B=4, 131072 tokens, 32/8 heads, d=128", "ms_per_step": r["ms_per_step"],
+    kms = r["kernel_ms"]["append_decode"]
+    return {"workload": "long: B=4, 131072 tokens, 32/8 heads, d=128, step = fused append 1 token + decode",
+            "ms_per_step": r["ms_per_step"],
             "gbs": r["gbs"], "pct_hbm_peak": 100 * r["gbs"] / HBM_PEAK_GBS,
             "decode_kernel_ms": kms, "decode_kernel_gbs": kb / (kms * 1e-3) / 1e9 if kms else None,
             "decode_kernel_frac": kb / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS if kms else None,
@@ -316,7 +328,7 @@ def main():
     w = wl.WORKLOADS["llama8b"]
     H, Hq, d = w.n_kv_heads, w.n_q_heads, w.head_dim
     main_leg = run_leg(hkv, torch, w, w.context - 1, args.steps, args.warmup, args.instances, "llama8b")
-    kms = main_leg["kernel_ms"]["decode"]
+    kms = main_leg["kernel_ms"]["append_decode"]
     achieved = main_leg["kernel_bytes"] / (kms * 1e-3) / 1e9 if kms else None
     gbs = main_leg["gbs"]
     ms = main_leg["ms_per_step"]
@@ -343,13 +355,17 @@ def main():
         "head_queries_per_s": round(w.batch * Hq / (ms * 1e-3), 1),
         "bytes_per_step": int(main_leg["bytes_per_step"]),
         "kernel_ms": main_leg["kernel_ms"],
-        "roofline": {"kernel": "decode_kernel", "bound": "hbm",
+        "roofline": {"kernel": "decode_kernel (fused append + decode)", "bound": "hbm",
                      "achieved": round(achieved, 1) if achieved else None, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None, "traffic": None,
                      "bytes_per_launch": int(main_leg["kernel_bytes"]),
                      "avg_launch_ms": kms},
     }
     if not args.no_extra:
+        sep = run_leg(hkv, torch, w, w.context - 1, min(args.steps, 320), args.warmup, args.instances,
+                      "llama8b (separate calls)", fused=False)
+        res["separate_calls"] = {"what": "the same step as hkv_append then hkv_decode_attn (two launches)",
+                                 "ms_per_step": sep["ms_per_step"], "gbs": sep["gbs"], "kernel_ms": sep["kernel_ms"]}
         res["long"] = long_leg(hkv, torch, 16)
         res["sparse"] = sparse_leg(hkv, torch, 20)
     if args.copy_calibration:

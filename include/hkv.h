@@ -159,13 +159,13 @@ hkv_status hkv_cache_sizes(hkv_handle h, int batch, int64_t max_tokens_per_seq, 
 hkv_status hkv_header_table_bytes(int hot_tokens, int block_size, int64_t total_tokens, int64_t* n_blocks,
                                   size_t* bytes);
 
-/* Workspace bytes needed by hkv_decode_attn (dense and sparse) and
- * hkv_topk_select on this cache with n_q_heads query heads and a top-K
- * budget k_sel (0 if top-K is not used).  The bound holds for every length
- * up to the cache's capacity, so one allocation serves all later calls.
- * The workspace must be zero-filled before its first use: its first bytes
- * hold per-(sequence, kv-head) arrival counters that every call leaves at
- * zero again.  Calls that share a workspace must be ordered on one stream.
+/* Workspace bytes needed by hkv_decode_attn (dense and sparse),
+ * hkv_append_decode and hkv_topk_select on this cache with n_q_heads query
+ * heads and a top-K budget k_sel (0 if top-K is not used).  The bound holds
+ * for every length up to the cache's capacity, so one allocation serves all
+ * later calls.  The workspace must be zero-filled before its first use: its
+ * first bytes hold per-(sequence, kv-head) and per-sequence arrival counters
+ * that every call leaves at zero again.  Calls that share a workspace must be ordered on one stream.
  * HKV_ERR_INVALID_VALUE if n_q_heads is not a positive multiple of
  * n_kv_heads or k_sel is outside [0, 512]. */
 hkv_status hkv_workspace_bytes(hkv_handle h, const hkv_cache_desc* c, int n_q_heads, int k_sel, size_t* bytes);
@@ -217,6 +217,27 @@ hkv_status hkv_decode_attn(hkv_handle h, const hkv_cache_desc* c, const void* q,
                            const int32_t* sel_idx, int k_sel, void* out, float* lse, void* workspace,
                            size_t ws_bytes, hipStream_t stream);
 
+/* One decode step in one launch: hkv_append of exactly one new token per
+ * sequence followed by the dense hkv_decode_attn of q against the updated
+ * cache (Hybrid KV Cache page 2.1 and 4.2: the token leaving the hot zone is
+ * quantised into its cold block, then the query attends hot plus cold).  The
+ * cache contents, out and lse are those of the two calls made in that order;
+ * the append's work runs inside the decode launch instead of in a launch of
+ * its own.
+ *   k_new, v_new  device fp16 [batch][n_kv_heads][head_dim]: the new token
+ *                 (position seq_len[b]) of every sequence.
+ *   q, n_q_heads, out, lse, workspace, ws_bytes  as for hkv_decode_attn
+ *                 (dense).
+ * seq_len_dev and seq_len_host are incremented by one.
+ *   HKV_ERR_CAPACITY: a sequence would need more than max_blocks_per_seq
+ *     cold blocks.  HKV_ERR_INVALID_VALUE: n_q_heads not a multiple of
+ *     n_kv_heads or a negative seq_len_host entry.  HKV_ERR_UNSUPPORTED: a
+ *     GQA group size other than 1, 2, 4 or 8, or block_size other than 64.
+ *   HKV_ERR_ALIGNMENT: k_new, v_new, q or workspace not 16-byte aligned. */
+hkv_status hkv_append_decode(hkv_handle h, const hkv_cache_desc* c, const void* k_new, const void* v_new,
+                             const void* q, int n_q_heads, void* out, float* lse, void* workspace, size_t ws_bytes,
+                             hipStream_t stream);
+
 /* HySparse-style top-K selection per (sequence, kv-head) over the cold
  * tokens (KV Cache reuse page 2 and 2.1):
  *   c_t = mean over the kv-head's query heads of cos(q_hq, k_t) in fp32
@@ -254,7 +275,8 @@ typedef enum {
   HKV_KERNEL_DECODE_SPARSE = 3, /* sparse decode over selected tokens, one launch */
   HKV_KERNEL_TOPK_SCORE = 4,
   HKV_KERNEL_TOPK_SELECT = 5,
-  HKV_KERNEL_KINDS = 6
+  HKV_KERNEL_APPEND_DECODE = 6, /* fused one-token append + dense decode, one launch */
+  HKV_KERNEL_KINDS = 7
 } hkv_kernel_kind;
 
 hkv_status hkv_timing_enable(hkv_handle h, int enable);

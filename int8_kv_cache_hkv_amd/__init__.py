@@ -24,9 +24,11 @@ LIB_PATH = os.path.join(_PKG, "libhkv.so")
 HKV_OK = 0
 STATUS_NAMES = {0: "HKV_OK", -1: "HKV_ERR_INVALID_VALUE", -2: "HKV_ERR_UNSUPPORTED", -3: "HKV_ERR_NULL_POINTER",
                 -4: "HKV_ERR_CAPACITY", -5: "HKV_ERR_WORKSPACE", -6: "HKV_ERR_HIP", -7: "HKV_ERR_ALIGNMENT"}
-KERNELS = {"append": 0, "append_ring": 1, "decode": 2, "decode_sparse": 3, "topk_score": 4, "topk_select": 5}
+KERNELS = {"append": 0, "append_ring": 1, "decode": 2, "decode_sparse": 3, "topk_score": 4, "topk_select": 5,
+           "append_decode": 6}
 EXPORTS = ["hkv_create", "hkv_destroy", "hkv_cache_sizes", "hkv_header_table_bytes", "hkv_workspace_bytes",
-           "hkv_append", "hkv_decode_attn", "hkv_topk_select", "hkv_status_string", "hkv_timing_enable",
+           "hkv_append", "hkv_decode_attn", "hkv_append_decode", "hkv_topk_select", "hkv_status_string",
+           "hkv_timing_enable",
            "hkv_timing_read", "hkv_last_error_detail"]
 
 
@@ -72,6 +74,7 @@ def _load() -> ctypes.CDLL:
         "hkv_workspace_bytes": [vp, ctypes.POINTER(CacheDesc), i32, i32, ctypes.POINTER(sz)],
         "hkv_append": [vp, ctypes.POINTER(CacheDesc), vp, vp, vp, i32, vp],
         "hkv_decode_attn": [vp, ctypes.POINTER(CacheDesc), vp, i32, vp, i32, vp, vp, vp, sz, vp],
+        "hkv_append_decode": [vp, ctypes.POINTER(CacheDesc), vp, vp, vp, i32, vp, vp, vp, sz, vp],
         "hkv_topk_select": [vp, ctypes.POINTER(CacheDesc), vp, i32, i32, vp, vp, sz, vp],
         "hkv_timing_enable": [vp, i32],
         "hkv_timing_read": [vp, i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64), i32],
@@ -171,6 +174,13 @@ def hkv_decode_attn(handle: int, desc: CacheDesc, q, out, workspace, lse=None, s
            "hkv_decode_attn")
 
 
+def hkv_append_decode(handle: int, desc: CacheDesc, k_new, v_new, q, out, workspace, lse=None, stream=None) -> None:
+    _check(_lib.hkv_append_decode(handle, ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(q), int(q.shape[1]),
+                                  _ptr(out), _ptr(lse), _ptr(workspace),
+                                  int(workspace.numel() * workspace.element_size()), _stream(stream)),
+           "hkv_append_decode")
+
+
 def hkv_topk_select(handle: int, desc: CacheDesc, q, k: int, out_idx, workspace, stream=None) -> None:
     _check(_lib.hkv_topk_select(handle, ctypes.byref(desc), _ptr(q), int(q.shape[1]), int(k), _ptr(out_idx),
                                 _ptr(workspace), int(workspace.numel() * workspace.element_size()),
@@ -243,6 +253,16 @@ class HybridKVCache:
             out = torch.empty_like(q)
         ws = workspace if workspace is not None else self.workspace(int(q.shape[1]), k_sel)
         hkv_decode_attn(self.handle, self.desc, q, out, ws, lse=lse, sel_idx=sel_idx, k_sel=k_sel, stream=stream)
+        return out
+
+    def append_decode(self, k_new, v_new, q, out=None, lse=None, workspace=None, stream=None):
+        """One decode step: append one token per sequence (k_new/v_new [batch, H, D] or [batch, 1, H, D])
+        and decode q against the updated cache, in one launch."""
+        torch = self.torch
+        if out is None:
+            out = torch.empty_like(q)
+        ws = workspace if workspace is not None else self.workspace(int(q.shape[1]))
+        hkv_append_decode(self.handle, self.desc, k_new, v_new, q, out, ws, lse=lse, stream=stream)
         return out
 
     def topk(self, q, k: int, out_idx=None, workspace=None, stream=None):

@@ -38,6 +38,8 @@
 // wave always has one unit's loads in flight.
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 #include "hkv_device.h"
 
 namespace hkv {
@@ -467,7 +469,7 @@ __device__ __forceinline__ float2 load_coherent2(const float* p) {
 // G query heads; records are 8-byte aligned (D + 2 is even).
 template <int D>
 __device__ __forceinline__ float* partial_ptr(const DecodeParams& p, int bh, int split, int g) {
-  return p.partials + ((static_cast<size_t>(bh) * (p.nsplit + 1) + split) * p.G + g) * (D + 2);
+  return p.partials + ((static_cast<size_t>(bh) * p.nparts + split) * p.G + g) * (D + 2);
 }
 
 // Query rows of one kv-head's group into LDS as fp16 (exact), 16 bytes per
@@ -484,7 +486,7 @@ __device__ __forceinline__ void copy_query(const _Float16* qg, _Float16 (*qh)[4]
 }
 
 // ---- cold split: stream its units, merge the 4 waves, write the partial
-template <int D, int G, bool SPARSE>
+template <int D, int G, bool SPARSE, bool FUSED>
 __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, int h, int bh, int split) {
   using C = Cfg<D, G>;
   constexpr int S = kBlockSize;
@@ -529,7 +531,9 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
   __syncthreads();
 
   const SeqGeom sg = seq_geom(__builtin_amdgcn_readfirstlane(n_seq_lane), c.T, S);
-  const int units = sg.n_cold > 0 ? (SPARSE ? cdiv(p.k_sel, 64) : sg.n_blk) : 0;
+  // fused append: only the full blocks before the one the appended token spills into (n_cold is
+  // the count before the append, so the block holding cold token n_cold is excluded)
+  const int units = sg.n_cold > 0 ? (SPARSE ? cdiv(p.k_sel, 64) : (FUSED ? sg.n_cold / S : sg.n_blk)) : 0;
   const int32_t* sel_bh = SPARSE ? p.sel + static_cast<size_t>(bh) * p.k_sel : nullptr;
 
   WaveState<D, G> st;
@@ -599,23 +603,25 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
   }
 }
 
-// ---- hot split: the FP16 ring (Hybrid KV Cache page 2.1: the most recent
+// ---- hot zone: the FP16 ring (Hybrid KV Cache page 2.1: the most recent
 // tokens in full precision).  Chunks of kHotChunk slots are staged through LDS
 // with coalesced loads; wave 0 computes the logits with the same MFMA as the
 // cold blocks (lane = slot, fp16 K rows are already MFMA operands) and the
 // softmax weights; all four waves then accumulate thread (g, d) = sum_t p v.
+// Attends ring slots [0, n_hot); slot sub_slot (if >= 0) is read from the
+// rows sub_k / sub_v instead of the ring (the token a fused append is putting
+// there).  Leaves m, l (base-2 units) and acc in hm.
 template <int D, int G>
-__device__ void hot_split(const DecodeParams& p, HotSmem<D, G>& hm, int b, int h, int bh) {
+__device__ void hot_attend(const DecodeParams& p, HotSmem<D, G>& hm, int b, int h, int bh, int n_hot, int sub_slot,
+                           const _Float16* sub_k, const _Float16* sub_v) {
   using C = Cfg<D, G>;
   constexpr int NG = 4 * C::NQ;
   constexpr int ROW = 2 * D + 8;          // padded fp16 [K|V] row
   constexpr int VPR = 2 * D / 8;          // 16-byte vectors per row
   const CacheView& c = p.c;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int n_seq = c.seq_len[b];
   copy_query<D, G>(p.q + (static_cast<size_t>(b) * c.H * G + static_cast<size_t>(h) * G) * D, hm.qh, tid);
   for (int i = tid; i < G * D; i += kThreads) hm.acc[i / D][i % D] = 0.f;
-  const SeqGeom sg = seq_geom(n_seq, c.T, kBlockSize);
   const _Float16* hot_bh = c.hot + static_cast<size_t>(bh) * c.T * 2 * D;
   float m[NG], l[NG];  // wave 0's running softmax state (wave-uniform)
 #pragma unroll
@@ -623,15 +629,24 @@ __device__ void hot_split(const DecodeParams& p, HotSmem<D, G>& hm, int b, int h
     m[g] = kNegInf;
     l[g] = 0.f;
   }
-  for (int base = 0; base < sg.n_hot; base += kHotChunk) {
-    const int cnt = min(kHotChunk, sg.n_hot - base);
+  for (int base = 0; base < n_hot; base += kHotChunk) {
+    const int cnt = min(kHotChunk, n_hot - base);
     const uint4* src = reinterpret_cast<const uint4*>(hot_bh + static_cast<size_t>(base) * 2 * D);
     constexpr int NV = (kHotChunk * VPR + kThreads - 1) / kThreads;
     uint4 buf[NV];  // all of the chunk's loads in flight together
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int i = tid + k * kThreads;
-      buf[k] = i < cnt * VPR ? src[i] : make_uint4(0, 0, 0, 0);
+      if (i < cnt * VPR) {
+        if (base + i / VPR == sub_slot) {
+          const int v = i % VPR;  // K row then V row
+          buf[k] = reinterpret_cast<const uint4*>(v < D / 8 ? sub_k : sub_v)[v % (D / 8)];
+        } else {
+          buf[k] = src[i];
+        }
+      } else {
+        buf[k] = make_uint4(0, 0, 0, 0);
+      }
     }
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
@@ -685,11 +700,316 @@ __device__ void hot_split(const DecodeParams& p, HotSmem<D, G>& hm, int b, int h
     }
   }
   __syncthreads();
-  for (int i = tid; i < G * (D / 2); i += kThreads) {
+}
+
+// ---- hot split of a plain decode: the whole ring, partial at split index nsplit
+template <int D, int G>
+__device__ void hot_split(const DecodeParams& p, HotSmem<D, G>& hm, int b, int h, int bh) {
+  const SeqGeom sg = seq_geom(p.c.seq_len[b], p.c.T, kBlockSize);
+  hot_attend<D, G>(p, hm, b, h, bh, sg.n_hot, -1, nullptr, nullptr);
+  for (int i = threadIdx.x; i < G * (D / 2); i += kThreads) {
     const int g = i / (D / 2), d = 2 * (i % (D / 2));
     float* pg = partial_ptr<D>(p, bh, p.nsplit, g);
     store_coherent2(pg + 2 + d, hm.acc[g][d], hm.acc[g][d + 1]);
     if (d == 0) store_coherent2(pg, hm.m[g], hm.l[g]);
+  }
+}
+
+// ---- fused one-token append (hkv_append_decode): two more workgroups per
+// (sequence, kv-head) next to the cold splits.
+//   A (split index nsplit): the new hot window, i.e. ring slots
+//     [0, min(n0 + 1, T)) with the new token's slot read from k_new / v_new
+//     (it never reads that slot from the ring, which B overwrites).
+//   B (split index nsplit + 1): the append itself (Hybrid KV Cache page 2.1 /
+//     4.2: the token leaving the hot zone joins the cold zone, quantised with
+//     its block's scale) and the attention over that tail block jt.  The
+//     spilled token becomes row ts of block jt, re-coded exactly as the
+//     standalone append codes it (only the new row while the block maximum is
+//     unchanged, else the whole block from its FP16 tail-shadow rows); the
+//     tail shadow, the header and the ring slot are written.  The block's tile
+//     registers for the attention come from this workgroup's own codes in LDS
+//     (whole block re-coded) or from a tile load patched with the new row, so
+//     nothing waits for the code stores.  The cold splits cover only the full
+//     blocks before jt.
+template <int D, int G>
+__device__ void hot_window_split(const DecodeParams& p, HotSmem<D, G>& hm, int b, int h, int bh) {
+  const int n0 = __builtin_amdgcn_readfirstlane(p.c.seq_len[b]);
+  const int slot = n0 % p.c.T;
+  const size_t bhs = static_cast<size_t>(bh);
+  hot_attend<D, G>(p, hm, b, h, bh, min(n0 + 1, p.c.T), slot, p.k_new + bhs * D, p.v_new + bhs * D);
+  for (int i = threadIdx.x; i < G * (D / 2); i += kThreads) {
+    const int g = i / (D / 2), d = 2 * (i % (D / 2));
+    float* pg = partial_ptr<D>(p, bh, p.nsplit, g);
+    store_coherent2(pg + 2 + d, hm.acc[g][d], hm.acc[g][d + 1]);
+    if (d == 0) store_coherent2(pg, hm.m[g], hm.l[g]);
+  }
+}
+
+template <int D, int G>
+struct AppendSmem {
+  DecodeSmem<D, G> unit;                                  // tail block jt, attended by wave 0
+  alignas(16) int8_t stage[2][kBlockSize * (D + 16)];     // its K and V codes, [token][channel]
+  float red[4][kWaves];
+};
+
+template <int D, int G>
+__device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G>& am, int b, int h, int bh) {
+  using C = Cfg<D, G>;
+  constexpr int S = kBlockSize;
+  constexpr int TPT = kThreads / S;     // threads per token row
+  constexpr int CPT = D / TPT;          // channels per thread
+  constexpr int NV = CPT / 8;           // 16-byte vectors per thread and row
+  constexpr int LDS_ROW = D + 16;
+  constexpr int VR = D / 8;             // 16-byte vectors per fp16 row
+  constexpr int NG = C::NG;
+  const CacheView& c = p.c;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int T = c.T, H = c.H;
+  const int t = tid / TPT, part = tid % TPT;
+  const size_t bhs = static_cast<size_t>(bh);
+  const int n0 = __builtin_amdgcn_readfirstlane(c.seq_len[b]);  // length before the append
+  const bool spill = n0 >= T;
+  const int ps = n0 - T;                   // the spilled token's position
+  const int jt = spill ? ps / S : 0;
+  const int ts = spill ? ps % S : 0;       // its row in block jt; rows below are already coded
+  const int slot = n0 % T;                 // ring slot of the spilled token and of the new one
+  const _Float16* knew = p.k_new + bhs * D;
+  const _Float16* vnew = p.v_new + bhs * D;
+
+  // ---- first round of loads: the spilled row, the block's old rows (tail shadow), its header, the
+  // new token, and (wave 0) the query rows
+  // row t of block jt: an old row (t < ts, from the tail shadow), the spilled row (t == ts, from its
+  // ring slot) or nothing; one slice per thread
+  u32x4_t x[2][NV];
+#pragma unroll
+  for (int kv = 0; kv < 2; ++kv) {
+    const u32x4_t* src = t < ts ? reinterpret_cast<const u32x4_t*>(c.tail + ((bhs * 2 + kv) * S + t) * D + part * CPT)
+                                : reinterpret_cast<const u32x4_t*>(c.hot + ((bhs * T + slot) * 2 + kv) * D + part * CPT);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) x[kv][v] = (spill && t <= ts) ? src[v] : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  const int it = min(tid, 2 * VR - 1);  // new token: K row then V row, one vector per thread
+  const u32x4_t nr = reinterpret_cast<const u32x4_t*>(it < VR ? knew : vnew)[it % VR];
+  int phys = -1;
+  if (spill && jt < c.max_blocks) {
+    const int ph = c.headers[static_cast<size_t>(b) * c.max_blocks + jt].phys_block;
+    phys = (ph >= 0 && ph < c.num_phys) ? ph : -1;
+  }
+  if (w == 0) {
+    const _Float16* qg = p.q + (static_cast<size_t>(b) * c.H * G + static_cast<size_t>(h) * G) * D;
+    for (int i = lane; i < 4 * C::NQ * (D / 8); i += 64) {
+      const int g = i / (D / 8);
+      const uint4 val = g < G ? reinterpret_cast<const uint4*>(qg + static_cast<size_t>(g) * D)[i % (D / 8)]
+                              : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(&am.unit.qh[g / 4][g % 4][(i % (D / 8)) * 8]) = val;
+    }
+  }
+  auto slice_max = [&](const u32x4_t (&x)[NV]) -> float {
+    float m = 0.f;
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(half_lo(x[v][i])), fabsf(half_hi(x[v][i]))));
+    return m;
+  };
+  const float m0 = slice_max(x[0]), m1 = slice_max(x[1]);
+  float mx[4] = {t < ts ? m0 : 0.f, t < ts ? m1 : 0.f, t == ts ? m0 : 0.f, t == ts ? m1 : 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    mx[i] = wave_max_dpp(mx[i]);
+    if (lane == 0) am.red[i][w] = mx[i];
+  }
+  __syncthreads();  // also: the spilled slot has been read, it may be overwritten
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float r = am.red[i][0];
+#pragma unroll
+    for (int ww = 1; ww < kWaves; ++ww) r = fmaxf(r, am.red[i][ww]);
+    mx[i] = r;
+  }
+
+  // ---- codes of block jt (as the standalone append codes them).  Every row is coded into
+  // stage[kv] for the attention below: with an unchanged maximum the old rows' codes are the
+  // stored ones (same FP16 values, same scale), and only row ts is written to memory; otherwise
+  // the whole block is.
+  float scl[2] = {0.f, 0.f};  // the block's scales after the append
+  bool whole[2] = {false, false};
+  if (phys >= 0) {
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv) {
+      const float m_old = mx[kv], m_new = mx[2 + kv];
+      int8_t* tile = c.cold + tile_offset(phys, h, kv, H, S, D);
+      whole[kv] = !(ts > 0 && m_new <= m_old);
+      const float sc = (whole[kv] ? fmaxf(m_old, m_new) : m_old) / 127.0f;
+      scl[kv] = sc;
+      {
+        uint32_t* srow = reinterpret_cast<uint32_t*>(am.stage[kv] + t * LDS_ROW + part * CPT);
+        uint32_t qw[CPT / 4];
+#pragma unroll
+        for (int i = 0; i < CPT / 4; ++i) {
+          uint32_t packed = 0;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int e = 4 * i + k;
+            const uint32_t wd = x[kv][e / 8][(e % 8) / 2];
+            const float xv = (e & 1) ? half_hi(wd) : half_lo(wd);
+            const float qv = sc > 0.f ? fminf(127.f, fmaxf(-127.f, __builtin_rintf(xv / sc))) : 0.f;
+            packed |= (static_cast<uint32_t>(static_cast<int>(qv)) & 0xffu) << (8 * k);
+          }
+          qw[i] = packed;
+          srow[i] = packed;
+        }
+        if (!whole[kv] && t == ts) {  // only row ts changes: write it in place
+          if (kv == 0) {
+#pragma unroll
+            for (int ch = 0; ch < CPT / 16; ++ch)
+              reinterpret_cast<uint4*>(tile)[((part * CPT) / 16 + ch) * S + t] =
+                  make_uint4(qw[4 * ch], qw[4 * ch + 1], qw[4 * ch + 2], qw[4 * ch + 3]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < CPT; ++i)
+              tile[((t / 16) * D + part * CPT + i) * 16 + (t % 16)] = static_cast<int8_t>(qw[i / 4] >> (8 * (i % 4)));
+          }
+        }
+      }
+    }
+    __syncthreads();  // stage complete
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv) {
+      if (!whole[kv]) continue;
+      int8_t* tile = c.cold + tile_offset(phys, h, kv, H, S, D);
+      constexpr int NVEC = S * D / 16;
+      for (int vi = tid; vi < NVEC; vi += kThreads) {
+        uint4 out;
+        if (kv == 0) {
+          const int dc = vi / S, tt = vi % S;
+          out = *reinterpret_cast<const uint4*>(am.stage[0] + tt * LDS_ROW + dc * 16);
+        } else {
+          const int tc = vi / D, cc = vi % D;
+          uint32_t wv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            uint32_t acc = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              acc |= static_cast<uint32_t>(static_cast<uint8_t>(am.stage[1][(tc * 16 + i * 4 + k) * LDS_ROW + cc])) << (8 * k);
+            wv[i] = acc;
+          }
+          out = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        }
+        reinterpret_cast<uint4*>(tile)[vi] = out;
+      }
+      if (tid == 0) c.scales[(static_cast<size_t>(phys) * H + h) * 2 + kv] = scl[kv];
+    }
+    if (h == 0 && tid == 0) {
+      hkv_block_header* hdr = c.headers + static_cast<size_t>(b) * c.max_blocks + jt;
+      hdr->n_valid = ts + 1;
+      hdr->logical_block = jt;
+      hdr->flags = 0u;
+    }
+  }
+  // FP16 shadow row of the still-partial block, and the new token into its ring slot
+  if (spill && ts + 1 < S && t == ts) {
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv) {
+      u32x4_t* dst = reinterpret_cast<u32x4_t*>(c.tail + ((bhs * 2 + kv) * S + t) * D + part * CPT);
+#pragma unroll
+      for (int v = 0; v < NV; ++v) dst[v] = x[kv][v];
+    }
+  }
+  if (tid < 2 * VR)
+    reinterpret_cast<u32x4_t*>(c.hot + ((bhs * T + slot) * 2 + tid / VR) * D)[tid % VR] = nr;
+
+  // ---- tail block jt, rows [0, ts], by wave 0 with the cold-unit code
+  if (w == 0) {
+    float um[NG], ul[NG], ubias[NG];
+    float4_t uacc[C::NQ][C::NDL];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      um[g] = kNegInf;
+      ul[g] = 0.f;
+      ubias[g] = 0.f;
+    }
+#pragma unroll
+    for (int quad = 0; quad < C::NQ; ++quad)
+#pragma unroll
+      for (int ps2 = 0; ps2 < C::NDL; ++ps2) uacc[quad][ps2] = float4_t{0.f, 0.f, 0.f, 0.f};
+    if (phys >= 0) {
+      // tile registers: K (lane = token) and V (lane = channel), from the codes in LDS
+      Tiles<D> tl;
+#pragma unroll
+      for (int ch = 0; ch < D / 16; ++ch) tl.kr[ch] = *reinterpret_cast<const uint4*>(am.stage[0] + lane * LDS_ROW + ch * 16);
+#pragma unroll
+      for (int ps2 = 0; ps2 < C::NDL; ++ps2) {
+        const int ch = 64 * ps2 + lane;
+#pragma unroll
+        for (int tc = 0; tc < 4; ++tc) {
+          uint32_t wv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            uint32_t acc = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              acc |= static_cast<uint32_t>(static_cast<uint8_t>(am.stage[1][(tc * 16 + i * 4 + k) * LDS_ROW + ch])) << (8 * k);
+            wv[i] = acc;
+          }
+          tl.vr[ps2][tc] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        }
+      }
+      WaveState<D, G> st;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        st.m[g] = kNegInf;
+        st.l[g] = 0.f;
+        st.pb[g] = 0.f;
+        float qs = 0.f;
+#pragma unroll
+        for (int k = lane; k < D; k += 64) qs += static_cast<float>(am.unit.qh[g / 4][g % 4][k]);
+        st.qb[g] = kCodeBias * wave_sum_dpp(qs);
+      }
+#pragma unroll
+      for (int quad = 0; quad < C::NQ; ++quad)
+#pragma unroll
+        for (int ps2 = 0; ps2 < C::NDL; ++ps2) st.acc[quad][ps2] = float4_t{0.f, 0.f, 0.f, 0.f};
+      float4_t sq[C::NQ];
+      qk_codes<D, G>(tl.kr, am.unit, lane, sq);
+      float alpha[NG], coef[NG];
+      softmax_unit<D, G, false>(st, am.unit, sq, lane <= ts, scl[0] * p.qscale, 1.f, scl[1], alpha, coef, 0, lane);
+      BlockAcc<D, G> blk;
+      pv_dense<D, G>(blk, am.unit, tl.vr, 0, lane);
+      fold_block<D, G>(st, blk, alpha, coef);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        um[g] = st.m[g];
+        ul[g] = wave_sum_dpp(st.l[g]);
+        ubias[g] = kCodeBias * wave_sum_dpp(st.pb[g]);
+      }
+#pragma unroll
+      for (int quad = 0; quad < C::NQ; ++quad)
+#pragma unroll
+        for (int ps2 = 0; ps2 < C::NDL; ++ps2) uacc[quad][ps2] = st.acc[quad][ps2];
+    }
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+      if (lane == 0) {
+        am.unit.wm[0][g] = um[g];
+        am.unit.wl[0][g] = ul[g];
+      }
+#pragma unroll
+    for (int quad = 0; quad < C::NQ; ++quad)
+#pragma unroll
+      for (int ps2 = 0; ps2 < C::NDL; ++ps2)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          am.unit.wacc[0][4 * quad + r][64 * ps2 + lane] = uacc[quad][ps2][r] - ubias[4 * quad + r];
+  }
+  __syncthreads();
+  for (int i = tid; i < G * (D / 2); i += kThreads) {
+    const int g = i / (D / 2), d = 2 * (i % (D / 2));
+    float* pg = partial_ptr<D>(p, bh, p.nsplit + 1, g);
+    store_coherent2(pg + 2 + d, am.unit.wacc[0][g][d], am.unit.wacc[0][g][d + 1]);
+    if (d == 0) store_coherent2(pg, am.unit.wm[0][g], am.unit.wl[0][g]);
   }
 }
 
@@ -701,18 +1021,21 @@ __device__ void hot_split(const DecodeParams& p, HotSmem<D, G>& hm, int b, int h
 // the workspace, which the merging workgroup resets to zero.  The merge runs
 // online over groups of kMergeChunk partials whose loads are all in flight
 // together; thread i owns two adjacent output columns of one query head.
-template <int D, int G, bool SPARSE>
+template <int D, int G, bool SPARSE, bool FUSED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G > 4 ? 2 : 4))) void decode_kernel(DecodeParams p) {
+  using AppendPart = typename std::conditional<FUSED, AppendSmem<D, G>, DecodeSmem<D, G>>::type;
   __shared__ union Smem {
     DecodeSmem<D, G> cold;
     HotSmem<D, G> hot;
+    AppendPart app;
   } sm;
   __shared__ int s_last;
   // grid (split, kv-head, sequence): no index depends on a kernel argument, and every argument the
   // kernel uses is consumed here, so its scalar loads are issued together and waited for once
   asm volatile("" ::"s"(p.c.H), "s"(p.c.T), "s"(p.c.max_blocks), "s"(p.c.num_phys), "s"(p.c.hot), "s"(p.c.cold),
                "s"(p.c.scales), "s"(p.c.headers), "s"(p.c.seq_len), "s"(p.q), "s"(p.sel), "s"(p.k_sel),
-               "s"(p.partials), "s"(p.counters), "s"(p.nsplit), "s"(p.units_per_split), "s"(p.qscale));
+               "s"(p.partials), "s"(p.counters), "s"(p.nsplit), "s"(p.nparts), "s"(p.units_per_split),
+               "s"(p.qscale));
   const CacheView& c = p.c;
   const int split = blockIdx.x;
   const int h = blockIdx.y;
@@ -720,7 +1043,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G > 4 
   const int bh = b * c.H + h;
   const int tid = threadIdx.x;
   if (split < p.nsplit) {
-    cold_split<D, G, SPARSE>(p, sm.cold, b, h, bh, split);
+    cold_split<D, G, SPARSE, FUSED>(p, sm.cold, b, h, bh, split);
+  } else if constexpr (FUSED) {
+    if (split == p.nsplit) hot_window_split<D, G>(p, sm.hot, b, h, bh);
+    else append_unit_split<D, G>(p, sm.app, b, h, bh);
   } else {
     hot_split<D, G>(p, sm.hot, b, h, bh);
   }
@@ -728,15 +1054,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G > 4 
   // last workgroup merge
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  const int NS = p.nsplit + (FUSED ? 2 : 1);  // partials of this (sequence, kv-head)
   if (tid == 0)
     s_last = __hip_atomic_fetch_add(&p.counters[bh], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             static_cast<unsigned>(p.nsplit);
+             static_cast<unsigned>(NS - 1);
   __syncthreads();
   if (!s_last) return;
-  const int NS = p.nsplit + 1;
   const int Hq = c.H * G;
   constexpr int REC = G * (D + 2);  // floats per split record of one (sequence, kv-head)
-  const float* base_bh = p.partials + static_cast<size_t>(bh) * NS * REC;
+  const float* base_bh = p.partials + static_cast<size_t>(bh) * p.nparts * REC;
   for (int idx = tid; idx < G * (D / 2); idx += kThreads) {
     const int g = idx / (D / 2), d = 2 * (idx % (D / 2));
     const int off_ml = g * (D + 2), off_a = off_ml + 2 + d;  // per lane; the split offset is uniform
@@ -778,6 +1104,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G > 4 
     if (d == 0 && p.lse) p.lse[static_cast<size_t>(b) * Hq + hq] = (M + __builtin_log2f(L)) * kLn2;
   }
   if (tid == 0) __hip_atomic_store(&p.counters[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if constexpr (FUSED) {
+    // every workgroup of (b, h) has read seq_len[b] before this merge; the last of the H merges
+    // of sequence b publishes the new length (and resets the counter)
+    if (tid == 0 &&
+        __hip_atomic_fetch_add(&p.seq_counters[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            static_cast<unsigned>(c.H - 1)) {
+      __hip_atomic_store(&c.seq_len[b], c.seq_len[b] + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&p.seq_counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 }
 
 template <typename K>
@@ -793,9 +1129,10 @@ hipError_t launch_k(K kernel, dim3 grid, int block, const DecodeParams& p, const
 
 template <int D, int G>
 hipError_t launch_dg(const DecodeParams& p, const LaunchCtx& ctx) {
-  const dim3 grid(p.nsplit + 1, p.c.H, p.c.B);  // (split, kv-head, sequence)
-  return p.sel ? launch_k(decode_kernel<D, G, true>, grid, kThreads, p, ctx)
-               : launch_k(decode_kernel<D, G, false>, grid, kThreads, p, ctx);
+  const dim3 grid(p.nparts, p.c.H, p.c.B);  // (split, kv-head, sequence)
+  if (p.k_new) return launch_k(decode_kernel<D, G, false, true>, grid, kThreads, p, ctx);
+  return p.sel ? launch_k(decode_kernel<D, G, true, false>, grid, kThreads, p, ctx)
+               : launch_k(decode_kernel<D, G, false, false>, grid, kThreads, p, ctx);
 }
 
 template <int D>

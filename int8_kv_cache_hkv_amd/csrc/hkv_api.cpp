@@ -120,10 +120,14 @@ size_t partials_bytes(const hkv_ctx* h, const hkv_cache_desc* c, int G, int k_se
   const int64_t bh = static_cast<int64_t>(c->batch) * h->H;
   int ns = max_splits(bh, std::max<int64_t>(1, c->max_blocks_per_seq));
   if (k_sel > 0) ns = std::max(ns, max_splits(bh, (k_sel + 63) / 64));
-  return static_cast<size_t>(bh) * (ns + 1) * G * (h->D + 2) * sizeof(float);
+  // ns cold splits + the hot zone (+ the tail block of a fused append)
+  return static_cast<size_t>(bh) * (ns + 2) * G * (h->D + 2) * sizeof(float);
 }
 
-size_t counters_bytes(const hkv_cache_desc* c, int H) { return static_cast<size_t>(c->batch) * H * sizeof(unsigned); }
+// arrival counters: [B*H] per (sequence, kv-head), then [B] per sequence (fused append + decode)
+size_t counters_bytes(const hkv_cache_desc* c, int H) {
+  return static_cast<size_t>(c->batch) * (H + 1) * sizeof(unsigned);
+}
 
 size_t topk_bytes(const hkv_ctx* h, const hkv_cache_desc* c) {
   return static_cast<size_t>(c->batch) * h->H * c->max_blocks_per_seq * h->S * sizeof(float);
@@ -328,12 +332,66 @@ hkv_status hkv_decode_attn(hkv_handle h, const hkv_cache_desc* c, const void* q,
   p.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(counters_bytes(c, h->H), 256));
   const SplitPlan sp = plan_splits(static_cast<int64_t>(c->batch) * h->H, units_max);
   p.nsplit = sp.nsplit;
+  p.nparts = sp.nsplit + 1;
   p.units_per_split = sp.per_split;
   p.qscale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(h->D)));
   p.out = static_cast<_Float16*>(out);
   p.lse = lse;
+  p.k_new = p.v_new = nullptr;
+  p.seq_counters = nullptr;
   LaunchCtx a = make_ctx(h, stream, sel_idx ? HKV_KERNEL_DECODE_SPARSE : HKV_KERNEL_DECODE);
   return hip_status(hkv::launch_decode(p, a), "hkv_decode_attn launch");
+}
+
+hkv_status hkv_append_decode(hkv_handle h, const hkv_cache_desc* c, const void* k_new, const void* v_new,
+                             const void* q, int n_q_heads, void* out, float* lse, void* workspace, size_t ws_bytes,
+                             hipStream_t stream) {
+  hkv_status st = check_desc(h, c);
+  if (st != HKV_OK) return st;
+  if (!k_new || !v_new || !q || !out) return HKV_ERR_NULL_POINTER;
+  if (n_q_heads < 1 || n_q_heads % h->H != 0) return HKV_ERR_INVALID_VALUE;
+  const int G = n_q_heads / h->H;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return HKV_ERR_UNSUPPORTED;
+  if (h->S != hkv::kBlockSize) return HKV_ERR_UNSUPPORTED;
+  int64_t units_max = 1;
+  for (int b = 0; b < c->batch; ++b) {
+    const int64_t n0 = c->seq_len_host[b];
+    if (n0 < 0) return HKV_ERR_INVALID_VALUE;
+    if (n0 + 1 > INT32_MAX) return HKV_ERR_CAPACITY;
+    if (cold_blocks(n0 + 1, h->T, h->S) > c->max_blocks_per_seq) return HKV_ERR_CAPACITY;
+    // cold units of the decode: the full blocks before the one the appended token spills into
+    units_max = std::max<int64_t>(units_max, std::max<int64_t>(0, n0 - h->T) / h->S);
+  }
+  size_t need = 0;
+  if (hkv_workspace_bytes(h, c, n_q_heads, 0, &need) != HKV_OK) return HKV_ERR_INVALID_VALUE;
+  if (!workspace || ws_bytes < need) return HKV_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0 || reinterpret_cast<uintptr_t>(q) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(k_new) % 16 != 0 || reinterpret_cast<uintptr_t>(v_new) % 16 != 0)
+    return HKV_ERR_ALIGNMENT;
+
+  hkv::DecodeParams p;
+  p.c = view_of(h, c);
+  p.G = G;
+  p.q = static_cast<const _Float16*>(q);
+  p.sel = nullptr;
+  p.k_sel = 0;
+  p.counters = static_cast<unsigned*>(workspace);
+  p.seq_counters = p.counters + static_cast<size_t>(c->batch) * h->H;
+  p.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(counters_bytes(c, h->H), 256));
+  const SplitPlan sp = plan_splits(static_cast<int64_t>(c->batch) * h->H, units_max);
+  p.nsplit = sp.nsplit;
+  p.nparts = sp.nsplit + 2;
+  p.units_per_split = sp.per_split;
+  p.qscale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(h->D)));
+  p.out = static_cast<_Float16*>(out);
+  p.lse = lse;
+  p.k_new = static_cast<const _Float16*>(k_new);
+  p.v_new = static_cast<const _Float16*>(v_new);
+  LaunchCtx a = make_ctx(h, stream, HKV_KERNEL_APPEND_DECODE);
+  const hkv_status r = hip_status(hkv::launch_decode(p, a), "hkv_append_decode launch");
+  if (r != HKV_OK) return r;
+  for (int b = 0; b < c->batch; ++b) c->seq_len_host[b] += 1;
+  return HKV_OK;
 }
 
 hkv_status hkv_topk_select(hkv_handle h, const hkv_cache_desc* c, const void* q, int n_q_heads, int k,

@@ -54,13 +54,18 @@ struct DecodeParams {
   const _Float16* q;       // [B][H*G][D]
   const int32_t* sel;      // sparse mode: [B][H][k_sel]; nullptr for dense
   int k_sel;
-  float* partials;         // [B][H][nsplit + 1][G][D + 2]  (m in log2 units, l, acc[D]); last = hot zone
+  float* partials;         // [B][H][nparts][G][D + 2]  (m in log2 units, l, acc[D]); then hot zone, tail block
   unsigned* counters;      // [B*H] arrival counters, zero between calls
   int nsplit;              // cold splits per (sequence, kv-head)
+  int nparts;              // partial records per (sequence, kv-head): nsplit + 1 (hot zone), + 1 more fused
   int units_per_split;     // units handled per split (multiple of kWaves)
   float qscale;            // log2(e) / sqrt(D)
   _Float16* out;           // [B][H*G][D]
   float* lse;              // [B][H*G] or nullptr
+  // fused single-token append (hkv_append_decode); nullptr for a plain decode
+  const _Float16* k_new;   // [B][H][D]
+  const _Float16* v_new;   // [B][H][D]
+  unsigned* seq_counters;  // [B] merged-head counters, zero between calls
 };
 
 struct TopkParams {

@@ -159,6 +159,19 @@ def test_decode_and_topk_host_errors():
         assert lib.hkv_decode_attn(h, d, q, 32, None, 0, out, None, ws, 16, None) == WORKSPACE
         assert lib.hkv_decode_attn(h, d, q, 32, None, 0, out, None, None, big, None) == WORKSPACE
         assert lib.hkv_decode_attn(h, d, None, 32, None, 0, out, None, ws, big, None) == NULLP
+        ad = lib.hkv_append_decode
+        assert ad(h, d, q, q, q, 30, out, None, ws, big, None) == INVALID        # 30 % 8
+        assert ad(h, d, q, q, q, 24, out, None, ws, big, None) == UNSUPPORTED    # G = 3
+        assert ad(h, d, None, q, q, 32, out, None, ws, big, None) == NULLP
+        assert ad(h, d, q, q, None, 32, out, None, ws, big, None) == NULLP
+        assert ad(h, d, q, q, q, 32, out, None, ws, 16, None) == WORKSPACE
+        assert ad(h, d, q + 8, q, q, 32, out, None, ws, big, None) == ALIGN
+        fc.lens[1] = 32 + 4 * 64        # full: the appended token needs a fifth cold block
+        assert ad(h, d, q, q, q, 32, out, None, ws, big, None) == CAPACITY
+        assert fc.lens.tolist() == [3, 32 + 4 * 64]   # the mirror is untouched on error
+        fc.lens[1] = -1
+        assert ad(h, d, q, q, q, 32, out, None, ws, big, None) == INVALID
+        fc.lens[1] = 5
         assert lib.hkv_topk_select(h, d, q, 32, 0, out, ws, big, None) == INVALID
         assert lib.hkv_topk_select(h, d, q, 32, 513, out, ws, big, None) == INVALID
         assert lib.hkv_topk_select(h, d, q, 32, 512, out, ws, 16, None) == WORKSPACE

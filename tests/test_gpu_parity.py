@@ -168,6 +168,89 @@ def test_ragged_config_parity():
         gh.compare_out(out[seqs], o_ref, f"ragged step {step}")
 
 
+# ------------------------------------------------------------------ fused one-token append + decode
+def _step_tokens(w, cur):
+    """The token at position cur[b] of every sequence b: K and V fp16 [B, H, D]."""
+    kb = np.stack([wl.tokens(w, b, cur[b], 1, "k")[0] for b in range(len(cur))])
+    vb = np.stack([wl.tokens(w, b, cur[b], 1, "v")[0] for b in range(len(cur))])
+    return kb, vb
+
+
+def _append_decode(cache, w, cur, q_np):
+    torch = gh.torch_mod()
+    kb, vb = _step_tokens(w, cur)
+    q = gh.upload(q_np)
+    out = torch.empty_like(q)
+    lse_t = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    cache.append_decode(gh.upload(kb), gh.upload(vb), q, out=out, lse=lse_t)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse_t.cpu().numpy()
+
+
+@pytest.mark.parametrize("n0", [0, 5, 31, 32, 33, 40, 95, 96, 97, 159, 160, 161, 287, 300])
+def test_append_decode_small(n0):
+    """One fused step from lengths where the hot zone is not full, where the spilled token opens a
+    block, lands inside one (maximum kept or raised) or completes one."""
+    w = wl.WORKLOADS["tiny"]
+    cache = gh.make_cache(w, 400)
+    gh.fill(cache, w, [n0])
+    q = wl.queries(w, step=n0)
+    out, lse = _append_decode(cache, w, [n0], q)
+    st = _oracle_states(w, [n0 + 1])
+    gh.check_state(cache, st)
+    o_ref, l_ref = orc.decode(q[0], st[0])
+    gh.compare_out(out[0], o_ref, f"fused n0={n0} out")
+    gh.compare_lse(lse[0], l_ref, f"fused n0={n0}")
+
+
+def test_append_decode_ragged_steps():
+    """16 fused steps over the ragged paged batch (permuted physical blocks): cache state and output
+    against the oracle after every step."""
+    w = wl.WORKLOADS["ragged"]
+    lens = [int(x) for x in wl.lengths(w)]
+    steps = 16
+    cap = max(lens) + steps + 64
+    mb = -(-(cap - w.hot_tokens) // w.block_size)
+    n_phys = w.batch * mb
+    perm = wl.block_permutation(w, n_phys).reshape(w.batch, mb)
+    cache = gh.make_cache(w, cap, phys_ids=perm)
+    gh.fill(cache, w, lens)
+    watch = [0, 1, int(np.argmax(lens)), int(np.argmin(lens))]
+    for step in range(steps):
+        cur = [n + step for n in lens]
+        q = wl.queries(w, step=step)
+        out, _ = _append_decode(cache, w, cur, q)
+        full = step in (0, steps - 1)
+        seqs = list(range(w.batch)) if full else watch
+        st = _oracle_states(w, [cur[b] + 1 for b in seqs], seqs)
+        gh.check_state(cache, st, seqs)
+        o_ref = np.stack([orc.decode(q[b], s)[0] for b, s in zip(seqs, st)])
+        gh.compare_out(out[seqs], o_ref, f"fused ragged step {step}")
+
+
+def test_append_decode_equals_separate_calls():
+    """The fused step leaves the same cache bytes as hkv_append + hkv_decode_attn, and the outputs
+    agree (different split plans: equal to the tolerance, not bitwise)."""
+    w = wl.WORKLOADS["llama8b"]
+    n0 = w.context - 1
+    a = gh.make_cache(w, n0 + 8)
+    b = gh.make_cache(w, n0 + 8)
+    gh.fill(a, w, [n0] * w.batch)
+    gh.fill(b, w, [n0] * w.batch)
+    q = wl.queries(w, step=3)
+    out_f, lse_f = _append_decode(a, w, [n0] * w.batch, q)
+    gh.fill(b, w, [n0 + 1] * w.batch, start=[n0] * w.batch)
+    out_s, lse_s = _decode(b, q)
+    assert np.array_equal(a.cold_codes(), b.cold_codes())
+    assert np.array_equal(a.scale_array(), b.scale_array())
+    assert np.array_equal(a.header_array(), b.header_array())
+    assert np.array_equal(a.hot_array(), b.hot_array())
+    assert np.array_equal(a.tail.cpu().numpy(), b.tail.cpu().numpy())
+    assert np.array_equal(a.seq_len.cpu().numpy(), b.seq_len.cpu().numpy())
+    gh.compare_out(out_f.astype(np.float64), out_s.astype(np.float64), "fused vs separate")
+    assert np.max(np.abs(lse_f - lse_s)) <= gh.LSE_MAX_ABS
+
+
 # ------------------------------------------------------------------ long context, sampled
 def test_long_config_parity_sampled():
     w = wl.WORKLOADS["long"]
