@@ -29,6 +29,22 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+
+# HBM bytes per launch of the fused llama8b-step kernel from hardware counters: FETCH_SIZE x 2.000 +
+# WRITE_SIZE x 1.000 (KiB per dispatch; the factors make a 256 MiB elementwise copy read and write
+# exactly its size), recorded in profiles/decode_kernel_llama8b_hbm_traffic.md.  Valid only for the
+# kernel sources they were measured on: reported as null once those sources change.
+COUNTER_TRAFFIC = {"sources_sha256": "148c0c7375910181d9d2924ffd6c9a8253fe1ceb4ca9b197e38bd7bae1c21285", "bytes_per_launch": 39953408}
+KERNEL_SOURCES = ("decode.hip", "hkv_device.h", "hkv_internal.h")
+
+
+def counter_traffic():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "int8_kv_cache_hkv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return COUNTER_TRAFFIC["bytes_per_launch"] if h.hexdigest() == COUNTER_TRAFFIC["sources_sha256"] else None
 METRIC = "decode-attn KV GB/s (% of HBM peak) + decode queries/sec, hybrid INT8/FP16"
 
 
@@ -357,7 +373,7 @@ def main():
         "kernel_ms": main_leg["kernel_ms"],
         "roofline": {"kernel": "decode_kernel (fused append + decode)", "bound": "hbm",
                      "achieved": round(achieved, 1) if achieved else None, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None, "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None, "traffic": counter_traffic(),
                      "bytes_per_launch": int(main_leg["kernel_bytes"]),
                      "avg_launch_ms": kms},
     }
