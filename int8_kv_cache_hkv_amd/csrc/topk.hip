@@ -13,8 +13,8 @@
 //                       copies (lane = token), |code|^2 from an integer dot4;
 //                       then the wave does the window softmax and stores p.
 //   topk_select_kernel  one 1024-thread workgroup per (sequence, kv-head):
-//                       4-pass 8-bit radix select of the K-th largest p (as
-//                       fp32 bit patterns, order-preserving for p >= 0), then
+//                       3-pass (11/10/10-bit) radix select of the K-th largest
+//                       p (fp32 bit patterns, order-preserving for p >= 0), then
 //                       an index-ordered block-scan compaction that takes
 //                       every p above the threshold and the lowest-index ties,
 //                       so the output is ascending and deterministic.
@@ -140,9 +140,155 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total
   return excl;
 }
 
+// Radix select over the key bits [30:0] (keys are fp32 bit patterns of
+// probabilities >= 0, so bit 31 is 0 and integer order is value order), in
+// three passes of 11, 10 and 10 bits from the top.  Window probabilities share
+// their exponent, so a first digit of exponent + 3 mantissa bits still spreads
+// them over dozens of bins (8-bit digits put most keys into two or three bins
+// and serialise the LDS atomics).
+constexpr int kSelPasses = 3;
+__device__ __forceinline__ int sel_shift(int pass) { return pass == 0 ? 20 : (pass == 1 ? 10 : 0); }
+__device__ __forceinline__ int sel_bins(int pass) { return pass == 0 ? 2048 : 1024; }
+constexpr int kSelMaxBins = 2048;
+
+// After a histogram pass: the digit of the krem-th largest key among those
+// matching `prefix`, scanning bins from the top digit down (thread t owns the
+// bins nb-1-t*bpt ... nb-t*bpt-bpt, in descending order).
+__device__ __forceinline__ void radix_pick(const unsigned* hist, int nb, int* wsum, unsigned* s_prefix,
+                                           unsigned* s_krem, unsigned prefix, unsigned krem, int shift) {
+  const int tid = threadIdx.x;
+  const int bpt = nb / kSelThreads;  // 1 or 2
+  const int top = nb - 1 - tid * bpt;
+  int local = 0;
+  for (int i = 0; i < bpt; ++i) local += static_cast<int>(hist[top - i]);
+  int total;
+  unsigned before = static_cast<unsigned>(block_exclusive_scan(local, wsum, &total));  // keys above my bins
+  for (int i = 0; i < bpt; ++i) {
+    const unsigned v = hist[top - i];
+    // the digit whose keys contain the krem-th largest: before < krem <= before + v (unique); the
+    // lowest digit takes whatever is left
+    if ((before < krem && krem <= before + v) || (top - i == 0 && before < krem && krem > before + v)) {
+      *s_prefix = prefix | (static_cast<unsigned>(top - i) << shift);
+      *s_krem = krem - before;
+    }
+    before += v;
+  }
+  __syncthreads();
+}
+
+// Rows of up to KPT * 1024 keys: every key is loaded into registers once
+// (thread t holds keys [t*KPT, t*KPT + KPT), so its indices are contiguous and
+// in order), the radix passes run from the registers, and the ordered
+// compaction needs two block scans.  Longer rows stream the keys from memory
+// on every pass (select_streaming).
+constexpr int kSelKPT = 32;
+
+__device__ void select_registers(const unsigned* keys, int n, int K, int32_t* out, unsigned* hist, int* wsum,
+                                 unsigned* s_prefix, unsigned* s_krem) {
+  constexpr int KPT = kSelKPT;
+  const int tid = threadIdx.x;
+  const int i0 = tid * KPT;
+  unsigned key[KPT];
+  if (i0 + KPT <= n) {
+    const u32x4_t* kv = reinterpret_cast<const u32x4_t*>(keys + i0);  // 16-byte aligned: i0 % 32 == 0
+#pragma unroll
+    for (int v = 0; v < KPT / 4; ++v) {
+      const u32x4_t x = kv[v];
+      key[4 * v] = x.x;
+      key[4 * v + 1] = x.y;
+      key[4 * v + 2] = x.z;
+      key[4 * v + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) key[k] = i0 + k < n ? keys[i0 + k] : 0u;
+  }
+  const int nv = max(0, min(KPT, n - i0));  // valid keys of this thread
+  // ---- radix select: the K-th largest key (tau) and how many keys equal to it to take
+  unsigned prefix = 0, mask = 0, krem = static_cast<unsigned>(K);
+  for (int pass = 0; pass < kSelPasses; ++pass) {
+    const int shift = sel_shift(pass), nb = sel_bins(pass);
+    for (int i = tid; i < nb; i += kSelThreads) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < KPT; ++k)
+      if (k < nv && (key[k] & mask) == prefix) atomicAdd(&hist[(key[k] >> shift) & static_cast<unsigned>(nb - 1)], 1u);
+    __syncthreads();
+    radix_pick(hist, nb, wsum, s_prefix, s_krem, prefix, krem, shift);
+    prefix = *s_prefix;
+    krem = *s_krem;
+    mask |= static_cast<unsigned>(nb - 1) << shift;
+    __syncthreads();  // every thread has read the pick before the next pass clears the histogram
+  }
+  const unsigned tau = prefix;
+  const int need_eq = static_cast<int>(krem);
+  // ---- ordered compaction: every key above tau, and the lowest-index need_eq keys equal to it
+  int gt = 0, eq = 0;
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    gt += (k < nv && key[k] > tau) ? 1 : 0;
+    eq += (k < nv && key[k] == tau) ? 1 : 0;
+  }
+  int eq_total;
+  const int eq_before = block_exclusive_scan(eq, wsum, &eq_total);
+  const int eq_take = max(0, min(eq, need_eq - eq_before));
+  int sel_total;
+  int pos = block_exclusive_scan(gt + eq_take, wsum, &sel_total);
+  int eq_seen = 0;
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    if (k >= nv) continue;
+    const bool is_eq = key[k] == tau;
+    const bool take = key[k] > tau || (is_eq && eq_seen < eq_take);
+    if (is_eq) ++eq_seen;
+    if (take) {
+      if (pos < K) out[pos] = i0 + k;
+      ++pos;
+    }
+  }
+}
+
+__device__ void select_streaming(const unsigned* keys, int n, int K, int32_t* out, unsigned* hist, int* wsum,
+                                 unsigned* s_prefix, unsigned* s_krem) {
+  const int tid = threadIdx.x;
+  unsigned prefix = 0, mask = 0, krem = static_cast<unsigned>(K);
+  for (int pass = 0; pass < kSelPasses; ++pass) {
+    const int shift = sel_shift(pass), nb = sel_bins(pass);
+    for (int i = tid; i < nb; i += kSelThreads) hist[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < n; i += kSelThreads) {
+      const unsigned key = keys[i];
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & static_cast<unsigned>(nb - 1)], 1u);
+    }
+    __syncthreads();
+    radix_pick(hist, nb, wsum, s_prefix, s_krem, prefix, krem, shift);
+    prefix = *s_prefix;
+    krem = *s_krem;
+    mask |= static_cast<unsigned>(nb - 1) << shift;
+    __syncthreads();
+  }
+  const unsigned tau = prefix;
+  const int need_eq = static_cast<int>(krem);
+  int carry_sel = 0, carry_eq = 0;
+  for (int base = 0; base < n; base += kSelThreads) {
+    const int i = base + tid;
+    const unsigned key = i < n ? keys[i] : 0u;
+    const int is_eq = (i < n && key == tau) ? 1 : 0;
+    const int is_gt = (i < n && key > tau) ? 1 : 0;
+    int eq_total;
+    const int eq_excl = block_exclusive_scan(is_eq, wsum, &eq_total);
+    const int take = (is_gt || (is_eq && carry_eq + eq_excl < need_eq)) ? 1 : 0;
+    int sel_total;
+    const int sel_excl = block_exclusive_scan(take, wsum, &sel_total);
+    if (take && carry_sel + sel_excl < K) out[carry_sel + sel_excl] = i;
+    carry_eq += eq_total;
+    carry_sel += sel_total;
+  }
+}
+
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkParams p) {
   constexpr int S = kBlockSize;
-  __shared__ unsigned hist[256];
+  __shared__ unsigned hist[kSelMaxBins];
   __shared__ int wsum[kSelThreads / 64 + 1];
   __shared__ unsigned s_prefix, s_krem;
   const CacheView& c = p.c;
@@ -160,50 +306,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkParams p) 
     for (int i = tid; i < K; i += kSelThreads) out[i] = i < n ? i : -1;
     return;
   }
-  // ---- radix select: the K-th largest key and how many copies of it to take
-  unsigned prefix = 0, mask = 0, krem = static_cast<unsigned>(K);
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    if (tid < 256) hist[tid] = 0u;
-    __syncthreads();
-    for (int i = tid; i < n; i += kSelThreads) {
-      const unsigned key = keys[i];
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (tid == 0) {
-      unsigned cum = 0;
-      int dgt = 255;
-      for (; dgt > 0; --dgt) {
-        if (cum + hist[dgt] >= krem) break;
-        cum += hist[dgt];
-      }
-      s_prefix = prefix | (static_cast<unsigned>(dgt) << shift);
-      s_krem = krem - cum;
-    }
-    __syncthreads();
-    prefix = s_prefix;
-    krem = s_krem;
-    mask |= 255u << shift;
-    __syncthreads();
-  }
-  const unsigned tau = prefix;
-  const int need_eq = static_cast<int>(krem);
-  // ---- ordered compaction in token order
-  int carry_sel = 0, carry_eq = 0;
-  for (int base = 0; base < n; base += kSelThreads) {
-    const int i = base + tid;
-    const unsigned key = i < n ? keys[i] : 0u;
-    const int is_eq = (i < n && key == tau) ? 1 : 0;
-    const int is_gt = (i < n && key > tau) ? 1 : 0;
-    int eq_total;
-    const int eq_excl = block_exclusive_scan(is_eq, wsum, &eq_total);
-    const int take = (is_gt || (is_eq && carry_eq + eq_excl < need_eq)) ? 1 : 0;
-    int sel_total;
-    const int sel_excl = block_exclusive_scan(take, wsum, &sel_total);
-    if (take && carry_sel + sel_excl < K) out[carry_sel + sel_excl] = i;
-    carry_eq += eq_total;
-    carry_sel += sel_total;
-  }
+  if (n <= kSelKPT * kSelThreads) select_registers(keys, n, K, out, hist, wsum, &s_prefix, &s_krem);
+  else select_streaming(keys, n, K, out, hist, wsum, &s_prefix, &s_krem);
 }
 
 template <typename Kf>

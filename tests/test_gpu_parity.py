@@ -275,7 +275,9 @@ def test_long_config_parity_sampled():
 
 
 # ------------------------------------------------------------------ top-K and sparse decode
-@pytest.mark.parametrize("n,k", [(32 + 100, 128), (32 + 300, 50), (32 + 64 * 9 + 17, 100), (20, 16)])
+@pytest.mark.parametrize("n,k", [(32 + 100, 128), (32 + 300, 50), (32 + 64 * 9 + 17, 100), (20, 16),
+                                 # rows at and just past the register-resident selection limit (32768 keys)
+                                 (32 + 32768, 512), (32 + 32769, 512), (32 + 40007, 300)])
 def test_topk_small(n, k):
     w = wl.WORKLOADS["tiny"]
     cache = gh.make_cache(w, n + 64)
