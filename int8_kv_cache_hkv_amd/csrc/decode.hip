@@ -223,6 +223,75 @@ __device__ __forceinline__ void qk_codes(const uint4 (&kr)[D / 16], const Decode
 }
 
 // ---------------------------------------------------------------- dense units
+// QK of a dense unit with progressive refill: as soon as chunk ch of the K tile
+// has been turned into MFMA operands, its registers receive chunk ch of the
+// next unit's K tile (rn; an empty descriptor when there is none), so the next
+// tile is requested chunk by chunk while this one is consumed.
+template <int D, int G>
+__device__ __forceinline__ void qk_codes_refill(uint4 (&kr)[D / 16], const DecodeSmem<D, G>& sm, int lane,
+                                                float4_t (&s)[Cfg<D, G>::NQ], __amdgpu_buffer_rsrc_t rn) {
+  using C = Cfg<D, G>;
+  constexpr int S = kBlockSize;
+  const uint32_t lo = static_cast<uint32_t>(lane) * 16u;
+  asm volatile("" ::: "memory");
+  float4_t s2[C::NQ];
+#pragma unroll
+  for (int quad = 0; quad < C::NQ; ++quad) s[quad] = s2[quad] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ch = 0; ch < D / 16; ++ch) {
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int wd = 0; wd < 4; ++wd) {
+      const half4_t b = codes_to_biased_half4(word_of(kr[ch], wd));
+      const int k0 = ch * 16 + wd * 4;
+#pragma unroll
+      for (int quad = 0; quad < C::NQ; ++quad) {
+        if (wd & 1) s2[quad] = mfma_qk(q_operand(sm, quad, lane, k0), b, s2[quad]);
+        else s[quad] = mfma_qk(q_operand(sm, quad, lane, k0), b, s[quad]);
+      }
+    }
+    kr[ch] = load_stream_buf(rn, lo + ch * S * 16);
+  }
+#pragma unroll
+  for (int quad = 0; quad < C::NQ; ++quad) s[quad] += s2[quad];
+  asm volatile("" ::: "memory");
+}
+
+// PV of a dense unit with progressive refill: once the last word of a 16-token
+// column chunk has been used, its registers receive the same chunk of the next
+// unit's V tile.
+template <int D, int G>
+__device__ __forceinline__ void pv_dense_refill(BlockAcc<D, G>& blk, const DecodeSmem<D, G>& sm,
+                                                uint4 (&vr)[Cfg<D, G>::NDL][4], int w, int lane,
+                                                __amdgpu_buffer_rsrc_t rn) {
+  using C = Cfg<D, G>;
+  constexpr int S = kBlockSize;
+  const uint32_t lo = static_cast<uint32_t>(lane) * 16u;
+  zero_blk<D, G>(blk);
+#pragma unroll
+  for (int t0 = 0; t0 < 64; t0 += 4) {
+    asm volatile("" ::: "memory");
+    uint32_t vw[C::NDL];
+#pragma unroll
+    for (int ps = 0; ps < C::NDL; ++ps) vw[ps] = word_of(vr[ps][t0 / 16], (t0 % 16) / 4);
+    pv_step<D, G>(blk, sm, vw, t0, w, lane);
+    if (t0 % 16 == 12) {
+#pragma unroll
+      for (int ps = 0; ps < C::NDL; ++ps)
+        vr[ps][t0 / 16] = load_stream_buf(rn, lo + S * D + ((t0 / 16) * D + 64 * ps) * 16);
+    }
+  }
+  asm volatile("" ::: "memory");
+}
+
+// The two scales (K, V) of a block; phys < 0 reads 0.  The offset is kept per
+// lane so the wave does not wait for the load right after issuing it.
+__device__ __forceinline__ float2 load_scales(__amdgpu_buffer_rsrc_t rs, int phys, int H, int h) {
+  const int so = static_cast<int>(opaque_index(static_cast<uint32_t>((phys * H + h) * 8)));
+  const int o = phys < 0 ? -8 : so;
+  return make_float2(__builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, o, 0, 0)),
+                     __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, o, 4, 0)));
+}
 // One dense unit's tiles in registers.
 template <int D>
 struct Tiles {
@@ -360,15 +429,14 @@ __device__ void dense_units(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const Dec
   int phys_n = un >= 0 ? phys_of(k + 1) : -1;
   while (u >= 0) {
     const int nv = phys_u >= 0 ? min(S, n_cold - u * S) : 0;
-    float4_t s[C::NQ];
-    qk_codes<D, G>(t.kr, sm, lane, s);
     const __amdgpu_buffer_rsrc_t rn = tile_rsrc<D>(c, phys_n, h);  // empty when there is no next unit
-    issue_k<D>(t, rn, lane);
+    float4_t s[C::NQ];
+    qk_codes_refill<D, G>(t.kr, sm, lane, s, rn);
     float alpha[C::NG], coef[C::NG];
     softmax_unit<D, G, false>(st, sm, s, lane < nv, sc.x * p.qscale, 1.f, sc.y, alpha, coef, w, lane);
+    sc = load_scales(rs, phys_n, c.H, h);  // the scale pair is free once the softmax has used it
     BlockAcc<D, G> blk;
-    pv_dense<D, G>(blk, sm, t.vr, w, lane);
-    issue_v<D>(t, sc, rn, rs, phys_n, c.H, h, lane);
+    pv_dense_refill<D, G>(blk, sm, t.vr, w, lane, rn);
     fold_block<D, G>(st, blk, alpha, coef);
     wave_lds_sync();  // this unit's weight reads are done before the next unit's writes
     u = un;

@@ -57,11 +57,12 @@ struct SplitPlan {
   int nsplit;
   int per_split;
 };
-SplitPlan plan_splits(int64_t bh, int64_t units) {
+SplitPlan plan_splits(int64_t bh, int64_t units, int extra_parts = 1) {
   units = std::max<int64_t>(1, units);
-  // all of a launch's workgroups (cold splits + one hot workgroup per (sequence, kv-head)) should be
-  // resident at once: a straggler that starts late delays the merge of its (sequence, kv-head)
-  int64_t target = std::max<int64_t>(1, kTargetWorkgroups / bh - 1);
+  // all of a launch's workgroups (cold splits + the extra_parts other workgroups of each (sequence,
+  // kv-head): hot zone, and the tail block of a fused append) should be resident at once: a straggler
+  // that starts late delays the merge of its (sequence, kv-head)
+  int64_t target = std::max<int64_t>(1, kTargetWorkgroups / bh - extra_parts);
   int64_t per = hkv::kWaves * ((units + hkv::kWaves * target - 1) / (hkv::kWaves * target));
   int64_t ns = (units + per - 1) / per;
   if (ns > kMaxSplits) {
@@ -378,7 +379,7 @@ hkv_status hkv_append_decode(hkv_handle h, const hkv_cache_desc* c, const void* 
   p.counters = static_cast<unsigned*>(workspace);
   p.seq_counters = p.counters + static_cast<size_t>(c->batch) * h->H;
   p.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(counters_bytes(c, h->H), 256));
-  const SplitPlan sp = plan_splits(static_cast<int64_t>(c->batch) * h->H, units_max);
+  const SplitPlan sp = plan_splits(static_cast<int64_t>(c->batch) * h->H, units_max, 2);
   p.nsplit = sp.nsplit;
   p.nparts = sp.nsplit + 2;
   p.units_per_split = sp.per_split;
