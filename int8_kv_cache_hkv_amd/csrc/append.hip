@@ -109,6 +109,7 @@ __global__ __launch_bounds__(kThreads) void append_quant_kernel(AppendParams p) 
     for (int w = 1; w < kWaves; ++w) m = fmaxf(m, red[w]);
     // ---- s = fl32(m / 127): IEEE fp32 division (correctly rounded)
     const float s = m / 127.0f;
+    const float rs = __builtin_amdgcn_rcpf(s);
     // ---- codes = clamp(rint(fl32(x / s)), -127, 127), round half to even
     int8_t* srow = stage + t * LDS_ROW + part * CPT;
 #pragma unroll
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void append_quant_kernel(AppendParams p) 
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         float qv = 0.f;
-        if (s > 0.f) qv = fminf(127.f, fmaxf(-127.f, __builtin_rintf(x[i + k] / s)));
+        if (s > 0.f) qv = quant_code(x[i + k], s, rs);
         packed |= (static_cast<uint32_t>(static_cast<int>(qv)) & 0xffu) << (8 * k);
       }
       *reinterpret_cast<uint32_t*>(srow + i) = packed;
@@ -296,8 +297,9 @@ __global__ __launch_bounds__(kThreads) void append_step_kernel(AppendParams p) {
       for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(half_lo(x[v][i])), fabsf(half_hi(x[v][i]))));
     return m;
   };
-  // codes of one row slice with scale s (IEEE division, round half to even, clamp)
+  // codes of one row slice with scale s (as the IEEE division gives them, round half to even, clamp)
   auto code_slice = [&](const u32x4_t (&x)[NV], float s, uint32_t (&q)[CPT / 4]) {
+    const float rs = __builtin_amdgcn_rcpf(s);
 #pragma unroll
     for (int i = 0; i < CPT / 4; ++i) {
       uint32_t packed = 0;
@@ -307,7 +309,7 @@ __global__ __launch_bounds__(kThreads) void append_step_kernel(AppendParams p) {
         const uint32_t wd = x[e / 8][(e % 8) / 2];
         const float xv = (e & 1) ? half_hi(wd) : half_lo(wd);
         float qv = 0.f;
-        if (s > 0.f) qv = fminf(127.f, fmaxf(-127.f, __builtin_rintf(xv / s)));
+        if (s > 0.f) qv = quant_code(xv, s, rs);
         packed |= (static_cast<uint32_t>(static_cast<int>(qv)) & 0xffu) << (8 * k);
       }
       q[i] = packed;

@@ -796,11 +796,12 @@ __device__ void hot_split(const DecodeParams& p, HotSmem<D, G>& hm, int b, int h
 //     unchanged, else the whole block from its FP16 tail-shadow rows); the
 //     tail shadow, the header and the ring slot are written.  The block's tile
 //     registers for the attention come from this workgroup's own codes in LDS
-//     (whole block re-coded) or from a tile load patched with the new row, so
-//     nothing waits for the code stores.  The cold splits cover only the full
-//     blocks before jt.
+//     (every row is coded there; with an unchanged maximum they equal the
+//     stored codes), so nothing waits for the code stores.  The cold splits
+//     cover only the full blocks before jt.
 template <int D, int G>
 __device__ void hot_window_split(const DecodeParams& p, HotSmem<D, G>& hm, int b, int h, int bh) {
+  __builtin_amdgcn_s_setprio(3);  // short, latency-bound work: issue ahead of the streaming waves
   const int n0 = __builtin_amdgcn_readfirstlane(p.c.seq_len[b]);
   const int slot = n0 % p.c.T;
   const size_t bhs = static_cast<size_t>(bh);
@@ -815,19 +816,24 @@ __device__ void hot_window_split(const DecodeParams& p, HotSmem<D, G>& hm, int b
 
 template <int D, int G>
 struct AppendSmem {
-  DecodeSmem<D, G> unit;                                  // tail block jt, attended by wave 0
-  alignas(16) int8_t stage[2][kBlockSize * (D + 16)];     // its K and V codes, [token][channel]
+  static constexpr int KROW = D + 16;          // K stage row: one token's channels (padded)
+  static constexpr int VROW = kBlockSize + 16; // V stage row: one channel's tokens (padded)
+  DecodeSmem<D, G> unit;                       // tail block jt, attended by wave 0
+  alignas(16) int8_t stage_k[kBlockSize * KROW];  // its K codes, [token][channel]
+  alignas(16) int8_t stage_v[D * VROW];           // its V codes, [channel][token] (the tile's order)
   float red[4][kWaves];
 };
 
 template <int D, int G>
 __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G>& am, int b, int h, int bh) {
+  __builtin_amdgcn_s_setprio(3);  // the append's coding and its block's attention sit on the step's critical path
   using C = Cfg<D, G>;
   constexpr int S = kBlockSize;
   constexpr int TPT = kThreads / S;     // threads per token row
   constexpr int CPT = D / TPT;          // channels per thread
   constexpr int NV = CPT / 8;           // 16-byte vectors per thread and row
-  constexpr int LDS_ROW = D + 16;
+  constexpr int KROW = AppendSmem<D, G>::KROW;
+  constexpr int VROW = AppendSmem<D, G>::VROW;
   constexpr int VR = D / 8;             // 16-byte vectors per fp16 row
   constexpr int NG = C::NG;
   const CacheView& c = p.c;
@@ -897,10 +903,10 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G>& am, i
     mx[i] = r;
   }
 
-  // ---- codes of block jt (as the standalone append codes them).  Every row is coded into
-  // stage[kv] for the attention below: with an unchanged maximum the old rows' codes are the
-  // stored ones (same FP16 values, same scale), and only row ts is written to memory; otherwise
-  // the whole block is.
+  // ---- codes of block jt (as the standalone append codes them).  Every row is coded into the
+  // stage for the attention below: with an unchanged maximum the old rows' codes are the stored
+  // ones (same FP16 values, same scale), and only row ts is written to memory; otherwise the
+  // whole block is.  V codes are staged channel-major, as the tile stores them.
   float scl[2] = {0.f, 0.f};  // the block's scales after the append
   bool whole[2] = {false, false};
   if (phys >= 0) {
@@ -911,8 +917,8 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G>& am, i
       whole[kv] = !(ts > 0 && m_new <= m_old);
       const float sc = (whole[kv] ? fmaxf(m_old, m_new) : m_old) / 127.0f;
       scl[kv] = sc;
+      const float rsc = __builtin_amdgcn_rcpf(sc);
       {
-        uint32_t* srow = reinterpret_cast<uint32_t*>(am.stage[kv] + t * LDS_ROW + part * CPT);
         uint32_t qw[CPT / 4];
 #pragma unroll
         for (int i = 0; i < CPT / 4; ++i) {
@@ -922,11 +928,19 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G>& am, i
             const int e = 4 * i + k;
             const uint32_t wd = x[kv][e / 8][(e % 8) / 2];
             const float xv = (e & 1) ? half_hi(wd) : half_lo(wd);
-            const float qv = sc > 0.f ? fminf(127.f, fmaxf(-127.f, __builtin_rintf(xv / sc))) : 0.f;
+            const float qv = sc > 0.f ? quant_code(xv, sc, rsc) : 0.f;
             packed |= (static_cast<uint32_t>(static_cast<int>(qv)) & 0xffu) << (8 * k);
           }
           qw[i] = packed;
-          srow[i] = packed;
+        }
+        if (kv == 0) {
+          uint32_t* srow = reinterpret_cast<uint32_t*>(am.stage_k + t * KROW + part * CPT);
+#pragma unroll
+          for (int i = 0; i < CPT / 4; ++i) srow[i] = qw[i];
+        } else {
+#pragma unroll
+          for (int i = 0; i < CPT; ++i)
+            am.stage_v[(part * CPT + i) * VROW + t] = static_cast<int8_t>(qw[i / 4] >> (8 * (i % 4)));
         }
         if (!whole[kv] && t == ts) {  // only row ts changes: write it in place
           if (kv == 0) {
@@ -952,19 +966,10 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G>& am, i
         uint4 out;
         if (kv == 0) {
           const int dc = vi / S, tt = vi % S;
-          out = *reinterpret_cast<const uint4*>(am.stage[0] + tt * LDS_ROW + dc * 16);
+          out = *reinterpret_cast<const uint4*>(am.stage_k + tt * KROW + dc * 16);
         } else {
           const int tc = vi / D, cc = vi % D;
-          uint32_t wv[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            uint32_t acc = 0;
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-              acc |= static_cast<uint32_t>(static_cast<uint8_t>(am.stage[1][(tc * 16 + i * 4 + k) * LDS_ROW + cc])) << (8 * k);
-            wv[i] = acc;
-          }
-          out = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+          out = *reinterpret_cast<const uint4*>(am.stage_v + cc * VROW + tc * 16);
         }
         reinterpret_cast<uint4*>(tile)[vi] = out;
       }
@@ -1007,24 +1012,12 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G>& am, i
       // tile registers: K (lane = token) and V (lane = channel), from the codes in LDS
       Tiles<D> tl;
 #pragma unroll
-      for (int ch = 0; ch < D / 16; ++ch) tl.kr[ch] = *reinterpret_cast<const uint4*>(am.stage[0] + lane * LDS_ROW + ch * 16);
+      for (int ch = 0; ch < D / 16; ++ch) tl.kr[ch] = *reinterpret_cast<const uint4*>(am.stage_k + lane * KROW + ch * 16);
 #pragma unroll
-      for (int ps2 = 0; ps2 < C::NDL; ++ps2) {
-        const int ch = 64 * ps2 + lane;
+      for (int ps2 = 0; ps2 < C::NDL; ++ps2)
 #pragma unroll
-        for (int tc = 0; tc < 4; ++tc) {
-          uint32_t wv[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            uint32_t acc = 0;
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-              acc |= static_cast<uint32_t>(static_cast<uint8_t>(am.stage[1][(tc * 16 + i * 4 + k) * LDS_ROW + ch])) << (8 * k);
-            wv[i] = acc;
-          }
-          tl.vr[ps2][tc] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-        }
-      }
+        for (int tc = 0; tc < 4; ++tc)
+          tl.vr[ps2][tc] = *reinterpret_cast<const uint4*>(am.stage_v + (64 * ps2 + lane) * VROW + tc * 16);
       WaveState<D, G> st;
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
@@ -1128,6 +1121,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G > 4 
              static_cast<unsigned>(NS - 1);
   __syncthreads();
   if (!s_last) return;
+  __builtin_amdgcn_s_setprio(3);  // the merge ends the (sequence, kv-head): ahead of streaming waves
   const int Hq = c.H * G;
   constexpr int REC = G * (D + 2);  // floats per split record of one (sequence, kv-head)
   const float* base_bh = p.partials + static_cast<size_t>(bh) * p.nparts * REC;

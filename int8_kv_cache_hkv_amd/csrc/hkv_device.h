@@ -101,6 +101,19 @@ __device__ __forceinline__ uint4 load_stream_buf(__amdgpu_buffer_rsrc_t r, uint3
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// INT8 code of x under scale s > 0 (r = __builtin_amdgcn_rcpf(s)): clamp(rint(fl32(x / s)), -127,
+// 127) with round half to even, the same value the IEEE fp32 division gives, at the cost of a
+// multiply.  y = fl32(x * r) differs from the rounded quotient fl32(x / s) by at most |x / s| * 2^-21
+// (v_rcp_f32 is within 1 ulp, plus two roundings), i.e. by less than 2^-14 for |x| <= 127 s.  So
+// rint(y) is the code unless y lies within 2^-13 of a half-integer (probability about 2^-12 per
+// element); those elements take the division.
+__device__ __forceinline__ float quant_code(float x, float s, float r) {
+  const float y = x * r;
+  float k = __builtin_rintf(y);
+  if (__builtin_fabsf(0.5f - __builtin_fabsf(y - k)) <= 0x1p-13f) k = __builtin_rintf(x / s);
+  return fminf(127.f, fmaxf(-127.f, k));
+}
+
 // Sequence geometry derived from the cached length.
 struct SeqGeom {
   int n, n_hot, n_cold, n_blk;
