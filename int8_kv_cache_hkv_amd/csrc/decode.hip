@@ -67,7 +67,6 @@ struct DecodeSmem {
   float wm[kWaves][C::NG];
   float wl[kWaves][C::NG];
   alignas(16) float wacc[kWaves][C::NG][D];
-  long long voff[kWaves][64];                         // sparse mode: byte offset of each selected token's V column
 };
 
 template <int D, int G>
@@ -450,41 +449,58 @@ __device__ void dense_units(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const Dec
 }
 
 // ---------------------------------------------------------------- sparse units
-// Up to 64 selected cold tokens, one gathered row per lane.  For PV, lane c
-// needs the value code of every selected token at channel c: the tokens'
-// V-tile offsets go through LDS and the byte loads of 16 tokens are issued
-// together, so the unit pays four memory latencies, not 64.  Each token has
-// its own block scales: the logit scale is per lane, and the value weight is
-// taken relative to the largest V scale of the unit (vcoef).
+// Up to kSparseUnit selected cold tokens, one per lane (lanes past the unit are
+// masked).  Once the tokens' physical blocks are known, all of the unit's
+// memory traffic is issued in one round: the K rows and block scales (lane =
+// token) and, for PV, the value codes of every token at the lane's channels
+// (lane c: channels c and 64 + c), read through a per-token buffer descriptor
+// that is empty for a masked token.  Each token has its own block scales: the
+// logit scale is per lane, and the value weight is taken relative to the
+// largest V scale of the unit (vcoef).
+// The lane's selection entry of a sparse unit (-1 past the unit or the list).
+__device__ __forceinline__ int sel_entry(const int32_t* sel_bh, int k_sel, int unit, int lane) {
+  const int e = unit * kSparseUnit + lane;
+  return (lane < kSparseUnit && e < k_sel) ? sel_bh[e] : -1;
+}
+
+// idx: the lane's selection entry (sel_entry of this unit).
 template <int D, int G>
-__device__ void gather_unit(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const CacheView& c, const int32_t* sel_bh,
-                            int k_sel, int b, int h, int chunk, int n_cold, float qscale, int w, int lane) {
+__device__ void gather_unit(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const CacheView& c, int idx, int b, int h,
+                            int n_cold, float qscale, int w, int lane) {
   using C = Cfg<D, G>;
   constexpr int S = kBlockSize;
-  constexpr int TB = 16;  // tokens whose value bytes are loaded together
-  const int e = chunk * 64 + lane;
-  const int idx = e < k_sel ? sel_bh[e] : -1;
+  constexpr int TU = kSparseUnit;
+  static_assert(TU % 4 == 0 && TU <= 64, "whole PV steps of 4 tokens, one token per lane");
   int phys = -1;
   if (idx >= 0 && idx < n_cold) {
     const int j = idx / S;
     if (j < c.max_blocks) phys = c.headers[static_cast<size_t>(b) * c.max_blocks + j].phys_block;
   }
   const bool valid = phys >= 0 && phys < c.num_phys;
+  if (__ballot(valid) == 0) return;  // no token: the state is unchanged (also: num_phys may be 0)
   const int t = valid ? idx % S : 0;
-  float2 sc = make_float2(0.f, 0.f);
+  // K row and scales of the lane's token; a masked lane reads block 0 (present: some token is
+  // valid) and its values are discarded
+  const int pl = valid ? phys : 0;
+  const uint4* tk = reinterpret_cast<const uint4*>(c.cold + tile_offset(pl, h, 0, c.H, S, D));
   uint4 kr[D / 16];
-  if (valid) {
-    sc = *reinterpret_cast<const float2*>(c.scales + (static_cast<size_t>(phys) * c.H + h) * 2);
-    const uint4* tk = reinterpret_cast<const uint4*>(c.cold + tile_offset(phys, h, 0, c.H, S, D));
 #pragma unroll
-    for (int ch = 0; ch < D / 16; ++ch) kr[ch] = tk[ch * S + t];
-  } else {
+  for (int ch = 0; ch < D / 16; ++ch) kr[ch] = tk[ch * S + t];
+  const float2 scl = *reinterpret_cast<const float2*>(c.scales + (static_cast<size_t>(pl) * c.H + h) * 2);
+  // value codes: token k of the unit at channel 64 ps + lane
+  const int pm = valid ? phys : -1;
+  uint32_t vb[TU][C::NDL];
 #pragma unroll
-    for (int ch = 0; ch < D / 16; ++ch) kr[ch] = make_uint4(0, 0, 0, 0);
+  for (int k = 0; k < TU; ++k) {
+    const int pk = __builtin_amdgcn_readlane(pm, k);
+    const int tt = __builtin_amdgcn_readlane(t, k);
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc<D>(c, pk, h);  // empty for a masked token: reads 0
+    const int o = S * D + (tt / 16) * D * 16 + tt % 16;
+#pragma unroll
+    for (int ps = 0; ps < C::NDL; ++ps)
+      vb[k][ps] = __builtin_amdgcn_raw_buffer_load_b8(r, o + (64 * ps + lane) * 16, 0, 0);
   }
-  // byte offset of (token, channel 0) in the cold pool, or -1 for a masked lane
-  sm.voff[w][lane] = valid ? static_cast<long long>(tile_offset(phys, h, 1, c.H, S, D)) + (t / 16) * D * 16 + (t % 16)
-                           : -1ll;
+  const float2 sc = valid ? scl : make_float2(0.f, 0.f);
   float4_t s[C::NQ];
   qk_codes<D, G>(kr, sm, lane, s);
   const float vmax = wave_max_dpp(sc.y);
@@ -493,24 +509,13 @@ __device__ void gather_unit(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const Cac
   softmax_unit<D, G, true>(st, sm, s, valid, sc.x * qscale, vw, vmax, alpha, coef, w, lane);
   BlockAcc<D, G> blk;
   zero_blk<D, G>(blk);
-  const int cnt = min(64, k_sel - chunk * 64);
-  for (int tb = 0; tb < cnt; tb += TB) {
-    uint32_t vb[TB][C::NDL];
 #pragma unroll
-    for (int k = 0; k < TB; ++k) {
-      const long long off = sm.voff[w][tb + k];  // uniform across the wave
+  for (int t0 = 0; t0 < TU; t0 += 4) {
+    uint32_t vw4[C::NDL];
 #pragma unroll
-      for (int ps = 0; ps < C::NDL; ++ps)
-        vb[k][ps] = off >= 0 ? static_cast<uint32_t>(reinterpret_cast<const uint8_t*>(c.cold)[off + (64 * ps + lane) * 16]) : 0u;
-    }
-#pragma unroll
-    for (int t0 = 0; t0 < TB; t0 += 4) {
-      uint32_t vw4[C::NDL];
-#pragma unroll
-      for (int ps = 0; ps < C::NDL; ++ps)
-        vw4[ps] = vb[t0][ps] | (vb[t0 + 1][ps] << 8) | (vb[t0 + 2][ps] << 16) | (vb[t0 + 3][ps] << 24);
-      pv_step<D, G>(blk, sm, vw4, tb + t0, w, lane);
-    }
+    for (int ps = 0; ps < C::NDL; ++ps)
+      vw4[ps] = vb[t0][ps] | (vb[t0 + 1][ps] << 8) | (vb[t0 + 2][ps] << 16) | (vb[t0 + 3][ps] << 24);
+    pv_step<D, G>(blk, sm, vw4, t0, w, lane);
   }
   fold_block<D, G>(st, blk, alpha, coef);
   wave_lds_sync();
@@ -584,7 +589,11 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
   Tiles<D> t0;
   float2 sc0 = make_float2(0.f, 0.f);
   int phys0 = -1, hb = -1;
-  if (!SPARSE) {
+  const int32_t* sel_bh = SPARSE ? p.sel + static_cast<size_t>(bh) * p.k_sel : nullptr;
+  int sel0 = -1;  // sparse: this wave's first unit's selection entry, requested with the query
+  if (SPARSE) {
+    sel0 = sel_entry(sel_bh, p.k_sel, split * p.units_per_split + w, lane);
+  } else {
     hb = header_batch(c, b, 0, split, p.nsplit, p.units_per_split, w, lane);
     phys0 = __builtin_amdgcn_readlane(hb, 0);
     const __amdgpu_buffer_rsrc_t r0 = tile_rsrc<D>(c, phys0, h);
@@ -601,8 +610,7 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
   const SeqGeom sg = seq_geom(__builtin_amdgcn_readfirstlane(n_seq_lane), c.T, S);
   // fused append: only the full blocks before the one the appended token spills into (n_cold is
   // the count before the append, so the block holding cold token n_cold is excluded)
-  const int units = sg.n_cold > 0 ? (SPARSE ? cdiv(p.k_sel, 64) : (FUSED ? sg.n_cold / S : sg.n_blk)) : 0;
-  const int32_t* sel_bh = SPARSE ? p.sel + static_cast<size_t>(bh) * p.k_sel : nullptr;
+  const int units = sg.n_cold > 0 ? (SPARSE ? cdiv(p.k_sel, kSparseUnit) : (FUSED ? sg.n_cold / S : sg.n_blk)) : 0;
 
   WaveState<D, G> st;
 #pragma unroll
@@ -624,8 +632,10 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
     const int CU = p.units_per_split;
     for (int run = split; run * CU < units; run += p.nsplit) {
       const int u_end = min(units, (run + 1) * CU);
-      for (int u = run * CU + w; u < u_end; u += kWaves)
-        gather_unit<D, G>(st, sm, c, sel_bh, p.k_sel, b, h, u, sg.n_cold, p.qscale, w, lane);
+      for (int u = run * CU + w; u < u_end; u += kWaves) {
+        const int idx = (run == split && u == run * CU + w) ? sel0 : sel_entry(sel_bh, p.k_sel, u, lane);
+        gather_unit<D, G>(st, sm, c, idx, b, h, sg.n_cold, p.qscale, w, lane);
+      }
     }
   } else {
     dense_units<D, G>(st, sm, p, b, h, split, units, sg.n_cold, w, lane, t0, phys0, sc0, hb);

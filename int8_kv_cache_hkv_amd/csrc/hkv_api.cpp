@@ -81,6 +81,14 @@ int max_splits(int64_t bh, int64_t units_cap) {
   return static_cast<int>(std::max<int64_t>(1, ns));
 }
 
+// Sparse decode: one unit of kSparseUnit selected tokens per wave, so every
+// gather chain of a call runs concurrently (k_sel <= kMaxTopK keeps this to a
+// few splits per (sequence, kv-head)).
+SplitPlan plan_sparse(int k_sel) {
+  const int units = std::max(1, (k_sel + hkv::kSparseUnit - 1) / hkv::kSparseUnit);
+  return {(units + hkv::kWaves - 1) / hkv::kWaves, hkv::kWaves};
+}
+
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 hkv_status check_desc(const hkv_ctx* h, const hkv_cache_desc* c) {
@@ -120,7 +128,7 @@ hkv::CacheView view_of(const hkv_ctx* h, const hkv_cache_desc* c) {
 size_t partials_bytes(const hkv_ctx* h, const hkv_cache_desc* c, int G, int k_sel) {
   const int64_t bh = static_cast<int64_t>(c->batch) * h->H;
   int ns = max_splits(bh, std::max<int64_t>(1, c->max_blocks_per_seq));
-  if (k_sel > 0) ns = std::max(ns, max_splits(bh, (k_sel + 63) / 64));
+  if (k_sel > 0) ns = std::max(ns, plan_sparse(k_sel).nsplit);
   // ns cold splits + the hot zone (+ the tail block of a fused append)
   return static_cast<size_t>(bh) * (ns + 2) * G * (h->D + 2) * sizeof(float);
 }
@@ -314,8 +322,7 @@ hkv_status hkv_decode_attn(hkv_handle h, const hkv_cache_desc* c, const void* q,
     const int n = c->seq_len_host[b];
     if (n == 0) return HKV_ERR_INVALID_VALUE;
     const int64_t nblk = cold_blocks(n, h->T, h->S);
-    const int64_t cold_units = sel_idx ? (nblk > 0 ? (k_sel + 63) / 64 : 0) : nblk;
-    units_max = std::max(units_max, cold_units);
+    if (!sel_idx) units_max = std::max(units_max, nblk);
   }
   size_t need = 0;
   if (hkv_workspace_bytes(h, c, n_q_heads, sel_idx ? k_sel : 0, &need) != HKV_OK) return HKV_ERR_INVALID_VALUE;
@@ -331,7 +338,7 @@ hkv_status hkv_decode_attn(hkv_handle h, const hkv_cache_desc* c, const void* q,
   p.k_sel = sel_idx ? k_sel : 0;
   p.counters = static_cast<unsigned*>(workspace);
   p.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(counters_bytes(c, h->H), 256));
-  const SplitPlan sp = plan_splits(static_cast<int64_t>(c->batch) * h->H, units_max);
+  const SplitPlan sp = sel_idx ? plan_sparse(k_sel) : plan_splits(static_cast<int64_t>(c->batch) * h->H, units_max);
   p.nsplit = sp.nsplit;
   p.nparts = sp.nsplit + 1;
   p.units_per_split = sp.per_split;

@@ -15,6 +15,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kAppendChunk = 256;   // sequences whose append counts travel in one kernel-argument block
 constexpr int kSinglePassMaxBlocks = 2;  // appends touching at most this many blocks per sequence use one launch
 constexpr int kMaxTopK = 512;       // fixed top-K budget of the sparse path
+constexpr int kSparseUnit = 16;     // selected tokens per wave unit of the sparse decode
 constexpr int kMaxSplits = 128;     // cold splits per (sequence, kv-head) at most
 
 // Per-launch timing: when start/stop are non-null the dispatch records them.

@@ -297,6 +297,28 @@ def test_topk_small(n, k):
         gh.compare_lse(lse[0], l_ref, "sparse")
 
 
+@pytest.mark.parametrize("k_sel", [1, 15, 16, 17, 37, 64, 100])
+def test_sparse_decode_explicit_indices(k_sel):
+    """Caller-built selections: ragged k_sel, -1 and out-of-range entries are ignored, duplicates count twice."""
+    w = wl.WORKLOADS["tiny"]
+    n = 32 + 64 * 5 + 9
+    cache = gh.make_cache(w, n + 64)
+    gh.fill(cache, w, [n])
+    st = _oracle_states(w, [n])[0]
+    q = wl.queries(w, step=5)
+    rng = np.random.default_rng(1000 + k_sel)
+    sel = rng.integers(0, st.n_cold, size=(1, w.n_kv_heads, k_sel)).astype(np.int32)
+    m = rng.random(sel.shape)
+    sel[m < 0.1] = -1
+    sel[(m >= 0.1) & (m < 0.14)] = st.n_cold + 7
+    sel[(m >= 0.14) & (m < 0.17)] = 2 ** 31 - 1
+    out, lse = _decode(cache, q, sel=gh.upload(sel), k_sel=k_sel)
+    ref_sel = np.where((sel[0] >= 0) & (sel[0] < st.n_cold), sel[0], -1)
+    o_ref, l_ref = orc.sparse_decode(q[0], st, ref_sel)
+    gh.compare_out(out[0], o_ref, f"sparse explicit k_sel={k_sel}")
+    gh.compare_lse(lse[0], l_ref, f"sparse explicit k_sel={k_sel}")
+
+
 def test_topk_ties_prefer_lower_index():
     """Identical keys tie exactly in fp32 too: the lowest token indices must be chosen."""
     torch = gh.torch_mod()
