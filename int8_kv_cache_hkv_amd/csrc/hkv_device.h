@@ -132,6 +132,29 @@ __device__ __forceinline__ size_t tile_offset(int phys, int h, int kv, int H, in
   return ((static_cast<size_t>(phys) * H + h) * 2 + kv) * static_cast<size_t>(S) * D;
 }
 
+// A wave's walk over its dense units: runs of CU = units_per_split units start
+// at split * CU and repeat every nsplit * CU; inside a run the wave takes every
+// 4th unit, CU / 4 of them.  Unit k of the walk (k = 0, 1, ...):
+__device__ __forceinline__ int walk_unit(int k, int split, int nsplit, int CU, int w) {
+  const int KR = CU / kWaves;
+  const int run = k / KR;
+  return (split + run * nsplit) * CU + w + kWaves * (k - run * KR);
+}
+
+// Physical blocks of walk units kb .. kb + 63, one per lane (-1 past the header
+// table or for an out-of-range id): one coalesced load serves 64 units, and
+// the walk reads them with readlane, so no header load waits inside the loop.
+__device__ __forceinline__ int header_batch(const CacheView& c, int b, int kb, int split, int nsplit, int CU, int w,
+                                            int lane) {
+  asm volatile("" : "+s"(CU));  // keeps the division by CU / 4 here (rarely executed), not hoisted and kept live
+  const int j = walk_unit(kb + lane, split, nsplit, CU, w);
+  const __amdgpu_buffer_rsrc_t rh =
+      make_rsrc(c.headers + static_cast<size_t>(b) * c.max_blocks, static_cast<uint32_t>(c.max_blocks) * 16u);
+  const bool in_table = j < c.max_blocks;
+  const int ph = __builtin_amdgcn_raw_buffer_load_b32(rh, in_table ? j * 16 : -1, 0, 0);  // phys_block at offset 0
+  return (in_table && ph >= 0 && ph < c.num_phys) ? ph : -1;
+}
+
 // ---------------------------------------------------------------- MFMA / DPP helpers
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {

@@ -6,7 +6,8 @@
 // 2.1: the cosine is computed in FP32, and the selection has a fixed width
 // max_K = 512 padded with a mask.
 //
-//   topk_score_kernel   one wave per cold block (window): lane t scores token
+//   topk_score_kernel   one wave per cold block (window), blocks streamed
+//                       through a software pipeline: lane t scores token
 //                       t as the mean over the kv-head's G query heads of
 //                       cos(q, code_t) (the block scale cancels in a cosine);
 //                       q.code comes from v_mfma_f32_4x4x4f16 on exact fp16
@@ -29,86 +30,140 @@ namespace detail {
 constexpr float kNegInfT = -__builtin_inff();
 constexpr int kSelThreads = 1024;
 
+// Window probabilities of one cold block from its K codes: kr[ch] holds codes
+// 16ch..16ch+15 of the lane's token.  As each chunk is consumed its registers
+// receive the same chunk of the next unit's K tile (rn; an empty descriptor
+// when there is none), so the next tile streams in while this one is scored.
+template <int D, int G>
+__device__ __forceinline__ float window_scores(uint4 (&kr)[D / 16], const _Float16 (*qh)[4][D + 8],
+                                               const float* qinv, int lane, int nv, __amdgpu_buffer_rsrc_t rn) {
+  constexpr int S = kBlockSize;
+  constexpr int NQ = (G + 3) / 4;
+  const uint32_t lo = static_cast<uint32_t>(lane) * 16u;
+  // dot(q_g, code_t) for the lane's token t (MFMA, exact products) and |code_t|^2 (integer dot4)
+  float4_t s[NQ];
+#pragma unroll
+  for (int quad = 0; quad < NQ; ++quad) s[quad] = float4_t{0.f, 0.f, 0.f, 0.f};
+  int n2 = 0;
+#pragma unroll
+  for (int ch = 0; ch < D / 16; ++ch) {
+    asm volatile("" ::: "memory");  // keep the chunks in order: each refill is issued right after its use
+#pragma unroll
+    for (int wd = 0; wd < 4; ++wd) {
+      const uint32_t word = word_of(kr[ch], wd);
+      n2 = __builtin_amdgcn_sdot4(static_cast<int>(word), static_cast<int>(word), n2, false);
+      const half4_t bk = codes_to_half4(word);
+      const int k0 = ch * 16 + wd * 4;
+#pragma unroll
+      for (int quad = 0; quad < NQ; ++quad)
+        s[quad] = mfma_qk(*reinterpret_cast<const half4_t*>(&qh[quad][lane & 3][k0]), bk, s[quad]);
+    }
+    kr[ch] = load_stream_buf(rn, lo + ch * S * 16);
+  }
+  asm volatile("" ::: "memory");
+  // c_t = mean over the G query heads of cos(q_g, code_t); cosine is scale-free, so codes suffice
+  const float kinv = n2 > 0 ? 1.f / __builtin_sqrtf(static_cast<float>(n2)) : 0.f;
+  float csum = 0.f;
+#pragma unroll
+  for (int quad = 0; quad < NQ; ++quad)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) csum += s[quad][r] * qinv[4 * quad + r];
+  const bool valid = lane < nv;
+  const float cs = valid ? (csum * kinv) / static_cast<float>(G) : kNegInfT;
+  // softmax inside the window (= this block's valid tokens)
+  const float mx = wave_max_dpp(cs);
+  const float e = valid ? exp2_approx((cs - mx) * kLog2e) : 0.f;
+  const float es = wave_sum_dpp(e);
+  return e / es;
+}
+
+// K tile of (phys, h) as a buffer resource (empty for phys < 0: loads read 0).
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t k_tile_rsrc(const CacheView& c, int phys, int h) {
+  const bool ok = phys >= 0;
+  return make_rsrc(c.cold + tile_offset(ok ? phys : 0, h, 0, c.H, kBlockSize, D), ok ? kBlockSize * D : 0u);
+}
+
+// Grid (split, kv-head, sequence).  Each wave walks its cold blocks (the same
+// walk as the decode's dense units); the first block's tile is requested with
+// the query, each next one while the current one is scored.
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void topk_score_kernel(TopkParams p) {
   constexpr int S = kBlockSize;
   constexpr int NQ = (G + 3) / 4;          // groups of 4 query heads (MFMA rows)
   constexpr int QROW = D + 8;              // padded fp16 query row
+  constexpr int VPR = D / 8;               // 16-byte vectors per query row
   __shared__ _Float16 qh[NQ][4][QROW];
   __shared__ float qinv[4 * NQ];           // 1 / |q_g| (0 for a zero query or a padding row)
+  asm volatile("" ::"s"(p.c.H), "s"(p.c.T), "s"(p.c.max_blocks), "s"(p.c.num_phys), "s"(p.c.cold),
+               "s"(p.c.headers), "s"(p.c.seq_len), "s"(p.q), "s"(p.prob), "s"(p.nsplit), "s"(p.units_per_split));
   const CacheView& c = p.c;
   const int H = c.H;
-  const int split = blockIdx.x % p.nsplit;
-  const int bh = blockIdx.x / p.nsplit;
-  const int h = bh % H;
-  const int b = bh / H;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int bh = b * H + h;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int CU = p.units_per_split;
+  // first memory round: query rows, the length and this wave's header batch; then the first tile
   const _Float16* qg = p.q + (static_cast<size_t>(b) * H * G + static_cast<size_t>(h) * G) * D;
-  for (int i = tid; i < 4 * NQ * D; i += kThreads) {
-    const int g = i / D, d = i % D;
-    qh[g / 4][g % 4][d] = g < G ? qg[g * D + d] : static_cast<_Float16>(0.f);
+  const int qi = tid < 4 * NQ * VPR ? tid : 0;
+  const bool q_ok = tid < G * VPR;
+  const u32x4_t qv = reinterpret_cast<const u32x4_t*>(qg)[q_ok ? qi : 0];
+  const int n_seq_lane = c.seq_len[opaque_index(b)];
+  int hb = header_batch(c, b, 0, split, p.nsplit, CU, w, lane);
+  int phys = __builtin_amdgcn_readlane(hb, 0);
+  uint4 kr[D / 16];
+  {
+    const __amdgpu_buffer_rsrc_t r0 = k_tile_rsrc<D>(c, phys, h);
+#pragma unroll
+    for (int ch = 0; ch < D / 16; ++ch) kr[ch] = load_stream_buf(r0, static_cast<uint32_t>(lane) * 16u + ch * S * 16);
   }
+  static_assert(4 * NQ * VPR <= kThreads, "one query vector per thread");
+  if (tid < 4 * NQ * VPR)
+    *reinterpret_cast<u32x4_t*>(&qh[qi / VPR / 4][qi / VPR % 4][(qi % VPR) * 8]) = q_ok ? qv : u32x4_t{0u, 0u, 0u, 0u};
   __syncthreads();
-  for (int g = w; g < 4 * NQ; g += kWaves) {  // query norms in fp32
-    float s2 = 0.f;
-    for (int d = lane; d < D; d += 64) {
-      const float x = static_cast<float>(qh[g / 4][g % 4][d]);
-      s2 = fmaf(x, x, s2);
+  if (w == 0) {  // query norms in fp32
+#pragma unroll
+    for (int g = 0; g < 4 * NQ; ++g) {
+      float s2 = 0.f;
+      for (int d = lane; d < D; d += 64) {
+        const float x = static_cast<float>(qh[g / 4][g % 4][d]);
+        s2 = fmaf(x, x, s2);
+      }
+      s2 = wave_sum_dpp(s2);
+      if (lane == 0) qinv[g] = (g < G && s2 > 0.f) ? 1.f / __builtin_sqrtf(s2) : 0.f;
     }
-    s2 = wave_sum(s2);
-    if (lane == 0) qinv[g] = (g < G && s2 > 0.f) ? 1.f / __builtin_sqrtf(s2) : 0.f;
   }
   __syncthreads();
 
-  const SeqGeom sg = seq_geom(c.seq_len[b], c.T, S);
+  const SeqGeom sg = seq_geom(__builtin_amdgcn_readfirstlane(n_seq_lane), c.T, S);
+  const int units = min(sg.n_blk, c.max_blocks);
   const size_t cap = static_cast<size_t>(c.max_blocks) * S;
   float* prob = p.prob + static_cast<size_t>(bh) * cap;
-  const int C = p.units_per_split;
-  for (int run = split; run * C < sg.n_blk; run += p.nsplit) {
-    const int u_end = min(sg.n_blk, (run + 1) * C);
-    for (int j = run * C + w; j < u_end; j += kWaves) {
-      if (j >= c.max_blocks) continue;
-      const int phys = c.headers[static_cast<size_t>(b) * c.max_blocks + j].phys_block;
-      if (phys < 0 || phys >= c.num_phys) continue;
-      const int nv = min(S, sg.n_cold - j * S);
-      const uint4* tk = reinterpret_cast<const uint4*>(c.cold + tile_offset(phys, h, 0, H, S, D));
-      uint4 kr[D / 16];
-#pragma unroll
-      for (int ch = 0; ch < D / 16; ++ch) kr[ch] = load_stream(tk + ch * S + lane);
-      asm volatile("" ::: "memory");
-      // dot(q_g, code_t) for the lane's token t (MFMA, exact products) and |code_t|^2 (integer dot4)
-      float4_t s[NQ];
-#pragma unroll
-      for (int quad = 0; quad < NQ; ++quad) s[quad] = float4_t{0.f, 0.f, 0.f, 0.f};
-      int n2 = 0;
-#pragma unroll
-      for (int ch = 0; ch < D / 16; ++ch) {
-#pragma unroll
-        for (int wd = 0; wd < 4; ++wd) {
-          const uint32_t word = word_of(kr[ch], wd);
-          n2 = __builtin_amdgcn_sdot4(static_cast<int>(word), static_cast<int>(word), n2, false);
-          const half4_t bk = codes_to_half4(word);
-          const int k0 = ch * 16 + wd * 4;
-#pragma unroll
-          for (int quad = 0; quad < NQ; ++quad)
-            s[quad] = mfma_qk(*reinterpret_cast<const half4_t*>(&qh[quad][lane & 3][k0]), bk, s[quad]);
-        }
-      }
-      // c_t = mean over the G query heads of cos(q_g, code_t); cosine is scale-free, so codes suffice
-      const float kinv = n2 > 0 ? 1.f / __builtin_sqrtf(static_cast<float>(n2)) : 0.f;
-      float csum = 0.f;
-#pragma unroll
-      for (int quad = 0; quad < NQ; ++quad)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) csum += s[quad][r] * qinv[4 * quad + r];
-      const bool valid = lane < nv;
-      const float cs = valid ? (csum * kinv) / static_cast<float>(G) : kNegInfT;
-      // softmax inside the window (= this block's valid tokens)
-      const float mx = wave_max_dpp(cs);
-      const float e = valid ? exp2_approx((cs - mx) * kLog2e) : 0.f;
-      const float es = wave_sum_dpp(e);
-      if (valid) prob[static_cast<size_t>(j) * S + lane] = e / es;
+  int kb = 0;  // walk index of lane 0 of the header batch
+  auto phys_of = [&](int k) -> int {
+    if (k - kb >= 64) {
+      kb = k;
+      hb = header_batch(c, b, kb, split, p.nsplit, CU, w, lane);
     }
+    return __builtin_amdgcn_readlane(hb, k - kb);
+  };
+  // the next unit's block id is looked up after this unit's refills are issued, so a header-batch
+  // refresh never makes the wave wait for them
+  int k = 0;
+  int u = walk_unit(0, split, p.nsplit, CU, w);
+  int un = walk_unit(1, split, p.nsplit, CU, w);
+  int phys_n = u < units && un < units ? phys_of(1) : -1;
+  while (u < units) {
+    const int nv = min(S, sg.n_cold - u * S);
+    const float pr = window_scores<D, G>(kr, qh, qinv, lane, nv, k_tile_rsrc<D>(c, phys_n, h));
+    // a block without a valid physical id contributes probability 0 (its tokens are never attended)
+    if (lane < nv) prob[static_cast<size_t>(u) * S + lane] = phys >= 0 ? pr : 0.f;
+    u = un;
+    phys = phys_n;
+    ++k;
+    un = walk_unit(k + 1, split, p.nsplit, CU, w);
+    phys_n = un < units ? phys_of(k + 1) : -1;
   }
 }
 
@@ -311,8 +366,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkParams p) 
 }
 
 template <typename Kf>
-hipError_t launch_t(Kf kernel, int grid, int block, const TopkParams& p, const LaunchCtx& ctx) {
-  if (grid <= 0) return hipSuccess;
+hipError_t launch_t(Kf kernel, dim3 grid, int block, const TopkParams& p, const LaunchCtx& ctx) {
+  if (grid.x == 0 || grid.y == 0 || grid.z == 0) return hipSuccess;
   if (ctx.start) {
     hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(block), 0, ctx.stream, ctx.start, ctx.stop, 0, p);
   } else {
@@ -323,9 +378,9 @@ hipError_t launch_t(Kf kernel, int grid, int block, const TopkParams& p, const L
 
 template <int D, int G>
 hipError_t launch_tg(const TopkParams& p, const LaunchCtx& a, const LaunchCtx& b) {
-  hipError_t e = launch_t(topk_score_kernel<D, G>, p.c.B * p.c.H * p.nsplit, kThreads, p, a);
+  hipError_t e = launch_t(topk_score_kernel<D, G>, dim3(p.nsplit, p.c.H, p.c.B), kThreads, p, a);
   if (e != hipSuccess) return e;
-  return launch_t(topk_select_kernel, p.c.B * p.c.H, kSelThreads, p, b);
+  return launch_t(topk_select_kernel, dim3(p.c.B * p.c.H), kSelThreads, p, b);
 }
 
 template <int D>
