@@ -179,20 +179,17 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total
   }
   if (lane == 63) wsum[w] = x;
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int i = 0; i < kSelThreads / 64; ++i) {
-      const int s = wsum[i];
-      wsum[i] = run;
-      run += s;
-    }
-    wsum[kSelThreads / 64] = run;
+  // every thread sums the wave totals itself (independent LDS reads, no serial pass)
+  int before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < kSelThreads / 64; ++i) {
+    const int s = wsum[i];
+    before += i < w ? s : 0;
+    all += s;
   }
-  __syncthreads();
-  const int excl = wsum[w] + x - v;
-  *total = wsum[kSelThreads / 64];
+  *total = all;
   __syncthreads();  // wsum is reused by the next scan
-  return excl;
+  return before + x - v;
 }
 
 // Radix select over the key bits [30:0] (keys are fp32 bit patterns of
@@ -205,6 +202,32 @@ constexpr int kSelPasses = 3;
 __device__ __forceinline__ int sel_shift(int pass) { return pass == 0 ? 20 : (pass == 1 ? 10 : 0); }
 __device__ __forceinline__ int sel_bins(int pass) { return pass == 0 ? 2048 : 1024; }
 constexpr int kSelMaxBins = 2048;
+// Histogram copies by lane % 16.  Window probabilities crowd into a handful of
+// bins, and the lanes of one LDS atomic that hit the same address are applied
+// one after another (measured: about 18 us for the first pass over 32768 keys
+// with a single copy).  With 16 copies, 4 banks apart, lanes that share a bin
+// mostly land on different addresses and banks.  The pick sums the copies.
+constexpr int kSelCopies = 16;
+constexpr int kSelStride = kSelMaxBins + 4;
+
+__device__ __forceinline__ unsigned* lane_hist(unsigned* hist) {
+  return hist + (threadIdx.x & (kSelCopies - 1)) * kSelStride;
+}
+
+// Zero the first nb bins (a power of two) of every copy, 16 bytes per store.
+__device__ __forceinline__ void clear_hist(unsigned* hist, int nb) {
+  const int lg = 29 - __builtin_clz(static_cast<unsigned>(nb));  // log2(nb / 4)
+  for (int i = threadIdx.x; i < kSelCopies * (nb >> 2); i += kSelThreads)
+    *reinterpret_cast<u32x4_t*>(hist + (i >> lg) * kSelStride + 4 * (i & ((nb >> 2) - 1))) = u32x4_t{0u, 0u, 0u, 0u};
+}
+
+// Count of bin i over the copies.
+__device__ __forceinline__ unsigned hist_bin(const unsigned* hist, int i) {
+  unsigned v = 0;
+#pragma unroll
+  for (int c = 0; c < kSelCopies; ++c) v += hist[c * kSelStride + i];
+  return v;
+}
 
 // After a histogram pass: the digit of the krem-th largest key among those
 // matching `prefix`, scanning bins from the top digit down (thread t owns the
@@ -215,18 +238,21 @@ __device__ __forceinline__ void radix_pick(const unsigned* hist, int nb, int* ws
   const int bpt = nb / kSelThreads;  // 1 or 2
   const int top = nb - 1 - tid * bpt;
   int local = 0;
-  for (int i = 0; i < bpt; ++i) local += static_cast<int>(hist[top - i]);
+  unsigned v[2] = {0u, 0u};
+  for (int i = 0; i < bpt; ++i) {
+    v[i] = hist_bin(hist, top - i);
+    local += static_cast<int>(v[i]);
+  }
   int total;
   unsigned before = static_cast<unsigned>(block_exclusive_scan(local, wsum, &total));  // keys above my bins
   for (int i = 0; i < bpt; ++i) {
-    const unsigned v = hist[top - i];
     // the digit whose keys contain the krem-th largest: before < krem <= before + v (unique); the
     // lowest digit takes whatever is left
-    if ((before < krem && krem <= before + v) || (top - i == 0 && before < krem && krem > before + v)) {
+    if ((before < krem && krem <= before + v[i]) || (top - i == 0 && before < krem && krem > before + v[i])) {
       *s_prefix = prefix | (static_cast<unsigned>(top - i) << shift);
       *s_krem = krem - before;
     }
-    before += v;
+    before += v[i];
   }
   __syncthreads();
 }
@@ -243,31 +269,66 @@ __device__ void select_registers(const unsigned* keys, int n, int K, int32_t* ou
   constexpr int KPT = kSelKPT;
   const int tid = threadIdx.x;
   const int i0 = tid * KPT;
-  unsigned key[KPT];
-  if (i0 + KPT <= n) {
-    const u32x4_t* kv = reinterpret_cast<const u32x4_t*>(keys + i0);  // 16-byte aligned: i0 % 32 == 0
+  // the row is read with coalesced 16-byte loads (vector v * 1024 + t by thread t) and handed over
+  // through LDS (rows padded to KPT + 1 words: conflict-free reads) to its owner, thread i / KPT;
+  // loading each thread's own 128 contiguous bytes directly makes every load instruction touch 64
+  // cache lines and thrashes the L1 (measured: about 6 us for a 32768-key row)
+  unsigned* stage = hist;
+  {
+    const u32x4_t* kv = reinterpret_cast<const u32x4_t*>(keys);  // 16-byte aligned: rows start at multiples of 64 keys
 #pragma unroll
     for (int v = 0; v < KPT / 4; ++v) {
-      const u32x4_t x = kv[v];
-      key[4 * v] = x.x;
-      key[4 * v + 1] = x.y;
-      key[4 * v + 2] = x.z;
-      key[4 * v + 3] = x.w;
-    }
-  } else {
+      const int vi = v * kSelThreads + tid;  // vector index: keys 4 vi .. 4 vi + 3
+      u32x4_t x;
+      if (4 * vi + 4 <= n) {
+        x = kv[vi];
+      } else {
 #pragma unroll
-    for (int k = 0; k < KPT; ++k) key[k] = i0 + k < n ? keys[i0 + k] : 0u;
+        for (int j = 0; j < 4; ++j) x[j] = 4 * vi + j < n ? keys[4 * vi + j] : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * vi + j;
+        stage[(i / KPT) * (KPT + 1) + i % KPT] = i < n ? x[j] + 1u : 0u;
+      }
+    }
   }
+  __syncthreads();
+  // keys are held as bit pattern + 1 (same order; bit 31 stays 0) and 0 past the row, so every
+  // test below against a floor or threshold >= 1 leaves the padding out without a per-key check
+  unsigned key[KPT];
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) key[k] = stage[tid * (KPT + 1) + k];
+  __syncthreads();  // the stage is the histogram's memory
   const int nv = max(0, min(KPT, n - i0));  // valid keys of this thread
+  // ---- a floor lo <= tau that most keys fall below: if at least K threads hold keys, the
+  // first-digit bin of the K-th largest per-thread maximum has K maxima at or above its lower
+  // edge, so at least K keys are >= lo and the K-th largest key is too.  Only keys >= lo take
+  // part in the radix passes (typically a few percent of the row).
+  unsigned lo = 1;
+  unsigned tmax = 0;
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) tmax = max(tmax, key[k]);
+  if (min(kSelThreads, cdiv(n, KPT)) >= K) {  // threads holding keys
+    clear_hist(hist, sel_bins(0));
+    __syncthreads();
+    if (nv > 0) atomicAdd(&lane_hist(hist)[tmax >> sel_shift(0)], 1u);
+    __syncthreads();
+    radix_pick(hist, sel_bins(0), wsum, s_prefix, s_krem, 0u, static_cast<unsigned>(K), sel_shift(0));
+    lo = max(1u, *s_prefix);
+    __syncthreads();  // every thread has read the pick before the histogram is cleared again
+  }
   // ---- radix select: the K-th largest key (tau) and how many keys equal to it to take
   unsigned prefix = 0, mask = 0, krem = static_cast<unsigned>(K);
   for (int pass = 0; pass < kSelPasses; ++pass) {
     const int shift = sel_shift(pass), nb = sel_bins(pass);
-    for (int i = tid; i < nb; i += kSelThreads) hist[i] = 0u;
+    clear_hist(hist, nb);
     __syncthreads();
+    unsigned* wh = lane_hist(hist);
 #pragma unroll
     for (int k = 0; k < KPT; ++k)
-      if (k < nv && (key[k] & mask) == prefix) atomicAdd(&hist[(key[k] >> shift) & static_cast<unsigned>(nb - 1)], 1u);
+      if (key[k] >= lo && (key[k] & mask) == prefix)
+        atomicAdd(&wh[(key[k] >> shift) & static_cast<unsigned>(nb - 1)], 1u);
     __syncthreads();
     radix_pick(hist, nb, wsum, s_prefix, s_krem, prefix, krem, shift);
     prefix = *s_prefix;
@@ -281,18 +342,18 @@ __device__ void select_registers(const unsigned* keys, int n, int K, int32_t* ou
   int gt = 0, eq = 0;
 #pragma unroll
   for (int k = 0; k < KPT; ++k) {
-    gt += (k < nv && key[k] > tau) ? 1 : 0;
-    eq += (k < nv && key[k] == tau) ? 1 : 0;
+    gt += key[k] > tau ? 1 : 0;
+    eq += key[k] == tau ? 1 : 0;
   }
-  int eq_total;
-  const int eq_before = block_exclusive_scan(eq, wsum, &eq_total);
+  // one scan of both counts (each total is at most 32768, so 16 bits apiece)
+  int both_total;
+  const int both_before = block_exclusive_scan((gt << 16) | eq, wsum, &both_total);
+  const int eq_before = both_before & 0xffff, gt_before = both_before >> 16;
   const int eq_take = max(0, min(eq, need_eq - eq_before));
-  int sel_total;
-  int pos = block_exclusive_scan(gt + eq_take, wsum, &sel_total);
+  int pos = gt_before + min(eq_before, need_eq);  // keys taken by the threads before this one
   int eq_seen = 0;
 #pragma unroll
   for (int k = 0; k < KPT; ++k) {
-    if (k >= nv) continue;
     const bool is_eq = key[k] == tau;
     const bool take = key[k] > tau || (is_eq && eq_seen < eq_take);
     if (is_eq) ++eq_seen;
@@ -309,11 +370,12 @@ __device__ void select_streaming(const unsigned* keys, int n, int K, int32_t* ou
   unsigned prefix = 0, mask = 0, krem = static_cast<unsigned>(K);
   for (int pass = 0; pass < kSelPasses; ++pass) {
     const int shift = sel_shift(pass), nb = sel_bins(pass);
-    for (int i = tid; i < nb; i += kSelThreads) hist[i] = 0u;
+    clear_hist(hist, nb);
     __syncthreads();
+    unsigned* wh = lane_hist(hist);
     for (int i = tid; i < n; i += kSelThreads) {
       const unsigned key = keys[i];
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & static_cast<unsigned>(nb - 1)], 1u);
+      if ((key & mask) == prefix) atomicAdd(&wh[(key >> shift) & static_cast<unsigned>(nb - 1)], 1u);
     }
     __syncthreads();
     radix_pick(hist, nb, wsum, s_prefix, s_krem, prefix, krem, shift);
@@ -343,7 +405,10 @@ __device__ void select_streaming(const unsigned* keys, int n, int K, int32_t* ou
 
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkParams p) {
   constexpr int S = kBlockSize;
-  __shared__ unsigned hist[kSelMaxBins];
+  // histogram copies; also the stage of the register path's key hand-over
+  constexpr int kLds = kSelCopies * kSelStride > kSelThreads * (kSelKPT + 1) ? kSelCopies * kSelStride
+                                                                            : kSelThreads * (kSelKPT + 1);
+  __shared__ __attribute__((aligned(16))) unsigned hist[kLds];
   __shared__ int wsum[kSelThreads / 64 + 1];
   __shared__ unsigned s_prefix, s_krem;
   const CacheView& c = p.c;
