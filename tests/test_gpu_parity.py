@@ -319,18 +319,25 @@ def test_sparse_decode_explicit_indices(k_sel):
     gh.compare_lse(lse[0], l_ref, f"sparse explicit k_sel={k_sel}")
 
 
-def test_topk_ties_prefer_lower_index():
-    """Identical keys tie exactly in fp32 too: the lowest token indices must be chosen."""
+@pytest.mark.parametrize("n,k", [(32 + 64 * 4, 10), (32 + 32768, 512), (32 + 32768 - 5, 300)])
+def test_topk_ties_prefer_lower_index(n, k):
+    """Identical keys tie exactly in fp32 too: the lowest token indices must be chosen (short rows,
+    and full register-resident rows where the selection first narrows to keys above a floor)."""
     torch = gh.torch_mod()
     import int8_kv_cache_hkv_amd as hkv
-    H, D, n = 2, 64, 32 + 64 * 4
+    H, D = 2, 64
     cache = hkv.HybridKVCache(H, D, 1, n)
-    k = np.ones((1, n, H, D), dtype=np.float16)
-    cache.append(gh.upload(k), gh.upload(k))
+    kv = np.ones((1, n, H, D), dtype=np.float16)
+    cache.append(gh.upload(kv), gh.upload(kv))
     q = np.ones((1, 2 * H, D), dtype=np.float16)
-    idx = cache.topk(gh.upload(q), 10)
+    idx = cache.topk(gh.upload(q), k)
     torch.cuda.synchronize()
-    assert idx.cpu().numpy()[0].tolist() == [list(range(10))] * H
+    # every cosine is 1, so a token's window probability is 1 / (valid tokens of its window): a
+    # short last window ranks first, then the lowest indices
+    n_cold = n - 32
+    p = np.array([1.0 / min(64, n_cold - (t // 64) * 64) for t in range(n_cold)])
+    want = sorted(sorted(range(n_cold), key=lambda t: (-p[t], t))[:k])
+    assert idx.cpu().numpy()[0].tolist() == [want] * H
 
 
 def test_topk_config_parity_sampled():
