@@ -34,7 +34,7 @@ HBM_PEAK_GBS = 8000.0
 # WRITE_SIZE x 1.000 (KiB per dispatch; the factors make a 256 MiB elementwise copy read and write
 # exactly its size), recorded in profiles/decode_kernel_llama8b_hbm_traffic.md.  Valid only for the
 # kernel sources they were measured on: reported as null once those sources change.
-COUNTER_TRAFFIC = {"sources_sha256": "148c0c7375910181d9d2924ffd6c9a8253fe1ceb4ca9b197e38bd7bae1c21285", "bytes_per_launch": 39953408}
+COUNTER_TRAFFIC = {"sources_sha256": "fccc47451ca58fe607ee4568d7434491408f20a67f0511ed9ab33f44dbc48467", "bytes_per_launch": 39856793}
 KERNEL_SOURCES = ("decode.hip", "hkv_device.h", "hkv_internal.h")
 
 
