@@ -6,7 +6,7 @@
 // full precision, cold blocks dequantised on read; here one joint softmax).
 //
 // Work decomposition.  For each (sequence, kv-head) the cold tokens are split
-// into "units": unit j is cold block j (dense mode) or the j-th run of 64
+// into "units": unit j is cold block j (dense mode) or the j-th run of 16
 // selected cold tokens (sparse mode, KV Cache reuse page 2: only the selected
 // tokens are loaded).  A workgroup of 4 waves owns one split = a run of
 // units_per_split units (round-robin over runs when a sequence has more units
@@ -33,9 +33,9 @@
 // Cold tiles are laid out so that one coalesced 16-byte load per lane lands
 // exactly these operands: lane t gets 16 channels of token t from a K tile,
 // lane c gets 16 tokens of channel c from a V tile.  Dense units are software
-// pipelined: the next unit's K tile is requested as soon as the QK products of
-// the current one are done, its V tile as soon as the PV products are, so a
-// wave always has one unit's loads in flight.
+// pipelined: each 1 KiB chunk of the current K (V) tile is replaced by the same
+// chunk of the next unit's tile as soon as its QK (PV) products are issued, so
+// a wave always has about one unit's loads in flight.
 #include <hip/hip_ext.h>
 
 #include <type_traits>

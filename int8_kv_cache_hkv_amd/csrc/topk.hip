@@ -15,7 +15,9 @@
 //                       then the wave does the window softmax and stores p.
 //   topk_select_kernel  one 1024-thread workgroup per (sequence, kv-head):
 //                       3-pass (11/10/10-bit) radix select of the K-th largest
-//                       p (fp32 bit patterns, order-preserving for p >= 0), then
+//                       p (fp32 bit patterns, order-preserving for p >= 0) over
+//                       lane-indexed histogram copies, restricted to keys at or
+//                       above a floor taken from the per-thread maxima, then
 //                       an index-ordered block-scan compaction that takes
 //                       every p above the threshold and the lowest-index ties,
 //                       so the output is ascending and deterministic.
