@@ -1078,16 +1078,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G > 4 
     AppendPart app;
   } sm;
   __shared__ int s_last;
-  // grid (split, kv-head, sequence): no index depends on a kernel argument, and every argument the
+  // grid (split, kv-head, sequence), read in XCD-major order for long splits; every argument the
   // kernel uses is consumed here, so its scalar loads are issued together and waited for once
   asm volatile("" ::"s"(p.c.H), "s"(p.c.T), "s"(p.c.max_blocks), "s"(p.c.num_phys), "s"(p.c.hot), "s"(p.c.cold),
                "s"(p.c.scales), "s"(p.c.headers), "s"(p.c.seq_len), "s"(p.q), "s"(p.sel), "s"(p.k_sel),
                "s"(p.partials), "s"(p.counters), "s"(p.nsplit), "s"(p.nparts), "s"(p.units_per_split),
                "s"(p.qscale));
   const CacheView& c = p.c;
-  const int split = blockIdx.x;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
+  const WgCoord wg = wg_coord(p.units_per_split >= kXcdMajorUnits);
+  const int split = wg.x;
+  const int h = wg.y;
+  const int b = wg.z;
   const int bh = b * c.H + h;
   const int tid = threadIdx.x;
   if (split < p.nsplit) {

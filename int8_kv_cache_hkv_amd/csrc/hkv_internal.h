@@ -16,6 +16,8 @@ constexpr int kAppendChunk = 256;   // sequences whose append counts travel in o
 constexpr int kSinglePassMaxBlocks = 2;  // appends touching at most this many blocks per sequence use one launch
 constexpr int kMaxTopK = 512;       // fixed top-K budget of the sparse path
 constexpr int kSparseUnit = 16;     // selected tokens per wave unit of the sparse decode
+constexpr int kXcds = 8;            // MI355X: accelerator complex dies, each with its own L2
+constexpr int kXcdMajorUnits = 16;  // splits of at least this many units use the XCD-major mapping
 constexpr int kMaxSplits = 128;     // cold splits per (sequence, kv-head) at most
 
 // Per-launch timing: when start/stop are non-null the dispatch records them.

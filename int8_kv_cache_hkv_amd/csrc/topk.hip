@@ -101,7 +101,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                "s"(p.c.headers), "s"(p.c.seq_len), "s"(p.q), "s"(p.prob), "s"(p.nsplit), "s"(p.units_per_split));
   const CacheView& c = p.c;
   const int H = c.H;
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const WgCoord wg = wg_coord(p.units_per_split >= kXcdMajorUnits);
+  const int split = wg.x, h = wg.y, b = wg.z;
   const int bh = b * H + h;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);

@@ -251,6 +251,40 @@ def test_append_decode_equals_separate_calls():
     assert np.max(np.abs(lse_f - lse_s)) <= gh.LSE_MAX_ABS
 
 
+# ------------------------------------------------------------------ every (head_dim, group) instance
+@pytest.mark.parametrize("d,g", [(64, 1), (64, 8), (128, 1), (128, 2), (128, 4), (128, 8)])
+def test_group_sizes_dense_sparse_fused(d, g):
+    """Every built (head_dim, GQA group) instance of the decode kernel, plain, sparse and fused, on two
+    sequences of different lengths (each with a ragged tail block) against the oracle."""
+    import dataclasses
+    w = dataclasses.replace(wl.WORKLOADS["tiny"], name=f"gqa_d{d}_g{g}", batch=2, n_q_heads=2 * g, head_dim=d)
+    lens = [32 + 64 * 3 + 17, 32 + 64 * 6 + 40]
+    cache = gh.make_cache(w, max(lens) + 64)
+    gh.fill(cache, w, lens)
+    q = wl.queries(w, step=7)
+    st = _oracle_states(w, lens)
+    out, lse = _decode(cache, q)
+    for b in range(2):
+        o_ref, l_ref = orc.decode(q[b], st[b])
+        gh.compare_out(out[b], o_ref, f"d={d} g={g} dense b={b}")
+        gh.compare_lse(lse[b], l_ref, f"d={d} g={g} dense b={b}")
+    k_sel = 50
+    rng = np.random.default_rng(10 * d + g)
+    sel = np.stack([rng.integers(0, s.n_cold, size=(w.n_kv_heads, k_sel)) for s in st]).astype(np.int32)
+    out_s, lse_s = _decode(cache, q, sel=gh.upload(sel), k_sel=k_sel)
+    for b in range(2):
+        o_ref, l_ref = orc.sparse_decode(q[b], st[b], sel[b])
+        gh.compare_out(out_s[b], o_ref, f"d={d} g={g} sparse b={b}")
+        gh.compare_lse(lse_s[b], l_ref, f"d={d} g={g} sparse b={b}")
+    out_f, lse_f = _append_decode(cache, w, lens, q)
+    st1 = _oracle_states(w, [n + 1 for n in lens])
+    gh.check_state(cache, st1)
+    for b in range(2):
+        o_ref, l_ref = orc.decode(q[b], st1[b])
+        gh.compare_out(out_f[b], o_ref, f"d={d} g={g} fused b={b}")
+        gh.compare_lse(lse_f[b], l_ref, f"d={d} g={g} fused b={b}")
+
+
 # ------------------------------------------------------------------ long context, sampled
 def test_long_config_parity_sampled():
     w = wl.WORKLOADS["long"]
