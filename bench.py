@@ -317,6 +317,152 @@ def sparse_leg(hkv, torch, steps):
             "topk_score_gbs": score_b / (km["topk_score"] * 1e-3) / 1e9 if km["topk_score"] else None}
 
 
+def ragged_leg(hkv, torch, steps=64, R=4):
+    """The ragged paged batch: 64 sequences of seeded lengths in [128, 8192], cold blocks at a seeded
+    permutation of the physical pool, `steps` decode steps (one token appended per sequence, then a
+    dense decode), rotating over R instances; fused launches and, separately, the two-call form so the
+    append is timed on its own."""
+    import workloads as wl
+    w = wl.WORKLOADS["ragged"]
+    B, H, Hq, d = w.batch, w.n_kv_heads, w.n_q_heads, w.head_dim
+    lens0 = [int(x) for x in wl.lengths(w)]
+    per_inst = -(-2 * steps // R) + 1
+    cap = max(lens0) + per_inst + 1
+    mb = -(-(cap - w.hot_tokens) // w.block_size)
+    perm = wl.block_permutation(w, B * mb).reshape(B, mb)
+    log(f"ragged: {R} instances of B={B}, lengths {min(lens0)}..{max(lens0)} (cap {cap}), generating inputs")
+    insts = [hkv.HybridKVCache(H, d, B, cap, phys_ids=perm) for _ in range(R)]
+    chunk = 2048
+    for s0 in range(0, max(lens0), chunk):
+        cnt = min(chunk, max(lens0) - s0)
+        kb = torch.from_numpy(wl.batch_tokens(w, list(range(B)), s0, cnt, "k")).cuda()
+        vb = torch.from_numpy(wl.batch_tokens(w, list(range(B)), s0, cnt, "v")).cuda()
+        n_new = np.array([max(0, min(cnt, n - s0)) for n in lens0], dtype=np.int32)
+        for c in insts:
+            c.append(kb, vb, n_new)
+        del kb, vb
+    torch.cuda.synchronize()
+    # the new token of each sequence at each of its steps, and the per-step queries
+    newk = [torch.from_numpy(np.stack([wl.tokens(w, b, lens0[b] + u, 1, "k")[0] for b in range(B)])).cuda()
+            for u in range(per_inst)]
+    newv = [torch.from_numpy(np.stack([wl.tokens(w, b, lens0[b] + u, 1, "v")[0] for b in range(B)])).cuda()
+            for u in range(per_inst)]
+    qs = [torch.from_numpy(wl.queries(w, step=i)).cuda() for i in range(8)]
+    out = torch.empty_like(qs[0])
+    ws = insts[0].workspace(Hq)
+    ones = np.ones(B, dtype=np.int32)
+    stream = torch.cuda.current_stream().cuda_stream
+    lib = hkv._lib
+    used = [0] * R
+
+    def step(i, fused):
+        r = i % R
+        c, u = insts[r], used[r]
+        if fused:
+            st = lib.hkv_append_decode(c.handle, ctypes.byref(c.desc), newk[u].data_ptr(), newv[u].data_ptr(),
+                                       qs[i % 8].data_ptr(), Hq, out.data_ptr(), None, ws.data_ptr(), ws.numel(),
+                                       stream)
+        else:
+            st = lib.hkv_append(c.handle, ctypes.byref(c.desc), newk[u].data_ptr(), newv[u].data_ptr(),
+                                ones.ctypes.data, 1, stream)
+            if not st:
+                st = lib.hkv_decode_attn(c.handle, ctypes.byref(c.desc), qs[i % 8].data_ptr(), Hq, None, 0,
+                                         out.data_ptr(), None, ws.data_ptr(), ws.numel(), stream)
+        if st:
+            raise hkv.HKVError(st, "ragged step")
+        used[r] += 1
+        return sum(decode_bytes(n + used[r], H, Hq, d) + append_bytes(1, H, d) for n in lens0)
+
+    res = {"workload": f"ragged: {B} sequences, lengths {min(lens0)}..{max(lens0)} (seeded uniform), permuted "
+                       f"physical blocks, step = append 1 token/seq + dense decode"}
+    for fused in (True, False):
+        for c in insts:
+            hkv.hkv_timing_enable(c.handle, True)
+        nbytes = 0
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            nbytes += step(i, fused)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        km = {}
+        for kname in (("append_decode",) if fused else ("append", "decode")):
+            tot, cnt = 0.0, 0
+            for c in insts:
+                a, b = hkv.hkv_timing_read(c.handle, kname, reset=True)
+                tot, cnt = tot + a, cnt + b
+            km[kname] = tot / cnt if cnt else None
+        for c in insts:
+            hkv.hkv_timing_enable(c.handle, False)
+        key = "fused" if fused else "separate_calls"
+        res[key] = {"ms_per_step": ms, "gbs": nbytes / steps / (ms * 1e-3) / 1e9,
+                    "pct_hbm_peak": 100 * nbytes / steps / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "bytes_per_step": nbytes / steps, "kernel_ms": km}
+    res["note"] = "per-step times include a dispatch-recorded event pair per kernel"
+    for c in insts:
+        c.close()
+    return res
+
+
+def graph_leg(hkv, torch, steps=640, R=64):
+    """The llama8b step replayed from a HIP graph (captured once: one fused launch per instance) against
+    the same launches issued one by one."""
+    import workloads as wl
+    w = wl.WORKLOADS["llama8b"]
+    B, H, Hq, d = w.batch, w.n_kv_heads, w.n_q_heads, w.head_dim
+    n0 = w.context - 1
+    reps = -(-steps // R)
+    cap = n0 + 2 * reps + 8
+    insts = [hkv.HybridKVCache(H, d, B, cap) for _ in range(R)]
+    kh = torch.from_numpy(wl.batch_tokens(w, list(range(B)), 0, n0, "k")).cuda()
+    vh = torch.from_numpy(wl.batch_tokens(w, list(range(B)), 0, n0, "v")).cuda()
+    for c in insts:
+        c.append(kh, vh)
+    del kh, vh
+    newk = torch.from_numpy(wl.batch_tokens(w, list(range(B)), n0, 1, "k")).cuda()
+    newv = torch.from_numpy(wl.batch_tokens(w, list(range(B)), n0, 1, "v")).cuda()
+    q = torch.from_numpy(wl.queries(w)).cuda()
+    out = torch.empty_like(q)
+    ws = insts[0].workspace(Hq)
+    lib = hkv._lib
+    torch.cuda.synchronize()
+
+    def all_instances(stream):
+        for c in insts:
+            st = lib.hkv_append_decode(c.handle, ctypes.byref(c.desc), newk.data_ptr(), newv.data_ptr(), q.data_ptr(),
+                                       Hq, out.data_ptr(), None, ws.data_ptr(), ws.numel(), stream)
+            if st:
+                raise hkv.HKVError(st, "hkv_append_decode")
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        all_instances(side.cuda_stream)  # eager warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        all_instances(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms_graph = (time.perf_counter() - t0) * 1e3 / (reps * R)
+    stream = torch.cuda.current_stream().cuda_stream
+    t0 = time.perf_counter()
+    for _ in range(reps - 1):
+        all_instances(stream)
+    torch.cuda.synchronize()
+    ms_eager = (time.perf_counter() - t0) * 1e3 / ((reps - 1) * R)
+    for c in insts:
+        c.close()
+    step_b = B * (decode_bytes(n0 + 2, H, Hq, d) + append_bytes(1, H, d))
+    return {"what": "llama8b step: one graph of 64 fused launches (one per instance) replayed, vs the same launches "
+                    "issued eagerly", "ms_per_step_graph": ms_graph, "ms_per_step_eager": ms_eager,
+            "gbs_graph": step_b / (ms_graph * 1e-3) / 1e9, "steps": reps * R}
+
+
 def copy_calibration(torch, mib=256, reps=4):
     """A plain elementwise copy of a known size (reads and writes `mib` MiB per launch).  Hardware
     counters of this launch calibrate the FETCH_SIZE / WRITE_SIZE readings of the decode kernel."""
@@ -393,6 +539,8 @@ def main():
                                  "ms_per_step": sep["ms_per_step"], "gbs": sep["gbs"], "kernel_ms": sep["kernel_ms"]}
         res["long"] = long_leg(hkv, torch, 16)
         res["sparse"] = sparse_leg(hkv, torch, 20)
+        res["ragged"] = ragged_leg(hkv, torch)
+        res["hip_graph"] = graph_leg(hkv, torch)
     if args.copy_calibration:
         res["copy_calibration"] = copy_calibration(torch)
     if not args.no_cpu_baseline:

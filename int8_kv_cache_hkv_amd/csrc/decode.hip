@@ -1083,9 +1083,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G > 4 
   asm volatile("" ::"s"(p.c.H), "s"(p.c.T), "s"(p.c.max_blocks), "s"(p.c.num_phys), "s"(p.c.hot), "s"(p.c.cold),
                "s"(p.c.scales), "s"(p.c.headers), "s"(p.c.seq_len), "s"(p.q), "s"(p.sel), "s"(p.k_sel),
                "s"(p.partials), "s"(p.counters), "s"(p.nsplit), "s"(p.nparts), "s"(p.units_per_split),
-               "s"(p.qscale));
+               "s"(p.xcd_major), "s"(p.qscale));
   const CacheView& c = p.c;
-  const WgCoord wg = wg_coord(p.units_per_split >= kXcdMajorUnits);
+  const WgCoord wg = wg_coord(p.xcd_major != 0);
   const int split = wg.x;
   const int h = wg.y;
   const int b = wg.z;

@@ -52,33 +52,46 @@ int64_t cold_blocks(int64_t tokens, int T, int S) {
 }
 
 // Split plan: units per split is a multiple of the 4 waves of a workgroup and
-// the grid aims at kTargetWorkgroups; a split count never exceeds kMaxSplits.
+// a split count never exceeds kMaxSplits.
+//  * When the launch fits the resident workgroup slots (about kTargetWorkgroups),
+//    all of its workgroups (cold splits + the extra_parts other workgroups of
+//    each (sequence, kv-head): hot zone, and the tail block of a fused append)
+//    are sized to be resident at once: a straggler that starts late delays the
+//    merge of its (sequence, kv-head).
+//  * With more (sequence, kv-head) pairs than that (large ragged batches), the
+//    grid cannot be resident anyway: short splits of kBatchSplitUnits units are
+//    scheduled as slots free up, so a long sequence does not leave one
+//    workgroup streaming alone at the end.
+constexpr int64_t kBatchSplitUnits = 32;
 struct SplitPlan {
   int nsplit;
   int per_split;
+  int xcd_major;  // resident plans with long splits read the grid in XCD-major order (see wg_coord)
 };
 SplitPlan plan_splits(int64_t bh, int64_t units, int extra_parts = 1) {
   units = std::max<int64_t>(1, units);
-  // all of a launch's workgroups (cold splits + the extra_parts other workgroups of each (sequence,
-  // kv-head): hot zone, and the tail block of a fused append) should be resident at once: a straggler
-  // that starts late delays the merge of its (sequence, kv-head)
-  int64_t target = std::max<int64_t>(1, kTargetWorkgroups / bh - extra_parts);
-  int64_t per = hkv::kWaves * ((units + hkv::kWaves * target - 1) / (hkv::kWaves * target));
+  const int64_t target = kTargetWorkgroups / bh - extra_parts;
+  int64_t per = target >= 2 ? hkv::kWaves * ((units + hkv::kWaves * target - 1) / (hkv::kWaves * target))
+                            : kBatchSplitUnits;
   int64_t ns = (units + per - 1) / per;
   if (ns > kMaxSplits) {
     per = hkv::kWaves * ((units + hkv::kWaves * kMaxSplits - 1) / (hkv::kWaves * kMaxSplits));
     ns = (units + per - 1) / per;
   }
-  return {static_cast<int>(ns), static_cast<int>(per)};
+  // measured: XCD-major order helps long resident splits (131072-token step) and hurts the batch plan
+  const int xcd = target >= 2 && per >= hkv::kXcdMajorUnits ? 1 : 0;
+  return {static_cast<int>(ns), static_cast<int>(per), xcd};
 }
 
-// Upper bound of the split count over every unit count in [1, units_cap]: a
-// plan has at most `target` splits (units_per_split >= units / target) and at
-// most ceil(units / 4) splits (units_per_split >= 4), capped by kMaxSplits.
+// Upper bound of the split count of plan_splits over every unit count in
+// [1, units_cap] and extra_parts >= 1: a resident plan has at most
+// kTargetWorkgroups / bh - 1 splits and at most ceil(units / 4); a batch plan
+// ceil(units / kBatchSplitUnits); both capped by kMaxSplits.
 int max_splits(int64_t bh, int64_t units_cap) {
-  const int64_t target = std::max<int64_t>(1, kTargetWorkgroups / bh - 1);
-  int64_t ns = std::min<int64_t>(std::min<int64_t>(target, kMaxSplits), (std::max<int64_t>(1, units_cap) + 3) / 4);
-  return static_cast<int>(std::max<int64_t>(1, ns));
+  const int64_t u = std::max<int64_t>(1, units_cap);
+  const int64_t resident = std::min<int64_t>(std::max<int64_t>(1, kTargetWorkgroups / bh - 1), (u + 3) / 4);
+  const int64_t batch = (u + kBatchSplitUnits - 1) / kBatchSplitUnits;
+  return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(kMaxSplits, std::max(resident, batch))));
 }
 
 // Sparse decode: one unit of kSparseUnit selected tokens per wave, so every
@@ -86,7 +99,7 @@ int max_splits(int64_t bh, int64_t units_cap) {
 // few splits per (sequence, kv-head)).
 SplitPlan plan_sparse(int k_sel) {
   const int units = std::max(1, (k_sel + hkv::kSparseUnit - 1) / hkv::kSparseUnit);
-  return {(units + hkv::kWaves - 1) / hkv::kWaves, hkv::kWaves};
+  return {(units + hkv::kWaves - 1) / hkv::kWaves, hkv::kWaves, 0};
 }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -342,6 +355,7 @@ hkv_status hkv_decode_attn(hkv_handle h, const hkv_cache_desc* c, const void* q,
   p.nsplit = sp.nsplit;
   p.nparts = sp.nsplit + 1;
   p.units_per_split = sp.per_split;
+  p.xcd_major = sp.xcd_major;
   p.qscale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(h->D)));
   p.out = static_cast<_Float16*>(out);
   p.lse = lse;
@@ -390,6 +404,7 @@ hkv_status hkv_append_decode(hkv_handle h, const hkv_cache_desc* c, const void* 
   p.nsplit = sp.nsplit;
   p.nparts = sp.nsplit + 2;
   p.units_per_split = sp.per_split;
+  p.xcd_major = sp.xcd_major;
   p.qscale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(h->D)));
   p.out = static_cast<_Float16*>(out);
   p.lse = lse;
@@ -428,6 +443,7 @@ hkv_status hkv_topk_select(hkv_handle h, const hkv_cache_desc* c, const void* q,
   const SplitPlan sp = plan_splits(static_cast<int64_t>(c->batch) * h->H, blk_max);
   p.nsplit = sp.nsplit;
   p.units_per_split = sp.per_split;
+  p.xcd_major = sp.xcd_major;
   p.k = k;
   p.out_idx = out_idx;
   LaunchCtx a = make_ctx(h, stream, HKV_KERNEL_TOPK_SCORE);

@@ -160,8 +160,8 @@ __device__ __forceinline__ int header_batch(const CacheView& c, int b, int kb, i
 // linear order becomes one contiguous range of logical workgroups (a bijection),
 // so the splits of one (sequence, kv-head) run on one die and each die streams
 // a few contiguous head ranges of the pool.  Measured on the 131072-token step:
-// 186 -> 178 us.  Short splits (latency-bound steps) keep the plain order,
-// which measured faster there.
+// 186 -> 178 us.  Short splits (latency-bound steps) and grids larger than the
+// resident slots keep the plain order, which measured faster there.
 struct WgCoord {
   int x, y, z;
 };

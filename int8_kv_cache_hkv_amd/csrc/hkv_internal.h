@@ -17,7 +17,7 @@ constexpr int kSinglePassMaxBlocks = 2;  // appends touching at most this many b
 constexpr int kMaxTopK = 512;       // fixed top-K budget of the sparse path
 constexpr int kSparseUnit = 16;     // selected tokens per wave unit of the sparse decode
 constexpr int kXcds = 8;            // MI355X: accelerator complex dies, each with its own L2
-constexpr int kXcdMajorUnits = 16;  // splits of at least this many units use the XCD-major mapping
+constexpr int kXcdMajorUnits = 16;  // resident plans with splits of at least this many units use XCD-major order
 constexpr int kMaxSplits = 128;     // cold splits per (sequence, kv-head) at most
 
 // Per-launch timing: when start/stop are non-null the dispatch records them.
@@ -62,6 +62,7 @@ struct DecodeParams {
   int nsplit;              // cold splits per (sequence, kv-head)
   int nparts;              // partial records per (sequence, kv-head): nsplit + 1 (hot zone), + 1 more fused
   int units_per_split;     // units handled per split (multiple of kWaves)
+  int xcd_major;           // 1: workgroups read the grid in XCD-major order
   float qscale;            // log2(e) / sqrt(D)
   _Float16* out;           // [B][H*G][D]
   float* lse;              // [B][H*G] or nullptr
@@ -78,6 +79,7 @@ struct TopkParams {
   float* prob;             // [B][H][max_blocks*S] window probabilities
   int nsplit;
   int units_per_split;
+  int xcd_major;           // 1: workgroups read the grid in XCD-major order
   int k;
   int32_t* out_idx;        // [B][H][k]
 };
