@@ -23,13 +23,15 @@
 //   PV  B operand = the value codes of 4 consecutive tokens at the lane's
 //       channel (lane = channel), A operand = the weights of those tokens for
 //       query row lane%4 (from LDS), so lane c accumulates out[g][c].
-// INT8 codes enter the MFMAs as the exact fp16 values code + 1152 (a byte
-// permute under the fp16 exponent of 1024; no subtraction), and the offset is
-// removed from the finished sums: 1152 * sum(q) from each logit, 1152 *
-// sum(weights) from the value accumulator.  Weights are p = 2^(z - block max)
-// in [0, 1], split into hi + lo fp16 halves (about 22 significant bits) and
-// accumulated per block; the block's V scale and its online-softmax factor are
-// applied once per block in fp32.
+// Key codes enter the QK MFMAs as the exact fp16 values code + 1152 (a byte
+// permute under the fp16 exponent of 1024; no subtraction), and 1152 * sum(q)
+// is removed from each finished logit.  Value codes enter the PV MFMAs as the
+// exact codes: an offset there would have to be cancelled from sums of size
+// 1152 * s_V, which costs absolute accuracy when s_V is large (fp16-range
+// values).  Weights are p = 2^(z - block max) in [0, 1], split into hi + lo
+// fp16 halves (about 22 significant bits) and accumulated per block; the
+// block's V scale and its online-softmax factor are applied once per block in
+// fp32.
 // Cold tiles are laid out so that one coalesced 16-byte load per lane lands
 // exactly these operands: lane t gets 16 channels of token t from a K tile,
 // lane c gets 16 tokens of channel c from a V tile.  Dense units are software
@@ -91,7 +93,6 @@ struct WaveState {
   using C = Cfg<D, G>;
   float m[C::NG];                          // running max of base-2 logits (wave-uniform)
   float l[C::NG];                          // lane-partial sum of softmax weights
-  float pb[C::NG];                         // lane-partial sum of weight * V scale (removes the code offset)
   float qb[C::NG];                         // 1152 * sum_k q[g][k] (wave-uniform)
   float4_t acc[C::NQ][C::NDL];             // out[4quad + r][64 pass + lane] (with the code offset)
 };
@@ -128,7 +129,6 @@ __device__ __forceinline__ void softmax_unit(WaveState<D, G>& st, DecodeSmem<D, 
       const float wv = PER_LANE_V ? pp * vw : pp;
       const float cf = be * vcoef;
       st.l[g] = fmaf(st.l[g], a, be * pp);
-      st.pb[g] = fmaf(st.pb[g], a, cf * wv);
       st.m[g] = mn;
       alpha[g] = a;
       coef[g] = cf;
@@ -157,7 +157,7 @@ __device__ __forceinline__ void pv_step(BlockAcc<D, G>& blk, const DecodeSmem<D,
   }
   half4_t bv[C::NDL];
 #pragma unroll
-  for (int ps = 0; ps < C::NDL; ++ps) bv[ps] = codes_to_biased_half4(vw[ps]);
+  for (int ps = 0; ps < C::NDL; ++ps) bv[ps] = codes_to_half4(vw[ps]);  // exact codes: no offset to cancel later
 #pragma unroll
   for (int quad = 0; quad < C::NQ; ++quad)
 #pragma unroll
@@ -594,7 +594,6 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
   for (int g = 0; g < NG; ++g) {
     st.m[g] = kNegInf;
     st.l[g] = 0.f;
-    st.pb[g] = 0.f;
     float qs = 0.f;
 #pragma unroll
     for (int k = lane; k < D; k += 64) qs += static_cast<float>(sm.qh[g / 4][g % 4][k]);
@@ -617,12 +616,10 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
   } else {
     dense_units<D, G>(st, sm, p, b, h, split, units, sg.n_cold, w, lane, t0, phys0, sc0, hb);
   }
-  // merge the 4 waves: lane holds out[4quad + r][64 pass + lane] + 1152 * pb
-  float bias[NG];
+  // merge the 4 waves: lane holds out[4quad + r][64 pass + lane]
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     const float lsum = wave_sum_dpp(st.l[g]);
-    bias[g] = kCodeBias * wave_sum_dpp(st.pb[g]);
     if (lane == 0) {
       sm.wm[w][g] = st.m[g];
       sm.wl[w][g] = lsum;
@@ -633,7 +630,7 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
 #pragma unroll
     for (int ps = 0; ps < C::NDL; ++ps)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm.wacc[w][4 * quad + r][64 * ps + lane] = st.acc[quad][ps][r] - bias[4 * quad + r];
+      for (int r = 0; r < 4; ++r) sm.wacc[w][4 * quad + r][64 * ps + lane] = st.acc[quad][ps][r];
   __syncthreads();
   for (int idx = tid; idx < G * (D / 2); idx += kThreads) {
     const int g = idx / (D / 2), d = 2 * (idx % (D / 2));
@@ -983,13 +980,12 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G>& am, i
 
   // ---- tail block jt, rows [0, ts], by wave 0 with the cold-unit code
   if (w == 0) {
-    float um[NG], ul[NG], ubias[NG];
+    float um[NG], ul[NG];
     float4_t uacc[C::NQ][C::NDL];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       um[g] = kNegInf;
       ul[g] = 0.f;
-      ubias[g] = 0.f;
     }
 #pragma unroll
     for (int quad = 0; quad < C::NQ; ++quad)
@@ -1010,7 +1006,6 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G>& am, i
       for (int g = 0; g < NG; ++g) {
         st.m[g] = kNegInf;
         st.l[g] = 0.f;
-        st.pb[g] = 0.f;
         float qs = 0.f;
 #pragma unroll
         for (int k = lane; k < D; k += 64) qs += static_cast<float>(am.unit.qh[g / 4][g % 4][k]);
@@ -1031,7 +1026,6 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G>& am, i
       for (int g = 0; g < NG; ++g) {
         um[g] = st.m[g];
         ul[g] = wave_sum_dpp(st.l[g]);
-        ubias[g] = kCodeBias * wave_sum_dpp(st.pb[g]);
       }
 #pragma unroll
       for (int quad = 0; quad < C::NQ; ++quad)
@@ -1050,7 +1044,7 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G>& am, i
       for (int ps2 = 0; ps2 < C::NDL; ++ps2)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          am.unit.wacc[0][4 * quad + r][64 * ps2 + lane] = uacc[quad][ps2][r] - ubias[4 * quad + r];
+          am.unit.wacc[0][4 * quad + r][64 * ps2 + lane] = uacc[quad][ps2][r];
   }
   __syncthreads();
   for (int i = tid; i < G * (D / 2); i += kThreads) {

@@ -251,6 +251,59 @@ def test_append_decode_equals_separate_calls():
     assert np.max(np.abs(lse_f - lse_s)) <= gh.LSE_MAX_ABS
 
 
+# ------------------------------------------------------------------ quantiser edge values
+def _edge_history(H=2, d=64, seed=5):
+    """Four cold blocks (all zero; exact half-integer ratios x/s with s = 1; fp16 extremes and
+    subnormals; random) followed by random hot tokens, as one sequence history [n, H, d]."""
+    rng = np.random.default_rng(seed)
+    S, T = 64, 32
+    blocks = []
+    blocks.append(np.zeros((S, H, d), dtype=np.float16))
+    half = (rng.integers(-127, 127, size=(S, H, d)) + 0.5).astype(np.float16)  # x / 1.0 = k + 0.5: a tie
+    half[0, :, 0] = 127.0                                                   # the maximum: s = fl32(127/127) = 1
+    blocks.append(half)
+    ext = rng.standard_normal((S, H, d)).astype(np.float16)
+    ext[:, :, ::3] = np.float16(6e-8)       # fp16 subnormals
+    ext[:, :, 1::7] = np.float16(-65504.0)  # fp16 extremes
+    ext[5, :, 2] = np.float16(65504.0)
+    blocks.append(ext)
+    blocks.append(rng.standard_normal((S, H, d)).astype(np.float16))
+    cold = np.concatenate(blocks)
+    hot = rng.standard_normal((T, H, d)).astype(np.float16)
+    return np.concatenate([cold, hot])
+
+
+def test_quantiser_edge_values():
+    """Zero blocks (scale 0), exact ties of x / s (round half to even), fp16 extremes and subnormals:
+    codes and scales bit-exact, decode within tolerance; then one fused step spilling an extreme token."""
+    torch = gh.torch_mod()
+    import int8_kv_cache_hkv_amd as hkv
+    H, d = 2, 64
+    hist = _edge_history(H, d)
+    vals = _edge_history(H, d, seed=6)
+    n = hist.shape[0]
+    cache = hkv.HybridKVCache(H, d, 1, n + 64)
+    cache.append(gh.upload(hist[None]), gh.upload(vals[None]))
+    torch.cuda.synchronize()
+    st = orc.build_state(hist, vals, 32, 64)
+    gh.check_state(cache, [st])
+    q = np.random.default_rng(7).standard_normal((1, 2 * H, d)).astype(np.float16) * np.float16(0.01)
+    out, lse = _decode(cache, q)
+    o_ref, l_ref = orc.decode(q[0], st)
+    gh.compare_out(out[0], o_ref, "edge values")
+    gh.compare_lse(lse[0], l_ref, "edge values")
+    # one fused step: the spilled token opens a fifth block; the new token holds an fp16 extreme
+    kn = np.random.default_rng(8).standard_normal((1, H, d)).astype(np.float16)
+    kn[0, 0, 3] = np.float16(65504.0)
+    out_f = torch.empty((1, 2 * H, d), dtype=torch.float16, device="cuda")
+    cache.append_decode(gh.upload(kn), gh.upload(kn), gh.upload(q), out=out_f)
+    torch.cuda.synchronize()
+    st1 = orc.build_state(np.concatenate([hist, kn]), np.concatenate([vals, kn]), 32, 64)
+    gh.check_state(cache, [st1])
+    o_ref1, _ = orc.decode(q[0], st1)
+    gh.compare_out(out_f.cpu().numpy()[0], o_ref1, "edge values, fused step")
+
+
 # ------------------------------------------------------------------ every (head_dim, group) instance
 @pytest.mark.parametrize("d,g", [(64, 1), (64, 8), (128, 1), (128, 2), (128, 4), (128, 8)])
 def test_group_sizes_dense_sparse_fused(d, g):
