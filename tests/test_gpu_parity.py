@@ -338,6 +338,30 @@ def test_group_sizes_dense_sparse_fused(d, g):
         gh.compare_lse(lse_f[b], l_ref, f"d={d} g={g} fused b={b}")
 
 
+# ------------------------------------------------------------------ XCD-major order on a grid not a multiple of 8
+def test_xcd_major_order_odd_grid():
+    """3 sequences x 3 kv-heads with ~86k tokens: the resident plan has splits of 16 units, so the
+    grid is read in XCD-major order, and its 86 x 3 x 3 = 774 workgroups are not a multiple of the 8
+    dies.  Every output against the oracle, plain decode and a fused step."""
+    import dataclasses
+    w = dataclasses.replace(wl.WORKLOADS["long"], name="xcd_odd", batch=3, n_kv_heads=3, n_q_heads=6)
+    n = 32 + 1345 * 64 + 17
+    cache = gh.make_cache(w, n + 8)
+    gh.fill(cache, w, [n] * w.batch, chunk=8192)
+    q = wl.queries(w, step=2)
+    out, lse = _decode(cache, q)
+    st = _oracle_states(w, [n] * w.batch)
+    for b in range(w.batch):
+        o_ref, l_ref = orc.decode(q[b], st[b])
+        gh.compare_out(out[b], o_ref, f"xcd-major b={b}")
+        gh.compare_lse(lse[b], l_ref, f"xcd-major b={b}")
+    out_f, _ = _append_decode(cache, w, [n] * w.batch, q)
+    st1 = _oracle_states(w, [n + 1] * w.batch)
+    for b in range(w.batch):
+        o_ref, _ = orc.decode(q[b], st1[b])
+        gh.compare_out(out_f[b], o_ref, f"xcd-major fused b={b}")
+
+
 # ------------------------------------------------------------------ long context, sampled
 def test_long_config_parity_sampled():
     w = wl.WORKLOADS["long"]
