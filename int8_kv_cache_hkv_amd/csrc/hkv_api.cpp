@@ -68,9 +68,9 @@ struct SplitPlan {
   int per_split;
   int xcd_major;  // resident plans with long splits read the grid in XCD-major order (see wg_coord)
 };
-SplitPlan plan_splits(int64_t bh, int64_t units, int extra_parts = 1) {
+SplitPlan plan_splits(int64_t bh, int64_t units, int extra_parts = 1, int64_t target_wg = kTargetWorkgroups) {
   units = std::max<int64_t>(1, units);
-  const int64_t target = kTargetWorkgroups / bh - extra_parts;
+  const int64_t target = target_wg / bh - extra_parts;
   int64_t per = target >= 2 ? hkv::kWaves * ((units + hkv::kWaves * target - 1) / (hkv::kWaves * target))
                             : kBatchSplitUnits;
   int64_t ns = (units + per - 1) / per;
@@ -440,7 +440,8 @@ hkv_status hkv_topk_select(hkv_handle h, const hkv_cache_desc* c, const void* q,
   p.G = G;
   p.q = static_cast<const _Float16*>(q);
   p.prob = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(counters_bytes(c, h->H), 256));
-  const SplitPlan sp = plan_splits(static_cast<int64_t>(c->batch) * h->H, blk_max);
+  // the score kernel holds 64 VGPRs per lane, so 8 of its workgroups fit a CU: twice the decode's grid
+  const SplitPlan sp = plan_splits(static_cast<int64_t>(c->batch) * h->H, blk_max, 1, 2 * kTargetWorkgroups);
   p.nsplit = sp.nsplit;
   p.units_per_split = sp.per_split;
   p.xcd_major = sp.xcd_major;
