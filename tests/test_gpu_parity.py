@@ -338,6 +338,43 @@ def test_group_sizes_dense_sparse_fused(d, g):
         gh.compare_lse(lse_f[b], l_ref, f"d={d} g={g} fused b={b}")
 
 
+# ------------------------------------------------------------------ other hot-zone sizes
+@pytest.mark.parametrize("T", [16, 64, 128])
+def test_hot_tokens_variants(T):
+    """hot_tokens 16, 64 and 128 (the other protocol values): bulk append, dense decode, a fused step,
+    top-K and sparse decode against the oracle; one sequence with a cold zone, one still all-hot."""
+    import dataclasses
+    w = dataclasses.replace(wl.WORKLOADS["tiny"], name=f"hot{T}", batch=2, hot_tokens=T)
+    lens = [T + 64 * 3 + 17, T - 5]
+    cache = gh.make_cache(w, max(lens) + 64)
+    gh.fill(cache, w, lens)
+    st = _oracle_states(w, lens)
+    gh.check_state(cache, st)
+    q = wl.queries(w, step=1)
+    out, lse = _decode(cache, q)
+    for b in range(2):
+        o_ref, l_ref = orc.decode(q[b], st[b])
+        gh.compare_out(out[b], o_ref, f"T={T} dense b={b}")
+        gh.compare_lse(lse[b], l_ref, f"T={T} dense b={b}")
+    k = 50
+    idx = cache.topk(gh.upload(q), k)
+    gh.torch_mod().cuda.synchronize()
+    got = idx.cpu().numpy()
+    want, pr, tau = orc.topk_select(q[0], st[0], k)
+    for h in range(w.n_kv_heads):
+        gh.compare_topk(got[0, h], want[h], pr[h], tau[h], st[0].n_cold, k, f"T={T} topk h={h}")
+    out_s, lse_s = _decode(cache, q, sel=idx, k_sel=k)
+    for b in range(2):
+        o_ref, l_ref = orc.sparse_decode(q[b], st[b], got[b])
+        gh.compare_out(out_s[b], o_ref, f"T={T} sparse b={b}")
+    out_f, _ = _append_decode(cache, w, lens, q)
+    st1 = _oracle_states(w, [n + 1 for n in lens])
+    gh.check_state(cache, st1)
+    for b in range(2):
+        o_ref, _ = orc.decode(q[b], st1[b])
+        gh.compare_out(out_f[b], o_ref, f"T={T} fused b={b}")
+
+
 # ------------------------------------------------------------------ XCD-major order on a grid not a multiple of 8
 def test_xcd_major_order_odd_grid():
     """3 sequences x 3 kv-heads with ~86k tokens: the resident plan has splits of 16 units, so the
