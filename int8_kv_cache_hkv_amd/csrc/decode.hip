@@ -291,18 +291,13 @@ __device__ __forceinline__ float2 load_scales(__amdgpu_buffer_rsrc_t rs, int phy
   return make_float2(__builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, o, 0, 0)),
                      __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, o, 4, 0)));
 }
+
 // One dense unit's tiles in registers.
 template <int D>
 struct Tiles {
   uint4 kr[D / 16];     // lane t: chunk ch = codes 16ch..16ch+15 of token t
   uint4 vr[D / 64][4];  // lane c: [pass][tc] = tokens 16tc..16tc+15 of channel 64 pass + lane
 };
-// Physical block of cold block j of sequence b, or -1 when the header is out of range.
-__device__ __forceinline__ int dense_phys(const CacheView& c, int b, int j) {
-  if (j >= c.max_blocks) return -1;
-  const int ph = c.headers[static_cast<size_t>(b) * c.max_blocks + j].phys_block;
-  return (ph >= 0 && ph < c.num_phys) ? ph : -1;
-}
 
 // Buffer resource over one block's K and V tiles of one kv-head (2*S*D
 // contiguous bytes, K first): the tile loads take a uniform descriptor plus a

@@ -21,18 +21,6 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
-__device__ __forceinline__ int wave_sum_int(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
 // Make LDS written by some lanes of this wave visible to the other lanes.
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -41,11 +29,6 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 __device__ __forceinline__ float exp2_approx(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Signed byte k (0..3) of a packed word, as float (exact).
-__device__ __forceinline__ float sbyte(uint32_t w, int k) {
-  return static_cast<float>(static_cast<int8_t>(static_cast<uint8_t>(w >> (8 * k))));
-}
 
 __device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
@@ -233,9 +216,6 @@ constexpr float kCodeBias = 1152.0f;
 
 __device__ __forceinline__ float4_t mfma_qk(half4_t a, half4_t b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ float4_t mfma_pv(float a, float b, float4_t c) {
-  return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
 }
 
 }  // namespace hkv
