@@ -51,6 +51,8 @@ namespace detail {
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kHotChunk = 32;         // hot-zone slots staged through LDS at a time
 constexpr int kMergeChunk = 16;       // partials whose loads are in flight together in the merge
+constexpr int kHoldUnits = 8;         // splits of at most this many units hold their first tiles ...
+constexpr uint64_t kHoldTicks = 100;  // ... until this many s_memrealtime ticks (100 MHz) after start
 
 template <int D, int G>
 struct Cfg {
@@ -566,8 +568,17 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
   if (SPARSE) {
     sel0 = sel_entry(sel_bh, p.k_sel, split * p.units_per_split + w, lane);
   } else {
+    const uint64_t t_entry = __builtin_amdgcn_s_memrealtime();
     hb = header_batch(c, b, 0, split, p.nsplit, p.units_per_split, w, lane);
     phys0 = __builtin_amdgcn_readlane(hb, 0);
+    // latency-bound launches (a few units per split): the first tiles wait until about 1 us after
+    // this workgroup started, so the workgroups that start later get their query and header loads
+    // through before the tile traffic of the early ones fills the memory queues (llama8b step
+    // 16.2 -> 15.3 us; the wait is bounded by the clock, 100 MHz)
+    if (p.units_per_split <= kHoldUnits) {
+      const uint64_t until = t_entry + kHoldTicks;
+      while (__builtin_amdgcn_s_memrealtime() < until) __builtin_amdgcn_s_sleep(1);
+    }
     const __amdgpu_buffer_rsrc_t r0 = tile_rsrc<D>(c, phys0, h);
     issue_k<D>(t0, r0, lane);
     issue_v<D>(t0, sc0, r0, scales_rsrc(c), phys0, c.H, h, lane);
