@@ -165,7 +165,8 @@ hkv_status hkv_header_table_bytes(int hot_tokens, int block_size, int64_t total_
  * for every length up to the cache's capacity, so one allocation serves all
  * later calls.  The workspace must be zero-filled before its first use: its
  * first bytes hold per-(sequence, kv-head) and per-sequence arrival counters
- * that every call leaves at zero again.  Calls that share a workspace must be ordered on one stream.
+ * and per-(sequence, kv-head) block-claim counters, which every call leaves at
+ * zero again.  Calls that share a workspace must be ordered on one stream.
  * HKV_ERR_INVALID_VALUE if n_q_heads is not a positive multiple of
  * n_kv_heads or k_sel is outside [0, 512]. */
 hkv_status hkv_workspace_bytes(hkv_handle h, const hkv_cache_desc* c, int n_q_heads, int k_sel, size_t* bytes);

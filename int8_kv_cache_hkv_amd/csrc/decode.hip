@@ -422,6 +422,89 @@ __device__ void dense_units(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const Dec
   }
 }
 
+// Physical block of logical block j of sequence b (-1 past the table or for
+// an out-of-range id).  The offset is kept per lane so the wave does not wait
+// for the load where it is issued.
+__device__ __forceinline__ int header_load(const CacheView& c, int b, int j) {
+  const __amdgpu_buffer_rsrc_t rh =
+      make_rsrc(c.headers + static_cast<size_t>(b) * c.max_blocks, static_cast<uint32_t>(c.max_blocks) * 16u);
+  const bool in_table = j < c.max_blocks;
+  const int o = static_cast<int>(opaque_index(static_cast<uint32_t>(in_table ? j * 16 : -1)));
+  const int ph = __builtin_amdgcn_raw_buffer_load_b32(rh, o, 0, 0);  // phys_block at offset 0
+  return in_table ? ph : -1;
+}
+__device__ __forceinline__ int header_phys(const CacheView& c, int hv) {
+  const int ph = __builtin_amdgcn_readfirstlane(hv);
+  return (ph >= 0 && ph < c.num_phys) ? ph : -1;
+}
+
+// One claim on the (sequence, kv-head) unit counter, issued by the whole wave
+// without a branch: the buffer resource covers only the counter's 4 bytes and
+// lane l addresses byte 4l, so the range check drops every lane but lane 0
+// (an out-of-range buffer atomic touches no memory).  The result is read
+// (readfirstlane) only when the claimed unit is needed; a branch around the
+// atomic, or a uniform address (combined by the compiler, which reads the
+// result at once), would make the wave wait for it where it is issued.
+__device__ __forceinline__ unsigned claim_issue(unsigned* work, int lane) {
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(work, 4u);
+  return static_cast<unsigned>(__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(1, r, lane * 4, 0, 0));
+}
+
+// The walk with dynamic unit claims (long resident splits).  Splits that
+// stream the same number of blocks were measured to finish up to 6x apart
+// (memory bandwidth is not shared evenly between workgroups), so after its
+// first unit (split * 4 + w, static: the first memory round needs no claim)
+// each wave claims units from the (sequence, kv-head) counter: unit =
+// nsplit * 4 + claim, until a claim lands past the last unit.  Every unit is
+// claimed exactly once and computed by the wave that claimed it.  Claims run
+// two units ahead: while unit u is computed, the tiles of the next unit are
+// requested (as in the static walk), and the claim for the unit after it is
+// resolved and its header requested.
+// t/phys_u/sc hold the first unit (requested by the caller), un/hn the next
+// unit and its pending header load (un < 0: none), cl the pending claim for
+// the unit after it (valid when un >= 0).
+template <int D, int G>
+__device__ void dense_units_claim(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const DecodeParams& p, int b, int h,
+                                  int bh, int units, int n_cold, int w, int lane, Tiles<D>& t, int u, int phys_u,
+                                  float2 sc, int un, int hn, unsigned cl) {
+  using C = Cfg<D, G>;
+  constexpr int S = kBlockSize;
+  const CacheView& c = p.c;
+  const int base = p.nsplit * kWaves;
+  unsigned* work = p.work + static_cast<size_t>(bh) * kClaimStride;
+  const __amdgpu_buffer_rsrc_t rs = scales_rsrc(c);
+  int phys_n = un >= 0 ? header_phys(c, hn) : -1;
+  while (u >= 0) {
+    const int nv = phys_u >= 0 ? min(S, n_cold - u * S) : 0;
+    const __amdgpu_buffer_rsrc_t rn = tile_rsrc<D>(c, phys_n, h);  // empty when there is no next unit
+    float4_t s[C::NQ];
+    qk_codes_refill<D, G>(t.kr, sm, lane, s, rn);
+    float alpha[C::NG], coef[C::NG];
+    softmax_unit<D, G, false>(st, sm, s, lane < nv, sc.x * p.qscale, 1.f, sc.y, alpha, coef, w, lane);
+    sc = load_scales(rs, phys_n, c.H, h);
+    // the unit after next: resolve its claim, request its header
+    int un2 = -1, hn2 = -1;
+    if (un >= 0) {
+      un2 = base + static_cast<int>(__builtin_amdgcn_readfirstlane(cl));
+      if (un2 >= units) un2 = -1;
+      else hn2 = header_load(c, b, un2);
+    }
+    BlockAcc<D, G> blk;
+    pv_dense_refill<D, G>(blk, sm, t.vr, w, lane, rn);
+    fold_block<D, G>(st, blk, alpha, coef);
+    wave_lds_sync();
+    u = un;
+    phys_u = phys_n;
+    un = un2;
+    if (un >= 0) {
+      phys_n = header_phys(c, hn2);
+      cl = claim_issue(work, lane);
+    } else {
+      phys_n = -1;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- sparse units
 // Up to kSparseUnit selected cold tokens, one per lane (lanes past the unit are
 // masked).  Once the tokens' physical blocks are known, all of the unit's
@@ -533,7 +616,7 @@ __device__ __forceinline__ void copy_query(const _Float16* qg, _Float16 (*qh)[4]
 }
 
 // ---- cold split: stream its units, merge the 4 waves, write the partial
-template <int D, int G, bool SPARSE, bool FUSED>
+template <int D, int G, bool SPARSE, bool FUSED, bool CLAIM>
 __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, int h, int bh, int split) {
   using C = Cfg<D, G>;
   constexpr int S = kBlockSize;
@@ -565,8 +648,17 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
   int phys0 = -1, hb = -1;
   const int32_t* sel_bh = SPARSE ? p.sel + static_cast<size_t>(bh) * p.k_sel : nullptr;
   int sel0 = -1;  // sparse: this wave's first unit's selection entry, requested with the query
+  unsigned cl0 = 0;  // claim walk: the first claim
   if (SPARSE) {
     sel0 = sel_entry(sel_bh, p.k_sel, split * p.units_per_split + w, lane);
+  } else if constexpr (CLAIM) {
+    // claim walk: the first unit is split * 4 + w; the first claim travels with the first round
+    hb = header_load(c, b, split * kWaves + w);
+    cl0 = claim_issue(p.work + static_cast<size_t>(bh) * kClaimStride, lane);
+    phys0 = header_phys(c, hb);
+    const __amdgpu_buffer_rsrc_t r0 = tile_rsrc<D>(c, phys0, h);
+    issue_k<D>(t0, r0, lane);
+    issue_v<D>(t0, sc0, r0, scales_rsrc(c), phys0, c.H, h, lane);
   } else {
     const uint64_t t_entry = __builtin_amdgcn_s_memrealtime();
     hb = header_batch(c, b, 0, split, p.nsplit, p.units_per_split, w, lane);
@@ -619,6 +711,21 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
         gather_unit<D, G>(st, sm, c, idx, b, h, sg.n_cold, p.qscale, w, lane);
       }
     }
+  } else if constexpr (CLAIM) {
+    const int u0 = split * kWaves + w;
+    int un = -1, hn = -1;
+    unsigned cl = 0;
+    if (u0 < units) {  // else units <= nsplit * 4: every claim lands past the last unit
+      un = p.nsplit * kWaves + static_cast<int>(__builtin_amdgcn_readfirstlane(cl0));
+      if (un >= units) {
+        un = -1;
+      } else {
+        hn = header_load(c, b, un);
+        cl = claim_issue(p.work + static_cast<size_t>(bh) * kClaimStride, lane);
+      }
+    }
+    dense_units_claim<D, G>(st, sm, p, b, h, bh, units, sg.n_cold, w, lane, t0, u0 < units ? u0 : -1, phys0, sc0,
+                            un, hn, cl);
   } else {
     dense_units<D, G>(st, sm, p, b, h, split, units, sg.n_cold, w, lane, t0, phys0, sc0, hb);
   }
@@ -1069,7 +1176,7 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G>& am, i
 // the workspace, which the merging workgroup resets to zero.  The merge runs
 // online over groups of kMergeChunk partials whose loads are all in flight
 // together; thread i owns two adjacent output columns of one query head.
-template <int D, int G, bool SPARSE, bool FUSED>
+template <int D, int G, bool SPARSE, bool FUSED, bool CLAIM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G > 4 ? 2 : 4))) void decode_kernel(DecodeParams p) {
   using AppendPart = typename std::conditional<FUSED, AppendSmem<D, G>, DecodeSmem<D, G>>::type;
   __shared__ union Smem {
@@ -1083,16 +1190,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G > 4 
   asm volatile("" ::"s"(p.c.H), "s"(p.c.T), "s"(p.c.max_blocks), "s"(p.c.num_phys), "s"(p.c.hot), "s"(p.c.cold),
                "s"(p.c.scales), "s"(p.c.headers), "s"(p.c.seq_len), "s"(p.q), "s"(p.sel), "s"(p.k_sel),
                "s"(p.partials), "s"(p.counters), "s"(p.nsplit), "s"(p.nparts), "s"(p.units_per_split),
-               "s"(p.xcd_major), "s"(p.qscale));
+               "s"(p.wg_order), "s"(p.work), "s"(p.qscale));
   const CacheView& c = p.c;
-  const WgCoord wg = wg_coord(p.xcd_major != 0);
+  const WgCoord wg = wg_coord(p.wg_order);
   const int split = wg.x;
   const int h = wg.y;
   const int b = wg.z;
   const int bh = b * c.H + h;
   const int tid = threadIdx.x;
   if (split < p.nsplit) {
-    cold_split<D, G, SPARSE, FUSED>(p, sm.cold, b, h, bh, split);
+    cold_split<D, G, SPARSE, FUSED, CLAIM>(p, sm.cold, b, h, bh, split);
   } else if constexpr (FUSED) {
     if (split == p.nsplit) hot_window_split<D, G>(p, sm.hot, b, h, bh);
     else append_unit_split<D, G>(p, sm.app, b, h, bh);
@@ -1153,7 +1260,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G > 4 
     *reinterpret_cast<half2_t*>(&p.out[(static_cast<size_t>(b) * Hq + hq) * D + d]) = o;
     if (d == 0 && p.lse) p.lse[static_cast<size_t>(b) * Hq + hq] = (M + __builtin_log2f(L)) * kLn2;
   }
-  if (tid == 0) __hip_atomic_store(&p.counters[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) {
+    __hip_atomic_store(&p.counters[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (CLAIM) __hip_atomic_store(&p.work[static_cast<size_t>(bh) * kClaimStride], 0u, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+  }
   if constexpr (FUSED) {
     // every workgroup of (b, h) has read seq_len[b] before this merge; the last of the H merges
     // of sequence b publishes the new length (and resets the counter)
@@ -1180,9 +1291,12 @@ hipError_t launch_k(K kernel, dim3 grid, int block, const DecodeParams& p, const
 template <int D, int G>
 hipError_t launch_dg(const DecodeParams& p, const LaunchCtx& ctx) {
   const dim3 grid(p.nparts, p.c.H, p.c.B);  // (split, kv-head, sequence)
-  if (p.k_new) return launch_k(decode_kernel<D, G, false, true>, grid, kThreads, p, ctx);
-  return p.sel ? launch_k(decode_kernel<D, G, true, false>, grid, kThreads, p, ctx)
-               : launch_k(decode_kernel<D, G, false, false>, grid, kThreads, p, ctx);
+  if (p.k_new)
+    return p.work ? launch_k(decode_kernel<D, G, false, true, true>, grid, kThreads, p, ctx)
+                  : launch_k(decode_kernel<D, G, false, true, false>, grid, kThreads, p, ctx);
+  if (p.sel) return launch_k(decode_kernel<D, G, true, false, false>, grid, kThreads, p, ctx);
+  return p.work ? launch_k(decode_kernel<D, G, false, false, true>, grid, kThreads, p, ctx)
+                : launch_k(decode_kernel<D, G, false, false, false>, grid, kThreads, p, ctx);
 }
 
 template <int D>

@@ -39,6 +39,10 @@ using hkv::LaunchCtx;
 
 // Target workgroups per decode/top-K launch: 4 per CU on 256 CUs, 16 waves/CU.
 constexpr int kTargetWorkgroups = 1024;
+// Claim plans (see plan_splits) target 2 workgroups per CU: with fewer waves in flight the loaded
+// memory latency is shorter, and so is the tail of units the waves have claimed ahead (131072-token
+// step, measured: 1024 -> 178, 768 -> 174, 512 -> 171, 384 -> 175, 256 -> 224 us).
+constexpr int kClaimTargetWorkgroups = 512;
 using hkv::kMaxSplits;
 
 bool valid_protocol(int hot_tokens, int block_size) {
@@ -66,9 +70,11 @@ constexpr int64_t kBatchSplitUnits = 32;
 struct SplitPlan {
   int nsplit;
   int per_split;
-  int xcd_major;  // resident plans with long splits read the grid in XCD-major order (see wg_coord)
+  int wg_order;   // workgroup order of the grid (see wg_coord)
+  int claim;      // resident plans with long splits claim their units dynamically (dense decode)
 };
-SplitPlan plan_splits(int64_t bh, int64_t units, int extra_parts = 1, int64_t target_wg = kTargetWorkgroups) {
+SplitPlan plan_splits(int64_t bh, int64_t units, int extra_parts = 1, int64_t target_wg = kTargetWorkgroups,
+                      bool claim_ok = true) {
   units = std::max<int64_t>(1, units);
   const int64_t target = target_wg / bh - extra_parts;
   int64_t per = target >= 2 ? hkv::kWaves * ((units + hkv::kWaves * target - 1) / (hkv::kWaves * target))
@@ -78,9 +84,21 @@ SplitPlan plan_splits(int64_t bh, int64_t units, int extra_parts = 1, int64_t ta
     per = hkv::kWaves * ((units + hkv::kWaves * kMaxSplits - 1) / (hkv::kWaves * kMaxSplits));
     ns = (units + per - 1) / per;
   }
-  // measured: XCD-major order helps long resident splits (131072-token step) and hurts the batch plan
-  const int xcd = target >= 2 && per >= hkv::kXcdMajorUnits ? 1 : 0;
-  return {static_cast<int>(ns), static_cast<int>(per), xcd};
+  // resident plans with long splits claim their units dynamically (static splits of equal size were
+  // measured to finish up to 6x apart) on a grid of kClaimTargetWorkgroups in split-major order;
+  // without claims, XCD-major order helps long resident splits (131072-token step) and hurts the
+  // batch plan
+  const int claim = claim_ok && target >= 2 && per >= hkv::kClaimUnits ? 1 : 0;
+  if (claim) {
+    const int64_t tc = std::max<int64_t>(2, kClaimTargetWorkgroups / bh - extra_parts);
+    if (tc < ns) {  // only ever fewer splits (ns <= kMaxSplits holds)
+      per = hkv::kWaves * ((units + hkv::kWaves * tc - 1) / (hkv::kWaves * tc));
+      ns = (units + per - 1) / per;
+    }
+  }
+  const int order = claim ? hkv::kOrderSplitMajor
+                          : (target >= 2 && per >= hkv::kXcdMajorUnits ? hkv::kOrderXcdMajor : hkv::kOrderPlain);
+  return {static_cast<int>(ns), static_cast<int>(per), order, claim};
 }
 
 // Upper bound of the split count of plan_splits over every unit count in
@@ -146,9 +164,18 @@ size_t partials_bytes(const hkv_ctx* h, const hkv_cache_desc* c, int G, int k_se
   return static_cast<size_t>(bh) * (ns + 2) * G * (h->D + 2) * sizeof(float);
 }
 
-// arrival counters: [B*H] per (sequence, kv-head), then [B] per sequence (fused append + decode)
+// counters: [B*H] arrivals per (sequence, kv-head), [B] per sequence (fused append + decode), then
+// (256-byte aligned) unit claims per (sequence, kv-head), one per 256 bytes: the claims of a
+// (sequence, kv-head) are a steady stream of atomics, and counters that share a cache line would
+// serialise each other's
+size_t claim_offset(const hkv_cache_desc* c, int H) {
+  return align_up(static_cast<size_t>(c->batch) * (H + 1) * sizeof(unsigned), 256);
+}
 size_t counters_bytes(const hkv_cache_desc* c, int H) {
-  return static_cast<size_t>(c->batch) * (H + 1) * sizeof(unsigned);
+  return claim_offset(c, H) + static_cast<size_t>(c->batch) * H * hkv::kClaimStride * sizeof(unsigned);
+}
+unsigned* claim_counters(void* workspace, const hkv_cache_desc* c, int H) {
+  return reinterpret_cast<unsigned*>(static_cast<char*>(workspace) + claim_offset(c, H));
 }
 
 size_t topk_bytes(const hkv_ctx* h, const hkv_cache_desc* c) {
@@ -355,7 +382,8 @@ hkv_status hkv_decode_attn(hkv_handle h, const hkv_cache_desc* c, const void* q,
   p.nsplit = sp.nsplit;
   p.nparts = sp.nsplit + 1;
   p.units_per_split = sp.per_split;
-  p.xcd_major = sp.xcd_major;
+  p.wg_order = sp.wg_order;
+  p.work = (!sel_idx && sp.claim) ? claim_counters(workspace, c, h->H) : nullptr;
   p.qscale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(h->D)));
   p.out = static_cast<_Float16*>(out);
   p.lse = lse;
@@ -404,7 +432,8 @@ hkv_status hkv_append_decode(hkv_handle h, const hkv_cache_desc* c, const void* 
   p.nsplit = sp.nsplit;
   p.nparts = sp.nsplit + 2;
   p.units_per_split = sp.per_split;
-  p.xcd_major = sp.xcd_major;
+  p.wg_order = sp.wg_order;
+  p.work = sp.claim ? claim_counters(workspace, c, h->H) : nullptr;
   p.qscale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(h->D)));
   p.out = static_cast<_Float16*>(out);
   p.lse = lse;
@@ -441,10 +470,10 @@ hkv_status hkv_topk_select(hkv_handle h, const hkv_cache_desc* c, const void* q,
   p.q = static_cast<const _Float16*>(q);
   p.prob = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(counters_bytes(c, h->H), 256));
   // the score kernel holds 64 VGPRs per lane, so 8 of its workgroups fit a CU: twice the decode's grid
-  const SplitPlan sp = plan_splits(static_cast<int64_t>(c->batch) * h->H, blk_max, 1, 2 * kTargetWorkgroups);
+  const SplitPlan sp = plan_splits(static_cast<int64_t>(c->batch) * h->H, blk_max, 1, 2 * kTargetWorkgroups, false);
   p.nsplit = sp.nsplit;
   p.units_per_split = sp.per_split;
-  p.xcd_major = sp.xcd_major;
+  p.wg_order = sp.wg_order;
   p.k = k;
   p.out_idx = out_idx;
   LaunchCtx a = make_ctx(h, stream, HKV_KERNEL_TOPK_SCORE);

@@ -138,21 +138,39 @@ __device__ __forceinline__ int header_batch(const CacheView& c, int b, int kb, i
   return (in_table && ph >= 0 && ph < c.num_phys) ? ph : -1;
 }
 
-// Workgroup coordinates of a 3D grid.  Workgroups are dispatched round-robin
-// over the kXcds dies in linear order; with xcd_major, each die's share of the
-// linear order becomes one contiguous range of logical workgroups (a bijection),
-// so the splits of one (sequence, kv-head) run on one die and each die streams
-// a few contiguous head ranges of the pool.  Measured on the 131072-token step:
-// 186 -> 178 us.  Short splits (latency-bound steps) and grids larger than the
-// resident slots keep the plain order, which measured faster there.
+// Workgroup coordinates of a 3D grid (x = split, y = kv-head, z = sequence).
+// Workgroups are dispatched round-robin over the kXcds dies in linear order,
+// and a workgroup dispatched earlier keeps a lead in memory bandwidth over the
+// ones dispatched after it (measured: in a resident 131072-token launch the
+// splits of the first sequence finished 47 us before those of the last).
+// Orders (each a bijection of the grid):
+//  * kOrderPlain: linear order; short splits (latency-bound steps) and grids
+//    larger than the resident slots, where it measured fastest;
+//  * kOrderXcdMajor: each die's share of the linear order becomes one
+//    contiguous range of logical workgroups, so the splits of one (sequence,
+//    kv-head) run on one die (131072-token step with static splits: 186 ->
+//    178 us);
+//  * kOrderSplitMajor: the linear order runs over (sequence, kv-head) first,
+//    so every (sequence, kv-head) gets early and late workgroups alike, and
+//    round k (split k) is rotated by k pairs, so its workgroups also visit
+//    every die (the dies' bandwidths differ too: up to 25 % in one measured
+//    launch); with dynamic unit claims the fast workgroups of a (sequence,
+//    kv-head) take the larger share and all of them end together.
 struct WgCoord {
   int x, y, z;
 };
-__device__ __forceinline__ WgCoord wg_coord(bool xcd_major) {
+__device__ __forceinline__ WgCoord wg_coord(int order) {
   const int X = gridDim.x, Y = gridDim.y;
-  if (!xcd_major) return {static_cast<int>(blockIdx.x), static_cast<int>(blockIdx.y), static_cast<int>(blockIdx.z)};
+  if (order == kOrderPlain)
+    return {static_cast<int>(blockIdx.x), static_cast<int>(blockIdx.y), static_cast<int>(blockIdx.z)};
   const int N = X * Y * static_cast<int>(gridDim.z);
   const int lin = blockIdx.x + X * (blockIdx.y + Y * blockIdx.z);
+  if (order == kOrderSplitMajor) {
+    const int P = N / X;  // (sequence, kv-head) pairs
+    const int k = lin / P;
+    const int pair = (lin - k * P + k) % P;
+    return {k, pair % Y, pair / Y};
+  }
   const int die = lin % kXcds, k = lin / kXcds;
   const int L = die * (N / kXcds) + min(die, N % kXcds) + k;
   return {L % X, (L / X) % Y, L / (X * Y)};

@@ -17,7 +17,10 @@ constexpr int kSinglePassMaxBlocks = 2;  // appends touching at most this many b
 constexpr int kMaxTopK = 512;       // fixed top-K budget of the sparse path
 constexpr int kSparseUnit = 16;     // selected tokens per wave unit of the sparse decode
 constexpr int kXcds = 8;            // MI355X: accelerator complex dies, each with its own L2
+constexpr int kOrderPlain = 0, kOrderXcdMajor = 1, kOrderSplitMajor = 2;  // workgroup orders of a grid
 constexpr int kXcdMajorUnits = 16;  // resident plans with splits of at least this many units use XCD-major order
+constexpr int kClaimUnits = 16;     // ... and claim their units dynamically (dense decode)
+constexpr int kClaimStride = 64;    // claim counters 256 bytes apart: one cache line each
 constexpr int kMaxSplits = 128;     // cold splits per (sequence, kv-head) at most
 
 // Per-launch timing: when start/stop are non-null the dispatch records them.
@@ -62,7 +65,8 @@ struct DecodeParams {
   int nsplit;              // cold splits per (sequence, kv-head)
   int nparts;              // partial records per (sequence, kv-head): nsplit + 1 (hot zone), + 1 more fused
   int units_per_split;     // units handled per split (multiple of kWaves)
-  int xcd_major;           // 1: workgroups read the grid in XCD-major order
+  int wg_order;            // kOrderPlain / kOrderXcdMajor / kOrderSplitMajor (see wg_coord)
+  unsigned* work;          // [B*H][kClaimStride] unit-claim counters (dense walk), zero between calls; nullptr: static
   float qscale;            // log2(e) / sqrt(D)
   _Float16* out;           // [B][H*G][D]
   float* lse;              // [B][H*G] or nullptr
@@ -79,7 +83,7 @@ struct TopkParams {
   float* prob;             // [B][H][max_blocks*S] window probabilities
   int nsplit;
   int units_per_split;
-  int xcd_major;           // 1: workgroups read the grid in XCD-major order
+  int wg_order;            // kOrderPlain / kOrderXcdMajor / kOrderSplitMajor (see wg_coord)
   int k;
   int32_t* out_idx;        // [B][H][k]
 };

@@ -99,10 +99,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   __shared__ float qinv[4 * NQ];           // 1 / |q_g| (0 for a zero query or a padding row)
   asm volatile("" ::"s"(p.c.H), "s"(p.c.T), "s"(p.c.max_blocks), "s"(p.c.num_phys), "s"(p.c.cold),
                "s"(p.c.headers), "s"(p.c.seq_len), "s"(p.q), "s"(p.prob), "s"(p.nsplit), "s"(p.units_per_split),
-               "s"(p.xcd_major));
+               "s"(p.wg_order));
   const CacheView& c = p.c;
   const int H = c.H;
-  const WgCoord wg = wg_coord(p.xcd_major != 0);
+  const WgCoord wg = wg_coord(p.wg_order);
   const int split = wg.x, h = wg.y, b = wg.z;
   const int bh = b * H + h;
   const int tid = threadIdx.x, lane = tid & 63;

@@ -376,12 +376,13 @@ def test_hot_tokens_variants(T):
 
 
 # ------------------------------------------------------------------ XCD-major order on a grid not a multiple of 8
-def test_xcd_major_order_odd_grid():
-    """3 sequences x 3 kv-heads with ~86k tokens: the resident plan has splits of 16 units, so the
-    grid is read in XCD-major order, and its 86 x 3 x 3 = 774 workgroups are not a multiple of the 8
-    dies.  Every output against the oracle, plain decode and a fused step."""
+def test_claim_walk_odd_grid():
+    """3 sequences x 3 kv-heads with ~86k tokens: a resident plan with long splits, so the waves claim
+    their blocks dynamically and the grid is read in the rotated split-major order over 9 (sequence,
+    kv-head) pairs, with a workgroup count that is not a multiple of the 8 dies.  Every output
+    against the oracle, plain decode and a fused step."""
     import dataclasses
-    w = dataclasses.replace(wl.WORKLOADS["long"], name="xcd_odd", batch=3, n_kv_heads=3, n_q_heads=6)
+    w = dataclasses.replace(wl.WORKLOADS["long"], name="claim_odd", batch=3, n_kv_heads=3, n_q_heads=6)
     n = 32 + 1345 * 64 + 17
     cache = gh.make_cache(w, n + 8)
     gh.fill(cache, w, [n] * w.batch, chunk=8192)
@@ -390,13 +391,46 @@ def test_xcd_major_order_odd_grid():
     st = _oracle_states(w, [n] * w.batch)
     for b in range(w.batch):
         o_ref, l_ref = orc.decode(q[b], st[b])
-        gh.compare_out(out[b], o_ref, f"xcd-major b={b}")
-        gh.compare_lse(lse[b], l_ref, f"xcd-major b={b}")
+        gh.compare_out(out[b], o_ref, f"claim odd grid b={b}")
+        gh.compare_lse(lse[b], l_ref, f"claim odd grid b={b}")
     out_f, _ = _append_decode(cache, w, [n] * w.batch, q)
     st1 = _oracle_states(w, [n + 1] * w.batch)
     for b in range(w.batch):
         o_ref, _ = orc.decode(q[b], st1[b])
-        gh.compare_out(out_f[b], o_ref, f"xcd-major fused b={b}")
+        gh.compare_out(out_f[b], o_ref, f"claim odd grid fused b={b}")
+
+
+def test_claim_walk_ragged_batch():
+    """32 sequences x 8 kv-heads, lengths from 40 tokens to 100 cold blocks, blocks at a permuted
+    physical placement: the resident plan has splits of at least 16 blocks, so after their first
+    block the waves claim blocks from the per-(sequence, kv-head) counters.  Sequences with fewer
+    blocks than the static first round (every claim lands past the end), with exactly one claimable
+    block, and with many.  Plain decode twice (the second call finds the counters back at zero),
+    then a fused step; every output against the oracle."""
+    import dataclasses
+    w = dataclasses.replace(wl.WORKLOADS["llama8b"], name="claim", batch=32)
+    rng = np.random.default_rng(11)
+    lens = [40, 32 + 64 * 11, 32 + 64 * 12 + 5, 32 + 64 * 100] + rng.integers(100, 32 + 64 * 100, 28).tolist()
+    cap = max(lens) + 8
+    mb = -(-(cap - 32) // 64)
+    perm = rng.permutation(w.batch * mb).reshape(w.batch, mb)
+    cache = gh.make_cache(w, cap, phys_ids=perm)
+    gh.fill(cache, w, lens)
+    q = wl.queries(w, step=7)
+    o1, l1 = _decode(cache, q)
+    o2, l2 = _decode(cache, q)
+    st = _oracle_states(w, lens)
+    for b in range(w.batch):
+        o_ref, l_ref = orc.decode(q[b], st[b])
+        for o, l, tag in ((o1, l1, "first"), (o2, l2, "second")):
+            gh.compare_out(o[b], o_ref, f"claim {tag} b={b} n={lens[b]}")
+            gh.compare_lse(l[b], l_ref, f"claim {tag} b={b}")
+    out_f, lse_f = _append_decode(cache, w, lens, q)
+    st1 = _oracle_states(w, [n + 1 for n in lens])
+    for b in range(w.batch):
+        o_ref, l_ref = orc.decode(q[b], st1[b])
+        gh.compare_out(out_f[b], o_ref, f"claim fused b={b} n={lens[b]}")
+        gh.compare_lse(lse_f[b], l_ref, f"claim fused b={b}")
 
 
 # ------------------------------------------------------------------ long context, sampled
