@@ -422,34 +422,6 @@ __device__ void dense_units(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const Dec
   }
 }
 
-// Physical block of logical block j of sequence b (-1 past the table or for
-// an out-of-range id).  The offset is kept per lane so the wave does not wait
-// for the load where it is issued.
-__device__ __forceinline__ int header_load(const CacheView& c, int b, int j) {
-  const __amdgpu_buffer_rsrc_t rh =
-      make_rsrc(c.headers + static_cast<size_t>(b) * c.max_blocks, static_cast<uint32_t>(c.max_blocks) * 16u);
-  const bool in_table = j < c.max_blocks;
-  const int o = static_cast<int>(opaque_index(static_cast<uint32_t>(in_table ? j * 16 : -1)));
-  const int ph = __builtin_amdgcn_raw_buffer_load_b32(rh, o, 0, 0);  // phys_block at offset 0
-  return in_table ? ph : -1;
-}
-__device__ __forceinline__ int header_phys(const CacheView& c, int hv) {
-  const int ph = __builtin_amdgcn_readfirstlane(hv);
-  return (ph >= 0 && ph < c.num_phys) ? ph : -1;
-}
-
-// One claim on the (sequence, kv-head) unit counter, issued by the whole wave
-// without a branch: the buffer resource covers only the counter's 4 bytes and
-// lane l addresses byte 4l, so the range check drops every lane but lane 0
-// (an out-of-range buffer atomic touches no memory).  The result is read
-// (readfirstlane) only when the claimed unit is needed; a branch around the
-// atomic, or a uniform address (combined by the compiler, which reads the
-// result at once), would make the wave wait for it where it is issued.
-__device__ __forceinline__ unsigned claim_issue(unsigned* work, int lane) {
-  const __amdgpu_buffer_rsrc_t r = make_rsrc(work, 4u);
-  return static_cast<unsigned>(__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(1, r, lane * 4, 0, 0));
-}
-
 // The walk with dynamic unit claims (long resident splits).  Splits that
 // stream the same number of blocks were measured to finish up to 6x apart
 // (memory bandwidth is not shared evenly between workgroups), so after its

@@ -43,6 +43,7 @@ constexpr int kTargetWorkgroups = 1024;
 // memory latency is shorter, and so is the tail of units the waves have claimed ahead (131072-token
 // step, measured: 1024 -> 178, 768 -> 174, 512 -> 171, 384 -> 175, 256 -> 224 us).
 constexpr int kClaimTargetWorkgroups = 512;
+constexpr int kTopkClaimTargetWorkgroups = 1024;
 using hkv::kMaxSplits;
 
 bool valid_protocol(int hot_tokens, int block_size) {
@@ -74,7 +75,7 @@ struct SplitPlan {
   int claim;      // resident plans with long splits claim their units dynamically (dense decode)
 };
 SplitPlan plan_splits(int64_t bh, int64_t units, int extra_parts = 1, int64_t target_wg = kTargetWorkgroups,
-                      bool claim_ok = true) {
+                      int64_t claim_target_wg = kClaimTargetWorkgroups) {
   units = std::max<int64_t>(1, units);
   const int64_t target = target_wg / bh - extra_parts;
   int64_t per = target >= 2 ? hkv::kWaves * ((units + hkv::kWaves * target - 1) / (hkv::kWaves * target))
@@ -88,9 +89,9 @@ SplitPlan plan_splits(int64_t bh, int64_t units, int extra_parts = 1, int64_t ta
   // measured to finish up to 6x apart) on a grid of kClaimTargetWorkgroups in split-major order;
   // without claims, XCD-major order helps long resident splits (131072-token step) and hurts the
   // batch plan
-  const int claim = claim_ok && target >= 2 && per >= hkv::kClaimUnits ? 1 : 0;
+  const int claim = claim_target_wg > 0 && target >= 2 && per >= hkv::kClaimUnits ? 1 : 0;
   if (claim) {
-    const int64_t tc = std::max<int64_t>(2, kClaimTargetWorkgroups / bh - extra_parts);
+    const int64_t tc = std::max<int64_t>(2, claim_target_wg / bh - extra_parts);
     if (tc < ns) {  // only ever fewer splits (ns <= kMaxSplits holds)
       per = hkv::kWaves * ((units + hkv::kWaves * tc - 1) / (hkv::kWaves * tc));
       ns = (units + per - 1) / per;
@@ -469,11 +470,15 @@ hkv_status hkv_topk_select(hkv_handle h, const hkv_cache_desc* c, const void* q,
   p.G = G;
   p.q = static_cast<const _Float16*>(q);
   p.prob = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(counters_bytes(c, h->H), 256));
-  // the score kernel holds 64 VGPRs per lane, so 8 of its workgroups fit a CU: twice the decode's grid
-  const SplitPlan sp = plan_splits(static_cast<int64_t>(c->batch) * h->H, blk_max, 1, 2 * kTargetWorkgroups, false);
+  // the score kernel holds at most 64 VGPRs per lane (D = 128, G <= 4), so 8 of its workgroups fit a
+  // CU: twice the decode's grid; its claim plans take 4 per CU (32768-token workload, measured:
+  // static splits 98.6 us, claims on 512 / 1024 / 2048 workgroups 98.5 / 91.3 / 92.7 us)
+  const SplitPlan sp = plan_splits(static_cast<int64_t>(c->batch) * h->H, blk_max, 1, 2 * kTargetWorkgroups,
+                                   kTopkClaimTargetWorkgroups);
   p.nsplit = sp.nsplit;
   p.units_per_split = sp.per_split;
   p.wg_order = sp.wg_order;
+  p.work = sp.claim ? claim_counters(workspace, c, h->H) : nullptr;
   p.k = k;
   p.out_idx = out_idx;
   LaunchCtx a = make_ctx(h, stream, HKV_KERNEL_TOPK_SCORE);

@@ -84,6 +84,7 @@ struct TopkParams {
   int nsplit;
   int units_per_split;
   int wg_order;            // kOrderPlain / kOrderXcdMajor / kOrderSplitMajor (see wg_coord)
+  unsigned* work;          // [B*H][kClaimStride] unit-claim counters of the score walk; nullptr: static walk
   int k;
   int32_t* out_idx;        // [B][H][k]
 };

@@ -30,6 +30,7 @@ namespace hkv {
 namespace detail {
 
 constexpr float kNegInfT = -__builtin_inff();
+constexpr int kStage = 16;  // claim walk: units whose probabilities are staged in LDS before a write-out
 constexpr int kSelThreads = 1024;
 
 // Window probabilities of one cold block from its K codes: kr[ch] holds codes
@@ -50,17 +51,25 @@ __device__ __forceinline__ float window_scores(uint4 (&kr)[D / 16], const _Float
 #pragma unroll
   for (int ch = 0; ch < D / 16; ++ch) {
     asm volatile("" ::: "memory");  // keep the chunks in order: each refill is issued right after its use
+    half4_t bk[4];
 #pragma unroll
     for (int wd = 0; wd < 4; ++wd) {
       const uint32_t word = word_of(kr[ch], wd);
       n2 = __builtin_amdgcn_sdot4(static_cast<int>(word), static_cast<int>(word), n2, false);
-      const half4_t bk = codes_to_half4(word);
+      bk[wd] = codes_to_half4(word);
+    }
+    // every read of the chunk happens before the load that refills its registers: a read left
+    // after it would need the old value in other registers, and the copy back at the end of the
+    // walk's iteration would wait for every load in flight
+    asm volatile("" ::"v"(bk[0]), "v"(bk[1]), "v"(bk[2]), "v"(bk[3]), "v"(n2) : "memory");
+    kr[ch] = load_stream_buf(rn, lo + ch * S * 16);
+#pragma unroll
+    for (int wd = 0; wd < 4; ++wd) {
       const int k0 = ch * 16 + wd * 4;
 #pragma unroll
       for (int quad = 0; quad < NQ; ++quad)
-        s[quad] = mfma_qk(*reinterpret_cast<const half4_t*>(&qh[quad][lane & 3][k0]), bk, s[quad]);
+        s[quad] = mfma_qk(*reinterpret_cast<const half4_t*>(&qh[quad][lane & 3][k0]), bk[wd], s[quad]);
     }
-    kr[ch] = load_stream_buf(rn, lo + ch * S * 16);
   }
   asm volatile("" ::: "memory");
   // c_t = mean over the G query heads of cos(q_g, code_t); cosine is scale-free, so codes suffice
@@ -89,7 +98,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t k_tile_rsrc(const CacheView& c
 // Grid (split, kv-head, sequence).  Each wave walks its cold blocks (the same
 // walk as the decode's dense units); the first block's tile is requested with
 // the query, each next one while the current one is scored.
-template <int D, int G>
+template <int D, int G, bool CLAIM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void topk_score_kernel(TopkParams p) {
   constexpr int S = kBlockSize;
   constexpr int NQ = (G + 3) / 4;          // groups of 4 query heads (MFMA rows)
@@ -97,9 +106,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   constexpr int VPR = D / 8;               // 16-byte vectors per query row
   __shared__ _Float16 qh[NQ][4][QROW];
   __shared__ float qinv[4 * NQ];           // 1 / |q_g| (0 for a zero query or a padding row)
+  __shared__ float pstage[CLAIM ? kWaves : 1][kStage][64];  // claim walk: staged window probabilities
+  __shared__ int ustage[CLAIM ? kWaves : 1][kStage];
   asm volatile("" ::"s"(p.c.H), "s"(p.c.T), "s"(p.c.max_blocks), "s"(p.c.num_phys), "s"(p.c.cold),
                "s"(p.c.headers), "s"(p.c.seq_len), "s"(p.q), "s"(p.prob), "s"(p.nsplit), "s"(p.units_per_split),
-               "s"(p.wg_order));
+               "s"(p.wg_order), "s"(p.work));
   const CacheView& c = p.c;
   const int H = c.H;
   const WgCoord wg = wg_coord(p.wg_order);
@@ -114,8 +125,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const bool q_ok = tid < G * VPR;
   const u32x4_t qv = reinterpret_cast<const u32x4_t*>(qg)[q_ok ? qi : 0];
   const int n_seq_lane = c.seq_len[opaque_index(b)];
-  int hb = header_batch(c, b, 0, split, p.nsplit, CU, w, lane);
-  int phys = __builtin_amdgcn_readlane(hb, 0);
+  unsigned* work = CLAIM ? p.work + static_cast<size_t>(bh) * kClaimStride : nullptr;
+  unsigned cl = 0;  // claim walk: the first claim travels with the first round
+  int hb = CLAIM ? header_load(c, b, split * kWaves + w) : header_batch(c, b, 0, split, p.nsplit, CU, w, lane);
+  if (CLAIM) cl = claim_issue(work, lane);
+  int phys = CLAIM ? header_phys(c, hb) : __builtin_amdgcn_readlane(hb, 0);
   uint4 kr[D / 16];
   {
     const __amdgpu_buffer_rsrc_t r0 = k_tile_rsrc<D>(c, phys, h);
@@ -144,6 +158,56 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const int units = min(sg.n_blk, c.max_blocks);
   const size_t cap = static_cast<size_t>(c.max_blocks) * S;
   float* prob = p.prob + static_cast<size_t>(bh) * cap;
+  if constexpr (CLAIM) {
+    // Claim walk (see the decode's): the first unit is split * 4 + w, then units nsplit * 4 + claim.
+    // A unit's chain is claim -> header -> tiles, each given a whole unit of time: at the start of
+    // the unit computed in iteration j, the next unit's header and the claim for the one after it
+    // (both issued at the start of iteration j - 1) are resolved, that unit's header is requested
+    // and the next claim issued; so claims run three units ahead.  The loop has no branch around a
+    // memory operation (a claim after one that landed past the end lands past it too, a header
+    // past the end is read and ignored), and no store: a store pending beside the loads makes
+    // every later wait a wait for all of them (stores and loads share the counter and may complete
+    // out of order), so the probabilities of kStage units are staged in LDS and written out
+    // together.
+    const int base = p.nsplit * kWaves;
+    int u = split * kWaves + w;
+    if (u >= units) return;  // then units <= base: every claim lands past the end
+    int un = base + static_cast<int>(__builtin_amdgcn_readfirstlane(cl));
+    int hn = header_load(c, b, un);
+    cl = claim_issue(work, lane);
+    int nst = 0;
+    auto flush = [&]() {
+#pragma unroll 1
+      for (int k = 0; k < nst; ++k)
+        prob[static_cast<size_t>(ustage[w][k]) * S + lane] = pstage[w][k][lane];
+      nst = 0;
+      // drain here, once per kStage units, so that no store is pending in the loop's other waits
+      __builtin_amdgcn_s_waitcnt(0);
+    };
+    while (u >= 0) {
+      const int phys_n = un < units ? header_phys(c, hn) : -1;
+      const int un2 = base + static_cast<int>(__builtin_amdgcn_readfirstlane(cl));
+      const int hn2 = header_load(c, b, un2);
+      cl = claim_issue(work, lane);
+      const int nv = min(S, sg.n_cold - u * S);
+      const float pr = window_scores<D, G>(kr, qh, qinv, lane, nv, k_tile_rsrc<D>(c, phys_n, h));
+      // a block without a valid physical id contributes probability 0 (its tokens are never
+      // attended); lanes past the last cold token write row entries the selection never reads
+      pstage[w][nst][lane] = phys >= 0 && lane < nv ? pr : 0.f;
+      if (lane == 0) ustage[w][nst] = u;
+      if (++nst == kStage) {
+        wave_lds_sync();
+        flush();
+      }
+      u = un < units ? un : -1;
+      phys = phys_n;
+      un = un2;
+      hn = hn2;
+    }
+    wave_lds_sync();
+    flush();
+    return;
+  }
   int kb = 0;  // walk index of lane 0 of the header batch
   auto phys_of = [&](int k) -> int {
     if (k - kb >= 64) {
@@ -419,6 +483,9 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkParams p) 
   const int bh = blockIdx.x;
   const int b = bh / c.H;
   const int tid = threadIdx.x;
+  // the score launch before this one is complete: its claim counter goes back to zero
+  if (p.work && tid == 0)
+    __hip_atomic_store(p.work + static_cast<size_t>(bh) * kClaimStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const SeqGeom sg = seq_geom(c.seq_len[b], c.T, S);
   const int n = min(sg.n_cold, c.max_blocks * S);  // never read past this (sequence, head)'s row
   const int K = p.k;
@@ -447,7 +514,8 @@ hipError_t launch_t(Kf kernel, dim3 grid, int block, const TopkParams& p, const 
 
 template <int D, int G>
 hipError_t launch_tg(const TopkParams& p, const LaunchCtx& a, const LaunchCtx& b) {
-  hipError_t e = launch_t(topk_score_kernel<D, G>, dim3(p.nsplit, p.c.H, p.c.B), kThreads, p, a);
+  hipError_t e = p.work ? launch_t(topk_score_kernel<D, G, true>, dim3(p.nsplit, p.c.H, p.c.B), kThreads, p, a)
+                        : launch_t(topk_score_kernel<D, G, false>, dim3(p.nsplit, p.c.H, p.c.B), kThreads, p, a);
   if (e != hipSuccess) return e;
   return launch_t(topk_select_kernel, dim3(p.c.B * p.c.H), kSelThreads, p, b);
 }
