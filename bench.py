@@ -317,16 +317,16 @@ def sparse_leg(hkv, torch, steps):
             "topk_score_gbs": score_b / (km["topk_score"] * 1e-3) / 1e9 if km["topk_score"] else None}
 
 
-def ragged_leg(hkv, torch, steps=64, R=4):
+def ragged_leg(hkv, torch, steps=64, R=4, warmup=8):
     """The ragged paged batch: 64 sequences of seeded lengths in [128, 8192], cold blocks at a seeded
     permutation of the physical pool, `steps` decode steps (one token appended per sequence, then a
     dense decode), rotating over R instances; fused launches and, separately, the two-call form so the
-    append is timed on its own."""
+    append is timed on its own.  `warmup` untimed steps of each form come first."""
     import workloads as wl
     w = wl.WORKLOADS["ragged"]
     B, H, Hq, d = w.batch, w.n_kv_heads, w.n_q_heads, w.head_dim
     lens0 = [int(x) for x in wl.lengths(w)]
-    per_inst = -(-2 * steps // R) + 1
+    per_inst = -(-2 * (steps + warmup) // R) + 1
     cap = max(lens0) + per_inst + 1
     mb = -(-(cap - w.hot_tokens) // w.block_size)
     perm = wl.block_permutation(w, B * mb).reshape(B, mb)
@@ -376,6 +376,8 @@ def ragged_leg(hkv, torch, steps=64, R=4):
     res = {"workload": f"ragged: {B} sequences, lengths {min(lens0)}..{max(lens0)} (seeded uniform), permuted "
                        f"physical blocks, step = append 1 token/seq + dense decode"}
     for fused in (True, False):
+        for i in range(warmup):
+            step(i, fused)
         for c in insts:
             hkv.hkv_timing_enable(c.handle, True)
         nbytes = 0

@@ -433,6 +433,34 @@ def test_claim_walk_ragged_batch():
         gh.compare_lse(lse_f[b], l_ref, f"claim fused b={b}")
 
 
+@pytest.mark.parametrize("d,g", [(64, 1), (64, 8), (128, 1), (128, 2), (128, 8)])
+def test_claim_walk_group_sizes(d, g):
+    """The claim walk in every other built (head_dim, GQA group) instance (d = 128, G = 4 runs in the
+    tests above): 16 sequences x 8 kv-heads of 70 to 95 cold blocks, so the plain and the fused plan
+    both have splits of at least 16 blocks; plain decode and a fused step against the oracle."""
+    import dataclasses
+    w = dataclasses.replace(wl.WORKLOADS["llama8b"], name=f"claim_d{d}_g{g}", batch=16, n_kv_heads=8,
+                            n_q_heads=8 * g, head_dim=d)
+    rng = np.random.default_rng(100 * d + g)
+    lens = (32 + 64 * rng.integers(70, 96, w.batch) + rng.integers(0, 64, w.batch)).tolist()
+    lens[0] = 32 + 64 * 95 + 5  # the longest sequence sets the plan: splits of 32 (plain) / 48 (fused) blocks
+    cache = gh.make_cache(w, max(lens) + 8)
+    gh.fill(cache, w, lens)
+    q = wl.queries(w, step=3)
+    out, lse = _decode(cache, q)
+    st = _oracle_states(w, lens)
+    for b in range(w.batch):
+        o_ref, l_ref = orc.decode(q[b], st[b])
+        gh.compare_out(out[b], o_ref, f"claim d={d} g={g} b={b}")
+        gh.compare_lse(lse[b], l_ref, f"claim d={d} g={g} b={b}")
+    out_f, lse_f = _append_decode(cache, w, lens, q)
+    st1 = _oracle_states(w, [n + 1 for n in lens])
+    for b in range(w.batch):
+        o_ref, l_ref = orc.decode(q[b], st1[b])
+        gh.compare_out(out_f[b], o_ref, f"claim fused d={d} g={g} b={b}")
+        gh.compare_lse(lse_f[b], l_ref, f"claim fused d={d} g={g} b={b}")
+
+
 # ------------------------------------------------------------------ long context, sampled
 def test_long_config_parity_sampled():
     w = wl.WORKLOADS["long"]
