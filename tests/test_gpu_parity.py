@@ -569,3 +569,13 @@ def test_topk_config_parity_sampled():
         o_ref, l_ref = orc.sparse_decode(q[b], st, got[b])
         gh.compare_out(out[b], o_ref, f"sparse b={b}")
         gh.compare_lse(lse[b], l_ref, f"sparse b={b}")
+    # the dense decode of this cache and the top-K score both claim blocks from the counters of the
+    # one workspace the cache keeps: a dense decode, then top-K again, must see them back at zero
+    out_d, lse_d = _decode(cache, q)
+    idx2 = cache.topk(qd, w.k_sel).cpu().numpy()
+    assert np.array_equal(idx2, got), "top-K differs after a dense decode on the same workspace"
+    for b in (0, w.batch - 1):
+        st = _oracle_states(w, [n], [b])[0]
+        o_ref, l_ref = orc.decode(q[b], st)
+        gh.compare_out(out_d[b], o_ref, f"dense after top-K b={b}")
+        gh.compare_lse(lse_d[b], l_ref, f"dense after top-K b={b}")
