@@ -40,6 +40,7 @@
 // a wave always has about one unit's loads in flight.
 #include <hip/hip_ext.h>
 
+#include <cstring>
 #include <type_traits>
 
 #include "hkv_device.h"
@@ -1149,7 +1150,7 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G>& am, i
 // online over groups of kMergeChunk partials whose loads are all in flight
 // together; thread i owns two adjacent output columns of one query head.
 template <int D, int G, bool SPARSE, bool FUSED, bool CLAIM>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G > 4 ? 2 : 4))) void decode_kernel(DecodeParams p) {
+__device__ __forceinline__ void decode_body(const DecodeParams& p, const WgCoord wg) {
   using AppendPart = typename std::conditional<FUSED, AppendSmem<D, G>, DecodeSmem<D, G>>::type;
   __shared__ union Smem {
     DecodeSmem<D, G> cold;
@@ -1157,14 +1158,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G > 4 
     AppendPart app;
   } sm;
   __shared__ int s_last;
-  // grid (split, kv-head, sequence), read in XCD-major order for long splits; every argument the
-  // kernel uses is consumed here, so its scalar loads are issued together and waited for once
-  asm volatile("" ::"s"(p.c.H), "s"(p.c.T), "s"(p.c.max_blocks), "s"(p.c.num_phys), "s"(p.c.hot), "s"(p.c.cold),
-               "s"(p.c.scales), "s"(p.c.headers), "s"(p.c.seq_len), "s"(p.q), "s"(p.sel), "s"(p.k_sel),
-               "s"(p.partials), "s"(p.counters), "s"(p.nsplit), "s"(p.nparts), "s"(p.units_per_split),
-               "s"(p.wg_order), "s"(p.work), "s"(p.qscale));
   const CacheView& c = p.c;
-  const WgCoord wg = wg_coord(p.wg_order);
   const int split = wg.x;
   const int h = wg.y;
   const int b = wg.z;
@@ -1249,8 +1243,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G > 4 
   }
 }
 
-template <typename K>
-hipError_t launch_k(K kernel, dim3 grid, int block, const DecodeParams& p, const LaunchCtx& ctx) {
+// Every argument the kernel uses is consumed at entry, so its scalar loads are issued together and
+// waited for once.
+__device__ __forceinline__ void consume_args(const DecodeParams& p) {
+  asm volatile("" ::"s"(p.c.H), "s"(p.c.T), "s"(p.c.max_blocks), "s"(p.c.num_phys), "s"(p.c.hot), "s"(p.c.cold),
+               "s"(p.c.scales), "s"(p.c.headers), "s"(p.c.seq_len), "s"(p.q), "s"(p.sel), "s"(p.k_sel),
+               "s"(p.partials), "s"(p.counters), "s"(p.nsplit), "s"(p.nparts), "s"(p.units_per_split),
+               "s"(p.wg_order), "s"(p.work), "s"(p.qscale));
+}
+
+// Grid (split, kv-head, sequence) in the plan's workgroup order (see wg_coord).
+template <int D, int G, bool SPARSE, bool FUSED, bool CLAIM>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G > 4 ? 2 : 4))) void decode_kernel(DecodeParams p) {
+  consume_args(p);
+  decode_body<D, G, SPARSE, FUSED, CLAIM>(p, wg_coord(p.wg_order));
+}
+
+// Batch plans: the same grid read in the host-built order of the table (see wg_coord_table); a kernel
+// of its own, so the table does not enlarge the arguments of every other launch.
+template <int D, int G, bool FUSED>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G > 4 ? 2 : 4))) void decode_kernel_ordered(
+    DecodeParamsOrdered po) {
+  consume_args(po.p);
+  decode_body<D, G, false, FUSED, false>(po.p, wg_coord_table(po.order, po.p.nsplit));
+}
+
+template <typename K, typename P>
+hipError_t launch_k(K kernel, dim3 grid, int block, const P& p, const LaunchCtx& ctx) {
   if (grid.x == 0 || grid.y == 0 || grid.z == 0) return hipSuccess;
   if (ctx.start) {
     hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(block), 0, ctx.stream, ctx.start, ctx.stop, 0, p);
@@ -1261,8 +1280,15 @@ hipError_t launch_k(K kernel, dim3 grid, int block, const DecodeParams& p, const
 }
 
 template <int D, int G>
-hipError_t launch_dg(const DecodeParams& p, const LaunchCtx& ctx) {
+hipError_t launch_dg(const DecodeParams& p, const LaunchCtx& ctx, const uint16_t* order) {
   const dim3 grid(p.nparts, p.c.H, p.c.B);  // (split, kv-head, sequence)
+  if (order && !p.sel && !p.work) {
+    DecodeParamsOrdered po;
+    po.p = p;
+    std::memcpy(po.order, order, sizeof(po.order));
+    return p.k_new ? launch_k(decode_kernel_ordered<D, G, true>, grid, kThreads, po, ctx)
+                   : launch_k(decode_kernel_ordered<D, G, false>, grid, kThreads, po, ctx);
+  }
   if (p.k_new)
     return p.work ? launch_k(decode_kernel<D, G, false, true, true>, grid, kThreads, p, ctx)
                   : launch_k(decode_kernel<D, G, false, true, false>, grid, kThreads, p, ctx);
@@ -1272,12 +1298,12 @@ hipError_t launch_dg(const DecodeParams& p, const LaunchCtx& ctx) {
 }
 
 template <int D>
-hipError_t launch_d(const DecodeParams& p, const LaunchCtx& a) {
+hipError_t launch_d(const DecodeParams& p, const LaunchCtx& a, const uint16_t* order) {
   switch (p.G) {
-    case 1: return launch_dg<D, 1>(p, a);
-    case 2: return launch_dg<D, 2>(p, a);
-    case 4: return launch_dg<D, 4>(p, a);
-    case 8: return launch_dg<D, 8>(p, a);
+    case 1: return launch_dg<D, 1>(p, a, order);
+    case 2: return launch_dg<D, 2>(p, a, order);
+    case 4: return launch_dg<D, 4>(p, a, order);
+    case 8: return launch_dg<D, 8>(p, a, order);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1286,8 +1312,8 @@ hipError_t launch_d(const DecodeParams& p, const LaunchCtx& a) {
 
 using namespace detail;
 
-hipError_t launch_decode(const DecodeParams& p, const LaunchCtx& ctx) {
-  return p.c.D == 128 ? launch_d<128>(p, ctx) : launch_d<64>(p, ctx);
+hipError_t launch_decode(const DecodeParams& p, const LaunchCtx& ctx, const uint16_t* order) {
+  return p.c.D == 128 ? launch_d<128>(p, ctx, order) : launch_d<64>(p, ctx, order);
 }
 
 }  // namespace hkv

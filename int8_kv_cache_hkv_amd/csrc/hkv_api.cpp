@@ -73,6 +73,7 @@ struct SplitPlan {
   int per_split;
   int wg_order;   // workgroup order of the grid (see wg_coord)
   int claim;      // resident plans with long splits claim their units dynamically (dense decode)
+  int batch;      // batch plan: splits of kBatchSplitUnits, scheduled as resident slots free up
 };
 SplitPlan plan_splits(int64_t bh, int64_t units, int extra_parts = 1, int64_t target_wg = kTargetWorkgroups,
                       int64_t claim_target_wg = kClaimTargetWorkgroups) {
@@ -99,7 +100,7 @@ SplitPlan plan_splits(int64_t bh, int64_t units, int extra_parts = 1, int64_t ta
   }
   const int order = claim ? hkv::kOrderSplitMajor
                           : (target >= 2 && per >= hkv::kXcdMajorUnits ? hkv::kOrderXcdMajor : hkv::kOrderPlain);
-  return {static_cast<int>(ns), static_cast<int>(per), order, claim};
+  return {static_cast<int>(ns), static_cast<int>(per), order, claim, target < 2 ? 1 : 0};
 }
 
 // Upper bound of the split count of plan_splits over every unit count in
@@ -116,6 +117,25 @@ int max_splits(int64_t bh, int64_t units_cap) {
 // Sparse decode: one unit of kSparseUnit selected tokens per wave, so every
 // gather chain of a call runs concurrently (k_sel <= kMaxTopK keeps this to a
 // few splits per (sequence, kv-head)).
+// Batch plans run in several rounds of the resident slots; a split that starts in the last round
+// with a full run of blocks ends long after the rest (a list-scheduling model of the 64-sequence
+// ragged batch: makespan 1.6x the mean slot load in sequence order, 1.2x longest first).  So the
+// cold-split groups are dispatched by their block count, most first (ties: sequence, split), after
+// the short hot-zone and append groups.  units[b]: the blocks of sequence b this launch attends.
+// Returns false (plain order kept) when the table cannot hold the groups.
+bool order_by_work(const hkv::DecodeParams& p, const std::vector<int64_t>& units, int64_t per, uint16_t* order) {
+  const int B = static_cast<int>(units.size());
+  if (static_cast<int64_t>(B) * p.nsplit > hkv::kOrderTableMax || B > 511) return false;
+  std::vector<std::pair<int64_t, int>> v;
+  v.reserve(static_cast<size_t>(B) * p.nsplit);
+  for (int b = 0; b < B; ++b)
+    for (int s = 0; s < p.nsplit; ++s)
+      v.push_back({-std::max<int64_t>(0, std::min<int64_t>(per, units[b] - s * per)), (b << 7) | s});
+  std::stable_sort(v.begin(), v.end(), [](const auto& x, const auto& y) { return x.first < y.first; });
+  for (size_t i = 0; i < v.size(); ++i) order[i] = static_cast<uint16_t>(v[i].second);
+  return true;
+}
+
 SplitPlan plan_sparse(int k_sel) {
   const int units = std::max(1, (k_sel + hkv::kSparseUnit - 1) / hkv::kSparseUnit);
   return {(units + hkv::kWaves - 1) / hkv::kWaves, hkv::kWaves, 0};
@@ -359,10 +379,12 @@ hkv_status hkv_decode_attn(hkv_handle h, const hkv_cache_desc* c, const void* q,
   if (sel_idx && (k_sel < 1 || k_sel > hkv::kMaxTopK)) return HKV_ERR_INVALID_VALUE;
   if (G != 1 && G != 2 && G != 4 && G != 8) return HKV_ERR_UNSUPPORTED;
   int64_t units_max = 1;
+  std::vector<int64_t> units(c->batch);
   for (int b = 0; b < c->batch; ++b) {
     const int n = c->seq_len_host[b];
     if (n == 0) return HKV_ERR_INVALID_VALUE;
     const int64_t nblk = cold_blocks(n, h->T, h->S);
+    units[b] = nblk;
     if (!sel_idx) units_max = std::max(units_max, nblk);
   }
   size_t need = 0;
@@ -385,13 +407,16 @@ hkv_status hkv_decode_attn(hkv_handle h, const hkv_cache_desc* c, const void* q,
   p.units_per_split = sp.per_split;
   p.wg_order = sp.wg_order;
   p.work = (!sel_idx && sp.claim) ? claim_counters(workspace, c, h->H) : nullptr;
+  uint16_t order[hkv::kOrderTableMax];
+  const bool ordered = !sel_idx && sp.batch && order_by_work(p, units, sp.per_split, order);
+  if (ordered) p.wg_order = hkv::kOrderTable;
   p.qscale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(h->D)));
   p.out = static_cast<_Float16*>(out);
   p.lse = lse;
   p.k_new = p.v_new = nullptr;
   p.seq_counters = nullptr;
   LaunchCtx a = make_ctx(h, stream, sel_idx ? HKV_KERNEL_DECODE_SPARSE : HKV_KERNEL_DECODE);
-  return hip_status(hkv::launch_decode(p, a), "hkv_decode_attn launch");
+  return hip_status(hkv::launch_decode(p, a, ordered ? order : nullptr), "hkv_decode_attn launch");
 }
 
 hkv_status hkv_append_decode(hkv_handle h, const hkv_cache_desc* c, const void* k_new, const void* v_new,
@@ -405,13 +430,15 @@ hkv_status hkv_append_decode(hkv_handle h, const hkv_cache_desc* c, const void* 
   if (G != 1 && G != 2 && G != 4 && G != 8) return HKV_ERR_UNSUPPORTED;
   if (h->S != hkv::kBlockSize) return HKV_ERR_UNSUPPORTED;
   int64_t units_max = 1;
+  std::vector<int64_t> units(c->batch);
   for (int b = 0; b < c->batch; ++b) {
     const int64_t n0 = c->seq_len_host[b];
     if (n0 < 0) return HKV_ERR_INVALID_VALUE;
     if (n0 + 1 > INT32_MAX) return HKV_ERR_CAPACITY;
     if (cold_blocks(n0 + 1, h->T, h->S) > c->max_blocks_per_seq) return HKV_ERR_CAPACITY;
     // cold units of the decode: the full blocks before the one the appended token spills into
-    units_max = std::max<int64_t>(units_max, std::max<int64_t>(0, n0 - h->T) / h->S);
+    units[b] = std::max<int64_t>(0, n0 - h->T) / h->S;
+    units_max = std::max<int64_t>(units_max, units[b]);
   }
   size_t need = 0;
   if (hkv_workspace_bytes(h, c, n_q_heads, 0, &need) != HKV_OK) return HKV_ERR_INVALID_VALUE;
@@ -435,13 +462,16 @@ hkv_status hkv_append_decode(hkv_handle h, const hkv_cache_desc* c, const void* 
   p.units_per_split = sp.per_split;
   p.wg_order = sp.wg_order;
   p.work = sp.claim ? claim_counters(workspace, c, h->H) : nullptr;
+  uint16_t order[hkv::kOrderTableMax];
+  const bool ordered = sp.batch && order_by_work(p, units, sp.per_split, order);
+  if (ordered) p.wg_order = hkv::kOrderTable;
   p.qscale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(h->D)));
   p.out = static_cast<_Float16*>(out);
   p.lse = lse;
   p.k_new = static_cast<const _Float16*>(k_new);
   p.v_new = static_cast<const _Float16*>(v_new);
   LaunchCtx a = make_ctx(h, stream, HKV_KERNEL_APPEND_DECODE);
-  const hkv_status r = hip_status(hkv::launch_decode(p, a), "hkv_append_decode launch");
+  const hkv_status r = hip_status(hkv::launch_decode(p, a, ordered ? order : nullptr), "hkv_append_decode launch");
   if (r != HKV_OK) return r;
   for (int b = 0; b < c->batch; ++b) c->seq_len_host[b] += 1;
   return HKV_OK;

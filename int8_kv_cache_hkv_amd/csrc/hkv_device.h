@@ -204,6 +204,23 @@ __device__ __forceinline__ WgCoord wg_coord(int order) {
   return {L % X, (L / X) % Y, L / (X * Y)};
 }
 
+// kOrderTable (batch plans, whose grid runs in several rounds of the resident
+// slots): the grid is read as groups of the H kv-heads of one (sequence,
+// part); first the hot-zone (and append) groups of every sequence, which are
+// short and needed by every merge, then the cold-split groups in the order of
+// `order` (host-built: most blocks first, so the longest splits do not start
+// in the last round).  x = split, y = kv-head, z = sequence as for the others.
+__device__ __forceinline__ WgCoord wg_coord_table(const uint16_t* order, int nsplit) {
+  const int X = gridDim.x, Y = gridDim.y;
+  const int lin = blockIdx.x + X * (blockIdx.y + Y * blockIdx.z);
+  const int gi = lin / Y, h = lin - gi * Y;
+  const int ns = X - nsplit;  // parts per (sequence, kv-head) that are not cold splits
+  const int nsmall = static_cast<int>(gridDim.z) * ns;
+  if (gi < nsmall) return {nsplit + gi % ns, h, gi / ns};
+  const int e = order[gi - nsmall];
+  return {e & 127, h, e >> 7};
+}
+
 // ---------------------------------------------------------------- MFMA / DPP helpers
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {

@@ -17,7 +17,8 @@ constexpr int kSinglePassMaxBlocks = 2;  // appends touching at most this many b
 constexpr int kMaxTopK = 512;       // fixed top-K budget of the sparse path
 constexpr int kSparseUnit = 16;     // selected tokens per wave unit of the sparse decode
 constexpr int kXcds = 8;            // MI355X: accelerator complex dies, each with its own L2
-constexpr int kOrderPlain = 0, kOrderXcdMajor = 1, kOrderSplitMajor = 2;  // workgroup orders of a grid
+constexpr int kOrderPlain = 0, kOrderXcdMajor = 1, kOrderSplitMajor = 2, kOrderTable = 3;  // workgroup orders
+constexpr int kOrderTableMax = 512;  // (sequence, split) groups a table order can list
 constexpr int kXcdMajorUnits = 16;  // resident plans with splits of at least this many units use XCD-major order
 constexpr int kClaimUnits = 16;     // ... and claim their units dynamically (dense decode)
 constexpr int kClaimStride = 64;    // claim counters 256 bytes apart: one cache line each
@@ -76,6 +77,13 @@ struct DecodeParams {
   unsigned* seq_counters;  // [B] merged-head counters, zero between calls
 };
 
+// Arguments of the table-ordered decode launch (batch plans): the cold (sequence << 7 | split)
+// groups in dispatch order, [B * nsplit] entries used.
+struct DecodeParamsOrdered {
+  DecodeParams p;
+  uint16_t order[kOrderTableMax];
+};
+
 struct TopkParams {
   CacheView c;
   int G;
@@ -90,7 +98,7 @@ struct TopkParams {
 };
 
 hipError_t launch_append(const AppendParams& p, const LaunchCtx& quant_ctx, const LaunchCtx& ring_ctx);
-hipError_t launch_decode(const DecodeParams& p, const LaunchCtx& ctx);
+hipError_t launch_decode(const DecodeParams& p, const LaunchCtx& ctx, const uint16_t* order = nullptr);
 hipError_t launch_topk(const TopkParams& p, const LaunchCtx& score_ctx, const LaunchCtx& sel_ctx);
 
 }  // namespace hkv
