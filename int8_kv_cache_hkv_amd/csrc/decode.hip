@@ -1265,7 +1265,7 @@ template <int D, int G, bool FUSED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G > 4 ? 2 : 4))) void decode_kernel_ordered(
     DecodeParamsOrdered po) {
   consume_args(po.p);
-  decode_body<D, G, false, FUSED, false>(po.p, wg_coord_table(po.order, po.p.nsplit));
+  decode_body<D, G, false, FUSED, false>(po.p, wg_coord_table(po.order));
 }
 
 template <typename K, typename P>

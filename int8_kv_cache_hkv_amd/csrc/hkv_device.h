@@ -206,18 +206,14 @@ __device__ __forceinline__ WgCoord wg_coord(int order) {
 
 // kOrderTable (batch plans, whose grid runs in several rounds of the resident
 // slots): the grid is read as groups of the H kv-heads of one (sequence,
-// part); first the hot-zone (and append) groups of every sequence, which are
-// short and needed by every merge, then the cold-split groups in the order of
-// `order` (host-built: most blocks first, so the longest splits do not start
-// in the last round).  x = split, y = kv-head, z = sequence as for the others.
-__device__ __forceinline__ WgCoord wg_coord_table(const uint16_t* order, int nsplit) {
+// part), in the order of the host-built table `order` of (sequence << 7 |
+// part) entries, one per group.  x = part, y = kv-head, z = sequence as for
+// the other orders.
+__device__ __forceinline__ WgCoord wg_coord_table(const uint16_t* order) {
   const int X = gridDim.x, Y = gridDim.y;
   const int lin = blockIdx.x + X * (blockIdx.y + Y * blockIdx.z);
   const int gi = lin / Y, h = lin - gi * Y;
-  const int ns = X - nsplit;  // parts per (sequence, kv-head) that are not cold splits
-  const int nsmall = static_cast<int>(gridDim.z) * ns;
-  if (gi < nsmall) return {nsplit + gi % ns, h, gi / ns};
-  const int e = order[gi - nsmall];
+  const int e = order[gi];
   return {e & 127, h, e >> 7};
 }
 

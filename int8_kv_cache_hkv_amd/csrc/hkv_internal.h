@@ -18,7 +18,7 @@ constexpr int kMaxTopK = 512;       // fixed top-K budget of the sparse path
 constexpr int kSparseUnit = 16;     // selected tokens per wave unit of the sparse decode
 constexpr int kXcds = 8;            // MI355X: accelerator complex dies, each with its own L2
 constexpr int kOrderPlain = 0, kOrderXcdMajor = 1, kOrderSplitMajor = 2, kOrderTable = 3;  // workgroup orders
-constexpr int kOrderTableMax = 512;  // (sequence, split) groups a table order can list
+constexpr int kOrderTableMax = 512;  // (sequence, part) groups a table order can list
 constexpr int kXcdMajorUnits = 16;  // resident plans with splits of at least this many units use XCD-major order
 constexpr int kClaimUnits = 16;     // ... and claim their units dynamically (dense decode)
 constexpr int kClaimStride = 64;    // claim counters 256 bytes apart: one cache line each
@@ -77,8 +77,8 @@ struct DecodeParams {
   unsigned* seq_counters;  // [B] merged-head counters, zero between calls
 };
 
-// Arguments of the table-ordered decode launch (batch plans): the cold (sequence << 7 | split)
-// groups in dispatch order, [B * nsplit] entries used.
+// Arguments of the table-ordered decode launch (batch plans): the (sequence << 7 | part) groups
+// of the grid in dispatch order, [B * nparts] entries used.
 struct DecodeParamsOrdered {
   DecodeParams p;
   uint16_t order[kOrderTableMax];
