@@ -129,7 +129,8 @@ int max_splits(int64_t bh, int64_t units_cap) {
 // the table cannot hold the groups.
 bool order_by_work(const hkv::DecodeParams& p, const std::vector<int64_t>& units, int64_t per, uint16_t* order) {
   const int B = static_cast<int>(units.size());
-  if (static_cast<int64_t>(B) * p.nparts > hkv::kOrderTableMax || B > 511) return false;
+  // entries are (sequence << 7 | part) in 16 bits
+  if (static_cast<int64_t>(B) * p.nparts > hkv::kOrderTableMax || B > 511 || p.nparts > 128) return false;
   std::vector<std::pair<int64_t, int>> v;
   v.reserve(static_cast<size_t>(B) * p.nsplit);
   for (int b = 0; b < B; ++b)
