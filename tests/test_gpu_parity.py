@@ -461,6 +461,33 @@ def test_claim_walk_group_sizes(d, g):
         gh.compare_lse(lse_f[b], l_ref, f"claim fused d={d} g={g} b={b}")
 
 
+@pytest.mark.parametrize("batch", [200, 300])
+def test_batch_plan_orders(batch):
+    """Batch plans (more (sequence, kv-head) pairs than resident slots): 200 sequences x 2 kv-heads fit
+    the longest-first order table (400 groups), 300 do not (600 groups: sequence order).  Lengths
+    40..420 tokens; plain decode and a fused step, every output against the oracle."""
+    import dataclasses
+    w = dataclasses.replace(wl.WORKLOADS["tiny"], name=f"batch{batch}", batch=batch)
+    rng = np.random.default_rng(batch)
+    lens = rng.integers(40, 421, batch).tolist()
+    cache = gh.make_cache(w, max(lens) + 8)
+    gh.fill(cache, w, lens)
+    q = wl.queries(w, step=5)
+    out, lse = _decode(cache, q)
+    st = _oracle_states(w, lens)
+    for b in range(batch):
+        o_ref, l_ref = orc.decode(q[b], st[b])
+        gh.compare_out(out[b], o_ref, f"batch {batch} b={b}")
+        gh.compare_lse(lse[b], l_ref, f"batch {batch} b={b}")
+    out_f, lse_f = _append_decode(cache, w, lens, q)
+    st1 = _oracle_states(w, [n + 1 for n in lens])
+    gh.check_state(cache, st1)
+    for b in range(batch):
+        o_ref, l_ref = orc.decode(q[b], st1[b])
+        gh.compare_out(out_f[b], o_ref, f"batch {batch} fused b={b}")
+        gh.compare_lse(lse_f[b], l_ref, f"batch {batch} fused b={b}")
+
+
 # ------------------------------------------------------------------ long context, sampled
 def test_long_config_parity_sampled():
     w = wl.WORKLOADS["long"]
