@@ -197,10 +197,11 @@ hkv_status hkv_append(hkv_handle h, const hkv_cache_desc* c, const void* k_new, 
  * Hybrid KV Cache page 4.2 computes the hot part with FlashAttention-2 and
  * dequantises cold blocks lazily; a joint softmax replaces its concatenation
  * of the two outputs).  Split-K partials are merged with a log-sum-exp
- * combine.  Long dense sequences are split dynamically (the cold blocks of a
- * (sequence, kv-head) are claimed by whichever wave is free), so repeated
- * calls on such caches agree to float rounding, not bit for bit; other
- * launches are bitwise reproducible.
+ * combine.  When the plan gives a split 16 or more cold blocks (long
+ * sequences, or more (sequence, kv-head) pairs than the GPU holds at once),
+ * the blocks of a (sequence, kv-head) are claimed by whichever wave is free,
+ * so repeated calls agree to float rounding, not bit for bit; other launches
+ * are bitwise reproducible.
  *   q        device fp16 [batch][n_q_heads][head_dim].
  *   sel_idx  NULL for dense decode, or device int32 [batch][n_kv_heads][k_sel]
  *            of selected cold-token indices (as written by

@@ -1261,11 +1261,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G > 4 
 
 // Batch plans: the same grid read in the host-built order of the table (see wg_coord_table); a kernel
 // of its own, so the table does not enlarge the arguments of every other launch.
-template <int D, int G, bool FUSED>
+template <int D, int G, bool FUSED, bool CLAIM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G > 4 ? 2 : 4))) void decode_kernel_ordered(
     DecodeParamsOrdered po) {
   consume_args(po.p);
-  decode_body<D, G, false, FUSED, false>(po.p, wg_coord_table(po.order));
+  decode_body<D, G, false, FUSED, CLAIM>(po.p, wg_coord_table(po.order));
 }
 
 template <typename K, typename P>
@@ -1282,12 +1282,15 @@ hipError_t launch_k(K kernel, dim3 grid, int block, const P& p, const LaunchCtx&
 template <int D, int G>
 hipError_t launch_dg(const DecodeParams& p, const LaunchCtx& ctx, const uint16_t* order) {
   const dim3 grid(p.nparts, p.c.H, p.c.B);  // (split, kv-head, sequence)
-  if (order && !p.sel && !p.work) {
+  if (order && !p.sel) {
     DecodeParamsOrdered po;
     po.p = p;
     std::memcpy(po.order, order, sizeof(po.order));
-    return p.k_new ? launch_k(decode_kernel_ordered<D, G, true>, grid, kThreads, po, ctx)
-                   : launch_k(decode_kernel_ordered<D, G, false>, grid, kThreads, po, ctx);
+    if (p.work)
+      return p.k_new ? launch_k(decode_kernel_ordered<D, G, true, true>, grid, kThreads, po, ctx)
+                     : launch_k(decode_kernel_ordered<D, G, false, true>, grid, kThreads, po, ctx);
+    return p.k_new ? launch_k(decode_kernel_ordered<D, G, true, false>, grid, kThreads, po, ctx)
+                   : launch_k(decode_kernel_ordered<D, G, false, false>, grid, kThreads, po, ctx);
   }
   if (p.k_new)
     return p.work ? launch_k(decode_kernel<D, G, false, true, true>, grid, kThreads, p, ctx)
