@@ -35,7 +35,7 @@ HBM_PEAK_GBS = 8000.0
 # exactly its size), recorded in profiles/decode_kernel_llama8b_hbm_traffic.md.  Valid only for the
 # kernel sources they were measured on: reported as null once the code of those sources changes
 # (the hash skips comments and blank lines, which do not change the kernel).
-COUNTER_TRAFFIC = {"sources_sha256": "7c60d3de35deece1062f9ab92847cd87b08724b8258bd306013459a440fa1f7e", "bytes_per_launch": 39874754}
+COUNTER_TRAFFIC = {"sources_sha256": "4f5da0b93cb07815b429b462502437b3b7b9a3bd4de4bd2ab2f09b781980dfbb", "bytes_per_launch": 39873979}
 KERNEL_SOURCES = ("decode.hip", "hkv_device.h", "hkv_internal.h")
 
 

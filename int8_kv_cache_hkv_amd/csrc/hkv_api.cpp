@@ -87,11 +87,9 @@ SplitPlan plan_splits(int64_t bh, int64_t units, int extra_parts = 1, int64_t ta
     ns = (units + per - 1) / per;
   }
   // plans with long splits claim their units dynamically (static splits of equal size were measured
-  // to finish up to 6x apart); resident ones on a grid of kClaimTargetWorkgroups in split-major order;
-  // without claims, XCD-major order helps long resident splits (131072-token step) and hurts the
-  // batch plan
-  // batch plans claim too: a sequence's splits that start in different rounds of the resident
-  // slots then share its blocks (ragged fused step, measured: 124.6 -> 122.0 us)
+  // to finish up to 6x apart); resident ones on a grid of kClaimTargetWorkgroups in split-major
+  // order.  Batch plans claim too: a sequence's splits that start in different rounds of the
+  // resident slots then share its blocks (ragged fused step, measured: 124.6 -> 122.0 us)
   const int claim = claim_target_wg > 0 && per >= hkv::kClaimUnits ? 1 : 0;
   if (claim && target >= 2) {
     const int64_t tc = std::max<int64_t>(2, claim_target_wg / bh - extra_parts);
@@ -100,8 +98,7 @@ SplitPlan plan_splits(int64_t bh, int64_t units, int extra_parts = 1, int64_t ta
       ns = (units + per - 1) / per;
     }
   }
-  const int order = (claim && target >= 2) ? hkv::kOrderSplitMajor
-                          : (target >= 2 && per >= hkv::kXcdMajorUnits ? hkv::kOrderXcdMajor : hkv::kOrderPlain);
+  const int order = (claim && target >= 2) ? hkv::kOrderSplitMajor : hkv::kOrderPlain;
   return {static_cast<int>(ns), static_cast<int>(per), order, claim, target < 2 ? 1 : 0};
 }
 

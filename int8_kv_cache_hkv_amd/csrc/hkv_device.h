@@ -167,17 +167,13 @@ __device__ __forceinline__ unsigned claim_issue(unsigned* work, int lane) {
 }
 
 // Workgroup coordinates of a 3D grid (x = split, y = kv-head, z = sequence).
-// Workgroups are dispatched round-robin over the kXcds dies in linear order,
+// Workgroups are dispatched round-robin over the 8 dies in linear order,
 // and a workgroup dispatched earlier keeps a lead in memory bandwidth over the
 // ones dispatched after it (measured: in a resident 131072-token launch the
 // splits of the first sequence finished 47 us before those of the last).
 // Orders (each a bijection of the grid):
-//  * kOrderPlain: linear order; short splits (latency-bound steps) and grids
-//    larger than the resident slots, where it measured fastest;
-//  * kOrderXcdMajor: each die's share of the linear order becomes one
-//    contiguous range of logical workgroups, so the splits of one (sequence,
-//    kv-head) run on one die (131072-token step with static splits: 186 ->
-//    178 us);
+//  * kOrderPlain: linear order; short splits (latency-bound steps), where it
+//    measured fastest;
 //  * kOrderSplitMajor: the linear order runs over (sequence, kv-head) first,
 //    so every (sequence, kv-head) gets early and late workgroups alike, and
 //    round k (split k) is rotated by k pairs, so its workgroups also visit
@@ -193,15 +189,10 @@ __device__ __forceinline__ WgCoord wg_coord(int order) {
     return {static_cast<int>(blockIdx.x), static_cast<int>(blockIdx.y), static_cast<int>(blockIdx.z)};
   const int N = X * Y * static_cast<int>(gridDim.z);
   const int lin = blockIdx.x + X * (blockIdx.y + Y * blockIdx.z);
-  if (order == kOrderSplitMajor) {
-    const int P = N / X;  // (sequence, kv-head) pairs
-    const int k = lin / P;
-    const int pair = (lin - k * P + k) % P;
-    return {k, pair % Y, pair / Y};
-  }
-  const int die = lin % kXcds, k = lin / kXcds;
-  const int L = die * (N / kXcds) + min(die, N % kXcds) + k;
-  return {L % X, (L / X) % Y, L / (X * Y)};
+  const int P = N / X;  // kOrderSplitMajor; (sequence, kv-head) pairs
+  const int k = lin / P;
+  const int pair = (lin - k * P + k) % P;
+  return {k, pair % Y, pair / Y};
 }
 
 // kOrderTable (batch plans, whose grid runs in several rounds of the resident

@@ -16,11 +16,9 @@ constexpr int kAppendChunk = 256;   // sequences whose append counts travel in o
 constexpr int kSinglePassMaxBlocks = 2;  // appends touching at most this many blocks per sequence use one launch
 constexpr int kMaxTopK = 512;       // fixed top-K budget of the sparse path
 constexpr int kSparseUnit = 16;     // selected tokens per wave unit of the sparse decode
-constexpr int kXcds = 8;            // MI355X: accelerator complex dies, each with its own L2
-constexpr int kOrderPlain = 0, kOrderXcdMajor = 1, kOrderSplitMajor = 2, kOrderTable = 3;  // workgroup orders
+constexpr int kOrderPlain = 0, kOrderSplitMajor = 2, kOrderTable = 3;  // workgroup orders (see wg_coord)
 constexpr int kOrderTableMax = 512;  // (sequence, part) groups a table order can list
-constexpr int kXcdMajorUnits = 16;  // resident plans with splits of at least this many units use XCD-major order
-constexpr int kClaimUnits = 16;     // ... and claim their units dynamically (dense decode)
+constexpr int kClaimUnits = 16;     // plans with splits of at least this many units claim them dynamically
 constexpr int kClaimStride = 64;    // claim counters 256 bytes apart: one cache line each
 constexpr int kMaxSplits = 128;     // cold splits per (sequence, kv-head) at most
 
@@ -66,7 +64,7 @@ struct DecodeParams {
   int nsplit;              // cold splits per (sequence, kv-head)
   int nparts;              // partial records per (sequence, kv-head): nsplit + 1 (hot zone), + 1 more fused
   int units_per_split;     // units handled per split (multiple of kWaves)
-  int wg_order;            // kOrderPlain / kOrderXcdMajor / kOrderSplitMajor (see wg_coord)
+  int wg_order;            // kOrderPlain / kOrderSplitMajor / kOrderTable (see wg_coord)
   unsigned* work;          // [B*H][kClaimStride] unit-claim counters (dense walk), zero between calls; nullptr: static
   float qscale;            // log2(e) / sqrt(D)
   _Float16* out;           // [B][H*G][D]
@@ -91,7 +89,7 @@ struct TopkParams {
   float* prob;             // [B][H][max_blocks*S] window probabilities
   int nsplit;
   int units_per_split;
-  int wg_order;            // kOrderPlain / kOrderXcdMajor / kOrderSplitMajor (see wg_coord)
+  int wg_order;            // kOrderPlain / kOrderSplitMajor / kOrderTable (see wg_coord)
   unsigned* work;          // [B*H][kClaimStride] unit-claim counters of the score walk; nullptr: static walk
   int k;
   int32_t* out_idx;        // [B][H][k]
