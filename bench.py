@@ -3,16 +3,26 @@
 
 One step = one decode step of a Llama-3-8B-shaped layer (batch 8, 32 query /
 8 kv heads, head_dim 128, 2048 cached tokens = 32 FP16 hot + 31 full INT8
-blocks + 1 half block): hkv_append of one new token per sequence (spill +
-re-quantisation of the touched cold block) followed by hkv_decode_attn.
-Steps rotate over independent cache instances whose combined size exceeds
-the 256 MB Infinity Cache, so every step streams its cache from HBM.
+blocks + 1 half block): one new token appended per sequence (spill +
+re-quantisation of the touched cold block) and the dense decode, issued as one
+fused launch (hkv_append_decode).  Steps rotate over independent cache
+instances whose combined size exceeds the 256 MB Infinity Cache, so every step
+streams its cache from HBM.
 
-Printed: one JSON line (value = algorithmic bytes per step / step time, in
-GB/s), with the dominant kernel's roofline (kernel duration from dispatch-
-recorded HIP events on the launch stream) and the fp64 CPU oracle timed on a
-bounded sample of the same workload.  Extra legs: the 131072-token
-long-context decode and the top-K sparse path (selection + sparse decode).
+Printed: one JSON line.  `value` = algorithmic bytes per step / step time (GB/s,
+median of --trials trials of --steps steps, host clock with device
+synchronisation around each trial).  Every leg carries a `roofline` block for
+its dominant launch: algorithmic bytes per launch / the launch's average
+duration, from a HIP event pair on the launch stream around each timed trial
+(median over trials).  After its timed trials every leg recomputes its last
+output outside the timed region (and, where it is cheap, with the fp64
+oracle) and the run exits with status 3 if any check fails.
+
+Legs (`--leg`, default all): llama8b (the headline step), separate (the same
+step as hkv_append + hkv_decode_attn), long (131072 tokens), sparse (top-K
+selection + sparse decode, 32768 tokens), ragged (64 sequences of seeded
+lengths), graph (the llama8b step from a HIP graph), read_floor (a plain
+one-launch read of the llama8b step's bytes), cpu (the fp64 oracle on the host).
 """
 from __future__ import annotations
 
@@ -20,6 +30,8 @@ import argparse
 import ctypes
 import json
 import os
+import platform
+import statistics
 import sys
 import time
 
@@ -29,14 +41,19 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+METRIC = "decode-attn KV GB/s (% of HBM peak) + decode queries/sec, hybrid INT8/FP16"
+OUT_MAX_ABS, OUT_MEAN_ABS = 4e-3, 5e-4
 
-# HBM bytes per launch of the fused llama8b-step kernel from hardware counters: FETCH_SIZE x 2.000 +
-# WRITE_SIZE x 1.000 (KiB per dispatch; the factors make a 256 MiB elementwise copy read and write
-# exactly its size), recorded in profiles/decode_kernel_llama8b_hbm_traffic.md.  Valid only for the
-# kernel sources they were measured on: reported as null once the code of those sources changes
-# (the hash skips comments and blank lines, which do not change the kernel).
-COUNTER_TRAFFIC = {"sources_sha256": "4f5da0b93cb07815b429b462502437b3b7b9a3bd4de4bd2ab2f09b781980dfbb", "bytes_per_launch": 39873979}
-KERNEL_SOURCES = ("decode.hip", "hkv_device.h", "hkv_internal.h")
+# HBM bytes per launch from hardware counters (FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 KiB per
+# dispatch; the factors make a 256 MiB elementwise copy read and write exactly its size), recorded
+# in the profiles folder (decode_kernel_llama8b_hbm_traffic.md, path_kernels_hbm_traffic.md).  They
+# hold only for the kernel sources they were taken on: reported as null once the code of those
+# sources changes (the hash skips comments and blank lines).
+COUNTER_TRAFFIC = {
+    "sources_sha256": "",
+    "bytes_per_launch": {},
+}
+KERNEL_SOURCES = ("append.hip", "decode.hip", "topk.hip", "hkv_device.h", "hkv_internal.h")
 
 
 def code_text(src: str) -> str:
@@ -47,14 +64,22 @@ def code_text(src: str) -> str:
     return "\n".join(ln for ln in lines if ln)
 
 
-def counter_traffic():
+def sources_hash() -> str:
     import hashlib
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "int8_kv_cache_hkv_amd", "csrc", f), encoding="utf-8") as fh:
-            h.update(code_text(fh.read()).encode())
-    return COUNTER_TRAFFIC["bytes_per_launch"] if h.hexdigest() == COUNTER_TRAFFIC["sources_sha256"] else None
-METRIC = "decode-attn KV GB/s (% of HBM peak) + decode queries/sec, hybrid INT8/FP16"
+        p = os.path.join(ROOT, "int8_kv_cache_hkv_amd", "csrc", f)
+        if os.path.exists(p):
+            with open(p, encoding="utf-8") as fh:
+                h.update(code_text(fh.read()).encode())
+    return h.hexdigest()
+
+
+def counter_traffic(leg: str):
+    """(bytes per launch, source) recorded from the counters for this leg, or (None, reason)."""
+    if COUNTER_TRAFFIC["sources_sha256"] != sources_hash() or leg not in COUNTER_TRAFFIC["bytes_per_launch"]:
+        return None, "not measured on the current kernel sources"
+    return COUNTER_TRAFFIC["bytes_per_launch"][leg], "recorded from rocprofv3 FETCH_SIZE/WRITE_SIZE (profiles folder)"
 
 
 def log(msg):
@@ -63,7 +88,9 @@ def log(msg):
 
 # ----------------------------------------------------------------------------- algorithmic bytes
 def decode_bytes(n, H, Hq, d, T=32, S=64, with_out=True):
-    """Bytes the dense decode must move for one sequence of n cached tokens."""
+    """Bytes the dense decode must move for one sequence of n cached tokens: int8 K and V codes of the
+    cold tokens, the two fp32 scales per cold block and kv-head, the 16-byte headers, the fp16 hot
+    tokens, the fp16 query (and the fp16 output)."""
     n_hot = min(n, T)
     n_cold = n - n_hot
     n_blk = -(-n_cold // S)
@@ -77,228 +104,264 @@ def append_bytes(n_new_tokens, H, d):
     return n_new_tokens * (18 * H * d + 8 * H + 16)
 
 
-def sparse_bytes(n, H, Hq, d, k, T=32, S=64):
+def sparse_bytes(n, H, Hq, d, k, T=32):
+    """Sparse decode of one sequence: the selected tokens' int8 K and V codes and their blocks' scales
+    and headers, the hot zone, q in / out, the selection read."""
     n_hot = min(n, T)
     sel = min(k, n - n_hot)
     return 2 * sel * H * d + 8 * sel * H + 16 * sel + 4 * n_hot * H * d + 4 * Hq * d + 4 * H * k
 
 
 def topk_bytes(n, H, Hq, d, k, T=32):
+    """Top-K selection of one sequence: the int8 K codes of the cold tokens (the scale cancels in a
+    cosine), the headers, the query and the index list written."""
     n_cold = n - min(n, T)
     return n_cold * H * d + 16 * (-(-n_cold // 64)) + 2 * Hq * d + 4 * H * k
 
 
-# ----------------------------------------------------------------------------- helpers
+def roofline(kernel, nbytes, ms, leg):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    traffic, src = counter_traffic(leg)
+    return {"kernel": kernel, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "traffic_source": src,
+            "bytes_per_launch": int(nbytes), "avg_launch_ms": round(ms, 6)}
+
+
+# ----------------------------------------------------------------------------- timing
+def timed_trials(torch, step, first, steps, trials):
+    """`trials` trials of `steps` calls step(i) (i counts on from `first`).  Each trial is bracketed by
+    torch.cuda.synchronize() on both sides (host clock) and by an event pair recorded on the current
+    stream, the stream every launch goes to.  Returns the median host and device milliseconds per
+    step, every trial's figures and the values step() returned."""
+    host, dev, rets = [], [], []
+    i = first
+    for _ in range(trials):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(steps):
+            rets.append(step(i))
+            i += 1
+        e1.record()
+        torch.cuda.synchronize()
+        host.append((time.perf_counter() - t0) * 1e3 / steps)
+        dev.append(e0.elapsed_time(e1) / steps)
+    return {"ms_per_step": statistics.median(host), "device_ms_per_step": statistics.median(dev),
+            "trials_ms": [round(x, 6) for x in host], "trials_device_ms": [round(x, 6) for x in dev],
+            "next": i, "rets": rets}
+
+
+def out_close(got, want, what):
+    """Max / mean absolute difference of two fp16 outputs against the bench's tolerance."""
+    d = np.abs(np.asarray(got, np.float64) - np.asarray(want, np.float64))
+    ok = bool(np.all(np.isfinite(got)) and d.max() <= OUT_MAX_ABS and d.mean() <= OUT_MEAN_ABS)
+    return {"what": what, "max_abs": float(d.max()), "mean_abs": float(d.mean()), "ok": ok}
+
+
+CHECKS = []
+
+
+def record_check(c):
+    CHECKS.append(c)
+    if not c["ok"]:
+        log(f"SELF-CHECK FAILED: {c}")
+
+
+# ----------------------------------------------------------------------------- legs
 class Inst:
     """One cache instance plus pre-marshalled C-ABI arguments."""
 
-    def __init__(self, hkv, w, cap_tokens):
-        self.c = hkv.HybridKVCache(w.n_kv_heads, w.head_dim, w.batch, cap_tokens)
+    def __init__(self, hkv, w, cap_tokens, quant_bits=8):
+        self.c = hkv.HybridKVCache(w.n_kv_heads, w.head_dim, w.batch, cap_tokens, quant_bits=quant_bits)
         self.desc_ref = ctypes.byref(self.c.desc)
 
 
-def run_leg(hkv, torch, w, n0, steps, warmup, R, label, do_append=True, fused=True):
-    """Rotating-instance append+decode loop (one hkv_append_decode launch per step, or hkv_append then
-    hkv_decode_attn when fused is False); returns timing and byte counts."""
+def decode_step_leg(hkv, torch, w, n0, steps, warmup, trials, R, label, fused=True, quant_bits=8,
+                    oracle_check=True):
+    """Rotating-instance decode steps of a uniform-length workload: one hkv_append_decode launch per
+    step (fused) or hkv_append then hkv_decode_attn.  Returns timing, bytes and the self-check."""
     import workloads as wl
-    H, Hq, d = w.n_kv_heads, w.n_q_heads, w.head_dim
-    uses = -(-(2 * steps + warmup) // R) + 1
+    B, H, Hq, d = w.batch, w.n_kv_heads, w.n_q_heads, w.head_dim
+    total = warmup + trials * steps
+    uses = -(-total // R) + 1
     cap = n0 + uses + 1
-    log(f"{label}: {R} instances of B={w.batch} n0={n0} (cap {cap}), generating inputs")
-    insts = [Inst(hkv, w, cap) for _ in range(R)]
-    # history, uploaded once and appended into every instance in chunks
+    log(f"{label}: {R} instances of B={B} n0={n0} (cap {cap}), generating inputs")
+    insts = [Inst(hkv, w, cap, quant_bits) for _ in range(R)]
     chunk = 16384
     for s in range(0, n0, chunk):
         cnt = min(chunk, n0 - s)
-        kh = torch.from_numpy(wl.batch_tokens(w, list(range(w.batch)), s, cnt, "k")).cuda()
-        vh = torch.from_numpy(wl.batch_tokens(w, list(range(w.batch)), s, cnt, "v")).cuda()
+        kh = torch.from_numpy(wl.batch_tokens(w, list(range(B)), s, cnt, "k")).cuda()
+        vh = torch.from_numpy(wl.batch_tokens(w, list(range(B)), s, cnt, "v")).cuda()
         for it in insts:
             it.c.append(kh, vh)
         del kh, vh
     torch.cuda.synchronize()
-    # per-use new tokens and per-step queries
-    newk = [torch.from_numpy(wl.batch_tokens(w, list(range(w.batch)), n0 + u, 1, "k")).cuda() for u in range(uses)]
-    newv = [torch.from_numpy(wl.batch_tokens(w, list(range(w.batch)), n0 + u, 1, "v")).cuda() for u in range(uses)]
+    newk = torch.from_numpy(wl.batch_tokens(w, list(range(B)), n0, uses, "k")).cuda()   # [B, uses, H, d]
+    newv = torch.from_numpy(wl.batch_tokens(w, list(range(B)), n0, uses, "v")).cuda()
+    newk_u = [newk[:, u].contiguous() for u in range(uses)]
+    newv_u = [newv[:, u].contiguous() for u in range(uses)]
     NQ = 32
     qs = [torch.from_numpy(wl.queries(w, step=i)).cuda() for i in range(NQ)]
     out = torch.empty_like(qs[0])
     ws = insts[0].c.workspace(Hq)
     ws_ptr, ws_len = ws.data_ptr(), ws.numel()
-    ones = np.ones(w.batch, dtype=np.int32)
-    ones_ptr = ones.ctypes.data
+    ones = np.ones(B, dtype=np.int32)
     stream = torch.cuda.current_stream().cuda_stream
     lib = hkv._lib
-    use_count = [0] * R
-    lens = [n0] * R
+    used = [0] * R
 
     def step(i):
         r = i % R
         it = insts[r]
-        if do_append and fused:
-            u = use_count[r]
-            st = lib.hkv_append_decode(it.c.handle, it.desc_ref, newk[u].data_ptr(), newv[u].data_ptr(),
+        u = used[r]
+        if fused:
+            st = lib.hkv_append_decode(it.c.handle, it.desc_ref, newk_u[u].data_ptr(), newv_u[u].data_ptr(),
                                        qs[i % NQ].data_ptr(), Hq, out.data_ptr(), None, ws_ptr, ws_len, stream)
-            if st:
-                raise hkv.HKVError(st, "hkv_append_decode")
-            use_count[r] += 1
-            lens[r] += 1
-            return lens[r]
-        if do_append:
-            u = use_count[r]
-            st = lib.hkv_append(it.c.handle, it.desc_ref, newk[u].data_ptr(), newv[u].data_ptr(), ones_ptr, 1, stream)
-            if st:
-                raise hkv.HKVError(st, "hkv_append")
-            use_count[r] += 1
-            lens[r] += 1
-        st = lib.hkv_decode_attn(it.c.handle, it.desc_ref, qs[i % NQ].data_ptr(), Hq, None, 0, out.data_ptr(), None,
-                                 ws_ptr, ws_len, stream)
+        else:
+            st = lib.hkv_append(it.c.handle, it.desc_ref, newk_u[u].data_ptr(), newv_u[u].data_ptr(),
+                                ones.ctypes.data, 1, stream)
+            if not st:
+                st = lib.hkv_decode_attn(it.c.handle, it.desc_ref, qs[i % NQ].data_ptr(), Hq, None, 0,
+                                         out.data_ptr(), None, ws_ptr, ws_len, stream)
         if st:
-            raise hkv.HKVError(st, "hkv_decode_attn")
-        return lens[r]
-
-    def step_bytes_of(n):
-        db = w.batch * decode_bytes(n, H, Hq, d)
-        return db, db + (w.batch * append_bytes(1, H, d) if do_append else 0)
+            raise hkv.HKVError(st, label)
+        used[r] += 1
+        return n0 + used[r]   # cached length after the step
 
     for i in range(warmup):
         step(i)
+    res = timed_trials(torch, step, warmup, steps, trials)
+    lens = res.pop("rets")
+    step_bytes = [B * (decode_bytes(n, H, Hq, d) + append_bytes(1, H, d)) for n in lens]
+    kern_bytes = step_bytes if fused else [B * decode_bytes(n, H, Hq, d) for n in lens]
+    # ---- self-check of the last timed step, outside the timed region
+    last = res["next"] - 1
+    r_last, q_last = last % R, qs[last % NQ]
+    n_last = n0 + used[r_last]
+    got = out.cpu().numpy()
+    chk = torch.empty_like(q_last)
+    it = insts[r_last]
+    st = lib.hkv_decode_attn(it.c.handle, it.desc_ref, q_last.data_ptr(), Hq, None, 0, chk.data_ptr(), None,
+                             ws_ptr, ws_len, stream)
+    if st:
+        raise hkv.HKVError(st, "self-check decode")
     torch.cuda.synchronize()
-    # timed pass: exactly `steps` steps, no per-kernel events, bracketed by device synchronisation
-    step_bytes = 0
-    t0 = time.perf_counter()
-    for i in range(warmup, warmup + steps):
-        step_bytes += step_bytes_of(step(i))[1]
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    # second pass of the same length with dispatch-recorded events, for per-kernel durations
+    record_check(out_close(got, chk.cpu().numpy(), f"{label}: last timed output vs hkv_decode_attn recompute"))
+    if oracle_check:
+        import oracle.hkv_oracle as orc
+        k = wl.tokens(w, 0, 0, n_last, "k")
+        v = wl.tokens(w, 0, 0, n_last, "v")
+        o_ref, _ = orc.decode(q_last.cpu().numpy()[0], orc.build_state(k, v, w.hot_tokens, w.block_size))
+        record_check(out_close(got[0], o_ref, f"{label}: last timed output, sequence 0, vs the fp64 oracle"))
     for it in insts:
-        hkv.hkv_timing_enable(it.c.handle, True)
-    kern_bytes = 0
-    for i in range(warmup + steps, warmup + 2 * steps):
-        # the fused kernel moves the append's bytes too; the plain decode kernel only the decode's
-        kern_bytes += step_bytes_of(step(i))[1 if (fused and do_append) else 0]
-    torch.cuda.synchronize()
-    kms = {}
-    for kname in ("append", "append_ring", "decode", "append_decode"):
-        tot, cnt = 0.0, 0
-        for it in insts:
-            a, b = hkv.hkv_timing_read(it.c.handle, kname, reset=True)
-            tot += a
-            cnt += b
-        kms[kname] = (tot / cnt if cnt else None, cnt)
-    for it in insts:
-        hkv.hkv_timing_enable(it.c.handle, False)
         it.c.close()
-    ms = wall * 1e3 / steps
-    res = {
-        "ms_per_step": ms,
-        "gbs": step_bytes / steps / (ms * 1e-3) / 1e9,
-        "bytes_per_step": step_bytes / steps,
-        "kernel_ms": {k: v[0] for k, v in kms.items()},
-        "kernel_launches": {k: v[1] for k, v in kms.items()},
-        "kernel_bytes": kern_bytes / steps,
-    }
+    del insts
+    torch.cuda.empty_cache()
+    res["bytes_per_step"] = statistics.mean(step_bytes)
+    res["kernel_bytes_per_step"] = statistics.mean(kern_bytes)
+    res["gbs"] = res["bytes_per_step"] / (res["ms_per_step"] * 1e-3) / 1e9
     return res
 
 
-def cpu_baseline(w, budget_s=12.0):
-    """The fp64 oracle on the same step (append one token + decode), 8 sequences, bounded time."""
-    import oracle.hkv_oracle as orc
+def leg_llama8b(hkv, torch, args):
     import workloads as wl
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    n0 = w.context - 1
-    S, T = w.block_size, w.hot_tokens
-    H, Hq, d = w.n_kv_heads, w.n_q_heads, w.head_dim
-    extra = 512  # appended tokens the sample may use (bounds the sample as well as the time budget)
-    hist_k = [wl.tokens(w, b, 0, n0 + extra, "k") for b in range(w.batch)]
-    hist_v = [wl.tokens(w, b, 0, n0 + extra, "v") for b in range(w.batch)]
-    states = [orc.build_state(hist_k[b][:n0], hist_v[b][:n0], T, S) for b in range(w.batch)]
-    steps = 0
-    nbytes = 0
-    t0 = time.perf_counter()
-    while True:
-        for b in range(w.batch):
-            st = states[b]
-            n1 = st.n_tokens + 1
-            n_hot, n_cold = orc.split_history(n1, T)
-            j = (n_cold - 1) // S
-            kr, vr = hist_k[b][j * S:n_cold], hist_v[b][j * S:n_cold]
-            codes, scales = orc.quantize_block(kr, vr, S)
-            if j >= st.n_blocks:
-                st.codes = np.concatenate([st.codes, codes[None]])
-                st.scales = np.concatenate([st.scales, scales[None]])
-                st.n_valid = np.concatenate([st.n_valid, [n_cold - j * S]])
-            else:
-                st.codes[j], st.scales[j], st.n_valid[j] = codes, scales, n_cold - j * S
-            st.hot_k, st.hot_v = hist_k[b][n_cold:n1], hist_v[b][n_cold:n1]
-            st.n_tokens = n1
-            orc.decode(wl.query(w, b, steps), st)
-            nbytes += decode_bytes(n1, H, Hq, d) + append_bytes(1, H, d)
-        steps += 1
-        if time.perf_counter() - t0 >= budget_s or steps >= extra:
-            break
-    el = time.perf_counter() - t0
-    return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{steps} steps x {w.batch} sequences of the llama8b step (fp64 NumPy oracle: re-quantise "
-                      f"the touched block + dense decode), {el:.1f} s",
-            "ms_per_step": el * 1e3 / steps}
+    w = wl.WORKLOADS["llama8b"]
+    r = decode_step_leg(hkv, torch, w, w.context - 1, args.steps, args.warmup, args.trials, args.instances,
+                        "llama8b")
+    return w, r
 
 
-def long_leg(hkv, torch, steps):
+def leg_separate(hkv, torch, args):
+    import workloads as wl
+    w = wl.WORKLOADS["llama8b"]
+    r = decode_step_leg(hkv, torch, w, w.context - 1, args.steps, args.warmup, args.trials, args.instances,
+                        "llama8b (separate calls)", fused=False)
+    return {"what": "the llama8b step as hkv_append then hkv_decode_attn (two launches per step)",
+            "ms_per_step": r["ms_per_step"], "trials_ms": r["trials_ms"], "gbs": r["gbs"],
+            "pct_hbm_peak": 100 * r["gbs"] / HBM_PEAK_GBS}
+
+
+def leg_long(hkv, torch, args):
     import workloads as wl
     w = wl.WORKLOADS["long"]
-    r = run_leg(hkv, torch, w, w.context - 1, steps, 3, 2, "long")
-    H, Hq, d = w.n_kv_heads, w.n_q_heads, w.head_dim
-    kb = r["kernel_bytes"]
-    kms = r["kernel_ms"]["append_decode"]
+    steps = max(8, min(args.steps, 16))
+    r = decode_step_leg(hkv, torch, w, w.context - 1, steps, 3, args.trials, 2, "long", oracle_check=False)
     return {"workload": "long: B=4, 131072 tokens, 32/8 heads, d=128, step = fused append 1 token + decode",
-            "ms_per_step": r["ms_per_step"],
-            "gbs": r["gbs"], "pct_hbm_peak": 100 * r["gbs"] / HBM_PEAK_GBS,
-            "decode_kernel_ms": kms, "decode_kernel_gbs": kb / (kms * 1e-3) / 1e9 if kms else None,
-            "decode_kernel_frac": kb / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS if kms else None,
-            "kernel_ms": r["kernel_ms"]}
+            "steps": steps, "ms_per_step": r["ms_per_step"], "trials_ms": r["trials_ms"], "gbs": r["gbs"],
+            "pct_hbm_peak": 100 * r["gbs"] / HBM_PEAK_GBS,
+            "roofline": roofline("decode_kernel (fused append + decode, claim walk)", r["kernel_bytes_per_step"],
+                                 r["device_ms_per_step"], "long")}
 
 
-def sparse_leg(hkv, torch, steps):
+def leg_sparse(hkv, torch, args):
+    """Top-K selection + sparse decode of the 32768-token workload, alternating two instances."""
     import workloads as wl
     w = wl.WORKLOADS["topk"]
-    H, Hq, d, k = w.n_kv_heads, w.n_q_heads, w.head_dim, w.k_sel
+    B, H, Hq, d, k = w.batch, w.n_kv_heads, w.n_q_heads, w.head_dim, w.k_sel
     n = w.context
-    log(f"sparse: 2 instances of B={w.batch} n={n}, K={k}")
-    insts = [hkv.HybridKVCache(H, d, w.batch, n) for _ in range(2)]
+    steps = max(8, min(args.steps, 20))
+    log(f"sparse: 2 instances of B={B} n={n}, K={k}")
+    insts = [hkv.HybridKVCache(H, d, B, n) for _ in range(2)]
     chunk = 8192
     for s in range(0, n, chunk):
-        kh = torch.from_numpy(wl.batch_tokens(w, list(range(w.batch)), s, chunk, "k")).cuda()
-        vh = torch.from_numpy(wl.batch_tokens(w, list(range(w.batch)), s, chunk, "v")).cuda()
+        kh = torch.from_numpy(wl.batch_tokens(w, list(range(B)), s, chunk, "k")).cuda()
+        vh = torch.from_numpy(wl.batch_tokens(w, list(range(B)), s, chunk, "v")).cuda()
         for c in insts:
             c.append(kh, vh)
         del kh, vh
     q = torch.from_numpy(wl.queries(w)).cuda()
     out = torch.empty_like(q)
-    idx = torch.empty((w.batch, H, k), dtype=torch.int32, device="cuda")
+    idx = torch.empty((B, H, k), dtype=torch.int32, device="cuda")
     ws = insts[0].workspace(Hq, k)
     for c in insts:
         c.topk(q, k, out_idx=idx, workspace=ws)
         c.decode(q, out=out, sel_idx=idx, k_sel=k, workspace=ws)
     torch.cuda.synchronize()
-    def sparse_step(i):
-        c = insts[i % 2]
-        c.topk(q, k, out_idx=idx, workspace=ws)
-        c.decode(q, out=out, sel_idx=idx, k_sel=k, workspace=ws)
 
-    t0 = time.perf_counter()
-    for i in range(steps):
-        sparse_step(i)
+    def topk_only(i):
+        insts[i % 2].topk(q, k, out_idx=idx, workspace=ws)
+
+    def sparse_only(i):
+        insts[i % 2].decode(q, out=out, sel_idx=idx, k_sel=k, workspace=ws)
+
+    def both(i):
+        topk_only(i)
+        sparse_only(i)
+
+    res = timed_trials(torch, both, 0, steps, args.trials)
+    t_topk = timed_trials(torch, topk_only, 0, steps, args.trials)
+    t_sparse = timed_trials(torch, sparse_only, 0, steps, args.trials)
+    # self-check: the last step's selection and output recomputed, then the oracle on sequence 0
+    c_last = insts[(res["next"] - 1) % 2]
+    idx_last, out_last = idx.cpu().numpy(), out.cpu().numpy()
+    idx2 = torch.empty_like(idx)
+    out2 = torch.empty_like(out)
+    c_last.topk(q, k, out_idx=idx2, workspace=ws)
+    c_last.decode(q, out=out2, sel_idx=idx2, k_sel=k, workspace=ws)
     torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / steps
+    same = bool(np.array_equal(idx2.cpu().numpy(), idx_last))
+    record_check({"what": "sparse: last timed selection vs recompute (bitwise)", "ok": same})
+    record_check(out_close(out_last, out2.cpu().numpy(), "sparse: last timed output vs recompute"))
+    import oracle.hkv_oracle as orc
+    kk = wl.tokens(w, 0, 0, n, "k")
+    vv = wl.tokens(w, 0, 0, n, "v")
+    st = orc.build_state(kk, vv, w.hot_tokens, w.block_size)
+    want, p, tau = orc.topk_select(wl.queries(w)[0], st, k)
+    ok = True
+    for h in range(H):
+        near = set(np.nonzero(np.abs(p[h] - tau[h]) <= 1e-5)[0].tolist())
+        ok &= (set(idx_last[0, h].tolist()) - near) == (set(want[h].tolist()) - near)
+    record_check({"what": "sparse: last timed selection, sequence 0, vs the fp64 oracle (outside near-ties)",
+                  "ok": bool(ok)})
+    o_ref, _ = orc.sparse_decode(wl.queries(w)[0], st, idx_last[0])
+    record_check(out_close(out_last[0], o_ref, "sparse: last timed output, sequence 0, vs the fp64 oracle"))
+    # per-kernel split of the selection (score vs select) from dispatch-recorded events, untimed pass
     for c in insts:
         hkv.hkv_timing_enable(c.handle, True)
     for i in range(steps):
-        sparse_step(i)
+        both(i)
     torch.cuda.synchronize()
     km = {}
     for kname in ("topk_score", "topk_select", "decode_sparse"):
@@ -308,25 +371,34 @@ def sparse_leg(hkv, torch, steps):
             tot, cnt = tot + a, cnt + b
         km[kname] = tot / cnt if cnt else None
     for c in insts:
+        hkv.hkv_timing_enable(c.handle, False)
         c.close()
-    sb = w.batch * (topk_bytes(n, H, Hq, d, k) + sparse_bytes(n, H, Hq, d, k))
-    score_b = w.batch * (n - 32) * H * d
-    return {"workload": "topk: B=16, 32768 tokens, 32/8 heads, d=128, K=512", "ms_per_step": ms,
-            "gbs": sb / (ms * 1e-3) / 1e9, "pct_hbm_peak": 100 * sb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "kernel_ms": km,
-            "topk_score_gbs": score_b / (km["topk_score"] * 1e-3) / 1e9 if km["topk_score"] else None}
+    del insts
+    torch.cuda.empty_cache()
+    tb = B * topk_bytes(n, H, Hq, d, k)
+    sb = B * sparse_bytes(n, H, Hq, d, k)
+    return {"workload": "topk: B=16, 32768 tokens, 32/8 heads, d=128, K=512; step = hkv_topk_select + sparse "
+                        "hkv_decode_attn", "steps": steps,
+            "ms_per_step": res["ms_per_step"], "trials_ms": res["trials_ms"],
+            "gbs": (tb + sb) / (res["ms_per_step"] * 1e-3) / 1e9,
+            "pct_hbm_peak": 100 * (tb + sb) / (res["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "roofline": roofline("topk_score_kernel + topk_select_kernel (one hkv_topk_select call)", tb,
+                                 t_topk["device_ms_per_step"], "topk"),
+            "roofline_sparse_decode": roofline("decode_kernel, sparse (gathered tokens)", sb,
+                                               t_sparse["device_ms_per_step"], "sparse_decode"),
+            "dispatch_event_ms": km}
 
 
-def ragged_leg(hkv, torch, steps=64, R=4, warmup=8):
+def leg_ragged(hkv, torch, args, steps=64, R=4, warmup=8):
     """The ragged paged batch: 64 sequences of seeded lengths in [128, 8192], cold blocks at a seeded
-    permutation of the physical pool, `steps` decode steps (one token appended per sequence, then a
-    dense decode), rotating over R instances; fused launches and, separately, the two-call form so the
-    append is timed on its own.  `warmup` untimed steps of each form come first."""
+    permutation of the physical pool, decode steps of one appended token per sequence plus a dense
+    decode (fused launch), rotating over R instances."""
     import workloads as wl
     w = wl.WORKLOADS["ragged"]
     B, H, Hq, d = w.batch, w.n_kv_heads, w.n_q_heads, w.head_dim
     lens0 = [int(x) for x in wl.lengths(w)]
-    per_inst = -(-2 * (steps + warmup) // R) + 1
+    trials = args.trials
+    per_inst = -(-(warmup + trials * steps) // R) + 2
     cap = max(lens0) + per_inst + 1
     mb = -(-(cap - w.hot_tokens) // w.block_size)
     perm = wl.block_permutation(w, B * mb).reshape(B, mb)
@@ -342,7 +414,6 @@ def ragged_leg(hkv, torch, steps=64, R=4, warmup=8):
             c.append(kb, vb, n_new)
         del kb, vb
     torch.cuda.synchronize()
-    # the new token of each sequence at each of its steps, and the per-step queries
     newk = [torch.from_numpy(np.stack([wl.tokens(w, b, lens0[b] + u, 1, "k")[0] for b in range(B)])).cuda()
             for u in range(per_inst)]
     newv = [torch.from_numpy(np.stack([wl.tokens(w, b, lens0[b] + u, 1, "v")[0] for b in range(B)])).cuda()
@@ -350,63 +421,52 @@ def ragged_leg(hkv, torch, steps=64, R=4, warmup=8):
     qs = [torch.from_numpy(wl.queries(w, step=i)).cuda() for i in range(8)]
     out = torch.empty_like(qs[0])
     ws = insts[0].workspace(Hq)
-    ones = np.ones(B, dtype=np.int32)
     stream = torch.cuda.current_stream().cuda_stream
     lib = hkv._lib
     used = [0] * R
 
-    def step(i, fused):
+    def step(i):
         r = i % R
         c, u = insts[r], used[r]
-        if fused:
-            st = lib.hkv_append_decode(c.handle, ctypes.byref(c.desc), newk[u].data_ptr(), newv[u].data_ptr(),
-                                       qs[i % 8].data_ptr(), Hq, out.data_ptr(), None, ws.data_ptr(), ws.numel(),
-                                       stream)
-        else:
-            st = lib.hkv_append(c.handle, ctypes.byref(c.desc), newk[u].data_ptr(), newv[u].data_ptr(),
-                                ones.ctypes.data, 1, stream)
-            if not st:
-                st = lib.hkv_decode_attn(c.handle, ctypes.byref(c.desc), qs[i % 8].data_ptr(), Hq, None, 0,
-                                         out.data_ptr(), None, ws.data_ptr(), ws.numel(), stream)
+        st = lib.hkv_append_decode(c.handle, ctypes.byref(c.desc), newk[u].data_ptr(), newv[u].data_ptr(),
+                                   qs[i % 8].data_ptr(), Hq, out.data_ptr(), None, ws.data_ptr(), ws.numel(), stream)
         if st:
             raise hkv.HKVError(st, "ragged step")
         used[r] += 1
         return sum(decode_bytes(n + used[r], H, Hq, d) + append_bytes(1, H, d) for n in lens0)
 
-    res = {"workload": f"ragged: {B} sequences, lengths {min(lens0)}..{max(lens0)} (seeded uniform), permuted "
-                       f"physical blocks, step = append 1 token/seq + dense decode"}
-    for fused in (True, False):
-        for i in range(warmup):
-            step(i, fused)
-        for c in insts:
-            hkv.hkv_timing_enable(c.handle, True)
-        nbytes = 0
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(steps):
-            nbytes += step(i, fused)
-        torch.cuda.synchronize()
-        ms = (time.perf_counter() - t0) * 1e3 / steps
-        km = {}
-        for kname in (("append_decode",) if fused else ("append", "decode")):
-            tot, cnt = 0.0, 0
-            for c in insts:
-                a, b = hkv.hkv_timing_read(c.handle, kname, reset=True)
-                tot, cnt = tot + a, cnt + b
-            km[kname] = tot / cnt if cnt else None
-        for c in insts:
-            hkv.hkv_timing_enable(c.handle, False)
-        key = "fused" if fused else "separate_calls"
-        res[key] = {"ms_per_step": ms, "gbs": nbytes / steps / (ms * 1e-3) / 1e9,
-                    "pct_hbm_peak": 100 * nbytes / steps / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                    "bytes_per_step": nbytes / steps, "kernel_ms": km}
-    res["note"] = "per-step times include a dispatch-recorded event pair per kernel"
+    for i in range(warmup):
+        step(i)
+    res = timed_trials(torch, step, warmup, steps, trials)
+    nbytes = statistics.mean(res.pop("rets"))
+    last = res["next"] - 1
+    r_last = last % R
+    got = out.cpu().numpy()
+    chk = torch.empty_like(out)
+    insts[r_last].decode(qs[last % 8], out=chk, workspace=ws)
+    torch.cuda.synchronize()
+    record_check(out_close(got, chk.cpu().numpy(), "ragged: last timed output vs hkv_decode_attn recompute"))
+    import oracle.hkv_oracle as orc
+    b0 = int(np.argmax(lens0))
+    n_b = lens0[b0] + used[r_last]
+    st = orc.build_state(wl.tokens(w, b0, 0, n_b, "k"), wl.tokens(w, b0, 0, n_b, "v"), w.hot_tokens, w.block_size)
+    o_ref, _ = orc.decode(qs[last % 8].cpu().numpy()[b0], st)
+    record_check(out_close(got[b0], o_ref, f"ragged: last timed output, longest sequence {b0}, vs the fp64 oracle"))
     for c in insts:
         c.close()
-    return res
+    del insts
+    torch.cuda.empty_cache()
+    return {"workload": f"ragged: {B} sequences, lengths {min(lens0)}..{max(lens0)} (seeded uniform), permuted "
+                        f"physical blocks, step = fused append 1 token/seq + dense decode", "steps": steps,
+            "ms_per_step": res["ms_per_step"], "trials_ms": res["trials_ms"],
+            "gbs": nbytes / (res["ms_per_step"] * 1e-3) / 1e9,
+            "pct_hbm_peak": 100 * nbytes / (res["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "bytes_per_step": nbytes,
+            "roofline": roofline("decode_kernel_ordered (fused append + decode, batch plan)", nbytes,
+                                 res["device_ms_per_step"], "ragged")}
 
 
-def graph_leg(hkv, torch, steps=640, R=64):
+def leg_graph(hkv, torch, args, steps=640, R=64):
     """The llama8b step replayed from a HIP graph (captured once: one fused launch per instance) against
     the same launches issued one by one."""
     import workloads as wl
@@ -459,15 +519,105 @@ def graph_leg(hkv, torch, steps=640, R=64):
     ms_eager = (time.perf_counter() - t0) * 1e3 / ((reps - 1) * R)
     for c in insts:
         c.close()
+    del insts
+    torch.cuda.empty_cache()
     step_b = B * (decode_bytes(n0 + 2, H, Hq, d) + append_bytes(1, H, d))
     return {"what": "llama8b step: one graph of 64 fused launches (one per instance) replayed, vs the same launches "
                     "issued eagerly", "ms_per_step_graph": ms_graph, "ms_per_step_eager": ms_eager,
             "gbs_graph": step_b / (ms_graph * 1e-3) / 1e9, "steps": reps * R}
 
 
+def leg_read_floor(hkv, torch, args, nbytes=34_406_400, R=64, reps=20):
+    """One-launch read of the llama8b step's bytes (34.4 MB, 64 rotating buffers, 16-byte non-temporal
+    loads) over launch shapes: the floor a one-launch decode of that size is measured against."""
+    bufs = [torch.ones(nbytes // 2, dtype=torch.float16, device="cuda") for _ in range(R)]
+    sink = torch.zeros(2048 * 1024, dtype=torch.int32, device="cuda")
+    shapes = [(256, 1024), (512, 512), (1024, 256), (2048, 256), (4096, 256)]
+    res = []
+    for wg, th in shapes:
+        def step(i, wg=wg, th=th):
+            hkv.hkv_read_probe(bufs[i % R], nbytes, wg, th, sink)
+        for i in range(R):
+            step(i)
+        t = timed_trials(torch, step, 0, R * reps, args.trials)
+        ms = t["device_ms_per_step"]
+        res.append({"workgroups": wg, "threads": th, "device_ms_per_launch": round(ms, 6),
+                    "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1), "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+    del bufs
+    torch.cuda.empty_cache()
+    best = min(res, key=lambda x: x["device_ms_per_launch"])
+    return {"what": "hkv_read_probe: one launch reading 34.4 MB once (the llama8b step's algorithmic bytes), "
+                    "64 rotating buffers", "bytes": nbytes, "shapes": res, "best": best}
+
+
+def host_info():
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    model = platform.processor() or ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        aff = os.cpu_count()
+    return {"cpu_count": os.cpu_count(), "affinity_cpus": aff, "cpu_model": model, "blas_threads": int(blas)}
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The fp64 oracle on the same step (append one token + decode), 8 sequences, bounded time."""
+    import oracle.hkv_oracle as orc
+    import workloads as wl
+    info = host_info()
+    n0 = w.context - 1
+    S, T = w.block_size, w.hot_tokens
+    H, Hq, d = w.n_kv_heads, w.n_q_heads, w.head_dim
+    extra = 512  # appended tokens the sample may use (bounds the sample as well as the time budget)
+    hist_k = [wl.tokens(w, b, 0, n0 + extra, "k") for b in range(w.batch)]
+    hist_v = [wl.tokens(w, b, 0, n0 + extra, "v") for b in range(w.batch)]
+    states = [orc.build_state(hist_k[b][:n0], hist_v[b][:n0], T, S) for b in range(w.batch)]
+    steps = 0
+    nbytes = 0
+    t0 = time.perf_counter()
+    while True:
+        for b in range(w.batch):
+            st = states[b]
+            n1 = st.n_tokens + 1
+            n_hot, n_cold = orc.split_history(n1, T)
+            j = (n_cold - 1) // S
+            kr, vr = hist_k[b][j * S:n_cold], hist_v[b][j * S:n_cold]
+            codes, scales = orc.quantize_block(kr, vr, S)
+            if j >= st.n_blocks:
+                st.codes = np.concatenate([st.codes, codes[None]])
+                st.scales = np.concatenate([st.scales, scales[None]])
+                st.n_valid = np.concatenate([st.n_valid, [n_cold - j * S]])
+            else:
+                st.codes[j], st.scales[j], st.n_valid[j] = codes, scales, n_cold - j * S
+            st.hot_k, st.hot_v = hist_k[b][n_cold:n1], hist_v[b][n_cold:n1]
+            st.n_tokens = n1
+            orc.decode(wl.query(w, b, steps), st)
+            nbytes += decode_bytes(n1, H, Hq, d) + append_bytes(1, H, d)
+        steps += 1
+        if time.perf_counter() - t0 >= budget_s or steps >= extra:
+            break
+    el = time.perf_counter() - t0
+    return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": info["blas_threads"], "kind": "oracle",
+            "sample": f"{steps} steps x {w.batch} sequences of the llama8b step (fp64 NumPy oracle: re-quantise "
+                      f"the touched block + dense decode), {el:.1f} s; cores = the BLAS threads of its matrix-vector "
+                      f"products (the rest of the oracle runs on one thread)",
+            "ms_per_step": el * 1e3 / steps, "host": info}
+
+
 def copy_calibration(torch, mib=256, reps=4):
     """A plain elementwise copy of a known size (reads and writes `mib` MiB per launch).  Hardware
-    counters of this launch calibrate the FETCH_SIZE / WRITE_SIZE readings of the decode kernel."""
+    counters of this launch calibrate the FETCH_SIZE / WRITE_SIZE readings of the path's kernels."""
     x = torch.ones(mib << 19, dtype=torch.float16, device="cuda")
     y = torch.empty_like(x)
     for _ in range(reps):
@@ -477,78 +627,82 @@ def copy_calibration(torch, mib=256, reps=4):
             "launches": reps}
 
 
+LEGS = ("llama8b", "separate", "long", "sparse", "ragged", "graph", "read_floor", "cpu")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=640)
     ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--trials", type=int, default=5)
     ap.add_argument("--instances", type=int, default=64)
+    ap.add_argument("--leg", default="all", help=f"comma-separated subset of {','.join(LEGS)} (default all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the long-context and sparse legs")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a known-size copy kernel (for hardware-counter traffic calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (this build runs the decode "
-              f"path on a single MI355X; the multi-GPU sharding is a design note, not a built path)",
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the decode path is built and "
+              f"measured on a single MI355X; how it would shard across GPUs is a design note, not a built path)",
               file=sys.stderr, flush=True)
         sys.exit(2)
+    legs = LEGS if args.leg == "all" else tuple(x for x in args.leg.split(",") if x)
+    for x in legs:
+        if x not in LEGS:
+            ap.error(f"unknown leg {x}")
+    if args.no_cpu_baseline:
+        legs = tuple(x for x in legs if x != "cpu")
     import torch
     import int8_kv_cache_hkv_amd as hkv
     import workloads as wl
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = wl.WORKLOADS["llama8b"]
     H, Hq, d = w.n_kv_heads, w.n_q_heads, w.head_dim
-    main_leg = run_leg(hkv, torch, w, w.context - 1, args.steps, args.warmup, args.instances, "llama8b")
-    kms = main_leg["kernel_ms"]["append_decode"]
-    achieved = main_leg["kernel_bytes"] / (kms * 1e-3) / 1e9 if kms else None
-    gbs = main_leg["gbs"]
-    ms = main_leg["ms_per_step"]
-    res = {
-        "metric": METRIC,
-        "value": round(gbs, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": "llama8b: Llama-3-8B-shaped layer, batch 8, 32 q / 8 kv heads, head_dim 128, "
-                               "2048 cached tokens (32 FP16 hot + 31 full + 1 half INT8 block), step = append 1 "
-                               "token/seq + dense decode",
-                   "batch": w.batch, "context": w.context, "hot_tokens": w.hot_tokens, "block_size": w.block_size,
-                   "quant_bits": w.quant_bits, "instances": args.instances},
-        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "queries_per_s": round(w.batch / (ms * 1e-3), 1),
-        "head_queries_per_s": round(w.batch * Hq / (ms * 1e-3), 1),
-        "bytes_per_step": int(main_leg["bytes_per_step"]),
-        "kernel_ms": main_leg["kernel_ms"],
-        "roofline": {"kernel": "decode_kernel (fused append + decode)", "bound": "hbm",
-                     "achieved": round(achieved, 1) if achieved else None, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None, "traffic": counter_traffic(),
-                     "bytes_per_launch": int(main_leg["kernel_bytes"]),
-                     "avg_launch_ms": kms},
-    }
-    if not args.no_extra:
-        sep = run_leg(hkv, torch, w, w.context - 1, min(args.steps, 320), args.warmup, args.instances,
-                      "llama8b (separate calls)", fused=False)
-        res["separate_calls"] = {"what": "the same step as hkv_append then hkv_decode_attn (two launches)",
-                                 "ms_per_step": sep["ms_per_step"], "gbs": sep["gbs"], "kernel_ms": sep["kernel_ms"]}
-        res["long"] = long_leg(hkv, torch, 16)
-        res["sparse"] = sparse_leg(hkv, torch, 20)
-        res["ragged"] = ragged_leg(hkv, torch)
-        res["hip_graph"] = graph_leg(hkv, torch)
+    res = {"metric": METRIC, "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": None, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f32", "data": "synthetic",
+           "config": {"workload": "llama8b: Llama-3-8B-shaped layer, batch 8, 32 q / 8 kv heads, head_dim 128, "
+                                  "2048 cached tokens (32 FP16 hot + 31 full + 1 half INT8 block), step = append 1 "
+                                  "token/seq + dense decode (one fused launch)",
+                      "batch": w.batch, "context": w.context, "hot_tokens": w.hot_tokens,
+                      "block_size": w.block_size, "quant_bits": w.quant_bits, "instances": args.instances},
+           "arithmetic": "int8 codes and fp16 values as exact fp16 MFMA operands, fp32 accumulation and softmax",
+           "trials": args.trials}
+    if "llama8b" in legs:
+        _, r = leg_llama8b(hkv, torch, args)
+        gbs, ms = r["gbs"], r["ms_per_step"]
+        res.update({
+            "value": round(gbs, 2), "ms_per_step": round(ms, 6), "trials_ms": r["trials_ms"],
+            "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "queries_per_s": round(w.batch / (ms * 1e-3), 1),
+            "head_queries_per_s": round(w.batch * Hq / (ms * 1e-3), 1),
+            "bytes_per_step": int(r["bytes_per_step"]),
+            "roofline": roofline("decode_kernel (fused append + decode)", r["kernel_bytes_per_step"],
+                                 r["device_ms_per_step"], "llama8b"),
+        })
+    if "separate" in legs:
+        res["separate_calls"] = leg_separate(hkv, torch, args)
+    if "long" in legs:
+        res["long"] = leg_long(hkv, torch, args)
+    if "sparse" in legs:
+        res["sparse"] = leg_sparse(hkv, torch, args)
+    if "ragged" in legs:
+        res["ragged"] = leg_ragged(hkv, torch, args)
+    if "graph" in legs:
+        res["hip_graph"] = leg_graph(hkv, torch, args)
+    if "read_floor" in legs:
+        res["read_floor"] = leg_read_floor(hkv, torch, args)
     if args.copy_calibration:
         res["copy_calibration"] = copy_calibration(torch)
-    if not args.no_cpu_baseline:
+    if "cpu" in legs:
         log("cpu baseline (fp64 oracle)")
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    res["self_check"] = {"passed": all(c["ok"] for c in CHECKS), "checks": CHECKS}
     print(json.dumps(res), flush=True)
+    if not res["self_check"]["passed"]:
+        sys.exit(3)
 
 
 if __name__ == "__main__":

@@ -26,7 +26,10 @@
  *     as raw device pointers (e.g. from torch tensors); arrays documented as
  *     "host" are plain host memory read during the call.
  *   - All validation is host-side and synchronous and happens before any HIP
- *     call; on an error nothing is launched and no buffer is touched.
+ *     call; on an error nothing is launched and no buffer is touched.  A
+ *     failed host-side allocation inside the library (launch planning uses a
+ *     few small host arrays) returns HKV_ERR_OUT_OF_MEMORY, also before any
+ *     launch; no C++ exception ever leaves an entry point.
  *   - Work is enqueued asynchronously on `stream` (0 = the null stream);
  *     results are valid after the stream is synchronised.  Calls on the same
  *     cache must be ordered on one stream; different caches are independent.
@@ -58,7 +61,8 @@ typedef enum {
   HKV_ERR_CAPACITY = -4,      /* an append would exceed max_blocks_per_seq or num_phys_blocks */
   HKV_ERR_WORKSPACE = -5,     /* workspace pointer NULL or smaller than hkv_workspace_bytes */
   HKV_ERR_HIP = -6,           /* a HIP runtime call or kernel launch failed */
-  HKV_ERR_ALIGNMENT = -7      /* a buffer is not aligned as documented */
+  HKV_ERR_ALIGNMENT = -7,     /* a buffer is not aligned as documented */
+  HKV_ERR_OUT_OF_MEMORY = -8  /* a host-side allocation of the library failed (nothing was launched) */
 } hkv_status;
 
 /* One cold block header, 16 bytes (Hybrid KV Cache page 3.2: each
@@ -134,6 +138,7 @@ typedef struct {
  *   HKV_ERR_UNSUPPORTED: protocol-valid values this library does not build:
  *     quant_bits != 8, block_size != 64, head_dim not in {64, 128}.
  *   HKV_ERR_NULL_POINTER: out is NULL.
+ *   HKV_ERR_OUT_OF_MEMORY: the handle could not be allocated.
  * On success *out owns a small host object released by hkv_destroy. */
 hkv_status hkv_create(int n_kv_heads, int head_dim, int hot_tokens, int block_size, int quant_bits,
                       hkv_handle* out);
@@ -149,6 +154,13 @@ hkv_status hkv_destroy(hkv_handle h);
  * HKV_ERR_INVALID_VALUE for negative counts or batch < 1. */
 hkv_status hkv_cache_sizes(hkv_handle h, int batch, int64_t max_tokens_per_seq, int64_t num_phys_blocks,
                            hkv_cache_sizes_t* out);
+
+/* The same sizes as hkv_cache_sizes, as a plain array of six byte counts in
+ * the order hot, tail, cold, scales, headers, seq_len (the layouts above; a
+ * dense pool when num_phys_blocks is 0).  HKV_ERR_INVALID_VALUE for negative
+ * counts, batch < 1 or sizes past the int32 block-id range;
+ * HKV_ERR_NULL_POINTER if h or bytes_out is NULL. */
+hkv_status hkv_sizes(hkv_handle h, int batch, int max_tokens_per_seq, int num_phys_blocks, size_t bytes_out[6]);
 
 /* Header-table size of one sequence (Hybrid KV Cache page 5.4: blocks =
  * ceil(tokens / block_size), about 16 bytes per block): *n_blocks =
@@ -286,6 +298,19 @@ typedef enum {
 
 hkv_status hkv_timing_enable(hkv_handle h, int enable);
 hkv_status hkv_timing_read(hkv_handle h, int kind, double* total_ms, int64_t* count, int reset);
+
+/* Streaming read probe (measurement aid, not part of the cache protocol): one
+ * launch of `workgroups` x `threads` threads reads the `bytes` bytes at `src`
+ * once with 16-byte non-temporal loads, the access pattern of the cold-tile
+ * streams.  Its duration is the read floor that a one-launch decode over the
+ * same number of bytes is measured against.
+ *   src   device, 16-byte aligned; bytes a multiple of 16.
+ *   sink  device uint32 [workgroups * threads]; written only if a lane's
+ *         folded data equals a fixed sentinel (it keeps the loads alive).
+ * HKV_ERR_INVALID_VALUE: threads not a multiple of 64 in [64, 1024],
+ * workgroups < 1 or bytes % 16 != 0. */
+hkv_status hkv_read_probe(const void* src, size_t bytes, int workgroups, int threads, uint32_t* sink,
+                          hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -23,13 +23,14 @@ LIB_PATH = os.path.join(_PKG, "libhkv.so")
 
 HKV_OK = 0
 STATUS_NAMES = {0: "HKV_OK", -1: "HKV_ERR_INVALID_VALUE", -2: "HKV_ERR_UNSUPPORTED", -3: "HKV_ERR_NULL_POINTER",
-                -4: "HKV_ERR_CAPACITY", -5: "HKV_ERR_WORKSPACE", -6: "HKV_ERR_HIP", -7: "HKV_ERR_ALIGNMENT"}
+                -4: "HKV_ERR_CAPACITY", -5: "HKV_ERR_WORKSPACE", -6: "HKV_ERR_HIP", -7: "HKV_ERR_ALIGNMENT",
+                -8: "HKV_ERR_OUT_OF_MEMORY"}
 KERNELS = {"append": 0, "append_ring": 1, "decode": 2, "decode_sparse": 3, "topk_score": 4, "topk_select": 5,
            "append_decode": 6}
-EXPORTS = ["hkv_create", "hkv_destroy", "hkv_cache_sizes", "hkv_header_table_bytes", "hkv_workspace_bytes",
+EXPORTS = ["hkv_create", "hkv_destroy", "hkv_cache_sizes", "hkv_sizes", "hkv_header_table_bytes", "hkv_workspace_bytes",
            "hkv_append", "hkv_decode_attn", "hkv_append_decode", "hkv_topk_select", "hkv_status_string",
            "hkv_timing_enable",
-           "hkv_timing_read", "hkv_last_error_detail"]
+           "hkv_timing_read", "hkv_last_error_detail", "hkv_read_probe"]
 
 
 class HKVError(RuntimeError):
@@ -70,6 +71,7 @@ def _load() -> ctypes.CDLL:
         "hkv_create": [i32, i32, i32, i32, i32, ctypes.POINTER(vp)],
         "hkv_destroy": [vp],
         "hkv_cache_sizes": [vp, i32, i64, i64, ctypes.POINTER(CacheSizes)],
+        "hkv_sizes": [vp, i32, i32, i32, ctypes.POINTER(sz)],
         "hkv_header_table_bytes": [i32, i32, i64, ctypes.POINTER(i64), ctypes.POINTER(sz)],
         "hkv_workspace_bytes": [vp, ctypes.POINTER(CacheDesc), i32, i32, ctypes.POINTER(sz)],
         "hkv_append": [vp, ctypes.POINTER(CacheDesc), vp, vp, vp, i32, vp],
@@ -78,6 +80,7 @@ def _load() -> ctypes.CDLL:
         "hkv_topk_select": [vp, ctypes.POINTER(CacheDesc), vp, i32, i32, vp, vp, sz, vp],
         "hkv_timing_enable": [vp, i32],
         "hkv_timing_read": [vp, i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64), i32],
+        "hkv_read_probe": [vp, sz, i32, i32, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -145,6 +148,13 @@ def hkv_cache_sizes(handle: int, batch: int, max_tokens_per_seq: int, num_phys_b
     return out
 
 
+def hkv_sizes(handle: int, batch: int, max_tokens_per_seq: int, num_phys_blocks: int = 0):
+    """Byte counts (hot, tail, cold, scales, headers, seq_len) as a tuple."""
+    out = (ctypes.c_size_t * 6)()
+    _check(_lib.hkv_sizes(handle, batch, max_tokens_per_seq, num_phys_blocks, out), "hkv_sizes")
+    return tuple(int(x) for x in out)
+
+
 def hkv_header_table_bytes(hot_tokens: int, block_size: int, total_tokens: int):
     nb, by = ctypes.c_int64(), ctypes.c_size_t()
     _check(_lib.hkv_header_table_bytes(hot_tokens, block_size, total_tokens, ctypes.byref(nb), ctypes.byref(by)),
@@ -185,6 +195,12 @@ def hkv_topk_select(handle: int, desc: CacheDesc, q, k: int, out_idx, workspace,
     _check(_lib.hkv_topk_select(handle, ctypes.byref(desc), _ptr(q), int(q.shape[1]), int(k), _ptr(out_idx),
                                 _ptr(workspace), int(workspace.numel() * workspace.element_size()),
                                 _stream(stream)), "hkv_topk_select")
+
+
+def hkv_read_probe(src, nbytes: int, workgroups: int, threads: int, sink, stream=None) -> None:
+    """One launch reading nbytes of src (a device tensor) once (measurement aid)."""
+    _check(_lib.hkv_read_probe(_ptr(src), int(nbytes), int(workgroups), int(threads), _ptr(sink), _stream(stream)),
+           "hkv_read_probe")
 
 
 def hkv_timing_enable(handle: int, enable: bool = True) -> None:

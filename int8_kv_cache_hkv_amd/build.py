@@ -1,24 +1,36 @@
-"""Build libhkv.so (all HIP kernels + the C-ABI host code) for gfx950, in-tree."""
+"""Build libhkv.so (all HIP kernels + the C-ABI host code) for gfx950, in-tree.
+
+Every source is compiled to an object of its own, in parallel, and the
+objects are linked into one shared library.
+"""
 from __future__ import annotations
 
+import concurrent.futures as cf
 import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libhkv.so")
-SOURCES = ["append.hip", "decode.hip", "topk.hip", "hkv_api.cpp"]
+
+
+def sources() -> list:
+    """Every translation unit of the library: the .hip kernel files and the host .cpp files."""
+    return sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
+
 
 HIPCC_FLAGS = [
-    "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
+    "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",
     "-fhip-fp32-correctly-rounded-divide-sqrt",   # IEEE fp32 division for the quantiser
     "-fno-fast-math", "-ffp-contract=fast", "-fno-strict-aliasing",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
+NOISE = "is not a recognized feature for this target"
 
 
 def hipcc() -> str:
@@ -28,21 +40,35 @@ def hipcc() -> str:
     return path
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into int8_kv_cache_hkv_amd/libhkv.so (always recompiles)."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in (res.stderr or "").splitlines() if noise not in l)
+    err = "\n".join(l for l in (res.stderr or "").splitlines() if NOISE not in l)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+        raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd[-3:])}\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
+
+
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    """Compile every source into int8_kv_cache_hkv_amd/libhkv.so (always recompiles)."""
+    cc = hipcc()
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    jobs = jobs or min(16, os.cpu_count() or 1)
+    with tempfile.TemporaryDirectory(prefix="hkv_build_") as tmpd:
+        objs = []
+        cmds = []
+        for src in sources():
+            obj = os.path.join(tmpd, src + ".o")
+            objs.append(obj)
+            cmds.append([cc, *HIPCC_FLAGS, *inc, "-c", os.path.join(CSRC, src), "-o", obj])
+        with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+            for f in [ex.submit(_run, c, verbose) for c in cmds]:
+                f.result()
+        tmp = LIB + ".tmp"
+        _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+        os.replace(tmp, LIB)
     return LIB
 
 

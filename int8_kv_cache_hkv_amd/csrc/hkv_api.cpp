@@ -239,6 +239,19 @@ hkv_status hip_status(hipError_t e, const char* where) {
   return HKV_ERR_HIP;
 }
 
+// Runs an entry point's body; a failed host allocation (std::bad_alloc, or a
+// length error from a huge count) becomes HKV_ERR_OUT_OF_MEMORY, so no C++
+// exception crosses the C ABI.  Every body validates and allocates before its
+// first HIP call, so nothing has been launched when this status is returned.
+template <typename F>
+hkv_status guarded(F&& body) noexcept {
+  try {
+    return body();
+  } catch (...) {
+    return HKV_ERR_OUT_OF_MEMORY;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -253,7 +266,7 @@ hkv_status hkv_create(int n_kv_heads, int head_dim, int hot_tokens, int block_si
   if (quant_bits != 8 || block_size != hkv::kBlockSize || (head_dim != 64 && head_dim != 128))
     return HKV_ERR_UNSUPPORTED;
   hkv_ctx* h = new (std::nothrow) hkv_ctx;
-  if (!h) return HKV_ERR_INVALID_VALUE;
+  if (!h) return HKV_ERR_OUT_OF_MEMORY;
   h->H = n_kv_heads;
   h->D = head_dim;
   h->T = hot_tokens;
@@ -294,6 +307,20 @@ hkv_status hkv_cache_sizes(hkv_handle h, int batch, int64_t max_tokens_per_seq, 
   return HKV_OK;
 }
 
+hkv_status hkv_sizes(hkv_handle h, int batch, int max_tokens_per_seq, int num_phys_blocks, size_t bytes_out[6]) {
+  if (!h || !bytes_out) return HKV_ERR_NULL_POINTER;
+  hkv_cache_sizes_t s;
+  const hkv_status st = hkv_cache_sizes(h, batch, max_tokens_per_seq, num_phys_blocks, &s);
+  if (st != HKV_OK) return st;
+  bytes_out[0] = s.hot;
+  bytes_out[1] = s.tail;
+  bytes_out[2] = s.cold;
+  bytes_out[3] = s.scales;
+  bytes_out[4] = s.headers;
+  bytes_out[5] = s.seq_len;
+  return HKV_OK;
+}
+
 hkv_status hkv_header_table_bytes(int hot_tokens, int block_size, int64_t total_tokens, int64_t* n_blocks,
                                   size_t* bytes) {
   if (!n_blocks || !bytes) return HKV_ERR_NULL_POINTER;
@@ -318,211 +345,235 @@ hkv_status hkv_workspace_bytes(hkv_handle h, const hkv_cache_desc* c, int n_q_he
 
 hkv_status hkv_append(hkv_handle h, const hkv_cache_desc* c, const void* k_new, const void* v_new,
                       const int32_t* n_new_host, int max_n_new, hipStream_t stream) {
-  hkv_status st = check_desc(h, c);
-  if (st != HKV_OK) return st;
-  if (!n_new_host) return HKV_ERR_NULL_POINTER;
-  if (max_n_new < 0) return HKV_ERR_INVALID_VALUE;
-  bool any = false;
-  for (int b = 0; b < c->batch; ++b) {
-    const int nn = n_new_host[b];
-    if (nn < 0 || nn > max_n_new) return HKV_ERR_INVALID_VALUE;
-    const int64_t n1 = static_cast<int64_t>(c->seq_len_host[b]) + nn;
-    if (n1 > INT32_MAX) return HKV_ERR_CAPACITY;
-    if (cold_blocks(n1, h->T, h->S) > c->max_blocks_per_seq) return HKV_ERR_CAPACITY;
-    if (nn > 0) any = true;
-  }
-  if (!any) return HKV_OK;
-  if (!k_new || !v_new) return HKV_ERR_NULL_POINTER;
-  if (reinterpret_cast<uintptr_t>(k_new) % 16 != 0 || reinterpret_cast<uintptr_t>(v_new) % 16 != 0)
-    return HKV_ERR_ALIGNMENT;
-
-  hkv::AppendParams p;
-  std::memset(&p, 0, sizeof(p));
-  p.c = view_of(h, c);
-  p.k_new = static_cast<const _Float16*>(k_new);
-  p.v_new = static_cast<const _Float16*>(v_new);
-  p.max_n_new = max_n_new;
-  for (int b0 = 0; b0 < c->batch; b0 += hkv::kAppendChunk) {
-    const int ns = std::min(hkv::kAppendChunk, c->batch - b0);
-    int touched = 0;
-    bool chunk_any = false;
-    for (int i = 0; i < ns; ++i) {
-      const int b = b0 + i;
+  return guarded([&]() -> hkv_status {
+    hkv_status st = check_desc(h, c);
+    if (st != HKV_OK) return st;
+    if (!n_new_host) return HKV_ERR_NULL_POINTER;
+    if (max_n_new < 0) return HKV_ERR_INVALID_VALUE;
+    bool any = false;
+    for (int b = 0; b < c->batch; ++b) {
       const int nn = n_new_host[b];
-      p.n_new[i] = nn;
-      p.n0[i] = c->seq_len_host[b];
-      if (nn == 0) continue;
-      chunk_any = true;
-      const int64_t n0 = c->seq_len_host[b], n1 = n0 + nn;
-      const int64_t cold0 = std::max<int64_t>(0, n0 - h->T), cold1 = std::max<int64_t>(0, n1 - h->T);
-      if (cold1 > cold0) touched = std::max<int>(touched, static_cast<int>((cold1 + h->S - 1) / h->S - cold0 / h->S));
+      if (nn < 0 || nn > max_n_new) return HKV_ERR_INVALID_VALUE;
+      const int64_t n1 = static_cast<int64_t>(c->seq_len_host[b]) + nn;
+      if (n1 > INT32_MAX) return HKV_ERR_CAPACITY;
+      if (cold_blocks(n1, h->T, h->S) > c->max_blocks_per_seq) return HKV_ERR_CAPACITY;
+      if (nn > 0) any = true;
     }
-    if (!chunk_any) continue;
-    p.b0 = b0;
-    p.n_seq = ns;
-    p.touched_max = touched;
-    p.single_pass = touched <= hkv::kSinglePassMaxBlocks ? 1 : 0;
-    LaunchCtx qctx = make_ctx(h, stream, HKV_KERNEL_APPEND);
-    LaunchCtx rctx = p.single_pass ? LaunchCtx{stream, nullptr, nullptr} : make_ctx(h, stream, HKV_KERNEL_APPEND_RING);
-    if (touched == 0 && !p.single_pass && qctx.start) {  // nothing to quantise: release the unused event pair
-      h->free_events.push_back(qctx.start);
-      h->free_events.push_back(qctx.stop);
-      h->pending.erase(h->pending.end() - 2);
-      qctx.start = qctx.stop = nullptr;
+    if (!any) return HKV_OK;
+    if (!k_new || !v_new) return HKV_ERR_NULL_POINTER;
+    if (reinterpret_cast<uintptr_t>(k_new) % 16 != 0 || reinterpret_cast<uintptr_t>(v_new) % 16 != 0)
+      return HKV_ERR_ALIGNMENT;
+
+    if (h->timing) {  // every host allocation of the call happens here, before the first launch
+      const size_t chunks = (static_cast<size_t>(c->batch) + hkv::kAppendChunk - 1) / hkv::kAppendChunk;
+      h->pending.reserve(h->pending.size() + 2 * chunks);
+      h->free_events.reserve(h->free_events.size() + 2 * chunks);
     }
-    hipError_t e = hkv::launch_append(p, qctx, rctx);
-    if (e != hipSuccess) return hip_status(e, "hkv_append launch");
-  }
-  for (int b = 0; b < c->batch; ++b) c->seq_len_host[b] += n_new_host[b];
-  return HKV_OK;
+    hkv::AppendParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.c = view_of(h, c);
+    p.k_new = static_cast<const _Float16*>(k_new);
+    p.v_new = static_cast<const _Float16*>(v_new);
+    p.max_n_new = max_n_new;
+    for (int b0 = 0; b0 < c->batch; b0 += hkv::kAppendChunk) {
+      const int ns = std::min(hkv::kAppendChunk, c->batch - b0);
+      int touched = 0;
+      bool chunk_any = false;
+      for (int i = 0; i < ns; ++i) {
+        const int b = b0 + i;
+        const int nn = n_new_host[b];
+        p.n_new[i] = nn;
+        p.n0[i] = c->seq_len_host[b];
+        if (nn == 0) continue;
+        chunk_any = true;
+        const int64_t n0 = c->seq_len_host[b], n1 = n0 + nn;
+        const int64_t cold0 = std::max<int64_t>(0, n0 - h->T), cold1 = std::max<int64_t>(0, n1 - h->T);
+        if (cold1 > cold0) touched = std::max<int>(touched, static_cast<int>((cold1 + h->S - 1) / h->S - cold0 / h->S));
+      }
+      if (!chunk_any) continue;
+      p.b0 = b0;
+      p.n_seq = ns;
+      p.touched_max = touched;
+      p.single_pass = touched <= hkv::kSinglePassMaxBlocks ? 1 : 0;
+      LaunchCtx qctx = make_ctx(h, stream, HKV_KERNEL_APPEND);
+      LaunchCtx rctx = p.single_pass ? LaunchCtx{stream, nullptr, nullptr} : make_ctx(h, stream, HKV_KERNEL_APPEND_RING);
+      if (touched == 0 && !p.single_pass && qctx.start) {  // nothing to quantise: release the unused event pair
+        h->free_events.push_back(qctx.start);
+        h->free_events.push_back(qctx.stop);
+        h->pending.erase(h->pending.end() - 2);
+        qctx.start = qctx.stop = nullptr;
+      }
+      hipError_t e = hkv::launch_append(p, qctx, rctx);
+      if (e != hipSuccess) return hip_status(e, "hkv_append launch");
+    }
+    for (int b = 0; b < c->batch; ++b) c->seq_len_host[b] += n_new_host[b];
+    return HKV_OK;
+  });
 }
 
 hkv_status hkv_decode_attn(hkv_handle h, const hkv_cache_desc* c, const void* q, int n_q_heads,
                            const int32_t* sel_idx, int k_sel, void* out, float* lse, void* workspace,
                            size_t ws_bytes, hipStream_t stream) {
-  hkv_status st = check_desc(h, c);
-  if (st != HKV_OK) return st;
-  if (!q || !out) return HKV_ERR_NULL_POINTER;
-  if (n_q_heads < 1 || n_q_heads % h->H != 0) return HKV_ERR_INVALID_VALUE;
-  const int G = n_q_heads / h->H;
-  if (sel_idx && (k_sel < 1 || k_sel > hkv::kMaxTopK)) return HKV_ERR_INVALID_VALUE;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return HKV_ERR_UNSUPPORTED;
-  int64_t units_max = 1;
-  std::vector<int64_t> units(c->batch);
-  for (int b = 0; b < c->batch; ++b) {
-    const int n = c->seq_len_host[b];
-    if (n == 0) return HKV_ERR_INVALID_VALUE;
-    const int64_t nblk = cold_blocks(n, h->T, h->S);
-    units[b] = nblk;
-    if (!sel_idx) units_max = std::max(units_max, nblk);
-  }
-  size_t need = 0;
-  if (hkv_workspace_bytes(h, c, n_q_heads, sel_idx ? k_sel : 0, &need) != HKV_OK) return HKV_ERR_INVALID_VALUE;
-  if (!workspace || ws_bytes < need) return HKV_ERR_WORKSPACE;
-  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0 || reinterpret_cast<uintptr_t>(q) % 16 != 0)
-    return HKV_ERR_ALIGNMENT;
+  return guarded([&]() -> hkv_status {
+    hkv_status st = check_desc(h, c);
+    if (st != HKV_OK) return st;
+    if (!q || !out) return HKV_ERR_NULL_POINTER;
+    if (n_q_heads < 1 || n_q_heads % h->H != 0) return HKV_ERR_INVALID_VALUE;
+    const int G = n_q_heads / h->H;
+    if (sel_idx && (k_sel < 1 || k_sel > hkv::kMaxTopK)) return HKV_ERR_INVALID_VALUE;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return HKV_ERR_UNSUPPORTED;
+    int64_t units_max = 1;
+    std::vector<int64_t> units(c->batch);
+    for (int b = 0; b < c->batch; ++b) {
+      const int n = c->seq_len_host[b];
+      if (n == 0) return HKV_ERR_INVALID_VALUE;
+      const int64_t nblk = cold_blocks(n, h->T, h->S);
+      units[b] = nblk;
+      if (!sel_idx) units_max = std::max(units_max, nblk);
+    }
+    size_t need = 0;
+    if (hkv_workspace_bytes(h, c, n_q_heads, sel_idx ? k_sel : 0, &need) != HKV_OK) return HKV_ERR_INVALID_VALUE;
+    if (!workspace || ws_bytes < need) return HKV_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0 || reinterpret_cast<uintptr_t>(q) % 16 != 0)
+      return HKV_ERR_ALIGNMENT;
 
-  hkv::DecodeParams p;
-  p.c = view_of(h, c);
-  p.G = G;
-  p.q = static_cast<const _Float16*>(q);
-  p.sel = sel_idx;
-  p.k_sel = sel_idx ? k_sel : 0;
-  p.counters = static_cast<unsigned*>(workspace);
-  p.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(counters_bytes(c, h->H), 256));
-  const SplitPlan sp = sel_idx ? plan_sparse(k_sel) : plan_splits(static_cast<int64_t>(c->batch) * h->H, units_max);
-  p.nsplit = sp.nsplit;
-  p.nparts = sp.nsplit + 1;
-  p.units_per_split = sp.per_split;
-  p.wg_order = sp.wg_order;
-  p.work = (!sel_idx && sp.claim) ? claim_counters(workspace, c, h->H) : nullptr;
-  uint16_t order[hkv::kOrderTableMax];
-  const bool ordered = !sel_idx && sp.batch && order_by_work(p, units, sp.per_split, order);
-  if (ordered) p.wg_order = hkv::kOrderTable;
-  p.qscale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(h->D)));
-  p.out = static_cast<_Float16*>(out);
-  p.lse = lse;
-  p.k_new = p.v_new = nullptr;
-  p.seq_counters = nullptr;
-  LaunchCtx a = make_ctx(h, stream, sel_idx ? HKV_KERNEL_DECODE_SPARSE : HKV_KERNEL_DECODE);
-  return hip_status(hkv::launch_decode(p, a, ordered ? order : nullptr), "hkv_decode_attn launch");
+    hkv::DecodeParams p;
+    p.c = view_of(h, c);
+    p.G = G;
+    p.q = static_cast<const _Float16*>(q);
+    p.sel = sel_idx;
+    p.k_sel = sel_idx ? k_sel : 0;
+    p.counters = static_cast<unsigned*>(workspace);
+    p.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(counters_bytes(c, h->H), 256));
+    const SplitPlan sp = sel_idx ? plan_sparse(k_sel) : plan_splits(static_cast<int64_t>(c->batch) * h->H, units_max);
+    p.nsplit = sp.nsplit;
+    p.nparts = sp.nsplit + 1;
+    p.units_per_split = sp.per_split;
+    p.wg_order = sp.wg_order;
+    p.work = (!sel_idx && sp.claim) ? claim_counters(workspace, c, h->H) : nullptr;
+    uint16_t order[hkv::kOrderTableMax];
+    const bool ordered = !sel_idx && sp.batch && order_by_work(p, units, sp.per_split, order);
+    if (ordered) p.wg_order = hkv::kOrderTable;
+    p.qscale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(h->D)));
+    p.out = static_cast<_Float16*>(out);
+    p.lse = lse;
+    p.k_new = p.v_new = nullptr;
+    p.seq_counters = nullptr;
+    LaunchCtx a = make_ctx(h, stream, sel_idx ? HKV_KERNEL_DECODE_SPARSE : HKV_KERNEL_DECODE);
+    return hip_status(hkv::launch_decode(p, a, ordered ? order : nullptr), "hkv_decode_attn launch");
+  });
 }
 
 hkv_status hkv_append_decode(hkv_handle h, const hkv_cache_desc* c, const void* k_new, const void* v_new,
                              const void* q, int n_q_heads, void* out, float* lse, void* workspace, size_t ws_bytes,
                              hipStream_t stream) {
-  hkv_status st = check_desc(h, c);
-  if (st != HKV_OK) return st;
-  if (!k_new || !v_new || !q || !out) return HKV_ERR_NULL_POINTER;
-  if (n_q_heads < 1 || n_q_heads % h->H != 0) return HKV_ERR_INVALID_VALUE;
-  const int G = n_q_heads / h->H;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return HKV_ERR_UNSUPPORTED;
-  if (h->S != hkv::kBlockSize) return HKV_ERR_UNSUPPORTED;
-  int64_t units_max = 1;
-  std::vector<int64_t> units(c->batch);
-  for (int b = 0; b < c->batch; ++b) {
-    const int64_t n0 = c->seq_len_host[b];
-    if (n0 < 0) return HKV_ERR_INVALID_VALUE;
-    if (n0 + 1 > INT32_MAX) return HKV_ERR_CAPACITY;
-    if (cold_blocks(n0 + 1, h->T, h->S) > c->max_blocks_per_seq) return HKV_ERR_CAPACITY;
-    // cold units of the decode: the full blocks before the one the appended token spills into
-    units[b] = std::max<int64_t>(0, n0 - h->T) / h->S;
-    units_max = std::max<int64_t>(units_max, units[b]);
-  }
-  size_t need = 0;
-  if (hkv_workspace_bytes(h, c, n_q_heads, 0, &need) != HKV_OK) return HKV_ERR_INVALID_VALUE;
-  if (!workspace || ws_bytes < need) return HKV_ERR_WORKSPACE;
-  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0 || reinterpret_cast<uintptr_t>(q) % 16 != 0 ||
-      reinterpret_cast<uintptr_t>(k_new) % 16 != 0 || reinterpret_cast<uintptr_t>(v_new) % 16 != 0)
-    return HKV_ERR_ALIGNMENT;
+  return guarded([&]() -> hkv_status {
+    hkv_status st = check_desc(h, c);
+    if (st != HKV_OK) return st;
+    if (!k_new || !v_new || !q || !out) return HKV_ERR_NULL_POINTER;
+    if (n_q_heads < 1 || n_q_heads % h->H != 0) return HKV_ERR_INVALID_VALUE;
+    const int G = n_q_heads / h->H;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return HKV_ERR_UNSUPPORTED;
+    if (h->S != hkv::kBlockSize) return HKV_ERR_UNSUPPORTED;
+    int64_t units_max = 1;
+    std::vector<int64_t> units(c->batch);
+    for (int b = 0; b < c->batch; ++b) {
+      const int64_t n0 = c->seq_len_host[b];
+      if (n0 < 0) return HKV_ERR_INVALID_VALUE;
+      if (n0 + 1 > INT32_MAX) return HKV_ERR_CAPACITY;
+      if (cold_blocks(n0 + 1, h->T, h->S) > c->max_blocks_per_seq) return HKV_ERR_CAPACITY;
+      // cold units of the decode: the full blocks before the one the appended token spills into
+      units[b] = std::max<int64_t>(0, n0 - h->T) / h->S;
+      units_max = std::max<int64_t>(units_max, units[b]);
+    }
+    size_t need = 0;
+    if (hkv_workspace_bytes(h, c, n_q_heads, 0, &need) != HKV_OK) return HKV_ERR_INVALID_VALUE;
+    if (!workspace || ws_bytes < need) return HKV_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0 || reinterpret_cast<uintptr_t>(q) % 16 != 0 ||
+        reinterpret_cast<uintptr_t>(k_new) % 16 != 0 || reinterpret_cast<uintptr_t>(v_new) % 16 != 0)
+      return HKV_ERR_ALIGNMENT;
 
-  hkv::DecodeParams p;
-  p.c = view_of(h, c);
-  p.G = G;
-  p.q = static_cast<const _Float16*>(q);
-  p.sel = nullptr;
-  p.k_sel = 0;
-  p.counters = static_cast<unsigned*>(workspace);
-  p.seq_counters = p.counters + static_cast<size_t>(c->batch) * h->H;
-  p.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(counters_bytes(c, h->H), 256));
-  const SplitPlan sp = plan_splits(static_cast<int64_t>(c->batch) * h->H, units_max, 2);
-  p.nsplit = sp.nsplit;
-  p.nparts = sp.nsplit + 2;
-  p.units_per_split = sp.per_split;
-  p.wg_order = sp.wg_order;
-  p.work = sp.claim ? claim_counters(workspace, c, h->H) : nullptr;
-  uint16_t order[hkv::kOrderTableMax];
-  const bool ordered = sp.batch && order_by_work(p, units, sp.per_split, order);
-  if (ordered) p.wg_order = hkv::kOrderTable;
-  p.qscale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(h->D)));
-  p.out = static_cast<_Float16*>(out);
-  p.lse = lse;
-  p.k_new = static_cast<const _Float16*>(k_new);
-  p.v_new = static_cast<const _Float16*>(v_new);
-  LaunchCtx a = make_ctx(h, stream, HKV_KERNEL_APPEND_DECODE);
-  const hkv_status r = hip_status(hkv::launch_decode(p, a, ordered ? order : nullptr), "hkv_append_decode launch");
-  if (r != HKV_OK) return r;
-  for (int b = 0; b < c->batch; ++b) c->seq_len_host[b] += 1;
-  return HKV_OK;
+    hkv::DecodeParams p;
+    p.c = view_of(h, c);
+    p.G = G;
+    p.q = static_cast<const _Float16*>(q);
+    p.sel = nullptr;
+    p.k_sel = 0;
+    p.counters = static_cast<unsigned*>(workspace);
+    p.seq_counters = p.counters + static_cast<size_t>(c->batch) * h->H;
+    p.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(counters_bytes(c, h->H), 256));
+    const SplitPlan sp = plan_splits(static_cast<int64_t>(c->batch) * h->H, units_max, 2);
+    p.nsplit = sp.nsplit;
+    p.nparts = sp.nsplit + 2;
+    p.units_per_split = sp.per_split;
+    p.wg_order = sp.wg_order;
+    p.work = sp.claim ? claim_counters(workspace, c, h->H) : nullptr;
+    uint16_t order[hkv::kOrderTableMax];
+    const bool ordered = sp.batch && order_by_work(p, units, sp.per_split, order);
+    if (ordered) p.wg_order = hkv::kOrderTable;
+    p.qscale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(h->D)));
+    p.out = static_cast<_Float16*>(out);
+    p.lse = lse;
+    p.k_new = static_cast<const _Float16*>(k_new);
+    p.v_new = static_cast<const _Float16*>(v_new);
+    LaunchCtx a = make_ctx(h, stream, HKV_KERNEL_APPEND_DECODE);
+    const hkv_status r = hip_status(hkv::launch_decode(p, a, ordered ? order : nullptr), "hkv_append_decode launch");
+    if (r != HKV_OK) return r;
+    for (int b = 0; b < c->batch; ++b) c->seq_len_host[b] += 1;
+    return HKV_OK;
+  });
 }
 
 hkv_status hkv_topk_select(hkv_handle h, const hkv_cache_desc* c, const void* q, int n_q_heads, int k,
                            int32_t* out_idx, void* workspace, size_t ws_bytes, hipStream_t stream) {
-  hkv_status st = check_desc(h, c);
-  if (st != HKV_OK) return st;
-  if (!q || !out_idx) return HKV_ERR_NULL_POINTER;
-  if (n_q_heads < 1 || n_q_heads % h->H != 0) return HKV_ERR_INVALID_VALUE;
-  if (k < 1 || k > hkv::kMaxTopK) return HKV_ERR_INVALID_VALUE;
-  const int G = n_q_heads / h->H;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return HKV_ERR_UNSUPPORTED;
-  if (h->S != hkv::kBlockSize) return HKV_ERR_UNSUPPORTED;
-  size_t need = 0;
-  if (hkv_workspace_bytes(h, c, n_q_heads, k, &need) != HKV_OK) return HKV_ERR_INVALID_VALUE;
-  if (!workspace || ws_bytes < need) return HKV_ERR_WORKSPACE;
-  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0 || reinterpret_cast<uintptr_t>(q) % 16 != 0)
-    return HKV_ERR_ALIGNMENT;
-  int64_t blk_max = 1;
-  for (int b = 0; b < c->batch; ++b) blk_max = std::max(blk_max, cold_blocks(c->seq_len_host[b], h->T, h->S));
+  return guarded([&]() -> hkv_status {
+    hkv_status st = check_desc(h, c);
+    if (st != HKV_OK) return st;
+    if (!q || !out_idx) return HKV_ERR_NULL_POINTER;
+    if (n_q_heads < 1 || n_q_heads % h->H != 0) return HKV_ERR_INVALID_VALUE;
+    if (k < 1 || k > hkv::kMaxTopK) return HKV_ERR_INVALID_VALUE;
+    const int G = n_q_heads / h->H;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return HKV_ERR_UNSUPPORTED;
+    if (h->S != hkv::kBlockSize) return HKV_ERR_UNSUPPORTED;
+    size_t need = 0;
+    if (hkv_workspace_bytes(h, c, n_q_heads, k, &need) != HKV_OK) return HKV_ERR_INVALID_VALUE;
+    if (!workspace || ws_bytes < need) return HKV_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0 || reinterpret_cast<uintptr_t>(q) % 16 != 0)
+      return HKV_ERR_ALIGNMENT;
+    int64_t blk_max = 1;
+    for (int b = 0; b < c->batch; ++b) blk_max = std::max(blk_max, cold_blocks(c->seq_len_host[b], h->T, h->S));
 
-  hkv::TopkParams p;
-  p.c = view_of(h, c);
-  p.G = G;
-  p.q = static_cast<const _Float16*>(q);
-  p.prob = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(counters_bytes(c, h->H), 256));
-  // the score kernel holds at most 64 VGPRs per lane (D = 128, G <= 4), so 8 of its workgroups fit a
-  // CU: twice the decode's grid; its claim plans take 4 per CU (32768-token workload, measured:
-  // static splits 98.6 us, claims on 512 / 1024 / 2048 workgroups 98.5 / 91.3 / 92.7 us)
-  const SplitPlan sp = plan_splits(static_cast<int64_t>(c->batch) * h->H, blk_max, 1, 2 * kTargetWorkgroups,
-                                   kTopkClaimTargetWorkgroups);
-  p.nsplit = sp.nsplit;
-  p.units_per_split = sp.per_split;
-  p.wg_order = sp.wg_order;
-  p.work = sp.claim ? claim_counters(workspace, c, h->H) : nullptr;
-  p.k = k;
-  p.out_idx = out_idx;
-  LaunchCtx a = make_ctx(h, stream, HKV_KERNEL_TOPK_SCORE);
-  LaunchCtx b = make_ctx(h, stream, HKV_KERNEL_TOPK_SELECT);
-  return hip_status(hkv::launch_topk(p, a, b), "hkv_topk_select launch");
+    hkv::TopkParams p;
+    p.c = view_of(h, c);
+    p.G = G;
+    p.q = static_cast<const _Float16*>(q);
+    p.prob = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(counters_bytes(c, h->H), 256));
+    // the score kernel holds at most 64 VGPRs per lane (D = 128, G <= 4), so 8 of its workgroups fit a
+    // CU: twice the decode's grid; its claim plans take 4 per CU (32768-token workload, measured:
+    // static splits 98.6 us, claims on 512 / 1024 / 2048 workgroups 98.5 / 91.3 / 92.7 us)
+    const SplitPlan sp = plan_splits(static_cast<int64_t>(c->batch) * h->H, blk_max, 1, 2 * kTargetWorkgroups,
+                                     kTopkClaimTargetWorkgroups);
+    p.nsplit = sp.nsplit;
+    p.units_per_split = sp.per_split;
+    p.wg_order = sp.wg_order;
+    p.work = sp.claim ? claim_counters(workspace, c, h->H) : nullptr;
+    p.k = k;
+    p.out_idx = out_idx;
+    LaunchCtx a = make_ctx(h, stream, HKV_KERNEL_TOPK_SCORE);
+    LaunchCtx b = make_ctx(h, stream, HKV_KERNEL_TOPK_SELECT);
+    return hip_status(hkv::launch_topk(p, a, b), "hkv_topk_select launch");
+  });
+}
+
+hkv_status hkv_read_probe(const void* src, size_t bytes, int workgroups, int threads, uint32_t* sink,
+                          hipStream_t stream) {
+  if (!src || !sink) return HKV_ERR_NULL_POINTER;
+  if (workgroups < 1 || threads < 64 || threads > 1024 || threads % 64 != 0 || bytes % 16 != 0)
+    return HKV_ERR_INVALID_VALUE;
+  if (reinterpret_cast<uintptr_t>(src) % 16 != 0 || reinterpret_cast<uintptr_t>(sink) % 4 != 0)
+    return HKV_ERR_ALIGNMENT;
+  return hip_status(hkv::launch_read_probe(src, bytes, workgroups, threads, sink, LaunchCtx{stream, nullptr, nullptr}),
+                    "hkv_read_probe launch");
 }
 
 const char* hkv_last_error_detail(void) { return g_detail; }
@@ -537,6 +588,7 @@ const char* hkv_status_string(hkv_status st) {
     case HKV_ERR_WORKSPACE: return "workspace missing or too small";
     case HKV_ERR_HIP: return "HIP runtime error";
     case HKV_ERR_ALIGNMENT: return "misaligned buffer";
+    case HKV_ERR_OUT_OF_MEMORY: return "out of host memory";
   }
   return "unknown status";
 }
@@ -548,33 +600,35 @@ hkv_status hkv_timing_enable(hkv_handle h, int enable) {
 }
 
 hkv_status hkv_timing_read(hkv_handle h, int kind, double* total_ms, int64_t* count, int reset) {
-  if (!h || !total_ms || !count) return HKV_ERR_NULL_POINTER;
-  if (kind < 0 || kind >= HKV_KERNEL_KINDS) return HKV_ERR_INVALID_VALUE;
-  std::vector<hkv_ctx::Pending> keep;
-  keep.reserve(h->pending.size());
-  for (auto& p : h->pending) {
-    if (p.kind != kind) {
-      keep.push_back(p);
-      continue;
+  return guarded([&]() -> hkv_status {
+    if (!h || !total_ms || !count) return HKV_ERR_NULL_POINTER;
+    if (kind < 0 || kind >= HKV_KERNEL_KINDS) return HKV_ERR_INVALID_VALUE;
+    std::vector<hkv_ctx::Pending> keep;
+    keep.reserve(h->pending.size());
+    for (auto& p : h->pending) {
+      if (p.kind != kind) {
+        keep.push_back(p);
+        continue;
+      }
+      hipError_t e = hipEventSynchronize(p.stop);
+      if (e != hipSuccess) return hip_status(e, "hkv_timing_read sync");
+      float ms = 0.f;
+      e = hipEventElapsedTime(&ms, p.start, p.stop);
+      if (e != hipSuccess) return hip_status(e, "hkv_timing_read elapsed");
+      h->total_ms[kind] += ms;
+      h->count[kind] += 1;
+      h->free_events.push_back(p.start);
+      h->free_events.push_back(p.stop);
     }
-    hipError_t e = hipEventSynchronize(p.stop);
-    if (e != hipSuccess) return hip_status(e, "hkv_timing_read sync");
-    float ms = 0.f;
-    e = hipEventElapsedTime(&ms, p.start, p.stop);
-    if (e != hipSuccess) return hip_status(e, "hkv_timing_read elapsed");
-    h->total_ms[kind] += ms;
-    h->count[kind] += 1;
-    h->free_events.push_back(p.start);
-    h->free_events.push_back(p.stop);
-  }
-  h->pending.swap(keep);
-  *total_ms = h->total_ms[kind];
-  *count = h->count[kind];
-  if (reset) {
-    h->total_ms[kind] = 0.0;
-    h->count[kind] = 0;
-  }
-  return HKV_OK;
+    h->pending.swap(keep);
+    *total_ms = h->total_ms[kind];
+    *count = h->count[kind];
+    if (reset) {
+      h->total_ms[kind] = 0.0;
+      h->count[kind] = 0;
+    }
+    return HKV_OK;
+  });
 }
 
 }  // extern "C"

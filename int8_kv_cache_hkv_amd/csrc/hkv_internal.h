@@ -98,5 +98,7 @@ struct TopkParams {
 hipError_t launch_append(const AppendParams& p, const LaunchCtx& quant_ctx, const LaunchCtx& ring_ctx);
 hipError_t launch_decode(const DecodeParams& p, const LaunchCtx& ctx, const uint16_t* order = nullptr);
 hipError_t launch_topk(const TopkParams& p, const LaunchCtx& score_ctx, const LaunchCtx& sel_ctx);
+hipError_t launch_read_probe(const void* src, size_t bytes, int workgroups, int threads, uint32_t* sink,
+                             const LaunchCtx& ctx);
 
 }  // namespace hkv

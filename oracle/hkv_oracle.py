@@ -220,14 +220,6 @@ def _decode_over(q: np.ndarray, state: SequenceState, sel: Optional[np.ndarray],
 
 
 # --------------------------------------------------------------------------- top-K (HySparse-style)
-def cosine(a: np.ndarray, b: np.ndarray) -> float:
-    """a . b / (|a| |b|), defined as 0 when either norm is 0."""
-    na, nb = float(np.linalg.norm(a)), float(np.linalg.norm(b))
-    if na == 0.0 or nb == 0.0:
-        return 0.0
-    return float(a @ b) / (na * nb)
-
-
 def token_scores(q: np.ndarray, state: SequenceState) -> np.ndarray:
     """c [H, n_cold]: per kv-head, mean over its query heads of cos(q_hq, k_hat_t)."""
     q64 = np.asarray(q, dtype=np.float16).astype(np.float64)

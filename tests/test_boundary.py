@@ -11,7 +11,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 hkv = pytest.importorskip("int8_kv_cache_hkv_amd")
 
-INVALID, UNSUPPORTED, NULLP, CAPACITY, WORKSPACE, ALIGN = -1, -2, -3, -4, -5, -7
+INVALID, UNSUPPORTED, NULLP, CAPACITY, WORKSPACE, ALIGN, OOM = -1, -2, -3, -4, -5, -7, -8
 
 
 def declared_functions():
@@ -180,7 +180,75 @@ def test_decode_and_topk_host_errors():
         hkv.hkv_destroy(h)
 
 
+def test_sizes_array_form():
+    """hkv_sizes (six byte counts) agrees with hkv_cache_sizes field by field."""
+    h = hkv.hkv_create(8, 128)
+    try:
+        for batch, tokens, phys in ((8, 2048, 0), (2, 32, 0), (4, 131072, 10000), (64, 8300, 0)):
+            s = hkv.hkv_cache_sizes(h, batch, tokens, phys)
+            assert hkv.hkv_sizes(h, batch, tokens, phys) == (s.hot, s.tail, s.cold, s.scales, s.headers, s.seq_len)
+        out = (ctypes.c_size_t * 6)()
+        assert hkv._lib.hkv_sizes(h, 0, 10, 0, out) == INVALID
+        assert hkv._lib.hkv_sizes(h, 2, -1, 0, out) == INVALID
+        assert hkv._lib.hkv_sizes(h, 2, 10, 0, None) == NULLP
+        assert hkv._lib.hkv_sizes(None, 2, 10, 0, out) == NULLP
+    finally:
+        hkv.hkv_destroy(h)
+
+
+_OOM_CHILD = r"""
+import ctypes, resource, sys
+import numpy as np
+sys.path.insert(0, sys.argv[1])
+import int8_kv_cache_hkv_amd as hkv
+h = hkv.hkv_create(8, 128)
+batch = 50_000_000
+lens = np.ones(batch, dtype=np.int32)           # allocated before the limit is set
+base = 1 << 40
+desc = hkv.CacheDesc(batch, 4, 4, base, base + 4096, base + 8192, base + 12288, base + 16384, base + 20480,
+                     lens.ctypes.data)
+vm = [int(l.split()[1]) * 1024 for l in open("/proc/self/status") if l.startswith("VmSize:")][0]
+resource.setrlimit(resource.RLIMIT_AS, (vm + (64 << 20), resource.RLIM_INFINITY))
+q = 1 << 41
+st = hkv._lib.hkv_decode_attn(h, ctypes.byref(desc), q, 32, None, 0, q, None, q, 1 << 40, None)
+st2 = hkv._lib.hkv_append_decode(h, ctypes.byref(desc), q, q, q, 32, q, None, q, 1 << 40, None)
+print(st, st2)
+"""
+
+
+def test_host_allocation_failure_is_reported():
+    """A host allocation the library cannot make (launch planning for 50 M sequences under an
+    address-space limit) returns HKV_ERR_OUT_OF_MEMORY instead of throwing across the C ABI."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, "-c", _OOM_CHILD, ROOT], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert r.stdout.split()[-2:] == [str(OOM), str(OOM)], r.stdout
+
+
 def test_status_strings():
-    for st in (0, -1, -2, -3, -4, -5, -6, -7):
+    assert hkv.hkv_status_string(OOM) == "out of host memory"
+    for st in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert hkv.hkv_status_string(st)
     assert hkv.hkv_status_string(99) == "unknown status"
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU only" in r.stderr
+
+
+def test_bench_algorithmic_bytes_match_the_workload_table():
+    """Algorithmic bytes per decode call of the tiny, llama8b and 131072-token workloads: 2 n_cold H d
+    (int8 K and V) + 8 n_blk H (scales) + 16 n_blk (headers) + 4 n_hot H d (fp16 hot) + 4 Hq d (q, out)."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    assert b.decode_bytes(288, 2, 4, 64) == 83_072
+    assert 8 * b.decode_bytes(2048, 8, 32, 128) == 34_230_272
+    assert 4 * b.decode_bytes(131072, 8, 32, 128) == 1_074_724_864
+    assert 16 * (32768 - 32) * 8 * 128 == 536_346_624

@@ -11,6 +11,7 @@ import pytest
 import oracle.hkv_oracle as orc
 import workloads as wl
 from tests import gpu_helpers as gh
+from tests import oracle_jobs as oj
 
 pytestmark = pytest.mark.gpu
 
@@ -488,27 +489,35 @@ def test_batch_plan_orders(batch):
         gh.compare_lse(lse_f[b], l_ref, f"batch {batch} fused b={b}")
 
 
-# ------------------------------------------------------------------ long context, sampled
-def test_long_config_parity_sampled():
+# ------------------------------------------------------------------ long context, every sequence
+def test_long_config_parity():
+    """The 131072-token workload at full size: a plain decode at 131071 tokens, then the fused step
+    (append one token + decode, the launch plan the benchmark times) to 131072 tokens, then a plain
+    decode there; out and lse of all 4 sequences against the oracle after each, and every block's
+    codes, scales, headers and the hot ring of all 4 sequences bit-exact after the fused step."""
     w = wl.WORKLOADS["long"]
-    n = w.context
-    gh.log(f"long: B={w.batch} n={n}")
-    cache = gh.make_cache(w, n)
-    gh.fill(cache, w, [n] * w.batch, chunk=8192)
-    q = wl.queries(w)
-    out, lse = _decode(cache, q)
-    for b in (0, w.batch - 1):
-        st = _oracle_states(w, [n], [b])[0]
-        o_ref, l_ref = orc.decode(q[b], st)
-        gh.compare_out(out[b], o_ref, f"long seq {b}")
-        gh.compare_lse(lse[b], l_ref, f"long seq {b}")
-        # codes of a sample of blocks, bit-exact
-        hdr = cache.header_array()
-        for j in (0, 1, 1000, st.n_blocks - 2, st.n_blocks - 1):
-            phys = int(hdr[b, j, 0])
-            got = cache.cold_codes_of([phys])[0]
-            nv = int(st.n_valid[j])
-            assert np.array_equal(got[:, :, :nv], st.codes[j][:, :, :nv]), (b, j)
+    B = w.batch
+    n0 = w.context - 1
+    gh.log(f"long: B={B} n0={n0} -> {n0 + 1} (fused step)")
+    cache = gh.make_cache(w, w.context)
+    q0, q1 = wl.queries(w), wl.queries(w, step=1)
+    with oj.pool(B) as ex:
+        futs = [ex.submit(oj.decode_job, "long", b, [n0, n0 + 1], [q0[b], q1[b]], n0 + 1) for b in range(B)]
+        gh.fill(cache, w, [n0] * B, chunk=8192)
+        out0, lse0 = _decode(cache, q0)
+        out1, lse1 = _append_decode(cache, w, [n0] * B, q1)
+        out2, lse2 = _decode(cache, q1)
+        codes, scales = cache.cold_codes(), cache.scale_array()
+        for b, f in enumerate(futs):
+            (r0, r1), st = f.result()
+            gh.log(f"  long seq {b}: oracle done")
+            gh.compare_out(out0[b], r0[0], f"long seq {b} n={n0}")
+            gh.compare_lse(lse0[b], r0[1], f"long seq {b} n={n0}")
+            gh.compare_out(out1[b], r1[0], f"long seq {b} fused step")
+            gh.compare_lse(lse1[b], r1[1], f"long seq {b} fused step")
+            gh.compare_out(out2[b], r1[0], f"long seq {b} n={n0 + 1}")
+            gh.compare_lse(lse2[b], r1[1], f"long seq {b} n={n0 + 1}")
+            gh.check_state(cache, [st], seqs=[b], codes=codes, scales=scales)
 
 
 # ------------------------------------------------------------------ top-K and sparse decode
@@ -577,32 +586,34 @@ def test_topk_ties_prefer_lower_index(n, k):
     assert idx.cpu().numpy()[0].tolist() == [want] * H
 
 
-def test_topk_config_parity_sampled():
+def test_topk_config_parity():
+    """The 32768-token top-K workload at full size: the index sets of all 16 sequences x 8 kv-heads
+    and the sparse decode over each selection against the oracle; then a dense decode and a second
+    selection on the same workspace (the claim counters must be back at zero)."""
     w = wl.WORKLOADS["topk"]
     n = w.context
-    gh.log(f"topk: B={w.batch} n={n} K={w.k_sel}")
+    B = w.batch
+    gh.log(f"topk: B={B} n={n} K={w.k_sel}")
     cache = gh.make_cache(w, n)
-    gh.fill(cache, w, [n] * w.batch, chunk=8192)
+    gh.fill(cache, w, [n] * B, chunk=8192)
     q = wl.queries(w)
     qd = gh.upload(q)
     idx = cache.topk(qd, w.k_sel)
     out, lse = _decode(cache, q, sel=idx, k_sel=w.k_sel)
     got = idx.cpu().numpy()
-    for b in (0, 7, w.batch - 1):
-        st = _oracle_states(w, [n], [b])[0]
-        want, p, tau = orc.topk_select(q[b], st, w.k_sel)
-        for h in range(w.n_kv_heads):
-            gh.compare_topk(got[b, h], want[h], p[h], tau[h], st.n_cold, w.k_sel, f"topk b={b} h={h}")
-        o_ref, l_ref = orc.sparse_decode(q[b], st, got[b])
-        gh.compare_out(out[b], o_ref, f"sparse b={b}")
-        gh.compare_lse(lse[b], l_ref, f"sparse b={b}")
-    # the dense decode of this cache and the top-K score both claim blocks from the counters of the
-    # one workspace the cache keeps: a dense decode, then top-K again, must see them back at zero
     out_d, lse_d = _decode(cache, q)
     idx2 = cache.topk(qd, w.k_sel).cpu().numpy()
     assert np.array_equal(idx2, got), "top-K differs after a dense decode on the same workspace"
-    for b in (0, w.batch - 1):
-        st = _oracle_states(w, [n], [b])[0]
-        o_ref, l_ref = orc.decode(q[b], st)
-        gh.compare_out(out_d[b], o_ref, f"dense after top-K b={b}")
-        gh.compare_lse(lse_d[b], l_ref, f"dense after top-K b={b}")
+    with oj.pool(B) as ex:
+        futs = [ex.submit(oj.topk_job, "topk", b, q[b], w.k_sel, got[b]) for b in range(B)]
+        dense = [ex.submit(oj.decode_job, "topk", b, [n], [q[b]]) for b in (0, B - 1)]
+        for b, f in enumerate(futs):
+            want, p, tau, n_cold, o_ref, l_ref = f.result()
+            for h in range(w.n_kv_heads):
+                gh.compare_topk(got[b, h], want[h], p[h], tau[h], n_cold, w.k_sel, f"topk b={b} h={h}")
+            gh.compare_out(out[b], o_ref, f"sparse b={b}")
+            gh.compare_lse(lse[b], l_ref, f"sparse b={b}")
+        for b, f in zip((0, B - 1), dense):
+            ((o_ref, l_ref),), _ = f.result()
+            gh.compare_out(out_d[b], o_ref, f"dense after top-K b={b}")
+            gh.compare_lse(lse_d[b], l_ref, f"dense after top-K b={b}")

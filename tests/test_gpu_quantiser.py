@@ -1,0 +1,189 @@
+"""GPU: exhaustive parity of the INT8 quantiser against the fp64 oracle, through the C ABI.
+
+The block scale s = fl32(max|x| / 127) and the codes clamp(rint(fl32(x / s)), -127, 127) (Hybrid
+KV Cache page 2.1: INT8 cold blocks with a block-wise scale; symmetric absmax with round half to
+even) are compared bit for bit:
+
+* every one of the 31744 non-negative finite fp16 values is the maximum of some tile (64 tokens x
+  head_dim channels of one kv-head, K or V); besides the maximum, each tile holds the fp16 values
+  next to (k + 1/2) * s for every k in [0, 127), the inputs whose quotient x / s lies closest to a
+  rounding boundary, with random signs, and random fill;
+* for the maxima 65504, 127, 40.72, 3.1416, 1, 6.1e-5, 37 * 2^-24 and 64 random ones, every finite
+  fp16 x with |x| <= max is coded;
+* three coders: a bulk append (every block of a sequence in one call), 64-token appends (one
+  block per call, the single-pass append kernel) and the fused decode step's coder, which codes
+  one spilled token at a time into a block whose maximum grows (the whole block is re-coded under
+  each new scale) or stays (only the new row is coded).
+"""
+import numpy as np
+import pytest
+
+import oracle.hkv_oracle as orc
+from tests import gpu_helpers as gh
+
+pytestmark = pytest.mark.gpu
+
+S, T = 64, 32
+SWEEP_MAXIMA = [65504.0, 127.0, 40.72, 3.1416, 1.0, 6.1e-5, 37 * 2.0 ** -24]
+
+
+def all_maxima() -> np.ndarray:
+    """Every non-negative finite fp16 value (bit patterns 0x0000 .. 0x7bff), ascending."""
+    return np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16)
+
+
+def near_half_values(m: np.ndarray) -> np.ndarray:
+    """[len(m), 127, 3]: for each maximum m and k in [0, 127), the fp16 value nearest (k + 1/2) m / 127
+    and its two fp16 neighbours; entries outside (0, m] are replaced by m."""
+    m64 = m.astype(np.float64)[:, None]
+    t = (np.arange(127, dtype=np.float64)[None, :] + 0.5) * m64 / 127.0
+    f = t.astype(np.float16)
+    c = np.stack([np.nextafter(f, np.float16(-np.inf)), f, np.nextafter(f, np.float16(np.inf))], axis=-1)
+    ok = (c > 0) & (c.astype(np.float64) <= m64[:, :, None]) & np.isfinite(c)
+    return np.where(ok, c, np.broadcast_to(m[:, None, None], c.shape)).astype(np.float16)
+
+
+def maxima_tiles(m: np.ndarray, n: int, rng) -> np.ndarray:
+    """[len(m), n] fp16 tiles whose largest magnitude is exactly m (row i: maximum m[i] at a random
+    position, the near-boundary values of its scale with random signs, uniform fill in [-m, m])."""
+    out = np.empty((len(m), n), dtype=np.float16)
+    step = 2048
+    for a in range(0, len(m), step):
+        mm = m[a:a + step]
+        k = len(mm)
+        fill = (rng.uniform(-1.0, 1.0, (k, n)) * mm.astype(np.float64)[:, None]).astype(np.float16)
+        nh = near_half_values(mm).reshape(k, -1)
+        nh = nh * np.where(rng.random(nh.shape) < 0.5, -1, 1).astype(np.float16)
+        w = min(nh.shape[1], n - 1)
+        fill[:, 1:1 + w] = nh[:, :w]
+        fill[:, 0] = mm * np.where(rng.random(k) < 0.5, -1, 1).astype(np.float16)
+        out[a:a + step] = rng.permuted(fill, axis=1)
+    return out
+
+
+def sweep_tiles(m: float, n: int) -> np.ndarray:
+    """Tiles holding every finite fp16 x with |x| <= m (both signs), each with m itself first."""
+    mb = int(np.array([m], dtype=np.float16).view(np.uint16)[0])
+    pos = np.arange(0, mb + 1, dtype=np.uint16)
+    vals = np.concatenate([pos, pos | np.uint16(0x8000)]).view(np.float16)
+    per = n - 1
+    cnt = -(-len(vals) // per)
+    out = np.zeros((cnt, n), dtype=np.float16)
+    out[:, 0] = np.float16(m)
+    flat = out[:, 1:].reshape(-1)
+    flat[:len(vals)] = vals
+    out[:, 1:] = flat.reshape(cnt, per)
+    return out
+
+
+def build_tiles(n: int, maxima: np.ndarray, sweep: list, rng):
+    tiles = [maxima_tiles(maxima, n, rng)]
+    for m in sweep:
+        tiles.append(sweep_tiles(m, n))
+    return np.concatenate(tiles)
+
+
+def histories(tiles: np.ndarray, B: int, H: int, D: int, rng):
+    """Place the tiles at seeded random (sequence, block, kv-head, K|V) slots of B sequences (random
+    N(0,1) tiles fill the rest) and return the K and V token histories [B, J*S + T, H, D], ending
+    with T random hot tokens."""
+    per_seq = 2 * H
+    J = -(-len(tiles) // (B * per_seq))
+    slots = B * J * per_seq
+    grid = rng.standard_normal((slots, S * D)).astype(np.float16)
+    grid[rng.permutation(slots)[:len(tiles)]] = tiles
+    g = grid.reshape(B, J, H, 2, S, D)
+    hot = rng.standard_normal((B, T, H, D, 2)).astype(np.float16)
+    k = np.concatenate([g[:, :, :, 0].transpose(0, 1, 3, 2, 4).reshape(B, J * S, H, D), hot[..., 0]], axis=1)
+    v = np.concatenate([g[:, :, :, 1].transpose(0, 1, 3, 2, 4).reshape(B, J * S, H, D), hot[..., 1]], axis=1)
+    return np.ascontiguousarray(k), np.ascontiguousarray(v)
+
+
+def sweep_list(rng, n_random=64):
+    rnd = rng.integers(1, 0x7C00, size=n_random).astype(np.uint16).view(np.float16).astype(np.float64)
+    return [float(np.float16(x)) for x in SWEEP_MAXIMA] + [float(x) for x in rnd]
+
+
+@pytest.mark.parametrize("D,H,stride", [(128, 8, 1), (64, 2, 5)])
+def test_quantiser_exhaustive_append(D, H, stride):
+    """Every fp16 maximum (every `stride`-th one for head_dim 64) and the full sweeps, coded by a bulk
+    append and by one-block appends: codes, scales, headers and the hot ring bit-exact."""
+    import int8_kv_cache_hkv_amd as hkv
+    torch = gh.torch_mod()
+    rng = np.random.default_rng(20261203 + D)
+    maxima = all_maxima()[::stride]
+    tiles = build_tiles(S * D, maxima, sweep_list(rng), rng)
+    B = 64
+    k, v = histories(tiles, B, H, D, rng)
+    n = k.shape[1]
+    gh.log(f"quantiser D={D} H={H}: {len(tiles)} designed tiles, {B} sequences of {n} tokens")
+    states = [orc.build_state(k[b], v[b], T, S) for b in range(B)]
+    bulk = hkv.HybridKVCache(H, D, B, n)
+    bulk.append(gh.upload(k), gh.upload(v))
+    torch.cuda.synchronize()
+    gh.check_state(bulk, states)
+    bulk.close()
+    gh.log("  bulk append: bit-exact")
+    blocks = hkv.HybridKVCache(H, D, B, n)
+    blocks.append(gh.upload(k[:, :T]), gh.upload(v[:, :T]))
+    for p in range(T, n, S):  # each call spills exactly one whole block
+        blocks.append(gh.upload(k[:, p:p + S]), gh.upload(v[:, p:p + S]))
+    torch.cuda.synchronize()
+    gh.check_state(blocks, states)
+    blocks.close()
+    gh.log("  one-block appends: bit-exact")
+
+
+def growth_rows(maxima: np.ndarray, n_tiles: int, D: int, rng) -> np.ndarray:
+    """[n_tiles, S, D] rows of one block per tile: tile t's maxima are maxima[t::n_tiles] (ascending);
+    even rows raise the block maximum to the next of them (row = the maximum plus values next to the
+    rounding boundaries of its scale), odd rows keep it (uniform values below it; every fourth odd
+    row holds the current maximum itself)."""
+    rows = np.zeros((n_tiles, S, D), dtype=np.float16)
+    for t in range(n_tiles):
+        ms = maxima[t::n_tiles]
+        cur = np.float16(0)
+        g = 0
+        for r in range(S):
+            if r % 2 == 0 and g < len(ms):
+                cur = ms[g]
+                g += 1
+                row = maxima_tiles(np.array([cur]), D, rng)[0]
+            else:
+                row = (rng.uniform(-1.0, 1.0, D) * float(cur)).astype(np.float16)
+                if r % 8 == 1:
+                    row[rng.integers(D)] = cur
+            rows[t, r] = row
+    return rows
+
+
+@pytest.mark.parametrize("D,H,G,stride", [(128, 8, 4, 1), (64, 2, 2, 4)])
+def test_quantiser_exhaustive_fused_step(D, H, G, stride):
+    """The fused decode step's coder: 64 fused steps spill the 64 designed rows of block 0 one at a
+    time (31 growing maxima per tile cover every fp16 maximum for head_dim 128); after every step
+    the block's codes and scales (and the rest of the cache) are bit-exact against the oracle."""
+    import int8_kv_cache_hkv_amd as hkv
+    torch = gh.torch_mod()
+    rng = np.random.default_rng(777 + D)
+    B = 64
+    n_tiles = B * H * 2
+    rows = growth_rows(all_maxima()[::stride], n_tiles, D, rng).reshape(B, H, 2, S, D)
+    k = np.concatenate([rows[:, :, 0].transpose(0, 2, 1, 3),
+                        rng.standard_normal((B, T, H, D)).astype(np.float16)], axis=1)
+    v = np.concatenate([rows[:, :, 1].transpose(0, 2, 1, 3),
+                        rng.standard_normal((B, T, H, D)).astype(np.float16)], axis=1)
+    k, v = np.ascontiguousarray(k), np.ascontiguousarray(v)
+    gh.log(f"fused coder D={D} H={H}: {n_tiles} tiles, 64 steps")
+    cache = hkv.HybridKVCache(H, D, B, S + T + 8)
+    cache.append(gh.upload(k[:, :T]), gh.upload(v[:, :T]))
+    q = gh.upload(rng.standard_normal((B, H * G, D)).astype(np.float16))
+    out = torch.empty_like(q)
+    for i in range(S):
+        n0 = T + i
+        cache.append_decode(gh.upload(k[:, n0]), gh.upload(v[:, n0]), q, out=out)
+        torch.cuda.synchronize()
+        states = [orc.build_state(k[b, :n0 + 1], v[b, :n0 + 1], T, S) for b in range(B)]
+        gh.check_state(cache, states)
+    o_ref = np.stack([orc.decode(q[b].cpu().numpy(), states[b])[0] for b in range(B)])
+    gh.compare_out(out.cpu().numpy(), o_ref, f"fused coder D={D} last step")
+    cache.close()
