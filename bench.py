@@ -128,29 +128,46 @@ def roofline(kernel, nbytes, ms, leg):
 
 
 # ----------------------------------------------------------------------------- timing
-def timed_trials(torch, step, first, steps, trials):
-    """`trials` trials of `steps` calls step(i) (i counts on from `first`).  Each trial is bracketed by
-    torch.cuda.synchronize() on both sides (host clock) and by an event pair recorded on the current
-    stream, the stream every launch goes to.  Returns the median host and device milliseconds per
-    step, every trial's figures and the values step() returned."""
+def timed_trials(torch, step, first, steps, trials, preroll=4):
+    """Host-clock trials: `trials` trials of exactly `steps` calls step(i) (i counts on from
+    `first`), each bracketed by torch.cuda.synchronize() on both sides.  Then as many device-timed
+    trials: `preroll` untimed calls are queued first so that the GPU is busy when the first timed
+    launch is issued, and an event pair recorded on the current stream (the stream every launch
+    goes to) brackets the `steps` timed calls, so the device interval is back-to-back launches only.
+    Returns the medians (host ms per step, device ms per launch-step), every trial's figures and the
+    values step() returned in the host-clock trials."""
     host, dev, rets = [], [], []
     i = first
+    for _ in range(trials):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            rets.append(step(i))
+            i += 1
+        torch.cuda.synchronize()
+        host.append((time.perf_counter() - t0) * 1e3 / steps)
     for _ in range(trials):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
+        for _ in range(preroll):
+            step(i)
+            i += 1
         e0.record()
         for _ in range(steps):
-            rets.append(step(i))
+            step(i)
             i += 1
         e1.record()
         torch.cuda.synchronize()
-        host.append((time.perf_counter() - t0) * 1e3 / steps)
         dev.append(e0.elapsed_time(e1) / steps)
     return {"ms_per_step": statistics.median(host), "device_ms_per_step": statistics.median(dev),
             "trials_ms": [round(x, 6) for x in host], "trials_device_ms": [round(x, 6) for x in dev],
             "next": i, "rets": rets}
+
+
+def timed_calls(trials, steps, preroll=4):
+    """Calls of step() that timed_trials makes."""
+    return trials * (2 * steps + preroll)
 
 
 def out_close(got, want, what):
@@ -184,7 +201,7 @@ def decode_step_leg(hkv, torch, w, n0, steps, warmup, trials, R, label, fused=Tr
     step (fused) or hkv_append then hkv_decode_attn.  Returns timing, bytes and the self-check."""
     import workloads as wl
     B, H, Hq, d = w.batch, w.n_kv_heads, w.n_q_heads, w.head_dim
-    total = warmup + trials * steps
+    total = warmup + timed_calls(trials, steps)
     uses = -(-total // R) + 1
     cap = n0 + uses + 1
     log(f"{label}: {R} instances of B={B} n0={n0} (cap {cap}), generating inputs")
@@ -398,7 +415,7 @@ def leg_ragged(hkv, torch, args, steps=64, R=4, warmup=8):
     B, H, Hq, d = w.batch, w.n_kv_heads, w.n_q_heads, w.head_dim
     lens0 = [int(x) for x in wl.lengths(w)]
     trials = args.trials
-    per_inst = -(-(warmup + trials * steps) // R) + 2
+    per_inst = -(-(warmup + timed_calls(trials, steps)) // R) + 2
     cap = max(lens0) + per_inst + 1
     mb = -(-(cap - w.hot_tokens) // w.block_size)
     perm = wl.block_permutation(w, B * mb).reshape(B, mb)
