@@ -179,6 +179,9 @@ hkv_status hkv_header_table_bytes(int hot_tokens, int block_size, int64_t total_
  * first bytes hold per-(sequence, kv-head) and per-sequence arrival counters
  * and per-(sequence, kv-head) block-claim counters, which every call leaves at
  * zero again.  Calls that share a workspace must be ordered on one stream.
+ * The counters' extent depends on the cache's batch and kv-head count, and
+ * the partials follow them: a workspace that served a cache of another batch
+ * or kv-head count must be zero-filled again before it serves this one.
  * HKV_ERR_INVALID_VALUE if n_q_heads is not a positive multiple of
  * n_kv_heads or k_sel is outside [0, 512]. */
 hkv_status hkv_workspace_bytes(hkv_handle h, const hkv_cache_desc* c, int n_q_heads, int k_sel, size_t* bytes);
@@ -233,6 +236,28 @@ hkv_status hkv_append(hkv_handle h, const hkv_cache_desc* c, const void* k_new, 
 hkv_status hkv_decode_attn(hkv_handle h, const hkv_cache_desc* c, const void* q, int n_q_heads,
                            const int32_t* sel_idx, int k_sel, void* out, float* lse, void* workspace,
                            size_t ws_bytes, hipStream_t stream);
+
+/* hkv_decode_attn without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops
+ * and harnesses that forbid hipMalloc.  Arguments, results and errors are
+ * those of hkv_decode_attn (dense when sel_idx is NULL, sparse otherwise); the
+ * call allocates nothing, on the host or the device.
+ * Its scratch (arrival and claim counters, split partials) is one fixed
+ * 32 MiB device array of the library, one copy per GPU, held until the
+ * process ends.  The first call on a device takes the array's address on that
+ * device and clears it with a kernel on `stream` (and waits for it unless the
+ * stream is being captured); every call leaves the counters at zero again.
+ * Every call on one GPU shares that GPU's array: calls that may overlap on one
+ * GPU (different streams without ordering, several host threads) race and
+ * must be serialised by the caller.
+ *   HKV_ERR_WORKSPACE: the call would need more scratch than the array holds:
+ *     counters are kept in its first 4 MiB (about 16000 (sequence, kv-head)
+ *     pairs) and the split partials in the other 28 MiB (the hkv_workspace_bytes
+ *     of the same arguments, less the counters, must fit); use hkv_decode_attn
+ *     with a workspace instead.
+ *   HKV_ERR_HIP: the scratch set-up or the launch failed. */
+hkv_status hkv_decode_attn_noalloc(hkv_handle h, const hkv_cache_desc* c, const void* q, int n_q_heads,
+                                   const int32_t* sel_idx, int k_sel, void* out, float* lse, hipStream_t stream);
 
 /* One decode step in one launch: hkv_append of exactly one new token per
  * sequence followed by the dense hkv_decode_attn of q against the updated

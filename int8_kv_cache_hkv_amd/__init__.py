@@ -28,7 +28,7 @@ STATUS_NAMES = {0: "HKV_OK", -1: "HKV_ERR_INVALID_VALUE", -2: "HKV_ERR_UNSUPPORT
 KERNELS = {"append": 0, "append_ring": 1, "decode": 2, "decode_sparse": 3, "topk_score": 4, "topk_select": 5,
            "append_decode": 6}
 EXPORTS = ["hkv_create", "hkv_destroy", "hkv_cache_sizes", "hkv_sizes", "hkv_header_table_bytes", "hkv_workspace_bytes",
-           "hkv_append", "hkv_decode_attn", "hkv_append_decode", "hkv_topk_select", "hkv_status_string",
+           "hkv_append", "hkv_decode_attn", "hkv_decode_attn_noalloc", "hkv_append_decode", "hkv_topk_select", "hkv_status_string",
            "hkv_timing_enable",
            "hkv_timing_read", "hkv_last_error_detail", "hkv_read_probe"]
 
@@ -76,6 +76,7 @@ def _load() -> ctypes.CDLL:
         "hkv_workspace_bytes": [vp, ctypes.POINTER(CacheDesc), i32, i32, ctypes.POINTER(sz)],
         "hkv_append": [vp, ctypes.POINTER(CacheDesc), vp, vp, vp, i32, vp],
         "hkv_decode_attn": [vp, ctypes.POINTER(CacheDesc), vp, i32, vp, i32, vp, vp, vp, sz, vp],
+        "hkv_decode_attn_noalloc": [vp, ctypes.POINTER(CacheDesc), vp, i32, vp, i32, vp, vp, vp],
         "hkv_append_decode": [vp, ctypes.POINTER(CacheDesc), vp, vp, vp, i32, vp, vp, vp, sz, vp],
         "hkv_topk_select": [vp, ctypes.POINTER(CacheDesc), vp, i32, i32, vp, vp, sz, vp],
         "hkv_timing_enable": [vp, i32],
@@ -182,6 +183,13 @@ def hkv_decode_attn(handle: int, desc: CacheDesc, q, out, workspace, lse=None, s
                                 int(k_sel), _ptr(out), _ptr(lse), _ptr(workspace),
                                 int(workspace.numel() * workspace.element_size()), _stream(stream)),
            "hkv_decode_attn")
+
+
+def hkv_decode_attn_noalloc(handle: int, desc: CacheDesc, q, out, lse=None, sel_idx=None, k_sel: int = 0,
+                            stream=None) -> None:
+    _check(_lib.hkv_decode_attn_noalloc(handle, ctypes.byref(desc), _ptr(q), int(q.shape[1]), _ptr(sel_idx),
+                                        int(k_sel), _ptr(out), _ptr(lse), _stream(stream)),
+           "hkv_decode_attn_noalloc")
 
 
 def hkv_append_decode(handle: int, desc: CacheDesc, k_new, v_new, q, out, workspace, lse=None, stream=None) -> None:

@@ -239,6 +239,77 @@ hkv_status hip_status(hipError_t e, const char* where) {
   return HKV_ERR_HIP;
 }
 
+// hkv_decode_attn and hkv_decode_attn_noalloc.  With `scratch` the workspace is the library's fixed
+// device array on the current device (set up after every validation, before the launch) instead of
+// the caller's buffer.
+hkv_status decode_impl(hkv_ctx* h, const hkv_cache_desc* c, const void* q, int n_q_heads, const int32_t* sel_idx,
+                       int k_sel, void* out, float* lse, void* workspace, size_t ws_bytes, hipStream_t stream,
+                       bool scratch) {
+  hkv_status st = check_desc(h, c);
+  if (st != HKV_OK) return st;
+  if (!q || !out) return HKV_ERR_NULL_POINTER;
+  if (n_q_heads < 1 || n_q_heads % h->H != 0) return HKV_ERR_INVALID_VALUE;
+  const int G = n_q_heads / h->H;
+  if (sel_idx && (k_sel < 1 || k_sel > hkv::kMaxTopK)) return HKV_ERR_INVALID_VALUE;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return HKV_ERR_UNSUPPORTED;
+  int64_t units_max = 1;
+  std::vector<int64_t> units(c->batch);
+  for (int b = 0; b < c->batch; ++b) {
+    const int n = c->seq_len_host[b];
+    if (n == 0) return HKV_ERR_INVALID_VALUE;
+    const int64_t nblk = cold_blocks(n, h->T, h->S);
+    units[b] = nblk;
+    if (!sel_idx) units_max = std::max(units_max, nblk);
+  }
+  size_t need = 0;
+  if (hkv_workspace_bytes(h, c, n_q_heads, sel_idx ? k_sel : 0, &need) != HKV_OK) return HKV_ERR_INVALID_VALUE;
+  // workspace layout: counters first, then the partials (for the fixed scratch: at a fixed offset)
+  const size_t ctr_bytes = align_up(counters_bytes(c, h->H), 256);
+  if (scratch) {
+    if (ctr_bytes > hkv::kScratchCounterBytes ||
+        align_up(partials_bytes(h, c, G, sel_idx ? k_sel : 0), 256) > hkv::kScratchBytes - hkv::kScratchCounterBytes)
+      return HKV_ERR_WORKSPACE;
+  } else if (!workspace || ws_bytes < need) {
+    return HKV_ERR_WORKSPACE;
+  }
+  if ((!scratch && reinterpret_cast<uintptr_t>(workspace) % 16 != 0) || reinterpret_cast<uintptr_t>(q) % 16 != 0)
+    return HKV_ERR_ALIGNMENT;
+  uint16_t order[hkv::kOrderTableMax];
+  if (h->timing) {  // the call's last host allocation, before its first HIP call
+    h->pending.reserve(h->pending.size() + 1);
+    h->free_events.reserve(h->free_events.size() + 2);
+  }
+  if (scratch) {
+    const hipError_t e = hkv::scratch_for_device(stream, &workspace);
+    if (e != hipSuccess) return hip_status(e, "hkv_decode_attn_noalloc scratch set-up");
+  }
+
+  hkv::DecodeParams p;
+  p.c = view_of(h, c);
+  p.G = G;
+  p.q = static_cast<const _Float16*>(q);
+  p.sel = sel_idx;
+  p.k_sel = sel_idx ? k_sel : 0;
+  p.counters = static_cast<unsigned*>(workspace);
+  p.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + (scratch ? hkv::kScratchCounterBytes : ctr_bytes));
+  const SplitPlan sp = sel_idx ? plan_sparse(k_sel) : plan_splits(static_cast<int64_t>(c->batch) * h->H, units_max);
+  p.nsplit = sp.nsplit;
+  p.nparts = sp.nsplit + 1;
+  p.units_per_split = sp.per_split;
+  p.wg_order = sp.wg_order;
+  p.work = (!sel_idx && sp.claim) ? claim_counters(workspace, c, h->H) : nullptr;
+  const bool ordered = !sel_idx && sp.batch && order_by_work(p, units, sp.per_split, order);
+  if (ordered) p.wg_order = hkv::kOrderTable;
+  p.qscale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(h->D)));
+  p.out = static_cast<_Float16*>(out);
+  p.lse = lse;
+  p.k_new = p.v_new = nullptr;
+  p.seq_counters = nullptr;
+  LaunchCtx a = make_ctx(h, stream, sel_idx ? HKV_KERNEL_DECODE_SPARSE : HKV_KERNEL_DECODE);
+  return hip_status(hkv::launch_decode(p, a, ordered ? order : nullptr),
+                    scratch ? "hkv_decode_attn_noalloc launch" : "hkv_decode_attn launch");
+}
+
 // Runs an entry point's body; a failed host allocation (std::bad_alloc, or a
 // length error from a huge count) becomes HKV_ERR_OUT_OF_MEMORY, so no C++
 // exception crosses the C ABI.  Every body validates and allocates before its
@@ -415,52 +486,14 @@ hkv_status hkv_decode_attn(hkv_handle h, const hkv_cache_desc* c, const void* q,
                            const int32_t* sel_idx, int k_sel, void* out, float* lse, void* workspace,
                            size_t ws_bytes, hipStream_t stream) {
   return guarded([&]() -> hkv_status {
-    hkv_status st = check_desc(h, c);
-    if (st != HKV_OK) return st;
-    if (!q || !out) return HKV_ERR_NULL_POINTER;
-    if (n_q_heads < 1 || n_q_heads % h->H != 0) return HKV_ERR_INVALID_VALUE;
-    const int G = n_q_heads / h->H;
-    if (sel_idx && (k_sel < 1 || k_sel > hkv::kMaxTopK)) return HKV_ERR_INVALID_VALUE;
-    if (G != 1 && G != 2 && G != 4 && G != 8) return HKV_ERR_UNSUPPORTED;
-    int64_t units_max = 1;
-    std::vector<int64_t> units(c->batch);
-    for (int b = 0; b < c->batch; ++b) {
-      const int n = c->seq_len_host[b];
-      if (n == 0) return HKV_ERR_INVALID_VALUE;
-      const int64_t nblk = cold_blocks(n, h->T, h->S);
-      units[b] = nblk;
-      if (!sel_idx) units_max = std::max(units_max, nblk);
-    }
-    size_t need = 0;
-    if (hkv_workspace_bytes(h, c, n_q_heads, sel_idx ? k_sel : 0, &need) != HKV_OK) return HKV_ERR_INVALID_VALUE;
-    if (!workspace || ws_bytes < need) return HKV_ERR_WORKSPACE;
-    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0 || reinterpret_cast<uintptr_t>(q) % 16 != 0)
-      return HKV_ERR_ALIGNMENT;
+    return decode_impl(h, c, q, n_q_heads, sel_idx, k_sel, out, lse, workspace, ws_bytes, stream, false);
+  });
+}
 
-    hkv::DecodeParams p;
-    p.c = view_of(h, c);
-    p.G = G;
-    p.q = static_cast<const _Float16*>(q);
-    p.sel = sel_idx;
-    p.k_sel = sel_idx ? k_sel : 0;
-    p.counters = static_cast<unsigned*>(workspace);
-    p.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(counters_bytes(c, h->H), 256));
-    const SplitPlan sp = sel_idx ? plan_sparse(k_sel) : plan_splits(static_cast<int64_t>(c->batch) * h->H, units_max);
-    p.nsplit = sp.nsplit;
-    p.nparts = sp.nsplit + 1;
-    p.units_per_split = sp.per_split;
-    p.wg_order = sp.wg_order;
-    p.work = (!sel_idx && sp.claim) ? claim_counters(workspace, c, h->H) : nullptr;
-    uint16_t order[hkv::kOrderTableMax];
-    const bool ordered = !sel_idx && sp.batch && order_by_work(p, units, sp.per_split, order);
-    if (ordered) p.wg_order = hkv::kOrderTable;
-    p.qscale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(h->D)));
-    p.out = static_cast<_Float16*>(out);
-    p.lse = lse;
-    p.k_new = p.v_new = nullptr;
-    p.seq_counters = nullptr;
-    LaunchCtx a = make_ctx(h, stream, sel_idx ? HKV_KERNEL_DECODE_SPARSE : HKV_KERNEL_DECODE);
-    return hip_status(hkv::launch_decode(p, a, ordered ? order : nullptr), "hkv_decode_attn launch");
+hkv_status hkv_decode_attn_noalloc(hkv_handle h, const hkv_cache_desc* c, const void* q, int n_q_heads,
+                                   const int32_t* sel_idx, int k_sel, void* out, float* lse, hipStream_t stream) {
+  return guarded([&]() -> hkv_status {
+    return decode_impl(h, c, q, n_q_heads, sel_idx, k_sel, out, lse, nullptr, 0, stream, true);
   });
 }
 

@@ -21,6 +21,11 @@ constexpr int kOrderTableMax = 512;  // (sequence, part) groups a table order ca
 constexpr int kClaimUnits = 16;     // plans with splits of at least this many units claim them dynamically
 constexpr int kClaimStride = 64;    // claim counters 256 bytes apart: one cache line each
 constexpr int kMaxSplits = 128;     // cold splits per (sequence, kv-head) at most
+// Fixed device scratch of hkv_decode_attn_noalloc, per GPU: the counters of every call live in the
+// first kScratchCounterBytes, the split partials after them, so the partials of one call never land
+// on the counters of another (every call leaves all of its counters at zero).
+constexpr size_t kScratchBytes = size_t(32) << 20;
+constexpr size_t kScratchCounterBytes = size_t(4) << 20;
 
 // Per-launch timing: when start/stop are non-null the dispatch records them.
 struct LaunchCtx {
@@ -98,6 +103,9 @@ struct TopkParams {
 hipError_t launch_append(const AppendParams& p, const LaunchCtx& quant_ctx, const LaunchCtx& ring_ctx);
 hipError_t launch_decode(const DecodeParams& p, const LaunchCtx& ctx, const uint16_t* order = nullptr);
 hipError_t launch_topk(const TopkParams& p, const LaunchCtx& score_ctx, const LaunchCtx& sel_ctx);
+// Device address of the fixed scratch array on the current device (set up on first use: address
+// taken with hipGetSymbolAddress, array cleared on `stream`).
+hipError_t scratch_for_device(hipStream_t stream, void** out);
 hipError_t launch_read_probe(const void* src, size_t bytes, int workgroups, int threads, uint32_t* sink,
                              const LaunchCtx& ctx);
 
