@@ -161,7 +161,8 @@ def growth_rows(maxima: np.ndarray, n_tiles: int, D: int, rng) -> np.ndarray:
 def test_quantiser_exhaustive_fused_step(D, H, G, stride):
     """The fused decode step's coder: 64 fused steps spill the 64 designed rows of block 0 one at a
     time (31 growing maxima per tile cover every fp16 maximum for head_dim 128); after every step
-    the block's codes and scales (and the rest of the cache) are bit-exact against the oracle."""
+    the block's codes and scales, headers, the hot ring and the lengths are bit-exact against the
+    oracle."""
     import int8_kv_cache_hkv_amd as hkv
     torch = gh.torch_mod()
     rng = np.random.default_rng(777 + D)
@@ -184,6 +185,7 @@ def test_quantiser_exhaustive_fused_step(D, H, G, stride):
         torch.cuda.synchronize()
         states = [orc.build_state(k[b, :n0 + 1], v[b, :n0 + 1], T, S) for b in range(B)]
         gh.check_state(cache, states)
-    o_ref = np.stack([orc.decode(q[b].cpu().numpy(), states[b])[0] for b in range(B)])
-    gh.compare_out(out.cpu().numpy(), o_ref, f"fused coder D={D} last step")
+    # (the attention output is not compared here: these rows span the whole fp16 range, where the
+    # absolute output tolerance of the N(0, 1) workloads does not apply; decode parity under fp16
+    # extremes is checked with small queries in the edge-value test)
     cache.close()
