@@ -48,6 +48,13 @@ What is computed (readings where the pages are silent are marked READING):
    tokens.
 8. Header table sizing (Hybrid KV Cache page 5.4): one 16-byte header per
    cold block, blocks = ceil(cold tokens / block_size).
+9. Cold-zone width (Hybrid KV Cache page 3.1: quantization_bits is 4 or 8,
+   INT4 for L2 cold blocks; 5.2: quantization_bits 0 turns quantisation off
+   and the cold zone stays FP16).  A b-bit code is the same symmetric absmax
+   code with the largest magnitude L = 2^(b-1) - 1 (127 for INT8, 7 for INT4):
+   s = fl32(m / L), q = clip(rint(fl32(x / s)), -L, L) (READING: the pages
+   define neither code).  With 0 bits the cold tokens keep their fp16 values
+   and the state records a scale of 1 for every (block, kv-head, K|V).
 """
 from __future__ import annotations
 
@@ -61,12 +68,23 @@ HEADER_BYTES = 16  # Hybrid KV Cache page 3.2: each block_header element is 16 b
 
 
 # --------------------------------------------------------------------------- quantisation
-def block_scale(x_valid: np.ndarray) -> np.float32:
-    """s = fl32(max|x| / 127) over every element of one (block, kv-head, K|V) tile.
+QUANT_BITS = (8, 4, 0)   # Hybrid KV Cache page 3.1 (4 or 8) and 5.2 (0 = FP16 cold zone)
 
-    Hybrid KV Cache page 2.1 (INT8 with a block-wise scale); formula is the
-    symmetric absmax reading.
+
+def code_limit(bits: int = 8) -> int:
+    """Largest code magnitude of the symmetric b-bit code: 2^(b-1) - 1 (127 at 8 bits, 7 at 4)."""
+    if bits not in (8, 4):
+        raise ValueError("only 8- and 4-bit cold blocks are quantised")
+    return (1 << (bits - 1)) - 1
+
+
+def block_scale(x_valid: np.ndarray, bits: int = 8) -> np.float32:
+    """s = fl32(max|x| / L) over every element of one (block, kv-head, K|V) tile, L = code_limit(bits).
+
+    Hybrid KV Cache page 2.1 (INT8 with a block-wise scale) and 3.1 (4 or 8
+    bits); the formula is the symmetric absmax reading.
     """
+    lim = code_limit(bits)
     x = np.asarray(x_valid)
     if x.size == 0:
         return np.float32(0.0)
@@ -74,21 +92,22 @@ def block_scale(x_valid: np.ndarray) -> np.float32:
     if not np.all(np.isfinite(xd)):
         raise ValueError("cache inputs must be finite")
     m = float(np.max(np.abs(xd)))
-    return np.float32(m / 127.0)
+    return np.float32(m / float(lim))
 
 
-def quantize_codes(x_valid: np.ndarray, s: np.float32) -> np.ndarray:
-    """int8 codes clip(rint(fl32(x / s)), -127, 127); zeros when s == 0."""
+def quantize_codes(x_valid: np.ndarray, s: np.float32, bits: int = 8) -> np.ndarray:
+    """Codes clip(rint(fl32(x / s)), -L, L) as int8 values (L = code_limit(bits)); zeros when s == 0."""
+    lim = code_limit(bits)
     x = np.asarray(x_valid)
     if float(s) == 0.0:
         return np.zeros(x.shape, dtype=np.int8)
     quot = (x.astype(np.float64) / np.float64(s)).astype(np.float32)  # correctly rounded fp32 quotient
     q = np.rint(quot.astype(np.float64))                               # round half to even
-    return np.clip(q, -127, 127).astype(np.int8)
+    return np.clip(q, -lim, lim).astype(np.int8)
 
 
 def dequantize(codes: np.ndarray, s: np.float32) -> np.ndarray:
-    """x_hat = code * s in fp64 (exact)."""
+    """x_hat = code * s in fp64 (exact; an FP16 cold zone stores its values with s = 1)."""
     return codes.astype(np.float64) * np.float64(s)
 
 
@@ -101,9 +120,11 @@ class SequenceState:
     n_tokens: int
     hot_k: np.ndarray        # fp16 [n_hot, H, d], position order
     hot_v: np.ndarray
-    codes: np.ndarray        # int8 [n_blk, H, 2, S, d]; rows >= n_valid are 0
-    scales: np.ndarray       # fp32 [n_blk, H, 2]
+    codes: np.ndarray        # [n_blk, H, 2, S, d]: int8 codes (8 or 4 bits) or fp16 values (0 bits);
+                             # rows >= n_valid are 0
+    scales: np.ndarray       # fp32 [n_blk, H, 2] (all 1 for an FP16 cold zone)
     n_valid: np.ndarray      # int64 [n_blk]
+    quant_bits: int = 8
 
     @property
     def n_hot(self) -> int:
@@ -124,37 +145,47 @@ def split_history(n: int, hot_tokens: int) -> Tuple[int, int]:
     return n_hot, n - n_hot
 
 
-def quantize_block(k_rows: np.ndarray, v_rows: np.ndarray, block_size: int
+def quantize_block(k_rows: np.ndarray, v_rows: np.ndarray, block_size: int, bits: int = 8
                    ) -> Tuple[np.ndarray, np.ndarray]:
-    """Codes [H, 2, S, d] and scales [H, 2] of one cold block from its valid fp16 rows [n_valid, H, d]."""
+    """Codes [H, 2, S, d] and scales [H, 2] of one cold block from its valid fp16 rows [n_valid, H, d].
+
+    bits 0 (FP16 cold zone, Hybrid KV Cache page 5.2): the rows themselves, scale 1."""
     n_valid, n_heads, d = k_rows.shape
+    if bits == 0:
+        codes = np.zeros((n_heads, 2, block_size, d), dtype=np.float16)
+        for c, rows in enumerate((k_rows, v_rows)):
+            codes[:, c, :n_valid, :] = np.asarray(rows, dtype=np.float16).transpose(1, 0, 2)
+        return codes, np.ones((n_heads, 2), dtype=np.float32)
     codes = np.zeros((n_heads, 2, block_size, d), dtype=np.int8)
     scales = np.zeros((n_heads, 2), dtype=np.float32)
     for h in range(n_heads):
         for c, rows in enumerate((k_rows, v_rows)):
             tile = rows[:, h, :]
-            s = block_scale(tile)
+            s = block_scale(tile, bits)
             scales[h, c] = s
-            codes[h, c, :n_valid, :] = quantize_codes(tile, s)
+            codes[h, c, :n_valid, :] = quantize_codes(tile, s, bits)
     return codes, scales
 
 
-def build_state(k_hist: np.ndarray, v_hist: np.ndarray, hot_tokens: int, block_size: int) -> SequenceState:
+def build_state(k_hist: np.ndarray, v_hist: np.ndarray, hot_tokens: int, block_size: int,
+                quant_bits: int = 8) -> SequenceState:
     """State after a sequence's whole history k_hist/v_hist (fp16 [n, H, d]) has been cached."""
+    if quant_bits not in QUANT_BITS:
+        raise ValueError("quantization_bits must be 8, 4 or 0")
     k_hist = np.asarray(k_hist, dtype=np.float16)
     v_hist = np.asarray(v_hist, dtype=np.float16)
     n, n_heads, d = k_hist.shape
     n_hot, n_cold = split_history(n, hot_tokens)
     n_blk = -(-n_cold // block_size)
-    codes = np.zeros((n_blk, n_heads, 2, block_size, d), dtype=np.int8)
+    codes = np.zeros((n_blk, n_heads, 2, block_size, d), dtype=np.float16 if quant_bits == 0 else np.int8)
     scales = np.zeros((n_blk, n_heads, 2), dtype=np.float32)
     n_valid = np.zeros(n_blk, dtype=np.int64)
     for j in range(n_blk):
         lo, hi = j * block_size, min((j + 1) * block_size, n_cold)
         n_valid[j] = hi - lo
-        codes[j], scales[j] = quantize_block(k_hist[lo:hi], v_hist[lo:hi], block_size)
+        codes[j], scales[j] = quantize_block(k_hist[lo:hi], v_hist[lo:hi], block_size, quant_bits)
     return SequenceState(hot_tokens, block_size, n, k_hist[n_cold:].copy(), v_hist[n_cold:].copy(),
-                         codes, scales, n_valid)
+                         codes, scales, n_valid, quant_bits)
 
 
 def cold_kv(state: SequenceState, h: int) -> Tuple[np.ndarray, np.ndarray]:

@@ -54,20 +54,25 @@ def round_half_even(x: float) -> int:
     return int(n)
 
 
-def exact_scale(tile: np.ndarray) -> float:
+def exact_scale(tile: np.ndarray, lim: int = 127) -> float:
     m = max((abs(Fraction(float(v))) for v in np.asarray(tile, dtype=np.float16).ravel()), default=Fraction(0))
-    return fp32_nearest(m / 127)
+    return fp32_nearest(m / lim)
 
 
-def exact_code(x: float, s: float) -> int:
+def exact_code(x: float, s: float, lim: int = 127) -> int:
     if s == 0.0:
         return 0
     quot = fp32_nearest(Fraction(float(x)) / Fraction(s))
-    return max(-127, min(127, round_half_even(quot)))
+    return max(-lim, min(lim, round_half_even(quot)))
 
 
-def brute_history_kv(k_hist, v_hist, hot: int, block: int, h: int) -> Tuple[List, List]:
-    """Key/value rows of kv-head h that decode attends to, built with exact arithmetic and loops."""
+# largest code magnitude per cold-zone width (written out, not taken from the oracle)
+LIMIT = {8: 127, 4: 7}
+
+
+def brute_history_kv(k_hist, v_hist, hot: int, block: int, h: int, bits: int = 8) -> Tuple[List, List]:
+    """Key/value rows of kv-head h that decode attends to, built with exact arithmetic and loops
+    (bits 0: the cold rows are the fp16 values themselves)."""
     n = len(k_hist)
     n_hot = min(n, hot)
     n_cold = n - n_hot
@@ -77,9 +82,14 @@ def brute_history_kv(k_hist, v_hist, hot: int, block: int, h: int) -> Tuple[List
         rows = range(j * block, min((j + 1) * block, n_cold))
         for src, dst in ((k_hist, keys), (v_hist, vals)):
             tile = np.array([[src[t][h][c] for c in range(src.shape[2])] for t in rows], dtype=np.float16)
-            s = exact_scale(tile)
+            if bits == 0:
+                for t in range(tile.shape[0]):
+                    dst.append([float(x) for x in tile[t]])
+                continue
+            lim = LIMIT[bits]
+            s = exact_scale(tile, lim)
             for t in range(tile.shape[0]):
-                dst.append([float(exact_code(float(x), s)) * s for x in tile[t]])
+                dst.append([float(exact_code(float(x), s, lim)) * s for x in tile[t]])
         j += 1
     for t in range(n_cold, n):
         keys.append([float(x) for x in k_hist[t][h]])
@@ -293,13 +303,13 @@ def pin_hot_is_most_recent(orc, rng) -> None:
     assert np.all(out[0] == float(np.float16(0.1)))
 
 
-def brute_topk(q, k_hist, hot, blk, n_kv, g, kk):
+def brute_topk(q, k_hist, hot, blk, n_kv, g, kk, bits=8):
     """Loops: dequantised cold keys, mean cosine over the group, softmax per block, sort with tie rule."""
     n = len(k_hist)
     n_cold = n - min(n, hot)
     result = []
     for h in range(n_kv):
-        keys, _ = brute_history_kv(k_hist, k_hist, hot, blk, h)
+        keys, _ = brute_history_kv(k_hist, k_hist, hot, blk, h, bits)
         keys = keys[:n_cold]
         c = []
         for t in range(n_cold):
@@ -407,6 +417,116 @@ def pin_sparse_subset(orc, rng) -> None:
     assert np.max(np.abs(out - ref)) < 1e-12
 
 
+# --------------------------------------------------------------------------- INT4 and FP16 cold zones
+def pin_int4_scale_exhaustive(orc) -> None:
+    """Every finite non-negative fp16 max maps to the correctly rounded fp32 of m/7 at 4 bits."""
+    ms = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16)
+    for m in ms:
+        got = float(orc.block_scale(np.array([[m, -m * np.float16(0.25)]], dtype=np.float16), 4))
+        want = fp32_nearest(Fraction(float(m)) / 7)
+        assert got == want, f"4-bit scale of m={float(m)!r}: {got!r} != {want!r}"
+
+
+def pin_int4_codes_exact(orc, rng) -> None:
+    """4-bit codes equal rint-half-even of the correctly rounded fp32 quotient, clipped to +-7, for every
+    fp16 input below a set of maxima (and the inputs next to each rounding boundary k + 1/2)."""
+    finite = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16)
+    for m in (np.float16(7.0), np.float16(65504.0), np.float16(1.0), np.float16(6.1035e-05),
+              np.float16(2.0 ** -24 * 37), np.float16(3.1416), np.float16(40.72), np.float16(0.3)):
+        cand = finite[finite.astype(np.float64) <= float(m)]
+        pick = cand[:: max(1, len(cand) // 3000)]
+        s = fp32_nearest(Fraction(float(m)) / 7)
+        near = []
+        for k in range(7):
+            t = np.float16((k + 0.5) * s)
+            near += [np.nextafter(t, np.float16(-np.inf)), t, np.nextafter(t, np.float16(np.inf))]
+        near = np.array([x for x in near if 0 < float(x) <= float(m)], dtype=np.float16)
+        xs = np.concatenate([pick, -pick, near, -near, np.array([m, -m], dtype=np.float16)])
+        tile = xs.reshape(1, -1)
+        so = orc.block_scale(tile, 4)
+        assert float(so) == s
+        got = orc.quantize_codes(tile, so, 4).ravel()
+        want = np.array([exact_code(float(x), s, 7) for x in xs], dtype=np.int64)
+        bad = np.nonzero(got.astype(np.int64) != want)[0]
+        assert bad.size == 0, f"m={float(m)}: 4-bit code mismatch at x={xs[bad[:5]]}: {got[bad[:5]]} vs {want[bad[:5]]}"
+
+
+def pin_int4_code_invariants(orc, rng) -> None:
+    """|q| <= 7, the max element maps to +-7, |x - q s| <= s (1/2 + 2^-18), x_hat = q s exactly."""
+    for trial in range(20):
+        t = rng_fp16(rng, (int(rng.integers(1, 65)), 32), float(rng.choice([1e-3, 1.0, 10.0, 300.0])))
+        s = orc.block_scale(t, 4)
+        q = orc.quantize_codes(t, s, 4).astype(np.int64)
+        assert np.all(np.abs(q) <= 7)
+        i = np.unravel_index(np.argmax(np.abs(t.astype(np.float64))), t.shape)
+        assert abs(q[i]) == 7
+        err = np.abs(t.astype(np.float64) - q * float(s))
+        assert np.all(err <= float(s) * (0.5 + 2.0 ** -18))
+        xh = orc.dequantize(q.astype(np.int8), s)
+        for a, b in zip(xh.ravel()[:50], q.ravel()[:50]):
+            assert Fraction(a) == Fraction(int(b)) * Fraction(float(s))
+
+
+def pin_int4_cold_sdpa(orc, rng) -> None:
+    """4-bit cold blocks: decode equals SDPA over exactly re-quantised (limit 7) cold rows + fp16 hot rows,
+    and explicit loops agree on a tiny shape."""
+    for n, n_kv, g, d, hot, blk in ((100, 2, 2, 8, 32, 64), (200, 1, 4, 16, 32, 64), (75, 2, 1, 8, 16, 8)):
+        k = rng_fp16(rng, (n, n_kv, d), 2.0)
+        v = rng_fp16(rng, (n, n_kv, d))
+        q = rng_fp16(rng, (n_kv * g, d))
+        st = orc.build_state(k, v, hot, blk, 4)
+        out, lse = orc.decode(q, st)
+        keys, vals = zip(*[brute_history_kv(k, v, hot, blk, h, 4) for h in range(n_kv)])
+        ref = _sdpa(q.astype(np.float64), keys, vals, g)
+        assert np.max(np.abs(out - ref)) < 1e-12, np.max(np.abs(out - ref))
+    n, n_kv, g, d = 90, 1, 2, 4
+    k = rng_fp16(rng, (n, n_kv, d), 1.5)
+    v = rng_fp16(rng, (n, n_kv, d))
+    q = rng_fp16(rng, (n_kv * g, d))
+    st = orc.build_state(k, v, 32, 64, 4)
+    out, lse = orc.decode(q, st)
+    for hq in range(n_kv * g):
+        keys, vals = brute_history_kv(k, v, 32, 64, hq // g, 4)
+        o_ref, l_ref = brute_attend([float(x) for x in q[hq]], keys, vals)
+        assert max(abs(a - b) for a, b in zip(out[hq], o_ref)) < 1e-12
+        assert abs(lse[hq] - l_ref) < 1e-12
+
+
+def pin_fp16_cold_is_dense_attention(orc, rng) -> None:
+    """quantization_bits 0: the cold zone keeps the fp16 values, so decode over any history (cold blocks
+    included) equals plain softmax attention over the whole fp16 history (torch SDPA), and the state
+    holds the history rows with scale 1."""
+    for n, n_kv, g, d in ((300, 2, 2, 16), (32 + 64 * 3 + 5, 1, 4, 8), (33, 2, 1, 8)):
+        k = rng_fp16(rng, (n, n_kv, d), 40.0)
+        v = rng_fp16(rng, (n, n_kv, d))
+        q = rng_fp16(rng, (n_kv * g, d))
+        st = orc.build_state(k, v, 32, 64, 0)
+        out, lse = orc.decode(q, st)
+        keys = [k[:, h, :].astype(np.float64) for h in range(n_kv)]
+        vals = [v[:, h, :].astype(np.float64) for h in range(n_kv)]
+        ref = _sdpa(q.astype(np.float64), keys, vals, g)
+        assert np.max(np.abs(out - ref)) < 1e-12
+        n_cold = n - min(n, 32)
+        for j in range(st.n_blocks):
+            nv = int(st.n_valid[j])
+            rows = k[j * 64:j * 64 + nv].transpose(1, 0, 2)
+            assert np.array_equal(st.codes[j, :, 0, :nv].view(np.uint16), rows.view(np.uint16))
+            assert np.all(st.scales[j] == 1.0)
+        assert st.n_cold == n_cold
+
+
+def pin_topk_other_widths(orc, rng) -> None:
+    """Top-K over 4-bit cold blocks (cosine of the codes) and over an FP16 cold zone (cosine of the fp16
+    keys) against the brute-force loops."""
+    for bits in (4, 0):
+        n, n_kv, g, d, kk = 200, 2, 2, 8, 20
+        k = rng_fp16(rng, (n, n_kv, d))
+        q = rng_fp16(rng, (n_kv * g, d))
+        st = orc.build_state(k, k, 32, 64, bits)
+        idx, _, _ = orc.topk_select(q, st, kk)
+        assert np.array_equal(idx, brute_topk(q, k, 32, 64, n_kv, g, kk, bits)), bits
+
+
 ALL_PINS = [
     ("scale_exhaustive", lambda o, r: pin_scale_exhaustive(o)),
     ("codes_exact", pin_codes_exact),
@@ -424,4 +544,10 @@ ALL_PINS = [
     ("topk_scale_invariance", pin_topk_scale_invariance),
     ("topk_all_selected", pin_topk_all_selected),
     ("sparse_subset", pin_sparse_subset),
+    ("int4_scale_exhaustive", lambda o, r: pin_int4_scale_exhaustive(o)),
+    ("int4_codes_exact", pin_int4_codes_exact),
+    ("int4_code_invariants", pin_int4_code_invariants),
+    ("int4_cold_sdpa", pin_int4_cold_sdpa),
+    ("fp16_cold_is_dense_attention", pin_fp16_cold_is_dense_attention),
+    ("topk_other_widths", pin_topk_other_widths),
 ]

@@ -11,22 +11,41 @@ def test_pin(name, fn):
     fn(orc, np.random.default_rng(1234))
 
 
-def _m_scale_128(x):
+_LIM = {8: 127, 4: 7}
+
+
+def _m_scale_128(x, bits=8):
     x = np.asarray(x)
-    return np.float32(float(np.max(np.abs(x.astype(np.float64)))) / 128.0) if x.size else np.float32(0)
+    div = 128.0 if bits == 8 else 7.0
+    return np.float32(float(np.max(np.abs(x.astype(np.float64)))) / div) if x.size else np.float32(0)
 
 
-def _m_round_half_up(x, s):
+def _m_int4_scale_8(x, bits=8):
+    x = np.asarray(x)
+    div = 127.0 if bits == 8 else 8.0
+    return np.float32(float(np.max(np.abs(x.astype(np.float64)))) / div) if x.size else np.float32(0)
+
+
+def _m_round_half_up(x, s, bits=8):
     if float(s) == 0.0:
         return np.zeros(np.asarray(x).shape, np.int8)
     quot = (np.asarray(x).astype(np.float64) / np.float64(s)).astype(np.float32).astype(np.float64)
-    return np.clip(np.floor(quot + 0.5), -127, 127).astype(np.int8)
+    return np.clip(np.floor(quot + 0.5), -_LIM[bits], _LIM[bits]).astype(np.int8)
 
 
-def _m_no_fp32_quotient(x, s):
+def _m_no_fp32_quotient(x, s, bits=8):
     if float(s) == 0.0:
         return np.zeros(np.asarray(x).shape, np.int8)
-    return np.clip(np.rint(np.asarray(x).astype(np.float64) / np.float64(s)), -127, 127).astype(np.int8)
+    return np.clip(np.rint(np.asarray(x).astype(np.float64) / np.float64(s)), -_LIM[bits], _LIM[bits]).astype(np.int8)
+
+
+def _m_int4_with_int8_scale(x, bits=8):
+    x = np.asarray(x)
+    return np.float32(float(np.max(np.abs(x.astype(np.float64)))) / 127.0) if x.size else np.float32(0)
+
+
+def _m_fp16_cold_quantised(k_rows, v_rows, block_size, bits=8):
+    return _REAL["quantize_block"](k_rows, v_rows, block_size, 8 if bits == 0 else bits)
 
 
 def _m_split_first_hot(n, hot):
@@ -35,8 +54,8 @@ def _m_split_first_hot(n, hot):
     return min(n, hot), n - min(n, hot)
 
 
-def _mutant_build_state_first_hot(k_hist, v_hist, hot, block):
-    st = _REAL["build_state"](k_hist[::-1].copy(), v_hist[::-1].copy(), hot, block)
+def _mutant_build_state_first_hot(k_hist, v_hist, hot, block, quant_bits=8):
+    st = _REAL["build_state"](k_hist[::-1].copy(), v_hist[::-1].copy(), hot, block, quant_bits)
     return st
 
 
@@ -69,7 +88,7 @@ def _m_cosine_no_knorm(q, state):
     return out
 
 
-_REAL = {"build_state": orc.build_state}
+_REAL = {"build_state": orc.build_state, "quantize_block": orc.quantize_block}
 
 MUTANTS = [
     ("scale_divides_by_128", "block_scale", _m_scale_128),
@@ -80,16 +99,20 @@ MUTANTS = [
     ("logit_sign_flipped", "attend", _m_attend_sign),
     ("softmax_over_all_tokens_not_windows", "window_softmax", _m_window_global),
     ("cosine_missing_key_norm", "token_scores", _m_cosine_no_knorm),
+    ("int4_scale_divides_by_8", "block_scale", _m_int4_scale_8),
+    ("int4_block_uses_the_int8_scale", "block_scale", _m_int4_with_int8_scale),
+    ("fp16_cold_zone_quantised", "quantize_block", _m_fp16_cold_quantised),
 ]
 
 
 @pytest.mark.parametrize("name,attr,fn", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_planted_mistake_is_caught(monkeypatch, name, attr, fn):
     monkeypatch.setattr(orc, attr, fn)
-    caught = []
+    caught = None
     for pin_name, pin in pins.ALL_PINS:
         try:
             pin(orc, np.random.default_rng(1234))
         except (AssertionError, ValueError, IndexError):
-            caught.append(pin_name)
+            caught = pin_name
+            break
     assert caught, f"no pin caught the planted mistake {name}"
