@@ -53,7 +53,7 @@ COUNTER_TRAFFIC = {
     "sources_sha256": "",
     "bytes_per_launch": {},
 }
-KERNEL_SOURCES = ("append.hip", "decode.hip", "topk.hip", "hkv_device.h", "hkv_internal.h")
+KERNEL_SOURCES = ("append.hip", "decode_impl.h", "decode_inst.hip", "topk.hip", "hkv_device.h", "hkv_internal.h")
 
 
 def code_text(src: str) -> str:

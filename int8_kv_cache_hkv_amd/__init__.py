@@ -237,6 +237,7 @@ class HybridKVCache:
         import torch
         self.torch = torch
         self.H, self.D, self.T, self.S = n_kv_heads, head_dim, hot_tokens, block_size
+        self.quant_bits = quant_bits
         self.batch = batch
         self.handle = hkv_create(n_kv_heads, head_dim, hot_tokens, block_size, quant_bits)
         sz = hkv_cache_sizes(self.handle, batch, max_tokens_per_seq, num_phys_blocks)
@@ -298,28 +299,51 @@ class HybridKVCache:
         return out_idx
 
     # -- layout helpers for inspection (host numpy views of device buffers)
-    def cold_codes(self) -> np.ndarray:
-        """int8 [P, H, 2, S, D] codes in (token, channel) order, un-doing the streaming tile layouts."""
-        S, D = self.S, self.D
-        raw = self.cold.cpu().numpy()[: self.num_phys * self.H * 2 * S * D]
-        tiles = raw.reshape(self.num_phys, self.H, 2, S * D)
-        out = np.empty((self.num_phys, self.H, 2, S, D), dtype=np.int8)
-        kv = tiles[:, :, 0].reshape(self.num_phys, self.H, D // 16, S, 16)      # [dc][t][16]
-        out[:, :, 0] = kv.transpose(0, 1, 3, 2, 4).reshape(self.num_phys, self.H, S, D)
-        vv = tiles[:, :, 1].reshape(self.num_phys, self.H, S // 16, D, 16)      # [tc][c][16]
-        out[:, :, 1] = vv.transpose(0, 1, 2, 4, 3).reshape(self.num_phys, self.H, S, D)
+    def _tile_elems(self) -> int:
+        """Elements per 16-byte tile chunk: 16 (8-bit codes), 32 (4-bit codes), 8 (fp16 values)."""
+        return {8: 16, 4: 32, 0: 8}[self.quant_bits]
+
+    def _tile_bytes(self) -> int:
+        n = self.S * self.D
+        return n * 2 if self.quant_bits == 0 else n * self.quant_bits // 8
+
+    def _unpack(self, raw: np.ndarray) -> np.ndarray:
+        """Tile bytes [..., TB] -> elements in chunk order [..., S*D]: int8 codes, or fp16 values."""
+        if self.quant_bits == 8:
+            return raw.view(np.int8)
+        if self.quant_bits == 0:
+            return raw.view(np.float16)
+        u = raw.view(np.uint8)
+        out = np.empty(u.shape[:-1] + (u.shape[-1] * 2,), dtype=np.int8)
+        out[..., 0::2] = (u & 0x0F).astype(np.int8) - 8   # offset binary: element 2i in the low nibble
+        out[..., 1::2] = (u >> 4).astype(np.int8) - 8
         return out
 
-    def cold_codes_of(self, phys: Sequence[int]) -> np.ndarray:
-        """int8 [len(phys), H, 2, S, D] codes of selected physical blocks only."""
-        S, D, H = self.S, self.D, self.H
-        tile = H * 2 * S * D
-        out = np.empty((len(phys), H, 2, S, D), dtype=np.int8)
-        for i, p in enumerate(phys):
-            raw = self.cold[int(p) * tile:(int(p) + 1) * tile].cpu().numpy().reshape(H, 2, S * D)
-            out[i, :, 0] = raw[:, 0].reshape(H, D // 16, S, 16).transpose(0, 2, 1, 3).reshape(H, S, D)
-            out[i, :, 1] = raw[:, 1].reshape(H, S // 16, D, 16).transpose(0, 1, 3, 2).reshape(H, S, D)
+    def _tiles_to_rows(self, tiles: np.ndarray) -> np.ndarray:
+        """[N, 2, TB] tile bytes of (block, kv-head) pairs -> [N, 2, S, D] codes (token, channel order)."""
+        S, D, E = self.S, self.D, self._tile_elems()
+        el = self._unpack(np.ascontiguousarray(tiles))
+        N = tiles.shape[0]
+        out = np.empty((N, 2, S, D), dtype=el.dtype)
+        out[:, 0] = el[:, 0].reshape(N, D // E, S, E).transpose(0, 2, 1, 3).reshape(N, S, D)   # chunk (kc, t)
+        out[:, 1] = el[:, 1].reshape(N, S // E, D, E).transpose(0, 1, 3, 2).reshape(N, S, D)   # chunk (vc, c)
         return out
+
+    def cold_codes(self) -> np.ndarray:
+        """[P, H, 2, S, D] cold contents in (token, channel) order, un-doing the streaming tile layouts:
+        int8 codes (8 and 4 bits) or fp16 values (quant_bits 0)."""
+        TB = self._tile_bytes()
+        raw = self.cold.cpu().numpy().view(np.uint8)[: self.num_phys * self.H * 2 * TB]
+        tiles = raw.reshape(self.num_phys * self.H, 2, TB)
+        return self._tiles_to_rows(tiles).reshape(self.num_phys, self.H, 2, self.S, self.D)
+
+    def cold_codes_of(self, phys: Sequence[int]) -> np.ndarray:
+        """[len(phys), H, 2, S, D] cold contents of selected physical blocks only."""
+        TB = self._tile_bytes()
+        blk = self.H * 2 * TB
+        raws = [self.cold[int(p) * blk:(int(p) + 1) * blk].cpu().numpy().view(np.uint8) for p in phys]
+        tiles = np.stack(raws).reshape(len(phys) * self.H, 2, TB)
+        return self._tiles_to_rows(tiles).reshape(len(phys), self.H, 2, self.S, self.D)
 
     def scale_array(self) -> np.ndarray:
         return self.scales.cpu().numpy()[: self.num_phys * self.H * 2].reshape(self.num_phys, self.H, 2)

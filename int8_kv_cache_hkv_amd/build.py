@@ -18,9 +18,27 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libhkv.so")
 
 
+# decode_inst.hip is compiled once per (head_dim, GQA group, cold-tile format) instance
+DECODE_INST = "decode_inst.hip"
+DECODE_INSTANCES = [(d, g, bits) for bits in (8, 4, 0) for d in (128, 64) for g in (1, 2, 4, 8)]
+
+
 def sources() -> list:
     """Every translation unit of the library: the .hip kernel files and the host .cpp files."""
     return sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
+
+
+def compile_units() -> list:
+    """(source, extra defines, object name) of every object the library is linked from."""
+    units = []
+    for src in sources():
+        if src == DECODE_INST:
+            for d, g, bits in DECODE_INSTANCES:
+                units.append((src, [f"-DHKV_D={d}", f"-DHKV_G={g}", f"-DHKV_BITS={bits}"],
+                              f"decode_d{d}_g{g}_b{bits}.o"))
+        else:
+            units.append((src, [], src + ".o"))
+    return units
 
 
 HIPCC_FLAGS = [
@@ -59,10 +77,10 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
     with tempfile.TemporaryDirectory(prefix="hkv_build_") as tmpd:
         objs = []
         cmds = []
-        for src in sources():
-            obj = os.path.join(tmpd, src + ".o")
+        for src, defs, name in compile_units():
+            obj = os.path.join(tmpd, name)
             objs.append(obj)
-            cmds.append([cc, *HIPCC_FLAGS, *inc, "-c", os.path.join(CSRC, src), "-o", obj])
+            cmds.append([cc, *HIPCC_FLAGS, *defs, *inc, "-c", os.path.join(CSRC, src), "-o", obj])
         with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
             for f in [ex.submit(_run, c, verbose) for c in cmds]:
                 f.result()

@@ -2,12 +2,14 @@
 //
 // Hybrid KV Cache page, 2.1: the hot zone keeps the full FP16 KV of the most
 // recent hot_tokens tokens; older tokens form the cold zone, stored as INT8
-// with a block-wise scale.  4.2 (step 2): the non-hot part is quantised.
-// Scale per (block, kv-head, K|V): s = fl32(max|x| / 127); code =
-// clamp(rint(fl32(x / s)), -127, 127), round half to even.  A partially
+// with a block-wise scale (3.1: 4 or 8 bits; 5.2: 0 bits keeps the cold zone
+// in FP16).  4.2 (step 2): the non-hot part is quantised.  Scale per (block,
+// kv-head, K|V): s = fl32(max|x| / L) with L = 127 (8 bits) or 7 (4 bits);
+// code = clamp(rint(fl32(x / s)), -L, L), round half to even.  A partially
 // filled block always holds the codes of its current tokens, so every block
 // an append touches is re-quantised from FP16 (older tokens of a partial block
-// come from the per-sequence tail shadow).
+// come from the per-sequence tail shadow).  FP16 tiles store the values
+// (scale 1).
 //
 // Two launches, in stream order (multi-block appends; the single-pass
 // append_step_kernel below serves appends that touch at most two blocks):
@@ -30,13 +32,104 @@ namespace hkv {
 
 namespace detail {
 
-template <int D>
+// Stage of one (block, kv-head, K|V) tile in LDS while it is coded: K row-major ([token][channel]),
+// V column-major ([channel][token]), the orders of the tiles' chunks; one byte per code, or the
+// fp16 value itself.
+template <int D, int BITS>
+struct TileStage {
+  static constexpr int EB = BITS == 0 ? 2 : 1;
+  static constexpr int KROW = D * EB + 16;            // padded K row (bytes)
+  static constexpr int VROW = kBlockSize * EB + 16;   // padded V row (bytes)
+  static constexpr int BYTES = (kBlockSize * KROW > D * VROW) ? kBlockSize * KROW : D * VROW;
+};
+
+// Element i of a row slice held as fp16 pairs (u32x4_t vectors).
+template <int NV>
+__device__ __forceinline__ uint32_t slice_half_bits(const u32x4_t (&x)[NV], int e) {
+  const uint32_t wd = x[e / 8][(e % 8) / 2];
+  return (e & 1) ? (wd >> 16) : (wd & 0xffffu);
+}
+
+// Stage the CPT elements of token t at channels [c0, c0 + CPT) of one tile: 8-/4-bit codes under
+// scale s (clamp(rint(fl32(x / s)), -L, L)), or the fp16 values.  kv selects the stage order.
+template <int D, int BITS, int CPT, int NV>
+__device__ __forceinline__ void stage_row(int8_t* stage, const u32x4_t (&x)[NV], float s, int kv, int t, int c0) {
+  using TS = TileStage<D, BITS>;
+  if constexpr (BITS == 0) {
+    if (kv == 0) {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(stage + t * TS::KROW + c0 * 2);
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[4 * v + i] = x[v][i];
+    } else {
+#pragma unroll
+      for (int e = 0; e < CPT; ++e)
+        *reinterpret_cast<uint16_t*>(stage + (c0 + e) * TS::VROW + 2 * t) = static_cast<uint16_t>(slice_half_bits(x, e));
+    }
+  } else {
+    const float rs = __builtin_amdgcn_rcpf(s);
+    uint32_t q[CPT / 4];
+#pragma unroll
+    for (int i = 0; i < CPT / 4; ++i) {
+      uint32_t packed = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int e = 4 * i + k;
+        const uint32_t wd = x[e / 8][(e % 8) / 2];
+        const float xv = (e & 1) ? half_hi(wd) : half_lo(wd);
+        float qv = 0.f;
+        if (s > 0.f) qv = quant_code<Fmt<BITS>::kLimit>(xv, s, rs);
+        packed |= (static_cast<uint32_t>(static_cast<int>(qv)) & 0xffu) << (8 * k);
+      }
+      q[i] = packed;
+    }
+    if (kv == 0) {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(stage + t * TS::KROW + c0);
+#pragma unroll
+      for (int i = 0; i < CPT / 4; ++i) dst[i] = q[i];
+    } else {
+#pragma unroll
+      for (int e = 0; e < CPT; ++e) stage[(c0 + e) * TS::VROW + t] = static_cast<int8_t>(q[e / 4] >> (8 * (e % 4)));
+    }
+  }
+}
+
+// Write a whole staged tile in its chunk layout (16-byte vectors, coalesced).
+template <int D, int BITS>
+__device__ __forceinline__ void write_tile(int8_t* tile, const int8_t* stage, int kv, int tid) {
+  using TS = TileStage<D, BITS>;
+  constexpr int S = kBlockSize;
+  constexpr int E = Fmt<BITS>::kElems;
+  constexpr int NVEC = Fmt<BITS>::template tile_bytes<D>() / 16;
+  for (int vi = tid; vi < NVEC; vi += kThreads) {
+    uint4 out;
+    if (kv == 0) {
+      const int kc = vi / S, tt = vi % S;  // chunk (kc, tt): elements [kc E, kc E + E) of token tt
+      out = chunk_from_stage<BITS>(stage + tt * TS::KROW + kc * E * TS::EB);
+    } else {
+      const int vc = vi / D, cc = vi % D;  // chunk (vc, cc): tokens [vc E, vc E + E) of channel cc
+      out = chunk_from_stage<BITS>(stage + cc * TS::VROW + vc * E * TS::EB);
+    }
+    reinterpret_cast<uint4*>(tile)[vi] = out;
+  }
+}
+
+// Scale of a tile whose largest magnitude is m: fl32(m / L) (IEEE fp32 division), or 1 for fp16 tiles.
+template <int BITS>
+__device__ __forceinline__ float tile_scale(float m) {
+  if constexpr (BITS == 0) return 1.f;
+  else return m / static_cast<float>(Fmt<BITS>::kLimit);
+}
+
+template <int D, int BITS>
 __global__ __launch_bounds__(kThreads) void append_quant_kernel(AppendParams p) {
   constexpr int S = kBlockSize;
   constexpr int TPT = kThreads / S;     // threads per token row
   constexpr int CPT = D / TPT;          // channels per thread (32 or 16)
-  constexpr int LDS_ROW = D + 16;       // padded staging row (bytes), 16-byte aligned
-  __shared__ __align__(16) int8_t stage[S * LDS_ROW];
+  constexpr int NV = CPT / 8;           // 16-byte vectors per thread and row
+  constexpr int TB = Fmt<BITS>::template tile_bytes<D>();
+  __shared__ __align__(16) int8_t stage[TileStage<D, BITS>::BYTES];
   __shared__ float red[kWaves];
 
   const CacheView& c = p.c;
@@ -80,75 +173,28 @@ __global__ __launch_bounds__(kThreads) void append_quant_kernel(AppendParams p) 
         row = src + ((static_cast<size_t>(b) * p.max_n_new + (pos - n0)) * H + h) * D;
       }
     }
-    float x[CPT];
-    if (row) {
-      const uint4* r4 = reinterpret_cast<const uint4*>(row + part * CPT);
+    u32x4_t x[NV];
 #pragma unroll
-      for (int v = 0; v < CPT / 8; ++v) {
-        uint4 w = r4[v];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          uint32_t u = word_of(w, i);
-          x[v * 8 + 2 * i] = half_lo(u);
-          x[v * 8 + 2 * i + 1] = half_hi(u);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < CPT; ++i) x[i] = 0.f;
-    }
+    for (int v = 0; v < NV; ++v)
+      x[v] = row ? reinterpret_cast<const u32x4_t*>(row + part * CPT)[v] : u32x4_t{0u, 0u, 0u, 0u};
     // ---- m = max |x| over the block (exact: every candidate is an fp16 value)
     float m = 0.f;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) m = fmaxf(m, fabsf(x[i]));
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(half_lo(x[v][i])), fabsf(half_hi(x[v][i]))));
     m = wave_max(m);
     if ((tid & 63) == 0) red[tid >> 6] = m;
     __syncthreads();
     m = red[0];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) m = fmaxf(m, red[w]);
-    // ---- s = fl32(m / 127): IEEE fp32 division (correctly rounded)
-    const float s = m / 127.0f;
-    const float rs = __builtin_amdgcn_rcpf(s);
-    // ---- codes = clamp(rint(fl32(x / s)), -127, 127), round half to even
-    int8_t* srow = stage + t * LDS_ROW + part * CPT;
-#pragma unroll
-    for (int i = 0; i < CPT; i += 4) {
-      uint32_t packed = 0;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        float qv = 0.f;
-        if (s > 0.f) qv = quant_code(x[i + k], s, rs);
-        packed |= (static_cast<uint32_t>(static_cast<int>(qv)) & 0xffu) << (8 * k);
-      }
-      *reinterpret_cast<uint32_t*>(srow + i) = packed;
-    }
+    // ---- s = fl32(m / L) (IEEE fp32 division), codes = clamp(rint(fl32(x / s)), -L, L)
+    const float s = tile_scale<BITS>(m);
+    stage_row<D, BITS, CPT, NV>(stage, x, s, kv, t, part * CPT);
     __syncthreads();
-    // ---- write the tile in its streaming layout (16-byte vectors, coalesced)
-    int8_t* tile = c.cold + tile_offset(phys, h, kv, H, S, D);
-    constexpr int NVEC = S * D / 16;
-    for (int vi = tid; vi < NVEC; vi += kThreads) {
-      uint4 out;
-      if (kv == 0) {
-        // K: vector (channel chunk dc, token tt) holds channels dc*16..dc*16+15 of token tt
-        const int dc = vi / S, tt = vi % S;
-        out = *reinterpret_cast<const uint4*>(stage + tt * LDS_ROW + dc * 16);
-      } else {
-        // V: vector (token chunk tc, channel cc) holds tokens tc*16..tc*16+15 of channel cc
-        const int tc = vi / D, cc = vi % D;
-        uint32_t wv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          uint32_t acc = 0;
-#pragma unroll
-          for (int k = 0; k < 4; ++k)
-            acc |= static_cast<uint32_t>(static_cast<uint8_t>(stage[(tc * 16 + i * 4 + k) * LDS_ROW + cc])) << (8 * k);
-          wv[i] = acc;
-        }
-        out = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-      }
-      reinterpret_cast<uint4*>(tile)[vi] = out;
-    }
+    // ---- write the tile in its streaming layout
+    write_tile<D, BITS>(c.cold + tile_offset(phys, h, kv, H, TB), stage, kv, tid);
     if (tid == 0) c.scales[(static_cast<size_t>(phys) * H + h) * 2 + kv] = s;
     __syncthreads();  // stage and red are reused by the V pass
   }
@@ -237,16 +283,18 @@ __global__ __launch_bounds__(kThreads) void append_ring_kernel(AppendParams p) {
 // are unchanged and only the new rows are coded (the old ones keep their
 // codes); otherwise the whole block is re-quantised from its FP16 rows.  Both
 // paths give the codes a full re-quantisation gives.
-template <int D>
+// 4-bit and fp16 tiles always re-write the whole touched block (a 4-bit row shares its V bytes
+// with the neighbouring row, and an fp16 row's values never change).
+template <int D, int BITS>
 __global__ __launch_bounds__(kThreads) void append_step_kernel(AppendParams p) {
   constexpr int S = kBlockSize;
   constexpr int TPT = kThreads / S;     // threads per token row
   constexpr int CPT = D / TPT;          // channels per thread
   constexpr int NV = CPT / 8;           // 16-byte vectors per thread and row
-  constexpr int LDS_ROW = D + 16;
   constexpr int VPR = D / 8;            // 16-byte vectors per fp16 row
   constexpr int RING_V = 4;             // ring vectors per thread held in registers
-  __shared__ __align__(16) int8_t stage[S * LDS_ROW];
+  constexpr int TB = Fmt<BITS>::template tile_bytes<D>();
+  __shared__ __align__(16) int8_t stage[TileStage<D, BITS>::BYTES];
   __shared__ float red[6][kWaves];
 
   // grid (kv-head, sequence of this launch): no index depends on a kernel argument, so every
@@ -309,7 +357,7 @@ __global__ __launch_bounds__(kThreads) void append_step_kernel(AppendParams p) {
         const uint32_t wd = x[e / 8][(e % 8) / 2];
         const float xv = (e & 1) ? half_hi(wd) : half_lo(wd);
         float qv = 0.f;
-        if (s > 0.f) qv = quant_code(xv, s, rs);
+        if (s > 0.f) qv = quant_code<127>(xv, s, rs);
         packed |= (static_cast<uint32_t>(static_cast<int>(qv)) & 0xffu) << (8 * k);
       }
       q[i] = packed;
@@ -393,8 +441,8 @@ __global__ __launch_bounds__(kThreads) void append_step_kernel(AppendParams p) {
       const float m_old = q == 0 ? mx[kv] : 0.f;
       const float m_new = mx[2 + 2 * q + kv];
       if (phys[q] < 0 || phys[q] >= c.num_phys) continue;
-      int8_t* tile = c.cold + tile_offset(phys[q], h, kv, H, S, D);
-      if (vo > 0 && m_new <= m_old) {
+      int8_t* tile = c.cold + tile_offset(phys[q], h, kv, H, TB);
+      if (BITS == 8 && vo > 0 && m_new <= m_old) {
         // ---- maximum unchanged: code only the new rows, in place
         if (is_new) {
           const float so = m_old / 127.0f;
@@ -415,37 +463,13 @@ __global__ __launch_bounds__(kThreads) void append_step_kernel(AppendParams p) {
         continue;
       }
       // ---- (re-)quantise the whole block: old rows from the tail shadow, new rows as loaded
-      const float s = fmaxf(m_old, m_new) / 127.0f;
+      const float s = tile_scale<BITS>(fmaxf(m_old, m_new));
       u32x4_t xs[NV];
 #pragma unroll
       for (int v = 0; v < NV; ++v) xs[v] = t < vo ? xo[kv][v] : xn[q][kv][v];  // element-wise: no indexed arrays
-      uint32_t qw[CPT / 4];
-      code_slice(xs, s, qw);
-      uint32_t* srow = reinterpret_cast<uint32_t*>(stage + t * LDS_ROW + part * CPT);
-#pragma unroll
-      for (int i = 0; i < CPT / 4; ++i) srow[i] = qw[i];
+      stage_row<D, BITS, CPT, NV>(stage, xs, s, kv, t, part * CPT);
       __syncthreads();
-      constexpr int NVEC = S * D / 16;
-      for (int vi = tid; vi < NVEC; vi += kThreads) {
-        uint4 out;
-        if (kv == 0) {
-          const int dc = vi / S, tt = vi % S;
-          out = *reinterpret_cast<const uint4*>(stage + tt * LDS_ROW + dc * 16);
-        } else {
-          const int tc = vi / D, cc = vi % D;
-          uint32_t wv[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            uint32_t acc = 0;
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-              acc |= static_cast<uint32_t>(static_cast<uint8_t>(stage[(tc * 16 + i * 4 + k) * LDS_ROW + cc])) << (8 * k);
-            wv[i] = acc;
-          }
-          out = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-        }
-        reinterpret_cast<uint4*>(tile)[vi] = out;
-      }
+      write_tile<D, BITS>(tile, stage, kv, tid);
       if (tid == 0) c.scales[(static_cast<size_t>(phys[q]) * H + h) * 2 + kv] = s;
       __syncthreads();  // stage is reused
     }
@@ -513,26 +537,32 @@ hipError_t launch_grid(K kernel, dim3 grid, const AppendParams& p, const LaunchC
   return hipGetLastError();
 }
 
+template <int D, int BITS>
+hipError_t launch_append_db(const AppendParams& p, const LaunchCtx& quant_ctx, const LaunchCtx& ring_ctx) {
+  if (p.single_pass) return launch_grid(append_step_kernel<D, BITS>, dim3(p.c.H, p.n_seq), p, quant_ctx);
+  const int qgrid = p.touched_max > 0 ? p.n_seq * p.touched_max * p.c.H : 0;
+  const hipError_t e = launch1(append_quant_kernel<D, BITS>, qgrid, p, quant_ctx);
+  return e == hipSuccess ? launch1(append_ring_kernel<D>, p.n_seq, p, ring_ctx) : e;
+}
+
+template <int D>
+hipError_t launch_append_d(const AppendParams& p, const LaunchCtx& quant_ctx, const LaunchCtx& ring_ctx) {
+  switch (p.c.bits) {
+    case 8: return launch_append_db<D, 8>(p, quant_ctx, ring_ctx);
+    case 4: return launch_append_db<D, 4>(p, quant_ctx, ring_ctx);
+    case 0: return launch_append_db<D, 0>(p, quant_ctx, ring_ctx);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace detail
 
 using namespace detail;
 
+// Single-pass appends (at most two touched blocks per sequence): grid (kv-head, sequence).
+// Otherwise the quantise launch (sequence, touched block, kv-head) and the ring/tail launch.
 hipError_t launch_append(const AppendParams& p, const LaunchCtx& quant_ctx, const LaunchCtx& ring_ctx) {
-  if (p.single_pass) {
-    const dim3 grid(p.c.H, p.n_seq);  // (kv-head, sequence)
-    return p.c.D == 128 ? launch_grid(append_step_kernel<128>, grid, p, quant_ctx)
-                        : launch_grid(append_step_kernel<64>, grid, p, quant_ctx);
-  }
-  const int qgrid = p.touched_max > 0 ? p.n_seq * p.touched_max * p.c.H : 0;
-  hipError_t e;
-  if (p.c.D == 128) {
-    e = launch1(append_quant_kernel<128>, qgrid, p, quant_ctx);
-    if (e == hipSuccess) e = launch1(append_ring_kernel<128>, p.n_seq, p, ring_ctx);
-  } else {
-    e = launch1(append_quant_kernel<64>, qgrid, p, quant_ctx);
-    if (e == hipSuccess) e = launch1(append_ring_kernel<64>, p.n_seq, p, ring_ctx);
-  }
-  return e;
+  return p.c.D == 128 ? launch_append_d<128>(p, quant_ctx, ring_ctx) : launch_append_d<64>(p, quant_ctx, ring_ctx);
 }
 
 }  // namespace hkv

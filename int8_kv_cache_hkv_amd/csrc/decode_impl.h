@@ -38,6 +38,12 @@
 // pipelined: each 1 KiB chunk of the current K (V) tile is replaced by the same
 // chunk of the next unit's tile as soon as its QK (PV) products are issued, so
 // a wave always has about one unit's loads in flight.
+//
+// Cold tiles come in three formats (8-bit codes, 4-bit codes, fp16 values; see Fmt): every
+// function that touches a tile takes the format as the template parameter BITS.  Each (head_dim,
+// group, format) instance is compiled from decode_inst.hip into an object of its own.
+#pragma once
+
 #include <hip/hip_ext.h>
 
 #include <cstring>
@@ -96,7 +102,7 @@ struct WaveState {
   using C = Cfg<D, G>;
   float m[C::NG];                          // running max of base-2 logits (wave-uniform)
   float l[C::NG];                          // lane-partial sum of softmax weights
-  float qb[C::NG];                         // 1152 * sum_k q[g][k] (wave-uniform)
+  float qb[C::NG];                         // bias * sum_k q[g][k] (wave-uniform; see Fmt::kBias)
   float4_t acc[C::NQ][C::NDL];             // out[4quad + r][64 pass + lane] (with the code offset)
 };
 
@@ -145,11 +151,11 @@ __device__ __forceinline__ void softmax_unit(WaveState<D, G>& st, DecodeSmem<D, 
   wave_lds_sync();
 }
 
-// PV products of four tokens t0..t0+3 into the block accumulators: vw[ps] is
-// the word holding their value codes at channel 64 ps + lane.
+// PV products of four tokens t0..t0+3 into the block accumulators: bv[ps] is the exact value
+// operand (the four tokens' values at channel 64 ps + lane).
 template <int D, int G>
 __device__ __forceinline__ void pv_step(BlockAcc<D, G>& blk, const DecodeSmem<D, G>& sm,
-                                        const uint32_t (&vw)[Cfg<D, G>::NDL], int t0, int w, int lane) {
+                                        const half4_t (&bv)[Cfg<D, G>::NDL], int t0, int w, int lane) {
   using C = Cfg<D, G>;
   half4_t ph[C::NQ], pl[C::NQ];
 #pragma unroll
@@ -158,9 +164,6 @@ __device__ __forceinline__ void pv_step(BlockAcc<D, G>& blk, const DecodeSmem<D,
     ph[quad] = pr[0];
     pl[quad] = pr[1];
   }
-  half4_t bv[C::NDL];
-#pragma unroll
-  for (int ps = 0; ps < C::NDL; ++ps) bv[ps] = codes_to_half4(vw[ps]);  // exact codes: no offset to cancel later
 #pragma unroll
   for (int quad = 0; quad < C::NQ; ++quad)
 #pragma unroll
@@ -196,25 +199,26 @@ __device__ __forceinline__ void fold_block(WaveState<D, G>& st, const BlockAcc<D
       }
 }
 
-// Logit sums of the lane's K row (D/16 chunks of 16 int8 codes, biased) for every query row.
-template <int D, int G>
-__device__ __forceinline__ void qk_codes(const uint4 (&kr)[D / 16], const DecodeSmem<D, G>& sm, int lane,
-                                         float4_t (&s)[Cfg<D, G>::NQ]) {
+// Logit sums of the lane's K row (D/E chunks of E elements, biased operands) for every query row.
+template <int D, int G, int BITS>
+__device__ __forceinline__ void qk_codes(const uint4 (&kr)[D / Fmt<BITS>::kElems], const DecodeSmem<D, G>& sm,
+                                         int lane, float4_t (&s)[Cfg<D, G>::NQ]) {
   using C = Cfg<D, G>;
+  using F = Fmt<BITS>;
   asm volatile("" ::: "memory");  // re-read the query operand from LDS for every unit
   float4_t s2[C::NQ];  // second accumulator chain: halves the dependent MFMA chain
 #pragma unroll
   for (int quad = 0; quad < C::NQ; ++quad) s[quad] = s2[quad] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int ch = 0; ch < D / 16; ++ch) {
+  for (int ch = 0; ch < D / F::kElems; ++ch) {
     asm volatile("" ::: "memory");  // bound how far the query-operand LDS reads are hoisted
 #pragma unroll
-    for (int wd = 0; wd < 4; ++wd) {
-      const half4_t b = codes_to_biased_half4(word_of(kr[ch], wd));
-      const int k0 = ch * 16 + wd * 4;
+    for (int st = 0; st < F::kSteps; ++st) {
+      const half4_t b = chunk_operand<BITS, F::kBiasedQK>(kr[ch], st);
+      const int k0 = ch * F::kElems + st * 4;
 #pragma unroll
       for (int quad = 0; quad < C::NQ; ++quad) {
-        if (wd & 1) s2[quad] = mfma_qk(q_operand(sm, quad, lane, k0), b, s2[quad]);
+        if (st & 1) s2[quad] = mfma_qk(q_operand(sm, quad, lane, k0), b, s2[quad]);
         else s[quad] = mfma_qk(q_operand(sm, quad, lane, k0), b, s[quad]);
       }
     }
@@ -229,10 +233,11 @@ __device__ __forceinline__ void qk_codes(const uint4 (&kr)[D / 16], const Decode
 // has been turned into MFMA operands, its registers receive chunk ch of the
 // next unit's K tile (rn; an empty descriptor when there is none), so the next
 // tile is requested chunk by chunk while this one is consumed.
-template <int D, int G>
-__device__ __forceinline__ void qk_codes_refill(uint4 (&kr)[D / 16], const DecodeSmem<D, G>& sm, int lane,
-                                                float4_t (&s)[Cfg<D, G>::NQ], __amdgpu_buffer_rsrc_t rn) {
+template <int D, int G, int BITS>
+__device__ __forceinline__ void qk_codes_refill(uint4 (&kr)[D / Fmt<BITS>::kElems], const DecodeSmem<D, G>& sm,
+                                                int lane, float4_t (&s)[Cfg<D, G>::NQ], __amdgpu_buffer_rsrc_t rn) {
   using C = Cfg<D, G>;
+  using F = Fmt<BITS>;
   constexpr int S = kBlockSize;
   const uint32_t lo = static_cast<uint32_t>(lane) * 16u;
   asm volatile("" ::: "memory");
@@ -240,15 +245,15 @@ __device__ __forceinline__ void qk_codes_refill(uint4 (&kr)[D / 16], const Decod
 #pragma unroll
   for (int quad = 0; quad < C::NQ; ++quad) s[quad] = s2[quad] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int ch = 0; ch < D / 16; ++ch) {
+  for (int ch = 0; ch < D / F::kElems; ++ch) {
     asm volatile("" ::: "memory");
 #pragma unroll
-    for (int wd = 0; wd < 4; ++wd) {
-      const half4_t b = codes_to_biased_half4(word_of(kr[ch], wd));
-      const int k0 = ch * 16 + wd * 4;
+    for (int st = 0; st < F::kSteps; ++st) {
+      const half4_t b = chunk_operand<BITS, F::kBiasedQK>(kr[ch], st);
+      const int k0 = ch * F::kElems + st * 4;
 #pragma unroll
       for (int quad = 0; quad < C::NQ; ++quad) {
-        if (wd & 1) s2[quad] = mfma_qk(q_operand(sm, quad, lane, k0), b, s2[quad]);
+        if (st & 1) s2[quad] = mfma_qk(q_operand(sm, quad, lane, k0), b, s2[quad]);
         else s[quad] = mfma_qk(q_operand(sm, quad, lane, k0), b, s[quad]);
       }
     }
@@ -259,28 +264,31 @@ __device__ __forceinline__ void qk_codes_refill(uint4 (&kr)[D / 16], const Decod
   asm volatile("" ::: "memory");
 }
 
-// PV of a dense unit with progressive refill: once the last word of a 16-token
-// column chunk has been used, its registers receive the same chunk of the next
-// unit's V tile.
-template <int D, int G>
+// PV of a dense unit with progressive refill: once the last operand of a column
+// chunk (E tokens of the lane's channel) has been used, its registers receive
+// the same chunk of the next unit's V tile.
+template <int D, int G, int BITS>
 __device__ __forceinline__ void pv_dense_refill(BlockAcc<D, G>& blk, const DecodeSmem<D, G>& sm,
-                                                uint4 (&vr)[Cfg<D, G>::NDL][4], int w, int lane,
-                                                __amdgpu_buffer_rsrc_t rn) {
+                                                uint4 (&vr)[Cfg<D, G>::NDL][64 / Fmt<BITS>::kElems], int w,
+                                                int lane, __amdgpu_buffer_rsrc_t rn) {
   using C = Cfg<D, G>;
+  using F = Fmt<BITS>;
   constexpr int S = kBlockSize;
+  constexpr int E = F::kElems;
+  constexpr int TB = F::template tile_bytes<D>();
   const uint32_t lo = static_cast<uint32_t>(lane) * 16u;
   zero_blk<D, G>(blk);
 #pragma unroll
-  for (int t0 = 0; t0 < 64; t0 += 4) {
+  for (int t0 = 0; t0 < S; t0 += 4) {
     asm volatile("" ::: "memory");
-    uint32_t vw[C::NDL];
+    half4_t bv[C::NDL];
 #pragma unroll
-    for (int ps = 0; ps < C::NDL; ++ps) vw[ps] = word_of(vr[ps][t0 / 16], (t0 % 16) / 4);
-    pv_step<D, G>(blk, sm, vw, t0, w, lane);
-    if (t0 % 16 == 12) {
+    for (int ps = 0; ps < C::NDL; ++ps) bv[ps] = chunk_operand<BITS, false>(vr[ps][t0 / E], (t0 % E) / 4);
+    pv_step<D, G>(blk, sm, bv, t0, w, lane);
+    if (t0 % E == E - 4) {
 #pragma unroll
       for (int ps = 0; ps < C::NDL; ++ps)
-        vr[ps][t0 / 16] = load_stream_buf(rn, lo + S * D + ((t0 / 16) * D + 64 * ps) * 16);
+        vr[ps][t0 / E] = load_stream_buf(rn, lo + TB + ((t0 / E) * D + 64 * ps) * 16);
     }
   }
   asm volatile("" ::: "memory");
@@ -296,21 +304,23 @@ __device__ __forceinline__ float2 load_scales(__amdgpu_buffer_rsrc_t rs, int phy
 }
 
 // One dense unit's tiles in registers.
-template <int D>
+template <int D, int BITS>
 struct Tiles {
-  uint4 kr[D / 16];     // lane t: chunk ch = codes 16ch..16ch+15 of token t
-  uint4 vr[D / 64][4];  // lane c: [pass][tc] = tokens 16tc..16tc+15 of channel 64 pass + lane
+  static constexpr int E = Fmt<BITS>::kElems;
+  uint4 kr[D / E];         // lane t: chunk ch = elements E ch .. E ch + E - 1 of token t
+  uint4 vr[D / 64][64 / E];  // lane c: [pass][vc] = tokens E vc .. E vc + E - 1 of channel 64 pass + lane
 };
 
-// Buffer resource over one block's K and V tiles of one kv-head (2*S*D
+// Buffer resource over one block's K and V tiles of one kv-head (2 tile_bytes
 // contiguous bytes, K first): the tile loads take a uniform descriptor plus a
 // 32-bit lane offset, and the hardware range check returns 0 past the end.
 // phys < 0 gives an empty descriptor: the loads return 0 and touch no memory.
-template <int D>
+template <int D, int BITS>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const CacheView& c, int phys, int h) {
+  constexpr int TB = Fmt<BITS>::template tile_bytes<D>();
   const bool ok = phys >= 0;
-  const int8_t* base = c.cold + tile_offset(ok ? phys : 0, h, 0, c.H, kBlockSize, D);
-  return make_rsrc(base, ok ? 2u * kBlockSize * D : 0u);
+  const int8_t* base = c.cold + tile_offset(ok ? phys : 0, h, 0, c.H, TB);
+  return make_rsrc(base, ok ? 2u * TB : 0u);
 }
 
 // Descriptor over the whole scales array [num_phys][H][2]: an out-of-range
@@ -319,22 +329,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t scales_rsrc(const CacheView& c
   return make_rsrc(c.scales, static_cast<uint32_t>(c.num_phys) * c.H * 8u);
 }
 
-// Request the K tile (lane t: 16 codes of token t per chunk).
-template <int D>
-__device__ __forceinline__ void issue_k(Tiles<D>& t, __amdgpu_buffer_rsrc_t r, int lane) {
+// Request the K tile (lane t: E elements of token t per chunk).
+template <int D, int BITS>
+__device__ __forceinline__ void issue_k(Tiles<D, BITS>& t, __amdgpu_buffer_rsrc_t r, int lane) {
   constexpr int S = kBlockSize;
   const uint32_t lo = static_cast<uint32_t>(lane) * 16u;
 #pragma unroll
-  for (int ch = 0; ch < D / 16; ++ch) t.kr[ch] = load_stream_buf(r, lo + ch * S * 16);
+  for (int ch = 0; ch < D / Fmt<BITS>::kElems; ++ch) t.kr[ch] = load_stream_buf(r, lo + ch * S * 16);
 }
 
-// Request the two scales (K, V) and the V tile (lane c: 16 tokens of channel c
+// Request the two scales (K, V) and the V tile (lane c: E tokens of channel c
 // per load).  The scales travel with the V tile: they are requested after the
 // previous unit's softmax has used the register pair.
-template <int D>
-__device__ __forceinline__ void issue_v(Tiles<D>& t, float2& sc, __amdgpu_buffer_rsrc_t r,
+template <int D, int BITS>
+__device__ __forceinline__ void issue_v(Tiles<D, BITS>& t, float2& sc, __amdgpu_buffer_rsrc_t r,
                                         __amdgpu_buffer_rsrc_t rs, int phys, int H, int h, int lane) {
-  constexpr int S = kBlockSize;
+  constexpr int E = Fmt<BITS>::kElems;
+  constexpr int TB = Fmt<BITS>::template tile_bytes<D>();
   // per-lane offset (kept out of scalar registers: no wait right after the load); phys < 0 reads 0
   const int so = static_cast<int>(opaque_index(static_cast<uint32_t>((phys * H + h) * 8)));
   // two 32-bit loads (the 64-bit buffer-load builtin can come out as a single dword load)
@@ -345,23 +356,24 @@ __device__ __forceinline__ void issue_v(Tiles<D>& t, float2& sc, __amdgpu_buffer
 #pragma unroll
   for (int ps = 0; ps < D / 64; ++ps)
 #pragma unroll
-    for (int tc = 0; tc < 4; ++tc) t.vr[ps][tc] = load_stream_buf(r, lo + S * D + (tc * D + 64 * ps) * 16);
+    for (int vc = 0; vc < 64 / E; ++vc) t.vr[ps][vc] = load_stream_buf(r, lo + TB + (vc * D + 64 * ps) * 16);
 }
 
-// PV over a dense unit whose value codes are lane-resident: vr[pass][tc] holds
-// tokens 16tc..16tc+15 of channel 64 pass + lane.
-template <int D, int G>
+// PV over a dense unit whose values are lane-resident: vr[pass][vc] holds
+// tokens E vc .. E vc + E - 1 of channel 64 pass + lane.
+template <int D, int G, int BITS>
 __device__ __forceinline__ void pv_dense(BlockAcc<D, G>& blk, const DecodeSmem<D, G>& sm,
-                                         const uint4 (&vr)[Cfg<D, G>::NDL][4], int w, int lane) {
+                                         const uint4 (&vr)[Cfg<D, G>::NDL][64 / Fmt<BITS>::kElems], int w, int lane) {
   using C = Cfg<D, G>;
+  constexpr int E = Fmt<BITS>::kElems;
   zero_blk<D, G>(blk);
 #pragma unroll
   for (int t0 = 0; t0 < 64; t0 += 4) {
     asm volatile("" ::: "memory");  // read the weights 4 tokens at a time (bounds live VGPRs)
-    uint32_t vw[C::NDL];
+    half4_t bv[C::NDL];
 #pragma unroll
-    for (int ps = 0; ps < C::NDL; ++ps) vw[ps] = word_of(vr[ps][t0 / 16], (t0 % 16) / 4);
-    pv_step<D, G>(blk, sm, vw, t0, w, lane);
+    for (int ps = 0; ps < C::NDL; ++ps) bv[ps] = chunk_operand<BITS, false>(vr[ps][t0 / E], (t0 % E) / 4);
+    pv_step<D, G>(blk, sm, bv, t0, w, lane);
   }
   asm volatile("" ::: "memory");
 }
@@ -369,9 +381,9 @@ __device__ __forceinline__ void pv_dense(BlockAcc<D, G>& blk, const DecodeSmem<D
 // The walk itself.  K and V of the unit after the current one are requested
 // while the current one is being computed.  t/phys_u/sc hold the first unit
 // (already requested by the caller), hb the header batch of walk units 0..63.
-template <int D, int G>
+template <int D, int G, int BITS>
 __device__ void dense_units(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const DecodeParams& p, int b, int h, int split,
-                            int units, int n_cold, int w, int lane, Tiles<D>& t, int phys_u, float2 sc, int hb) {
+                            int units, int n_cold, int w, int lane, Tiles<D, BITS>& t, int phys_u, float2 sc, int hb) {
   using C = Cfg<D, G>;
   constexpr int S = kBlockSize;
   const CacheView& c = p.c;
@@ -403,14 +415,14 @@ __device__ void dense_units(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const Dec
   int phys_n = un >= 0 ? phys_of(k + 1) : -1;
   while (u >= 0) {
     const int nv = phys_u >= 0 ? min(S, n_cold - u * S) : 0;
-    const __amdgpu_buffer_rsrc_t rn = tile_rsrc<D>(c, phys_n, h);  // empty when there is no next unit
+    const __amdgpu_buffer_rsrc_t rn = tile_rsrc<D, BITS>(c, phys_n, h);  // empty when there is no next unit
     float4_t s[C::NQ];
-    qk_codes_refill<D, G>(t.kr, sm, lane, s, rn);
+    qk_codes_refill<D, G, BITS>(t.kr, sm, lane, s, rn);
     float alpha[C::NG], coef[C::NG];
     softmax_unit<D, G, false>(st, sm, s, lane < nv, sc.x * p.qscale, 1.f, sc.y, alpha, coef, w, lane);
     sc = load_scales(rs, phys_n, c.H, h);  // the scale pair is free once the softmax has used it
     BlockAcc<D, G> blk;
-    pv_dense_refill<D, G>(blk, sm, t.vr, w, lane, rn);
+    pv_dense_refill<D, G, BITS>(blk, sm, t.vr, w, lane, rn);
     fold_block<D, G>(st, blk, alpha, coef);
     wave_lds_sync();  // this unit's weight reads are done before the next unit's writes
     u = un;
@@ -436,9 +448,9 @@ __device__ void dense_units(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const Dec
 // t/phys_u/sc hold the first unit (requested by the caller), un/hn the next
 // unit and its pending header load (un < 0: none), cl the pending claim for
 // the unit after it (valid when un >= 0).
-template <int D, int G>
+template <int D, int G, int BITS>
 __device__ void dense_units_claim(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const DecodeParams& p, int b, int h,
-                                  int bh, int units, int n_cold, int w, int lane, Tiles<D>& t, int u, int phys_u,
+                                  int bh, int units, int n_cold, int w, int lane, Tiles<D, BITS>& t, int u, int phys_u,
                                   float2 sc, int un, int hn, unsigned cl) {
   using C = Cfg<D, G>;
   constexpr int S = kBlockSize;
@@ -449,9 +461,9 @@ __device__ void dense_units_claim(WaveState<D, G>& st, DecodeSmem<D, G>& sm, con
   int phys_n = un >= 0 ? header_phys(c, hn) : -1;
   while (u >= 0) {
     const int nv = phys_u >= 0 ? min(S, n_cold - u * S) : 0;
-    const __amdgpu_buffer_rsrc_t rn = tile_rsrc<D>(c, phys_n, h);  // empty when there is no next unit
+    const __amdgpu_buffer_rsrc_t rn = tile_rsrc<D, BITS>(c, phys_n, h);  // empty when there is no next unit
     float4_t s[C::NQ];
-    qk_codes_refill<D, G>(t.kr, sm, lane, s, rn);
+    qk_codes_refill<D, G, BITS>(t.kr, sm, lane, s, rn);
     float alpha[C::NG], coef[C::NG];
     softmax_unit<D, G, false>(st, sm, s, lane < nv, sc.x * p.qscale, 1.f, sc.y, alpha, coef, w, lane);
     sc = load_scales(rs, phys_n, c.H, h);
@@ -463,7 +475,7 @@ __device__ void dense_units_claim(WaveState<D, G>& st, DecodeSmem<D, G>& sm, con
       else hn2 = header_load(c, b, un2);
     }
     BlockAcc<D, G> blk;
-    pv_dense_refill<D, G>(blk, sm, t.vr, w, lane, rn);
+    pv_dense_refill<D, G, BITS>(blk, sm, t.vr, w, lane, rn);
     fold_block<D, G>(st, blk, alpha, coef);
     wave_lds_sync();
     u = un;
@@ -493,13 +505,50 @@ __device__ __forceinline__ int sel_entry(const int32_t* sel_bh, int k_sel, int u
   return (lane < kSparseUnit && e < k_sel) ? sel_bh[e] : -1;
 }
 
+// Value element of token tt (row of a V tile) at channel c, as the bits of the tile format: an
+// 8-bit code byte, a 4-bit offset-binary nibble or an fp16 value (b8/b16 buffer loads; an empty
+// descriptor reads 0).
+template <int D, int BITS>
+__device__ __forceinline__ uint32_t v_element(__amdgpu_buffer_rsrc_t r, int tt, int c) {
+  using F = Fmt<BITS>;
+  constexpr int TB = F::template tile_bytes<D>();
+  constexpr int E = F::kElems;
+  const int chunk = TB + ((tt / E) * D + c) * 16;
+  if constexpr (BITS == 8) return __builtin_amdgcn_raw_buffer_load_b8(r, chunk + tt % E, 0, 0);
+  else if constexpr (BITS == 4) return __builtin_amdgcn_raw_buffer_load_b8(r, chunk + (tt % E) / 2, 0, 0);
+  else return __builtin_amdgcn_raw_buffer_load_b16(r, chunk + (tt % E) * 2, 0, 0);
+}
+
+// Exact PV operand of four gathered tokens from their value elements (v_element of each, and for
+// 4-bit tiles the token index, whose parity names the nibble).
+template <int BITS>
+__device__ __forceinline__ half4_t gathered_operand(const uint32_t (&e)[4], const int (&tt)[4]) {
+  if constexpr (BITS == 8) {
+    return codes_to_half4(e[0] | (e[1] << 8) | (e[2] << 16) | (e[3] << 24));
+  } else if constexpr (BITS == 4) {
+    uint32_t n[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) n[i] = (e[i] >> (4 * (tt[i] & 1))) & 0xFu;
+    const half2_t off = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
+    const half2_t a = __builtin_bit_cast(half2_t, 0x64006400u | n[0] | (n[1] << 16)) - off;
+    const half2_t b = __builtin_bit_cast(half2_t, 0x64006400u | n[2] | (n[3] << 16)) - off;
+    return half4_t{a.x, a.y, b.x, b.y};
+  } else {
+    const half2_t a = __builtin_bit_cast(half2_t, e[0] | (e[1] << 16));
+    const half2_t b = __builtin_bit_cast(half2_t, e[2] | (e[3] << 16));
+    return half4_t{a.x, a.y, b.x, b.y};
+  }
+}
+
 // idx: the lane's selection entry (sel_entry of this unit).
-template <int D, int G>
+template <int D, int G, int BITS>
 __device__ void gather_unit(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const CacheView& c, int idx, int b, int h,
                             int n_cold, float qscale, int w, int lane) {
   using C = Cfg<D, G>;
+  using F = Fmt<BITS>;
   constexpr int S = kBlockSize;
   constexpr int TU = kSparseUnit;
+  constexpr int TB = F::template tile_bytes<D>();
   static_assert(TU % 4 == 0 && TU <= 64, "whole PV steps of 4 tokens, one token per lane");
   int phys = -1;
   if (idx >= 0 && idx < n_cold) {
@@ -512,27 +561,27 @@ __device__ void gather_unit(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const Cac
   // K row and scales of the lane's token; a masked lane reads block 0 (present: some token is
   // valid) and its values are discarded
   const int pl = valid ? phys : 0;
-  const uint4* tk = reinterpret_cast<const uint4*>(c.cold + tile_offset(pl, h, 0, c.H, S, D));
-  uint4 kr[D / 16];
+  const uint4* tk = reinterpret_cast<const uint4*>(c.cold + tile_offset(pl, h, 0, c.H, TB));
+  uint4 kr[D / F::kElems];
 #pragma unroll
-  for (int ch = 0; ch < D / 16; ++ch) kr[ch] = tk[ch * S + t];
+  for (int ch = 0; ch < D / F::kElems; ++ch) kr[ch] = tk[ch * S + t];
   const float2 scl = *reinterpret_cast<const float2*>(c.scales + (static_cast<size_t>(pl) * c.H + h) * 2);
-  // value codes: token k of the unit at channel 64 ps + lane
+  // value elements: token k of the unit at channel 64 ps + lane
   const int pm = valid ? phys : -1;
   uint32_t vb[TU][C::NDL];
+  int tts[TU];
 #pragma unroll
   for (int k = 0; k < TU; ++k) {
     const int pk = __builtin_amdgcn_readlane(pm, k);
     const int tt = __builtin_amdgcn_readlane(t, k);
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc<D>(c, pk, h);  // empty for a masked token: reads 0
-    const int o = S * D + (tt / 16) * D * 16 + tt % 16;
+    tts[k] = tt;
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc<D, BITS>(c, pk, h);  // empty for a masked token: reads 0
 #pragma unroll
-    for (int ps = 0; ps < C::NDL; ++ps)
-      vb[k][ps] = __builtin_amdgcn_raw_buffer_load_b8(r, o + (64 * ps + lane) * 16, 0, 0);
+    for (int ps = 0; ps < C::NDL; ++ps) vb[k][ps] = v_element<D, BITS>(r, tt, 64 * ps + lane);
   }
   const float2 sc = valid ? scl : make_float2(0.f, 0.f);
   float4_t s[C::NQ];
-  qk_codes<D, G>(kr, sm, lane, s);
+  qk_codes<D, G, BITS>(kr, sm, lane, s);
   const float vmax = wave_max_dpp(sc.y);
   const float vw = vmax > 0.f ? sc.y * __builtin_amdgcn_rcpf(vmax) : 0.f;
   float alpha[C::NG], coef[C::NG];
@@ -541,11 +590,14 @@ __device__ void gather_unit(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const Cac
   zero_blk<D, G>(blk);
 #pragma unroll
   for (int t0 = 0; t0 < TU; t0 += 4) {
-    uint32_t vw4[C::NDL];
+    half4_t bv[C::NDL];
+    const int tq[4] = {tts[t0], tts[t0 + 1], tts[t0 + 2], tts[t0 + 3]};
 #pragma unroll
-    for (int ps = 0; ps < C::NDL; ++ps)
-      vw4[ps] = vb[t0][ps] | (vb[t0 + 1][ps] << 8) | (vb[t0 + 2][ps] << 16) | (vb[t0 + 3][ps] << 24);
-    pv_step<D, G>(blk, sm, vw4, t0, w, lane);
+    for (int ps = 0; ps < C::NDL; ++ps) {
+      const uint32_t e[4] = {vb[t0][ps], vb[t0 + 1][ps], vb[t0 + 2][ps], vb[t0 + 3][ps]};
+      bv[ps] = gathered_operand<BITS>(e, tq);
+    }
+    pv_step<D, G>(blk, sm, bv, t0, w, lane);
   }
   fold_block<D, G>(st, blk, alpha, coef);
   wave_lds_sync();
@@ -589,7 +641,7 @@ __device__ __forceinline__ void copy_query(const _Float16* qg, _Float16 (*qh)[4]
 }
 
 // ---- cold split: stream its units, merge the 4 waves, write the partial
-template <int D, int G, bool SPARSE, bool FUSED, bool CLAIM>
+template <int D, int G, int BITS, bool SPARSE, bool FUSED, bool CLAIM>
 __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, int h, int bh, int split) {
   using C = Cfg<D, G>;
   constexpr int S = kBlockSize;
@@ -616,7 +668,7 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
   // needed only after the barrier: kept in a vector register, waited for there (issued before the
   // tiles, so that wait does not include them)
   const int n_seq_lane = c.seq_len[opaque_index(b)];
-  Tiles<D> t0;
+  Tiles<D, BITS> t0;
   float2 sc0 = make_float2(0.f, 0.f);
   int phys0 = -1, hb = -1;
   const int32_t* sel_bh = SPARSE ? p.sel + static_cast<size_t>(bh) * p.k_sel : nullptr;
@@ -629,9 +681,9 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
     hb = header_load(c, b, split * kWaves + w);
     cl0 = claim_issue(p.work + static_cast<size_t>(bh) * kClaimStride, lane);
     phys0 = header_phys(c, hb);
-    const __amdgpu_buffer_rsrc_t r0 = tile_rsrc<D>(c, phys0, h);
-    issue_k<D>(t0, r0, lane);
-    issue_v<D>(t0, sc0, r0, scales_rsrc(c), phys0, c.H, h, lane);
+    const __amdgpu_buffer_rsrc_t r0 = tile_rsrc<D, BITS>(c, phys0, h);
+    issue_k<D, BITS>(t0, r0, lane);
+    issue_v<D, BITS>(t0, sc0, r0, scales_rsrc(c), phys0, c.H, h, lane);
   } else {
     const uint64_t t_entry = __builtin_amdgcn_s_memrealtime();
     hb = header_batch(c, b, 0, split, p.nsplit, p.units_per_split, w, lane);
@@ -644,9 +696,9 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
       const uint64_t until = t_entry + kHoldTicks;
       while (__builtin_amdgcn_s_memrealtime() < until) __builtin_amdgcn_s_sleep(1);
     }
-    const __amdgpu_buffer_rsrc_t r0 = tile_rsrc<D>(c, phys0, h);
-    issue_k<D>(t0, r0, lane);
-    issue_v<D>(t0, sc0, r0, scales_rsrc(c), phys0, c.H, h, lane);
+    const __amdgpu_buffer_rsrc_t r0 = tile_rsrc<D, BITS>(c, phys0, h);
+    issue_k<D, BITS>(t0, r0, lane);
+    issue_v<D, BITS>(t0, sc0, r0, scales_rsrc(c), phys0, c.H, h, lane);
   }
 #pragma unroll
   for (int k = 0; k < QPT; ++k) {
@@ -668,7 +720,7 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
     float qs = 0.f;
 #pragma unroll
     for (int k = lane; k < D; k += 64) qs += static_cast<float>(sm.qh[g / 4][g % 4][k]);
-    st.qb[g] = kCodeBias * wave_sum_dpp(qs);
+    st.qb[g] = Fmt<BITS>::kBias * wave_sum_dpp(qs);
   }
 #pragma unroll
   for (int quad = 0; quad < C::NQ; ++quad)
@@ -681,7 +733,7 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
       const int u_end = min(units, (run + 1) * CU);
       for (int u = run * CU + w; u < u_end; u += kWaves) {
         const int idx = (run == split && u == run * CU + w) ? sel0 : sel_entry(sel_bh, p.k_sel, u, lane);
-        gather_unit<D, G>(st, sm, c, idx, b, h, sg.n_cold, p.qscale, w, lane);
+        gather_unit<D, G, BITS>(st, sm, c, idx, b, h, sg.n_cold, p.qscale, w, lane);
       }
     }
   } else if constexpr (CLAIM) {
@@ -697,10 +749,10 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
         cl = claim_issue(p.work + static_cast<size_t>(bh) * kClaimStride, lane);
       }
     }
-    dense_units_claim<D, G>(st, sm, p, b, h, bh, units, sg.n_cold, w, lane, t0, u0 < units ? u0 : -1, phys0, sc0,
+    dense_units_claim<D, G, BITS>(st, sm, p, b, h, bh, units, sg.n_cold, w, lane, t0, u0 < units ? u0 : -1, phys0, sc0,
                             un, hn, cl);
   } else {
-    dense_units<D, G>(st, sm, p, b, h, split, units, sg.n_cold, w, lane, t0, phys0, sc0, hb);
+    dense_units<D, G, BITS>(st, sm, p, b, h, split, units, sg.n_cold, w, lane, t0, phys0, sc0, hb);
   }
   // merge the 4 waves: lane holds out[4quad + r][64 pass + lane]
 #pragma unroll
@@ -884,26 +936,32 @@ __device__ void hot_window_split(const DecodeParams& p, HotSmem<D, G>& hm, int b
   }
 }
 
-template <int D, int G>
+template <int D, int G, int BITS>
 struct AppendSmem {
-  static constexpr int KROW = D + 16;          // K stage row: one token's channels (padded)
-  static constexpr int VROW = kBlockSize + 16; // V stage row: one channel's tokens (padded)
-  DecodeSmem<D, G> unit;                       // tail block jt, attended by wave 0
-  alignas(16) int8_t stage_k[kBlockSize * KROW];  // its K codes, [token][channel]
-  alignas(16) int8_t stage_v[D * VROW];           // its V codes, [channel][token] (the tile's order)
+  static constexpr int EB = BITS == 0 ? 2 : 1;       // stage bytes per element: one code, or one fp16 value
+  static constexpr int KROW = D * EB + 16;           // K stage row: one token's channels (padded)
+  static constexpr int VROW = kBlockSize * EB + 16;  // V stage row: one channel's tokens (padded)
+  DecodeSmem<D, G> unit;                             // tail block jt, attended by wave 0
+  alignas(16) int8_t stage_k[kBlockSize * KROW];     // its K codes / values, [token][channel]
+  alignas(16) int8_t stage_v[D * VROW];              // its V codes / values, [channel][token]
   float red[4][kWaves];
 };
 
-template <int D, int G>
-__device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G>& am, int b, int h, int bh) {
+template <int D, int G, int BITS>
+__device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>& am, int b, int h, int bh) {
   __builtin_amdgcn_s_setprio(3);  // the append's coding and its block's attention sit on the step's critical path
   using C = Cfg<D, G>;
+  using F = Fmt<BITS>;
+  using AS = AppendSmem<D, G, BITS>;
   constexpr int S = kBlockSize;
   constexpr int TPT = kThreads / S;     // threads per token row
   constexpr int CPT = D / TPT;          // channels per thread
   constexpr int NV = CPT / 8;           // 16-byte vectors per thread and row
-  constexpr int KROW = AppendSmem<D, G>::KROW;
-  constexpr int VROW = AppendSmem<D, G>::VROW;
+  constexpr int KROW = AS::KROW;
+  constexpr int VROW = AS::VROW;
+  constexpr int EB = AS::EB;
+  constexpr int E = F::kElems;
+  constexpr int TB = F::template tile_bytes<D>();
   constexpr int VR = D / 8;             // 16-byte vectors per fp16 row
   constexpr int NG = C::NG;
   const CacheView& c = p.c;
@@ -976,19 +1034,40 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G>& am, i
   // ---- codes of block jt (as the standalone append codes them).  Every row is coded into the
   // stage for the attention below: with an unchanged maximum the old rows' codes are the stored
   // ones (same FP16 values, same scale), and only row ts is written to memory; otherwise the
-  // whole block is.  V codes are staged channel-major, as the tile stores them.
+  // whole block is.  V codes are staged channel-major, as the tile stores them.  fp16 tiles stage
+  // the values themselves (scale 1): the whole tile is written when the block opens (ts = 0),
+  // afterwards only row ts.
   float scl[2] = {0.f, 0.f};  // the block's scales after the append
   bool whole[2] = {false, false};
   if (phys >= 0) {
 #pragma unroll
     for (int kv = 0; kv < 2; ++kv) {
       const float m_old = mx[kv], m_new = mx[2 + kv];
-      int8_t* tile = c.cold + tile_offset(phys, h, kv, H, S, D);
-      whole[kv] = !(ts > 0 && m_new <= m_old);
-      const float sc = (whole[kv] ? fmaxf(m_old, m_new) : m_old) / 127.0f;
-      scl[kv] = sc;
-      const float rsc = __builtin_amdgcn_rcpf(sc);
-      {
+      int8_t* tile = c.cold + tile_offset(phys, h, kv, H, TB);
+      if constexpr (BITS == 0) {
+        whole[kv] = ts == 0;
+        scl[kv] = 1.f;
+        uint32_t* srow = reinterpret_cast<uint32_t*>(am.stage_k + t * KROW + part * CPT * 2);
+        if (kv == 0) {
+#pragma unroll
+          for (int v = 0; v < NV; ++v)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) srow[4 * v + i] = x[0][v][i];
+        } else {
+#pragma unroll
+          for (int v = 0; v < NV; ++v)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int cc = part * CPT + 8 * v + 2 * i;
+              *reinterpret_cast<uint16_t*>(am.stage_v + cc * VROW + 2 * t) = static_cast<uint16_t>(x[1][v][i]);
+              *reinterpret_cast<uint16_t*>(am.stage_v + (cc + 1) * VROW + 2 * t) = static_cast<uint16_t>(x[1][v][i] >> 16);
+            }
+        }
+      } else {
+        whole[kv] = !(ts > 0 && m_new <= m_old);
+        const float sc = (whole[kv] ? fmaxf(m_old, m_new) : m_old) / static_cast<float>(F::kLimit);
+        scl[kv] = sc;
+        const float rsc = __builtin_amdgcn_rcpf(sc);
         uint32_t qw[CPT / 4];
 #pragma unroll
         for (int i = 0; i < CPT / 4; ++i) {
@@ -998,7 +1077,7 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G>& am, i
             const int e = 4 * i + k;
             const uint32_t wd = x[kv][e / 8][(e % 8) / 2];
             const float xv = (e & 1) ? half_hi(wd) : half_lo(wd);
-            const float qv = sc > 0.f ? quant_code(xv, sc, rsc) : 0.f;
+            const float qv = sc > 0.f ? quant_code<F::kLimit>(xv, sc, rsc) : 0.f;
             packed |= (static_cast<uint32_t>(static_cast<int>(qv)) & 0xffu) << (8 * k);
           }
           qw[i] = packed;
@@ -1012,7 +1091,7 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G>& am, i
           for (int i = 0; i < CPT; ++i)
             am.stage_v[(part * CPT + i) * VROW + t] = static_cast<int8_t>(qw[i / 4] >> (8 * (i % 4)));
         }
-        if (!whole[kv] && t == ts) {  // only row ts changes: write it in place
+        if (BITS == 8 && !whole[kv] && t == ts) {  // only row ts changes: write it in place
           if (kv == 0) {
 #pragma unroll
             for (int ch = 0; ch < CPT / 16; ++ch)
@@ -1029,17 +1108,36 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G>& am, i
     __syncthreads();  // stage complete
 #pragma unroll
     for (int kv = 0; kv < 2; ++kv) {
-      if (!whole[kv]) continue;
-      int8_t* tile = c.cold + tile_offset(phys, h, kv, H, S, D);
-      constexpr int NVEC = S * D / 16;
+      int8_t* tile = c.cold + tile_offset(phys, h, kv, H, TB);
+      if (!whole[kv]) {
+        if constexpr (BITS != 8) {
+          // only row ts changes: its K chunks, and per channel the V bytes that hold it (4-bit: the
+          // byte shared with row ts ^ 1, rewritten from the stage)
+          if (kv == 0) {
+            if (tid < D / E)
+              reinterpret_cast<uint4*>(tile)[tid * S + ts] = chunk_from_stage<BITS>(am.stage_k + ts * KROW + tid * E * EB);
+          } else if (tid < D) {
+            const int8_t* col = am.stage_v + tid * VROW;
+            int8_t* chunk = tile + ((ts / E) * D + tid) * 16;
+            if constexpr (BITS == 4) {
+              const int t2 = ts & ~1;
+              chunk[(ts % E) / 2] = static_cast<int8_t>(((col[t2] & 0xF) ^ 8) | (((col[t2 + 1] & 0xF) ^ 8) << 4));
+            } else {
+              *reinterpret_cast<uint16_t*>(chunk + (ts % E) * 2) = *reinterpret_cast<const uint16_t*>(col + 2 * ts);
+            }
+          }
+        }
+        continue;
+      }
+      constexpr int NVEC = TB / 16;
       for (int vi = tid; vi < NVEC; vi += kThreads) {
         uint4 out;
         if (kv == 0) {
-          const int dc = vi / S, tt = vi % S;
-          out = *reinterpret_cast<const uint4*>(am.stage_k + tt * KROW + dc * 16);
+          const int kc = vi / S, tt = vi % S;
+          out = chunk_from_stage<BITS>(am.stage_k + tt * KROW + kc * E * EB);
         } else {
-          const int tc = vi / D, cc = vi % D;
-          out = *reinterpret_cast<const uint4*>(am.stage_v + cc * VROW + tc * 16);
+          const int vc = vi / D, cc = vi % D;
+          out = chunk_from_stage<BITS>(am.stage_v + cc * VROW + vc * E * EB);
         }
         reinterpret_cast<uint4*>(tile)[vi] = out;
       }
@@ -1078,15 +1176,15 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G>& am, i
 #pragma unroll
       for (int ps2 = 0; ps2 < C::NDL; ++ps2) uacc[quad][ps2] = float4_t{0.f, 0.f, 0.f, 0.f};
     if (phys >= 0) {
-      // tile registers: K (lane = token) and V (lane = channel), from the codes in LDS
-      Tiles<D> tl;
+      // tile registers: K (lane = token) and V (lane = channel), from the stage
+      Tiles<D, BITS> tl;
 #pragma unroll
-      for (int ch = 0; ch < D / 16; ++ch) tl.kr[ch] = *reinterpret_cast<const uint4*>(am.stage_k + lane * KROW + ch * 16);
+      for (int ch = 0; ch < D / E; ++ch) tl.kr[ch] = chunk_from_stage<BITS>(am.stage_k + lane * KROW + ch * E * EB);
 #pragma unroll
       for (int ps2 = 0; ps2 < C::NDL; ++ps2)
 #pragma unroll
-        for (int tc = 0; tc < 4; ++tc)
-          tl.vr[ps2][tc] = *reinterpret_cast<const uint4*>(am.stage_v + (64 * ps2 + lane) * VROW + tc * 16);
+        for (int vc = 0; vc < 64 / E; ++vc)
+          tl.vr[ps2][vc] = chunk_from_stage<BITS>(am.stage_v + (64 * ps2 + lane) * VROW + vc * E * EB);
       WaveState<D, G> st;
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
@@ -1095,18 +1193,18 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G>& am, i
         float qs = 0.f;
 #pragma unroll
         for (int k = lane; k < D; k += 64) qs += static_cast<float>(am.unit.qh[g / 4][g % 4][k]);
-        st.qb[g] = kCodeBias * wave_sum_dpp(qs);
+        st.qb[g] = F::kBias * wave_sum_dpp(qs);
       }
 #pragma unroll
       for (int quad = 0; quad < C::NQ; ++quad)
 #pragma unroll
         for (int ps2 = 0; ps2 < C::NDL; ++ps2) st.acc[quad][ps2] = float4_t{0.f, 0.f, 0.f, 0.f};
       float4_t sq[C::NQ];
-      qk_codes<D, G>(tl.kr, am.unit, lane, sq);
+      qk_codes<D, G, BITS>(tl.kr, am.unit, lane, sq);
       float alpha[NG], coef[NG];
       softmax_unit<D, G, false>(st, am.unit, sq, lane <= ts, scl[0] * p.qscale, 1.f, scl[1], alpha, coef, 0, lane);
       BlockAcc<D, G> blk;
-      pv_dense<D, G>(blk, am.unit, tl.vr, 0, lane);
+      pv_dense<D, G, BITS>(blk, am.unit, tl.vr, 0, lane);
       fold_block<D, G>(st, blk, alpha, coef);
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
@@ -1149,9 +1247,9 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G>& am, i
 // the workspace, which the merging workgroup resets to zero.  The merge runs
 // online over groups of kMergeChunk partials whose loads are all in flight
 // together; thread i owns two adjacent output columns of one query head.
-template <int D, int G, bool SPARSE, bool FUSED, bool CLAIM>
+template <int D, int G, int BITS, bool SPARSE, bool FUSED, bool CLAIM>
 __device__ __forceinline__ void decode_body(const DecodeParams& p, const WgCoord wg) {
-  using AppendPart = typename std::conditional<FUSED, AppendSmem<D, G>, DecodeSmem<D, G>>::type;
+  using AppendPart = typename std::conditional<FUSED, AppendSmem<D, G, BITS>, DecodeSmem<D, G>>::type;
   __shared__ union Smem {
     DecodeSmem<D, G> cold;
     HotSmem<D, G> hot;
@@ -1165,10 +1263,10 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, const WgCoord
   const int bh = b * c.H + h;
   const int tid = threadIdx.x;
   if (split < p.nsplit) {
-    cold_split<D, G, SPARSE, FUSED, CLAIM>(p, sm.cold, b, h, bh, split);
+    cold_split<D, G, BITS, SPARSE, FUSED, CLAIM>(p, sm.cold, b, h, bh, split);
   } else if constexpr (FUSED) {
     if (split == p.nsplit) hot_window_split<D, G>(p, sm.hot, b, h, bh);
-    else append_unit_split<D, G>(p, sm.app, b, h, bh);
+    else append_unit_split<D, G, BITS>(p, sm.app, b, h, bh);
   } else {
     hot_split<D, G>(p, sm.hot, b, h, bh);
   }
@@ -1253,19 +1351,24 @@ __device__ __forceinline__ void consume_args(const DecodeParams& p) {
 }
 
 // Grid (split, kv-head, sequence) in the plan's workgroup order (see wg_coord).
-template <int D, int G, bool SPARSE, bool FUSED, bool CLAIM>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G > 4 ? 2 : 4))) void decode_kernel(DecodeParams p) {
+// Waves per SIMD the register budget is sized for: fp16 tiles hold twice the registers of 8-bit ones.
+template <int G, int BITS>
+constexpr int decode_waves() { return (G > 4 || BITS == 0) ? 2 : 4; }
+
+template <int D, int G, int BITS, bool SPARSE, bool FUSED, bool CLAIM>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves<G, BITS>()))) void decode_kernel(
+    DecodeParams p) {
   consume_args(p);
-  decode_body<D, G, SPARSE, FUSED, CLAIM>(p, wg_coord(p.wg_order));
+  decode_body<D, G, BITS, SPARSE, FUSED, CLAIM>(p, wg_coord(p.wg_order));
 }
 
 // Batch plans: the same grid read in the host-built order of the table (see wg_coord_table); a kernel
 // of its own, so the table does not enlarge the arguments of every other launch.
-template <int D, int G, bool FUSED, bool CLAIM>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G > 4 ? 2 : 4))) void decode_kernel_ordered(
-    DecodeParamsOrdered po) {
+template <int D, int G, int BITS, bool FUSED, bool CLAIM>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves<G, BITS>()))) void
+decode_kernel_ordered(DecodeParamsOrdered po) {
   consume_args(po.p);
-  decode_body<D, G, false, FUSED, CLAIM>(po.p, wg_coord_table(po.order));
+  decode_body<D, G, BITS, false, FUSED, CLAIM>(po.p, wg_coord_table(po.order));
 }
 
 template <typename K, typename P>
@@ -1279,7 +1382,7 @@ hipError_t launch_k(K kernel, dim3 grid, int block, const P& p, const LaunchCtx&
   return hipGetLastError();
 }
 
-template <int D, int G>
+template <int D, int G, int BITS>
 hipError_t launch_dg(const DecodeParams& p, const LaunchCtx& ctx, const uint16_t* order) {
   const dim3 grid(p.nparts, p.c.H, p.c.B);  // (split, kv-head, sequence)
   if (order && !p.sel) {
@@ -1287,36 +1390,26 @@ hipError_t launch_dg(const DecodeParams& p, const LaunchCtx& ctx, const uint16_t
     po.p = p;
     std::memcpy(po.order, order, sizeof(po.order));
     if (p.work)
-      return p.k_new ? launch_k(decode_kernel_ordered<D, G, true, true>, grid, kThreads, po, ctx)
-                     : launch_k(decode_kernel_ordered<D, G, false, true>, grid, kThreads, po, ctx);
-    return p.k_new ? launch_k(decode_kernel_ordered<D, G, true, false>, grid, kThreads, po, ctx)
-                   : launch_k(decode_kernel_ordered<D, G, false, false>, grid, kThreads, po, ctx);
+      return p.k_new ? launch_k(decode_kernel_ordered<D, G, BITS, true, true>, grid, kThreads, po, ctx)
+                     : launch_k(decode_kernel_ordered<D, G, BITS, false, true>, grid, kThreads, po, ctx);
+    return p.k_new ? launch_k(decode_kernel_ordered<D, G, BITS, true, false>, grid, kThreads, po, ctx)
+                   : launch_k(decode_kernel_ordered<D, G, BITS, false, false>, grid, kThreads, po, ctx);
   }
   if (p.k_new)
-    return p.work ? launch_k(decode_kernel<D, G, false, true, true>, grid, kThreads, p, ctx)
-                  : launch_k(decode_kernel<D, G, false, true, false>, grid, kThreads, p, ctx);
-  if (p.sel) return launch_k(decode_kernel<D, G, true, false, false>, grid, kThreads, p, ctx);
-  return p.work ? launch_k(decode_kernel<D, G, false, false, true>, grid, kThreads, p, ctx)
-                : launch_k(decode_kernel<D, G, false, false, false>, grid, kThreads, p, ctx);
-}
-
-template <int D>
-hipError_t launch_d(const DecodeParams& p, const LaunchCtx& a, const uint16_t* order) {
-  switch (p.G) {
-    case 1: return launch_dg<D, 1>(p, a, order);
-    case 2: return launch_dg<D, 2>(p, a, order);
-    case 4: return launch_dg<D, 4>(p, a, order);
-    case 8: return launch_dg<D, 8>(p, a, order);
-    default: return hipErrorInvalidValue;
-  }
+    return p.work ? launch_k(decode_kernel<D, G, BITS, false, true, true>, grid, kThreads, p, ctx)
+                  : launch_k(decode_kernel<D, G, BITS, false, true, false>, grid, kThreads, p, ctx);
+  if (p.sel) return launch_k(decode_kernel<D, G, BITS, true, false, false>, grid, kThreads, p, ctx);
+  return p.work ? launch_k(decode_kernel<D, G, BITS, false, false, true>, grid, kThreads, p, ctx)
+                : launch_k(decode_kernel<D, G, BITS, false, false, false>, grid, kThreads, p, ctx);
 }
 
 }  // namespace detail
 
-using namespace detail;
-
-hipError_t launch_decode(const DecodeParams& p, const LaunchCtx& ctx, const uint16_t* order) {
-  return p.c.D == 128 ? launch_d<128>(p, ctx, order) : launch_d<64>(p, ctx, order);
+// The decode launches of one (head_dim, group, cold-tile format) instance (explicitly instantiated by
+// decode_inst.hip, one object per instance).
+template <int D, int G, int BITS>
+hipError_t launch_decode_dgb(const DecodeParams& p, const LaunchCtx& ctx, const uint16_t* order) {
+  return detail::launch_dg<D, G, BITS>(p, ctx, order);
 }
 
 }  // namespace hkv

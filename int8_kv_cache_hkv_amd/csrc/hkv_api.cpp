@@ -3,7 +3,8 @@
 //
 // Protocol rules (Hybrid KV Cache page, 3.1 and 5.1): hot_tokens is a power of
 // two in {16, 32, 64, 128}; block_size is a positive multiple of 8;
-// quantization_bits is 4 or 8 (5.2 adds 0 = FP16 cold zone).  The pages
+// quantization_bits is 4 or 8 (5.2 adds 0 = FP16 cold zone); all three widths
+// are built.  The pages
 // describe a launch-time CUDA_ERROR_INVALID_VALUE for violations; here every
 // check runs on the host before any HIP call.
 #include <hip/hip_ext.h>
@@ -19,6 +20,35 @@
 
 #include "hkv.h"
 #include "hkv_internal.h"
+
+namespace hkv {
+
+template <int D, int BITS>
+hipError_t launch_decode_db(const DecodeParams& p, const LaunchCtx& ctx, const uint16_t* order) {
+  switch (p.G) {
+    case 1: return launch_decode_dgb<D, 1, BITS>(p, ctx, order);
+    case 2: return launch_decode_dgb<D, 2, BITS>(p, ctx, order);
+    case 4: return launch_decode_dgb<D, 4, BITS>(p, ctx, order);
+    case 8: return launch_decode_dgb<D, 8, BITS>(p, ctx, order);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int BITS>
+hipError_t launch_decode_b(const DecodeParams& p, const LaunchCtx& ctx, const uint16_t* order) {
+  return p.c.D == 128 ? launch_decode_db<128, BITS>(p, ctx, order) : launch_decode_db<64, BITS>(p, ctx, order);
+}
+
+hipError_t launch_decode(const DecodeParams& p, const LaunchCtx& ctx, const uint16_t* order) {
+  switch (p.c.bits) {
+    case 8: return launch_decode_b<8>(p, ctx, order);
+    case 4: return launch_decode_b<4>(p, ctx, order);
+    case 0: return launch_decode_b<0>(p, ctx, order);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace hkv
 
 struct hkv_ctx {
   int H, D, T, S, bits;
@@ -152,6 +182,12 @@ SplitPlan plan_sparse(int k_sel) {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Bytes of one (block, kv-head, K|V) cold tile: S x D codes of 8 or 4 bits, or fp16 values.
+size_t tile_bytes(const hkv_ctx* h) {
+  const size_t elems = static_cast<size_t>(h->S) * h->D;
+  return h->bits == 0 ? elems * 2 : elems * h->bits / 8;
+}
+
 hkv_status check_desc(const hkv_ctx* h, const hkv_cache_desc* c) {
   if (!h || !c) return HKV_ERR_NULL_POINTER;
   if (!c->hot || !c->tail || !c->cold || !c->scales || !c->headers || !c->seq_len_dev || !c->seq_len_host)
@@ -173,6 +209,7 @@ hkv::CacheView view_of(const hkv_ctx* h, const hkv_cache_desc* c) {
   v.D = h->D;
   v.T = h->T;
   v.S = h->S;
+  v.bits = h->bits;
   v.max_blocks = c->max_blocks_per_seq;
   v.num_phys = c->num_phys_blocks;
   v.hot = static_cast<_Float16*>(c->hot);
@@ -334,8 +371,7 @@ hkv_status hkv_create(int n_kv_heads, int head_dim, int hot_tokens, int block_si
   if (n_kv_heads < 1 || head_dim < 1) return HKV_ERR_INVALID_VALUE;
   if (!valid_protocol(hot_tokens, block_size)) return HKV_ERR_INVALID_VALUE;
   if (quant_bits != 0 && quant_bits != 4 && quant_bits != 8) return HKV_ERR_INVALID_VALUE;
-  if (quant_bits != 8 || block_size != hkv::kBlockSize || (head_dim != 64 && head_dim != 128))
-    return HKV_ERR_UNSUPPORTED;
+  if (block_size != hkv::kBlockSize || (head_dim != 64 && head_dim != 128)) return HKV_ERR_UNSUPPORTED;
   hkv_ctx* h = new (std::nothrow) hkv_ctx;
   if (!h) return HKV_ERR_OUT_OF_MEMORY;
   h->H = n_kv_heads;
@@ -369,7 +405,7 @@ hkv_status hkv_cache_sizes(hkv_handle h, int batch, int64_t max_tokens_per_seq, 
   if (P > INT32_MAX) return HKV_ERR_INVALID_VALUE;
   out->hot = static_cast<size_t>(batch) * h->H * h->T * 2 * h->D * 2;
   out->tail = static_cast<size_t>(batch) * h->H * 2 * h->S * h->D * 2;
-  out->cold = static_cast<size_t>(P) * h->H * 2 * h->S * h->D;
+  out->cold = static_cast<size_t>(P) * h->H * 2 * tile_bytes(h);
   out->scales = static_cast<size_t>(P) * h->H * 2 * sizeof(float);
   out->headers = static_cast<size_t>(batch) * mb * sizeof(hkv_block_header);
   out->seq_len = static_cast<size_t>(batch) * sizeof(int32_t);

@@ -84,17 +84,18 @@ __device__ __forceinline__ uint4 load_stream_buf(__amdgpu_buffer_rsrc_t r, uint3
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// INT8 code of x under scale s > 0 (r = __builtin_amdgcn_rcpf(s)): clamp(rint(fl32(x / s)), -127,
-// 127) with round half to even, the same value the IEEE fp32 division gives, at the cost of a
-// multiply.  y = fl32(x * r) differs from the rounded quotient fl32(x / s) by at most |x / s| * 2^-21
-// (v_rcp_f32 is within 1 ulp, plus two roundings), i.e. by less than 2^-14 for |x| <= 127 s.  So
-// rint(y) is the code unless y lies within 2^-13 of a half-integer (probability about 2^-12 per
-// element); those elements take the division.
+// Code of x under scale s > 0 (r = __builtin_amdgcn_rcpf(s)) with largest magnitude LIMIT (127 for
+// 8-bit, 7 for 4-bit tiles): clamp(rint(fl32(x / s)), -LIMIT, LIMIT) with round half to even, the
+// same value the IEEE fp32 division gives, at the cost of a multiply.  y = fl32(x * r) differs from
+// the rounded quotient fl32(x / s) by at most |x / s| * 2^-21 (v_rcp_f32 is within 1 ulp, plus two
+// roundings), i.e. by less than 2^-14 for |x| <= 127 s.  So rint(y) is the code unless y lies within
+// 2^-13 of a half-integer (probability about 2^-12 per element); those elements take the division.
+template <int LIMIT>
 __device__ __forceinline__ float quant_code(float x, float s, float r) {
   const float y = x * r;
   float k = __builtin_rintf(y);
   if (__builtin_fabsf(0.5f - __builtin_fabsf(y - k)) <= 0x1p-13f) k = __builtin_rintf(x / s);
-  return fminf(127.f, fmaxf(-127.f, k));
+  return fminf(static_cast<float>(LIMIT), fmaxf(-static_cast<float>(LIMIT), k));
 }
 
 // Sequence geometry derived from the cached length.
@@ -110,9 +111,9 @@ __device__ __forceinline__ SeqGeom seq_geom(int n, int T, int S) {
   return g;
 }
 
-// Byte offset of the (phys, head, K|V) tile inside the cold pool.
-__device__ __forceinline__ size_t tile_offset(int phys, int h, int kv, int H, int S, int D) {
-  return ((static_cast<size_t>(phys) * H + h) * 2 + kv) * static_cast<size_t>(S) * D;
+// Byte offset of the (phys, head, K|V) tile inside the cold pool (tile_bytes per tile).
+__device__ __forceinline__ size_t tile_offset(int phys, int h, int kv, int H, int tile_bytes) {
+  return ((static_cast<size_t>(phys) * H + h) * 2 + kv) * static_cast<size_t>(tile_bytes);
 }
 
 // A wave's walk over its dense units: runs of CU = units_per_split units start
@@ -264,8 +265,90 @@ __device__ __forceinline__ half4_t codes_to_biased_half4(uint32_t w) {
 }
 constexpr float kCodeBias = 1152.0f;
 
+// ---------------------------------------------------------------- cold-tile formats
+// One cold tile holds the S = 64 tokens x D channels of one (block, kv-head, K|V) as 8-bit codes,
+// 4-bit codes or fp16 values (quant_bits 8, 4, 0), in 16-byte chunks laid out so that one coalesced
+// wave load gives every lane its MFMA operand:
+//   K tile: chunk (kc, t) at byte (kc * S + t) * 16 holds channels [kc * E, kc * E + E) of token t;
+//   V tile: chunk (vc, c) at byte (vc * D + c) * 16 holds tokens [vc * E, vc * E + E) of channel c;
+// E = elements per chunk (16, 32 or 8).  Element e of a chunk is byte e (8-bit, two's complement),
+// the nibble e % 2 (0 = low) of byte e / 2 holding code + 8 (4-bit, offset binary: code 0 is 8), or
+// bytes 2e, 2e + 1 (fp16).  An FP16 tile's scale is stored as 1.
+template <int BITS>
+struct Fmt {
+  static_assert(BITS == 8 || BITS == 4 || BITS == 0, "8-bit, 4-bit or fp16 tiles");
+  static constexpr int kElems = BITS == 8 ? 16 : (BITS == 4 ? 32 : 8);  // elements per 16-byte chunk
+  static constexpr int kSteps = kElems / 4;                            // 4-element MFMA operands per chunk
+  static constexpr int kLimit = BITS == 8 ? 127 : 7;                   // largest code magnitude
+  // 8-bit QK operands are biased (no subtraction per element): code + kBias, removed from each logit.
+  // The removal's fp32 rounding (relative to the offset sum) is multiplied by the block scale, which
+  // is 127/7 times larger at 4 bits for the same maximum: 4-bit QK operands are the exact codes.
+  static constexpr bool kBiasedQK = BITS == 8;
+  static constexpr float kBias = BITS == 8 ? kCodeBias : 0.0f;
+  template <int D>
+  static constexpr int tile_bytes() { return BITS == 0 ? 64 * D * 2 : 64 * D * BITS / 8; }
+};
+
+// 4-bit codes: elements 2i and 2i + 1 of a word (offset-binary nibbles) as the fp16 pair
+// (1024 + nibble): the nibbles are split into byte lanes, a byte permute places one of each under
+// the exponent of 1024.  Every step is exact.
+__device__ __forceinline__ uint32_t nib_pair(uint32_t lo, uint32_t hi, int i) {
+  // lo = even elements (bytes 0..3), hi = odd elements; selector bytes: lo.b_i, 0, hi.b_i, 0
+  const uint32_t sel = 0x0C000C00u | (static_cast<uint32_t>(4 + i) << 16) | static_cast<uint32_t>(i);
+  return __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u;
+}
+
+// MFMA operand `step` (4 consecutive elements) of a 16-byte chunk, as fp16 values: biased
+// (code + kBias, the QK operand) or exact (the code itself, the PV operand).  fp16 tiles give the
+// values themselves either way.
+template <int BITS, bool BIASED>
+__device__ __forceinline__ half4_t chunk_operand(const uint4& ck, int step) {
+  if constexpr (BITS == 8) {
+    return BIASED ? codes_to_biased_half4(word_of(ck, step)) : codes_to_half4(word_of(ck, step));
+  } else if constexpr (BITS == 4) {
+    const uint32_t w = word_of(ck, step >> 1);
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    const int p = (step & 1) * 2;  // element pairs 2p, 2p + 1 of the word
+    half2_t a = __builtin_bit_cast(half2_t, nib_pair(lo, hi, p));
+    half2_t b = __builtin_bit_cast(half2_t, nib_pair(lo, hi, p + 1));
+    if (!BIASED) {
+      const half2_t off = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
+      a = a - off;
+      b = b - off;
+    }
+    return half4_t{a.x, a.y, b.x, b.y};
+  } else {
+    const uint32_t w0 = word_of(ck, 2 * step), w1 = word_of(ck, 2 * step + 1);
+    const half2_t a = __builtin_bit_cast(half2_t, w0), b = __builtin_bit_cast(half2_t, w1);
+    return half4_t{a.x, a.y, b.x, b.y};
+  }
+}
+
 __device__ __forceinline__ float4_t mfma_qk(half4_t a, half4_t b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c, 0, 0, 0);
+}
+
+// 4-bit tiles: eight int8 codes (x0: elements 0..3, x1: 4..7) as one word of offset-binary nibbles
+// (element e in nibble e).  (c & 15) ^ 8 = c + 8 for c in [-7, 7].
+__device__ __forceinline__ uint32_t pack_nib8(uint32_t x0, uint32_t x1) {
+  uint32_t a = (x0 & 0x0F0F0F0Fu) ^ 0x08080808u;
+  uint32_t b = (x1 & 0x0F0F0F0Fu) ^ 0x08080808u;
+  a |= a >> 4;  // byte 0 = e0 | e1 << 4, byte 2 = e2 | e3 << 4
+  b |= b >> 4;
+  return __builtin_amdgcn_perm(b, a, 0x06040200u);
+}
+
+// A 16-byte tile chunk from 16 bytes of stage (8-bit codes or fp16 values), or from 32 code bytes
+// packed into nibbles (4-bit).
+template <int BITS>
+__device__ __forceinline__ uint4 chunk_from_stage(const int8_t* src) {
+  if constexpr (BITS == 4) {
+    const uint4 a = *reinterpret_cast<const uint4*>(src);
+    const uint4 b = *reinterpret_cast<const uint4*>(src + 16);
+    return make_uint4(pack_nib8(a.x, a.y), pack_nib8(a.z, a.w), pack_nib8(b.x, b.y), pack_nib8(b.z, b.w));
+  } else {
+    return *reinterpret_cast<const uint4*>(src);
+  }
 }
 
 }  // namespace hkv

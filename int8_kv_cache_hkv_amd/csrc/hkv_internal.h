@@ -36,10 +36,11 @@ struct LaunchCtx {
 
 struct CacheView {
   int B, H, D, T, S;
+  int bits;            // cold-tile format: 8- or 4-bit codes, 0 = fp16 values
   int max_blocks, num_phys;
   _Float16* hot;       // [B][H][T][2][D]
   _Float16* tail;      // [B][H][2][S][D]
-  int8_t* cold;        // [P][H][2][S*D]
+  int8_t* cold;        // [P][H][2][tile bytes]
   float* scales;       // [P][H][2]
   hkv_block_header* headers;  // [B][max_blocks]
   int32_t* seq_len;    // [B]
@@ -101,6 +102,12 @@ struct TopkParams {
 };
 
 hipError_t launch_append(const AppendParams& p, const LaunchCtx& quant_ctx, const LaunchCtx& ring_ctx);
+// Decode launches of one (head_dim, group, cold-tile format) instance (decode_inst.hip).
+template <int D, int G, int BITS>
+hipError_t launch_decode_dgb(const DecodeParams& p, const LaunchCtx& ctx, const uint16_t* order);
+
+// Dispatch on (cold-tile format, head_dim, group) to the instances above (host code only: where the
+// kernels' template definitions are visible, this body would instantiate every instance).
 hipError_t launch_decode(const DecodeParams& p, const LaunchCtx& ctx, const uint16_t* order = nullptr);
 hipError_t launch_topk(const TopkParams& p, const LaunchCtx& score_ctx, const LaunchCtx& sel_ctx);
 // Device address of the fixed scratch array on the current device (set up on first use: address

@@ -36,47 +36,60 @@ constexpr float kNegInfT = -__builtin_inff();
 constexpr int kStage = 32;
 constexpr int kSelThreads = 1024;
 
-// Window probabilities of one cold block from its K codes: kr[ch] holds codes
-// 16ch..16ch+15 of the lane's token.  As each chunk is consumed its registers
-// receive the same chunk of the next unit's K tile (rn; an empty descriptor
-// when there is none), so the next tile streams in while this one is scored.
-template <int D, int G>
-__device__ __forceinline__ float window_scores(uint4 (&kr)[D / 16], const _Float16 (*qh)[4][D + 8],
+// Window probabilities of one cold block from its K tile: kr[ch] holds elements
+// E ch .. E ch + E - 1 of the lane's token.  As each chunk is consumed its
+// registers receive the same chunk of the next unit's K tile (rn; an empty
+// descriptor when there is none), so the next tile streams in while this one
+// is scored.
+template <int D, int G, int BITS>
+__device__ __forceinline__ float window_scores(uint4 (&kr)[D / Fmt<BITS>::kElems], const _Float16 (*qh)[4][D + 8],
                                                const float* qinv, int lane, int nv, __amdgpu_buffer_rsrc_t rn) {
+  using F = Fmt<BITS>;
   constexpr int S = kBlockSize;
   constexpr int NQ = (G + 3) / 4;
   const uint32_t lo = static_cast<uint32_t>(lane) * 16u;
-  // dot(q_g, code_t) for the lane's token t (MFMA, exact products) and |code_t|^2 (integer dot4)
+  // dot(q_g, k_t) for the lane's token t (MFMA, exact products) and |k_t|^2 (an integer dot4 of the
+  // 8-bit codes; for 4-bit codes and fp16 values an fp32 dot2 of the exact fp16 operands)
   float4_t s[NQ];
 #pragma unroll
   for (int quad = 0; quad < NQ; ++quad) s[quad] = float4_t{0.f, 0.f, 0.f, 0.f};
   int n2 = 0;
+  float f2 = 0.f;
 #pragma unroll
-  for (int ch = 0; ch < D / 16; ++ch) {
+  for (int ch = 0; ch < D / F::kElems; ++ch) {
     asm volatile("" ::: "memory");  // keep the chunks in order: each refill is issued right after its use
-    half4_t bk[4];
+    half4_t bk[F::kSteps];
 #pragma unroll
-    for (int wd = 0; wd < 4; ++wd) {
-      const uint32_t word = word_of(kr[ch], wd);
-      n2 = __builtin_amdgcn_sdot4(static_cast<int>(word), static_cast<int>(word), n2, false);
-      bk[wd] = codes_to_half4(word);
+    for (int st = 0; st < F::kSteps; ++st) {
+      bk[st] = chunk_operand<BITS, false>(kr[ch], st);
+      if constexpr (BITS == 8) {
+        const uint32_t word = word_of(kr[ch], st);
+        n2 = __builtin_amdgcn_sdot4(static_cast<int>(word), static_cast<int>(word), n2, false);
+      } else {
+        const half2_t a = {bk[st].x, bk[st].y}, b = {bk[st].z, bk[st].w};
+        f2 = __builtin_amdgcn_fdot2(a, a, f2, false);
+        f2 = __builtin_amdgcn_fdot2(b, b, f2, false);
+      }
     }
     // every read of the chunk happens before the load that refills its registers: a read left
     // after it would need the old value in other registers, and the copy back at the end of the
     // walk's iteration would wait for every load in flight
-    asm volatile("" ::"v"(bk[0]), "v"(bk[1]), "v"(bk[2]), "v"(bk[3]), "v"(n2) : "memory");
+#pragma unroll
+    for (int st = 0; st < F::kSteps; ++st) asm volatile("" ::"v"(bk[st]) : "memory");
+    asm volatile("" ::"v"(n2), "v"(f2) : "memory");
     kr[ch] = load_stream_buf(rn, lo + ch * S * 16);
 #pragma unroll
-    for (int wd = 0; wd < 4; ++wd) {
-      const int k0 = ch * 16 + wd * 4;
+    for (int st = 0; st < F::kSteps; ++st) {
+      const int k0 = ch * F::kElems + st * 4;
 #pragma unroll
       for (int quad = 0; quad < NQ; ++quad)
-        s[quad] = mfma_qk(*reinterpret_cast<const half4_t*>(&qh[quad][lane & 3][k0]), bk[wd], s[quad]);
+        s[quad] = mfma_qk(*reinterpret_cast<const half4_t*>(&qh[quad][lane & 3][k0]), bk[st], s[quad]);
     }
   }
   asm volatile("" ::: "memory");
-  // c_t = mean over the G query heads of cos(q_g, code_t); cosine is scale-free, so codes suffice
-  const float kinv = n2 > 0 ? 1.f / __builtin_sqrtf(static_cast<float>(n2)) : 0.f;
+  // c_t = mean over the G query heads of cos(q_g, k_t); cosine is scale-free, so codes suffice
+  const float knorm2 = BITS == 8 ? static_cast<float>(n2) : f2;
+  const float kinv = knorm2 > 0.f ? 1.f / __builtin_sqrtf(knorm2) : 0.f;
   float csum = 0.f;
 #pragma unroll
   for (int quad = 0; quad < NQ; ++quad)
@@ -92,17 +105,19 @@ __device__ __forceinline__ float window_scores(uint4 (&kr)[D / 16], const _Float
 }
 
 // K tile of (phys, h) as a buffer resource (empty for phys < 0: loads read 0).
-template <int D>
+template <int D, int BITS>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t k_tile_rsrc(const CacheView& c, int phys, int h) {
+  constexpr int TB = Fmt<BITS>::template tile_bytes<D>();
   const bool ok = phys >= 0;
-  return make_rsrc(c.cold + tile_offset(ok ? phys : 0, h, 0, c.H, kBlockSize, D), ok ? kBlockSize * D : 0u);
+  return make_rsrc(c.cold + tile_offset(ok ? phys : 0, h, 0, c.H, TB), ok ? TB : 0u);
 }
 
 // Grid (split, kv-head, sequence).  Each wave walks its cold blocks (the same
 // walk as the decode's dense units); the first block's tile is requested with
 // the query, each next one while the current one is scored.
-template <int D, int G, bool CLAIM>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void topk_score_kernel(TopkParams p) {
+template <int D, int G, int BITS, bool CLAIM>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BITS == 0 ? 2 : 4))) void topk_score_kernel(
+    TopkParams p) {
   constexpr int S = kBlockSize;
   constexpr int NQ = (G + 3) / 4;          // groups of 4 query heads (MFMA rows)
   constexpr int QROW = D + 8;              // padded fp16 query row
@@ -133,11 +148,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   int hb = CLAIM ? header_load(c, b, split * kWaves + w) : header_batch(c, b, 0, split, p.nsplit, CU, w, lane);
   if (CLAIM) cl = claim_issue(work, lane);
   int phys = CLAIM ? header_phys(c, hb) : __builtin_amdgcn_readlane(hb, 0);
-  uint4 kr[D / 16];
+  uint4 kr[D / Fmt<BITS>::kElems];
   {
-    const __amdgpu_buffer_rsrc_t r0 = k_tile_rsrc<D>(c, phys, h);
+    const __amdgpu_buffer_rsrc_t r0 = k_tile_rsrc<D, BITS>(c, phys, h);
 #pragma unroll
-    for (int ch = 0; ch < D / 16; ++ch) kr[ch] = load_stream_buf(r0, static_cast<uint32_t>(lane) * 16u + ch * S * 16);
+    for (int ch = 0; ch < D / Fmt<BITS>::kElems; ++ch)
+      kr[ch] = load_stream_buf(r0, static_cast<uint32_t>(lane) * 16u + ch * S * 16);
   }
   static_assert(4 * NQ * VPR <= kThreads, "one query vector per thread");
   if (tid < 4 * NQ * VPR)
@@ -193,7 +209,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       const int hn2 = header_load(c, b, un2);
       cl = claim_issue(work, lane);
       const int nv = min(S, sg.n_cold - u * S);
-      const float pr = window_scores<D, G>(kr, qh, qinv, lane, nv, k_tile_rsrc<D>(c, phys_n, h));
+      const float pr = window_scores<D, G, BITS>(kr, qh, qinv, lane, nv, k_tile_rsrc<D, BITS>(c, phys_n, h));
       // a block without a valid physical id contributes probability 0 (its tokens are never
       // attended); lanes past the last cold token write row entries the selection never reads
       pstage[w][nst][lane] = phys >= 0 && lane < nv ? pr : 0.f;
@@ -227,7 +243,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   int phys_n = u < units && un < units ? phys_of(1) : -1;
   while (u < units) {
     const int nv = min(S, sg.n_cold - u * S);
-    const float pr = window_scores<D, G>(kr, qh, qinv, lane, nv, k_tile_rsrc<D>(c, phys_n, h));
+    const float pr = window_scores<D, G, BITS>(kr, qh, qinv, lane, nv, k_tile_rsrc<D, BITS>(c, phys_n, h));
     // a block without a valid physical id contributes probability 0 (its tokens are never attended)
     if (lane < nv) prob[static_cast<size_t>(u) * S + lane] = phys >= 0 ? pr : 0.f;
     u = un;
@@ -515,21 +531,31 @@ hipError_t launch_t(Kf kernel, dim3 grid, int block, const TopkParams& p, const 
   return hipGetLastError();
 }
 
-template <int D, int G>
+template <int D, int G, int BITS>
 hipError_t launch_tg(const TopkParams& p, const LaunchCtx& a, const LaunchCtx& b) {
-  hipError_t e = p.work ? launch_t(topk_score_kernel<D, G, true>, dim3(p.nsplit, p.c.H, p.c.B), kThreads, p, a)
-                        : launch_t(topk_score_kernel<D, G, false>, dim3(p.nsplit, p.c.H, p.c.B), kThreads, p, a);
+  hipError_t e = p.work ? launch_t(topk_score_kernel<D, G, BITS, true>, dim3(p.nsplit, p.c.H, p.c.B), kThreads, p, a)
+                        : launch_t(topk_score_kernel<D, G, BITS, false>, dim3(p.nsplit, p.c.H, p.c.B), kThreads, p, a);
   if (e != hipSuccess) return e;
   return launch_t(topk_select_kernel, dim3(p.c.B * p.c.H), kSelThreads, p, b);
 }
 
+template <int D, int BITS>
+hipError_t launch_tdb(const TopkParams& p, const LaunchCtx& a, const LaunchCtx& b) {
+  switch (p.G) {
+    case 1: return launch_tg<D, 1, BITS>(p, a, b);
+    case 2: return launch_tg<D, 2, BITS>(p, a, b);
+    case 4: return launch_tg<D, 4, BITS>(p, a, b);
+    case 8: return launch_tg<D, 8, BITS>(p, a, b);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int D>
 hipError_t launch_td(const TopkParams& p, const LaunchCtx& a, const LaunchCtx& b) {
-  switch (p.G) {
-    case 1: return launch_tg<D, 1>(p, a, b);
-    case 2: return launch_tg<D, 2>(p, a, b);
-    case 4: return launch_tg<D, 4>(p, a, b);
-    case 8: return launch_tg<D, 8>(p, a, b);
+  switch (p.c.bits) {
+    case 8: return launch_tdb<D, 8>(p, a, b);
+    case 4: return launch_tdb<D, 4>(p, a, b);
+    case 0: return launch_tdb<D, 0>(p, a, b);
     default: return hipErrorInvalidValue;
   }
 }

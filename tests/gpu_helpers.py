@@ -86,6 +86,8 @@ def check_state(cache, states: List[orc.SequenceState], seqs: Optional[Sequence[
             assert int(hdr[b, j, 1]) == nv and int(hdr[b, j, 2]) == j, (b, j, hdr[b, j])
             got = codes[phys]
             want = st.codes[j]
+            if got.dtype == np.float16:  # an FP16 cold zone: compare bit patterns
+                got, want = got.view(np.uint16), np.asarray(want, dtype=np.float16).view(np.uint16)
             if not np.array_equal(got[:, :, :nv], want[:, :, :nv]):
                 bad = np.argwhere(got[:, :, :nv] != want[:, :, :nv])
                 raise AssertionError(f"seq {b} block {j}: {len(bad)} code mismatches, first {bad[:3].tolist()}")

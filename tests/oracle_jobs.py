@@ -35,7 +35,7 @@ def state_of(name: str, seq: int, n: int, overrides: Optional[Dict] = None) -> o
     w = _workload(name, overrides)
     k = wl.tokens(w, seq, 0, n, "k")
     v = wl.tokens(w, seq, 0, n, "v")
-    return orc.build_state(k, v, w.hot_tokens, w.block_size)
+    return orc.build_state(k, v, w.hot_tokens, w.block_size, w.quant_bits)
 
 
 def decode_job(name: str, seq: int, lengths, queries, with_state_at: int = -1,
@@ -49,7 +49,7 @@ def decode_job(name: str, seq: int, lengths, queries, with_state_at: int = -1,
     res = []
     keep = None
     for n, q in zip(lengths, queries):
-        st = orc.build_state(k[:n], v[:n], w.hot_tokens, w.block_size)
+        st = orc.build_state(k[:n], v[:n], w.hot_tokens, w.block_size, w.quant_bits)
         res.append(orc.decode(q, st))
         if n == with_state_at:
             keep = st

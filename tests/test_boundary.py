@@ -45,7 +45,8 @@ def _create(*args):
     (33, 64, 8, INVALID), (48, 64, 8, INVALID), (8, 64, 8, INVALID), (256, 64, 8, INVALID),
     (32, 63, 8, INVALID), (32, 0, 8, INVALID), (32, -8, 8, INVALID),
     (32, 64, 7, INVALID), (32, 64, 16, INVALID),
-    (32, 64, 4, UNSUPPORTED), (32, 64, 0, UNSUPPORTED), (32, 128, 8, UNSUPPORTED), (32, 32, 8, UNSUPPORTED),
+    (32, 64, 4, 0), (32, 64, 0, 0), (16, 64, 4, 0), (128, 64, 0, 0),
+    (32, 128, 8, UNSUPPORTED), (32, 32, 8, UNSUPPORTED), (32, 128, 4, UNSUPPORTED),
 ])
 def test_create_protocol_rules(hot, block, bits, want):
     assert _create(8, 128, hot, block, bits) == want
@@ -178,6 +179,19 @@ def test_decode_and_topk_host_errors():
         assert lib.hkv_topk_select(h, d, q, 24, 16, out, ws, big, None) == UNSUPPORTED
     finally:
         hkv.hkv_destroy(h)
+
+
+def test_cache_sizes_per_width():
+    """The cold pool holds S x D codes per (block, kv-head, K|V) tile: 1 byte each at 8 bits, half a
+    byte at 4 bits, 2 bytes (fp16 values) at 0 bits; the other buffers do not depend on the width."""
+    for bits, per in ((8, 1.0), (4, 0.5), (0, 2.0)):
+        h = hkv.hkv_create(8, 128, 32, 64, bits)
+        try:
+            s = hkv.hkv_cache_sizes(h, 8, 2048)
+            assert s.cold == int(256 * 8 * 2 * 64 * 128 * per)
+            assert s.hot == 8 * 8 * 32 * 2 * 128 * 2 and s.scales == 256 * 8 * 2 * 4
+        finally:
+            hkv.hkv_destroy(h)
 
 
 def test_sizes_array_form():

@@ -31,7 +31,7 @@ def _oracle_states(w, lens, seqs=None):
     out = []
     for b, n in zip(seqs, lens):
         k, v = gh.history(w, b, n)
-        out.append(orc.build_state(k, v, w.hot_tokens, w.block_size))
+        out.append(orc.build_state(k, v, w.hot_tokens, w.block_size, w.quant_bits))
     return out
 
 

@@ -1,12 +1,12 @@
-"""GPU: exhaustive parity of the INT8 quantiser against the fp64 oracle, through the C ABI.
+"""GPU: exhaustive parity of the 8-bit and 4-bit quantisers against the fp64 oracle, through the C ABI.
 
-The block scale s = fl32(max|x| / 127) and the codes clamp(rint(fl32(x / s)), -127, 127) (Hybrid
-KV Cache page 2.1: INT8 cold blocks with a block-wise scale; symmetric absmax with round half to
-even) are compared bit for bit:
+The block scale s = fl32(max|x| / L) and the codes clamp(rint(fl32(x / s)), -L, L), L = 127 (8
+bits) or 7 (4 bits) (Hybrid KV Cache page 2.1: INT8 cold blocks with a block-wise scale; 3.1: 4 or 8
+bits; symmetric absmax with round half to even) are compared bit for bit:
 
 * every one of the 31744 non-negative finite fp16 values is the maximum of some tile (64 tokens x
   head_dim channels of one kv-head, K or V); besides the maximum, each tile holds the fp16 values
-  next to (k + 1/2) * s for every k in [0, 127), the inputs whose quotient x / s lies closest to a
+  next to (k + 1/2) * s for every k in [0, L), the inputs whose quotient x / s lies closest to a
   rounding boundary, with random signs, and random fill;
 * for the maxima 65504, 127, 40.72, 3.1416, 1, 6.1e-5, 37 * 2^-24 and 64 random ones, every finite
   fp16 x with |x| <= max is coded;
@@ -32,18 +32,21 @@ def all_maxima() -> np.ndarray:
     return np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16)
 
 
-def near_half_values(m: np.ndarray) -> np.ndarray:
-    """[len(m), 127, 3]: for each maximum m and k in [0, 127), the fp16 value nearest (k + 1/2) m / 127
+LIMIT = {8: 127, 4: 7}
+
+
+def near_half_values(m: np.ndarray, lim: int = 127) -> np.ndarray:
+    """[len(m), lim, 3]: for each maximum m and k in [0, lim), the fp16 value nearest (k + 1/2) m / lim
     and its two fp16 neighbours; entries outside (0, m] are replaced by m."""
     m64 = m.astype(np.float64)[:, None]
-    t = (np.arange(127, dtype=np.float64)[None, :] + 0.5) * m64 / 127.0
+    t = (np.arange(lim, dtype=np.float64)[None, :] + 0.5) * m64 / float(lim)
     f = t.astype(np.float16)
     c = np.stack([np.nextafter(f, np.float16(-np.inf)), f, np.nextafter(f, np.float16(np.inf))], axis=-1)
     ok = (c > 0) & (c.astype(np.float64) <= m64[:, :, None]) & np.isfinite(c)
     return np.where(ok, c, np.broadcast_to(m[:, None, None], c.shape)).astype(np.float16)
 
 
-def maxima_tiles(m: np.ndarray, n: int, rng) -> np.ndarray:
+def maxima_tiles(m: np.ndarray, n: int, rng, lim: int = 127) -> np.ndarray:
     """[len(m), n] fp16 tiles whose largest magnitude is exactly m (row i: maximum m[i] at a random
     position, the near-boundary values of its scale with random signs, uniform fill in [-m, m])."""
     out = np.empty((len(m), n), dtype=np.float16)
@@ -52,7 +55,7 @@ def maxima_tiles(m: np.ndarray, n: int, rng) -> np.ndarray:
         mm = m[a:a + step]
         k = len(mm)
         fill = (rng.uniform(-1.0, 1.0, (k, n)) * mm.astype(np.float64)[:, None]).astype(np.float16)
-        nh = near_half_values(mm).reshape(k, -1)
+        nh = near_half_values(mm, lim).reshape(k, -1)
         nh = nh * np.where(rng.random(nh.shape) < 0.5, -1, 1).astype(np.float16)
         w = min(nh.shape[1], n - 1)
         fill[:, 1:1 + w] = nh[:, :w]
@@ -76,8 +79,8 @@ def sweep_tiles(m: float, n: int) -> np.ndarray:
     return out
 
 
-def build_tiles(n: int, maxima: np.ndarray, sweep: list, rng):
-    tiles = [maxima_tiles(maxima, n, rng)]
+def build_tiles(n: int, maxima: np.ndarray, sweep: list, rng, lim: int = 127):
+    tiles = [maxima_tiles(maxima, n, rng, lim)]
     for m in sweep:
         tiles.append(sweep_tiles(m, n))
     return np.concatenate(tiles)
@@ -104,27 +107,27 @@ def sweep_list(rng, n_random=64):
     return [float(np.float16(x)) for x in SWEEP_MAXIMA] + [float(x) for x in rnd]
 
 
-@pytest.mark.parametrize("D,H,stride", [(128, 8, 1), (64, 2, 5)])
-def test_quantiser_exhaustive_append(D, H, stride):
+@pytest.mark.parametrize("D,H,stride,bits", [(128, 8, 1, 8), (64, 2, 5, 8), (128, 8, 1, 4), (64, 2, 5, 4)])
+def test_quantiser_exhaustive_append(D, H, stride, bits):
     """Every fp16 maximum (every `stride`-th one for head_dim 64) and the full sweeps, coded by a bulk
     append and by one-block appends: codes, scales, headers and the hot ring bit-exact."""
     import int8_kv_cache_hkv_amd as hkv
     torch = gh.torch_mod()
-    rng = np.random.default_rng(20261203 + D)
+    rng = np.random.default_rng(20261203 + D + bits)
     maxima = all_maxima()[::stride]
-    tiles = build_tiles(S * D, maxima, sweep_list(rng), rng)
+    tiles = build_tiles(S * D, maxima, sweep_list(rng), rng, LIMIT[bits])
     B = 64
     k, v = histories(tiles, B, H, D, rng)
     n = k.shape[1]
-    gh.log(f"quantiser D={D} H={H}: {len(tiles)} designed tiles, {B} sequences of {n} tokens")
-    states = [orc.build_state(k[b], v[b], T, S) for b in range(B)]
-    bulk = hkv.HybridKVCache(H, D, B, n)
+    gh.log(f"quantiser {bits}-bit D={D} H={H}: {len(tiles)} designed tiles, {B} sequences of {n} tokens")
+    states = [orc.build_state(k[b], v[b], T, S, bits) for b in range(B)]
+    bulk = hkv.HybridKVCache(H, D, B, n, quant_bits=bits)
     bulk.append(gh.upload(k), gh.upload(v))
     torch.cuda.synchronize()
     gh.check_state(bulk, states)
     bulk.close()
     gh.log("  bulk append: bit-exact")
-    blocks = hkv.HybridKVCache(H, D, B, n)
+    blocks = hkv.HybridKVCache(H, D, B, n, quant_bits=bits)
     blocks.append(gh.upload(k[:, :T]), gh.upload(v[:, :T]))
     for p in range(T, n, S):  # each call spills exactly one whole block
         blocks.append(gh.upload(k[:, p:p + S]), gh.upload(v[:, p:p + S]))
@@ -134,7 +137,7 @@ def test_quantiser_exhaustive_append(D, H, stride):
     gh.log("  one-block appends: bit-exact")
 
 
-def growth_rows(maxima: np.ndarray, n_tiles: int, D: int, rng) -> np.ndarray:
+def growth_rows(maxima: np.ndarray, n_tiles: int, D: int, rng, lim: int = 127) -> np.ndarray:
     """[n_tiles, S, D] rows of one block per tile: tile t's maxima are maxima[t::n_tiles] (ascending);
     even rows raise the block maximum to the next of them (row = the maximum plus values next to the
     rounding boundaries of its scale), odd rows keep it (uniform values below it; every fourth odd
@@ -148,7 +151,7 @@ def growth_rows(maxima: np.ndarray, n_tiles: int, D: int, rng) -> np.ndarray:
             if r % 2 == 0 and g < len(ms):
                 cur = ms[g]
                 g += 1
-                row = maxima_tiles(np.array([cur]), D, rng)[0]
+                row = maxima_tiles(np.array([cur]), D, rng, lim)[0]
             else:
                 row = (rng.uniform(-1.0, 1.0, D) * float(cur)).astype(np.float16)
                 if r % 8 == 1:
@@ -157,25 +160,26 @@ def growth_rows(maxima: np.ndarray, n_tiles: int, D: int, rng) -> np.ndarray:
     return rows
 
 
-@pytest.mark.parametrize("D,H,G,stride", [(128, 8, 4, 1), (64, 2, 2, 4)])
-def test_quantiser_exhaustive_fused_step(D, H, G, stride):
+@pytest.mark.parametrize("D,H,G,stride,bits", [(128, 8, 4, 1, 8), (64, 2, 2, 4, 8), (128, 8, 4, 1, 4),
+                                                (64, 2, 2, 4, 4)])
+def test_quantiser_exhaustive_fused_step(D, H, G, stride, bits):
     """The fused decode step's coder: 64 fused steps spill the 64 designed rows of block 0 one at a
     time (31 growing maxima per tile cover every fp16 maximum for head_dim 128); after every step
     the block's codes and scales, headers, the hot ring and the lengths are bit-exact against the
     oracle."""
     import int8_kv_cache_hkv_amd as hkv
     torch = gh.torch_mod()
-    rng = np.random.default_rng(777 + D)
+    rng = np.random.default_rng(777 + D + bits)
     B = 64
     n_tiles = B * H * 2
-    rows = growth_rows(all_maxima()[::stride], n_tiles, D, rng).reshape(B, H, 2, S, D)
+    rows = growth_rows(all_maxima()[::stride], n_tiles, D, rng, LIMIT[bits]).reshape(B, H, 2, S, D)
     k = np.concatenate([rows[:, :, 0].transpose(0, 2, 1, 3),
                         rng.standard_normal((B, T, H, D)).astype(np.float16)], axis=1)
     v = np.concatenate([rows[:, :, 1].transpose(0, 2, 1, 3),
                         rng.standard_normal((B, T, H, D)).astype(np.float16)], axis=1)
     k, v = np.ascontiguousarray(k), np.ascontiguousarray(v)
-    gh.log(f"fused coder D={D} H={H}: {n_tiles} tiles, 64 steps")
-    cache = hkv.HybridKVCache(H, D, B, S + T + 8)
+    gh.log(f"fused coder {bits}-bit D={D} H={H}: {n_tiles} tiles, 64 steps")
+    cache = hkv.HybridKVCache(H, D, B, S + T + 8, quant_bits=bits)
     cache.append(gh.upload(k[:, :T]), gh.upload(v[:, :T]))
     q = gh.upload(rng.standard_normal((B, H * G, D)).astype(np.float16))
     out = torch.empty_like(q)
@@ -183,7 +187,7 @@ def test_quantiser_exhaustive_fused_step(D, H, G, stride):
         n0 = T + i
         cache.append_decode(gh.upload(k[:, n0]), gh.upload(v[:, n0]), q, out=out)
         torch.cuda.synchronize()
-        states = [orc.build_state(k[b, :n0 + 1], v[b, :n0 + 1], T, S) for b in range(B)]
+        states = [orc.build_state(k[b, :n0 + 1], v[b, :n0 + 1], T, S, bits) for b in range(B)]
         gh.check_state(cache, states)
     # (the attention output is not compared here: these rows span the whole fp16 range, where the
     # absolute output tolerance of the N(0, 1) workloads does not apply; decode parity under fp16
