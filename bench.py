@@ -19,7 +19,9 @@ output outside the timed region (and, where it is cheap, with the fp64
 oracle) and the run exits with status 3 if any check fails.
 
 Legs (`--leg`, default all): llama8b (the headline step), separate (the same
-step as hkv_append + hkv_decode_attn), long (131072 tokens), sparse (top-K
+step as hkv_append + hkv_decode_attn), long (131072 tokens), llama8b_int4 /
+long_int4 / llama8b_fp16 / long_fp16 (the same steps with 4-bit cold blocks or
+an FP16 cold zone), sparse (top-K
 selection + sparse decode, 32768 tokens), ragged (64 sequences of seeded
 lengths), graph (the llama8b step from a HIP graph), read_floor (a plain
 one-launch read of the llama8b step's bytes), cpu (the fp64 oracle on the host).
@@ -87,21 +89,27 @@ def log(msg):
 
 
 # ----------------------------------------------------------------------------- algorithmic bytes
-def decode_bytes(n, H, Hq, d, T=32, S=64, with_out=True):
-    """Bytes the dense decode must move for one sequence of n cached tokens: int8 K and V codes of the
-    cold tokens, the two fp32 scales per cold block and kv-head, the 16-byte headers, the fp16 hot
-    tokens, the fp16 query (and the fp16 output)."""
+def cold_elem_bytes(bits=8):
+    """Bytes per cold element: an 8-bit code, a 4-bit code, or an fp16 value (quant_bits 0)."""
+    return {8: 1.0, 4: 0.5, 0: 2.0}[bits]
+
+
+def decode_bytes(n, H, Hq, d, T=32, S=64, with_out=True, bits=8):
+    """Bytes the dense decode must move for one sequence of n cached tokens: the K and V codes (or fp16
+    values) of the cold tokens, the two fp32 scales per cold block and kv-head, the 16-byte headers,
+    the fp16 hot tokens, the fp16 query (and the fp16 output)."""
     n_hot = min(n, T)
     n_cold = n - n_hot
     n_blk = -(-n_cold // S)
-    b = 2 * n_cold * H * d + 8 * n_blk * H + 16 * n_blk + 4 * n_hot * H * d + 2 * Hq * d
-    return b + (2 * Hq * d if with_out else 0)
+    b = 2 * n_cold * H * d * cold_elem_bytes(bits) + 8 * n_blk * H + 16 * n_blk + 4 * n_hot * H * d + 2 * Hq * d
+    return int(b + (2 * Hq * d if with_out else 0))
 
 
-def append_bytes(n_new_tokens, H, d):
+def append_bytes(n_new_tokens, H, d, bits=8):
     """Per appended token once the hot zone is full: read K,V (4Hd), write the ring slot (4Hd),
-    read the spilled token (4Hd), write its codes (2Hd), write the tail shadow (4Hd), scales + header."""
-    return n_new_tokens * (18 * H * d + 8 * H + 16)
+    read the spilled token (4Hd), write its codes (2Hd x element bytes), write the tail shadow (4Hd),
+    scales + header."""
+    return int(n_new_tokens * ((16 + 2 * cold_elem_bytes(bits)) * H * d + 8 * H + 16))
 
 
 def sparse_bytes(n, H, Hq, d, k, T=32):
@@ -251,8 +259,8 @@ def decode_step_leg(hkv, torch, w, n0, steps, warmup, trials, R, label, fused=Tr
         step(i)
     res = timed_trials(torch, step, warmup, steps, trials)
     lens = res.pop("rets")
-    step_bytes = [B * (decode_bytes(n, H, Hq, d) + append_bytes(1, H, d)) for n in lens]
-    kern_bytes = step_bytes if fused else [B * decode_bytes(n, H, Hq, d) for n in lens]
+    step_bytes = [B * (decode_bytes(n, H, Hq, d, bits=quant_bits) + append_bytes(1, H, d, quant_bits)) for n in lens]
+    kern_bytes = step_bytes if fused else [B * decode_bytes(n, H, Hq, d, bits=quant_bits) for n in lens]
     # ---- self-check of the last timed step, outside the timed region
     last = res["next"] - 1
     r_last, q_last = last % R, qs[last % NQ]
@@ -270,7 +278,7 @@ def decode_step_leg(hkv, torch, w, n0, steps, warmup, trials, R, label, fused=Tr
         import oracle.hkv_oracle as orc
         k = wl.tokens(w, 0, 0, n_last, "k")
         v = wl.tokens(w, 0, 0, n_last, "v")
-        o_ref, _ = orc.decode(q_last.cpu().numpy()[0], orc.build_state(k, v, w.hot_tokens, w.block_size))
+        o_ref, _ = orc.decode(q_last.cpu().numpy()[0], orc.build_state(k, v, w.hot_tokens, w.block_size, quant_bits))
         record_check(out_close(got[0], o_ref, f"{label}: last timed output, sequence 0, vs the fp64 oracle"))
     for it in insts:
         it.c.close()
@@ -310,6 +318,27 @@ def leg_long(hkv, torch, args):
             "pct_hbm_peak": 100 * r["gbs"] / HBM_PEAK_GBS,
             "roofline": roofline("decode_kernel (fused append + decode, claim walk)", r["kernel_bytes_per_step"],
                                  r["device_ms_per_step"], "long")}
+
+
+def leg_width(hkv, torch, args, name, bits):
+    """The llama8b step or the 131072-token step with 4-bit cold blocks or an FP16 cold zone (Hybrid KV
+    Cache page 3.1: quantization_bits 4; 5.2: quantization_bits 0)."""
+    import workloads as wl
+    w = wl.WORKLOADS[name]
+    if name == "long":
+        steps, warmup, R, check = max(8, min(args.steps, 16)), 3, 2, False
+    else:
+        steps, warmup, R, check = args.steps, args.warmup, args.instances, True
+    label = f"{name} {'fp16' if bits == 0 else str(bits) + '-bit'} cold"
+    r = decode_step_leg(hkv, torch, w, w.context - 1, steps, warmup, args.trials, R, label, quant_bits=bits,
+                        oracle_check=check)
+    ms = r["ms_per_step"]
+    return {"workload": f"{name} workload, quant_bits {bits}, step = fused append 1 token + decode", "steps": steps,
+            "ms_per_step": ms, "trials_ms": r["trials_ms"], "gbs": r["gbs"],
+            "pct_hbm_peak": 100 * r["gbs"] / HBM_PEAK_GBS,
+            "queries_per_s": w.batch / (ms * 1e-3), "head_queries_per_s": w.batch * w.n_q_heads / (ms * 1e-3),
+            "roofline": roofline(f"decode_kernel (fused append + decode, {label})", r["kernel_bytes_per_step"],
+                                 r["device_ms_per_step"], f"{name}_b{bits}")}
 
 
 def leg_sparse(hkv, torch, args):
@@ -644,7 +673,8 @@ def copy_calibration(torch, mib=256, reps=4):
             "launches": reps}
 
 
-LEGS = ("llama8b", "separate", "long", "sparse", "ragged", "graph", "read_floor", "cpu")
+LEGS = ("llama8b", "separate", "long", "llama8b_int4", "long_int4", "llama8b_fp16", "long_fp16", "sparse", "ragged",
+        "graph", "read_floor", "cpu")
 
 
 def main():
@@ -703,6 +733,10 @@ def main():
         res["separate_calls"] = leg_separate(hkv, torch, args)
     if "long" in legs:
         res["long"] = leg_long(hkv, torch, args)
+    for name in ("llama8b", "long"):
+        for bits, tag in ((4, "int4"), (0, "fp16")):
+            if f"{name}_{tag}" in legs:
+                res[f"{name}_{tag}"] = leg_width(hkv, torch, args, name, bits)
     if "sparse" in legs:
         res["sparse"] = leg_sparse(hkv, torch, args)
     if "ragged" in legs:

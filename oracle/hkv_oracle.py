@@ -48,6 +48,13 @@ What is computed (readings where the pages are silent are marked READING):
    tokens.
 8. Header table sizing (Hybrid KV Cache page 5.4): one 16-byte header per
    cold block, blocks = ceil(cold tokens / block_size).
+10. Debug statistics (Hybrid KV Cache page 6.3: a kv_cache_debug switch logs
+   quantisation-error statistics every step; KV Cache reuse page 6: monitor
+   the attention entropy, whose sudden drop signals lost context).  READING:
+   the quantisation error of a (block, kv-head, K|V) tile is the largest
+   |x - x_hat| over its valid elements (0 for an FP16 cold zone), and the
+   entropy of a decode is -sum_t p_t ln p_t of each query head's attention
+   distribution over the tokens it attends.
 9. Cold-zone width (Hybrid KV Cache page 3.1: quantization_bits is 4 or 8,
    INT4 for L2 cold blocks; 5.2: quantization_bits 0 turns quantisation off
    and the cold zone stays FP16).  A b-bit code is the same symmetric absmax
@@ -302,6 +309,45 @@ def sparse_decode(q: np.ndarray, state: SequenceState, idx: np.ndarray,
                   heads: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Decode over the hot zone plus the selected cold tokens idx [H, k] (-1 entries ignored)."""
     return _decode_over(q, state, np.asarray(idx), heads)
+
+
+# --------------------------------------------------------------------------- debug statistics
+def quant_errors(k_hist: np.ndarray, v_hist: np.ndarray, hot_tokens: int, block_size: int,
+                 quant_bits: int = 8) -> np.ndarray:
+    """[n_blk, H, 2] fp64: max |x - q s| over the valid elements of every cold tile (0 for FP16 tiles)."""
+    st = build_state(k_hist, v_hist, hot_tokens, block_size, quant_bits)
+    k64 = np.asarray(k_hist, dtype=np.float16).astype(np.float64)
+    v64 = np.asarray(v_hist, dtype=np.float16).astype(np.float64)
+    err = np.zeros((st.n_blocks, st.hot_k.shape[1], 2))
+    for j in range(st.n_blocks):
+        nv = int(st.n_valid[j])
+        for c, x in enumerate((k64, v64)):
+            rows = x[j * block_size:j * block_size + nv]          # [nv, H, d]
+            for h in range(err.shape[1]):
+                xhat = dequantize(st.codes[j, h, c, :nv], st.scales[j, h, c])
+                err[j, h, c] = float(np.max(np.abs(rows[:, h, :] - xhat))) if nv else 0.0
+    return err
+
+
+def attention_entropy(q: np.ndarray, state: SequenceState, sel: Optional[np.ndarray] = None) -> np.ndarray:
+    """[Hq] fp64: -sum_t p_t ln p_t of each query head's softmax over the tokens decode attends (hot plus
+    cold, or hot plus the selected cold tokens when sel [H, k] is given)."""
+    q64 = np.asarray(q, dtype=np.float16).astype(np.float64)
+    n_q, d = q64.shape
+    g = _group(n_q, state.hot_k.shape[1])
+    ent = np.zeros(n_q)
+    for hq in range(n_q):
+        h = hq // g
+        ck, _ = cold_kv(state, h)
+        if sel is not None:
+            ck = ck[sel[h][sel[h] >= 0]]
+        keys = np.concatenate([ck, state.hot_k[:, h, :].astype(np.float64)])
+        z = keys @ q64[hq] / math.sqrt(d)
+        e = np.exp(z - np.max(z))
+        p = e / np.sum(e)
+        nz = p > 0
+        ent[hq] = -float(np.sum(p[nz] * np.log(p[nz])))
+    return ent
 
 
 # --------------------------------------------------------------------------- metadata sizing

@@ -527,6 +527,73 @@ def pin_topk_other_widths(orc, rng) -> None:
         assert np.array_equal(idx, brute_topk(q, k, 32, 64, n_kv, g, kk, bits)), bits
 
 
+# --------------------------------------------------------------------------- debug statistics
+def pin_quant_error_exact(orc, rng) -> None:
+    """The largest |x - q s| of each tile against exact rational arithmetic (codes and scales from the
+    exact helpers), for 8 and 4 bits; rounding bounds it by s/2; FP16 tiles and tiles of exact
+    multiples of the scale have error 0."""
+    for bits, lim in ((8, 127), (4, 7)):
+        n, n_kv, d = 32 + 2 * 64 + 9, 2, 8
+        k = rng_fp16(rng, (n, n_kv, d), 3.0)
+        v = rng_fp16(rng, (n, n_kv, d))
+        err = orc.quant_errors(k, v, 32, 64, bits)
+        n_cold = n - 32
+        for j in range(err.shape[0]):
+            rows = range(j * 64, min((j + 1) * 64, n_cold))
+            for h in range(n_kv):
+                for c, src in enumerate((k, v)):
+                    tile = np.array([src[t][h] for t in rows], dtype=np.float16)
+                    s = exact_scale(tile, lim)
+                    want = max(abs(Fraction(float(x)) - exact_code(float(x), s, lim) * Fraction(s)) for x in tile.ravel())
+                    assert Fraction(err[j, h, c]) == want, (bits, j, h, c)
+                    assert err[j, h, c] <= s / 2 * (1 + 2.0 ** -17)
+    ints = np.tile(np.arange(-63, 64, dtype=np.float16)[:, None, None], (1, 1, 4))[:96]
+    ints[0, 0, 0] = ints[64, 0, 0] = np.float16(127.0)   # each block's max is 127: s = 1, every value a multiple
+    hist = np.concatenate([ints, rng_fp16(rng, (32, 1, 4))])
+    assert np.all(orc.quant_errors(hist, hist, 32, 64, 8)[:, :, 0] == 0.0)
+    assert np.all(orc.quant_errors(hist, hist, 32, 64, 0) == 0.0)
+
+
+def pin_entropy(orc, rng) -> None:
+    """Entropy of the decode softmax: equal logits give ln n (zero query); one overwhelming token gives
+    ~0; explicit loops agree on a tiny shape; the sparse form covers exactly the selected tokens."""
+    n, n_kv, g, d = 200, 2, 2, 8
+    k = rng_fp16(rng, (n, n_kv, d))
+    v = rng_fp16(rng, (n, n_kv, d))
+    st = orc.build_state(k, v, 32, 64)
+    ent0 = orc.attention_entropy(np.zeros((n_kv * g, d), np.float16), st)
+    assert np.all(np.abs(ent0 - math.log(n)) < 1e-12)
+    kk = np.zeros((96, 1, d), dtype=np.float16)
+    kk[-1, 0, 0] = np.float16(64.0)
+    q1 = np.zeros((1, d), dtype=np.float16)
+    q1[0, 0] = np.float16(8.0)
+    assert orc.attention_entropy(q1, orc.build_state(kk, kk, 32, 64))[0] < 1e-60
+    q = rng_fp16(rng, (n_kv * g, d))
+    ent = orc.attention_entropy(q, st)
+    for hq in range(n_kv * g):
+        keys, _ = brute_history_kv(k, v, 32, 64, hq // g)
+        z = [sum(float(q[hq][c]) * kr[c] for c in range(d)) / math.sqrt(d) for kr in keys]
+        zm = max(z)
+        e = [math.exp(x - zm) for x in z]
+        tot = sum(e)
+        want = -sum((x / tot) * math.log(x / tot) for x in e if x > 0)
+        assert abs(ent[hq] - want) < 1e-12
+    idx = np.full((n_kv, 8), -1)
+    idx[0, :3] = [0, 5, 100]
+    idx[1, :2] = [7, 150]
+    ent_s = orc.attention_entropy(q, st, idx)
+    for hq in range(n_kv * g):
+        h = hq // g
+        keys, _ = brute_history_kv(k, v, 32, 64, h)
+        sel = [int(t) for t in idx[h] if t >= 0] + list(range(n - 32, n))
+        z = [sum(float(q[hq][c]) * keys[t][c] for c in range(d)) / math.sqrt(d) for t in sel]
+        zm = max(z)
+        e = [math.exp(x - zm) for x in z]
+        tot = sum(e)
+        want = -sum((x / tot) * math.log(x / tot) for x in e if x > 0)
+        assert abs(ent_s[hq] - want) < 1e-12
+
+
 ALL_PINS = [
     ("scale_exhaustive", lambda o, r: pin_scale_exhaustive(o)),
     ("codes_exact", pin_codes_exact),
@@ -550,4 +617,6 @@ ALL_PINS = [
     ("int4_cold_sdpa", pin_int4_cold_sdpa),
     ("fp16_cold_is_dense_attention", pin_fp16_cold_is_dense_attention),
     ("topk_other_widths", pin_topk_other_widths),
+    ("quant_error_exact", pin_quant_error_exact),
+    ("entropy", pin_entropy),
 ]

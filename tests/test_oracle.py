@@ -88,7 +88,18 @@ def _m_cosine_no_knorm(q, state):
     return out
 
 
-_REAL = {"build_state": orc.build_state, "quantize_block": orc.quantize_block}
+def _m_entropy_log2(q, state, sel=None):
+    return _REAL["attention_entropy"](q, state, sel) / np.log(2.0)
+
+
+def _m_quant_error_relative(k_hist, v_hist, hot, block, bits=8):
+    st = _REAL["build_state"](k_hist, v_hist, hot, block, bits)
+    err = _REAL["quant_errors"](k_hist, v_hist, hot, block, bits)
+    return err / np.where(st.scales > 0, st.scales, 1.0)
+
+
+_REAL = {"build_state": orc.build_state, "quantize_block": orc.quantize_block,
+         "attention_entropy": orc.attention_entropy, "quant_errors": orc.quant_errors}
 
 MUTANTS = [
     ("scale_divides_by_128", "block_scale", _m_scale_128),
@@ -102,6 +113,8 @@ MUTANTS = [
     ("int4_scale_divides_by_8", "block_scale", _m_int4_scale_8),
     ("int4_block_uses_the_int8_scale", "block_scale", _m_int4_with_int8_scale),
     ("fp16_cold_zone_quantised", "quantize_block", _m_fp16_cold_quantised),
+    ("entropy_in_bits_not_nats", "attention_entropy", _m_entropy_log2),
+    ("quant_error_relative_to_scale", "quant_errors", _m_quant_error_relative),
 ]
 
 
