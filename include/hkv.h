@@ -101,8 +101,20 @@ typedef struct {
  *   seq_len_dev   int32 [batch] device: tokens cached per sequence.
  *   seq_len_host  int32 [batch] host mirror of seq_len_dev, used to plan
  *            launches and check capacity; hkv_append updates both.
+ *   quant_err     optional (NULL = off) device fp32 [P][H][2]: debug statistic
+ *            (Hybrid KV Cache page 6.3, kv_cache_debug: quantisation-error
+ *            statistics).  Every append and fused step writes, for each
+ *            (block, kv-head, K|V) tile it codes, the largest |x - code*scale|
+ *            over the tile's valid elements, in fp32 (0 for fp16 tiles).
+ *   entropy       optional (NULL = off) device fp32 [batch][n_q_heads]: debug
+ *            statistic (KV Cache reuse page 6: monitor attention entropy).
+ *            Every decode (dense, sparse, fused, no-alloc) writes the entropy
+ *            -sum p ln p (nats) of each query head's softmax over the tokens it
+ *            attends, computed as lse - E_p[z] from the same fp32 online
+ *            softmax.
  * A new cache is all zero except headers[].phys_block; every buffer except
- * hot must be 16-byte aligned. */
+ * hot must be 16-byte aligned.  Both statistics cost a few instructions per
+ * block when enabled and nothing else. */
 typedef struct {
   int32_t batch;
   int32_t max_blocks_per_seq;
@@ -114,6 +126,8 @@ typedef struct {
   hkv_block_header* headers;
   int32_t* seq_len_dev;
   int32_t* seq_len_host;
+  float* quant_err;  /* optional debug statistic, NULL = off */
+  float* entropy;    /* optional debug statistic, NULL = off */
 } hkv_cache_desc;
 
 /* Bytes of every cache buffer, for one configuration (see hkv_cache_sizes). */

@@ -49,7 +49,8 @@ class CacheDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
                 ("num_phys_blocks", ctypes.c_int32), ("hot", ctypes.c_void_p), ("tail", ctypes.c_void_p),
                 ("cold", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("headers", ctypes.c_void_p),
-                ("seq_len_dev", ctypes.c_void_p), ("seq_len_host", ctypes.c_void_p)]
+                ("seq_len_dev", ctypes.c_void_p), ("seq_len_host", ctypes.c_void_p),
+                ("quant_err", ctypes.c_void_p), ("entropy", ctypes.c_void_p)]
 
 
 class CacheSizes(ctypes.Structure):
@@ -259,6 +260,22 @@ class HybridKVCache:
                               self.cold.data_ptr(), self.scales.data_ptr(), self.headers.data_ptr(),
                               self.seq_len.data_ptr(), self.seq_len_host.ctypes.data)
         self._ws = None
+
+    # -- debug statistics (optional descriptor fields)
+    def enable_debug(self, n_q_heads: int):
+        """Allocate and register the debug statistics: quant_err fp32 [P, H, 2] (written by appends for
+        every tile they code) and entropy fp32 [batch, n_q_heads] (written by every decode).  Returns
+        (quant_err, entropy)."""
+        torch = self.torch
+        self.quant_err = torch.zeros(max(self.num_phys * self.H * 2, 1), dtype=torch.float32, device=self.hot.device)
+        self.entropy = torch.full((self.batch, n_q_heads), float("nan"), dtype=torch.float32, device=self.hot.device)
+        self.desc.quant_err = self.quant_err.data_ptr()
+        self.desc.entropy = self.entropy.data_ptr()
+        return self.quant_err, self.entropy
+
+    def disable_debug(self) -> None:
+        self.desc.quant_err = None
+        self.desc.entropy = None
 
     # -- C-ABI wrappers bound to this cache
     def workspace(self, n_q_heads: int, k_sel: int = 0):

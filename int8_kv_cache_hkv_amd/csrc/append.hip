@@ -52,8 +52,10 @@ __device__ __forceinline__ uint32_t slice_half_bits(const u32x4_t (&x)[NV], int 
 
 // Stage the CPT elements of token t at channels [c0, c0 + CPT) of one tile: 8-/4-bit codes under
 // scale s (clamp(rint(fl32(x / s)), -L, L)), or the fp16 values.  kv selects the stage order.
+// Returns the largest |x - code * s| of these elements (fma: the exact difference rounded once to
+// fp32), 0 for fp16 tiles.
 template <int D, int BITS, int CPT, int NV>
-__device__ __forceinline__ void stage_row(int8_t* stage, const u32x4_t (&x)[NV], float s, int kv, int t, int c0) {
+__device__ __forceinline__ float stage_row(int8_t* stage, const u32x4_t (&x)[NV], float s, int kv, int t, int c0) {
   using TS = TileStage<D, BITS>;
   if constexpr (BITS == 0) {
     if (kv == 0) {
@@ -67,8 +69,10 @@ __device__ __forceinline__ void stage_row(int8_t* stage, const u32x4_t (&x)[NV],
       for (int e = 0; e < CPT; ++e)
         *reinterpret_cast<uint16_t*>(stage + (c0 + e) * TS::VROW + 2 * t) = static_cast<uint16_t>(slice_half_bits(x, e));
     }
+    return 0.f;
   } else {
     const float rs = __builtin_amdgcn_rcpf(s);
+    float err = 0.f;
     uint32_t q[CPT / 4];
 #pragma unroll
     for (int i = 0; i < CPT / 4; ++i) {
@@ -80,6 +84,7 @@ __device__ __forceinline__ void stage_row(int8_t* stage, const u32x4_t (&x)[NV],
         const float xv = (e & 1) ? half_hi(wd) : half_lo(wd);
         float qv = 0.f;
         if (s > 0.f) qv = quant_code<Fmt<BITS>::kLimit>(xv, s, rs);
+        err = fmaxf(err, __builtin_fabsf(fmaf(-qv, s, xv)));
         packed |= (static_cast<uint32_t>(static_cast<int>(qv)) & 0xffu) << (8 * k);
       }
       q[i] = packed;
@@ -92,7 +97,36 @@ __device__ __forceinline__ void stage_row(int8_t* stage, const u32x4_t (&x)[NV],
 #pragma unroll
       for (int e = 0; e < CPT; ++e) stage[(c0 + e) * TS::VROW + t] = static_cast<int8_t>(q[e / 4] >> (8 * (e % 4)));
     }
+    return err;
   }
+}
+
+// Largest value of v over the workgroup (every thread calls it; red holds kWaves floats).
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max_dpp(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) r = fmaxf(r, red[w]);
+  return r;
+}
+
+// Largest |x - code * s| over a row slice coded with scale s (8-bit codes; the codes are recomputed).
+template <int NV>
+__device__ __forceinline__ float slice_err8(const u32x4_t (&x)[NV], float s) {
+  if (!(s > 0.f)) return 0.f;
+  const float rs = __builtin_amdgcn_rcpf(s);
+  float err = 0.f;
+#pragma unroll
+  for (int v = 0; v < NV; ++v)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a = half_lo(x[v][i]), b = half_hi(x[v][i]);
+      err = fmaxf(err, __builtin_fabsf(fmaf(-quant_code<127>(a, s, rs), s, a)));
+      err = fmaxf(err, __builtin_fabsf(fmaf(-quant_code<127>(b, s, rs), s, b)));
+    }
+  return err;
 }
 
 // Write a whole staged tile in its chunk layout (16-byte vectors, coalesced).
@@ -131,6 +165,7 @@ __global__ __launch_bounds__(kThreads) void append_quant_kernel(AppendParams p) 
   constexpr int TB = Fmt<BITS>::template tile_bytes<D>();
   __shared__ __align__(16) int8_t stage[TileStage<D, BITS>::BYTES];
   __shared__ float red[kWaves];
+  __shared__ float rerr[kWaves];
 
   const CacheView& c = p.c;
   const int H = c.H, T = c.T;
@@ -191,11 +226,13 @@ __global__ __launch_bounds__(kThreads) void append_quant_kernel(AppendParams p) 
     for (int w = 1; w < kWaves; ++w) m = fmaxf(m, red[w]);
     // ---- s = fl32(m / L) (IEEE fp32 division), codes = clamp(rint(fl32(x / s)), -L, L)
     const float s = tile_scale<BITS>(m);
-    stage_row<D, BITS, CPT, NV>(stage, x, s, kv, t, part * CPT);
+    const float err = stage_row<D, BITS, CPT, NV>(stage, x, s, kv, t, part * CPT);
+    const float tile_err = c.quant_err ? block_max(err, rerr) : 0.f;  // (also the stage barrier)
     __syncthreads();
     // ---- write the tile in its streaming layout
     write_tile<D, BITS>(c.cold + tile_offset(phys, h, kv, H, TB), stage, kv, tid);
     if (tid == 0) c.scales[(static_cast<size_t>(phys) * H + h) * 2 + kv] = s;
+    if (tid == 0 && c.quant_err) c.quant_err[(static_cast<size_t>(phys) * H + h) * 2 + kv] = tile_err;
     __syncthreads();  // stage and red are reused by the V pass
   }
   if (h == 0 && tid == 0) {
@@ -296,6 +333,7 @@ __global__ __launch_bounds__(kThreads) void append_step_kernel(AppendParams p) {
   constexpr int TB = Fmt<BITS>::template tile_bytes<D>();
   __shared__ __align__(16) int8_t stage[TileStage<D, BITS>::BYTES];
   __shared__ float red[6][kWaves];
+  __shared__ float rerr[kWaves];
 
   // grid (kv-head, sequence of this launch): no index depends on a kernel argument, so every
   // argument the kernel uses is read in one round of scalar loads, before any branch
@@ -443,7 +481,15 @@ __global__ __launch_bounds__(kThreads) void append_step_kernel(AppendParams p) {
       if (phys[q] < 0 || phys[q] >= c.num_phys) continue;
       int8_t* tile = c.cold + tile_offset(phys[q], h, kv, H, TB);
       if (BITS == 8 && vo > 0 && m_new <= m_old) {
-        // ---- maximum unchanged: code only the new rows, in place
+        // ---- maximum unchanged: code only the new rows, in place (the debug error statistic
+        // covers every row: the old rows' codes are recomputed for it)
+        if (c.quant_err) {
+          const float so = m_old / 127.0f;
+          const float e = t < vo ? slice_err8(xo[kv], so) : (is_new ? slice_err8(xn[q][kv], so) : 0.f);
+          const float te = block_max(e, rerr);
+          if (tid == 0) c.quant_err[(static_cast<size_t>(phys[q]) * H + h) * 2 + kv] = te;
+          __syncthreads();  // rerr is reused
+        }
         if (is_new) {
           const float so = m_old / 127.0f;
           uint32_t qw[CPT / 4];
@@ -467,10 +513,12 @@ __global__ __launch_bounds__(kThreads) void append_step_kernel(AppendParams p) {
       u32x4_t xs[NV];
 #pragma unroll
       for (int v = 0; v < NV; ++v) xs[v] = t < vo ? xo[kv][v] : xn[q][kv][v];  // element-wise: no indexed arrays
-      stage_row<D, BITS, CPT, NV>(stage, xs, s, kv, t, part * CPT);
+      const float err = stage_row<D, BITS, CPT, NV>(stage, xs, s, kv, t, part * CPT);
+      const float tile_err = c.quant_err ? block_max(err, rerr) : 0.f;
       __syncthreads();
       write_tile<D, BITS>(tile, stage, kv, tid);
       if (tid == 0) c.scales[(static_cast<size_t>(phys[q]) * H + h) * 2 + kv] = s;
+      if (tid == 0 && c.quant_err) c.quant_err[(static_cast<size_t>(phys[q]) * H + h) * 2 + kv] = tile_err;
       __syncthreads();  // stage is reused
     }
     if (h == 0 && tid == 0 && j < c.max_blocks) {

@@ -77,6 +77,7 @@ struct DecodeSmem {
   alignas(16) _Float16 pw[kWaves][C::NQ][4][C::PROW]; // per-wave weights of the current unit (hi/lo)
   float wm[kWaves][C::NG];
   float wl[kWaves][C::NG];
+  float wz[kWaves][C::NG];                          // per-wave sums of w * logit (entropy statistic)
   alignas(16) float wacc[kWaves][C::NG][D];
 };
 
@@ -86,7 +87,7 @@ struct HotSmem {
   alignas(16) _Float16 qh[C::NQ][4][C::QROW];          // query rows (fp16), zero rows past G
   float acc[G][D];
   float z[C::NG][kHotChunk];               // softmax weights of the current chunk (rows stay 0 past cnt)
-  float m[C::NG], l[C::NG], alpha[C::NG];
+  float m[C::NG], l[C::NG], zs[C::NG], alpha[C::NG];
   alignas(16) _Float16 kv[kHotChunk * (2 * D + 8)];     // staged [K|V] rows of the current chunk (padded)
 };
 
@@ -102,6 +103,7 @@ struct WaveState {
   using C = Cfg<D, G>;
   float m[C::NG];                          // running max of base-2 logits (wave-uniform)
   float l[C::NG];                          // lane-partial sum of softmax weights
+  float zs[C::NG];                         // lane-partial sum of weight * logit (entropy statistic)
   float qb[C::NG];                         // bias * sum_k q[g][k] (wave-uniform; see Fmt::kBias)
   float4_t acc[C::NQ][C::NDL];             // out[4quad + r][64 pass + lane] (with the code offset)
 };
@@ -138,6 +140,7 @@ __device__ __forceinline__ void softmax_unit(WaveState<D, G>& st, DecodeSmem<D, 
       const float wv = PER_LANE_V ? pp * vw : pp;
       const float cf = be * vcoef;
       st.l[g] = fmaf(st.l[g], a, be * pp);
+      st.zs[g] = fmaf(st.zs[g], a, valid ? be * pp * z : 0.f);
       st.m[g] = mn;
       alpha[g] = a;
       coef[g] = cf;
@@ -620,11 +623,11 @@ __device__ __forceinline__ float2 load_coherent2(const float* p) {
                      __builtin_bit_cast(float, static_cast<uint32_t>(v >> 32)));
 }
 
-// Partial record of one split: m (base-2 log units), l, acc[D] for each of the
-// G query heads; records are 8-byte aligned (D + 2 is even).
+// Partial record of one split: m (base-2 log units), l, z (sum of weight * base-2 logit), 0 and
+// acc[D] for each of the G query heads; records are 16-byte aligned (D + 4 is a multiple of 4).
 template <int D>
 __device__ __forceinline__ float* partial_ptr(const DecodeParams& p, int bh, int split, int g) {
-  return p.partials + ((static_cast<size_t>(bh) * p.nparts + split) * p.G + g) * (D + 2);
+  return p.partials + ((static_cast<size_t>(bh) * p.nparts + split) * p.G + g) * (D + kRecHead);
 }
 
 // Query rows of one kv-head's group into LDS as fp16 (exact), 16 bytes per
@@ -717,6 +720,7 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
   for (int g = 0; g < NG; ++g) {
     st.m[g] = kNegInf;
     st.l[g] = 0.f;
+    st.zs[g] = 0.f;
     float qs = 0.f;
 #pragma unroll
     for (int k = lane; k < D; k += 64) qs += static_cast<float>(sm.qh[g / 4][g % 4][k]);
@@ -758,9 +762,11 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     const float lsum = wave_sum_dpp(st.l[g]);
+    const float zsum = wave_sum_dpp(st.zs[g]);
     if (lane == 0) {
       sm.wm[w][g] = st.m[g];
       sm.wl[w][g] = lsum;
+      sm.wz[w][g] = zsum;
     }
   }
 #pragma unroll
@@ -775,7 +781,7 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
     float M = kNegInf;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm.wm[ww][g]);
-    float L = 0.f, A0 = 0.f, A1 = 0.f;
+    float L = 0.f, Z = 0.f, A0 = 0.f, A1 = 0.f;
     if (M != kNegInf) {
 #pragma unroll
       for (int ww = 0; ww < kWaves; ++ww) {
@@ -783,13 +789,17 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
         const float f = exp2_approx(sm.wm[ww][g] - M);
         const float2 a = *reinterpret_cast<const float2*>(&sm.wacc[ww][g][d]);
         L = fmaf(f, sm.wl[ww][g], L);
+        Z = fmaf(f, sm.wz[ww][g], Z);
         A0 = fmaf(f, a.x, A0);
         A1 = fmaf(f, a.y, A1);
       }
     }
     float* pg = partial_ptr<D>(p, bh, split, g);
-    store_coherent2(pg + 2 + d, A0, A1);
-    if (d == 0) store_coherent2(pg, M, L);
+    store_coherent2(pg + kRecHead + d, A0, A1);
+    if (d == 0) {
+      store_coherent2(pg, M, L);
+      store_coherent2(pg + 2, Z, 0.f);
+    }
   }
 }
 
@@ -813,11 +823,12 @@ __device__ void hot_attend(const DecodeParams& p, HotSmem<D, G>& hm, int b, int 
   copy_query<D, G>(p.q + (static_cast<size_t>(b) * c.H * G + static_cast<size_t>(h) * G) * D, hm.qh, tid);
   for (int i = tid; i < G * D; i += kThreads) hm.acc[i / D][i % D] = 0.f;
   const _Float16* hot_bh = c.hot + static_cast<size_t>(bh) * c.T * 2 * D;
-  float m[NG], l[NG];  // wave 0's running softmax state (wave-uniform)
+  float m[NG], l[NG], zs[NG];  // wave 0's running softmax state (wave-uniform)
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     m[g] = kNegInf;
     l[g] = 0.f;
+    zs[g] = 0.f;
   }
   for (int base = 0; base < n_hot; base += kHotChunk) {
     const int cnt = min(kHotChunk, n_hot - base);
@@ -867,6 +878,7 @@ __device__ void hot_attend(const DecodeParams& p, HotSmem<D, G>& hm, int b, int 
           const float alpha = exp2_approx(m[g] - mn);
           const float pt = valid ? exp2_approx(z - mn) : 0.f;
           l[g] = l[g] * alpha + wave_sum_dpp(pt);
+          zs[g] = zs[g] * alpha + wave_sum_dpp(valid ? pt * z : 0.f);
           m[g] = mn;
           if (lane < kHotChunk) hm.z[g][lane] = pt;
           if (lane == 0) hm.alpha[g] = alpha;
@@ -887,6 +899,7 @@ __device__ void hot_attend(const DecodeParams& p, HotSmem<D, G>& hm, int b, int 
     for (int g = 0; g < NG; ++g) {
       hm.m[g] = m[g];
       hm.l[g] = l[g];
+      hm.zs[g] = zs[g];
     }
   }
   __syncthreads();
@@ -900,8 +913,11 @@ __device__ void hot_split(const DecodeParams& p, HotSmem<D, G>& hm, int b, int h
   for (int i = threadIdx.x; i < G * (D / 2); i += kThreads) {
     const int g = i / (D / 2), d = 2 * (i % (D / 2));
     float* pg = partial_ptr<D>(p, bh, p.nsplit, g);
-    store_coherent2(pg + 2 + d, hm.acc[g][d], hm.acc[g][d + 1]);
-    if (d == 0) store_coherent2(pg, hm.m[g], hm.l[g]);
+    store_coherent2(pg + kRecHead + d, hm.acc[g][d], hm.acc[g][d + 1]);
+    if (d == 0) {
+      store_coherent2(pg, hm.m[g], hm.l[g]);
+      store_coherent2(pg + 2, hm.zs[g], 0.f);
+    }
   }
 }
 
@@ -931,8 +947,11 @@ __device__ void hot_window_split(const DecodeParams& p, HotSmem<D, G>& hm, int b
   for (int i = threadIdx.x; i < G * (D / 2); i += kThreads) {
     const int g = i / (D / 2), d = 2 * (i % (D / 2));
     float* pg = partial_ptr<D>(p, bh, p.nsplit, g);
-    store_coherent2(pg + 2 + d, hm.acc[g][d], hm.acc[g][d + 1]);
-    if (d == 0) store_coherent2(pg, hm.m[g], hm.l[g]);
+    store_coherent2(pg + kRecHead + d, hm.acc[g][d], hm.acc[g][d + 1]);
+    if (d == 0) {
+      store_coherent2(pg, hm.m[g], hm.l[g]);
+      store_coherent2(pg + 2, hm.zs[g], 0.f);
+    }
   }
 }
 
@@ -945,6 +964,7 @@ struct AppendSmem {
   alignas(16) int8_t stage_k[kBlockSize * KROW];     // its K codes / values, [token][channel]
   alignas(16) int8_t stage_v[D * VROW];              // its V codes / values, [channel][token]
   float red[4][kWaves];
+  float rerr[2][kWaves];                             // debug statistic: per-wave largest |x - code * scale|
 };
 
 template <int D, int G, int BITS>
@@ -1069,6 +1089,7 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
         scl[kv] = sc;
         const float rsc = __builtin_amdgcn_rcpf(sc);
         uint32_t qw[CPT / 4];
+        float err = 0.f;
 #pragma unroll
         for (int i = 0; i < CPT / 4; ++i) {
           uint32_t packed = 0;
@@ -1078,10 +1099,13 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
             const uint32_t wd = x[kv][e / 8][(e % 8) / 2];
             const float xv = (e & 1) ? half_hi(wd) : half_lo(wd);
             const float qv = sc > 0.f ? quant_code<F::kLimit>(xv, sc, rsc) : 0.f;
+            err = fmaxf(err, __builtin_fabsf(fmaf(-qv, sc, xv)));
             packed |= (static_cast<uint32_t>(static_cast<int>(qv)) & 0xffu) << (8 * k);
           }
           qw[i] = packed;
         }
+        err = wave_max_dpp(err);
+        if (lane == 0) am.rerr[kv][w] = err;
         if (kv == 0) {
           uint32_t* srow = reinterpret_cast<uint32_t*>(am.stage_k + t * KROW + part * CPT);
 #pragma unroll
@@ -1106,6 +1130,12 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
       }
     }
     __syncthreads();  // stage complete
+    if (tid < 2 && c.quant_err) {  // debug statistic: the block's largest |x - code * scale| (0 for fp16)
+      float e = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) e = fmaxf(e, BITS == 0 ? 0.f : am.rerr[tid][ww]);
+      c.quant_err[(static_cast<size_t>(phys) * H + h) * 2 + tid] = e;
+    }
 #pragma unroll
     for (int kv = 0; kv < 2; ++kv) {
       int8_t* tile = c.cold + tile_offset(phys, h, kv, H, TB);
@@ -1164,12 +1194,13 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
 
   // ---- tail block jt, rows [0, ts], by wave 0 with the cold-unit code
   if (w == 0) {
-    float um[NG], ul[NG];
+    float um[NG], ul[NG], uz[NG];
     float4_t uacc[C::NQ][C::NDL];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       um[g] = kNegInf;
       ul[g] = 0.f;
+      uz[g] = 0.f;
     }
 #pragma unroll
     for (int quad = 0; quad < C::NQ; ++quad)
@@ -1190,6 +1221,7 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
       for (int g = 0; g < NG; ++g) {
         st.m[g] = kNegInf;
         st.l[g] = 0.f;
+        st.zs[g] = 0.f;
         float qs = 0.f;
 #pragma unroll
         for (int k = lane; k < D; k += 64) qs += static_cast<float>(am.unit.qh[g / 4][g % 4][k]);
@@ -1210,6 +1242,7 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
       for (int g = 0; g < NG; ++g) {
         um[g] = st.m[g];
         ul[g] = wave_sum_dpp(st.l[g]);
+        uz[g] = wave_sum_dpp(st.zs[g]);
       }
 #pragma unroll
       for (int quad = 0; quad < C::NQ; ++quad)
@@ -1221,6 +1254,7 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
       if (lane == 0) {
         am.unit.wm[0][g] = um[g];
         am.unit.wl[0][g] = ul[g];
+        am.unit.wz[0][g] = uz[g];
       }
 #pragma unroll
     for (int quad = 0; quad < C::NQ; ++quad)
@@ -1234,8 +1268,11 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
   for (int i = tid; i < G * (D / 2); i += kThreads) {
     const int g = i / (D / 2), d = 2 * (i % (D / 2));
     float* pg = partial_ptr<D>(p, bh, p.nsplit + 1, g);
-    store_coherent2(pg + 2 + d, am.unit.wacc[0][g][d], am.unit.wacc[0][g][d + 1]);
-    if (d == 0) store_coherent2(pg, am.unit.wm[0][g], am.unit.wl[0][g]);
+    store_coherent2(pg + kRecHead + d, am.unit.wacc[0][g][d], am.unit.wacc[0][g][d + 1]);
+    if (d == 0) {
+      store_coherent2(pg, am.unit.wm[0][g], am.unit.wl[0][g]);
+      store_coherent2(pg + 2, am.unit.wz[0][g], 0.f);
+    }
   }
 }
 
@@ -1282,23 +1319,28 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, const WgCoord
   if (!s_last) return;
   __builtin_amdgcn_s_setprio(3);  // the merge ends the (sequence, kv-head): ahead of streaming waves
   const int Hq = c.H * G;
-  constexpr int REC = G * (D + 2);  // floats per split record of one (sequence, kv-head)
+  constexpr int REC = G * (D + kRecHead);  // floats per split record of one (sequence, kv-head)
   const float* base_bh = p.partials + static_cast<size_t>(bh) * p.nparts * REC;
+  float* const entropy = c.entropy;
   for (int idx = tid; idx < G * (D / 2); idx += kThreads) {
     const int g = idx / (D / 2), d = 2 * (idx % (D / 2));
-    const int off_ml = g * (D + 2), off_a = off_ml + 2 + d;  // per lane; the split offset is uniform
-    float M = kNegInf, L = 0.f, A0 = 0.f, A1 = 0.f;
+    const int off_ml = g * (D + kRecHead), off_a = off_ml + kRecHead + d;  // per lane; the split offset is uniform
+    const bool want_z = entropy != nullptr && d == 0;  // the entropy statistic: the thread of column 0
+    float M = kNegInf, L = 0.f, Z = 0.f, A0 = 0.f, A1 = 0.f;
     for (int s0 = 0; s0 < NS; s0 += kMergeChunk) {
       float2 ml[kMergeChunk], av[kMergeChunk];
+      float zz[kMergeChunk];
 #pragma unroll
       for (int k = 0; k < kMergeChunk; ++k) {
         if (s0 + k < NS) {
           const float* rec = base_bh + (s0 + k) * REC;
           ml[k] = load_coherent2(rec + off_ml);
           av[k] = load_coherent2(rec + off_a);
+          zz[k] = want_z ? load_coherent2(rec + off_ml + 2).x : 0.f;
         } else {
           ml[k] = make_float2(kNegInf, 0.f);
           av[k] = make_float2(0.f, 0.f);
+          zz[k] = 0.f;
         }
       }
       float cm = kNegInf;
@@ -1308,12 +1350,14 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, const WgCoord
       if (Mn == kNegInf) continue;
       const float sc = exp2_approx(M - Mn);  // 0 while M is still -inf
       L *= sc;
+      Z *= sc;
       A0 *= sc;
       A1 *= sc;
 #pragma unroll
       for (int k = 0; k < kMergeChunk; ++k) {
         const float f = ml[k].x == kNegInf ? 0.f : exp2_approx(ml[k].x - Mn);
         L = fmaf(f, ml[k].y, L);
+        Z = fmaf(f, zz[k], Z);
         A0 = fmaf(f, av[k].x, A0);
         A1 = fmaf(f, av[k].y, A1);
       }
@@ -1323,6 +1367,8 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, const WgCoord
     const half2_t o = {static_cast<_Float16>(A0 / L), static_cast<_Float16>(A1 / L)};
     *reinterpret_cast<half2_t*>(&p.out[(static_cast<size_t>(b) * Hq + hq) * D + d]) = o;
     if (d == 0 && p.lse) p.lse[static_cast<size_t>(b) * Hq + hq] = (M + __builtin_log2f(L)) * kLn2;
+    // entropy -sum p ln p = lse - E_p[z] (z the natural-log logits): in base-2 units M + log2 L - Z / L
+    if (want_z) entropy[static_cast<size_t>(b) * Hq + hq] = (M + __builtin_log2f(L) - Z / L) * kLn2;
   }
   if (tid == 0) {
     __hip_atomic_store(&p.counters[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -218,6 +218,8 @@ hkv::CacheView view_of(const hkv_ctx* h, const hkv_cache_desc* c) {
   v.scales = c->scales;
   v.headers = c->headers;
   v.seq_len = c->seq_len_dev;
+  v.quant_err = c->quant_err;
+  v.entropy = c->entropy;
   return v;
 }
 
@@ -228,7 +230,7 @@ size_t partials_bytes(const hkv_ctx* h, const hkv_cache_desc* c, int G, int k_se
   int ns = max_splits(bh, std::max<int64_t>(1, c->max_blocks_per_seq));
   if (k_sel > 0) ns = std::max(ns, plan_sparse(k_sel).nsplit);
   // ns cold splits + the hot zone (+ the tail block of a fused append)
-  return static_cast<size_t>(bh) * (ns + 2) * G * (h->D + 2) * sizeof(float);
+  return static_cast<size_t>(bh) * (ns + 2) * G * (h->D + hkv::kRecHead) * sizeof(float);
 }
 
 // counters: [B*H] arrivals per (sequence, kv-head), [B] per sequence (fused append + decode), then

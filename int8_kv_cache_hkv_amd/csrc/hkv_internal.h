@@ -21,6 +21,7 @@ constexpr int kOrderTableMax = 512;  // (sequence, part) groups a table order ca
 constexpr int kClaimUnits = 16;     // plans with splits of at least this many units claim them dynamically
 constexpr int kClaimStride = 64;    // claim counters 256 bytes apart: one cache line each
 constexpr int kMaxSplits = 128;     // cold splits per (sequence, kv-head) at most
+constexpr int kRecHead = 4;         // floats before acc[D] in a partial record: m, l, z (sum of w * logit), 0
 // Fixed device scratch of hkv_decode_attn_noalloc, per GPU: the counters of every call live in the
 // first kScratchCounterBytes, the split partials after them, so the partials of one call never land
 // on the counters of another (every call leaves all of its counters at zero).
@@ -44,6 +45,8 @@ struct CacheView {
   float* scales;       // [P][H][2]
   hkv_block_header* headers;  // [B][max_blocks]
   int32_t* seq_len;    // [B]
+  float* quant_err;    // [P][H][2] debug statistic or nullptr
+  float* entropy;      // [B][H*G] debug statistic or nullptr
 };
 
 struct AppendParams {
@@ -65,7 +68,7 @@ struct DecodeParams {
   const _Float16* q;       // [B][H*G][D]
   const int32_t* sel;      // sparse mode: [B][H][k_sel]; nullptr for dense
   int k_sel;
-  float* partials;         // [B][H][nparts][G][D + 2]  (m in log2 units, l, acc[D]); then hot zone, tail block
+  float* partials;         // [B][H][nparts][G][D + 4]  (m in log2 units, l, z, 0, acc[D]); then hot zone, tail block
   unsigned* counters;      // [B*H] arrival counters, zero between calls
   int nsplit;              // cold splits per (sequence, kv-head)
   int nparts;              // partial records per (sequence, kv-head): nsplit + 1 (hot zone), + 1 more fused
