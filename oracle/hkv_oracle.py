@@ -48,6 +48,13 @@ What is computed (readings where the pages are silent are marked READING):
    tokens.
 8. Header table sizing (Hybrid KV Cache page 5.4): one 16-byte header per
    cold block, blocks = ceil(cold tokens / block_size).
+11. Compacted sparse store (KV Cache reuse page 2: the Index-Aware Cache
+   Layout re-packs the KV of the selected top-K tokens into a compact block
+   that is the only thing loaded; 2.1: aligned, padded blocks).  The store of
+   a (sequence, kv-head) is its selected cold rows in selection order (masked
+   and out-of-range entries skipped, duplicates kept), each with its own
+   block's K and V scales; decoding over the hot zone plus the store is the
+   sparse decode of item 7.
 10. Debug statistics (Hybrid KV Cache page 6.3: a kv_cache_debug switch logs
    quantisation-error statistics every step; KV Cache reuse page 6: monitor
    the attention entropy, whose sudden drop signals lost context).  READING:
@@ -309,6 +316,50 @@ def sparse_decode(q: np.ndarray, state: SequenceState, idx: np.ndarray,
                   heads: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Decode over the hot zone plus the selected cold tokens idx [H, k] (-1 entries ignored)."""
     return _decode_over(q, state, np.asarray(idx), heads)
+
+
+# --------------------------------------------------------------------------- compacted sparse store
+@dataclasses.dataclass
+class SparseStore:
+    """Selected cold rows of one sequence per kv-head, in selection order (KV Cache reuse page 2)."""
+    k_codes: list            # per kv-head: [m_h, d] codes (int8) or fp16 values
+    v_codes: list
+    k_scales: list           # per kv-head: [m_h] fp32 (the token's block scale)
+    v_scales: list
+    counts: np.ndarray       # int64 [H]: m_h, the valid entries of the selection
+
+
+def sparse_store(state: SequenceState, idx: np.ndarray) -> SparseStore:
+    """The compacted store of a selection idx [H, k]: for every entry 0 <= t < n_cold, the codes of
+    cold token t (block t // S, row t % S) and its block's scales; other entries are skipped."""
+    S = state.block_size
+    ks, vs, kss, vss, cnt = [], [], [], [], []
+    for h in range(idx.shape[0]):
+        rows = [int(t) for t in idx[h] if 0 <= int(t) < state.n_cold]
+        ks.append(np.array([state.codes[t // S, h, 0, t % S] for t in rows]).reshape(len(rows), -1))
+        vs.append(np.array([state.codes[t // S, h, 1, t % S] for t in rows]).reshape(len(rows), -1))
+        kss.append(np.array([state.scales[t // S, h, 0] for t in rows], dtype=np.float32))
+        vss.append(np.array([state.scales[t // S, h, 1] for t in rows], dtype=np.float32))
+        cnt.append(len(rows))
+    return SparseStore(ks, vs, kss, vss, np.array(cnt, dtype=np.int64))
+
+
+def decode_over_store(q: np.ndarray, state: SequenceState, store: SparseStore,
+                      heads: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Decode over the hot zone plus the rows of a compacted store (dequantised with their own scales)."""
+    q64 = np.asarray(q, dtype=np.float16).astype(np.float64)
+    n_q, d = q64.shape
+    g = _group(n_q, state.hot_k.shape[1])
+    out = np.full((n_q, d), np.nan)
+    lse = np.full(n_q, np.nan)
+    for hq in (range(n_q) if heads is None else heads):
+        h = hq // g
+        ck = store.k_codes[h].astype(np.float64) * store.k_scales[h].astype(np.float64)[:, None]
+        cv = store.v_codes[h].astype(np.float64) * store.v_scales[h].astype(np.float64)[:, None]
+        keys = np.concatenate([ck.reshape(-1, d), state.hot_k[:, h, :].astype(np.float64)])
+        vals = np.concatenate([cv.reshape(-1, d), state.hot_v[:, h, :].astype(np.float64)])
+        out[hq], lse[hq] = attend(q64[hq], keys, vals)
+    return out, lse
 
 
 # --------------------------------------------------------------------------- debug statistics

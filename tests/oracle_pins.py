@@ -594,6 +594,39 @@ def pin_entropy(orc, rng) -> None:
         assert abs(ent_s[hq] - want) < 1e-12
 
 
+# --------------------------------------------------------------------------- compacted sparse store
+def pin_sparse_store(orc, rng) -> None:
+    """The store holds exactly the selected rows (explicit loops over blocks and rows), in selection
+    order, with each row's own block scales; masked and out-of-range entries are skipped, duplicates
+    kept; decoding over it equals the sparse decode and SDPA over the selected dequantised rows."""
+    for bits in (8, 4, 0):
+        n, n_kv, g, d = 32 + 3 * 64 + 10, 2, 2, 8
+        k = rng_fp16(rng, (n, n_kv, d))
+        v = rng_fp16(rng, (n, n_kv, d))
+        q = rng_fp16(rng, (n_kv * g, d))
+        st = orc.build_state(k, v, 32, 64, bits)
+        n_cold = n - 32
+        idx = np.full((n_kv, 12), -1)
+        idx[0, :7] = [0, 3, 64, 150, 201, 3, n_cold + 5]     # a duplicate and an out-of-range entry
+        idx[1, :4] = [10, 11, 199, 63]
+        store = orc.sparse_store(st, idx)
+        keys, vals = zip(*[brute_history_kv(k, v, 32, 64, h, bits) for h in range(n_kv)])
+        want_rows = [[0, 3, 64, 150, 201, 3], [10, 11, 199, 63]]
+        assert store.counts.tolist() == [6, 4]
+        for h in range(n_kv):
+            for i, t in enumerate(want_rows[h]):
+                xk = store.k_codes[h][i].astype(np.float64) * float(store.k_scales[h][i])
+                xv = store.v_codes[h][i].astype(np.float64) * float(store.v_scales[h][i])
+                assert np.array_equal(xk, np.array(keys[h][t])) and np.array_equal(xv, np.array(vals[h][t]))
+        o1, l1 = orc.decode_over_store(q, st, store)
+        o2, l2 = orc.sparse_decode(q, st, np.where((idx >= 0) & (idx < n_cold), idx, -1))
+        assert np.max(np.abs(o1 - o2)) < 1e-12 and np.max(np.abs(l1 - l2)) < 1e-12
+        sel_k = [[keys[h][t] for t in want_rows[h]] + keys[h][n_cold:] for h in range(n_kv)]
+        sel_v = [[vals[h][t] for t in want_rows[h]] + vals[h][n_cold:] for h in range(n_kv)]
+        ref = _sdpa(q.astype(np.float64), sel_k, sel_v, g)
+        assert np.max(np.abs(o1 - ref)) < 1e-12
+
+
 ALL_PINS = [
     ("scale_exhaustive", lambda o, r: pin_scale_exhaustive(o)),
     ("codes_exact", pin_codes_exact),
@@ -619,4 +652,5 @@ ALL_PINS = [
     ("topk_other_widths", pin_topk_other_widths),
     ("quant_error_exact", pin_quant_error_exact),
     ("entropy", pin_entropy),
+    ("sparse_store", pin_sparse_store),
 ]

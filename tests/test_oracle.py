@@ -98,7 +98,16 @@ def _m_quant_error_relative(k_hist, v_hist, hot, block, bits=8):
     return err / np.where(st.scales > 0, st.scales, 1.0)
 
 
-_REAL = {"build_state": orc.build_state, "quantize_block": orc.quantize_block,
+def _m_store_block_scale_of_first(state, idx):
+    st = _REAL["sparse_store"](state, idx)
+    for h in range(len(st.k_scales)):   # every row dequantised with the first row's block scale
+        if len(st.k_scales[h]):
+            st.k_scales[h][:] = st.k_scales[h][0]
+            st.v_scales[h][:] = st.v_scales[h][0]
+    return st
+
+
+_REAL = {"build_state": orc.build_state, "quantize_block": orc.quantize_block, "sparse_store": orc.sparse_store,
          "attention_entropy": orc.attention_entropy, "quant_errors": orc.quant_errors}
 
 MUTANTS = [
@@ -115,6 +124,7 @@ MUTANTS = [
     ("fp16_cold_zone_quantised", "quantize_block", _m_fp16_cold_quantised),
     ("entropy_in_bits_not_nats", "attention_entropy", _m_entropy_log2),
     ("quant_error_relative_to_scale", "quant_errors", _m_quant_error_relative),
+    ("store_rows_share_one_scale", "sparse_store", _m_store_block_scale_of_first),
 ]
 
 
