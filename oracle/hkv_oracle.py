@@ -333,11 +333,12 @@ def sparse_store(state: SequenceState, idx: np.ndarray) -> SparseStore:
     """The compacted store of a selection idx [H, k]: for every entry 0 <= t < n_cold, the codes of
     cold token t (block t // S, row t % S) and its block's scales; other entries are skipped."""
     S = state.block_size
+    d = state.hot_k.shape[2]
     ks, vs, kss, vss, cnt = [], [], [], [], []
     for h in range(idx.shape[0]):
         rows = [int(t) for t in idx[h] if 0 <= int(t) < state.n_cold]
-        ks.append(np.array([state.codes[t // S, h, 0, t % S] for t in rows]).reshape(len(rows), -1))
-        vs.append(np.array([state.codes[t // S, h, 1, t % S] for t in rows]).reshape(len(rows), -1))
+        ks.append(np.array([state.codes[t // S, h, 0, t % S] for t in rows], dtype=state.codes.dtype).reshape(len(rows), d))
+        vs.append(np.array([state.codes[t // S, h, 1, t % S] for t in rows], dtype=state.codes.dtype).reshape(len(rows), d))
         kss.append(np.array([state.scales[t // S, h, 0] for t in rows], dtype=np.float32))
         vss.append(np.array([state.scales[t // S, h, 1] for t in rows], dtype=np.float32))
         cnt.append(len(rows))

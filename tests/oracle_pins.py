@@ -618,6 +618,8 @@ def pin_sparse_store(orc, rng) -> None:
                 xk = store.k_codes[h][i].astype(np.float64) * float(store.k_scales[h][i])
                 xv = store.v_codes[h][i].astype(np.float64) * float(store.v_scales[h][i])
                 assert np.array_equal(xk, np.array(keys[h][t])) and np.array_equal(xv, np.array(vals[h][t]))
+        empty = orc.sparse_store(st, np.full((n_kv, 4), -1))  # a selection with no valid entry
+        assert empty.counts.tolist() == [0] * n_kv and all(x.shape == (0, d) for x in empty.k_codes)
         o1, l1 = orc.decode_over_store(q, st, store)
         o2, l2 = orc.sparse_decode(q, st, np.where((idx >= 0) & (idx < n_cold), idx, -1))
         assert np.max(np.abs(o1 - o2)) < 1e-12 and np.max(np.abs(l1 - l2)) < 1e-12
