@@ -310,6 +310,44 @@ hkv_status hkv_append_decode(hkv_handle h, const hkv_cache_desc* c, const void* 
 hkv_status hkv_topk_select(hkv_handle h, const hkv_cache_desc* c, const void* q, int n_q_heads, int k,
                            int32_t* out_idx, void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Compacted sparse store (KV Cache reuse page 2: the Index-Aware Cache
+ * Layout re-packs the KV of the selected top-K tokens into a compact
+ * "effective" block, and only that block is loaded; 2.1: blocks aligned to
+ * 256 bytes and padded to a power of two).  A store holds, per (sequence,
+ * kv-head), the valid entries of a selection in selection order (-1 and
+ * out-of-range entries skipped, duplicates kept), in units of 64 tokens; a
+ * unit is one K tile and one V tile in the cold-block chunk layouts (2 x tile
+ * bytes: 16 KiB for 8-bit codes at head_dim 128), and every stored token keeps
+ * its own block's K and V scales.  Layout (this library's): int32 counts
+ * [batch][H]; at the next 256-byte boundary float2 scales
+ * [batch][H][U][64]; at the next 256-byte boundary the units
+ * [batch][H][U][2][tile bytes]; U = ceil(k_sel / 64).  The store is a copy:
+ * it describes the cache as it was when hkv_sparse_compact ran (an append
+ * that re-quantises a selected token's block is not reflected).
+ *
+ * Bytes of a store for `batch` sequences and selections of width k_sel.
+ * HKV_ERR_INVALID_VALUE: batch < 1 or k_sel outside [1, 512]. */
+hkv_status hkv_sparse_store_bytes(hkv_handle h, int batch, int k_sel, size_t* bytes);
+
+/* Build a compacted store from a selection.
+ *   sel_idx  device int32 [batch][n_kv_heads][k_sel] (as written by
+ *            hkv_topk_select; the entry rules of hkv_decode_attn).
+ *   store    device, 256-byte aligned, at least hkv_sparse_store_bytes.
+ * HKV_ERR_WORKSPACE: store_bytes too small.  HKV_ERR_UNSUPPORTED: block_size
+ * other than 64.  One launch of one workgroup per (unit, kv-head, sequence). */
+hkv_status hkv_sparse_compact(hkv_handle h, const hkv_cache_desc* c, const int32_t* sel_idx, int k_sel, void* store,
+                              size_t store_bytes, hipStream_t stream);
+
+/* Decode over the hot zone plus the tokens of a compacted store (built by
+ * hkv_sparse_compact for this cache, batch and k_sel): the result of the sparse
+ * hkv_decode_attn with the selection the store was built from, reading only
+ * the store's units and the hot zone.
+ *   workspace  at least hkv_workspace_bytes(h, c, n_q_heads, k_sel).
+ * Errors as hkv_decode_attn (sparse). */
+hkv_status hkv_decode_attn_compact(hkv_handle h, const hkv_cache_desc* c, const void* store, int k_sel, const void* q,
+                                   int n_q_heads, void* out, float* lse, void* workspace, size_t ws_bytes,
+                                   hipStream_t stream);
+
 /* Static, human-readable text for a status code. */
 const char* hkv_status_string(hkv_status st);
 
@@ -332,7 +370,9 @@ typedef enum {
   HKV_KERNEL_TOPK_SCORE = 4,
   HKV_KERNEL_TOPK_SELECT = 5,
   HKV_KERNEL_APPEND_DECODE = 6, /* fused one-token append + dense decode, one launch */
-  HKV_KERNEL_KINDS = 7
+  HKV_KERNEL_SPARSE_COMPACT = 7, /* building a compacted sparse store */
+  HKV_KERNEL_DECODE_COMPACT = 8, /* decode over a compacted sparse store */
+  HKV_KERNEL_KINDS = 9
 } hkv_kernel_kind;
 
 hkv_status hkv_timing_enable(hkv_handle h, int enable);

@@ -26,9 +26,10 @@ STATUS_NAMES = {0: "HKV_OK", -1: "HKV_ERR_INVALID_VALUE", -2: "HKV_ERR_UNSUPPORT
                 -4: "HKV_ERR_CAPACITY", -5: "HKV_ERR_WORKSPACE", -6: "HKV_ERR_HIP", -7: "HKV_ERR_ALIGNMENT",
                 -8: "HKV_ERR_OUT_OF_MEMORY"}
 KERNELS = {"append": 0, "append_ring": 1, "decode": 2, "decode_sparse": 3, "topk_score": 4, "topk_select": 5,
-           "append_decode": 6}
+           "append_decode": 6, "sparse_compact": 7, "decode_compact": 8}
 EXPORTS = ["hkv_create", "hkv_destroy", "hkv_cache_sizes", "hkv_sizes", "hkv_header_table_bytes", "hkv_workspace_bytes",
-           "hkv_append", "hkv_decode_attn", "hkv_decode_attn_noalloc", "hkv_append_decode", "hkv_topk_select", "hkv_status_string",
+           "hkv_append", "hkv_decode_attn", "hkv_decode_attn_noalloc", "hkv_append_decode",
+           "hkv_sparse_store_bytes", "hkv_sparse_compact", "hkv_decode_attn_compact", "hkv_topk_select", "hkv_status_string",
            "hkv_timing_enable",
            "hkv_timing_read", "hkv_last_error_detail", "hkv_read_probe"]
 
@@ -80,6 +81,9 @@ def _load() -> ctypes.CDLL:
         "hkv_decode_attn_noalloc": [vp, ctypes.POINTER(CacheDesc), vp, i32, vp, i32, vp, vp, vp],
         "hkv_append_decode": [vp, ctypes.POINTER(CacheDesc), vp, vp, vp, i32, vp, vp, vp, sz, vp],
         "hkv_topk_select": [vp, ctypes.POINTER(CacheDesc), vp, i32, i32, vp, vp, sz, vp],
+        "hkv_sparse_store_bytes": [vp, i32, i32, ctypes.POINTER(sz)],
+        "hkv_sparse_compact": [vp, ctypes.POINTER(CacheDesc), vp, i32, vp, sz, vp],
+        "hkv_decode_attn_compact": [vp, ctypes.POINTER(CacheDesc), vp, i32, vp, i32, vp, vp, vp, sz, vp],
         "hkv_timing_enable": [vp, i32],
         "hkv_timing_read": [vp, i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64), i32],
         "hkv_read_probe": [vp, sz, i32, i32, vp, vp],
@@ -212,6 +216,25 @@ def hkv_read_probe(src, nbytes: int, workgroups: int, threads: int, sink, stream
            "hkv_read_probe")
 
 
+def hkv_sparse_store_bytes(handle: int, batch: int, k_sel: int) -> int:
+    out = ctypes.c_size_t()
+    _check(_lib.hkv_sparse_store_bytes(handle, batch, k_sel, ctypes.byref(out)), "hkv_sparse_store_bytes")
+    return out.value
+
+
+def hkv_sparse_compact(handle: int, desc: CacheDesc, sel_idx, k_sel: int, store, stream=None) -> None:
+    _check(_lib.hkv_sparse_compact(handle, ctypes.byref(desc), _ptr(sel_idx), int(k_sel), _ptr(store),
+                                   int(store.numel() * store.element_size()), _stream(stream)), "hkv_sparse_compact")
+
+
+def hkv_decode_attn_compact(handle: int, desc: CacheDesc, store, k_sel: int, q, out, workspace, lse=None,
+                            stream=None) -> None:
+    _check(_lib.hkv_decode_attn_compact(handle, ctypes.byref(desc), _ptr(store), int(k_sel), _ptr(q), int(q.shape[1]),
+                                        _ptr(out), _ptr(lse), _ptr(workspace),
+                                        int(workspace.numel() * workspace.element_size()), _stream(stream)),
+           "hkv_decode_attn_compact")
+
+
 def hkv_timing_enable(handle: int, enable: bool = True) -> None:
     _check(_lib.hkv_timing_enable(handle, 1 if enable else 0), "hkv_timing_enable")
 
@@ -306,6 +329,41 @@ class HybridKVCache:
         ws = workspace if workspace is not None else self.workspace(int(q.shape[1]))
         hkv_append_decode(self.handle, self.desc, k_new, v_new, q, out, ws, lse=lse, stream=stream)
         return out
+
+    def sparse_store(self, sel_idx, k_sel: int, store=None, stream=None):
+        """Build a compacted sparse store of the selection sel_idx [batch, H, k_sel]; returns the store."""
+        torch = self.torch
+        if store is None:
+            store = torch.zeros(hkv_sparse_store_bytes(self.handle, self.batch, k_sel), dtype=torch.uint8,
+                                device=self.hot.device)
+        hkv_sparse_compact(self.handle, self.desc, sel_idx, k_sel, store, stream=stream)
+        return store
+
+    def decode_store(self, q, store, k_sel: int, out=None, lse=None, workspace=None, stream=None):
+        """Decode over the hot zone plus a compacted sparse store."""
+        torch = self.torch
+        if out is None:
+            out = torch.empty_like(q)
+        ws = workspace if workspace is not None else self.workspace(int(q.shape[1]), k_sel)
+        hkv_decode_attn_compact(self.handle, self.desc, store, k_sel, q, out, ws, lse=lse, stream=stream)
+        return out
+
+    def store_rows(self, store, k_sel: int):
+        """Host view of a store: (counts [B, H], k rows [B, H, U*64, D], v rows, scales [B, H, U*64, 2])."""
+        B, H, S, D = self.batch, self.H, self.S, self.D
+        U = -(-k_sel // S)
+        raw = store.cpu().numpy().view(np.uint8)
+        bh = B * H
+        scales_off = -(-(bh * 4) // 256) * 256
+        units_off = -(-(scales_off + bh * U * S * 8) // 256) * 256
+        counts = raw[:bh * 4].view(np.int32).reshape(B, H)
+        scales = raw[scales_off:scales_off + bh * U * S * 8].view(np.float32).reshape(B, H, U * S, 2)
+        TB = self._tile_bytes()
+        tiles = raw[units_off:units_off + bh * U * 2 * TB].reshape(bh * U, 2, TB)
+        rows = self._tiles_to_rows(tiles).reshape(B, H, U, 2, S, D)
+        k_rows = rows[:, :, :, 0].reshape(B, H, U * S, D)
+        v_rows = rows[:, :, :, 1].reshape(B, H, U * S, D)
+        return counts, k_rows, v_rows, scales
 
     def topk(self, q, k: int, out_idx=None, workspace=None, stream=None):
         torch = self.torch

@@ -56,6 +56,9 @@ namespace hkv {
 namespace detail {
 
 constexpr float kNegInf = -__builtin_inff();
+constexpr int kModeDense = 0;   // cold blocks of the header table
+constexpr int kModeGather = 1;  // selected tokens gathered from their blocks (sel_idx)
+constexpr int kModeStore = 2;   // units of a compacted sparse store
 constexpr int kHotChunk = 32;         // hot-zone slots staged through LDS at a time
 constexpr int kMergeChunk = 16;       // partials whose loads are in flight together in the merge
 constexpr int kHoldUnits = 8;         // splits of at most this many units hold their first tiles ...
@@ -606,6 +609,42 @@ __device__ void gather_unit(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const Cac
   wave_lds_sync();
 }
 
+// ---------------------------------------------------------------- compacted store units
+// Unit u (64 stored tokens) of a (sequence, kv-head) of a compacted sparse store: a K tile and a V
+// tile in the cold-block chunk layouts, read like a dense block, and each token's own (K, V) scales
+// (lane = token).  The logit scale is per lane and the value weight is taken relative to the unit's
+// largest V scale, as for gathered tokens.  count: the stored tokens of the (sequence, kv-head).
+template <int D, int G, int BITS>
+__device__ void store_unit(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const DecodeParams& p, int bh, int u, int count,
+                           int w, int lane) {
+  using C = Cfg<D, G>;
+  constexpr int S = kBlockSize;
+  constexpr int E = Fmt<BITS>::kElems;
+  constexpr int TB = Fmt<BITS>::template tile_bytes<D>();
+  const size_t unit = static_cast<size_t>(bh) * p.store_units + u;
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(p.store_units_base + unit * 2 * TB, 2u * TB);
+  Tiles<D, BITS> t;
+  issue_k<D, BITS>(t, r, lane);
+  const uint32_t lo = static_cast<uint32_t>(lane) * 16u;
+#pragma unroll
+  for (int ps = 0; ps < D / 64; ++ps)
+#pragma unroll
+    for (int vc = 0; vc < S / E; ++vc) t.vr[ps][vc] = load_stream_buf(r, lo + TB + (vc * D + 64 * ps) * 16);
+  const float2 sc = p.store_scales[unit * S + lane];
+  const bool valid = lane < count - u * S;
+  float4_t s[C::NQ];
+  qk_codes<D, G, BITS>(t.kr, sm, lane, s);
+  const float sv = valid ? sc.y : 0.f;
+  const float vmax = wave_max_dpp(sv);
+  const float vw = vmax > 0.f ? sv * __builtin_amdgcn_rcpf(vmax) : 0.f;
+  float alpha[C::NG], coef[C::NG];
+  softmax_unit<D, G, true>(st, sm, s, valid, sc.x * p.qscale, vw, vmax, alpha, coef, w, lane);
+  BlockAcc<D, G> blk;
+  pv_dense<D, G, BITS>(blk, sm, t.vr, w, lane);
+  fold_block<D, G>(st, blk, alpha, coef);
+  wave_lds_sync();
+}
+
 // Partials are exchanged between workgroups that may sit on different XCDs
 // (each with its own L2).  They are written and read with agent-scope relaxed
 // atomic accesses (device-coherent sc1 loads/stores, 8 bytes each), so
@@ -644,7 +683,7 @@ __device__ __forceinline__ void copy_query(const _Float16* qg, _Float16 (*qh)[4]
 }
 
 // ---- cold split: stream its units, merge the 4 waves, write the partial
-template <int D, int G, int BITS, bool SPARSE, bool FUSED, bool CLAIM>
+template <int D, int G, int BITS, int MODE, bool FUSED, bool CLAIM>
 __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, int h, int bh, int split) {
   using C = Cfg<D, G>;
   constexpr int S = kBlockSize;
@@ -674,11 +713,16 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
   Tiles<D, BITS> t0;
   float2 sc0 = make_float2(0.f, 0.f);
   int phys0 = -1, hb = -1;
+  constexpr bool SPARSE = MODE == kModeGather;
   const int32_t* sel_bh = SPARSE ? p.sel + static_cast<size_t>(bh) * p.k_sel : nullptr;
+  // store mode: the (sequence, kv-head)'s stored token count, with the first round
+  const int count_lane = MODE == kModeStore ? p.store_counts[opaque_index(bh)] : 0;
   int sel0 = -1;  // sparse: this wave's first unit's selection entry, requested with the query
   unsigned cl0 = 0;  // claim walk: the first claim
   if (SPARSE) {
     sel0 = sel_entry(sel_bh, p.k_sel, split * p.units_per_split + w, lane);
+  } else if constexpr (MODE == kModeStore) {
+    // the units are read in the walk
   } else if constexpr (CLAIM) {
     // claim walk: the first unit is split * 4 + w; the first claim travels with the first round
     hb = header_load(c, b, split * kWaves + w);
@@ -713,7 +757,11 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
   const SeqGeom sg = seq_geom(__builtin_amdgcn_readfirstlane(n_seq_lane), c.T, S);
   // fused append: only the full blocks before the one the appended token spills into (n_cold is
   // the count before the append, so the block holding cold token n_cold is excluded)
-  const int units = sg.n_cold > 0 ? (SPARSE ? cdiv(p.k_sel, kSparseUnit) : (FUSED ? sg.n_cold / S : sg.n_blk)) : 0;
+  const int store_count = MODE == kModeStore ? __builtin_amdgcn_readfirstlane(count_lane) : 0;
+  // (a store holds at most store_units units per (sequence, kv-head): a count from a store built for
+  // another width never walks past it)
+  const int units = MODE == kModeStore ? min(cdiv(max(store_count, 0), S), p.store_units)
+                    : (sg.n_cold > 0 ? (SPARSE ? cdiv(p.k_sel, kSparseUnit) : (FUSED ? sg.n_cold / S : sg.n_blk)) : 0);
 
   WaveState<D, G> st;
 #pragma unroll
@@ -739,6 +787,12 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
         const int idx = (run == split && u == run * CU + w) ? sel0 : sel_entry(sel_bh, p.k_sel, u, lane);
         gather_unit<D, G, BITS>(st, sm, c, idx, b, h, sg.n_cold, p.qscale, w, lane);
       }
+    }
+  } else if constexpr (MODE == kModeStore) {
+    const int CU = p.units_per_split;
+    for (int run = split; run * CU < units; run += p.nsplit) {
+      const int u_end = min(units, (run + 1) * CU);
+      for (int u = run * CU + w; u < u_end; u += kWaves) store_unit<D, G, BITS>(st, sm, p, bh, u, store_count, w, lane);
     }
   } else if constexpr (CLAIM) {
     const int u0 = split * kWaves + w;
@@ -1284,7 +1338,7 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
 // the workspace, which the merging workgroup resets to zero.  The merge runs
 // online over groups of kMergeChunk partials whose loads are all in flight
 // together; thread i owns two adjacent output columns of one query head.
-template <int D, int G, int BITS, bool SPARSE, bool FUSED, bool CLAIM>
+template <int D, int G, int BITS, int MODE, bool FUSED, bool CLAIM>
 __device__ __forceinline__ void decode_body(const DecodeParams& p, const WgCoord wg) {
   using AppendPart = typename std::conditional<FUSED, AppendSmem<D, G, BITS>, DecodeSmem<D, G>>::type;
   __shared__ union Smem {
@@ -1300,7 +1354,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, const WgCoord
   const int bh = b * c.H + h;
   const int tid = threadIdx.x;
   if (split < p.nsplit) {
-    cold_split<D, G, BITS, SPARSE, FUSED, CLAIM>(p, sm.cold, b, h, bh, split);
+    cold_split<D, G, BITS, MODE, FUSED, CLAIM>(p, sm.cold, b, h, bh, split);
   } else if constexpr (FUSED) {
     if (split == p.nsplit) hot_window_split<D, G>(p, sm.hot, b, h, bh);
     else append_unit_split<D, G, BITS>(p, sm.app, b, h, bh);
@@ -1401,11 +1455,11 @@ __device__ __forceinline__ void consume_args(const DecodeParams& p) {
 template <int G, int BITS>
 constexpr int decode_waves() { return (G > 4 || BITS == 0) ? 2 : 4; }
 
-template <int D, int G, int BITS, bool SPARSE, bool FUSED, bool CLAIM>
+template <int D, int G, int BITS, int MODE, bool FUSED, bool CLAIM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves<G, BITS>()))) void decode_kernel(
     DecodeParams p) {
   consume_args(p);
-  decode_body<D, G, BITS, SPARSE, FUSED, CLAIM>(p, wg_coord(p.wg_order));
+  decode_body<D, G, BITS, MODE, FUSED, CLAIM>(p, wg_coord(p.wg_order));
 }
 
 // Batch plans: the same grid read in the host-built order of the table (see wg_coord_table); a kernel
@@ -1414,7 +1468,7 @@ template <int D, int G, int BITS, bool FUSED, bool CLAIM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves<G, BITS>()))) void
 decode_kernel_ordered(DecodeParamsOrdered po) {
   consume_args(po.p);
-  decode_body<D, G, BITS, false, FUSED, CLAIM>(po.p, wg_coord_table(po.order));
+  decode_body<D, G, BITS, kModeDense, FUSED, CLAIM>(po.p, wg_coord_table(po.order));
 }
 
 template <typename K, typename P>
@@ -1442,11 +1496,12 @@ hipError_t launch_dg(const DecodeParams& p, const LaunchCtx& ctx, const uint16_t
                    : launch_k(decode_kernel_ordered<D, G, BITS, false, false>, grid, kThreads, po, ctx);
   }
   if (p.k_new)
-    return p.work ? launch_k(decode_kernel<D, G, BITS, false, true, true>, grid, kThreads, p, ctx)
-                  : launch_k(decode_kernel<D, G, BITS, false, true, false>, grid, kThreads, p, ctx);
-  if (p.sel) return launch_k(decode_kernel<D, G, BITS, true, false, false>, grid, kThreads, p, ctx);
-  return p.work ? launch_k(decode_kernel<D, G, BITS, false, false, true>, grid, kThreads, p, ctx)
-                : launch_k(decode_kernel<D, G, BITS, false, false, false>, grid, kThreads, p, ctx);
+    return p.work ? launch_k(decode_kernel<D, G, BITS, kModeDense, true, true>, grid, kThreads, p, ctx)
+                  : launch_k(decode_kernel<D, G, BITS, kModeDense, true, false>, grid, kThreads, p, ctx);
+  if (p.store_units_base) return launch_k(decode_kernel<D, G, BITS, kModeStore, false, false>, grid, kThreads, p, ctx);
+  if (p.sel) return launch_k(decode_kernel<D, G, BITS, kModeGather, false, false>, grid, kThreads, p, ctx);
+  return p.work ? launch_k(decode_kernel<D, G, BITS, kModeDense, false, true>, grid, kThreads, p, ctx)
+                : launch_k(decode_kernel<D, G, BITS, kModeDense, false, false>, grid, kThreads, p, ctx);
 }
 
 }  // namespace detail

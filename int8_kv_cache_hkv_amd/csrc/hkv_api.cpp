@@ -188,6 +188,22 @@ size_t tile_bytes(const hkv_ctx* h) {
   return h->bits == 0 ? elems * 2 : elems * h->bits / 8;
 }
 
+// Compacted sparse store: counts int32 [B*H], then (256-byte aligned) the per-token scales float2
+// [B*H][U][64], then (256-byte aligned) the units [B*H][U][2][tile bytes]; U = ceil(k_sel / 64).
+struct StoreLayout {
+  int units;
+  size_t scales_off, units_off, bytes;
+};
+StoreLayout store_layout(const hkv_ctx* h, int batch, int k_sel) {
+  StoreLayout l;
+  l.units = (k_sel + hkv::kBlockSize - 1) / hkv::kBlockSize;
+  const size_t bh = static_cast<size_t>(batch) * h->H;
+  l.scales_off = align_up(bh * sizeof(int32_t), 256);
+  l.units_off = align_up(l.scales_off + bh * l.units * hkv::kBlockSize * 2 * sizeof(float), 256);
+  l.bytes = l.units_off + bh * l.units * 2 * tile_bytes(h);
+  return l;
+}
+
 hkv_status check_desc(const hkv_ctx* h, const hkv_cache_desc* c) {
   if (!h || !c) return HKV_ERR_NULL_POINTER;
   if (!c->hot || !c->tail || !c->cold || !c->scales || !c->headers || !c->seq_len_dev || !c->seq_len_host)
@@ -344,6 +360,10 @@ hkv_status decode_impl(hkv_ctx* h, const hkv_cache_desc* c, const void* q, int n
   p.lse = lse;
   p.k_new = p.v_new = nullptr;
   p.seq_counters = nullptr;
+  p.store_units_base = nullptr;
+  p.store_scales = nullptr;
+  p.store_counts = nullptr;
+  p.store_units = 0;
   LaunchCtx a = make_ctx(h, stream, sel_idx ? HKV_KERNEL_DECODE_SPARSE : HKV_KERNEL_DECODE);
   return hip_status(hkv::launch_decode(p, a, ordered ? order : nullptr),
                     scratch ? "hkv_decode_attn_noalloc launch" : "hkv_decode_attn launch");
@@ -587,11 +607,104 @@ hkv_status hkv_append_decode(hkv_handle h, const hkv_cache_desc* c, const void* 
     p.lse = lse;
     p.k_new = static_cast<const _Float16*>(k_new);
     p.v_new = static_cast<const _Float16*>(v_new);
+    p.store_units_base = nullptr;
+    p.store_scales = nullptr;
+    p.store_counts = nullptr;
+    p.store_units = 0;
     LaunchCtx a = make_ctx(h, stream, HKV_KERNEL_APPEND_DECODE);
     const hkv_status r = hip_status(hkv::launch_decode(p, a, ordered ? order : nullptr), "hkv_append_decode launch");
     if (r != HKV_OK) return r;
     for (int b = 0; b < c->batch; ++b) c->seq_len_host[b] += 1;
     return HKV_OK;
+  });
+}
+
+hkv_status hkv_sparse_store_bytes(hkv_handle h, int batch, int k_sel, size_t* bytes) {
+  if (!h || !bytes) return HKV_ERR_NULL_POINTER;
+  if (batch < 1 || k_sel < 1 || k_sel > hkv::kMaxTopK) return HKV_ERR_INVALID_VALUE;
+  *bytes = store_layout(h, batch, k_sel).bytes;
+  return HKV_OK;
+}
+
+hkv_status hkv_sparse_compact(hkv_handle h, const hkv_cache_desc* c, const int32_t* sel_idx, int k_sel, void* store,
+                              size_t store_bytes, hipStream_t stream) {
+  return guarded([&]() -> hkv_status {
+    hkv_status st = check_desc(h, c);
+    if (st != HKV_OK) return st;
+    if (!sel_idx || !store) return HKV_ERR_NULL_POINTER;
+    if (k_sel < 1 || k_sel > hkv::kMaxTopK) return HKV_ERR_INVALID_VALUE;
+    if (h->S != hkv::kBlockSize) return HKV_ERR_UNSUPPORTED;
+    const StoreLayout l = store_layout(h, c->batch, k_sel);
+    if (store_bytes < l.bytes) return HKV_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(store) % 256 != 0 || reinterpret_cast<uintptr_t>(sel_idx) % 4 != 0)
+      return HKV_ERR_ALIGNMENT;
+    if (h->timing) {
+      h->pending.reserve(h->pending.size() + 1);
+      h->free_events.reserve(h->free_events.size() + 2);
+    }
+    hkv::CompactParams p;
+    p.c = view_of(h, c);
+    p.sel = sel_idx;
+    p.k_sel = k_sel;
+    p.units = l.units;
+    p.counts = static_cast<int32_t*>(store);
+    p.scales = reinterpret_cast<float2*>(static_cast<char*>(store) + l.scales_off);
+    p.units_base = static_cast<int8_t*>(store) + l.units_off;
+    LaunchCtx a = make_ctx(h, stream, HKV_KERNEL_SPARSE_COMPACT);
+    return hip_status(hkv::launch_compact(p, a), "hkv_sparse_compact launch");
+  });
+}
+
+hkv_status hkv_decode_attn_compact(hkv_handle h, const hkv_cache_desc* c, const void* store, int k_sel, const void* q,
+                                   int n_q_heads, void* out, float* lse, void* workspace, size_t ws_bytes,
+                                   hipStream_t stream) {
+  return guarded([&]() -> hkv_status {
+    hkv_status st = check_desc(h, c);
+    if (st != HKV_OK) return st;
+    if (!store || !q || !out) return HKV_ERR_NULL_POINTER;
+    if (n_q_heads < 1 || n_q_heads % h->H != 0) return HKV_ERR_INVALID_VALUE;
+    const int G = n_q_heads / h->H;
+    if (k_sel < 1 || k_sel > hkv::kMaxTopK) return HKV_ERR_INVALID_VALUE;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return HKV_ERR_UNSUPPORTED;
+    if (h->S != hkv::kBlockSize) return HKV_ERR_UNSUPPORTED;
+    for (int b = 0; b < c->batch; ++b)
+      if (c->seq_len_host[b] == 0) return HKV_ERR_INVALID_VALUE;
+    size_t need = 0;
+    if (hkv_workspace_bytes(h, c, n_q_heads, k_sel, &need) != HKV_OK) return HKV_ERR_INVALID_VALUE;
+    if (!workspace || ws_bytes < need) return HKV_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0 || reinterpret_cast<uintptr_t>(q) % 16 != 0 ||
+        reinterpret_cast<uintptr_t>(store) % 256 != 0)
+      return HKV_ERR_ALIGNMENT;
+    if (h->timing) {
+      h->pending.reserve(h->pending.size() + 1);
+      h->free_events.reserve(h->free_events.size() + 2);
+    }
+    const StoreLayout l = store_layout(h, c->batch, k_sel);
+    hkv::DecodeParams p;
+    p.c = view_of(h, c);
+    p.G = G;
+    p.q = static_cast<const _Float16*>(q);
+    p.sel = nullptr;
+    p.k_sel = k_sel;
+    p.counters = static_cast<unsigned*>(workspace);
+    p.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(counters_bytes(c, h->H), 256));
+    // one unit of 64 stored tokens per wave: every unit of the call is in flight at once
+    p.units_per_split = hkv::kWaves;
+    p.nsplit = (l.units + hkv::kWaves - 1) / hkv::kWaves;
+    p.nparts = p.nsplit + 1;
+    p.wg_order = hkv::kOrderPlain;
+    p.work = nullptr;
+    p.qscale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(h->D)));
+    p.out = static_cast<_Float16*>(out);
+    p.lse = lse;
+    p.k_new = p.v_new = nullptr;
+    p.seq_counters = nullptr;
+    p.store_counts = static_cast<const int32_t*>(store);
+    p.store_scales = reinterpret_cast<const float2*>(static_cast<const char*>(store) + l.scales_off);
+    p.store_units_base = static_cast<const int8_t*>(store) + l.units_off;
+    p.store_units = l.units;
+    LaunchCtx a = make_ctx(h, stream, HKV_KERNEL_DECODE_COMPACT);
+    return hip_status(hkv::launch_decode(p, a, nullptr), "hkv_decode_attn_compact launch");
   });
 }
 

@@ -82,6 +82,23 @@ struct DecodeParams {
   const _Float16* k_new;   // [B][H][D]
   const _Float16* v_new;   // [B][H][D]
   unsigned* seq_counters;  // [B] merged-head counters, zero between calls
+  // decode over a compacted sparse store (CompactParams layout); store_units_base nullptr otherwise
+  const int8_t* store_units_base;
+  const float2* store_scales;
+  const int32_t* store_counts;
+  int store_units;
+};
+
+// Compacted sparse store of a selection (see compact.hip): per (sequence, kv-head) `units` units of
+// 64 tokens, each a K tile and a V tile in the cold-block chunk layouts.
+struct CompactParams {
+  CacheView c;
+  const int32_t* sel;      // [B][H][k_sel]
+  int k_sel;
+  int units;               // units per (sequence, kv-head) = ceil(k_sel / 64)
+  int32_t* counts;         // [B*H] stored tokens
+  float2* scales;          // [B*H][units][64] (K scale, V scale) of each stored token
+  int8_t* units_base;      // [B*H][units][2][tile bytes]
 };
 
 // Arguments of the table-ordered decode launch (batch plans): the (sequence << 7 | part) groups
@@ -116,6 +133,7 @@ hipError_t launch_topk(const TopkParams& p, const LaunchCtx& score_ctx, const La
 // Device address of the fixed scratch array on the current device (set up on first use: address
 // taken with hipGetSymbolAddress, array cleared on `stream`).
 hipError_t scratch_for_device(hipStream_t stream, void** out);
+hipError_t launch_compact(const CompactParams& p, const LaunchCtx& ctx);
 hipError_t launch_read_probe(const void* src, size_t bytes, int workgroups, int threads, uint32_t* sink,
                              const LaunchCtx& ctx);
 
