@@ -120,6 +120,21 @@ def sparse_bytes(n, H, Hq, d, k, T=32):
     return 2 * sel * H * d + 8 * sel * H + 16 * sel + 4 * n_hot * H * d + 4 * Hq * d + 4 * H * k
 
 
+def store_decode_bytes(n, H, Hq, d, k, T=32):
+    """Decode over a compacted sparse store of one sequence: the stored tokens' int8 K and V codes and
+    their own scales, the counts, the hot zone, q in / out."""
+    n_hot = min(n, T)
+    sel = min(k, n - n_hot)
+    return 2 * sel * H * d + 8 * sel * H + 4 * H + 4 * n_hot * H * d + 4 * Hq * d
+
+
+def compact_bytes(n, H, d, k, T=32):
+    """Building the compacted store of one sequence: read the selection and the selected tokens' headers,
+    codes and scales, write the codes, scales and counts."""
+    sel = min(k, n - min(n, T))
+    return 4 * H * k + 16 * sel * H + 2 * (2 * sel * H * d + 8 * sel * H) + 4 * H
+
+
 def topk_bytes(n, H, Hq, d, k, T=32):
     """Top-K selection of one sequence: the int8 K codes of the cold tokens (the scale cancels in a
     cosine), the headers, the query and the index list written."""
@@ -376,9 +391,29 @@ def leg_sparse(hkv, torch, args):
         topk_only(i)
         sparse_only(i)
 
+    stores = [c.sparse_store(idx, k) for c in insts]
+    out_st = torch.empty_like(q)
+
+    def compact_only(i):
+        insts[i % 2].sparse_store(idx, k, store=stores[i % 2])
+
+    def store_only(i):
+        insts[i % 2].decode_store(q, stores[i % 2], k, out=out_st, workspace=ws)
+
+    def select_compact_decode(i):
+        topk_only(i)
+        compact_only(i)
+        store_only(i)
+
     res = timed_trials(torch, both, 0, steps, args.trials)
     t_topk = timed_trials(torch, topk_only, 0, steps, args.trials)
     t_sparse = timed_trials(torch, sparse_only, 0, steps, args.trials)
+    res_c = timed_trials(torch, select_compact_decode, 0, steps, args.trials)
+    t_compact = timed_trials(torch, compact_only, 0, steps, args.trials)
+    t_store = timed_trials(torch, store_only, 0, steps, args.trials)
+    torch.cuda.synchronize()
+    record_check(out_close(out_st.cpu().numpy(), out.cpu().numpy(),
+                           "sparse: decode over the compacted store vs the gather decode of the same selection"))
     # self-check: the last step's selection and output recomputed, then the oracle on sequence 0
     c_last = insts[(res["next"] - 1) % 2]
     idx_last, out_last = idx.cpu().numpy(), out.cpu().numpy()
@@ -423,6 +458,8 @@ def leg_sparse(hkv, torch, args):
     torch.cuda.empty_cache()
     tb = B * topk_bytes(n, H, Hq, d, k)
     sb = B * sparse_bytes(n, H, Hq, d, k)
+    stb = B * store_decode_bytes(n, H, Hq, d, k)
+    cb = B * compact_bytes(n, H, d, k)
     return {"workload": "topk: B=16, 32768 tokens, 32/8 heads, d=128, K=512; step = hkv_topk_select + sparse "
                         "hkv_decode_attn", "steps": steps,
             "ms_per_step": res["ms_per_step"], "trials_ms": res["trials_ms"],
@@ -432,6 +469,15 @@ def leg_sparse(hkv, torch, args):
                                  t_topk["device_ms_per_step"], "topk"),
             "roofline_sparse_decode": roofline("decode_kernel, sparse (gathered tokens)", sb,
                                                t_sparse["device_ms_per_step"], "sparse_decode"),
+            "compacted_store": {
+                "what": "KV Cache reuse page 2: the selected tokens re-packed into a compacted store "
+                        "(hkv_sparse_compact), decoded from it (hkv_decode_attn_compact)",
+                "ms_per_step_select_compact_decode": res_c["ms_per_step"],
+                "trials_ms": res_c["trials_ms"],
+                "roofline_store_decode": roofline("decode_kernel, compacted store units", stb,
+                                                  t_store["device_ms_per_step"], "store_decode"),
+                "roofline_compact": roofline("sparse_compact_kernel (gathers the selection)", cb,
+                                             t_compact["device_ms_per_step"], "compact")},
             "dispatch_event_ms": km}
 
 

@@ -112,9 +112,13 @@ typedef struct {
  *            -sum p ln p (nats) of each query head's softmax over the tokens it
  *            attends, computed as lse - E_p[z] from the same fp32 online
  *            softmax.
+ *            A decode with entropy set runs a kernel variant that carries the
+ *            statistic, under a static launch plan (no dynamic block claims,
+ *            so long contexts decode more slowly); with entropy NULL the
+ *            kernels hold no register for it.
  * A new cache is all zero except headers[].phys_block; every buffer except
- * hot must be 16-byte aligned.  Both statistics cost a few instructions per
- * block when enabled and nothing else. */
+ * hot must be 16-byte aligned.  The quantisation-error statistic costs a few
+ * instructions per coded tile when enabled and nothing else. */
 typedef struct {
   int32_t batch;
   int32_t max_blocks_per_seq;
@@ -376,6 +380,17 @@ typedef enum {
 } hkv_kernel_kind;
 
 hkv_status hkv_timing_enable(hkv_handle h, int enable);
+
+/* Launch-plan override (testing and tuning aid; like the timing state, it is
+ * the handle's only other mutable state).  nsplit > 0 makes every dense decode
+ * and fused step use a static plan of (at most) nsplit cold splits per
+ * (sequence, kv-head), without block claims (results then agree bit for bit
+ * between calls, and across split counts to fp32 rounding); claim_workgroups
+ * > 0 sets the grid of plans that claim blocks.  0 restores the automatic
+ * choice.  Workspace sizes queried after the call account for nsplit.
+ * HKV_ERR_INVALID_VALUE: nsplit outside [0, 128] or claim_workgroups outside
+ * [0, 65536]. */
+hkv_status hkv_plan_override(hkv_handle h, int nsplit, int claim_workgroups);
 hkv_status hkv_timing_read(hkv_handle h, int kind, double* total_ms, int64_t* count, int reset);
 
 /* Streaming read probe (measurement aid, not part of the cache protocol): one

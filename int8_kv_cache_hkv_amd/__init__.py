@@ -31,7 +31,7 @@ EXPORTS = ["hkv_create", "hkv_destroy", "hkv_cache_sizes", "hkv_sizes", "hkv_hea
            "hkv_append", "hkv_decode_attn", "hkv_decode_attn_noalloc", "hkv_append_decode",
            "hkv_sparse_store_bytes", "hkv_sparse_compact", "hkv_decode_attn_compact", "hkv_topk_select", "hkv_status_string",
            "hkv_timing_enable",
-           "hkv_timing_read", "hkv_last_error_detail", "hkv_read_probe"]
+           "hkv_timing_read", "hkv_last_error_detail", "hkv_read_probe", "hkv_plan_override"]
 
 
 class HKVError(RuntimeError):
@@ -87,6 +87,7 @@ def _load() -> ctypes.CDLL:
         "hkv_timing_enable": [vp, i32],
         "hkv_timing_read": [vp, i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64), i32],
         "hkv_read_probe": [vp, sz, i32, i32, vp, vp],
+        "hkv_plan_override": [vp, i32, i32],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -233,6 +234,10 @@ def hkv_decode_attn_compact(handle: int, desc: CacheDesc, store, k_sel: int, q, 
                                         _ptr(out), _ptr(lse), _ptr(workspace),
                                         int(workspace.numel() * workspace.element_size()), _stream(stream)),
            "hkv_decode_attn_compact")
+
+
+def hkv_plan_override(handle: int, nsplit: int = 0, claim_workgroups: int = 0) -> None:
+    _check(_lib.hkv_plan_override(handle, int(nsplit), int(claim_workgroups)), "hkv_plan_override")
 
 
 def hkv_timing_enable(handle: int, enable: bool = True) -> None:

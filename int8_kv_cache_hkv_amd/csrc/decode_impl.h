@@ -106,10 +106,19 @@ struct WaveState {
   using C = Cfg<D, G>;
   float m[C::NG];                          // running max of base-2 logits (wave-uniform)
   float l[C::NG];                          // lane-partial sum of softmax weights
-  float zs[C::NG];                         // lane-partial sum of weight * logit (entropy statistic)
+  bool stats;                              // carry the entropy statistic (the cache view asks for it)
   float qb[C::NG];                         // bias * sum_k q[g][k] (wave-uniform; see Fmt::kBias)
   float4_t acc[C::NQ][C::NDL];             // out[4quad + r][64 pass + lane] (with the code offset)
 };
+
+// Lane-partial sums of weight * logit (entropy statistic) of wave w's row g: kept in the wave's own
+// wacc rows, which the wave writes only after it has read them back (LDS operations of one wave stay
+// in order), so the statistic costs no registers in the unit loop.
+template <int D, int G>
+__device__ __forceinline__ float& z_lane(DecodeSmem<D, G>& sm, int w, int g, int lane) {
+  static_assert(D >= 64, "the per-lane sums of a wave fit its wacc rows");
+  return (&sm.wacc[w][0][0])[g * 64 + lane];
+}
 
 template <int D, int G>
 __device__ __forceinline__ half4_t q_operand(const DecodeSmem<D, G>& sm, int quad, int lane, int k0) {
@@ -143,7 +152,6 @@ __device__ __forceinline__ void softmax_unit(WaveState<D, G>& st, DecodeSmem<D, 
       const float wv = PER_LANE_V ? pp * vw : pp;
       const float cf = be * vcoef;
       st.l[g] = fmaf(st.l[g], a, be * pp);
-      st.zs[g] = fmaf(st.zs[g], a, valid ? be * pp * z : 0.f);
       st.m[g] = mn;
       alpha[g] = a;
       coef[g] = cf;
@@ -152,6 +160,20 @@ __device__ __forceinline__ void softmax_unit(WaveState<D, G>& st, DecodeSmem<D, 
       _Float16* row = &sm.pw[w][quad][r][(lane >> 2) * 8 + (lane & 3)];
       row[0] = hi;
       row[4] = lo;
+    }
+  }
+  // entropy statistic, outside the row loop so that it holds no registers there: the weight
+  // 2^(z - m) of the new maximum m (equal to 2^(mb - m) 2^(z - mb) up to rounding)
+  if (st.stats) {
+#pragma unroll
+    for (int quad = 0; quad < C::NQ; ++quad) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int g = 4 * quad + r;
+        const float z = (s[quad][r] - st.qb[g]) * scale;
+        float& zl = z_lane(sm, w, g, lane);
+        zl = fmaf(zl, alpha[g], valid && st.m[g] != kNegInf ? exp2_approx(z - st.m[g]) * z : 0.f);
+      }
     }
   }
   wave_lds_sync();
@@ -614,23 +636,34 @@ __device__ void gather_unit(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const Cac
 // tile in the cold-block chunk layouts, read like a dense block, and each token's own (K, V) scales
 // (lane = token).  The logit scale is per lane and the value weight is taken relative to the unit's
 // largest V scale, as for gathered tokens.  count: the stored tokens of the (sequence, kv-head).
-template <int D, int G, int BITS>
-__device__ void store_unit(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const DecodeParams& p, int bh, int u, int count,
-                           int w, int lane) {
-  using C = Cfg<D, G>;
+// Request unit u's tiles (an empty descriptor past the store's units: the loads return 0) and the
+// lane's token scales.
+template <int D, int BITS>
+__device__ __forceinline__ void store_issue(const DecodeParams& p, int bh, int u, int lane, Tiles<D, BITS>& t,
+                                            float2& sc) {
   constexpr int S = kBlockSize;
   constexpr int E = Fmt<BITS>::kElems;
   constexpr int TB = Fmt<BITS>::template tile_bytes<D>();
-  const size_t unit = static_cast<size_t>(bh) * p.store_units + u;
-  const __amdgpu_buffer_rsrc_t r = make_rsrc(p.store_units_base + unit * 2 * TB, 2u * TB);
-  Tiles<D, BITS> t;
+  const bool ok = u < p.store_units;
+  const size_t unit = static_cast<size_t>(bh) * p.store_units + (ok ? u : 0);
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(p.store_units_base + unit * 2 * TB, ok ? 2u * TB : 0u);
   issue_k<D, BITS>(t, r, lane);
   const uint32_t lo = static_cast<uint32_t>(lane) * 16u;
 #pragma unroll
   for (int ps = 0; ps < D / 64; ++ps)
 #pragma unroll
     for (int vc = 0; vc < S / E; ++vc) t.vr[ps][vc] = load_stream_buf(r, lo + TB + (vc * D + 64 * ps) * 16);
-  const float2 sc = p.store_scales[unit * S + lane];
+  const float2 z = make_float2(0.f, 0.f);
+  sc = ok ? p.store_scales[unit * S + opaque_index(lane)] : z;
+}
+
+// Attend unit u from its requested tiles and the lane's token scales; count: the stored tokens of the
+// (sequence, kv-head).
+template <int D, int G, int BITS>
+__device__ void store_unit(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const DecodeParams& p, int u, int count,
+                           const Tiles<D, BITS>& t, float2 sc, int w, int lane) {
+  using C = Cfg<D, G>;
+  constexpr int S = kBlockSize;
   const bool valid = lane < count - u * S;
   float4_t s[C::NQ];
   qk_codes<D, G, BITS>(t.kr, sm, lane, s);
@@ -683,7 +716,7 @@ __device__ __forceinline__ void copy_query(const _Float16* qg, _Float16 (*qh)[4]
 }
 
 // ---- cold split: stream its units, merge the 4 waves, write the partial
-template <int D, int G, int BITS, int MODE, bool FUSED, bool CLAIM>
+template <int D, int G, int BITS, int MODE, bool FUSED, bool CLAIM, bool STATS>
 __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, int h, int bh, int split) {
   using C = Cfg<D, G>;
   constexpr int S = kBlockSize;
@@ -722,7 +755,9 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
   if (SPARSE) {
     sel0 = sel_entry(sel_bh, p.k_sel, split * p.units_per_split + w, lane);
   } else if constexpr (MODE == kModeStore) {
-    // the units are read in the walk
+    // the first unit's tiles and scales travel with the first round (their addresses do not
+    // depend on the stored count)
+    store_issue<D, BITS>(p, bh, split * p.units_per_split + w, lane, t0, sc0);
   } else if constexpr (CLAIM) {
     // claim walk: the first unit is split * 4 + w; the first claim travels with the first round
     hb = header_load(c, b, split * kWaves + w);
@@ -764,11 +799,12 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
                     : (sg.n_cold > 0 ? (SPARSE ? cdiv(p.k_sel, kSparseUnit) : (FUSED ? sg.n_cold / S : sg.n_blk)) : 0);
 
   WaveState<D, G> st;
+  st.stats = STATS;
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     st.m[g] = kNegInf;
     st.l[g] = 0.f;
-    st.zs[g] = 0.f;
+    if (st.stats) z_lane(sm, w, g, lane) = 0.f;
     float qs = 0.f;
 #pragma unroll
     for (int k = lane; k < D; k += 64) qs += static_cast<float>(sm.qh[g / 4][g % 4][k]);
@@ -792,7 +828,10 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
     const int CU = p.units_per_split;
     for (int run = split; run * CU < units; run += p.nsplit) {
       const int u_end = min(units, (run + 1) * CU);
-      for (int u = run * CU + w; u < u_end; u += kWaves) store_unit<D, G, BITS>(st, sm, p, bh, u, store_count, w, lane);
+      for (int u = run * CU + w; u < u_end; u += kWaves) {
+        if (run != split || u != run * CU + w) store_issue<D, BITS>(p, bh, u, lane, t0, sc0);
+        store_unit<D, G, BITS>(st, sm, p, u, store_count, t0, sc0, w, lane);
+      }
     }
   } else if constexpr (CLAIM) {
     const int u0 = split * kWaves + w;
@@ -816,7 +855,7 @@ __device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, i
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     const float lsum = wave_sum_dpp(st.l[g]);
-    const float zsum = wave_sum_dpp(st.zs[g]);
+    const float zsum = st.stats ? wave_sum_dpp(z_lane(sm, w, g, lane)) : 0.f;
     if (lane == 0) {
       sm.wm[w][g] = st.m[g];
       sm.wl[w][g] = lsum;
@@ -877,13 +916,14 @@ __device__ void hot_attend(const DecodeParams& p, HotSmem<D, G>& hm, int b, int 
   copy_query<D, G>(p.q + (static_cast<size_t>(b) * c.H * G + static_cast<size_t>(h) * G) * D, hm.qh, tid);
   for (int i = tid; i < G * D; i += kThreads) hm.acc[i / D][i % D] = 0.f;
   const _Float16* hot_bh = c.hot + static_cast<size_t>(bh) * c.T * 2 * D;
-  float m[NG], l[NG], zs[NG];  // wave 0's running softmax state (wave-uniform)
+  float m[NG], l[NG];  // wave 0's running softmax state (wave-uniform)
+  const bool stats = p.c.entropy != nullptr;  // entropy statistic asked for: its sum runs in hm.zs
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     m[g] = kNegInf;
     l[g] = 0.f;
-    zs[g] = 0.f;
   }
+  if (tid < NG) hm.zs[tid] = 0.f;  // (wave 0, the only wave that updates it)
   for (int base = 0; base < n_hot; base += kHotChunk) {
     const int cnt = min(kHotChunk, n_hot - base);
     const uint4* src = reinterpret_cast<const uint4*>(hot_bh + static_cast<size_t>(base) * 2 * D);
@@ -932,7 +972,10 @@ __device__ void hot_attend(const DecodeParams& p, HotSmem<D, G>& hm, int b, int 
           const float alpha = exp2_approx(m[g] - mn);
           const float pt = valid ? exp2_approx(z - mn) : 0.f;
           l[g] = l[g] * alpha + wave_sum_dpp(pt);
-          zs[g] = zs[g] * alpha + wave_sum_dpp(valid ? pt * z : 0.f);
+          if (stats) {
+            const float zsum = wave_sum_dpp(valid ? pt * z : 0.f);
+            if (lane == 0) hm.zs[g] = fmaf(hm.zs[g], alpha, zsum);
+          }
           m[g] = mn;
           if (lane < kHotChunk) hm.z[g][lane] = pt;
           if (lane == 0) hm.alpha[g] = alpha;
@@ -953,7 +996,6 @@ __device__ void hot_attend(const DecodeParams& p, HotSmem<D, G>& hm, int b, int 
     for (int g = 0; g < NG; ++g) {
       hm.m[g] = m[g];
       hm.l[g] = l[g];
-      hm.zs[g] = zs[g];
     }
   }
   __syncthreads();
@@ -1021,7 +1063,7 @@ struct AppendSmem {
   float rerr[2][kWaves];                             // debug statistic: per-wave largest |x - code * scale|
 };
 
-template <int D, int G, int BITS>
+template <int D, int G, int BITS, bool STATS>
 __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>& am, int b, int h, int bh) {
   __builtin_amdgcn_s_setprio(3);  // the append's coding and its block's attention sit on the step's critical path
   using C = Cfg<D, G>;
@@ -1271,11 +1313,12 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
         for (int vc = 0; vc < 64 / E; ++vc)
           tl.vr[ps2][vc] = chunk_from_stage<BITS>(am.stage_v + (64 * ps2 + lane) * VROW + vc * E * EB);
       WaveState<D, G> st;
+      st.stats = STATS;
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         st.m[g] = kNegInf;
         st.l[g] = 0.f;
-        st.zs[g] = 0.f;
+        if (st.stats) z_lane(am.unit, 0, g, lane) = 0.f;
         float qs = 0.f;
 #pragma unroll
         for (int k = lane; k < D; k += 64) qs += static_cast<float>(am.unit.qh[g / 4][g % 4][k]);
@@ -1296,7 +1339,7 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
       for (int g = 0; g < NG; ++g) {
         um[g] = st.m[g];
         ul[g] = wave_sum_dpp(st.l[g]);
-        uz[g] = wave_sum_dpp(st.zs[g]);
+        uz[g] = st.stats ? wave_sum_dpp(z_lane(am.unit, 0, g, lane)) : 0.f;
       }
 #pragma unroll
       for (int quad = 0; quad < C::NQ; ++quad)
@@ -1338,7 +1381,7 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
 // the workspace, which the merging workgroup resets to zero.  The merge runs
 // online over groups of kMergeChunk partials whose loads are all in flight
 // together; thread i owns two adjacent output columns of one query head.
-template <int D, int G, int BITS, int MODE, bool FUSED, bool CLAIM>
+template <int D, int G, int BITS, int MODE, bool FUSED, bool CLAIM, bool STATS>
 __device__ __forceinline__ void decode_body(const DecodeParams& p, const WgCoord wg) {
   using AppendPart = typename std::conditional<FUSED, AppendSmem<D, G, BITS>, DecodeSmem<D, G>>::type;
   __shared__ union Smem {
@@ -1354,10 +1397,10 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, const WgCoord
   const int bh = b * c.H + h;
   const int tid = threadIdx.x;
   if (split < p.nsplit) {
-    cold_split<D, G, BITS, MODE, FUSED, CLAIM>(p, sm.cold, b, h, bh, split);
+    cold_split<D, G, BITS, MODE, FUSED, CLAIM, STATS>(p, sm.cold, b, h, bh, split);
   } else if constexpr (FUSED) {
     if (split == p.nsplit) hot_window_split<D, G>(p, sm.hot, b, h, bh);
-    else append_unit_split<D, G, BITS>(p, sm.app, b, h, bh);
+    else append_unit_split<D, G, BITS, STATS>(p, sm.app, b, h, bh);
   } else {
     hot_split<D, G>(p, sm.hot, b, h, bh);
   }
@@ -1455,11 +1498,13 @@ __device__ __forceinline__ void consume_args(const DecodeParams& p) {
 template <int G, int BITS>
 constexpr int decode_waves() { return (G > 4 || BITS == 0) ? 2 : 4; }
 
-template <int D, int G, int BITS, int MODE, bool FUSED, bool CLAIM>
+// STATS: the variant that also carries the entropy statistic (launched only when the cache view
+// asks for it, with a static plan); the others hold no register for it.
+template <int D, int G, int BITS, int MODE, bool FUSED, bool CLAIM, bool STATS = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves<G, BITS>()))) void decode_kernel(
     DecodeParams p) {
   consume_args(p);
-  decode_body<D, G, BITS, MODE, FUSED, CLAIM>(p, wg_coord(p.wg_order));
+  decode_body<D, G, BITS, MODE, FUSED, CLAIM, STATS>(p, wg_coord(p.wg_order));
 }
 
 // Batch plans: the same grid read in the host-built order of the table (see wg_coord_table); a kernel
@@ -1468,7 +1513,7 @@ template <int D, int G, int BITS, bool FUSED, bool CLAIM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves<G, BITS>()))) void
 decode_kernel_ordered(DecodeParamsOrdered po) {
   consume_args(po.p);
-  decode_body<D, G, BITS, kModeDense, FUSED, CLAIM>(po.p, wg_coord_table(po.order));
+  decode_body<D, G, BITS, kModeDense, FUSED, CLAIM, false>(po.p, wg_coord_table(po.order));
 }
 
 template <typename K, typename P>
@@ -1485,6 +1530,14 @@ hipError_t launch_k(K kernel, dim3 grid, int block, const P& p, const LaunchCtx&
 template <int D, int G, int BITS>
 hipError_t launch_dg(const DecodeParams& p, const LaunchCtx& ctx, const uint16_t* order) {
   const dim3 grid(p.nparts, p.c.H, p.c.B);  // (split, kv-head, sequence)
+  if (p.c.entropy) {  // statistics: static plans in plain order only
+    if (order || p.work || p.wg_order != kOrderPlain) return hipErrorInvalidValue;
+    if (p.k_new) return launch_k(decode_kernel<D, G, BITS, kModeDense, true, false, true>, grid, kThreads, p, ctx);
+    if (p.store_units_base)
+      return launch_k(decode_kernel<D, G, BITS, kModeStore, false, false, true>, grid, kThreads, p, ctx);
+    if (p.sel) return launch_k(decode_kernel<D, G, BITS, kModeGather, false, false, true>, grid, kThreads, p, ctx);
+    return launch_k(decode_kernel<D, G, BITS, kModeDense, false, false, true>, grid, kThreads, p, ctx);
+  }
   if (order && !p.sel) {
     DecodeParamsOrdered po;
     po.p = p;

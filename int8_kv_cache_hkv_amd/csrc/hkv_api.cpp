@@ -52,6 +52,8 @@ hipError_t launch_decode(const DecodeParams& p, const LaunchCtx& ctx, const uint
 
 struct hkv_ctx {
   int H, D, T, S, bits;
+  int force_splits = 0;      // plan override (hkv_plan_override): static plans of this many splits
+  int claim_workgroups = 0;  // plan override: grid of claim plans (0 = the width's default)
   bool timing = false;
   struct Pending {
     int kind;
@@ -130,6 +132,28 @@ SplitPlan plan_splits(int64_t bh, int64_t units, int extra_parts = 1, int64_t ta
   }
   const int order = (claim && target >= 2) ? hkv::kOrderSplitMajor : hkv::kOrderPlain;
   return {static_cast<int>(ns), static_cast<int>(per), order, claim, target < 2 ? 1 : 0};
+}
+
+// Workgroups of a claim plan's grid (2 per CU at 8 bits: fewer waves in flight keep the loaded
+// latency and the tail of claimed-ahead units short).  A 4-bit unit is half an 8-bit one: its
+// grid is doubled so that as many bytes stay in flight.
+int64_t claim_target(const hkv_ctx* h) {
+  if (h->claim_workgroups > 0) return h->claim_workgroups;
+  return h->bits == 4 ? 2 * kClaimTargetWorkgroups : kClaimTargetWorkgroups;
+}
+
+// Static plan of n splits (plan override): units per split a multiple of the 4 waves, plain order.
+SplitPlan forced_plan(int64_t units, int n) {
+  units = std::max<int64_t>(1, units);
+  const int64_t per = hkv::kWaves * ((units + hkv::kWaves * n - 1) / (hkv::kWaves * n));
+  return {static_cast<int>((units + per - 1) / per), static_cast<int>(per), hkv::kOrderPlain, 0, 0};
+}
+
+// The decode variant that carries the entropy statistic runs static plans in plain order only:
+// with the statistic asked for, a claim or batch plan becomes the static plan of as many splits.
+SplitPlan stats_plan(const hkv_cache_desc* c, const SplitPlan& sp, int64_t units) {
+  if (!c->entropy || (!sp.claim && !sp.batch && sp.wg_order == hkv::kOrderPlain)) return sp;
+  return forced_plan(units, sp.nsplit);
 }
 
 // Upper bound of the split count of plan_splits over every unit count in
@@ -244,6 +268,7 @@ hkv::CacheView view_of(const hkv_ctx* h, const hkv_cache_desc* c) {
 size_t partials_bytes(const hkv_ctx* h, const hkv_cache_desc* c, int G, int k_sel) {
   const int64_t bh = static_cast<int64_t>(c->batch) * h->H;
   int ns = max_splits(bh, std::max<int64_t>(1, c->max_blocks_per_seq));
+  if (h->force_splits > 0) ns = std::max(ns, std::min(h->force_splits, kMaxSplits));
   if (k_sel > 0) ns = std::max(ns, plan_sparse(k_sel).nsplit);
   // ns cold splits + the hot zone (+ the tail block of a fused append)
   return static_cast<size_t>(bh) * (ns + 2) * G * (h->D + hkv::kRecHead) * sizeof(float);
@@ -347,7 +372,11 @@ hkv_status decode_impl(hkv_ctx* h, const hkv_cache_desc* c, const void* q, int n
   p.k_sel = sel_idx ? k_sel : 0;
   p.counters = static_cast<unsigned*>(workspace);
   p.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + (scratch ? hkv::kScratchCounterBytes : ctr_bytes));
-  const SplitPlan sp = sel_idx ? plan_sparse(k_sel) : plan_splits(static_cast<int64_t>(c->batch) * h->H, units_max);
+  const SplitPlan sp = sel_idx ? plan_sparse(k_sel)
+                      : h->force_splits > 0 ? forced_plan(units_max, h->force_splits)
+                                            : stats_plan(c, plan_splits(static_cast<int64_t>(c->batch) * h->H,
+                                                                        units_max, 1, kTargetWorkgroups,
+                                                                        claim_target(h)), units_max);
   p.nsplit = sp.nsplit;
   p.nparts = sp.nsplit + 1;
   p.units_per_split = sp.per_split;
@@ -593,7 +622,10 @@ hkv_status hkv_append_decode(hkv_handle h, const hkv_cache_desc* c, const void* 
     p.counters = static_cast<unsigned*>(workspace);
     p.seq_counters = p.counters + static_cast<size_t>(c->batch) * h->H;
     p.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(counters_bytes(c, h->H), 256));
-    const SplitPlan sp = plan_splits(static_cast<int64_t>(c->batch) * h->H, units_max, 2);
+    const SplitPlan sp = h->force_splits > 0 ? forced_plan(units_max, h->force_splits)
+                                             : stats_plan(c, plan_splits(static_cast<int64_t>(c->batch) * h->H,
+                                                                         units_max, 2, kTargetWorkgroups,
+                                                                         claim_target(h)), units_max);
     p.nsplit = sp.nsplit;
     p.nparts = sp.nsplit + 2;
     p.units_per_split = sp.per_split;
@@ -775,6 +807,15 @@ const char* hkv_status_string(hkv_status st) {
     case HKV_ERR_OUT_OF_MEMORY: return "out of host memory";
   }
   return "unknown status";
+}
+
+hkv_status hkv_plan_override(hkv_handle h, int nsplit, int claim_workgroups) {
+  if (!h) return HKV_ERR_NULL_POINTER;
+  if (nsplit < 0 || nsplit > kMaxSplits || claim_workgroups < 0 || claim_workgroups > 65536)
+    return HKV_ERR_INVALID_VALUE;
+  h->force_splits = nsplit;
+  h->claim_workgroups = claim_workgroups;
+  return HKV_OK;
 }
 
 hkv_status hkv_timing_enable(hkv_handle h, int enable) {

@@ -240,6 +240,25 @@ def test_host_allocation_failure_is_reported():
     assert r.stdout.split()[-2:] == [str(OOM), str(OOM)], r.stdout
 
 
+def test_plan_override_values():
+    """The plan override takes nsplit in [0, 128] and a claim grid in [0, 65536]; anything else is
+    HKV_ERR_INVALID_VALUE and leaves the handle as it was."""
+    h = hkv.hkv_create(8, 128)
+    try:
+        fc = FakeCache(h, batch=4, max_blocks=2048, lens=[0] * 4)
+        base = hkv.hkv_workspace_bytes(h, fc.desc, 32)
+        for ns, grid in [(-1, 0), (129, 0), (0, -5), (0, 65537)]:
+            assert hkv._lib.hkv_plan_override(h, ns, grid) == -1
+        assert hkv.hkv_workspace_bytes(h, fc.desc, 32) == base
+        hkv.hkv_plan_override(h, 128, 0)   # a forced split count can widen the partials area
+        assert hkv.hkv_workspace_bytes(h, fc.desc, 32) >= base
+        hkv.hkv_plan_override(h, 0, 0)
+        assert hkv.hkv_workspace_bytes(h, fc.desc, 32) == base
+        assert hkv._lib.hkv_plan_override(None, 1, 0) == -3
+    finally:
+        hkv.hkv_destroy(h)
+
+
 def test_status_strings():
     assert hkv.hkv_status_string(OOM) == "out of host memory"
     for st in (0, -1, -2, -3, -4, -5, -6, -7, -8):
