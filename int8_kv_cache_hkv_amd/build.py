@@ -69,9 +69,13 @@ def _run(cmd, verbose):
         print(err, file=sys.stderr)
 
 
-def build(verbose: bool = False, jobs: int = 0) -> str:
-    """Compile every source into int8_kv_cache_hkv_amd/libhkv.so (always recompiles)."""
+def build(verbose: bool = False, jobs: int = 0, out: str = LIB, host_flags: tuple = ()) -> str:
+    """Compile every source into int8_kv_cache_hkv_amd/libhkv.so, or `out` (always recompiles).
+
+    host_flags: extra options for the host side of every compile only (each is passed behind
+    -Xarch_host, e.g. a sanitizer build of the host code; device code is unchanged)."""
     cc = hipcc()
+    host = [x for f in host_flags for x in ("-Xarch_host", f)]
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
     jobs = jobs or min(16, os.cpu_count() or 1)
     with tempfile.TemporaryDirectory(prefix="hkv_build_") as tmpd:
@@ -80,14 +84,14 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
         for src, defs, name in compile_units():
             obj = os.path.join(tmpd, name)
             objs.append(obj)
-            cmds.append([cc, *HIPCC_FLAGS, *defs, *inc, "-c", os.path.join(CSRC, src), "-o", obj])
+            cmds.append([cc, *HIPCC_FLAGS, *host, *defs, *inc, "-c", os.path.join(CSRC, src), "-o", obj])
         with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
             for f in [ex.submit(_run, c, verbose) for c in cmds]:
                 f.result()
-        tmp = LIB + ".tmp"
+        tmp = out + ".tmp"
         _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-        os.replace(tmp, LIB)
-    return LIB
+        os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
