@@ -288,9 +288,22 @@ unsigned* claim_counters(void* workspace, const hkv_cache_desc* c, int H) {
   return reinterpret_cast<unsigned*>(static_cast<char*>(workspace) + claim_offset(c, H));
 }
 
-size_t topk_bytes(const hkv_ctx* h, const hkv_cache_desc* c) {
-  return static_cast<size_t>(c->batch) * h->H * c->max_blocks_per_seq * h->S * sizeof(float);
+// Top-K workspace after the counters: window probabilities [B][H][max_blocks * S] fp32, window tops
+// [B][H][max_blocks] (32 bytes each) and their lanes [B][H][max_blocks] (8 bytes each), every area
+// 256-byte aligned.
+struct TopkLayout {
+  size_t wtop_off, wlane_off, bytes;  // offsets from the start of the probabilities
+};
+TopkLayout topk_layout(const hkv_ctx* h, const hkv_cache_desc* c) {
+  const size_t bh = static_cast<size_t>(c->batch) * h->H;
+  const size_t mb = static_cast<size_t>(std::max(0, c->max_blocks_per_seq));
+  TopkLayout l;
+  l.wtop_off = align_up(bh * mb * h->S * sizeof(float), 256);
+  l.wlane_off = l.wtop_off + align_up(bh * mb * 32, 256);
+  l.bytes = l.wlane_off + bh * mb * 8;
+  return l;
 }
+size_t topk_bytes(const hkv_ctx* h, const hkv_cache_desc* c) { return topk_layout(h, c).bytes; }
 
 LaunchCtx make_ctx(hkv_ctx* h, hipStream_t s, int kind) {
   LaunchCtx ctx{s, nullptr, nullptr};
@@ -759,11 +772,15 @@ hkv_status hkv_topk_select(hkv_handle h, const hkv_cache_desc* c, const void* q,
     int64_t blk_max = 1;
     for (int b = 0; b < c->batch; ++b) blk_max = std::max(blk_max, cold_blocks(c->seq_len_host[b], h->T, h->S));
 
+    const TopkLayout tl = topk_layout(h, c);
     hkv::TopkParams p;
     p.c = view_of(h, c);
     p.G = G;
     p.q = static_cast<const _Float16*>(q);
-    p.prob = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(counters_bytes(c, h->H), 256));
+    char* const area = static_cast<char*>(workspace) + align_up(counters_bytes(c, h->H), 256);
+    p.prob = reinterpret_cast<float*>(area);
+    p.wtop = reinterpret_cast<uint4*>(area + tl.wtop_off);
+    p.wlane = reinterpret_cast<uint2*>(area + tl.wlane_off);
     // the score kernel holds at most 64 VGPRs per lane (D = 128, G <= 4), so 8 of its workgroups fit a
     // CU: twice the decode's grid; its claim plans take 4 per CU (32768-token workload, measured:
     // static splits 98.6 us, claims on 512 / 1024 / 2048 workgroups 98.5 / 91.3 / 92.7 us)

@@ -34,7 +34,6 @@ constexpr float kNegInfT = -__builtin_inff();
 // the wave's loads; a wave walks about 16 units of the 32768-token workload, measured: stage of 16
 // -> 91.8 us, 32 -> 90.0 us)
 constexpr int kStage = 32;
-constexpr int kSelThreads = 1024;
 
 // Window probabilities of one cold block from its K tile: kr[ch] holds elements
 // E ch .. E ch + E - 1 of the lane's token.  As each chunk is consumed its
@@ -112,6 +111,54 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t k_tile_rsrc(const CacheView& c
   return make_rsrc(c.cold + tile_offset(ok ? phys : 0, h, 0, c.H, TB), ok ? TB : 0u);
 }
 
+// The kWinTop largest of the wave's 64 keys (unsigned; 0 = no key) and their lanes, wave-uniform,
+// in lane order: each of kWinTop rounds takes the wave maximum (DPP inside rows of 16 lanes, then
+// the four row results) and retires it in its lowest lane; the retired lanes are then read out in
+// ascending order.
+template <int CTRL>
+__device__ __forceinline__ unsigned dpp_mov_u(unsigned x) {
+  return static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ unsigned wave_max_u32(unsigned x) {
+  x = max(x, dpp_mov_u<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = max(x, dpp_mov_u<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = max(x, dpp_mov_u<0x141>(x));  // row_half_mirror
+  x = max(x, dpp_mov_u<0x140>(x));  // row_mirror
+  const unsigned a = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(x), 0));
+  const unsigned b = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(x), 16));
+  const unsigned c = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(x), 32));
+  const unsigned d = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(x), 48));
+  return max(max(a, b), max(c, d));
+}
+struct WinTop {
+  uint4 k0, k1;  // keys of the 8 lanes, in lane order
+  uint2 lanes;   // those lanes, 8 bits apiece (lanes of k0 in .x, of k1 in .y)
+};
+__device__ __forceinline__ WinTop wave_top8(unsigned key, int lane) {
+  static_assert(kWinTop == 8, "eight keys per window");
+  const unsigned orig = key;
+  bool taken = false;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const unsigned m = wave_max_u32(key);
+    const uint64_t hit = __ballot(key == m && !taken);  // never empty: 64 > 8 lanes
+    if (lane == static_cast<int>(__builtin_ctzll(hit))) {
+      key = 0u;
+      taken = true;
+    }
+  }
+  uint64_t mask = __ballot(taken);  // exactly 8 lanes
+  unsigned t[8], ln[2] = {0u, 0u};
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int l = static_cast<int>(__builtin_ctzll(mask));
+    mask &= mask - 1;
+    t[r] = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(orig), l));
+    ln[r / 4] |= static_cast<unsigned>(l) << (8 * (r % 4));
+  }
+  return {make_uint4(t[0], t[1], t[2], t[3]), make_uint4(t[4], t[5], t[6], t[7]), make_uint2(ln[0], ln[1])};
+}
+
 // Grid (split, kv-head, sequence).  Each wave walks its cold blocks (the same
 // walk as the decode's dense units); the first block's tile is requested with
 // the query, each next one while the current one is scored.
@@ -126,6 +173,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BITS =
   __shared__ float qinv[4 * NQ];           // 1 / |q_g| (0 for a zero query or a padding row)
   __shared__ float pstage[CLAIM ? kWaves : 1][CLAIM ? kStage : 1][64];  // claim walk: staged window probabilities
   __shared__ int ustage[CLAIM ? kWaves : 1][CLAIM ? kStage : 1];
+  // claim walk: staged window tops, 40 bytes apiece (8 keys, 8 lanes), so that four workgroups
+  // still fit a CU's LDS
+  __shared__ uint2 tstage[CLAIM ? kWaves : 1][CLAIM ? kStage : 1][5];
   asm volatile("" ::"s"(p.c.H), "s"(p.c.T), "s"(p.c.max_blocks), "s"(p.c.num_phys), "s"(p.c.cold),
                "s"(p.c.headers), "s"(p.c.seq_len), "s"(p.q), "s"(p.prob), "s"(p.nsplit), "s"(p.units_per_split),
                "s"(p.wg_order), "s"(p.work));
@@ -177,6 +227,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BITS =
   const int units = min(sg.n_blk, c.max_blocks);
   const size_t cap = static_cast<size_t>(c.max_blocks) * S;
   float* prob = p.prob + static_cast<size_t>(bh) * cap;
+  uint4* wtop = p.wtop + static_cast<size_t>(bh) * c.max_blocks * 2;  // per window: its kWinTop largest keys + 1
+  uint2* wlane = p.wlane + static_cast<size_t>(bh) * c.max_blocks;     // ... and their lanes
   if constexpr (CLAIM) {
     // Claim walk (see the decode's): the first unit is split * 4 + w, then units nsplit * 4 + claim.
     // A unit's chain is claim -> header -> tiles, each given a whole unit of time: at the start of
@@ -197,8 +249,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BITS =
     int nst = 0;
     auto flush = [&]() {
 #pragma unroll 1
-      for (int k = 0; k < nst; ++k)
+      for (int k = 0; k < nst; ++k) {
         prob[static_cast<size_t>(ustage[w][k]) * S + lane] = pstage[w][k][lane];
+        if (lane == 0) {
+          const uint2* t8 = tstage[w][k];
+          wtop[2 * ustage[w][k]] = make_uint4(t8[0].x, t8[0].y, t8[1].x, t8[1].y);
+          wtop[2 * ustage[w][k] + 1] = make_uint4(t8[2].x, t8[2].y, t8[3].x, t8[3].y);
+          wlane[ustage[w][k]] = t8[4];
+        }
+      }
       nst = 0;
       // drain here, once per kStage units, so that no store is pending in the loop's other waits
       __builtin_amdgcn_s_waitcnt(0);
@@ -212,8 +271,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BITS =
       const float pr = window_scores<D, G, BITS>(kr, qh, qinv, lane, nv, k_tile_rsrc<D, BITS>(c, phys_n, h));
       // a block without a valid physical id contributes probability 0 (its tokens are never
       // attended); lanes past the last cold token write row entries the selection never reads
-      pstage[w][nst][lane] = phys >= 0 && lane < nv ? pr : 0.f;
-      if (lane == 0) ustage[w][nst] = u;
+      const float pv = phys >= 0 && lane < nv ? pr : 0.f;
+      pstage[w][nst][lane] = pv;
+      const WinTop t8 = wave_top8(lane < nv ? __builtin_bit_cast(unsigned, pv) + 1u : 0u, lane);
+      if (lane == 0) {
+        ustage[w][nst] = u;
+        tstage[w][nst][0] = make_uint2(t8.k0.x, t8.k0.y);
+        tstage[w][nst][1] = make_uint2(t8.k0.z, t8.k0.w);
+        tstage[w][nst][2] = make_uint2(t8.k1.x, t8.k1.y);
+        tstage[w][nst][3] = make_uint2(t8.k1.z, t8.k1.w);
+        tstage[w][nst][4] = t8.lanes;
+      }
       if (++nst == kStage) {
         wave_lds_sync();
         flush();
@@ -245,7 +313,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BITS =
     const int nv = min(S, sg.n_cold - u * S);
     const float pr = window_scores<D, G, BITS>(kr, qh, qinv, lane, nv, k_tile_rsrc<D, BITS>(c, phys_n, h));
     // a block without a valid physical id contributes probability 0 (its tokens are never attended)
-    if (lane < nv) prob[static_cast<size_t>(u) * S + lane] = phys >= 0 ? pr : 0.f;
+    const float pv = phys >= 0 ? pr : 0.f;
+    if (lane < nv) prob[static_cast<size_t>(u) * S + lane] = pv;
+    const WinTop t8 = wave_top8(lane < nv ? __builtin_bit_cast(unsigned, pv) + 1u : 0u, lane);
+    if (lane == 0) {
+      wtop[2 * u] = t8.k0;
+      wtop[2 * u + 1] = t8.k1;
+      wlane[u] = t8.lanes;
+    }
     u = un;
     phys = phys_n;
     ++k;
@@ -254,190 +329,270 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BITS =
   }
 }
 
-// Inclusive scan of v over the 1024-thread block; returns the exclusive prefix
-// and writes the block total to *total.
-__device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total) {
+// ---------------------------------------------------------------- selection
+// The K largest window probabilities of a (sequence, kv-head) row, ties to the lower index, in
+// ascending index order.  Keys are the fp32 bit patterns plus one: probabilities are >= 0, so
+// integer order is value order, bit 31 stays 0, and 0 is free to mark "no key".
+//
+// topk_select_kernel: one workgroup per row.  It reads the window tops, not the row:
+//  1. a floor lo <= tau (tau: the K-th largest key): at least K keys of the row are >= the K-th
+//     largest window top, so the lower edge of the histogram bin holding it is a floor (the bins
+//     split the range of the tops into 2048, so lo sits just below tau).
+//  2. candidates (every key >= lo) in index order: a window whose smallest top is below lo has all
+//     of its keys >= lo among its tops, which are kept in lane order (so in index order); only a
+//     window whose tops are all >= lo is read whole (next to none of the 32768-token workload's).
+//     Their count is scanned over the workgroup and the candidates are staged in LDS in index order.
+//  3. tau and how many keys equal to it to take (radix passes over the range [lo, largest key]):
+//     one wave alone when the candidates fit it (no workgroup barrier in the passes), else the
+//     whole workgroup; then the ordered output.
+// A row of at most kDirectKeys keys is selected from the row itself (then K window tops may not
+// exist); a row of more than kTopsWindows windows, or with more than kFinalKeys candidates (keys
+// crowded at the floor: many equal keys), by streaming the whole row.
+constexpr int kDirectKPT = kDirectKeys / kSelThreads;  // keys per thread of the direct selection
+constexpr int kFinalKPT = kFinalKeys / kSelThreads;    // candidates per thread of the block selection
+constexpr int kWaveKPT = 16;                            // candidates per lane of the one-wave selection
+constexpr int kWaveKeys = 64 * kWaveKPT;
+constexpr int kTopsWPT = kTopsWindows / kSelThreads;   // windows per thread
+static_assert(kDirectKeys % kSelThreads == 0 && kFinalKeys % kSelThreads == 0 && kTopsWindows % kSelThreads == 0,
+              "whole keys per thread");
+static_assert(kWinTop * (kDirectKeys / kBlockSize) >= kMaxTopK,
+              "a row past kDirectKeys keys has at least K window tops, so the floor exists");
+constexpr int kDigitBits = 11;
+constexpr int kSelMaxBins = 1 << kDigitBits;
+// histogram copies by lane % kSelCopies, 4 banks apart: lanes whose keys share a bin mostly hit
+// different addresses (one copy serialises crowded bins); the pick sums the copies
+constexpr int kSelCopies = 4;
+constexpr int kSelStride = kSelMaxBins + 4;
+static_assert(kSelCopies * kSelStride * 4 >= kFinalKeys * 8, "the candidate stage fits the histogram memory");
+static_assert(kWaveKeys * 8 + 256 * 4 <= kSelCopies * kSelStride * 4, "one-wave stage and histogram");
+
+struct SelSmem {
+  alignas(16) unsigned hist[kSelCopies * kSelStride];  // also the candidate stage
+  int wsum[kSelThreads / 64];
+  unsigned wred[3][kSelThreads / 64];
+  unsigned prefix, krem;
+};
+
+// Inclusive prefix sum over the wave's lanes with DPP moves (no LDS): shifts by 1, 2, 4 and 8 inside
+// rows of 16 lanes, then lane 15 of rows 0 and 2 into rows 1 and 3, then lane 31 into rows 2 and 3.
+// Lanes whose source is outside the pattern add 0.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 (rows 1, 3)
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 (rows 2, 3)
+  return x;
+}
+
+// Exclusive prefix of v over the workgroup; *total gets the sum.
+__device__ __forceinline__ int block_exclusive_scan(int v, SelSmem& sm, int* total) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) wsum[w] = x;
+  const int x = wave_inclusive_scan(v);
+  if (lane == 63) sm.wsum[w] = x;
   __syncthreads();
-  // every thread sums the wave totals itself (independent LDS reads, no serial pass)
-  int before = 0, all = 0;
+  int before = 0, all = 0;  // every thread sums the wave totals itself (independent LDS reads)
 #pragma unroll
   for (int i = 0; i < kSelThreads / 64; ++i) {
-    const int s = wsum[i];
-    before += i < w ? s : 0;
-    all += s;
+    const int t = sm.wsum[i];
+    before += i < w ? t : 0;
+    all += t;
   }
   *total = all;
   __syncthreads();  // wsum is reused by the next scan
   return before + x - v;
 }
 
-// Radix select over the key bits [30:0] (keys are fp32 bit patterns of
-// probabilities >= 0, so bit 31 is 0 and integer order is value order), in
-// three passes of 11, 10 and 10 bits from the top.  Window probabilities share
-// their exponent, so a first digit of exponent + 3 mantissa bits still spreads
-// them over dozens of bins (8-bit digits put most keys into two or three bins
-// and serialise the LDS atomics).
-constexpr int kSelPasses = 3;
-__device__ __forceinline__ int sel_shift(int pass) { return pass == 0 ? 20 : (pass == 1 ? 10 : 0); }
-__device__ __forceinline__ int sel_bins(int pass) { return pass == 0 ? 2048 : 1024; }
-constexpr int kSelMaxBins = 2048;
-// Histogram copies by lane % 16.  Window probabilities crowd into a handful of
-// bins, and the lanes of one LDS atomic that hit the same address are applied
-// one after another (measured: about 18 us for the first pass over 32768 keys
-// with a single copy).  With 16 copies, 4 banks apart, lanes that share a bin
-// mostly land on different addresses and banks.  The pick sums the copies.
-constexpr int kSelCopies = 16;
-constexpr int kSelStride = kSelMaxBins + 4;
-
-__device__ __forceinline__ unsigned* lane_hist(unsigned* hist) {
-  return hist + (threadIdx.x & (kSelCopies - 1)) * kSelStride;
+// Exclusive prefix of v over the wave's lanes; *total gets the sum (wave-uniform).
+__device__ __forceinline__ int wave_exclusive_scan(int v, int lane, int* total) {
+  const int x = wave_inclusive_scan(v);
+  *total = __builtin_amdgcn_readlane(x, 63);
+  return x - v;
 }
 
-// Zero the first nb bins (a power of two) of every copy, 16 bytes per store.
-__device__ __forceinline__ void clear_hist(unsigned* hist, int nb) {
+// Workgroup minimum and maximum of the nonzero keys and their count (min is ~0u when there is none).
+__device__ __forceinline__ void block_min_max_count(unsigned kmin, unsigned kmax, unsigned cnt, SelSmem& sm,
+                                                    unsigned* out_min, unsigned* out_max, unsigned* out_cnt) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  kmin = ~wave_max_u32(~kmin);
+  kmax = wave_max_u32(kmax);
+  cnt = static_cast<unsigned>(wave_sum_dpp(static_cast<float>(cnt)));  // < 2^24: exact in fp32
+  if (lane == 0) {
+    sm.wred[0][w] = kmin;
+    sm.wred[1][w] = kmax;
+    sm.wred[2][w] = cnt;
+  }
+  __syncthreads();
+  unsigned a = ~0u, b = 0u, c = 0u;
+#pragma unroll
+  for (int i = 0; i < kSelThreads / 64; ++i) {
+    a = min(a, sm.wred[0][i]);
+    b = max(b, sm.wred[1][i]);
+    c += sm.wred[2][i];
+  }
+  *out_min = a;
+  *out_max = b;
+  *out_cnt = c;
+  __syncthreads();  // wred is reused
+}
+
+__device__ __forceinline__ unsigned* lane_hist(SelSmem& sm) {
+  return sm.hist + (threadIdx.x & (kSelCopies - 1)) * kSelStride;
+}
+
+// Zero the first nb bins (a power of two >= 4) of every copy, 16 bytes per store.
+__device__ __forceinline__ void clear_hist(SelSmem& sm, int nb) {
   const int lg = 29 - __builtin_clz(static_cast<unsigned>(nb));  // log2(nb / 4)
   for (int i = threadIdx.x; i < kSelCopies * (nb >> 2); i += kSelThreads)
-    *reinterpret_cast<u32x4_t*>(hist + (i >> lg) * kSelStride + 4 * (i & ((nb >> 2) - 1))) = u32x4_t{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4_t*>(sm.hist + (i >> lg) * kSelStride + 4 * (i & ((nb >> 2) - 1))) =
+        u32x4_t{0u, 0u, 0u, 0u};
 }
 
-// Count of bin i over the copies.
-__device__ __forceinline__ unsigned hist_bin(const unsigned* hist, int i) {
-  unsigned v = 0;
-#pragma unroll
-  for (int c = 0; c < kSelCopies; ++c) v += hist[c * kSelStride + i];
-  return v;
-}
-
-// After a histogram pass: the digit of the krem-th largest key among those
-// matching `prefix`, scanning bins from the top digit down (thread t owns the
-// bins nb-1-t*bpt ... nb-t*bpt-bpt, in descending order).
-__device__ __forceinline__ void radix_pick(const unsigned* hist, int nb, int* wsum, unsigned* s_prefix,
-                                           unsigned* s_krem, unsigned prefix, unsigned krem, int shift) {
+// After a histogram pass over the kSelMaxBins bins: the digit of the krem-th largest counted key,
+// scanning bins from the top digit down (thread t owns bins 4 (511 - t) .. 4 (511 - t) + 3, read
+// as one 16-byte vector per copy).  Sets sm.prefix = prefix | digit << shift and sm.krem = its rank
+// among the keys of that digit.  A krem beyond the counted keys takes digit 0.
+constexpr int kPickBins = kSelMaxBins / kSelThreads;
+static_assert(kPickBins == 4, "one 16-byte vector of bins per thread and copy");
+__device__ __forceinline__ void radix_pick(SelSmem& sm, unsigned prefix, unsigned krem, int shift) {
   const int tid = threadIdx.x;
-  const int bpt = nb / kSelThreads;  // 1 or 2
-  const int top = nb - 1 - tid * bpt;
-  int local = 0;
-  unsigned v[2] = {0u, 0u};
-  for (int i = 0; i < bpt; ++i) {
-    v[i] = hist_bin(hist, top - i);
-    local += static_cast<int>(v[i]);
-  }
+  const int b0 = kSelMaxBins - kPickBins * (tid + 1);  // lowest bin of this thread
+  u32x4_t v = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int c = 0; c < kSelCopies; ++c) v += *reinterpret_cast<const u32x4_t*>(&sm.hist[c * kSelStride + b0]);
+  const int local = static_cast<int>(v[0] + v[1] + v[2] + v[3]);
   int total;
-  unsigned before = static_cast<unsigned>(block_exclusive_scan(local, wsum, &total));  // keys above my bins
-  for (int i = 0; i < bpt; ++i) {
-    // the digit whose keys contain the krem-th largest: before < krem <= before + v (unique); the
-    // lowest digit takes whatever is left
-    if ((before < krem && krem <= before + v[i]) || (top - i == 0 && before < krem && krem > before + v[i])) {
-      *s_prefix = prefix | (static_cast<unsigned>(top - i) << shift);
-      *s_krem = krem - before;
+  unsigned before = static_cast<unsigned>(block_exclusive_scan(local, sm, &total));  // keys above my bins
+#pragma unroll
+  for (int i = kPickBins - 1; i >= 0; --i) {
+    const int bin = b0 + i;
+    if ((before < krem && krem <= before + v[i]) || (bin == 0 && before < krem && krem > before + v[i])) {
+      sm.prefix = prefix | (static_cast<unsigned>(bin) << shift);
+      sm.krem = krem - before;
     }
     before += v[i];
   }
   __syncthreads();
 }
 
-// Rows of up to KPT * 1024 keys: every key is loaded into registers once
-// (thread t holds keys [t*KPT, t*KPT + KPT), so its indices are contiguous and
-// in order), the radix passes run from the registers, and the ordered
-// compaction needs two block scans.  Longer rows stream the keys from memory
-// on every pass (select_streaming).
-constexpr int kSelKPT = 32;
-
-__device__ void select_registers(const unsigned* keys, int n, int K, int32_t* out, unsigned* hist, int* wsum,
-                                 unsigned* s_prefix, unsigned* s_krem) {
-  constexpr int KPT = kSelKPT;
-  const int tid = threadIdx.x;
-  const int i0 = tid * KPT;
-  // the row is read with coalesced 16-byte loads (vector v * 1024 + t by thread t) and handed over
-  // through LDS (rows padded to KPT + 1 words: conflict-free reads) to its owner, thread i / KPT;
-  // loading each thread's own 128 contiguous bytes directly makes every load instruction touch 64
-  // cache lines and thrashes the L1 (measured: about 6 us for a 32768-key row)
-  unsigned* stage = hist;
-  {
-    const u32x4_t* kv = reinterpret_cast<const u32x4_t*>(keys);  // 16-byte aligned: rows start at multiples of 64 keys
-#pragma unroll
-    for (int v = 0; v < KPT / 4; ++v) {
-      const int vi = v * kSelThreads + tid;  // vector index: keys 4 vi .. 4 vi + 3
-      u32x4_t x;
-      if (4 * vi + 4 <= n) {
-        x = kv[vi];
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] = 4 * vi + j < n ? keys[4 * vi + j] : 0u;
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = 4 * vi + j;
-        stage[(i / KPT) * (KPT + 1) + i % KPT] = i < n ? x[j] + 1u : 0u;
-      }
-    }
-  }
-  __syncthreads();
-  // keys are held as bit pattern + 1 (same order; bit 31 stays 0) and 0 past the row, so every
-  // test below against a floor or threshold >= 1 leaves the padding out without a per-key check
-  unsigned key[KPT];
-#pragma unroll
-  for (int k = 0; k < KPT; ++k) key[k] = stage[tid * (KPT + 1) + k];
-  __syncthreads();  // the stage is the histogram's memory
-  const int nv = max(0, min(KPT, n - i0));  // valid keys of this thread
-  // ---- a floor lo <= tau that most keys fall below: if at least K threads hold keys, the
-  // first-digit bin of the K-th largest per-thread maximum has K maxima at or above its lower
-  // edge, so at least K keys are >= lo and the K-th largest key is too.  Only keys >= lo take
-  // part in the radix passes (typically a few percent of the row).
-  unsigned lo = 1;
-  unsigned tmax = 0;
-#pragma unroll
-  for (int k = 0; k < KPT; ++k) tmax = max(tmax, key[k]);
-  if (min(kSelThreads, cdiv(n, KPT)) >= K) {  // threads holding keys
-    clear_hist(hist, sel_bins(0));
-    __syncthreads();
-    if (nv > 0) atomicAdd(&lane_hist(hist)[tmax >> sel_shift(0)], 1u);
-    __syncthreads();
-    radix_pick(hist, sel_bins(0), wsum, s_prefix, s_krem, 0u, static_cast<unsigned>(K), sel_shift(0));
-    lo = max(1u, *s_prefix);
-    __syncthreads();  // every thread has read the pick before the histogram is cleared again
-  }
-  // ---- radix select: the K-th largest key (tau) and how many keys equal to it to take
+// Radix select over keys held in registers across the workgroup (0 = none): the K-th largest key
+// among those >= base, by digits of (key - base) below bit `bits` (every counted key - base is
+// < 2^bits), 11 bits per pass from the top, at most max_passes passes.  Returns base + the selected
+// digits (the lower edge of the last bin) and, in *krem, the rank of the K-th largest among the keys
+// of that bin.  With every pass run, that is tau itself and *krem the number of keys equal to tau
+// among the K largest.
+template <int KPT>
+__device__ unsigned range_select(const unsigned (&key)[KPT], unsigned base, int bits, int K, int max_passes,
+                                 SelSmem& sm, int* krem_out) {
   unsigned prefix = 0, mask = 0, krem = static_cast<unsigned>(K);
-  for (int pass = 0; pass < kSelPasses; ++pass) {
-    const int shift = sel_shift(pass), nb = sel_bins(pass);
-    clear_hist(hist, nb);
+  int hi = bits;
+  for (int pass = 0; pass < max_passes && hi > 0; ++pass) {
+    const int wd = min(kDigitBits, hi);
+    const int shift = hi - wd;
+    const unsigned dm = (1u << wd) - 1u;  // digit mask (bins past it stay empty)
+    clear_hist(sm, kSelMaxBins);
     __syncthreads();
-    unsigned* wh = lane_hist(hist);
+    unsigned* wh = lane_hist(sm);
 #pragma unroll
-    for (int k = 0; k < KPT; ++k)
-      if (key[k] >= lo && (key[k] & mask) == prefix)
-        atomicAdd(&wh[(key[k] >> shift) & static_cast<unsigned>(nb - 1)], 1u);
+    for (int k = 0; k < KPT; ++k) {
+      const unsigned r = key[k] - base;
+      if (key[k] >= base && key[k] != 0u && (r & mask) == prefix) atomicAdd(&wh[(r >> shift) & dm], 1u);
+    }
     __syncthreads();
-    radix_pick(hist, nb, wsum, s_prefix, s_krem, prefix, krem, shift);
-    prefix = *s_prefix;
-    krem = *s_krem;
-    mask |= static_cast<unsigned>(nb - 1) << shift;
+    radix_pick(sm, prefix, krem, shift);
+    prefix = sm.prefix;
+    krem = sm.krem;
+    mask |= dm << shift;
+    hi = shift;
     __syncthreads();  // every thread has read the pick before the next pass clears the histogram
   }
-  const unsigned tau = prefix;
-  const int need_eq = static_cast<int>(krem);
-  // ---- ordered compaction: every key above tau, and the lowest-index need_eq keys equal to it
+  *krem_out = static_cast<int>(krem);
+  return base + prefix;
+}
+
+// The same selection by one wave over the keys its lanes hold, in 8-bit digits (256 bins, four
+// per lane: a pass is a few dozen instructions), with a histogram of its own in LDS (hist: 256 words
+// no other wave touches).  Every pass stays inside the wave.
+constexpr int kWaveDigitBits = 8;
+constexpr int kWaveBins = 1 << kWaveDigitBits;
+template <int KPT>
+__device__ unsigned wave_range_select(const unsigned (&key)[KPT], unsigned base, int bits, int K, unsigned* hist,
+                                      int lane, int* krem_out) {
+  unsigned prefix = 0, mask = 0, krem = static_cast<unsigned>(K);
+  int hi = bits;
+  constexpr int BPL = kWaveBins / 64;  // lane l owns bins 4 (63 - l) .. 4 (63 - l) + 3
+  static_assert(BPL == 4, "one 16-byte vector of bins per lane");
+  const int b0 = kWaveBins - BPL * (lane + 1);
+  while (hi > 0) {
+    const int wd = min(kWaveDigitBits, hi);
+    const int shift = hi - wd;
+    const unsigned dm = (1u << wd) - 1u;  // digit mask (bins past it stay empty)
+    *reinterpret_cast<u32x4_t*>(&hist[b0]) = u32x4_t{0u, 0u, 0u, 0u};
+    wave_lds_sync();
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) {
+      const unsigned r = key[k] - base;
+      if (key[k] >= base && key[k] != 0u && (r & mask) == prefix) atomicAdd(&hist[(r >> shift) & dm], 1u);
+    }
+    wave_lds_sync();
+    const u32x4_t hv = *reinterpret_cast<const u32x4_t*>(&hist[b0]);
+    const int local = static_cast<int>(hv[0] + hv[1] + hv[2] + hv[3]);
+    int total;
+    const unsigned before = static_cast<unsigned>(wave_exclusive_scan(local, lane, &total));
+    // the lane whose bins hold the krem-th largest (or, past the counted keys, lane 63: bin 0)
+    const bool mine = (before < krem && krem <= before + static_cast<unsigned>(local)) ||
+                      (lane == 63 && krem > before + static_cast<unsigned>(local));
+    const uint64_t who = __ballot(mine);
+    const int at = static_cast<int>(__builtin_ctzll(who));  // never empty
+    unsigned digit = 0, kr = krem, bf = before;
+    bool found = false;
+#pragma unroll
+    for (int i = BPL - 1; i >= 0; --i) {
+      const bool hit = !found && ((bf < krem && krem <= bf + hv[i]) || b0 + i == 0);
+      digit = hit ? static_cast<unsigned>(b0 + i) : digit;
+      kr = hit ? krem - bf : kr;
+      found = found || hit;
+      bf += hv[i];
+    }
+    digit = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(digit), at));
+    krem = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(kr), at));
+    prefix |= digit << shift;
+    mask |= dm << shift;
+    hi = shift;
+    wave_lds_sync();  // the next pass clears the bins this one read
+  }
+  *krem_out = static_cast<int>(krem);
+  return base + prefix;
+}
+
+// Bits of the range of keys in [lo, hi]: every key - lo < 2^result.
+__device__ __forceinline__ int range_bits(unsigned lo, unsigned hi) {
+  return hi > lo ? 32 - __builtin_clz(hi - lo) : 0;
+}
+
+// (greater << 16 | equal) counts of one holder's keys against tau (each total is below 65536).
+template <int KPT>
+__device__ __forceinline__ int count_both(const unsigned (&key)[KPT], unsigned tau, int* eq_out) {
   int gt = 0, eq = 0;
 #pragma unroll
   for (int k = 0; k < KPT; ++k) {
     gt += key[k] > tau ? 1 : 0;
     eq += key[k] == tau ? 1 : 0;
   }
-  // one scan of both counts (each total is at most 32768, so 16 bits apiece)
-  int both_total;
-  const int both_before = block_exclusive_scan((gt << 16) | eq, wsum, &both_total);
+  *eq_out = eq;
+  return (gt << 16) | eq;
+}
+
+// Output positions of one holder's keys (held in list order): every key above tau and the first
+// need_eq keys equal to it are taken; both_before is the (greater << 16 | equal) count of the
+// holders before this one.  Writes out[pos] = idx for each taken key with pos < K.
+template <int KPT>
+__device__ __forceinline__ void take_keys(const unsigned (&key)[KPT], const int (&idx)[KPT], unsigned tau,
+                                          int need_eq, int K, int both_before, int eq, int32_t* out) {
   const int eq_before = both_before & 0xffff, gt_before = both_before >> 16;
   const int eq_take = max(0, min(eq, need_eq - eq_before));
-  int pos = gt_before + min(eq_before, need_eq);  // keys taken by the threads before this one
+  int pos = gt_before + min(eq_before, need_eq);  // keys taken by the holders before this one
   int eq_seen = 0;
 #pragma unroll
   for (int k = 0; k < KPT; ++k) {
@@ -445,30 +600,31 @@ __device__ void select_registers(const unsigned* keys, int n, int K, int32_t* ou
     const bool take = key[k] > tau || (is_eq && eq_seen < eq_take);
     if (is_eq) ++eq_seen;
     if (take) {
-      if (pos < K) out[pos] = i0 + k;
+      if (pos < K) out[pos] = idx[k];
       ++pos;
     }
   }
 }
 
-__device__ void select_streaming(const unsigned* keys, int n, int K, int32_t* out, unsigned* hist, int* wsum,
-                                 unsigned* s_prefix, unsigned* s_krem) {
+// The whole row streamed from memory on every pass (three fixed 11/10/10-bit digits of the key).
+__device__ void select_streaming(const unsigned* prob_bits, int n, int K, int32_t* out, SelSmem& sm) {
   const int tid = threadIdx.x;
   unsigned prefix = 0, mask = 0, krem = static_cast<unsigned>(K);
-  for (int pass = 0; pass < kSelPasses; ++pass) {
-    const int shift = sel_shift(pass), nb = sel_bins(pass);
-    clear_hist(hist, nb);
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 20 : (pass == 1 ? 10 : 0);
+    const unsigned dm = pass == 0 ? 2047u : 1023u;
+    clear_hist(sm, kSelMaxBins);
     __syncthreads();
-    unsigned* wh = lane_hist(hist);
+    unsigned* wh = lane_hist(sm);
     for (int i = tid; i < n; i += kSelThreads) {
-      const unsigned key = keys[i];
-      if ((key & mask) == prefix) atomicAdd(&wh[(key >> shift) & static_cast<unsigned>(nb - 1)], 1u);
+      const unsigned key = prob_bits[i] + 1u;
+      if ((key & mask) == prefix) atomicAdd(&wh[(key >> shift) & dm], 1u);
     }
     __syncthreads();
-    radix_pick(hist, nb, wsum, s_prefix, s_krem, prefix, krem, shift);
-    prefix = *s_prefix;
-    krem = *s_krem;
-    mask |= static_cast<unsigned>(nb - 1) << shift;
+    radix_pick(sm, prefix, krem, shift);
+    prefix = sm.prefix;
+    krem = sm.krem;
+    mask |= dm << shift;
     __syncthreads();
   }
   const unsigned tau = prefix;
@@ -476,32 +632,40 @@ __device__ void select_streaming(const unsigned* keys, int n, int K, int32_t* ou
   int carry_sel = 0, carry_eq = 0;
   for (int base = 0; base < n; base += kSelThreads) {
     const int i = base + tid;
-    const unsigned key = i < n ? keys[i] : 0u;
-    const int is_eq = (i < n && key == tau) ? 1 : 0;
-    const int is_gt = (i < n && key > tau) ? 1 : 0;
+    const unsigned key = i < n ? prob_bits[i] + 1u : 0u;
+    const int is_eq = key == tau ? 1 : 0;
+    const int is_gt = key > tau ? 1 : 0;
     int eq_total;
-    const int eq_excl = block_exclusive_scan(is_eq, wsum, &eq_total);
+    const int eq_excl = block_exclusive_scan(is_eq, sm, &eq_total);
     const int take = (is_gt || (is_eq && carry_eq + eq_excl < need_eq)) ? 1 : 0;
     int sel_total;
-    const int sel_excl = block_exclusive_scan(take, wsum, &sel_total);
+    const int sel_excl = block_exclusive_scan(take, sm, &sel_total);
     if (take && carry_sel + sel_excl < K) out[carry_sel + sel_excl] = i;
     carry_eq += eq_total;
     carry_sel += sel_total;
   }
 }
 
+// The 64 keys of window wi of a row, with 16-byte loads issued together (the row's buffer holds
+// whole windows, so the loads stay inside it); keys past the row's n are 0.
+__device__ __forceinline__ void window_keys(const unsigned* pb, int wi, int n, unsigned (&k)[kBlockSize]) {
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(pb + static_cast<size_t>(wi) * kBlockSize);
+  u32x4_t v[kBlockSize / 4];
+#pragma unroll
+  for (int i = 0; i < kBlockSize / 4; ++i) v[i] = src[i];
+#pragma unroll
+  for (int i = 0; i < kBlockSize / 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) k[4 * i + j] = wi * kBlockSize + 4 * i + j < n ? v[i][j] + 1u : 0u;
+}
+
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkParams p) {
   constexpr int S = kBlockSize;
-  // histogram copies; also the stage of the register path's key hand-over
-  constexpr int kLds = kSelCopies * kSelStride > kSelThreads * (kSelKPT + 1) ? kSelCopies * kSelStride
-                                                                            : kSelThreads * (kSelKPT + 1);
-  __shared__ __attribute__((aligned(16))) unsigned hist[kLds];
-  __shared__ int wsum[kSelThreads / 64 + 1];
-  __shared__ unsigned s_prefix, s_krem;
+  __shared__ SelSmem sm;
   const CacheView& c = p.c;
   const int bh = blockIdx.x;
   const int b = bh / c.H;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   // the score launch before this one is complete: its claim counter goes back to zero
   if (p.work && tid == 0)
     __hip_atomic_store(p.work + static_cast<size_t>(bh) * kClaimStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -510,14 +674,155 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkParams p) 
   const int K = p.k;
   int32_t* out = p.out_idx + static_cast<size_t>(bh) * K;
   const size_t cap = static_cast<size_t>(c.max_blocks) * S;
-  const unsigned* keys = reinterpret_cast<const unsigned*>(p.prob + static_cast<size_t>(bh) * cap);
+  const unsigned* pb = reinterpret_cast<const unsigned*>(p.prob + static_cast<size_t>(bh) * cap);
 
   if (n <= K) {
     for (int i = tid; i < K; i += kSelThreads) out[i] = i < n ? i : -1;
     return;
   }
-  if (n <= kSelKPT * kSelThreads) select_registers(keys, n, K, out, hist, wsum, &s_prefix, &s_krem);
-  else select_streaming(keys, n, K, out, hist, wsum, &s_prefix, &s_krem);
+  const int nw = cdiv(n, S);
+  if (n <= kDirectKeys) {  // from the row (thread t: keys [t KPT, t KPT + KPT))
+    unsigned key[kDirectKPT];
+    int idx[kDirectKPT];
+#pragma unroll
+    for (int k = 0; k < kDirectKPT; ++k) {
+      const int i = tid * kDirectKPT + k;
+      key[k] = i < n ? pb[i] + 1u : 0u;
+      idx[k] = i;
+    }
+    int need_eq;
+    const unsigned tau = range_select<kDirectKPT>(key, 1u, 31, K, 3, sm, &need_eq);
+    int eq, tot;
+    const int both = count_both<kDirectKPT>(key, tau, &eq);
+    const int before = block_exclusive_scan(both, sm, &tot);
+    take_keys<kDirectKPT>(key, idx, tau, need_eq, K, before, eq, out);
+    return;
+  }
+  if (nw > kTopsWindows) {
+    select_streaming(pb, n, K, out, sm);
+    return;
+  }
+  // ---- 1. the floor.  Thread t holds windows t + 512 v (v < kTopsWPT), so every thread has work in
+  // the first round and the later rounds are skipped as a whole when the row is short.
+  const uint4* tops = p.wtop + static_cast<size_t>(bh) * c.max_blocks * 2;
+  const uint2* lanes = p.wlane + static_cast<size_t>(bh) * c.max_blocks;
+  constexpr int WT = kWinTop;
+  const int rounds = cdiv(nw, kSelThreads);  // (workgroup-uniform)
+  unsigned tk[WT * kTopsWPT];
+  uint2 tl[kTopsWPT];
+#pragma unroll
+  for (int v = 0; v < kTopsWPT; ++v) {
+    const int wi = v * kSelThreads + tid;
+    const bool ok = v < rounds && wi < nw;
+    const uint4 a0 = ok ? tops[2 * wi] : make_uint4(0u, 0u, 0u, 0u);
+    const uint4 a1 = ok ? tops[2 * wi + 1] : make_uint4(0u, 0u, 0u, 0u);
+    tl[v] = ok ? lanes[wi] : make_uint2(0u, 0u);
+    const unsigned t8[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+    for (int r = 0; r < WT; ++r) tk[WT * v + r] = t8[r];
+  }
+  unsigned tmin = ~0u, tmax = 0u, tcnt = 0u;
+#pragma unroll
+  for (int k = 0; k < WT * kTopsWPT; ++k) {
+    if (tk[k] != 0u) {
+      tmin = min(tmin, tk[k]);
+      tmax = max(tmax, tk[k]);
+      ++tcnt;
+    }
+  }
+  unsigned bmin, kmax, bcnt;
+  block_min_max_count(tmin, tmax, tcnt, sm, &bmin, &kmax, &bcnt);
+  int unused;
+  // (bcnt >= K: a row of more than kDirectKeys keys has more than kWinTop kDirectKeys / 64 >= K tops)
+  const unsigned lo = max(1u, range_select<WT * kTopsWPT>(tk, bmin, range_bits(bmin, kmax), K, 1, sm, &unused));
+  // ---- 2. the candidates of each round's windows (one window per thread), counted, scanned and
+  // staged in index order
+  uint64_t* stage = reinterpret_cast<uint64_t*>(sm.hist);
+  int m_all = 0;
+  for (int v = 0; v < rounds; ++v) {
+    const int wi = v * kSelThreads + tid;
+    unsigned kv[WT];
+    unsigned tmn = ~0u;
+#pragma unroll
+    for (int r = 0; r < WT; ++r) {
+      kv[r] = 0u;
+#pragma unroll
+      for (int u = 0; u < kTopsWPT; ++u) kv[r] = u == v ? tk[WT * u + r] : kv[r];
+      tmn = min(tmn, kv[r]);
+    }
+    uint2 lv = tl[0];
+#pragma unroll
+    for (int u = 1; u < kTopsWPT; ++u) lv = u == v ? tl[u] : lv;
+    const bool whole = wi < nw && tmn >= lo;  // every top >= lo: more keys may be
+    int nc = 0;
+#pragma unroll
+    for (int r = 0; r < WT; ++r) nc += !whole && kv[r] >= lo ? 1 : 0;
+    if (whole) {
+      unsigned wk[S];
+      window_keys(pb, wi, n, wk);
+      for (int j = 0; j < S; ++j) nc += wk[j] >= lo ? 1 : 0;
+    }
+    int tot;
+    int pos = m_all + block_exclusive_scan(nc, sm, &tot);
+    if (m_all + tot > kFinalKeys) {  // (uniform)
+      select_streaming(pb, n, K, out, sm);
+      return;
+    }
+    if (whole) {
+      unsigned wk[S];
+      window_keys(pb, wi, n, wk);
+      for (int j = 0; j < S; ++j)
+        if (wk[j] >= lo)
+          stage[pos++] = static_cast<uint64_t>(wk[j]) | (static_cast<uint64_t>(static_cast<uint32_t>(wi * S + j)) << 32);
+    } else {
+#pragma unroll
+      for (int r = 0; r < WT; ++r) {
+        const unsigned ln = ((r < 4 ? lv.x : lv.y) >> (8 * (r % 4))) & 63u;
+        if (kv[r] >= lo)  // (a window past the row has no keys: its tops are 0)
+          stage[pos++] = static_cast<uint64_t>(kv[r]) |
+                         (static_cast<uint64_t>(static_cast<uint32_t>(wi * S + static_cast<int>(ln))) << 32);
+      }
+    }
+    m_all += tot;
+  }
+  __syncthreads();
+  // ---- 3. tau among the candidates, then the ordered output
+  if (m_all <= kWaveKeys) {  // one wave (lane l: candidates [l KPT, l KPT + KPT))
+    if (w != 0) return;
+    unsigned key[kWaveKPT];
+    int idx[kWaveKPT];
+#pragma unroll
+    for (int k = 0; k < kWaveKPT; ++k) {
+      const int j = lane * kWaveKPT + k;
+      const uint64_t e = j < m_all ? stage[j] : 0ull;
+      key[k] = static_cast<unsigned>(e);
+      idx[k] = static_cast<int>(e >> 32);
+    }
+    unsigned* whist = sm.hist + 2 * kWaveKeys;  // past the stage (words)
+    int need_eq;
+    const unsigned tau = wave_range_select<kWaveKPT>(key, lo, range_bits(lo, kmax), K, whist, lane, &need_eq);
+    int eq, tot;
+    const int both = count_both<kWaveKPT>(key, tau, &eq);
+    const int before = wave_exclusive_scan(both, lane, &tot);
+    take_keys<kWaveKPT>(key, idx, tau, need_eq, K, before, eq, out);
+    return;
+  }
+  unsigned key[kFinalKPT];
+  int idx[kFinalKPT];
+#pragma unroll
+  for (int k = 0; k < kFinalKPT; ++k) {
+    const int j = tid * kFinalKPT + k;
+    const uint64_t e = j < m_all ? stage[j] : 0ull;
+    key[k] = static_cast<unsigned>(e);
+    idx[k] = static_cast<int>(e >> 32);
+  }
+  __syncthreads();  // the stage is the histogram's memory
+  int need_eq;
+  const unsigned tau = range_select<kFinalKPT>(key, lo, range_bits(lo, kmax), K, 3, sm, &need_eq);
+  int eq, tot;
+  const int both = count_both<kFinalKPT>(key, tau, &eq);
+  const int before = block_exclusive_scan(both, sm, &tot);
+  take_keys<kFinalKPT>(key, idx, tau, need_eq, K, before, eq, out);
 }
 
 template <typename Kf>

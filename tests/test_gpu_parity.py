@@ -543,6 +543,32 @@ def test_topk_small(n, k):
         gh.compare_lse(lse[0], l_ref, "sparse")
 
 
+@pytest.mark.parametrize("k", [512, 100, 1])
+def test_topk_ragged_rows(k):
+    """One batch whose rows take every selection path: at most K keys (identity), rows of up to 8192
+    keys (one workgroup, keys from the row), and longer rows split into 4096-key chunks that hand
+    their candidates above a floor to the row's last workgroup (8193 keys: a 1-key last chunk;
+    20000 and 40017 keys: several chunks).  Every row's index set against the oracle."""
+    w = wl.WORKLOADS["tiny"]
+    lens = [32 + 100, 32 + 600, 32 + 8192, 32 + 8193, 32 + 20000, 32 + 40017]
+    import dataclasses
+    w = dataclasses.replace(w, batch=len(lens))
+    cache = gh.make_cache(w, max(lens) + 64)
+    gh.fill(cache, w, lens, chunk=8192)
+    states = _oracle_states(w, lens)
+    q = wl.queries(w, step=4)
+    idx = cache.topk(gh.upload(q), k)
+    gh.torch_mod().cuda.synchronize()
+    got = idx.cpu().numpy()
+    for b, st in enumerate(states):
+        want, p, tau = orc.topk_select(q[b], st, k)
+        for h in range(w.n_kv_heads):
+            gh.compare_topk(got[b, h], want[h], p[h], tau[h], st.n_cold, k, f"n={lens[b]} k={k} b={b} h={h}")
+    # the same workspace again: the chunk arrival counters are back at zero
+    idx2 = cache.topk(gh.upload(q), k).cpu().numpy()
+    assert np.array_equal(idx2, got)
+
+
 @pytest.mark.parametrize("k_sel", [1, 15, 16, 17, 37, 64, 100])
 def test_sparse_decode_explicit_indices(k_sel):
     """Caller-built selections: ragged k_sel, -1 and out-of-range entries are ignored, duplicates count twice."""
