@@ -410,7 +410,7 @@ __device__ __forceinline__ void pv_dense(BlockAcc<D, G>& blk, const DecodeSmem<D
 // while the current one is being computed.  t/phys_u/sc hold the first unit
 // (already requested by the caller), hb the header batch of walk units 0..63.
 template <int D, int G, int BITS>
-__device__ void dense_units(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const DecodeParams& p, int b, int h, int split,
+__device__ __forceinline__ void dense_units(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const DecodeParams& p, int b, int h, int split,
                             int units, int n_cold, int w, int lane, Tiles<D, BITS>& t, int phys_u, float2 sc, int hb) {
   using C = Cfg<D, G>;
   constexpr int S = kBlockSize;
@@ -477,7 +477,7 @@ __device__ void dense_units(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const Dec
 // unit and its pending header load (un < 0: none), cl the pending claim for
 // the unit after it (valid when un >= 0).
 template <int D, int G, int BITS>
-__device__ void dense_units_claim(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const DecodeParams& p, int b, int h,
+__device__ __forceinline__ void dense_units_claim(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const DecodeParams& p, int b, int h,
                                   int bh, int units, int n_cold, int w, int lane, Tiles<D, BITS>& t, int u, int phys_u,
                                   float2 sc, int un, int hn, unsigned cl) {
   using C = Cfg<D, G>;
@@ -570,7 +570,7 @@ __device__ __forceinline__ half4_t gathered_operand(const uint32_t (&e)[4], cons
 
 // idx: the lane's selection entry (sel_entry of this unit).
 template <int D, int G, int BITS>
-__device__ void gather_unit(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const CacheView& c, int idx, int b, int h,
+__device__ __forceinline__ void gather_unit(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const CacheView& c, int idx, int b, int h,
                             int n_cold, float qscale, int w, int lane) {
   using C = Cfg<D, G>;
   using F = Fmt<BITS>;
@@ -653,14 +653,14 @@ __device__ __forceinline__ void store_issue(const DecodeParams& p, int bh, int u
   for (int ps = 0; ps < D / 64; ++ps)
 #pragma unroll
     for (int vc = 0; vc < S / E; ++vc) t.vr[ps][vc] = load_stream_buf(r, lo + TB + (vc * D + 64 * ps) * 16);
-  const float2 z = make_float2(0.f, 0.f);
-  sc = ok ? p.store_scales[unit * S + opaque_index(lane)] : z;
+  const float2 v = p.store_scales[unit * S + opaque_index(lane)];  // (unit 0 of the pair when !ok: in bounds)
+  sc = make_float2(ok ? v.x : 0.f, ok ? v.y : 0.f);
 }
 
 // Attend unit u from its requested tiles and the lane's token scales; count: the stored tokens of the
 // (sequence, kv-head).
 template <int D, int G, int BITS>
-__device__ void store_unit(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const DecodeParams& p, int u, int count,
+__device__ __forceinline__ void store_unit(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const DecodeParams& p, int u, int count,
                            const Tiles<D, BITS>& t, float2 sc, int w, int lane) {
   using C = Cfg<D, G>;
   constexpr int S = kBlockSize;
@@ -717,7 +717,7 @@ __device__ __forceinline__ void copy_query(const _Float16* qg, _Float16 (*qh)[4]
 
 // ---- cold split: stream its units, merge the 4 waves, write the partial
 template <int D, int G, int BITS, int MODE, bool FUSED, bool CLAIM, bool STATS>
-__device__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, int h, int bh, int split) {
+__device__ __forceinline__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, int h, int bh, int split) {
   using C = Cfg<D, G>;
   constexpr int S = kBlockSize;
   constexpr int NG = C::NG;

@@ -318,9 +318,8 @@ __device__ __forceinline__ half4_t chunk_operand(const uint4& ck, int step) {
     }
     return half4_t{a.x, a.y, b.x, b.y};
   } else {
-    const uint32_t w0 = word_of(ck, 2 * step), w1 = word_of(ck, 2 * step + 1);
-    const half2_t a = __builtin_bit_cast(half2_t, w0), b = __builtin_bit_cast(half2_t, w1);
-    return half4_t{a.x, a.y, b.x, b.y};
+    const uint2 v = step == 0 ? make_uint2(ck.x, ck.y) : make_uint2(ck.z, ck.w);
+    return __builtin_bit_cast(half4_t, v);
   }
 }
 
