@@ -76,6 +76,12 @@ constexpr int kTargetWorkgroups = 1024;
 // step, measured: 1024 -> 178, 768 -> 174, 512 -> 171, 384 -> 175, 256 -> 224 us).
 constexpr int kClaimTargetWorkgroups = 512;
 constexpr int kTopkClaimTargetWorkgroups = 1024;
+// Small launches (at most kSmallLaunchUnits cold units in all) are latency-bound: fewer workgroups,
+// each wave walking several units with the next one's tiles in flight, and static splits
+// (2048-token fused step, measured over batch 4 / 8 / 16: 14.4 / 16.4 / 22.3 us with the 1024
+// target; 14.0 / 15.5 us with 256, batch 16 above the threshold).
+constexpr int64_t kSmallLaunchUnits = 2048;
+constexpr int kSmallTargetWorkgroups = 256;
 using hkv::kMaxSplits;
 
 bool valid_protocol(int hot_tokens, int block_size) {
@@ -140,6 +146,19 @@ SplitPlan plan_splits(int64_t bh, int64_t units, int extra_parts = 1, int64_t ta
 int64_t claim_target(const hkv_ctx* h) {
   if (h->claim_workgroups > 0) return h->claim_workgroups;
   return h->bits == 4 ? 2 * kClaimTargetWorkgroups : kClaimTargetWorkgroups;
+}
+
+int64_t units_sum(const std::vector<int64_t>& units) {
+  int64_t t = 0;
+  for (int64_t u : units) t += u;
+  return t;
+}
+
+// Plan of a dense decode or fused step over bh (sequence, kv-head) pairs of at most units_max units.
+SplitPlan dense_plan(const hkv_ctx* h, int64_t bh, int64_t units_max, int64_t units_total, int extra_parts) {
+  if (units_total <= kSmallLaunchUnits)
+    return plan_splits(bh, units_max, extra_parts, kSmallTargetWorkgroups, 0);
+  return plan_splits(bh, units_max, extra_parts, kTargetWorkgroups, claim_target(h));
 }
 
 // Static plan of n splits (plan override): units per split a multiple of the 4 waves, plain order.
@@ -387,9 +406,8 @@ hkv_status decode_impl(hkv_ctx* h, const hkv_cache_desc* c, const void* q, int n
   p.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + (scratch ? hkv::kScratchCounterBytes : ctr_bytes));
   const SplitPlan sp = sel_idx ? plan_sparse(k_sel)
                       : h->force_splits > 0 ? forced_plan(units_max, h->force_splits)
-                                            : stats_plan(c, plan_splits(static_cast<int64_t>(c->batch) * h->H,
-                                                                        units_max, 1, kTargetWorkgroups,
-                                                                        claim_target(h)), units_max);
+                                            : stats_plan(c, dense_plan(h, static_cast<int64_t>(c->batch) * h->H, units_max,
+                                                                       units_sum(units) * h->H, 1), units_max);
   p.nsplit = sp.nsplit;
   p.nparts = sp.nsplit + 1;
   p.units_per_split = sp.per_split;
@@ -636,9 +654,8 @@ hkv_status hkv_append_decode(hkv_handle h, const hkv_cache_desc* c, const void* 
     p.seq_counters = p.counters + static_cast<size_t>(c->batch) * h->H;
     p.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(counters_bytes(c, h->H), 256));
     const SplitPlan sp = h->force_splits > 0 ? forced_plan(units_max, h->force_splits)
-                                             : stats_plan(c, plan_splits(static_cast<int64_t>(c->batch) * h->H,
-                                                                         units_max, 2, kTargetWorkgroups,
-                                                                         claim_target(h)), units_max);
+                                             : stats_plan(c, dense_plan(h, static_cast<int64_t>(c->batch) * h->H, units_max,
+                                                                        units_sum(units) * h->H, 2), units_max);
     p.nsplit = sp.nsplit;
     p.nparts = sp.nsplit + 2;
     p.units_per_split = sp.per_split;
