@@ -91,11 +91,16 @@ typedef struct {
  *            Base 512-byte aligned (Hybrid KV Cache page 3.2).
  *   tail     fp16 [batch][H][2][S][d]; FP16 originals of each sequence's
  *            partially filled last cold block (row-major [token][channel]).
- *   cold     int8 [P][H][2][S*d]; one 8 KiB (S=64, d=128) tile per
- *            (physical block, kv-head, K|V).  K tiles are stored as 16-byte
- *            channel chunks: byte (t, c) at ((c/16)*S + t)*16 + c%16.  V tiles
- *            are stored as 16-token column chunks: byte (t, c) at
- *            ((t/16)*d + c)*16 + t%16.  Rows t >= n_valid hold code 0.
+ *   cold     [P][H][2][tile bytes]; one tile per (physical block, kv-head,
+ *            K|V) of S*d elements: 8-bit codes (8 KiB at S=64, d=128), 4-bit
+ *            codes (4 KiB) or fp16 values (16 KiB, quant_bits 0).  A tile is
+ *            made of 16-byte chunks of E elements (E = 16, 32 or 8).  K tiles:
+ *            chunk (k, t) = channels E*k .. E*k+E-1 of token t, at byte
+ *            (k*S + t)*16.  V tiles: chunk (v, c) = tokens E*v .. E*v+E-1 of
+ *            channel c, at byte (v*d + c)*16.  Element e of a chunk is byte e
+ *            (int8 code), the half-byte e%2 (low first) of byte e/2 (4-bit
+ *            code + 8, so code -7..7 is stored 1..15) or the fp16 at bytes 2e,
+ *            2e+1.  Rows t >= n_valid hold code 0 (value 0).
  *   scales   fp32 [P][H][2]  (K scale, V scale).
  *   headers  hkv_block_header [batch][max_blocks_per_seq].
  *   seq_len_dev   int32 [batch] device: tokens cached per sequence.
@@ -154,7 +159,9 @@ typedef struct {
  *     {0, 4, 8} (3.1 allows 4 and 8; 5.2 uses 0 for an FP16 cold zone),
  *     n_kv_heads < 1 or head_dim < 1.
  *   HKV_ERR_UNSUPPORTED: protocol-valid values this library does not build:
- *     quant_bits != 8, block_size != 64, head_dim not in {64, 128}.
+ *     block_size != 64, head_dim not in {64, 128}.  All three widths are
+ *     built: quant_bits 8 (INT8 codes), 4 (INT4 codes, two per byte) and 0
+ *     (FP16 cold zone); see the cold-tile layouts above.
  *   HKV_ERR_NULL_POINTER: out is NULL.
  *   HKV_ERR_OUT_OF_MEMORY: the handle could not be allocated.
  * On success *out owns a small host object released by hkv_destroy. */

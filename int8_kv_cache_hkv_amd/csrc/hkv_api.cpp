@@ -4,7 +4,7 @@
 // Protocol rules (Hybrid KV Cache page, 3.1 and 5.1): hot_tokens is a power of
 // two in {16, 32, 64, 128}; block_size is a positive multiple of 8;
 // quantization_bits is 4 or 8 (5.2 adds 0 = FP16 cold zone); all three widths
-// are built.  The pages
+// are built (block_size 64 and head_dim 64 / 128 only).  The pages
 // describe a launch-time CUDA_ERROR_INVALID_VALUE for violations; here every
 // check runs on the host before any HIP call.
 #include <hip/hip_ext.h>

@@ -48,20 +48,6 @@ What is computed (readings where the pages are silent are marked READING):
    tokens.
 8. Header table sizing (Hybrid KV Cache page 5.4): one 16-byte header per
    cold block, blocks = ceil(cold tokens / block_size).
-11. Compacted sparse store (KV Cache reuse page 2: the Index-Aware Cache
-   Layout re-packs the KV of the selected top-K tokens into a compact block
-   that is the only thing loaded; 2.1: aligned, padded blocks).  The store of
-   a (sequence, kv-head) is its selected cold rows in selection order (masked
-   and out-of-range entries skipped, duplicates kept), each with its own
-   block's K and V scales; decoding over the hot zone plus the store is the
-   sparse decode of item 7.
-10. Debug statistics (Hybrid KV Cache page 6.3: a kv_cache_debug switch logs
-   quantisation-error statistics every step; KV Cache reuse page 6: monitor
-   the attention entropy, whose sudden drop signals lost context).  READING:
-   the quantisation error of a (block, kv-head, K|V) tile is the largest
-   |x - x_hat| over its valid elements (0 for an FP16 cold zone), and the
-   entropy of a decode is -sum_t p_t ln p_t of each query head's attention
-   distribution over the tokens it attends.
 9. Cold-zone width (Hybrid KV Cache page 3.1: quantization_bits is 4 or 8,
    INT4 for L2 cold blocks; 5.2: quantization_bits 0 turns quantisation off
    and the cold zone stays FP16).  A b-bit code is the same symmetric absmax
@@ -69,6 +55,20 @@ What is computed (readings where the pages are silent are marked READING):
    s = fl32(m / L), q = clip(rint(fl32(x / s)), -L, L) (READING: the pages
    define neither code).  With 0 bits the cold tokens keep their fp16 values
    and the state records a scale of 1 for every (block, kv-head, K|V).
+10. Debug statistics (Hybrid KV Cache page 6.3: a kv_cache_debug switch logs
+   quantisation-error statistics every step; KV Cache reuse page 6: monitor
+   the attention entropy, whose sudden drop signals lost context).  READING:
+   the quantisation error of a (block, kv-head, K|V) tile is the largest
+   |x - x_hat| over its valid elements (0 for an FP16 cold zone), and the
+   entropy of a decode is -sum_t p_t ln p_t of each query head's attention
+   distribution over the tokens it attends.
+11. Compacted sparse store (KV Cache reuse page 2: the Index-Aware Cache
+   Layout re-packs the KV of the selected top-K tokens into a compact block
+   that is the only thing loaded; 2.1: aligned, padded blocks).  The store of
+   a (sequence, kv-head) is its selected cold rows in selection order (masked
+   and out-of-range entries skipped, duplicates kept), each with its own
+   block's K and V scales; decoding over the hot zone plus the store is the
+   sparse decode of item 7.
 """
 from __future__ import annotations
 
