@@ -23,8 +23,10 @@ step as hkv_append + hkv_decode_attn), long (131072 tokens), llama8b_int4 /
 long_int4 / llama8b_fp16 / long_fp16 (the same steps with 4-bit cold blocks or
 an FP16 cold zone), sparse (top-K
 selection + sparse decode, 32768 tokens), ragged (64 sequences of seeded
-lengths), graph (the llama8b step from a HIP graph), read_floor (a plain
-one-launch read of the llama8b step's bytes), cpu (the fp64 oracle on the host).
+lengths), phases (per-workgroup timestamps of one llama8b step, and of the same
+step at 544 tokens), graph (the llama8b step from a HIP graph), read_floor (a
+plain one-launch read of the llama8b step's bytes), cpu (the fp64 oracle on the
+host).
 """
 from __future__ import annotations
 
@@ -619,6 +621,76 @@ def leg_graph(hkv, torch, args, steps=640, R=64):
             "gbs_graph": step_b / (ms_graph * 1e-3) / 1e9, "steps": reps * R}
 
 
+def phase_breakdown(hkv, torch, w, n0, R=64, rounds=3):
+    """Per-workgroup phase timestamps (hkv_phase_stamps) of one fused step launch among back-to-back
+    launches over R rotating instances: per role (cold split, hot window, append), when its work was
+    done, and for the append workgroup its phases; when the merges were done.  Times in us from the
+    first workgroup's start (100 MHz clock)."""
+    import workloads as wl
+    B, H, Hq, d = w.batch, w.n_kv_heads, w.n_q_heads, w.head_dim
+    insts = [Inst(hkv, w, n0 + rounds + 2) for _ in range(R)]
+    for s0 in range(0, n0, 16384):
+        cnt = min(16384, n0 - s0)
+        kh = torch.from_numpy(wl.batch_tokens(w, list(range(B)), s0, cnt, "k")).cuda()
+        vh = torch.from_numpy(wl.batch_tokens(w, list(range(B)), s0, cnt, "v")).cuda()
+        for it in insts:
+            it.c.append(kh, vh)
+    kn = torch.from_numpy(wl.batch_tokens(w, list(range(B)), n0, rounds, "k")).cuda()
+    vn = torch.from_numpy(wl.batch_tokens(w, list(range(B)), n0, rounds, "v")).cuda()
+    q = torch.from_numpy(wl.queries(w)).cuda()
+    out = torch.empty_like(q)
+    ws = insts[0].c.workspace(Hq)
+    buf = torch.zeros(B * H * 160 * 8, dtype=torch.int64, device="cuda")
+    for r in range(rounds):
+        for i, it in enumerate(insts):
+            mark = r == rounds - 1 and i == R // 2
+            if mark:
+                hkv.hkv_phase_stamps(it.c.handle, buf)
+            it.c.append_decode(kn[:, r].contiguous(), vn[:, r].contiguous(), q, out=out, workspace=ws)
+            if mark:
+                hkv.hkv_phase_stamps(it.c.handle, None)
+    torch.cuda.synchronize()
+    flat = buf.cpu().numpy()
+    for it in insts:
+        it.c.close()
+    del insts
+    torch.cuda.empty_cache()
+    rows = flat.reshape(-1, 8)
+    nparts = int((rows[:, 0] != 0).sum()) // (B * H)
+    a = rows[:B * H * nparts].reshape(B * H, nparts, 8).astype(np.int64)
+    t0 = a[:, :, 0].min()
+    us = lambda v: (np.asarray(v, np.float64) - t0) / 100.0
+    pct = lambda v: {f"p{p}": round(float(np.percentile(v, p)), 2) for p in (0, 50, 100)}
+    cold, hot, app = a[:, :nparts - 2], a[:, nparts - 2], a[:, nparts - 1]
+    merged = a[:, :, 3].max(axis=1)
+    last = a[:, :, 1].max(axis=1)
+    return {"context": n0 + rounds, "batch": B, "workgroups_per_pair": int(nparts),
+            "cold_split_done_us": pct(us(cold[:, :, 1])), "hot_window_done_us": pct(us(hot[:, 1])),
+            "append_done_us": pct(us(app[:, 1])),
+            "append_phases_us": {"first_loads": pct((app[:, 4] - app[:, 0]) / 100.0),
+                                 "coding": pct((app[:, 5] - app[:, 4]) / 100.0),
+                                 "code_stores": pct((app[:, 6] - app[:, 5]) / 100.0),
+                                 "block_attention": pct((app[:, 7] - app[:, 6]) / 100.0),
+                                 "partial_and_arrival": pct((app[:, 1] - app[:, 7]) / 100.0)},
+            "merge_done_us": pct(us(merged)), "merge_after_last_arrival_us": pct((merged - last) / 100.0),
+            "last_to_arrive": {"cold": int((np.argmax(a[:, :, 1], axis=1) < nparts - 2).sum()),
+                               "hot": int((np.argmax(a[:, :, 1], axis=1) == nparts - 2).sum()),
+                               "append": int((np.argmax(a[:, :, 1], axis=1) == nparts - 1).sum())}}
+
+
+def leg_phases(hkv, torch, args):
+    """Phase breakdown of the llama8b fused step (2048 tokens) and of the same step at 544 tokens
+    (8 MB: what remains is the step's fixed chain)."""
+    import dataclasses
+    import workloads as wl
+    w = wl.WORKLOADS["llama8b"]
+    log("phases: llama8b fused step, per-workgroup timestamps")
+    res = {"what": "hkv_phase_stamps of one fused step launch among back-to-back launches (64 instances)",
+           "llama8b": phase_breakdown(hkv, torch, w, w.context - 3)}
+    res["llama8b_544_tokens"] = phase_breakdown(hkv, torch, dataclasses.replace(w, context=544), 541)
+    return res
+
+
 def leg_read_floor(hkv, torch, args, nbytes=34_406_400, R=64, reps=20):
     """One-launch read of the llama8b step's bytes (34.4 MB, 64 rotating buffers, 16-byte non-temporal
     loads) over launch shapes: the floor a one-launch decode of that size is measured against."""
@@ -719,7 +791,7 @@ def copy_calibration(torch, mib=256, reps=4):
             "launches": reps}
 
 
-LEGS = ("llama8b", "separate", "long", "llama8b_int4", "long_int4", "llama8b_fp16", "long_fp16", "sparse", "ragged",
+LEGS = ("llama8b", "separate", "long", "llama8b_int4", "long_int4", "llama8b_fp16", "long_fp16", "sparse", "ragged", "phases",
         "graph", "read_floor", "cpu")
 
 
@@ -789,6 +861,8 @@ def main():
         res["ragged"] = leg_ragged(hkv, torch, args)
     if "graph" in legs:
         res["hip_graph"] = leg_graph(hkv, torch, args)
+    if "phases" in legs:
+        res["phases"] = leg_phases(hkv, torch, args)
     if "read_floor" in legs:
         res["read_floor"] = leg_read_floor(hkv, torch, args)
     if args.copy_calibration:

@@ -388,6 +388,23 @@ typedef enum {
 
 hkv_status hkv_timing_enable(hkv_handle h, int enable);
 
+/* Phase timestamps (measurement aid, like the timing state).  While buf is
+ * not NULL, every decode launch of the handle (hkv_decode_attn and its
+ * no-allocation form, hkv_decode_attn_compact, hkv_append_decode) writes, per
+ * workgroup, 8 uint64 readings of the GPU's constant 100 MHz clock
+ * (s_memrealtime) to buf[w*8 + i], w = (sequence*H + kv_head)*nparts + part,
+ * nparts = the launch's workgroups per (sequence, kv-head) (cold splits, then
+ * the hot zone, then, for the fused step, the append workgroup):
+ *   [0] workgroup start, [1] its partial record stored, [2] its arrival
+ *   counted, [3] merge done (0 unless this workgroup merged);
+ *   append workgroup of the fused step also: [4] its first loads done,
+ *   [5] its codes staged (0 without a valid block), [6] its code stores
+ *   issued, [7] its block attended.  Other slots are not written.
+ * Workgroups past bytes / 64 are not recorded; the caller clears buf.  NULL
+ * turns it off.  The clock is the same on every die.
+ * HKV_ERR_ALIGNMENT: buf not 8-byte aligned. */
+hkv_status hkv_phase_stamps(hkv_handle h, uint64_t* buf, size_t bytes);
+
 /* Launch-plan override (testing and tuning aid; like the timing state, it is
  * the handle's only other mutable state).  nsplit > 0 makes every dense decode
  * and fused step use a static plan of (at most) nsplit cold splits per

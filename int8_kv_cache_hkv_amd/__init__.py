@@ -31,7 +31,7 @@ EXPORTS = ["hkv_create", "hkv_destroy", "hkv_cache_sizes", "hkv_sizes", "hkv_hea
            "hkv_append", "hkv_decode_attn", "hkv_decode_attn_noalloc", "hkv_append_decode",
            "hkv_sparse_store_bytes", "hkv_sparse_compact", "hkv_decode_attn_compact", "hkv_topk_select", "hkv_status_string",
            "hkv_timing_enable",
-           "hkv_timing_read", "hkv_last_error_detail", "hkv_read_probe", "hkv_plan_override"]
+           "hkv_timing_read", "hkv_last_error_detail", "hkv_read_probe", "hkv_plan_override", "hkv_phase_stamps"]
 
 
 class HKVError(RuntimeError):
@@ -88,6 +88,7 @@ def _load() -> ctypes.CDLL:
         "hkv_timing_read": [vp, i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64), i32],
         "hkv_read_probe": [vp, sz, i32, i32, vp, vp],
         "hkv_plan_override": [vp, i32, i32],
+        "hkv_phase_stamps": [vp, vp, sz],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -234,6 +235,15 @@ def hkv_decode_attn_compact(handle: int, desc: CacheDesc, store, k_sel: int, q, 
                                         _ptr(out), _ptr(lse), _ptr(workspace),
                                         int(workspace.numel() * workspace.element_size()), _stream(stream)),
            "hkv_decode_attn_compact")
+
+
+def hkv_phase_stamps(handle: int, buf=None) -> None:
+    """Per-workgroup phase timestamps of the handle's decode launches into `buf` (uint64 / int64
+    device tensor, 8 per workgroup), or off with None."""
+    if buf is None:
+        _check(_lib.hkv_phase_stamps(handle, None, 0), "hkv_phase_stamps")
+    else:
+        _check(_lib.hkv_phase_stamps(handle, _ptr(buf), int(buf.numel() * buf.element_size())), "hkv_phase_stamps")
 
 
 def hkv_plan_override(handle: int, nsplit: int = 0, claim_workgroups: int = 0) -> None:

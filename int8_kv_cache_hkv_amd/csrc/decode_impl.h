@@ -1139,6 +1139,9 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
     if (lane == 0) am.red[i][w] = mx[i];
   }
   __syncthreads();  // also: the spilled slot has been read, it may be overwritten
+  const bool stamp = p.stamps != nullptr;
+  const unsigned long long t_loaded = stamp ? __builtin_amdgcn_s_memrealtime() : 0ull;
+  unsigned long long t_coded = 0ull;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float r = am.red[i][0];
@@ -1159,7 +1162,6 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
 #pragma unroll
     for (int kv = 0; kv < 2; ++kv) {
       const float m_old = mx[kv], m_new = mx[2 + kv];
-      int8_t* tile = c.cold + tile_offset(phys, h, kv, H, TB);
       if constexpr (BITS == 0) {
         whole[kv] = ts == 0;
         scl[kv] = 1.f;
@@ -1180,6 +1182,7 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
             }
         }
       } else {
+        int8_t* tile = c.cold + tile_offset(phys, h, kv, H, TB);
         whole[kv] = !(ts > 0 && m_new <= m_old);
         const float sc = (whole[kv] ? fmaxf(m_old, m_new) : m_old) / static_cast<float>(F::kLimit);
         scl[kv] = sc;
@@ -1226,6 +1229,7 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
       }
     }
     __syncthreads();  // stage complete
+    if (stamp) t_coded = __builtin_amdgcn_s_memrealtime();
     if (tid < 2 && c.quant_err) {  // debug statistic: the block's largest |x - code * scale| (0 for fp16)
       float e = 0.f;
 #pragma unroll
@@ -1288,6 +1292,7 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
   if (tid < 2 * VR)
     reinterpret_cast<u32x4_t*>(c.hot + ((bhs * T + slot) * 2 + tid / VR) * D)[tid % VR] = nr;
 
+  const unsigned long long t_stored = stamp ? __builtin_amdgcn_s_memrealtime() : 0ull;
   // ---- tail block jt, rows [0, ts], by wave 0 with the cold-unit code
   if (w == 0) {
     float um[NG], ul[NG], uz[NG];
@@ -1362,6 +1367,16 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
           am.unit.wacc[0][4 * quad + r][64 * ps2 + lane] = uacc[quad][ps2][r];
   }
   __syncthreads();
+  if (stamp && tid == 0) {  // phase timestamps of this workgroup: loads, codes, code stores, block attended
+    const size_t wg = static_cast<size_t>(bh) * gridDim.x + p.nsplit + 1;
+    if (wg < static_cast<size_t>(p.stamp_wgs)) {
+      unsigned long long* a = p.stamps + wg * 8;
+      a[4] = t_loaded;
+      a[5] = t_coded;
+      a[6] = t_stored;
+      a[7] = __builtin_amdgcn_s_memrealtime();
+    }
+  }
   for (int i = tid; i < G * (D / 2); i += kThreads) {
     const int g = i / (D / 2), d = 2 * (i % (D / 2));
     float* pg = partial_ptr<D>(p, bh, p.nsplit + 1, g);
@@ -1396,6 +1411,10 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, const WgCoord
   const int b = wg.z;
   const int bh = b * c.H + h;
   const int tid = threadIdx.x;
+  // phase timestamps: this workgroup's 8 slots, when asked for and inside the buffer
+  const size_t stamp_wg = static_cast<size_t>(bh) * gridDim.x + split;
+  unsigned long long* const st = p.stamps && stamp_wg < static_cast<size_t>(p.stamp_wgs) ? p.stamps + stamp_wg * 8 : nullptr;
+  const unsigned long long t_start = st ? __builtin_amdgcn_s_memrealtime() : 0ull;
   if (split < p.nsplit) {
     cold_split<D, G, BITS, MODE, FUSED, CLAIM, STATS>(p, sm.cold, b, h, bh, split);
   } else if constexpr (FUSED) {
@@ -1407,12 +1426,19 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, const WgCoord
   // ---- arrival: wait until this workgroup's partial stores are complete, count, and let the
   // last workgroup merge
   __builtin_amdgcn_s_waitcnt(0);
+  const unsigned long long t_done = st ? __builtin_amdgcn_s_memrealtime() : 0ull;
   __syncthreads();
   const int NS = p.nsplit + (FUSED ? 2 : 1);  // partials of this (sequence, kv-head)
   if (tid == 0)
     s_last = __hip_atomic_fetch_add(&p.counters[bh], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
              static_cast<unsigned>(NS - 1);
   __syncthreads();
+  if (st && tid == 0) {
+    st[0] = t_start;
+    st[1] = t_done;
+    st[2] = __builtin_amdgcn_s_memrealtime();
+    st[3] = 0ull;
+  }
   if (!s_last) return;
   __builtin_amdgcn_s_setprio(3);  // the merge ends the (sequence, kv-head): ahead of streaming waves
   const int Hq = c.H * G;
@@ -1466,6 +1492,10 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, const WgCoord
     if (d == 0 && p.lse) p.lse[static_cast<size_t>(b) * Hq + hq] = (M + __builtin_log2f(L)) * kLn2;
     // entropy -sum p ln p = lse - E_p[z] (z the natural-log logits): in base-2 units M + log2 L - Z / L
     if (want_z) entropy[static_cast<size_t>(b) * Hq + hq] = (M + __builtin_log2f(L) - Z / L) * kLn2;
+  }
+  if (st) {
+    __syncthreads();  // every output of the merge is written
+    if (tid == 0) st[3] = __builtin_amdgcn_s_memrealtime();
   }
   if (tid == 0) {
     __hip_atomic_store(&p.counters[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

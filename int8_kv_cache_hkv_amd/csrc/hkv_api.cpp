@@ -55,6 +55,8 @@ struct hkv_ctx {
   int force_splits = 0;      // plan override (hkv_plan_override): static plans of this many splits
   int claim_workgroups = 0;  // plan override: grid of claim plans (0 = the width's default)
   bool timing = false;
+  unsigned long long* stamps = nullptr;  // phase timestamps (hkv_phase_stamps), nullptr = off
+  size_t stamp_wgs = 0;
   struct Pending {
     int kind;
     hipEvent_t start, stop;
@@ -398,6 +400,8 @@ hkv_status decode_impl(hkv_ctx* h, const hkv_cache_desc* c, const void* q, int n
 
   hkv::DecodeParams p;
   p.c = view_of(h, c);
+  p.stamps = h->stamps;
+  p.stamp_wgs = static_cast<int>(std::min<size_t>(h->stamp_wgs, INT32_MAX));
   p.G = G;
   p.q = static_cast<const _Float16*>(q);
   p.sel = sel_idx;
@@ -646,6 +650,8 @@ hkv_status hkv_append_decode(hkv_handle h, const hkv_cache_desc* c, const void* 
 
     hkv::DecodeParams p;
     p.c = view_of(h, c);
+    p.stamps = h->stamps;
+    p.stamp_wgs = static_cast<int>(std::min<size_t>(h->stamp_wgs, INT32_MAX));
     p.G = G;
     p.q = static_cast<const _Float16*>(q);
     p.sel = nullptr;
@@ -744,6 +750,8 @@ hkv_status hkv_decode_attn_compact(hkv_handle h, const hkv_cache_desc* c, const 
     const StoreLayout l = store_layout(h, c->batch, k_sel);
     hkv::DecodeParams p;
     p.c = view_of(h, c);
+    p.stamps = h->stamps;
+    p.stamp_wgs = static_cast<int>(std::min<size_t>(h->stamp_wgs, INT32_MAX));
     p.G = G;
     p.q = static_cast<const _Float16*>(q);
     p.sel = nullptr;
@@ -849,6 +857,14 @@ hkv_status hkv_plan_override(hkv_handle h, int nsplit, int claim_workgroups) {
     return HKV_ERR_INVALID_VALUE;
   h->force_splits = nsplit;
   h->claim_workgroups = claim_workgroups;
+  return HKV_OK;
+}
+
+hkv_status hkv_phase_stamps(hkv_handle h, uint64_t* buf, size_t bytes) {
+  if (!h) return HKV_ERR_NULL_POINTER;
+  if (buf && reinterpret_cast<uintptr_t>(buf) % 8 != 0) return HKV_ERR_ALIGNMENT;
+  h->stamps = reinterpret_cast<unsigned long long*>(buf);
+  h->stamp_wgs = buf ? bytes / (8 * sizeof(uint64_t)) : 0;
   return HKV_OK;
 }
 

@@ -87,6 +87,9 @@ struct DecodeParams {
   const float2* store_scales;
   const int32_t* store_counts;
   int store_units;
+  // phase timestamps (hkv_phase_stamps): 8 x uint64 per workgroup, stamp_wgs workgroups; nullptr = off
+  unsigned long long* stamps;
+  int stamp_wgs;
 };
 
 // Compacted sparse store of a selection (see compact.hip): per (sequence, kv-head) `units` units of

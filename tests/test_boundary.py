@@ -259,6 +259,16 @@ def test_plan_override_values():
         hkv.hkv_destroy(h)
 
 
+def test_phase_stamps_arguments():
+    h = hkv.hkv_create(8, 128)
+    try:
+        assert hkv._lib.hkv_phase_stamps(None, None, 0) == -3
+        assert hkv._lib.hkv_phase_stamps(h, 4, 64) == -7          # misaligned (no device access)
+        assert hkv._lib.hkv_phase_stamps(h, None, 0) == 0
+    finally:
+        hkv.hkv_destroy(h)
+
+
 def test_status_strings():
     assert hkv.hkv_status_string(OOM) == "out of host memory"
     for st in (0, -1, -2, -3, -4, -5, -6, -7, -8):

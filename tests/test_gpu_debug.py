@@ -143,3 +143,59 @@ def test_debug_entropy_claim_plan():
     torch.cuda.synchronize()
     _check_entropy(ent, q, states, "claim plan, no-allocation entry point")
     cache.close()
+
+
+def test_phase_stamps_are_ordered_and_change_nothing():
+    """hkv_phase_stamps: every workgroup's start <= work done <= arrival, each (sequence, kv-head)
+    merged once after its last arrival, the fused step's append phases in order; the outputs with
+    and without timestamps are equal bit for bit (static plans)."""
+    import int8_kv_cache_hkv_amd as hkv
+    torch = gh.torch_mod()
+    w = wl.WORKLOADS["llama8b"]
+    n = 32 + 64 * 9 + 5
+    B = 4
+    caches = [gh.make_cache(w, n + 8, batch=B) for _ in range(2)]
+    for c in caches:
+        gh.fill(c, w, [n] * B)
+    q = gh.upload(wl.queries(w)[:B])
+    kb = gh.upload(np.stack([wl.tokens(w, b, n, 1, "k")[0] for b in range(B)]))
+    vb = gh.upload(np.stack([wl.tokens(w, b, n, 1, "v")[0] for b in range(B)]))
+    outs = []
+    for use in (False, True):
+        c = caches[int(use)]
+        buf = torch.zeros(B * w.n_kv_heads * 140 * 8, dtype=torch.int64, device=q.device)
+        if use:
+            hkv.hkv_phase_stamps(c.handle, buf)
+        o1 = torch.empty_like(q)
+        c.decode(q, out=o1)
+        torch.cuda.synchronize()
+        st_plain = buf.cpu().numpy().copy()
+        buf.zero_()
+        o2 = torch.empty_like(q)
+        c.append_decode(kb, vb, q, out=o2)
+        torch.cuda.synchronize()
+        st_fused = buf.cpu().numpy().copy()
+        hkv.hkv_phase_stamps(c.handle, None)
+        outs.append((o1.cpu().numpy(), o2.cpu().numpy()))
+        if not use:
+            assert not st_plain.any() and not st_fused.any()
+            continue
+        for st, fused in ((st_plain, False), (st_fused, True)):
+            rows = st.reshape(-1, 8)
+            npart = int((rows[:, 0] != 0).sum()) // (B * w.n_kv_heads)
+            a = rows[:B * w.n_kv_heads * npart].reshape(B * w.n_kv_heads, npart, 8)
+            assert (a[:, :, 0] > 0).all()
+            assert (a[:, :, 0] <= a[:, :, 1]).all() and (a[:, :, 1] <= a[:, :, 2]).all()
+            merges = (a[:, :, 3] != 0).sum(axis=1)
+            assert (merges == 1).all(), "each (sequence, kv-head) merges once"
+            assert (a[:, :, 3].max(axis=1) >= a[:, :, 1].max(axis=1)).all()
+            if fused:
+                app = a[:, npart - 1]
+                assert (app[:, 0] <= app[:, 4]).all() and (app[:, 4] <= app[:, 6]).all()
+                assert (app[:, 6] <= app[:, 7]).all() and (app[:, 7] <= app[:, 1]).all()
+                coded = app[:, 5] != 0
+                assert ((app[coded, 4] <= app[coded, 5]) & (app[coded, 5] <= app[coded, 6])).all()
+    for x, y in zip(outs[0], outs[1]):
+        assert np.array_equal(x.view(np.uint16), y.view(np.uint16))
+    for c in caches:
+        c.close()
