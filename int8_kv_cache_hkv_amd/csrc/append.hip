@@ -71,23 +71,22 @@ __device__ __forceinline__ float stage_row(int8_t* stage, const u32x4_t (&x)[NV]
     }
     return 0.f;
   } else {
-    const float rs = __builtin_amdgcn_rcpf(s);
+    const float rs = quant_recip(s);
     float err = 0.f;
     uint32_t q[CPT / 4];
 #pragma unroll
     for (int i = 0; i < CPT / 4; ++i) {
-      uint32_t packed = 0;
+      uint32_t cb[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int e = 4 * i + k;
         const uint32_t wd = x[e / 8][(e % 8) / 2];
         const float xv = (e & 1) ? half_hi(wd) : half_lo(wd);
-        float qv = 0.f;
-        if (s > 0.f) qv = quant_code<Fmt<BITS>::kLimit>(xv, s, rs);
+        const float qv = quant_code<Fmt<BITS>::kLimit>(xv, s, rs);
         err = fmaxf(err, __builtin_fabsf(fmaf(-qv, s, xv)));
-        packed |= (static_cast<uint32_t>(static_cast<int>(qv)) & 0xffu) << (8 * k);
+        cb[k] = static_cast<uint32_t>(static_cast<int>(qv));
       }
-      q[i] = packed;
+      q[i] = pack_low_bytes(cb[0], cb[1], cb[2], cb[3]);
     }
     if (kv == 0) {
       uint32_t* dst = reinterpret_cast<uint32_t*>(stage + t * TS::KROW + c0);
@@ -116,7 +115,7 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 template <int NV>
 __device__ __forceinline__ float slice_err8(const u32x4_t (&x)[NV], float s) {
   if (!(s > 0.f)) return 0.f;
-  const float rs = __builtin_amdgcn_rcpf(s);
+  const float rs = quant_recip(s);
   float err = 0.f;
 #pragma unroll
   for (int v = 0; v < NV; ++v)
@@ -385,20 +384,17 @@ __global__ __launch_bounds__(kThreads) void append_step_kernel(AppendParams p) {
   };
   // codes of one row slice with scale s (as the IEEE division gives them, round half to even, clamp)
   auto code_slice = [&](const u32x4_t (&x)[NV], float s, uint32_t (&q)[CPT / 4]) {
-    const float rs = __builtin_amdgcn_rcpf(s);
+    const float rs = quant_recip(s);
 #pragma unroll
     for (int i = 0; i < CPT / 4; ++i) {
-      uint32_t packed = 0;
+      uint32_t cb[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int e = 4 * i + k;
         const uint32_t wd = x[e / 8][(e % 8) / 2];
-        const float xv = (e & 1) ? half_hi(wd) : half_lo(wd);
-        float qv = 0.f;
-        if (s > 0.f) qv = quant_code<127>(xv, s, rs);
-        packed |= (static_cast<uint32_t>(static_cast<int>(qv)) & 0xffu) << (8 * k);
+        cb[k] = static_cast<uint32_t>(static_cast<int>(quant_code<127>((e & 1) ? half_hi(wd) : half_lo(wd), s, rs)));
       }
-      q[i] = packed;
+      q[i] = pack_low_bytes(cb[0], cb[1], cb[2], cb[3]);
     }
   };
 

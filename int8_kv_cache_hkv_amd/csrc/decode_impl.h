@@ -1186,25 +1186,32 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
         whole[kv] = !(ts > 0 && m_new <= m_old);
         const float sc = (whole[kv] ? fmaxf(m_old, m_new) : m_old) / static_cast<float>(F::kLimit);
         scl[kv] = sc;
-        const float rsc = __builtin_amdgcn_rcpf(sc);
+        // branch-free: every value lies inside the scale's maximum, so the byte form needs no clamp
+        const float rsc = quant_recip(sc);
         uint32_t qw[CPT / 4];
-        float err = 0.f;
 #pragma unroll
         for (int i = 0; i < CPT / 4; ++i) {
-          uint32_t packed = 0;
+          uint32_t cb[4];
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             const int e = 4 * i + k;
             const uint32_t wd = x[kv][e / 8][(e % 8) / 2];
-            const float xv = (e & 1) ? half_hi(wd) : half_lo(wd);
-            const float qv = sc > 0.f ? quant_code<F::kLimit>(xv, sc, rsc) : 0.f;
-            err = fmaxf(err, __builtin_fabsf(fmaf(-qv, sc, xv)));
-            packed |= (static_cast<uint32_t>(static_cast<int>(qv)) & 0xffu) << (8 * k);
+            cb[k] = code_bits(quant_quotient((e & 1) ? half_hi(wd) : half_lo(wd), sc, rsc));
           }
-          qw[i] = packed;
+          qw[i] = pack_low_bytes(cb[0], cb[1], cb[2], cb[3]);
         }
-        err = wave_max_dpp(err);
-        if (lane == 0) am.rerr[kv][w] = err;
+        if (c.quant_err) {  // debug statistic: largest |x - code * scale| of the codes just made
+          float err = 0.f;
+#pragma unroll
+          for (int e = 0; e < CPT; ++e) {
+            const uint32_t wd = x[kv][e / 8][(e % 8) / 2];
+            const float xv = (e & 1) ? half_hi(wd) : half_lo(wd);
+            const float qv = static_cast<float>(static_cast<int8_t>(qw[e / 4] >> (8 * (e % 4))));
+            err = fmaxf(err, __builtin_fabsf(fmaf(-qv, sc, xv)));
+          }
+          err = wave_max_dpp(err);
+          if (lane == 0) am.rerr[kv][w] = err;
+        }
         if (kv == 0) {
           uint32_t* srow = reinterpret_cast<uint32_t*>(am.stage_k + t * KROW + part * CPT);
 #pragma unroll
