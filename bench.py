@@ -623,9 +623,10 @@ def leg_graph(hkv, torch, args, steps=640, R=64):
 
 def phase_breakdown(hkv, torch, w, n0, R=64, rounds=3):
     """Per-workgroup phase timestamps (hkv_phase_stamps) of one fused step launch among back-to-back
-    launches over R rotating instances: per role (cold split, hot window, append), when its work was
-    done, and for the append workgroup its phases; when the merges were done.  Times in us from the
-    first workgroup's start (100 MHz clock)."""
+    launches over R rotating instances: per role (cold split; the append workgroup, which attends the
+    hot window and then appends and attends the tail block), when its work was done, and the append
+    workgroup's phases; when the merges were done.  Times in us from the first workgroup's start
+    (100 MHz clock)."""
     import workloads as wl
     B, H, Hq, d = w.batch, w.n_kv_heads, w.n_q_heads, w.head_dim
     insts = [Inst(hkv, w, n0 + rounds + 2) for _ in range(R)]
@@ -661,20 +662,18 @@ def phase_breakdown(hkv, torch, w, n0, R=64, rounds=3):
     t0 = a[:, :, 0].min()
     us = lambda v: (np.asarray(v, np.float64) - t0) / 100.0
     pct = lambda v: {f"p{p}": round(float(np.percentile(v, p)), 2) for p in (0, 50, 100)}
-    cold, hot, app = a[:, :nparts - 2], a[:, nparts - 2], a[:, nparts - 1]
+    cold, app = a[:, :nparts - 1], a[:, nparts - 1]
     merged = a[:, :, 3].max(axis=1)
     last = a[:, :, 1].max(axis=1)
     return {"context": n0 + rounds, "batch": B, "workgroups_per_pair": int(nparts),
-            "cold_split_done_us": pct(us(cold[:, :, 1])), "hot_window_done_us": pct(us(hot[:, 1])),
-            "append_done_us": pct(us(app[:, 1])),
-            "append_phases_us": {"first_loads": pct((app[:, 4] - app[:, 0]) / 100.0),
+            "cold_split_done_us": pct(us(cold[:, :, 1])), "append_done_us": pct(us(app[:, 1])),
+            "append_phases_us": {"loads_and_hot_window": pct((app[:, 4] - app[:, 0]) / 100.0),
                                  "coding": pct((app[:, 5] - app[:, 4]) / 100.0),
                                  "code_stores": pct((app[:, 6] - app[:, 5]) / 100.0),
                                  "block_attention": pct((app[:, 7] - app[:, 6]) / 100.0),
                                  "partial_and_arrival": pct((app[:, 1] - app[:, 7]) / 100.0)},
             "merge_done_us": pct(us(merged)), "merge_after_last_arrival_us": pct((merged - last) / 100.0),
-            "last_to_arrive": {"cold": int((np.argmax(a[:, :, 1], axis=1) < nparts - 2).sum()),
-                               "hot": int((np.argmax(a[:, :, 1], axis=1) == nparts - 2).sum()),
+            "last_to_arrive": {"cold": int((np.argmax(a[:, :, 1], axis=1) < nparts - 1).sum()),
                                "append": int((np.argmax(a[:, :, 1], axis=1) == nparts - 1).sum())}}
 
 

@@ -218,6 +218,8 @@ hkv_status hkv_workspace_bytes(hkv_handle h, const hkv_cache_desc* c, int n_q_he
  *   k_new, v_new  device fp16 [batch][max_n_new][n_kv_heads][head_dim]; row
  *                 i < n_new_host[b] of sequence b is token seq_len[b] + i.
  *   n_new_host    host int32 [batch], each in [0, max_n_new].
+ * The values are finite fp16 (a block's scale is its largest magnitude; a
+ * NaN or infinity gives that block undefined codes).
  * Every cold block touched by the append is (re-)quantised from its FP16
  * values; headers get n_valid/logical_block; the hot ring, tail shadow,
  * seq_len_dev and seq_len_host are updated.  The result does not depend on
@@ -394,12 +396,14 @@ hkv_status hkv_timing_enable(hkv_handle h, int enable);
  * workgroup, 8 uint64 readings of the GPU's constant 100 MHz clock
  * (s_memrealtime) to buf[w*8 + i], w = (sequence*H + kv_head)*nparts + part,
  * nparts = the launch's workgroups per (sequence, kv-head) (cold splits, then
- * the hot zone, then, for the fused step, the append workgroup):
- *   [0] workgroup start, [1] its partial record stored, [2] its arrival
+ * the hot zone; for the fused step, in place of the hot zone's, the append
+ * workgroup, which attends the new hot window and then appends):
+ *   [0] workgroup start, [1] its partial records stored, [2] its arrival
  *   counted, [3] merge done (0 unless this workgroup merged);
- *   append workgroup of the fused step also: [4] its first loads done,
- *   [5] its codes staged (0 without a valid block), [6] its code stores
- *   issued, [7] its block attended.  Other slots are not written.
+ *   append workgroup of the fused step also: [4] its hot window attended
+ *   (its first loads included), [5] its codes staged (0 without a valid
+ *   block), [6] its code stores issued, [7] its block attended.  Other slots
+ *   are not written.
  * Workgroups past bytes / 64 are not recorded; the caller clears buf.  NULL
  * turns it off.  The clock is the same on every die.
  * HKV_ERR_ALIGNMENT: buf not 8-byte aligned. */

@@ -374,14 +374,7 @@ __global__ __launch_bounds__(kThreads) void append_step_kernel(AppendParams p) {
 #pragma unroll
     for (int v = 0; v < NV; ++v) x[v] = u32x4_t{0u, 0u, 0u, 0u};
   };
-  auto slice_max = [&](const u32x4_t (&x)[NV]) -> float {
-    float m = 0.f;
-#pragma unroll
-    for (int v = 0; v < NV; ++v)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(half_lo(x[v][i])), fabsf(half_hi(x[v][i]))));
-    return m;
-  };
+  auto slice_max = [&](const u32x4_t (&x)[NV]) -> float { return slice_absmax<NV>(x); };
   // codes of one row slice with scale s (as the IEEE division gives them, round half to even, clamp)
   auto code_slice = [&](const u32x4_t (&x)[NV], float s, uint32_t (&q)[CPT / 4]) {
     const float rs = quant_recip(s);

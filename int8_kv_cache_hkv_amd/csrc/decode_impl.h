@@ -903,50 +903,44 @@ __device__ __forceinline__ void cold_split(const DecodeParams& p, DecodeSmem<D, 
 // softmax weights; all four waves then accumulate thread (g, d) = sum_t p v.
 // Attends ring slots [0, n_hot); slot sub_slot (if >= 0) is read from the
 // rows sub_k / sub_v instead of the ring (the token a fused append is putting
-// there).  Leaves m, l (base-2 units) and acc in hm.
+// there).  The first chunk's loads are issued ahead of the query's, so both
+// take one memory round trip.  Leaves m, l (base-2 units) and acc in hm.
 template <int D, int G>
-__device__ void hot_attend(const DecodeParams& p, HotSmem<D, G>& hm, int b, int h, int bh, int n_hot, int sub_slot,
-                           const _Float16* sub_k, const _Float16* sub_v) {
+__device__ void hot_attend(const DecodeParams& p, HotSmem<D, G>& hm, _Float16 (*qh)[4][Cfg<D, G>::QROW], int b, int h,
+                           int bh, int n_hot, int sub_slot, const _Float16* sub_k, const _Float16* sub_v) {
   using C = Cfg<D, G>;
   constexpr int NG = 4 * C::NQ;
   constexpr int ROW = 2 * D + 8;          // padded fp16 [K|V] row
   constexpr int VPR = 2 * D / 8;          // 16-byte vectors per row
+  constexpr int NV = (kHotChunk * VPR + kThreads - 1) / kThreads;
   const CacheView& c = p.c;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  copy_query<D, G>(p.q + (static_cast<size_t>(b) * c.H * G + static_cast<size_t>(h) * G) * D, hm.qh, tid);
-  for (int i = tid; i < G * D; i += kThreads) hm.acc[i / D][i % D] = 0.f;
   const _Float16* hot_bh = c.hot + static_cast<size_t>(bh) * c.T * 2 * D;
+  static_assert(kHotChunk * VPR % kThreads == 0, "a chunk is a whole number of vectors per thread");
+  // this thread's vectors of the chunk at `base`, loaded without branches (a branch would merge the
+  // loaded value at its join and wait there): rows past the window read the chunk's row 0, which the
+  // ring always holds, and are zeroed when staged
+  auto load_chunk = [&](int base, uint4 (&buf)[NV]) {
+    const uint4* src = reinterpret_cast<const uint4*>(hot_bh + static_cast<size_t>(base) * 2 * D);
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int i = tid + k * kThreads;
+      const int r = i / VPR, v = i % VPR;  // row, and vector of its K row then V row
+      const uint4* ptr = base + r == sub_slot ? reinterpret_cast<const uint4*>(v < D / 8 ? sub_k : sub_v) + v % (D / 8)
+                                              : src + (base + r < n_hot ? i : v);
+      buf[k] = *ptr;
+    }
+  };
   float m[NG], l[NG];  // wave 0's running softmax state (wave-uniform)
   const bool stats = p.c.entropy != nullptr;  // entropy statistic asked for: its sum runs in hm.zs
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    m[g] = kNegInf;
-    l[g] = 0.f;
-  }
-  if (tid < NG) hm.zs[tid] = 0.f;  // (wave 0, the only wave that updates it)
-  for (int base = 0; base < n_hot; base += kHotChunk) {
+  // one chunk: stage it (with the query on the first), logits and weights by wave 0, then every
+  // thread's share of acc
+  auto attend_chunk = [&](int base, const uint4 (&buf)[NV]) {
     const int cnt = min(kHotChunk, n_hot - base);
-    const uint4* src = reinterpret_cast<const uint4*>(hot_bh + static_cast<size_t>(base) * 2 * D);
-    constexpr int NV = (kHotChunk * VPR + kThreads - 1) / kThreads;
-    uint4 buf[NV];  // all of the chunk's loads in flight together
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int i = tid + k * kThreads;
-      if (i < cnt * VPR) {
-        if (base + i / VPR == sub_slot) {
-          const int v = i % VPR;  // K row then V row
-          buf[k] = reinterpret_cast<const uint4*>(v < D / 8 ? sub_k : sub_v)[v % (D / 8)];
-        } else {
-          buf[k] = src[i];
-        }
-      } else {
-        buf[k] = make_uint4(0, 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      const int i = tid + k * kThreads;
-      if (i < kHotChunk * VPR) *reinterpret_cast<uint4*>(&hm.kv[(i / VPR) * ROW + (i % VPR) * 8]) = buf[k];
+      *reinterpret_cast<uint4*>(&hm.kv[(i / VPR) * ROW + (i % VPR) * 8]) = i / VPR < cnt ? buf[k] : make_uint4(0, 0, 0, 0);
     }
     __syncthreads();
     if (w == 0) {
@@ -960,7 +954,7 @@ __device__ void hot_attend(const DecodeParams& p, HotSmem<D, G>& hm, int b, int 
         const half4_t bk = *reinterpret_cast<const half4_t*>(kr + k0);
 #pragma unroll
         for (int quad = 0; quad < C::NQ; ++quad)
-          s[quad] = mfma_qk(*reinterpret_cast<const half4_t*>(&hm.qh[quad][lane & 3][k0]), bk, s[quad]);
+          s[quad] = mfma_qk(*reinterpret_cast<const half4_t*>(&qh[quad][lane & 3][k0]), bk, s[quad]);
       }
 #pragma unroll
       for (int quad = 0; quad < C::NQ; ++quad) {
@@ -983,13 +977,38 @@ __device__ void hot_attend(const DecodeParams& p, HotSmem<D, G>& hm, int b, int 
       }
     }
     __syncthreads();
-    for (int i = tid; i < G * D; i += kThreads) {
-      const int g = i / D, d = i % D;
-      float a = hm.acc[g][d] * hm.alpha[g];
-      for (int t = 0; t < cnt; ++t) a = fmaf(hm.z[g][t], static_cast<float>(hm.kv[t * ROW + D + d]), a);  // rows past cnt are not staged
-      hm.acc[g][d] = a;
+    // thread (g, d): channels d, d + 1 of query head g over every staged row, a fixed count so that
+    // the LDS reads are issued together (rows past cnt are zero with weight 0: fma(0, 0, a) = a)
+    for (int i = tid; i < G * (D / 2); i += kThreads) {
+      const int g = i / (D / 2), d = 2 * (i % (D / 2));
+      float a0 = hm.acc[g][d] * hm.alpha[g], a1 = hm.acc[g][d + 1] * hm.alpha[g];
+#pragma unroll
+      for (int t = 0; t < kHotChunk; ++t) {
+        const float z = hm.z[g][t];
+        const uint32_t v2 = *reinterpret_cast<const uint32_t*>(&hm.kv[t * ROW + D + d]);
+        a0 = fmaf(z, half_lo(v2), a0);
+        a1 = fmaf(z, half_hi(v2), a1);
+      }
+      hm.acc[g][d] = a0;
+      hm.acc[g][d + 1] = a1;
     }
     __syncthreads();
+  };
+  // the first chunk's loads and the query's go out together (straight-line code: one round trip)
+  uint4 buf[NV];  // all of a chunk's loads in flight together
+  load_chunk(0, buf);
+  copy_query<D, G>(p.q + (static_cast<size_t>(b) * c.H * G + static_cast<size_t>(h) * G) * D, qh, tid);
+  for (int i = tid; i < G * D; i += kThreads) hm.acc[i / D][i % D] = 0.f;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    m[g] = kNegInf;
+    l[g] = 0.f;
+  }
+  if (tid < NG) hm.zs[tid] = 0.f;  // (wave 0, the only wave that updates it)
+  if (n_hot > 0) attend_chunk(0, buf);
+  for (int base = kHotChunk; base < n_hot; base += kHotChunk) {
+    load_chunk(base, buf);
+    attend_chunk(base, buf);
   }
   if (w == 0 && lane == 0) {
 #pragma unroll
@@ -1001,11 +1020,9 @@ __device__ void hot_attend(const DecodeParams& p, HotSmem<D, G>& hm, int b, int 
   __syncthreads();
 }
 
-// ---- hot split of a plain decode: the whole ring, partial at split index nsplit
+// The hot zone's partial record (split index nsplit).
 template <int D, int G>
-__device__ void hot_split(const DecodeParams& p, HotSmem<D, G>& hm, int b, int h, int bh) {
-  const SeqGeom sg = seq_geom(p.c.seq_len[b], p.c.T, kBlockSize);
-  hot_attend<D, G>(p, hm, b, h, bh, sg.n_hot, -1, nullptr, nullptr);
+__device__ __forceinline__ void store_hot_partial(const DecodeParams& p, const HotSmem<D, G>& hm, int bh) {
   for (int i = threadIdx.x; i < G * (D / 2); i += kThreads) {
     const int g = i / (D / 2), d = 2 * (i % (D / 2));
     float* pg = partial_ptr<D>(p, bh, p.nsplit, g);
@@ -1017,12 +1034,20 @@ __device__ void hot_split(const DecodeParams& p, HotSmem<D, G>& hm, int b, int h
   }
 }
 
-// ---- fused one-token append (hkv_append_decode): two more workgroups per
-// (sequence, kv-head) next to the cold splits.
-//   A (split index nsplit): the new hot window, i.e. ring slots
-//     [0, min(n0 + 1, T)) with the new token's slot read from k_new / v_new
-//     (it never reads that slot from the ring, which B overwrites).
-//   B (split index nsplit + 1): the append itself (Hybrid KV Cache page 2.1 /
+// ---- hot split of a plain decode: the whole ring, partial at split index nsplit
+template <int D, int G>
+__device__ void hot_split(const DecodeParams& p, HotSmem<D, G>& hm, int b, int h, int bh) {
+  const SeqGeom sg = seq_geom(p.c.seq_len[b], p.c.T, kBlockSize);
+  hot_attend<D, G>(p, hm, hm.qh, b, h, bh, sg.n_hot, -1, nullptr, nullptr);
+  store_hot_partial<D, G>(p, hm, bh);
+}
+
+// ---- fused one-token append (hkv_append_decode): one more workgroup per
+// (sequence, kv-head) next to the cold splits, with two partial records.
+//   The new hot window (split index nsplit): ring slots [0, min(n0 + 1, T))
+//     with the new token's slot read from k_new / v_new (it never reads that
+//     slot from the ring, which the append overwrites).
+//   The append itself (split index nsplit + 1; Hybrid KV Cache page 2.1 /
 //     4.2: the token leaving the hot zone joins the cold zone, quantised with
 //     its block's scale) and the attention over that tail block jt.  The
 //     spilled token becomes row ts of block jt, re-coded exactly as the
@@ -1033,32 +1058,23 @@ __device__ void hot_split(const DecodeParams& p, HotSmem<D, G>& hm, int b, int h
 //     (every row is coded there; with an unchanged maximum they equal the
 //     stored codes), so nothing waits for the code stores.  The cold splits
 //     cover only the full blocks before jt.
-template <int D, int G>
-__device__ void hot_window_split(const DecodeParams& p, HotSmem<D, G>& hm, int b, int h, int bh) {
-  __builtin_amdgcn_s_setprio(3);  // short, latency-bound work: issue ahead of the streaming waves
-  const int n0 = __builtin_amdgcn_readfirstlane(p.c.seq_len[b]);
-  const int slot = n0 % p.c.T;
-  const size_t bhs = static_cast<size_t>(bh);
-  hot_attend<D, G>(p, hm, b, h, bh, min(n0 + 1, p.c.T), slot, p.k_new + bhs * D, p.v_new + bhs * D);
-  for (int i = threadIdx.x; i < G * (D / 2); i += kThreads) {
-    const int g = i / (D / 2), d = 2 * (i % (D / 2));
-    float* pg = partial_ptr<D>(p, bh, p.nsplit, g);
-    store_coherent2(pg + kRecHead + d, hm.acc[g][d], hm.acc[g][d + 1]);
-    if (d == 0) {
-      store_coherent2(pg, hm.m[g], hm.l[g]);
-      store_coherent2(pg + 2, hm.zs[g], 0.f);
-    }
-  }
-}
+// The hot window goes first, in the LDS the block's codes take afterwards; its loads are issued
+// behind the append's first round, so the two share one memory round trip.
 
 template <int D, int G, int BITS>
 struct AppendSmem {
   static constexpr int EB = BITS == 0 ? 2 : 1;       // stage bytes per element: one code, or one fp16 value
   static constexpr int KROW = D * EB + 16;           // K stage row: one token's channels (padded)
   static constexpr int VROW = kBlockSize * EB + 16;  // V stage row: one channel's tokens (padded)
+  struct Stage {
+    alignas(16) int8_t k[kBlockSize * KROW];         // the block's K codes / values, [token][channel]
+    alignas(16) int8_t v[D * VROW];                  // its V codes / values, [channel][token]
+  };
   DecodeSmem<D, G> unit;                             // tail block jt, attended by wave 0
-  alignas(16) int8_t stage_k[kBlockSize * KROW];     // its K codes / values, [token][channel]
-  alignas(16) int8_t stage_v[D * VROW];              // its V codes / values, [channel][token]
+  union {
+    Stage stage;                                     // from the coding on
+    HotSmem<D, G> hot;                               // the hot window, attended before the coding
+  };
   float red[4][kWaves];
   float rerr[2][kWaves];                             // debug statistic: per-wave largest |x - code * scale|
 };
@@ -1095,8 +1111,8 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
   const _Float16* knew = p.k_new + bhs * D;
   const _Float16* vnew = p.v_new + bhs * D;
 
-  // ---- first round of loads: the spilled row, the block's old rows (tail shadow), its header, the
-  // new token, and (wave 0) the query rows
+  // ---- first round of loads: the spilled row, the block's old rows (tail shadow), its header and
+  // the new token (the hot window's loads and the query's follow without a wait in between)
   // row t of block jt: an old row (t < ts, from the tail shadow), the spilled row (t == ts, from its
   // ring slot) or nothing; one slice per thread
   u32x4_t x[2][NV];
@@ -1109,28 +1125,20 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
   }
   const int it = min(tid, 2 * VR - 1);  // new token: K row then V row, one vector per thread
   const u32x4_t nr = reinterpret_cast<const u32x4_t*>(it < VR ? knew : vnew)[it % VR];
-  int phys = -1;
-  if (spill && jt < c.max_blocks) {
-    const int ph = c.headers[static_cast<size_t>(b) * c.max_blocks + jt].phys_block;
-    phys = (ph >= 0 && ph < c.num_phys) ? ph : -1;
-  }
-  if (w == 0) {
-    const _Float16* qg = p.q + (static_cast<size_t>(b) * c.H * G + static_cast<size_t>(h) * G) * D;
-    for (int i = lane; i < 4 * C::NQ * (D / 8); i += 64) {
-      const int g = i / (D / 8);
-      const uint4 val = g < G ? reinterpret_cast<const uint4*>(qg + static_cast<size_t>(g) * D)[i % (D / 8)]
-                              : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(&am.unit.qh[g / 4][g % 4][(i % (D / 8)) * 8]) = val;
-    }
-  }
-  auto slice_max = [&](const u32x4_t (&x)[NV]) -> float {
-    float m = 0.f;
-#pragma unroll
-    for (int v = 0; v < NV; ++v)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(half_lo(x[v][i])), fabsf(half_hi(x[v][i]))));
-    return m;
-  };
+  // the block's header: loaded now (from a clamped entry when the table has one) and resolved after
+  // the hot window, so that waiting for it does not hold back the hot window's loads
+  int ph_lane = -1;
+  if (c.max_blocks > 0)
+    ph_lane = c.headers[static_cast<size_t>(b) * c.max_blocks + min(jt, c.max_blocks - 1)].phys_block;
+  // ---- the new hot window (partial nsplit), in the LDS the codes take next; it also puts the query
+  // rows where the block attention reads them
+  hot_attend<D, G>(p, am.hot, am.unit.qh, b, h, bh, min(n0 + 1, T), slot, knew, vnew);
+  store_hot_partial<D, G>(p, am.hot, bh);
+  const int ph = __builtin_amdgcn_readfirstlane(ph_lane);
+  const int phys = spill && jt < c.max_blocks && ph >= 0 && ph < c.num_phys ? ph : -1;
+  const bool stamp = p.stamps != nullptr;
+  const unsigned long long t_hot = stamp ? __builtin_amdgcn_s_memrealtime() : 0ull;
+  auto slice_max = [&](const u32x4_t (&x)[NV]) -> float { return slice_absmax<NV>(x); };
   const float m0 = slice_max(x[0]), m1 = slice_max(x[1]);
   float mx[4] = {t < ts ? m0 : 0.f, t < ts ? m1 : 0.f, t == ts ? m0 : 0.f, t == ts ? m1 : 0.f};
 #pragma unroll
@@ -1138,9 +1146,8 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
     mx[i] = wave_max_dpp(mx[i]);
     if (lane == 0) am.red[i][w] = mx[i];
   }
-  __syncthreads();  // also: the spilled slot has been read, it may be overwritten
-  const bool stamp = p.stamps != nullptr;
-  const unsigned long long t_loaded = stamp ? __builtin_amdgcn_s_memrealtime() : 0ull;
+  __syncthreads();  // also: the spilled slot has been read, it may be overwritten; the hot window's
+                    // LDS has been read
   unsigned long long t_coded = 0ull;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -1165,7 +1172,7 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
       if constexpr (BITS == 0) {
         whole[kv] = ts == 0;
         scl[kv] = 1.f;
-        uint32_t* srow = reinterpret_cast<uint32_t*>(am.stage_k + t * KROW + part * CPT * 2);
+        uint32_t* srow = reinterpret_cast<uint32_t*>(am.stage.k + t * KROW + part * CPT * 2);
         if (kv == 0) {
 #pragma unroll
           for (int v = 0; v < NV; ++v)
@@ -1177,8 +1184,8 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int cc = part * CPT + 8 * v + 2 * i;
-              *reinterpret_cast<uint16_t*>(am.stage_v + cc * VROW + 2 * t) = static_cast<uint16_t>(x[1][v][i]);
-              *reinterpret_cast<uint16_t*>(am.stage_v + (cc + 1) * VROW + 2 * t) = static_cast<uint16_t>(x[1][v][i] >> 16);
+              *reinterpret_cast<uint16_t*>(am.stage.v + cc * VROW + 2 * t) = static_cast<uint16_t>(x[1][v][i]);
+              *reinterpret_cast<uint16_t*>(am.stage.v + (cc + 1) * VROW + 2 * t) = static_cast<uint16_t>(x[1][v][i] >> 16);
             }
         }
       } else {
@@ -1213,13 +1220,13 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
           if (lane == 0) am.rerr[kv][w] = err;
         }
         if (kv == 0) {
-          uint32_t* srow = reinterpret_cast<uint32_t*>(am.stage_k + t * KROW + part * CPT);
+          uint32_t* srow = reinterpret_cast<uint32_t*>(am.stage.k + t * KROW + part * CPT);
 #pragma unroll
           for (int i = 0; i < CPT / 4; ++i) srow[i] = qw[i];
         } else {
 #pragma unroll
           for (int i = 0; i < CPT; ++i)
-            am.stage_v[(part * CPT + i) * VROW + t] = static_cast<int8_t>(qw[i / 4] >> (8 * (i % 4)));
+            am.stage.v[(part * CPT + i) * VROW + t] = static_cast<int8_t>(qw[i / 4] >> (8 * (i % 4)));
         }
         if (BITS == 8 && !whole[kv] && t == ts) {  // only row ts changes: write it in place
           if (kv == 0) {
@@ -1252,9 +1259,9 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
           // byte shared with row ts ^ 1, rewritten from the stage)
           if (kv == 0) {
             if (tid < D / E)
-              reinterpret_cast<uint4*>(tile)[tid * S + ts] = chunk_from_stage<BITS>(am.stage_k + ts * KROW + tid * E * EB);
+              reinterpret_cast<uint4*>(tile)[tid * S + ts] = chunk_from_stage<BITS>(am.stage.k + ts * KROW + tid * E * EB);
           } else if (tid < D) {
-            const int8_t* col = am.stage_v + tid * VROW;
+            const int8_t* col = am.stage.v + tid * VROW;
             int8_t* chunk = tile + ((ts / E) * D + tid) * 16;
             if constexpr (BITS == 4) {
               const int t2 = ts & ~1;
@@ -1271,10 +1278,10 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
         uint4 out;
         if (kv == 0) {
           const int kc = vi / S, tt = vi % S;
-          out = chunk_from_stage<BITS>(am.stage_k + tt * KROW + kc * E * EB);
+          out = chunk_from_stage<BITS>(am.stage.k + tt * KROW + kc * E * EB);
         } else {
           const int vc = vi / D, cc = vi % D;
-          out = chunk_from_stage<BITS>(am.stage_v + cc * VROW + vc * E * EB);
+          out = chunk_from_stage<BITS>(am.stage.v + cc * VROW + vc * E * EB);
         }
         reinterpret_cast<uint4*>(tile)[vi] = out;
       }
@@ -1318,12 +1325,12 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
       // tile registers: K (lane = token) and V (lane = channel), from the stage
       Tiles<D, BITS> tl;
 #pragma unroll
-      for (int ch = 0; ch < D / E; ++ch) tl.kr[ch] = chunk_from_stage<BITS>(am.stage_k + lane * KROW + ch * E * EB);
+      for (int ch = 0; ch < D / E; ++ch) tl.kr[ch] = chunk_from_stage<BITS>(am.stage.k + lane * KROW + ch * E * EB);
 #pragma unroll
       for (int ps2 = 0; ps2 < C::NDL; ++ps2)
 #pragma unroll
         for (int vc = 0; vc < 64 / E; ++vc)
-          tl.vr[ps2][vc] = chunk_from_stage<BITS>(am.stage_v + (64 * ps2 + lane) * VROW + vc * E * EB);
+          tl.vr[ps2][vc] = chunk_from_stage<BITS>(am.stage.v + (64 * ps2 + lane) * VROW + vc * E * EB);
       WaveState<D, G> st;
       st.stats = STATS;
 #pragma unroll
@@ -1374,11 +1381,11 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
           am.unit.wacc[0][4 * quad + r][64 * ps2 + lane] = uacc[quad][ps2][r];
   }
   __syncthreads();
-  if (stamp && tid == 0) {  // phase timestamps of this workgroup: loads, codes, code stores, block attended
-    const size_t wg = static_cast<size_t>(bh) * gridDim.x + p.nsplit + 1;
+  if (stamp && tid == 0) {  // phase timestamps of this workgroup: hot window, codes, code stores, block attended
+    const size_t wg = static_cast<size_t>(bh) * gridDim.x + p.nsplit;
     if (wg < static_cast<size_t>(p.stamp_wgs)) {
       unsigned long long* a = p.stamps + wg * 8;
-      a[4] = t_loaded;
+      a[4] = t_hot;
       a[5] = t_coded;
       a[6] = t_stored;
       a[7] = __builtin_amdgcn_s_memrealtime();
@@ -1425,8 +1432,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, const WgCoord
   if (split < p.nsplit) {
     cold_split<D, G, BITS, MODE, FUSED, CLAIM, STATS>(p, sm.cold, b, h, bh, split);
   } else if constexpr (FUSED) {
-    if (split == p.nsplit) hot_window_split<D, G>(p, sm.hot, b, h, bh);
-    else append_unit_split<D, G, BITS, STATS>(p, sm.app, b, h, bh);
+    append_unit_split<D, G, BITS, STATS>(p, sm.app, b, h, bh);  // the hot window, then the append
   } else {
     hot_split<D, G>(p, sm.hot, b, h, bh);
   }
@@ -1436,9 +1442,10 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, const WgCoord
   const unsigned long long t_done = st ? __builtin_amdgcn_s_memrealtime() : 0ull;
   __syncthreads();
   const int NS = p.nsplit + (FUSED ? 2 : 1);  // partials of this (sequence, kv-head)
+  const unsigned arrivals = FUSED && split >= p.nsplit ? 2u : 1u;  // the fused append's workgroup writes two
   if (tid == 0)
-    s_last = __hip_atomic_fetch_add(&p.counters[bh], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             static_cast<unsigned>(NS - 1);
+    s_last = __hip_atomic_fetch_add(&p.counters[bh], arrivals, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             static_cast<unsigned>(NS) - arrivals;
   __syncthreads();
   if (st && tid == 0) {
     st[0] = t_start;
@@ -1566,7 +1573,7 @@ hipError_t launch_k(K kernel, dim3 grid, int block, const P& p, const LaunchCtx&
 
 template <int D, int G, int BITS>
 hipError_t launch_dg(const DecodeParams& p, const LaunchCtx& ctx, const uint16_t* order) {
-  const dim3 grid(p.nparts, p.c.H, p.c.B);  // (split, kv-head, sequence)
+  const dim3 grid(grid_parts(p), p.c.H, p.c.B);  // (split, kv-head, sequence)
   if (p.c.entropy) {  // statistics: static plans in plain order only
     if (order || p.work || p.wg_order != kOrderPlain) return hipErrorInvalidValue;
     if (p.k_new) return launch_k(decode_kernel<D, G, BITS, kModeDense, true, false, true>, grid, kThreads, p, ctx);

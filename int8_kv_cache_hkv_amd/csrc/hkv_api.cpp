@@ -204,7 +204,8 @@ int max_splits(int64_t bh, int64_t units_cap) {
 bool order_by_work(const hkv::DecodeParams& p, const std::vector<int64_t>& units, int64_t per, uint16_t* order) {
   const int B = static_cast<int>(units.size());
   // entries are (sequence << 7 | part) in 16 bits
-  if (static_cast<int64_t>(B) * p.nparts > hkv::kOrderTableMax || B > 511 || p.nparts > 128) return false;
+  const int parts = hkv::grid_parts(p);
+  if (static_cast<int64_t>(B) * parts > hkv::kOrderTableMax || B > 511 || parts > 128) return false;
   std::vector<std::pair<int64_t, int>> v;
   v.reserve(static_cast<size_t>(B) * p.nsplit);
   for (int b = 0; b < B; ++b)
@@ -215,7 +216,7 @@ bool order_by_work(const hkv::DecodeParams& p, const std::vector<int64_t>& units
   size_t i = 0;
   for (size_t k = 0; k < at; ++k) order[i++] = static_cast<uint16_t>(v[k].second);
   for (int b = 0; b < B; ++b)
-    for (int s = p.nsplit; s < p.nparts; ++s) order[i++] = static_cast<uint16_t>((b << 7) | s);
+    for (int s = p.nsplit; s < parts; ++s) order[i++] = static_cast<uint16_t>((b << 7) | s);
   for (size_t k = at; k < v.size(); ++k) order[i++] = static_cast<uint16_t>(v[k].second);
   return true;
 }
@@ -398,7 +399,7 @@ hkv_status decode_impl(hkv_ctx* h, const hkv_cache_desc* c, const void* q, int n
     if (e != hipSuccess) return hip_status(e, "hkv_decode_attn_noalloc scratch set-up");
   }
 
-  hkv::DecodeParams p;
+  hkv::DecodeParams p{};
   p.c = view_of(h, c);
   p.stamps = h->stamps;
   p.stamp_wgs = static_cast<int>(std::min<size_t>(h->stamp_wgs, INT32_MAX));
@@ -417,12 +418,12 @@ hkv_status decode_impl(hkv_ctx* h, const hkv_cache_desc* c, const void* q, int n
   p.units_per_split = sp.per_split;
   p.wg_order = sp.wg_order;
   p.work = (!sel_idx && sp.claim) ? claim_counters(workspace, c, h->H) : nullptr;
+  p.k_new = p.v_new = nullptr;  // (before the order table: it counts the workgroups from them)
   const bool ordered = !sel_idx && sp.batch && order_by_work(p, units, sp.per_split, order);
   if (ordered) p.wg_order = hkv::kOrderTable;
   p.qscale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(h->D)));
   p.out = static_cast<_Float16*>(out);
   p.lse = lse;
-  p.k_new = p.v_new = nullptr;
   p.seq_counters = nullptr;
   p.store_units_base = nullptr;
   p.store_scales = nullptr;
@@ -562,7 +563,7 @@ hkv_status hkv_append(hkv_handle h, const hkv_cache_desc* c, const void* k_new, 
       h->pending.reserve(h->pending.size() + 2 * chunks);
       h->free_events.reserve(h->free_events.size() + 2 * chunks);
     }
-    hkv::AppendParams p;
+    hkv::AppendParams p{};
     std::memset(&p, 0, sizeof(p));
     p.c = view_of(h, c);
     p.k_new = static_cast<const _Float16*>(k_new);
@@ -648,7 +649,7 @@ hkv_status hkv_append_decode(hkv_handle h, const hkv_cache_desc* c, const void* 
         reinterpret_cast<uintptr_t>(k_new) % 16 != 0 || reinterpret_cast<uintptr_t>(v_new) % 16 != 0)
       return HKV_ERR_ALIGNMENT;
 
-    hkv::DecodeParams p;
+    hkv::DecodeParams p{};
     p.c = view_of(h, c);
     p.stamps = h->stamps;
     p.stamp_wgs = static_cast<int>(std::min<size_t>(h->stamp_wgs, INT32_MAX));
@@ -661,20 +662,20 @@ hkv_status hkv_append_decode(hkv_handle h, const hkv_cache_desc* c, const void* 
     p.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(counters_bytes(c, h->H), 256));
     const SplitPlan sp = h->force_splits > 0 ? forced_plan(units_max, h->force_splits)
                                              : stats_plan(c, dense_plan(h, static_cast<int64_t>(c->batch) * h->H, units_max,
-                                                                        units_sum(units) * h->H, 2), units_max);
+                                                                        units_sum(units) * h->H, 1), units_max);
     p.nsplit = sp.nsplit;
     p.nparts = sp.nsplit + 2;
     p.units_per_split = sp.per_split;
     p.wg_order = sp.wg_order;
     p.work = sp.claim ? claim_counters(workspace, c, h->H) : nullptr;
+    p.k_new = static_cast<const _Float16*>(k_new);  // (before the order table: it counts the workgroups from them)
+    p.v_new = static_cast<const _Float16*>(v_new);
     uint16_t order[hkv::kOrderTableMax];
     const bool ordered = sp.batch && order_by_work(p, units, sp.per_split, order);
     if (ordered) p.wg_order = hkv::kOrderTable;
     p.qscale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(h->D)));
     p.out = static_cast<_Float16*>(out);
     p.lse = lse;
-    p.k_new = static_cast<const _Float16*>(k_new);
-    p.v_new = static_cast<const _Float16*>(v_new);
     p.store_units_base = nullptr;
     p.store_scales = nullptr;
     p.store_counts = nullptr;
@@ -710,7 +711,7 @@ hkv_status hkv_sparse_compact(hkv_handle h, const hkv_cache_desc* c, const int32
       h->pending.reserve(h->pending.size() + 1);
       h->free_events.reserve(h->free_events.size() + 2);
     }
-    hkv::CompactParams p;
+    hkv::CompactParams p{};
     p.c = view_of(h, c);
     p.sel = sel_idx;
     p.k_sel = k_sel;
@@ -748,7 +749,7 @@ hkv_status hkv_decode_attn_compact(hkv_handle h, const hkv_cache_desc* c, const 
       h->free_events.reserve(h->free_events.size() + 2);
     }
     const StoreLayout l = store_layout(h, c->batch, k_sel);
-    hkv::DecodeParams p;
+    hkv::DecodeParams p{};
     p.c = view_of(h, c);
     p.stamps = h->stamps;
     p.stamp_wgs = static_cast<int>(std::min<size_t>(h->stamp_wgs, INT32_MAX));
@@ -798,7 +799,7 @@ hkv_status hkv_topk_select(hkv_handle h, const hkv_cache_desc* c, const void* q,
     for (int b = 0; b < c->batch; ++b) blk_max = std::max(blk_max, cold_blocks(c->seq_len_host[b], h->T, h->S));
 
     const TopkLayout tl = topk_layout(h, c);
-    hkv::TopkParams p;
+    hkv::TopkParams p{};
     p.c = view_of(h, c);
     p.G = G;
     p.q = static_cast<const _Float16*>(q);

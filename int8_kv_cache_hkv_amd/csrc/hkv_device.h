@@ -84,6 +84,21 @@ __device__ __forceinline__ uint4 load_stream_buf(__amdgpu_buffer_rsrc_t r, uint3
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Largest |x| over the fp16 values of a row slice (finite values, as the cache holds): for
+// non-negative fp16 values the order of the bit patterns as unsigned integers is the numeric order, so
+// the largest magnitude is the packed unsigned 16-bit maximum of the patterns with the sign bit
+// cleared, two values per operation.
+template <int NV>
+__device__ __forceinline__ float slice_absmax(const u32x4_t (&x)[NV]) {
+  typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+  u16x2_t m = {0, 0};
+#pragma unroll
+  for (int v = 0; v < NV; ++v)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, x[v][i] & 0x7fff7fffu));
+  return half_lo(m.x > m.y ? m.x : m.y);
+}
+
 // Reciprocal of a block scale for the coding helpers below: fl32(1 / s), the correctly rounded IEEE
 // division (once per block), or 0 for s = 0 (every value of such a block is 0, and so is its code).
 __device__ __forceinline__ float quant_recip(float s) { return s > 0.f ? 1.f / s : 0.f; }

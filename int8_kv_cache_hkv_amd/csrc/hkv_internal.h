@@ -72,6 +72,7 @@ struct DecodeParams {
   unsigned* counters;      // [B*H] arrival counters, zero between calls
   int nsplit;              // cold splits per (sequence, kv-head)
   int nparts;              // partial records per (sequence, kv-head): nsplit + 1 (hot zone), + 1 more fused
+                           // (the fused append's workgroup writes the last two: see grid_parts)
   int units_per_split;     // units handled per split (multiple of kWaves)
   int wg_order;            // kOrderPlain / kOrderSplitMajor / kOrderTable (see wg_coord)
   unsigned* work;          // [B*H][kClaimStride] unit-claim counters (dense walk), zero between calls; nullptr: static
@@ -104,8 +105,12 @@ struct CompactParams {
   int8_t* units_base;      // [B*H][units][2][tile bytes]
 };
 
+// Workgroups per (sequence, kv-head) of a decode launch: one per partial record, except that a fused
+// append + decode's last workgroup attends the hot window and the tail block, two records.
+__host__ __device__ inline int grid_parts(const DecodeParams& p) { return p.nparts - (p.k_new ? 1 : 0); }
+
 // Arguments of the table-ordered decode launch (batch plans): the (sequence << 7 | part) groups
-// of the grid in dispatch order, [B * nparts] entries used.
+// of the grid in dispatch order, [B * grid_parts] entries used.
 struct DecodeParamsOrdered {
   DecodeParams p;
   uint16_t order[kOrderTableMax];
