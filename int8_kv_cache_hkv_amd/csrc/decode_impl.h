@@ -61,8 +61,6 @@ constexpr int kModeGather = 1;  // selected tokens gathered from their blocks (s
 constexpr int kModeStore = 2;   // units of a compacted sparse store
 constexpr int kHotChunk = 32;         // hot-zone slots staged through LDS at a time
 constexpr int kMergeChunk = 16;       // partials whose loads are in flight together in the merge
-constexpr int kHoldUnits = 8;         // splits of at most this many units hold their first tiles ...
-constexpr uint64_t kHoldTicks = 100;  // ... until this many s_memrealtime ticks (100 MHz) after start
 
 template <int D, int G>
 struct Cfg {
@@ -179,19 +177,24 @@ __device__ __forceinline__ void softmax_unit(WaveState<D, G>& st, DecodeSmem<D, 
   wave_lds_sync();
 }
 
-// PV products of four tokens t0..t0+3 into the block accumulators: bv[ps] is the exact value
-// operand (the four tokens' values at channel 64 ps + lane).
+// The weights (hi and lo halves) of tokens t0 .. t0 + 3 for every query quad, from wave w's rows.
 template <int D, int G>
-__device__ __forceinline__ void pv_step(BlockAcc<D, G>& blk, const DecodeSmem<D, G>& sm,
-                                        const half4_t (&bv)[Cfg<D, G>::NDL], int t0, int w, int lane) {
+__device__ __forceinline__ void pv_weights(const DecodeSmem<D, G>& sm, int t0, int w, int lane,
+                                           half4_t (&ph)[Cfg<D, G>::NQ], half4_t (&pl)[Cfg<D, G>::NQ]) {
   using C = Cfg<D, G>;
-  half4_t ph[C::NQ], pl[C::NQ];
 #pragma unroll
   for (int quad = 0; quad < C::NQ; ++quad) {
     const half4_t* pr = reinterpret_cast<const half4_t*>(&sm.pw[w][quad][lane & 3][(t0 >> 2) * 8]);
     ph[quad] = pr[0];
     pl[quad] = pr[1];
   }
+}
+
+// PV products of 4 tokens: both weight halves into the same chain.
+template <int D, int G>
+__device__ __forceinline__ void pv_mfma(BlockAcc<D, G>& blk, const half4_t (&ph)[Cfg<D, G>::NQ],
+                                        const half4_t (&pl)[Cfg<D, G>::NQ], const half4_t (&bv)[Cfg<D, G>::NDL]) {
+  using C = Cfg<D, G>;
 #pragma unroll
   for (int quad = 0; quad < C::NQ; ++quad)
 #pragma unroll
@@ -200,6 +203,17 @@ __device__ __forceinline__ void pv_step(BlockAcc<D, G>& blk, const DecodeSmem<D,
   for (int quad = 0; quad < C::NQ; ++quad)
 #pragma unroll
     for (int ps = 0; ps < C::NDL; ++ps) blk.v[quad][ps] = mfma_qk(pl[quad], bv[ps], blk.v[quad][ps]);
+}
+
+// PV products of four tokens t0..t0+3 into the block accumulators: bv[ps] is the exact value
+// operand (the four tokens' values at channel 64 ps + lane).
+template <int D, int G>
+__device__ __forceinline__ void pv_step(BlockAcc<D, G>& blk, const DecodeSmem<D, G>& sm,
+                                        const half4_t (&bv)[Cfg<D, G>::NDL], int t0, int w, int lane) {
+  using C = Cfg<D, G>;
+  half4_t ph[C::NQ], pl[C::NQ];
+  pv_weights<D, G>(sm, t0, w, lane, ph, pl);
+  pv_mfma<D, G>(blk, ph, pl, bv);
 }
 
 template <int D, int G>
@@ -227,28 +241,52 @@ __device__ __forceinline__ void fold_block(WaveState<D, G>& st, const BlockAcc<D
       }
 }
 
+// The query operands of K chunk ch (kSteps MFMA steps) for every query quad.
+template <int D, int G, int BITS>
+__device__ __forceinline__ void q_chunk(const DecodeSmem<D, G>& sm, int lane, int ch,
+                                        half4_t (&q)[Fmt<BITS>::kSteps][Cfg<D, G>::NQ]) {
+  using C = Cfg<D, G>;
+  using F = Fmt<BITS>;
+#pragma unroll
+  for (int st = 0; st < F::kSteps; ++st)
+#pragma unroll
+    for (int quad = 0; quad < C::NQ; ++quad) q[st][quad] = q_operand(sm, quad, lane, ch * F::kElems + st * 4);
+}
+
 // Logit sums of the lane's K row (D/E chunks of E elements, biased operands) for every query row.
+// The query operands of the next chunk are read from LDS while this chunk's MFMAs run (a read
+// issued right before its MFMA leaves the LDS latency exposed at one wave per SIMD).
 template <int D, int G, int BITS>
 __device__ __forceinline__ void qk_codes(const uint4 (&kr)[D / Fmt<BITS>::kElems], const DecodeSmem<D, G>& sm,
                                          int lane, float4_t (&s)[Cfg<D, G>::NQ]) {
   using C = Cfg<D, G>;
   using F = Fmt<BITS>;
+  constexpr int NCH = D / F::kElems;
   asm volatile("" ::: "memory");  // re-read the query operand from LDS for every unit
   float4_t s2[C::NQ];  // second accumulator chain: halves the dependent MFMA chain
 #pragma unroll
   for (int quad = 0; quad < C::NQ; ++quad) s[quad] = s2[quad] = float4_t{0.f, 0.f, 0.f, 0.f};
+  half4_t qc[F::kSteps][C::NQ];
+  q_chunk<D, G, BITS>(sm, lane, 0, qc);
 #pragma unroll
-  for (int ch = 0; ch < D / F::kElems; ++ch) {
+  for (int ch = 0; ch < NCH; ++ch) {
     asm volatile("" ::: "memory");  // bound how far the query-operand LDS reads are hoisted
+    half4_t qn[F::kSteps][C::NQ];
+    if (ch + 1 < NCH) q_chunk<D, G, BITS>(sm, lane, ch + 1, qn);
 #pragma unroll
     for (int st = 0; st < F::kSteps; ++st) {
       const half4_t b = chunk_operand<BITS, F::kBiasedQK>(kr[ch], st);
-      const int k0 = ch * F::kElems + st * 4;
 #pragma unroll
       for (int quad = 0; quad < C::NQ; ++quad) {
-        if (st & 1) s2[quad] = mfma_qk(q_operand(sm, quad, lane, k0), b, s2[quad]);
-        else s[quad] = mfma_qk(q_operand(sm, quad, lane, k0), b, s[quad]);
+        if (st & 1) s2[quad] = mfma_qk(qc[st][quad], b, s2[quad]);
+        else s[quad] = mfma_qk(qc[st][quad], b, s[quad]);
       }
+    }
+    if (ch + 1 < NCH) {
+#pragma unroll
+      for (int st = 0; st < F::kSteps; ++st)
+#pragma unroll
+        for (int quad = 0; quad < C::NQ; ++quad) qc[st][quad] = qn[st][quad];
     }
   }
 #pragma unroll
@@ -267,25 +305,35 @@ __device__ __forceinline__ void qk_codes_refill(uint4 (&kr)[D / Fmt<BITS>::kElem
   using C = Cfg<D, G>;
   using F = Fmt<BITS>;
   constexpr int S = kBlockSize;
+  constexpr int NCH = D / F::kElems;
   const uint32_t lo = static_cast<uint32_t>(lane) * 16u;
   asm volatile("" ::: "memory");
   float4_t s2[C::NQ];
 #pragma unroll
   for (int quad = 0; quad < C::NQ; ++quad) s[quad] = s2[quad] = float4_t{0.f, 0.f, 0.f, 0.f};
+  half4_t qc[F::kSteps][C::NQ];  // this chunk's query operands; the next chunk's are read meanwhile
+  q_chunk<D, G, BITS>(sm, lane, 0, qc);
 #pragma unroll
-  for (int ch = 0; ch < D / F::kElems; ++ch) {
+  for (int ch = 0; ch < NCH; ++ch) {
     asm volatile("" ::: "memory");
+    half4_t qn[F::kSteps][C::NQ];
+    if (ch + 1 < NCH) q_chunk<D, G, BITS>(sm, lane, ch + 1, qn);
 #pragma unroll
     for (int st = 0; st < F::kSteps; ++st) {
       const half4_t b = chunk_operand<BITS, F::kBiasedQK>(kr[ch], st);
-      const int k0 = ch * F::kElems + st * 4;
 #pragma unroll
       for (int quad = 0; quad < C::NQ; ++quad) {
-        if (st & 1) s2[quad] = mfma_qk(q_operand(sm, quad, lane, k0), b, s2[quad]);
-        else s[quad] = mfma_qk(q_operand(sm, quad, lane, k0), b, s[quad]);
+        if (st & 1) s2[quad] = mfma_qk(qc[st][quad], b, s2[quad]);
+        else s[quad] = mfma_qk(qc[st][quad], b, s[quad]);
       }
     }
     kr[ch] = load_stream_buf(rn, lo + ch * S * 16);
+    if (ch + 1 < NCH) {
+#pragma unroll
+      for (int st = 0; st < F::kSteps; ++st)
+#pragma unroll
+        for (int quad = 0; quad < C::NQ; ++quad) qc[st][quad] = qn[st][quad];
+    }
   }
 #pragma unroll
   for (int quad = 0; quad < C::NQ; ++quad) s[quad] += s2[quad];
@@ -306,13 +354,24 @@ __device__ __forceinline__ void pv_dense_refill(BlockAcc<D, G>& blk, const Decod
   constexpr int TB = F::template tile_bytes<D>();
   const uint32_t lo = static_cast<uint32_t>(lane) * 16u;
   zero_blk<D, G>(blk);
+  half4_t ph[C::NQ], pl[C::NQ];  // this step's weights; the next step's are read meanwhile
+  pv_weights<D, G>(sm, 0, w, lane, ph, pl);
 #pragma unroll
   for (int t0 = 0; t0 < S; t0 += 4) {
     asm volatile("" ::: "memory");
+    half4_t nh[C::NQ], nl[C::NQ];
+    if (t0 + 4 < S) pv_weights<D, G>(sm, t0 + 4, w, lane, nh, nl);
     half4_t bv[C::NDL];
 #pragma unroll
     for (int ps = 0; ps < C::NDL; ++ps) bv[ps] = chunk_operand<BITS, false>(vr[ps][t0 / E], (t0 % E) / 4);
-    pv_step<D, G>(blk, sm, bv, t0, w, lane);
+    pv_mfma<D, G>(blk, ph, pl, bv);
+    if (t0 + 4 < S) {
+#pragma unroll
+      for (int quad = 0; quad < C::NQ; ++quad) {
+        ph[quad] = nh[quad];
+        pl[quad] = nl[quad];
+      }
+    }
     if (t0 % E == E - 4) {
 #pragma unroll
       for (int ps = 0; ps < C::NDL; ++ps)
@@ -767,17 +826,8 @@ __device__ __forceinline__ void cold_split(const DecodeParams& p, DecodeSmem<D, 
     issue_k<D, BITS>(t0, r0, lane);
     issue_v<D, BITS>(t0, sc0, r0, scales_rsrc(c), phys0, c.H, h, lane);
   } else {
-    const uint64_t t_entry = __builtin_amdgcn_s_memrealtime();
     hb = header_batch(c, b, 0, split, p.nsplit, p.units_per_split, w, lane);
     phys0 = __builtin_amdgcn_readlane(hb, 0);
-    // latency-bound launches (a few units per split): the first tiles wait until about 1 us after
-    // this workgroup started, so the workgroups that start later get their query and header loads
-    // through before the tile traffic of the early ones fills the memory queues (llama8b step
-    // 16.2 -> 15.3 us; the wait is bounded by the clock, 100 MHz)
-    if (p.units_per_split <= kHoldUnits) {
-      const uint64_t until = t_entry + kHoldTicks;
-      while (__builtin_amdgcn_s_memrealtime() < until) __builtin_amdgcn_s_sleep(1);
-    }
     const __amdgpu_buffer_rsrc_t r0 = tile_rsrc<D, BITS>(c, phys0, h);
     issue_k<D, BITS>(t0, r0, lane);
     issue_v<D, BITS>(t0, sc0, r0, scales_rsrc(c), phys0, c.H, h, lane);
@@ -1403,13 +1453,14 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
 }
 
 // One launch per decode call: (nsplit + 1) x H x B workgroups; for each (sequence,
-// kv-head) nsplit cold splits and one hot split write partials, and the last
-// of them to arrive merges all nsplit + 1 partials with the log-sum-exp rule
-// (M = max m_s, L = sum e^(m_s - M) l_s, out = sum e^(m_s - M) acc_s / L) and
-// writes the fp16 output.  Arrival is counted with a device-scope atomic in
-// the workspace, which the merging workgroup resets to zero.  The merge runs
-// online over groups of kMergeChunk partials whose loads are all in flight
-// together; thread i owns two adjacent output columns of one query head.
+// kv-head) nsplit cold splits and one hot split (for a fused append, one workgroup with the hot
+// window's and the tail block's records) write partial records, and the last of them to arrive
+// merges all of them with the log-sum-exp rule (M = max m_s, L = sum e^(m_s - M) l_s,
+// out = sum e^(m_s - M) acc_s / L) and writes the fp16 output.  Arrival is counted with a
+// device-scope atomic in the workspace after the workgroup's record stores are complete; the
+// merging workgroup resets it to zero.  The merge runs online over groups of kMergeChunk partials
+// whose loads are all in flight together; thread i owns two adjacent output columns of one query
+// head.
 template <int D, int G, int BITS, int MODE, bool FUSED, bool CLAIM, bool STATS>
 __device__ __forceinline__ void decode_body(const DecodeParams& p, const WgCoord wg) {
   using AppendPart = typename std::conditional<FUSED, AppendSmem<D, G, BITS>, DecodeSmem<D, G>>::type;

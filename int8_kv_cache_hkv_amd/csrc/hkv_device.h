@@ -256,18 +256,39 @@ __device__ __forceinline__ float readlane_f(float x, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }
 
-// Max over the 64 lanes, wave-uniform result: DPP inside rows of 16 lanes, then
-// the four row results are read as scalars (no LDS round trip).
+// One step of a wave maximum: x = max(x, x of the lane the DPP control names), a single v_max_f32
+// with a DPP source (through a DPP move, fmaxf costs the move, a NaN-canonicalising max and the
+// max).  The s_nop gives the two wait states a DPP read needs after a VALU write of its source.
+// Rows outside the row mask keep x.  For the values maximised here (never a signalling NaN) this is
+// fmaxf.
+#define HKV_MAX_DPP_STEP(name, ctrl)                                                     \
+  __device__ __forceinline__ float name(float x) {                                       \
+    asm("s_nop 1\n\tv_max_f32_dpp %0, %0, %0 " ctrl : "+v"(x));                         \
+    return x;                                                                            \
+  }
+HKV_MAX_DPP_STEP(max_dpp_quad_swap1, "quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf")
+HKV_MAX_DPP_STEP(max_dpp_quad_swap2, "quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf")
+HKV_MAX_DPP_STEP(max_dpp_half_mirror, "row_half_mirror row_mask:0xf bank_mask:0xf")
+HKV_MAX_DPP_STEP(max_dpp_mirror, "row_mirror row_mask:0xf bank_mask:0xf")
+HKV_MAX_DPP_STEP(max_dpp_bcast15, "row_bcast:15 row_mask:0xa bank_mask:0xf")
+HKV_MAX_DPP_STEP(max_dpp_bcast31, "row_bcast:31 row_mask:0xc bank_mask:0xf")
+#undef HKV_MAX_DPP_STEP
+
+// Max over the 64 lanes, wave-uniform result: inside rows of 16 lanes by quad swaps and row
+// mirrors, then row 1 takes row 0's and row 3 row 2's (row_bcast:15), row 3 takes row 1's
+// (row_bcast:31), and lane 63 holds the maximum.
 __device__ __forceinline__ float wave_max_dpp(float x) {
-  x = fmaxf(x, dpp_mov<0xB1>(x));    // quad_perm [1,0,3,2]
-  x = fmaxf(x, dpp_mov<0x4E>(x));    // quad_perm [2,3,0,1]
-  x = fmaxf(x, dpp_mov<0x141>(x));   // row_half_mirror
-  x = fmaxf(x, dpp_mov<0x140>(x));   // row_mirror
-  return fmaxf(fmaxf(readlane_f(x, 0), readlane_f(x, 16)), fmaxf(readlane_f(x, 32), readlane_f(x, 48)));
+  x = max_dpp_quad_swap1(x);
+  x = max_dpp_quad_swap2(x);
+  x = max_dpp_half_mirror(x);
+  x = max_dpp_mirror(x);
+  x = max_dpp_bcast15(x);
+  x = max_dpp_bcast31(x);
+  return readlane_f(x, 63);
 }
 
-// Sum over the 64 lanes, wave-uniform result (same pattern as wave_max_dpp;
-// fixed order, so deterministic).
+// Sum over the 64 lanes, wave-uniform result: DPP inside rows of 16 lanes, then the four row
+// sums read as scalars and added in a fixed order (deterministic).
 __device__ __forceinline__ float wave_sum_dpp(float x) {
   x += dpp_mov<0xB1>(x);
   x += dpp_mov<0x4E>(x);
