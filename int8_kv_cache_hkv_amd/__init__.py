@@ -398,9 +398,9 @@ class HybridKVCache:
         return n * 2 if self.quant_bits == 0 else n * self.quant_bits // 8
 
     def _unpack(self, raw: np.ndarray) -> np.ndarray:
-        """Tile bytes [..., TB] -> elements in chunk order [..., S*D]: int8 codes, or fp16 values."""
+        """Tile bytes [..., TB] -> elements in chunk order [..., S*D]: codes (int8), or fp16 values."""
         if self.quant_bits == 8:
-            return raw.view(np.int8)
+            return (raw.view(np.uint8) ^ 0x80).view(np.int8)  # offset binary: byte = code + 128
         if self.quant_bits == 0:
             return raw.view(np.float16)
         u = raw.view(np.uint8)

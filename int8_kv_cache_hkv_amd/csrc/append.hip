@@ -487,12 +487,15 @@ __global__ __launch_bounds__(kThreads) void append_step_kernel(AppendParams p) {
 #pragma unroll
             for (int ch = 0; ch < CPT / 16; ++ch) {
               const int dc = (part * CPT) / 16 + ch;
-              reinterpret_cast<uint4*>(tile)[dc * S + t] = make_uint4(qw[4 * ch], qw[4 * ch + 1], qw[4 * ch + 2], qw[4 * ch + 3]);
+              reinterpret_cast<uint4*>(tile)[dc * S + t] =  // stored offset binary
+                  make_uint4(qw[4 * ch] ^ kCodeOffsetWord, qw[4 * ch + 1] ^ kCodeOffsetWord,
+                             qw[4 * ch + 2] ^ kCodeOffsetWord, qw[4 * ch + 3] ^ kCodeOffsetWord);
             }
           } else {
 #pragma unroll
             for (int i = 0; i < CPT; ++i)
-              tile[((t / 16) * D + part * CPT + i) * 16 + (t % 16)] = static_cast<int8_t>(qw[i / 4] >> (8 * (i % 4)));
+              tile[((t / 16) * D + part * CPT + i) * 16 + (t % 16)] =
+                  static_cast<int8_t>((qw[i / 4] >> (8 * (i % 4))) ^ 0x80u);
           }
         }
         continue;

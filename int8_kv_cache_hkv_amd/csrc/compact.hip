@@ -48,9 +48,10 @@ __device__ __forceinline__ int wg_exclusive_scan(int v, int* wsum, int* total) {
   return before + x - v;
 }
 
-// Stored value element of a row past the count: code 0 (8-bit 0x00, 4-bit offset binary 0x8), fp16 0.
+// Stored value element of a row past the count: code 0 (8-bit offset binary 0x80, 4-bit offset
+// binary 0x8), fp16 0.
 template <int BITS>
-constexpr uint32_t zero_elem() { return BITS == 4 ? 8u : 0u; }
+constexpr uint32_t zero_elem() { return BITS == 8 ? 0x80u : BITS == 4 ? 8u : 0u; }
 
 template <int D, int BITS>
 __global__ __launch_bounds__(kCompactThreads) void sparse_compact_kernel(CompactParams p) {
@@ -121,8 +122,8 @@ __global__ __launch_bounds__(kCompactThreads) void sparse_compact_kernel(Compact
       const int8_t* src = c.cold + tile_offset(ph, h, 0, H, TB);
       v = reinterpret_cast<const uint4*>(src)[kc * S + src_row[r]];
     } else {
-      const uint32_t z = zero_elem<BITS>() * 0x11111111u;
-      v = BITS == 4 ? make_uint4(z, z, z, z) : make_uint4(0u, 0u, 0u, 0u);
+      const uint32_t z = BITS == 8 ? 0x80808080u : zero_elem<BITS>() * 0x11111111u;
+      v = make_uint4(z, z, z, z);
     }
     reinterpret_cast<uint4*>(dst)[vi] = v;
   }

@@ -1283,11 +1283,13 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
 #pragma unroll
             for (int ch = 0; ch < CPT / 16; ++ch)
               reinterpret_cast<uint4*>(tile)[((part * CPT) / 16 + ch) * S + t] =
-                  make_uint4(qw[4 * ch], qw[4 * ch + 1], qw[4 * ch + 2], qw[4 * ch + 3]);
+                  make_uint4(qw[4 * ch] ^ kCodeOffsetWord, qw[4 * ch + 1] ^ kCodeOffsetWord,
+                             qw[4 * ch + 2] ^ kCodeOffsetWord, qw[4 * ch + 3] ^ kCodeOffsetWord);
           } else {
 #pragma unroll
             for (int i = 0; i < CPT; ++i)
-              tile[((t / 16) * D + part * CPT + i) * 16 + (t % 16)] = static_cast<int8_t>(qw[i / 4] >> (8 * (i % 4)));
+              tile[((t / 16) * D + part * CPT + i) * 16 + (t % 16)] =
+                  static_cast<int8_t>((qw[i / 4] >> (8 * (i % 4))) ^ 0x80u);
           }
         }
       }

@@ -297,11 +297,14 @@ __device__ __forceinline__ float wave_sum_dpp(float x) {
   return (readlane_f(x, 0) + readlane_f(x, 16)) + (readlane_f(x, 32) + readlane_f(x, 48));
 }
 
-// Four signed int8 codes (one word) to four exact fp16 values: bias the bytes to
-// c + 128, place each under the fp16 exponent of 1024 (0x64xx = 1024 + byte),
-// subtract 1152.  Every step is exact.
-__device__ __forceinline__ half4_t codes_to_half4(uint32_t w) {
-  const uint32_t u = w ^ 0x80808080u;
+// 8-bit codes are stored offset binary: byte = code + 128 (code -127..127 is stored 1..255,
+// code 0 as 0x80), so a byte placed under the fp16 exponent of 1024 is the exact value
+// code + 1152 with no work on the byte itself.
+constexpr uint32_t kCodeOffsetWord = 0x80808080u;  // the offset of four code bytes (an exclusive or)
+
+// Four stored 8-bit codes (one word) to four exact fp16 values: each byte under the fp16
+// exponent of 1024 (0x64xx = 1024 + byte = code + 1152), minus 1152.  Every step is exact.
+__device__ __forceinline__ half4_t codes_to_half4(uint32_t u) {
   const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
   const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
   const half2_t off = {static_cast<_Float16>(1152.0f), static_cast<_Float16>(1152.0f)};
@@ -310,11 +313,10 @@ __device__ __forceinline__ half4_t codes_to_half4(uint32_t w) {
   return half4_t{a.x, a.y, b.x, b.y};
 }
 
-// Four signed int8 codes (one word) to the four exact fp16 values code + 1152:
-// the same byte placement as codes_to_half4 without the final subtraction.
-// Callers remove the 1152 offset from the finished dot products.
-__device__ __forceinline__ half4_t codes_to_biased_half4(uint32_t w) {
-  const uint32_t u = w ^ 0x80808080u;
+// Four stored 8-bit codes (one word) to the four exact fp16 values code + 1152: the same byte
+// placement as codes_to_half4 without the final subtraction.  Callers remove the 1152 offset from
+// the finished dot products.
+__device__ __forceinline__ half4_t codes_to_biased_half4(uint32_t u) {
   const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
   const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
   const half2_t a = __builtin_bit_cast(half2_t, lo);
@@ -403,6 +405,9 @@ __device__ __forceinline__ uint4 chunk_from_stage(const int8_t* src) {
     const uint4 a = *reinterpret_cast<const uint4*>(src);
     const uint4 b = *reinterpret_cast<const uint4*>(src + 16);
     return make_uint4(pack_nib8(a.x, a.y), pack_nib8(a.z, a.w), pack_nib8(b.x, b.y), pack_nib8(b.z, b.w));
+  } else if constexpr (BITS == 8) {  // signed stage codes to the stored offset-binary bytes
+    const uint4 a = *reinterpret_cast<const uint4*>(src);
+    return make_uint4(a.x ^ kCodeOffsetWord, a.y ^ kCodeOffsetWord, a.z ^ kCodeOffsetWord, a.w ^ kCodeOffsetWord);
   } else {
     return *reinterpret_cast<const uint4*>(src);
   }

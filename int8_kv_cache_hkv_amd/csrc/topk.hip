@@ -62,7 +62,7 @@ __device__ __forceinline__ float window_scores(uint4 (&kr)[D / Fmt<BITS>::kElems
     for (int st = 0; st < F::kSteps; ++st) {
       bk[st] = chunk_operand<BITS, false>(kr[ch], st);
       if constexpr (BITS == 8) {
-        const uint32_t word = word_of(kr[ch], st);
+        const uint32_t word = word_of(kr[ch], st) ^ kCodeOffsetWord;  // stored offset binary -> signed codes
         n2 = __builtin_amdgcn_sdot4(static_cast<int>(word), static_cast<int>(word), n2, false);
       } else {
         const half2_t a = {bk[st].x, bk[st].y}, b = {bk[st].z, bk[st].w};
