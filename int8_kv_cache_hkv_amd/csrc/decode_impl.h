@@ -527,7 +527,8 @@ __device__ __forceinline__ void dense_units(WaveState<D, G>& st, DecodeSmem<D, G
 // (memory bandwidth is not shared evenly between workgroups), so after its
 // first unit (split * 4 + w, static: the first memory round needs no claim)
 // each wave claims units from the (sequence, kv-head) counter: unit =
-// nsplit * 4 + claim, until a claim lands past the last unit.  Every unit is
+// base + claim (base = 4 x the splits of this (sequence, kv-head), past every
+// static first unit), until a claim lands past the last unit.  Every unit is
 // claimed exactly once and computed by the wave that claimed it.  Claims run
 // two units ahead: while unit u is computed, the tiles of the next unit are
 // requested (as in the static walk), and the claim for the unit after it is
@@ -537,12 +538,11 @@ __device__ __forceinline__ void dense_units(WaveState<D, G>& st, DecodeSmem<D, G
 // the unit after it (valid when un >= 0).
 template <int D, int G, int BITS>
 __device__ __forceinline__ void dense_units_claim(WaveState<D, G>& st, DecodeSmem<D, G>& sm, const DecodeParams& p, int b, int h,
-                                  int bh, int units, int n_cold, int w, int lane, Tiles<D, BITS>& t, int u, int phys_u,
-                                  float2 sc, int un, int hn, unsigned cl) {
+                                  int bh, int units, int base, int n_cold, int w, int lane, Tiles<D, BITS>& t, int u,
+                                  int phys_u, float2 sc, int un, int hn, unsigned cl) {
   using C = Cfg<D, G>;
   constexpr int S = kBlockSize;
   const CacheView& c = p.c;
-  const int base = p.nsplit * kWaves;
   unsigned* work = p.work + static_cast<size_t>(bh) * kClaimStride;
   const __amdgpu_buffer_rsrc_t rs = scales_rsrc(c);
   int phys_n = un >= 0 ? header_phys(c, hn) : -1;
@@ -774,6 +774,23 @@ __device__ __forceinline__ void copy_query(const _Float16* qg, _Float16 (*qh)[4]
   }
 }
 
+// Units one (sequence, kv-head) attends in its cold splits: stored units (compacted store), sparse
+// units of the selection, or cold blocks (the fused step: the full blocks before the tail block).
+template <int MODE, bool FUSED>
+__device__ __forceinline__ int pair_units(const DecodeParams& p, int n_seq, int store_count) {
+  const SeqGeom sg = seq_geom(n_seq, p.c.T, kBlockSize);
+  // (a store holds at most store_units units per (sequence, kv-head): a count from a store built for
+  // another width never walks past it)
+  if (MODE == kModeStore) return min(cdiv(max(store_count, 0), kBlockSize), p.store_units);
+  if (sg.n_cold <= 0) return 0;
+  return MODE == kModeGather ? cdiv(p.k_sel, kSparseUnit) : (FUSED ? sg.n_cold / kBlockSize : sg.n_blk);
+}
+
+// Cold splits taking part for a (sequence, kv-head) of `units` units (see table_splits).
+__device__ __forceinline__ int splits_of_pair(const DecodeParams& p, int units) {
+  return p.wg_order == kOrderTable ? table_splits(p.nsplit, p.units_per_split, units) : p.nsplit;
+}
+
 // ---- cold split: stream its units, merge the 4 waves, write the partial
 template <int D, int G, int BITS, int MODE, bool FUSED, bool CLAIM, bool STATS>
 __device__ __forceinline__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, int h, int bh, int split) {
@@ -843,10 +860,7 @@ __device__ __forceinline__ void cold_split(const DecodeParams& p, DecodeSmem<D, 
   // fused append: only the full blocks before the one the appended token spills into (n_cold is
   // the count before the append, so the block holding cold token n_cold is excluded)
   const int store_count = MODE == kModeStore ? __builtin_amdgcn_readfirstlane(count_lane) : 0;
-  // (a store holds at most store_units units per (sequence, kv-head): a count from a store built for
-  // another width never walks past it)
-  const int units = MODE == kModeStore ? min(cdiv(max(store_count, 0), S), p.store_units)
-                    : (sg.n_cold > 0 ? (SPARSE ? cdiv(p.k_sel, kSparseUnit) : (FUSED ? sg.n_cold / S : sg.n_blk)) : 0);
+  const int units = pair_units<MODE, FUSED>(p, sg.n, store_count);
 
   WaveState<D, G> st;
   st.stats = STATS;
@@ -887,8 +901,10 @@ __device__ __forceinline__ void cold_split(const DecodeParams& p, DecodeSmem<D, 
     const int u0 = split * kWaves + w;
     int un = -1, hn = -1;
     unsigned cl = 0;
-    if (u0 < units) {  // else units <= nsplit * 4: every claim lands past the last unit
-      un = p.nsplit * kWaves + static_cast<int>(__builtin_amdgcn_readfirstlane(cl0));
+    // claims start past the static first units of this (sequence, kv-head)'s splits
+    const int base = splits_of_pair(p, units) * kWaves;
+    if (u0 < units) {  // else units <= base: every claim lands past the last unit
+      un = base + static_cast<int>(__builtin_amdgcn_readfirstlane(cl0));
       if (un >= units) {
         un = -1;
       } else {
@@ -896,8 +912,8 @@ __device__ __forceinline__ void cold_split(const DecodeParams& p, DecodeSmem<D, 
         cl = claim_issue(p.work + static_cast<size_t>(bh) * kClaimStride, lane);
       }
     }
-    dense_units_claim<D, G, BITS>(st, sm, p, b, h, bh, units, sg.n_cold, w, lane, t0, u0 < units ? u0 : -1, phys0, sc0,
-                            un, hn, cl);
+    dense_units_claim<D, G, BITS>(st, sm, p, b, h, bh, units, base, sg.n_cold, w, lane, t0, u0 < units ? u0 : -1, phys0,
+                                  sc0, un, hn, cl);
   } else {
     dense_units<D, G, BITS>(st, sm, p, b, h, split, units, sg.n_cold, w, lane, t0, phys0, sc0, hb);
   }
@@ -1434,7 +1450,7 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
   }
   __syncthreads();
   if (stamp && tid == 0) {  // phase timestamps of this workgroup: hot window, codes, code stores, block attended
-    const size_t wg = static_cast<size_t>(bh) * gridDim.x + p.nsplit;
+    const size_t wg = static_cast<size_t>(bh) * grid_parts(p) + p.nsplit;
     if (wg < static_cast<size_t>(p.stamp_wgs)) {
       unsigned long long* a = p.stamps + wg * 8;
       a[4] = t_hot;
@@ -1479,7 +1495,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, const WgCoord
   const int bh = b * c.H + h;
   const int tid = threadIdx.x;
   // phase timestamps: this workgroup's 8 slots, when asked for and inside the buffer
-  const size_t stamp_wg = static_cast<size_t>(bh) * gridDim.x + split;
+  const size_t stamp_wg = static_cast<size_t>(bh) * grid_parts(p) + split;
   unsigned long long* const st = p.stamps && stamp_wg < static_cast<size_t>(p.stamp_wgs) ? p.stamps + stamp_wg * 8 : nullptr;
   const unsigned long long t_start = st ? __builtin_amdgcn_s_memrealtime() : 0ull;
   if (split < p.nsplit) {
@@ -1489,12 +1505,20 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, const WgCoord
   } else {
     hot_split<D, G>(p, sm.hot, b, h, bh);
   }
+  // this (sequence, kv-head)'s unit count, for the number of its cold splits (loaded with the wait
+  // for the partial stores)
+  const int n_seq_lane = c.seq_len[opaque_index(b)];
+  const int count_lane = MODE == kModeStore ? p.store_counts[opaque_index(bh)] : 0;
   // ---- arrival: wait until this workgroup's partial stores are complete, count, and let the
   // last workgroup merge
   __builtin_amdgcn_s_waitcnt(0);
   const unsigned long long t_done = st ? __builtin_amdgcn_s_memrealtime() : 0ull;
   __syncthreads();
-  const int NS = p.nsplit + (FUSED ? 2 : 1);  // partials of this (sequence, kv-head)
+  // partials of this (sequence, kv-head): its cold splits (records 0 .. ns_pair - 1), then the hot
+  // zone's (and the tail block's) at nsplit (, nsplit + 1)
+  const int ns_pair = splits_of_pair(p, pair_units<MODE, FUSED>(p, __builtin_amdgcn_readfirstlane(n_seq_lane),
+                                                                 __builtin_amdgcn_readfirstlane(count_lane)));
+  const int NS = ns_pair + (FUSED ? 2 : 1);
   const unsigned arrivals = FUSED && split >= p.nsplit ? 2u : 1u;  // the fused append's workgroup writes two
   if (tid == 0)
     s_last = __hip_atomic_fetch_add(&p.counters[bh], arrivals, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
@@ -1523,7 +1547,8 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, const WgCoord
 #pragma unroll
       for (int k = 0; k < kMergeChunk; ++k) {
         if (s0 + k < NS) {
-          const float* rec = base_bh + (s0 + k) * REC;
+          const int si = s0 + k < ns_pair ? s0 + k : p.nsplit + (s0 + k - ns_pair);  // record index
+          const float* rec = base_bh + si * REC;
           ml[k] = load_coherent2(rec + off_ml);
           av[k] = load_coherent2(rec + off_a);
           zz[k] = want_z ? load_coherent2(rec + off_ml + 2).x : 0.f;
@@ -1636,14 +1661,16 @@ hipError_t launch_dg(const DecodeParams& p, const LaunchCtx& ctx, const uint16_t
     return launch_k(decode_kernel<D, G, BITS, kModeDense, false, false, true>, grid, kThreads, p, ctx);
   }
   if (order && !p.sel) {
+    if (p.order_groups < 1 || p.order_groups > kOrderTableMax) return hipErrorInvalidValue;
+    const dim3 tgrid(p.c.H, p.order_groups);  // (kv-head, table group)
     DecodeParamsOrdered po;
     po.p = p;
     std::memcpy(po.order, order, sizeof(po.order));
     if (p.work)
-      return p.k_new ? launch_k(decode_kernel_ordered<D, G, BITS, true, true>, grid, kThreads, po, ctx)
-                     : launch_k(decode_kernel_ordered<D, G, BITS, false, true>, grid, kThreads, po, ctx);
-    return p.k_new ? launch_k(decode_kernel_ordered<D, G, BITS, true, false>, grid, kThreads, po, ctx)
-                   : launch_k(decode_kernel_ordered<D, G, BITS, false, false>, grid, kThreads, po, ctx);
+      return p.k_new ? launch_k(decode_kernel_ordered<D, G, BITS, true, true>, tgrid, kThreads, po, ctx)
+                     : launch_k(decode_kernel_ordered<D, G, BITS, false, true>, tgrid, kThreads, po, ctx);
+    return p.k_new ? launch_k(decode_kernel_ordered<D, G, BITS, true, false>, tgrid, kThreads, po, ctx)
+                   : launch_k(decode_kernel_ordered<D, G, BITS, false, false>, tgrid, kThreads, po, ctx);
   }
   if (p.k_new)
     return p.work ? launch_k(decode_kernel<D, G, BITS, kModeDense, true, true>, grid, kThreads, p, ctx)

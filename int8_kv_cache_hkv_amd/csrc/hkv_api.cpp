@@ -201,7 +201,10 @@ int max_splits(int64_t bh, int64_t units_cap) {
 // 192 cold groups 128 / 128 / 124 / 124 / 127 us, last 130 us; sequence order 141 us).
 // units[b]: the blocks of sequence b this launch attends.  Returns false (plain order kept) when
 // the table cannot hold the groups.
-bool order_by_work(const hkv::DecodeParams& p, const std::vector<int64_t>& units, int64_t per, uint16_t* order) {
+// Only the cold splits a sequence takes part with are listed (hkv::table_splits of its unit count;
+// the kernel derives the same count), so a sequence's merge never waits for a split that would only
+// have found its units taken.  Sets p.order_groups.
+bool order_by_work(hkv::DecodeParams& p, const std::vector<int64_t>& units, int64_t per, uint16_t* order) {
   const int B = static_cast<int>(units.size());
   // entries are (sequence << 7 | part) in 16 bits
   const int parts = hkv::grid_parts(p);
@@ -209,7 +212,7 @@ bool order_by_work(const hkv::DecodeParams& p, const std::vector<int64_t>& units
   std::vector<std::pair<int64_t, int>> v;
   v.reserve(static_cast<size_t>(B) * p.nsplit);
   for (int b = 0; b < B; ++b)
-    for (int s = 0; s < p.nsplit; ++s)
+    for (int s = 0; s < hkv::table_splits(p.nsplit, static_cast<int>(per), units[b]); ++s)
       v.push_back({-std::max<int64_t>(0, std::min<int64_t>(per, units[b] - s * per)), (b << 7) | s});
   std::stable_sort(v.begin(), v.end(), [](const auto& x, const auto& y) { return x.first < y.first; });
   const size_t at = std::min<size_t>(kTargetWorkgroups / p.c.H, v.size());
@@ -218,6 +221,7 @@ bool order_by_work(const hkv::DecodeParams& p, const std::vector<int64_t>& units
   for (int b = 0; b < B; ++b)
     for (int s = p.nsplit; s < parts; ++s) order[i++] = static_cast<uint16_t>((b << 7) | s);
   for (size_t k = at; k < v.size(); ++k) order[i++] = static_cast<uint16_t>(v[k].second);
+  p.order_groups = static_cast<int>(i);
   return true;
 }
 

@@ -234,16 +234,14 @@ __device__ __forceinline__ WgCoord wg_coord(int order) {
 }
 
 // kOrderTable (batch plans, whose grid runs in several rounds of the resident
-// slots): the grid is read as groups of the H kv-heads of one (sequence,
-// part), in the order of the host-built table `order` of (sequence << 7 |
-// part) entries, one per group.  x = part, y = kv-head, z = sequence as for
-// the other orders.
+// slots): a grid of H x groups workgroups, group g being the H kv-heads of one
+// (sequence, part) of the host-built table `order` of (sequence << 7 | part)
+// entries (only the parts that sequence takes part with).  Returns x = part,
+// y = kv-head, z = sequence as for the other orders.
 __device__ __forceinline__ WgCoord wg_coord_table(const uint16_t* order) {
-  const int X = gridDim.x, Y = gridDim.y;
-  const int lin = blockIdx.x + X * (blockIdx.y + Y * blockIdx.z);
-  const int gi = lin / Y, h = lin - gi * Y;
-  const int e = order[gi];
-  return {e & 127, h, e >> 7};
+  // grid (H, groups): the H kv-heads of group blockIdx.y are consecutive in dispatch order
+  const int e = order[blockIdx.y];
+  return {e & 127, static_cast<int>(blockIdx.x), e >> 7};
 }
 
 // ---------------------------------------------------------------- MFMA / DPP helpers

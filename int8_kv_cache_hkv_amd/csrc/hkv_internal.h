@@ -75,6 +75,7 @@ struct DecodeParams {
                            // (the fused append's workgroup writes the last two: see grid_parts)
   int units_per_split;     // units handled per split (multiple of kWaves)
   int wg_order;            // kOrderPlain / kOrderSplitMajor / kOrderTable (see wg_coord)
+  int order_groups;        // kOrderTable: (sequence, part) groups the table lists (the grid is H x groups)
   unsigned* work;          // [B*H][kClaimStride] unit-claim counters (dense walk), zero between calls; nullptr: static
   float qscale;            // log2(e) / sqrt(D)
   _Float16* out;           // [B][H*G][D]
@@ -115,6 +116,14 @@ struct DecodeParamsOrdered {
   DecodeParams p;
   uint16_t order[kOrderTableMax];
 };
+
+// Cold splits of one (sequence, kv-head) in a table-ordered launch: enough splits of units_per_split
+// units for its own unit count (at least one, at most nsplit); the host's table lists only these
+// (device and host compute it from the same unit count).  Other launches use all nsplit.
+__host__ __device__ inline int table_splits(int nsplit, int units_per_split, int64_t units) {
+  const int64_t n = (units + units_per_split - 1) / units_per_split;
+  return static_cast<int>(n < 1 ? 1 : (n > nsplit ? nsplit : n));
+}
 
 // Top-K selection (topk.hip): the score kernel keeps the kWinTop largest keys of every window and
 // their lanes; one kSelThreads-thread workgroup per row selects from those (rows of up to
