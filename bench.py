@@ -54,8 +54,8 @@ OUT_MAX_ABS, OUT_MEAN_ABS = 4e-3, 5e-4
 # hold only for the kernel sources they were taken on: reported as null once the code of those
 # sources changes (the hash skips comments and blank lines).
 COUNTER_TRAFFIC = {
-    "sources_sha256": "a18c97230365a2195c7c88d5302f234dee5dae678c1e941e513a9ebc2f16196d",
-    "bytes_per_launch": {"llama8b": 39975512, "long": 1084449038, "llama8b_b4": 23247135, "long_b4": 550054612, "llama8b_b0": 103812292, "long_b0": 2503550523, "topk": 564771334, "sparse_decode": 189752816, "store_decode": 22457822, "compact": 197184808, "ragged": 625878711},
+    "sources_sha256": "01ea170a250da02b90ed032eb1b0b85af921e76528e8f212a629c7558976e99c",
+    "bytes_per_launch": {"llama8b": 36968721, "long": 1084489402, "llama8b_b4": 20720565, "long_b4": 550181240, "llama8b_b0": 69422994, "long_b0": 2157546298, "topk": 564771434, "sparse_decode": 190043143, "store_decode": 21981703, "compact": 197185489, "ragged": 615006047},
 }
 KERNEL_SOURCES = ("append.hip", "decode_impl.h", "decode_inst.hip", "topk.hip", "hkv_device.h", "hkv_internal.h")
 
