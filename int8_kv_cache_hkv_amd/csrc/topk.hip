@@ -757,8 +757,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkParams p) 
     int nc = 0;
 #pragma unroll
     for (int r = 0; r < WT; ++r) nc += !whole && kv[r] >= lo ? 1 : 0;
+    unsigned wk[S];  // a whole window's keys, read once for the count and the stage
     if (whole) {
-      unsigned wk[S];
       window_keys(pb, wi, n, wk);
       for (int j = 0; j < S; ++j) nc += wk[j] >= lo ? 1 : 0;
     }
@@ -769,8 +769,6 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkParams p) 
       return;
     }
     if (whole) {
-      unsigned wk[S];
-      window_keys(pb, wi, n, wk);
       for (int j = 0; j < S; ++j)
         if (wk[j] >= lo)
           stage[pos++] = static_cast<uint64_t>(wk[j]) | (static_cast<uint64_t>(static_cast<uint32_t>(wi * S + j)) << 32);
