@@ -54,8 +54,8 @@ OUT_MAX_ABS, OUT_MEAN_ABS = 4e-3, 5e-4
 # hold only for the kernel sources they were taken on: reported as null once the code of those
 # sources changes (the hash skips comments and blank lines).
 COUNTER_TRAFFIC = {
-    "sources_sha256": "01ea170a250da02b90ed032eb1b0b85af921e76528e8f212a629c7558976e99c",
-    "bytes_per_launch": {"llama8b": 36968721, "long": 1084489402, "llama8b_b4": 20720565, "long_b4": 550181240, "llama8b_b0": 69422994, "long_b0": 2157546298, "topk": 564771434, "sparse_decode": 190043143, "store_decode": 21981703, "compact": 197185489, "ragged": 615006047},
+    "sources_sha256": "cc7b1b9878e14195a335163e5a3989fc69334de1adc27a4843439b0cbbc8814b",
+    "bytes_per_launch": {"llama8b": 36969045, "long": 1084465875, "llama8b_b4": 20720522, "long_b4": 550185679, "llama8b_b0": 69422932, "long_b0": 2157503970, "topk": 564762786, "sparse_decode": 190046256, "store_decode": 21981706, "compact": 197185588, "ragged": 615006679},
 }
 KERNEL_SOURCES = ("append.hip", "decode_impl.h", "decode_inst.hip", "topk.hip", "hkv_device.h", "hkv_internal.h")
 
