@@ -646,18 +646,17 @@ __device__ void select_streaming(const unsigned* prob_bits, int n, int K, int32_
   }
 }
 
-// The 64 keys of window wi of a row, with 16-byte loads issued together (the row's buffer holds
-// whole windows, so the loads stay inside it); keys past the row's n are 0.
-__device__ __forceinline__ void window_keys(const unsigned* pb, int wi, int n, unsigned (&k)[kBlockSize]) {
-  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(pb + static_cast<size_t>(wi) * kBlockSize);
-  u32x4_t v[kBlockSize / 4];
-#pragma unroll
-  for (int i = 0; i < kBlockSize / 4; ++i) v[i] = src[i];
-#pragma unroll
-  for (int i = 0; i < kBlockSize / 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) k[4 * i + j] = wi * kBlockSize + 4 * i + j < n ? v[i][j] + 1u : 0u;
+// Key `lane` of window wi of a row (0 past the row's n): a whole window is read by one wave, one
+// coalesced 4-byte load per lane (lane = token of the window).
+static_assert(kBlockSize == 64, "a window is one key per lane");
+__device__ __forceinline__ unsigned window_key(const unsigned* pb, int wi, int n, int lane) {
+  const int i = wi * kBlockSize + lane;
+  return i < n ? pb[i] + 1u : 0u;
 }
+
+// Whole windows a wave keeps in registers between the count and the stage (one key per lane and
+// window); any further whole window of the wave is read again for the stage.
+constexpr int kHeldWhole = 4;
 
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkParams p) {
   constexpr int S = kBlockSize;
@@ -757,10 +756,24 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkParams p) 
     int nc = 0;
 #pragma unroll
     for (int r = 0; r < WT; ++r) nc += !whole && kv[r] >= lo ? 1 : 0;
-    unsigned wk[S];  // a whole window's keys, read once for the count and the stage
-    if (whole) {
-      window_keys(pb, wi, n, wk);
-      for (int j = 0; j < S; ++j) nc += wk[j] >= lo ? 1 : 0;
+    // whole windows (next to none; the short last window of a row is one): the wave reads each of
+    // its threads' whole windows together, lane j holding key j, and counts it with a ballot
+    const uint64_t wmask = __ballot(whole);  // (wave-uniform)
+    const int wbase = v * kSelThreads + w * 64;  // window of lane 0's thread
+    unsigned held[kHeldWhole];
+#pragma unroll
+    for (int k = 0; k < kHeldWhole; ++k) held[k] = 0u;
+    {
+      uint64_t m = wmask;
+      for (int k = 0; m != 0ull; ++k) {
+        const int owner = __builtin_ctzll(m);
+        m &= m - 1ull;
+        const unsigned key = window_key(pb, wbase + owner, n, lane);
+        const int cnt = __builtin_popcountll(__ballot(key >= lo));
+        nc += lane == owner ? cnt : 0;
+#pragma unroll
+        for (int j = 0; j < kHeldWhole; ++j) held[j] = j == k ? key : held[j];
+      }
     }
     int tot;
     int pos = m_all + block_exclusive_scan(nc, sm, &tot);
@@ -768,17 +781,34 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkParams p) 
       select_streaming(pb, n, K, out, sm);
       return;
     }
-    if (whole) {
-      for (int j = 0; j < S; ++j)
-        if (wk[j] >= lo)
-          stage[pos++] = static_cast<uint64_t>(wk[j]) | (static_cast<uint64_t>(static_cast<uint32_t>(wi * S + j)) << 32);
-    } else {
+    if (!whole) {
 #pragma unroll
       for (int r = 0; r < WT; ++r) {
         const unsigned ln = ((r < 4 ? lv.x : lv.y) >> (8 * (r % 4))) & 63u;
         if (kv[r] >= lo)  // (a window past the row has no keys: its tops are 0)
           stage[pos++] = static_cast<uint64_t>(kv[r]) |
                          (static_cast<uint64_t>(static_cast<uint32_t>(wi * S + static_cast<int>(ln))) << 32);
+      }
+    }
+    {
+      // a whole window's kept keys in index order: from its owner's position, each lane at the
+      // rank of its key among the window's kept keys
+      uint64_t m = wmask;
+      for (int k = 0; m != 0ull; ++k) {
+        const int owner = __builtin_ctzll(m);
+        m &= m - 1ull;
+        unsigned key = 0u;
+#pragma unroll
+        for (int j = 0; j < kHeldWhole; ++j) key = j == k ? held[j] : key;
+        if (k >= kHeldWhole) key = window_key(pb, wbase + owner, n, lane);
+        const bool keep = key >= lo;
+        const uint64_t km = __ballot(keep);
+        const int at = __builtin_amdgcn_readlane(pos, owner) +
+                       static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(km >> 32),
+                                                                  __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(km), 0u)));
+        if (keep)
+          stage[at] = static_cast<uint64_t>(key) |
+                      (static_cast<uint64_t>(static_cast<uint32_t>((wbase + owner) * S + lane)) << 32);
       }
     }
     m_all += tot;

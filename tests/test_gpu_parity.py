@@ -612,6 +612,46 @@ def test_topk_ties_prefer_lower_index(n, k):
     assert idx.cpu().numpy()[0].tolist() == [want] * H
 
 
+@pytest.mark.parametrize("flat,k", [(tuple(range(12)), 180),
+                                    (tuple(range(12)) + tuple(range(64, 70)), 200),
+                                    ((3, 63, 64, 127, 159), 170)])
+def test_topk_whole_windows(flat, k):
+    """Windows whose every top clears the floor are read whole (by their wave, one key per lane):
+    a row of 160 windows where the `flat` windows hold 64 equal keys (probability 1/64 each) and
+    every other window one key aligned with the query and 63 opposed ones (1/(1 + 63/e^2) and
+    that / e^2), with K between the aligned keys and the flat ones.  Covers more whole windows in
+    one wave than it keeps in registers, whole windows in two waves, and the one-wave and workgroup
+    selections of the candidates (916, 1294 and 475 of them).  Exact index set (equal keys tie exactly:
+    the lowest indices), and the oracle's."""
+    import int8_kv_cache_hkv_amd as hkv
+    torch = gh.torch_mod()
+    H, D, T, S, nw = 2, 64, 32, 64, 160
+    n_cold = S * nw
+    n = n_cold + T
+    kv = -np.ones((1, n, H, D), dtype=np.float16)
+    for wi in range(nw):
+        if wi in flat:
+            kv[0, S * wi:S * (wi + 1)] = 1
+        else:
+            kv[0, S * wi + 5] = 1
+    kv[0, n_cold:] = 1
+    cache = hkv.HybridKVCache(H, D, 1, n)
+    cache.append(gh.upload(kv), gh.upload(kv))
+    q = np.ones((1, 2 * H, D), dtype=np.float16)
+    idx = cache.topk(gh.upload(q), k)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()[0]
+    aligned = [S * wi + 5 for wi in range(nw) if wi not in flat]
+    flat_tokens = [t for wi in sorted(flat) for t in range(S * wi, S * (wi + 1))]
+    want = sorted(aligned + flat_tokens[:k - len(aligned)])
+    assert got.tolist() == [want] * H
+    st = orc.build_state(kv[0], kv[0], T, S)
+    w_or, p, tau = orc.topk_select(q[0], st, k)
+    for h in range(H):
+        assert w_or[h].tolist() == want
+        gh.compare_topk(got[h], w_or[h], p[h], tau[h], st.n_cold, k, f"whole windows {flat} k={k} h={h}")
+
+
 def test_topk_config_parity():
     """The 32768-token top-K workload at full size: the index sets of all 16 sequences x 8 kv-heads
     and the sparse decode over each selection against the oracle; then a dense decode and a second
