@@ -733,7 +733,12 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkParams p) 
   block_min_max_count(tmin, tmax, tcnt, sm, &bmin, &kmax, &bcnt);
   int unused;
   // (bcnt >= K: a row of more than kDirectKeys keys has more than kWinTop kDirectKeys / 64 >= K tops)
-  const unsigned lo = max(1u, range_select<WT * kTopsWPT>(tk, bmin, range_bits(bmin, kmax), K, 1, sm, &unused));
+  const int fbits = range_bits(bmin, kmax);
+  const unsigned lo = max(1u, range_select<WT * kTopsWPT>(tk, bmin, fbits, K, 1, sm, &unused));
+  // the floor's bin [lo, band_hi): fewer than K tops lie above it, so tau lies in it unless the keys
+  // of whole windows push it higher
+  const int fshift = max(0, fbits - kDigitBits);
+  const unsigned band_hi = lo + (1u << fshift);
   // ---- 2. the candidates of each round's windows (one window per thread), counted, scanned and
   // staged in index order
   uint64_t* stage = reinterpret_cast<uint64_t*>(sm.hist);
@@ -827,8 +832,21 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkParams p) 
       idx[k] = static_cast<int>(e >> 32);
     }
     unsigned* whist = sm.hist + 2 * kWaveKeys;  // past the stage (words)
+    int above = 0;
+#pragma unroll
+    for (int k = 0; k < kWaveKPT; ++k) above += key[k] >= band_hi ? 1 : 0;
+    int n_above;
+    (void)wave_exclusive_scan(above, lane, &n_above);
     int need_eq;
-    const unsigned tau = wave_range_select<kWaveKPT>(key, lo, range_bits(lo, kmax), K, whist, lane, &need_eq);
+    unsigned tau;
+    if (n_above < K) {  // tau is in the floor's bin: select among the keys inside it only
+      unsigned kb[kWaveKPT];
+#pragma unroll
+      for (int k = 0; k < kWaveKPT; ++k) kb[k] = key[k] < band_hi ? key[k] : 0u;
+      tau = wave_range_select<kWaveKPT>(kb, lo, fshift, K - n_above, whist, lane, &need_eq);
+    } else {
+      tau = wave_range_select<kWaveKPT>(key, lo, range_bits(lo, kmax), K, whist, lane, &need_eq);
+    }
     int eq, tot;
     const int both = count_both<kWaveKPT>(key, tau, &eq);
     const int before = wave_exclusive_scan(both, lane, &tot);
@@ -844,9 +862,22 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkParams p) 
     key[k] = static_cast<unsigned>(e);
     idx[k] = static_cast<int>(e >> 32);
   }
-  __syncthreads();  // the stage is the histogram's memory
+  int above = 0;
+#pragma unroll
+  for (int k = 0; k < kFinalKPT; ++k) above += key[k] >= band_hi ? 1 : 0;
+  int n_above;
+  (void)block_exclusive_scan(above, sm, &n_above);  // (its barriers also end the reads of the stage,
+                                                    // which is the histogram's memory)
   int need_eq;
-  const unsigned tau = range_select<kFinalKPT>(key, lo, range_bits(lo, kmax), K, 3, sm, &need_eq);
+  unsigned tau;
+  if (n_above < K) {  // tau is in the floor's bin: select among the keys inside it only
+    unsigned kb[kFinalKPT];
+#pragma unroll
+    for (int k = 0; k < kFinalKPT; ++k) kb[k] = key[k] < band_hi ? key[k] : 0u;
+    tau = range_select<kFinalKPT>(kb, lo, fshift, K - n_above, 3, sm, &need_eq);
+  } else {
+    tau = range_select<kFinalKPT>(key, lo, range_bits(lo, kmax), K, 3, sm, &need_eq);
+  }
   int eq, tot;
   const int both = count_both<kFinalKPT>(key, tau, &eq);
   const int before = block_exclusive_scan(both, sm, &tot);

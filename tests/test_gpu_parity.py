@@ -652,6 +652,47 @@ def test_topk_whole_windows(flat, k):
         gh.compare_topk(got[h], w_or[h], p[h], tau[h], st.n_cold, k, f"whole windows {flat} k={k} h={h}")
 
 
+@pytest.mark.parametrize("n_uniform,k", [(3, 505), (4, 510)])
+def test_topk_whole_windows_above_floor_bin(n_uniform, k):
+    """The K-th largest key above the floor's bin: `n_uniform` windows of 64 equal keys (1/64 each,
+    whole) among windows of 3 keys aligned with the query, 2 keys at cosine -0.9 and 59 opposed ones
+    (0.0886, 0.0133, 0.0120).  The K-th largest window top is a 0.0133 key, so the floor sits there,
+    but the uniform windows' keys put tau at 1/64, above its bin: the selection searches the whole
+    candidate range (977 candidates: one wave; 1036: the workgroup).  Exact index set, and the
+    oracle's."""
+    import int8_kv_cache_hkv_amd as hkv
+    torch = gh.torch_mod()
+    H, D, T, S, nw = 2, 64, 32, 64, 160
+    n_cold = S * nw
+    n = n_cold + T
+    alt = np.where(np.arange(D) % 2 == 0, 1.0, -1.0)
+    uniform = list(range(0, nw, nw // n_uniform))[:n_uniform]
+    kv = -np.ones((1, n, H, D), dtype=np.float16)
+    for wi in range(nw):
+        base = S * wi
+        if wi in uniform:
+            kv[0, base:base + S] = 1
+        else:
+            kv[0, base:base + 3] = 1
+            kv[0, base + 3:base + 5] = (-0.9 + 0.436 * alt).astype(np.float16)
+    kv[0, n_cold:] = 1
+    cache = hkv.HybridKVCache(H, D, 1, n)
+    cache.append(gh.upload(kv), gh.upload(kv))
+    q = np.ones((1, 2 * H, D), dtype=np.float16)
+    idx = cache.topk(gh.upload(q), k)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()[0]
+    aligned = [S * wi + j for wi in range(nw) if wi not in uniform for j in range(3)]
+    flat_tokens = [S * wi + j for wi in uniform for j in range(S)]
+    want = sorted(aligned + flat_tokens[:k - len(aligned)])
+    assert got.tolist() == [want] * H
+    st = orc.build_state(kv[0], kv[0], T, S)
+    w_or, p, tau = orc.topk_select(q[0], st, k)
+    for h in range(H):
+        assert w_or[h].tolist() == want
+        gh.compare_topk(got[h], w_or[h], p[h], tau[h], st.n_cold, k, f"above the floor's bin k={k} h={h}")
+
+
 def test_topk_config_parity():
     """The 32768-token top-K workload at full size: the index sets of all 16 sequences x 8 kv-heads
     and the sparse decode over each selection against the oracle; then a dense decode and a second
