@@ -50,14 +50,20 @@ OUT_MAX_ABS, OUT_MEAN_ABS = 4e-3, 5e-4
 
 # HBM bytes per launch from hardware counters (FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 KiB per
 # dispatch; the factors make a 256 MiB elementwise copy read and write exactly its size), recorded
-# in the profiles folder (decode_kernel_llama8b_hbm_traffic.md, path_kernels_hbm_traffic.md).  They
-# hold only for the kernel sources they were taken on: reported as null once the code of those
-# sources changes (the hash skips comments and blank lines).
+# in the profiles folder (path_kernels_hbm_traffic.md).  A figure holds only for the kernel sources
+# of its leg (TRAFFIC_SOURCES) as they were when it was taken: it is reported as null once their code
+# changes (the hash skips comments and blank lines).
 COUNTER_TRAFFIC = {
-    "sources_sha256": "cc7b1b9878e14195a335163e5a3989fc69334de1adc27a4843439b0cbbc8814b",
-    "bytes_per_launch": {"llama8b": 36969045, "long": 1084465875, "llama8b_b4": 20720522, "long_b4": 550185679, "llama8b_b0": 69422932, "long_b0": 2157503970, "topk": 564762786, "sparse_decode": 190046256, "store_decode": 21981706, "compact": 197185588, "ragged": 615006679},
+    "sources_sha256": {"llama8b": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "long": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "llama8b_b4": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "long_b4": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "llama8b_b0": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "long_b0": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "sparse_decode": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "store_decode": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "compact": "309892a2957f1162f4cc9fd38f16e916f346bed68dfd667b08dd4cdac4f49fcb", "ragged": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897"},
+    "bytes_per_launch": {"llama8b": 36969045, "long": 1084465875, "llama8b_b4": 20720522, "long_b4": 550185679, "llama8b_b0": 69422932, "long_b0": 2157503970, "sparse_decode": 190046256, "store_decode": 21981706, "compact": 197185588, "ragged": 615006679},
 }
-KERNEL_SOURCES = ("append.hip", "decode_impl.h", "decode_inst.hip", "topk.hip", "hkv_device.h", "hkv_internal.h")
+DECODE_SOURCES = ("decode_impl.h", "decode_inst.hip", "hkv_device.h", "hkv_internal.h")
+TRAFFIC_SOURCES = {"topk": ("topk.hip", "hkv_device.h", "hkv_internal.h"),
+                   "compact": ("compact.hip", "hkv_device.h", "hkv_internal.h")}  # every other leg: the decode's
+
+
+def leg_sources(leg: str):
+    return TRAFFIC_SOURCES.get(leg, DECODE_SOURCES)
 
 
 def code_text(src: str) -> str:
@@ -68,10 +74,10 @@ def code_text(src: str) -> str:
     return "\n".join(ln for ln in lines if ln)
 
 
-def sources_hash() -> str:
+def sources_hash(files=DECODE_SOURCES) -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files:
         p = os.path.join(ROOT, "int8_kv_cache_hkv_amd", "csrc", f)
         if os.path.exists(p):
             with open(p, encoding="utf-8") as fh:
@@ -81,7 +87,8 @@ def sources_hash() -> str:
 
 def counter_traffic(leg: str):
     """(bytes per launch, source) recorded from the counters for this leg, or (None, reason)."""
-    if COUNTER_TRAFFIC["sources_sha256"] != sources_hash() or leg not in COUNTER_TRAFFIC["bytes_per_launch"]:
+    if (leg not in COUNTER_TRAFFIC["bytes_per_launch"]
+            or COUNTER_TRAFFIC["sources_sha256"].get(leg) != sources_hash(leg_sources(leg))):
         return None, "not measured on the current kernel sources"
     return COUNTER_TRAFFIC["bytes_per_launch"][leg], "recorded from rocprofv3 FETCH_SIZE/WRITE_SIZE (profiles folder)"
 
