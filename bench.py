@@ -720,6 +720,77 @@ def leg_read_floor(hkv, torch, args, nbytes=34_406_400, R=64, reps=20):
                     "64 rotating buffers", "bytes": nbytes, "shapes": res, "best": best}
 
 
+def leg_prefill(hkv, torch, args):
+    """Bulk append (a prompt's whole K/V in one hkv_append call into an empty cache): the
+    quantise launch (every touched block coded from FP16) and the ring/tail launch.  Two shapes:
+    the llama8b layer's 8 sequences x 2048 tokens, and the 32768-token top-K workload's fill chunk,
+    16 sequences x 8192 tokens.  Each trial empties R instances (seq_len 0, outside the timed
+    region) and appends the same tokens to each, back to back."""
+    import oracle.hkv_oracle as orc
+    import workloads as wl
+    out = {"what": "hkv_append of a whole prompt into empty caches (append_quant_kernel + append_ring_kernel)"}
+    for name, wname, n, R in (("llama8b_2048", "llama8b", 2048, 16), ("topk_8192", "topk", 8192, 4)):
+        w = wl.WORKLOADS[wname]
+        B, H, d, T, S = w.batch, w.n_kv_heads, w.head_dim, w.hot_tokens, w.block_size
+        log(f"prefill {name}: {R} instances of B={B}, {n} tokens per sequence")
+        insts = [hkv.HybridKVCache(H, d, B, n) for _ in range(R)]
+        kb = torch.from_numpy(wl.batch_tokens(w, list(range(B)), 0, n, "k")).cuda()
+        vb = torch.from_numpy(wl.batch_tokens(w, list(range(B)), 0, n, "v")).cuda()
+
+        def reset():
+            for c in insts:
+                c.seq_len.zero_()
+                c.seq_len_host[:] = 0
+            torch.cuda.synchronize()
+
+        host, dev = [], []
+        for _ in range(1 + args.trials):  # the first round warms up
+            reset()
+            t0 = time.perf_counter()
+            for c in insts:
+                c.append(kb, vb)
+            torch.cuda.synchronize()
+            host.append((time.perf_counter() - t0) * 1e3 / R)
+            reset()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for c in insts:
+                c.append(kb, vb)
+            e1.record()
+            torch.cuda.synchronize()
+            dev.append(e0.elapsed_time(e1) / R)
+        host, dev = host[1:], dev[1:]
+        n_cold = n - T
+        blocks = -(-n_cold // S)
+        tile = S * d  # bytes of one 8-bit (block, kv-head, K|V) tile
+        nbytes = (B * n * H * d * 2 * 2            # every new K and V row read (fp16)
+                  + B * blocks * H * 2 * tile      # the touched tiles written
+                  + B * blocks * H * 2 * 4         # their scales
+                  + B * (n_cold % S) * H * d * 2 * 2  # the partial block's rows into the tail shadow
+                  + B * T * H * d * 2 * 2)         # the hot ring
+        ms = statistics.median(dev)
+        # the last trial's caches: all instances equal, and sequence 0's codes and scales equal the oracle's
+        # (sequence 0's logical blocks are physical blocks 0, 1, ... in the default placement)
+        c0 = insts[0]
+        same = all(torch.equal(c0.cold, c.cold) and torch.equal(c0.scales, c.scales) and torch.equal(c0.hot, c.hot)
+                   for c in insts[1:])
+        record_check({"what": f"prefill {name}: every instance holds the same bytes", "ok": bool(same)})
+        st = orc.build_state(kb[0].cpu().numpy(), vb[0].cpu().numpy(), T, S)
+        codes = c0.cold_codes()
+        scales = c0.scale_array()
+        nb = min(4, blocks)
+        ok = bool(np.array_equal(codes[:nb], st.codes[:nb]) and np.array_equal(scales[:nb], st.scales[:nb]))
+        record_check({"what": f"prefill {name}: sequence 0, blocks 0-{nb - 1}: codes and scales vs the fp64 oracle "
+                              "(bitwise)", "ok": ok})
+        out[name] = {"batch": B, "tokens": n, "instances": R, "ms_per_call": round(statistics.median(host), 6),
+                     "trials_ms": [round(x, 6) for x in host],
+                     "roofline": roofline("append_quant_kernel + append_ring_kernel (one hkv_append call)", nbytes, ms,
+                                          f"prefill_{name}")}
+        del insts, kb, vb
+        torch.cuda.empty_cache()
+    return out
+
+
 def host_info():
     try:
         from threadpoolctl import threadpool_info
@@ -798,7 +869,7 @@ def copy_calibration(torch, mib=256, reps=4):
 
 
 LEGS = ("llama8b", "separate", "long", "llama8b_int4", "long_int4", "llama8b_fp16", "long_fp16", "sparse", "ragged", "phases",
-        "graph", "read_floor", "cpu")
+        "graph", "read_floor", "prefill", "cpu")
 
 
 def main():
@@ -871,6 +942,8 @@ def main():
         res["phases"] = leg_phases(hkv, torch, args)
     if "read_floor" in legs:
         res["read_floor"] = leg_read_floor(hkv, torch, args)
+    if "prefill" in legs:
+        res["prefill"] = leg_prefill(hkv, torch, args)
     if args.copy_calibration:
         res["copy_calibration"] = copy_calibration(torch)
     if "cpu" in legs:

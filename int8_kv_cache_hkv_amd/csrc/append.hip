@@ -13,15 +13,18 @@
 //
 // Two launches, in stream order (multi-block appends; the single-pass
 // append_step_kernel below serves appends that touch at most two blocks):
-//   append_quant_kernel  one workgroup per (sequence, touched block, kv-head):
-//                        gathers the block's FP16 rows (tail shadow, hot ring,
-//                        new tokens), reduces max|x|, divides and rounds, and
-//                        writes the codes in the tile layouts the decode
-//                        kernels stream, plus scales and the block header.
-//   append_ring_kernel   one workgroup per sequence: copies the new partial
-//                        block's FP16 rows into the tail shadow, then writes
-//                        the new tokens into the hot ring (after every read of
-//                        the slots they replace), then publishes seq_len.
+//   append_quant_kernel  one workgroup per (sequence, touched block, kv-head,
+//                        K|V): gathers the tile's FP16 rows (tail shadow, hot
+//                        ring, new tokens), reduces max|x|, divides and rounds,
+//                        and writes the codes in the tile layout the decode
+//                        kernels stream, plus the scale and the block header.
+//   append_ring_kernel   one workgroup per (sequence, kv-head): copies the new
+//                        partial block's FP16 rows into the tail shadow, then
+//                        writes the new tokens into the hot ring (after every
+//                        read of the slots they replace); the kv-head 0
+//                        workgroup publishes seq_len.
+// Both take the cached lengths from the host mirror (kernel arguments), so
+// their first loads are the rows themselves.
 #include <hip/hip_ext.h>
 
 #include <type_traits>
@@ -51,11 +54,12 @@ __device__ __forceinline__ uint32_t slice_half_bits(const u32x4_t (&x)[NV], int 
 }
 
 // Stage the CPT elements of token t at channels [c0, c0 + CPT) of one tile: 8-/4-bit codes under
-// scale s (clamp(rint(fl32(x / s)), -L, L)), or the fp16 values.  kv selects the stage order.
-// Returns the largest |x - code * s| of these elements (fma: the exact difference rounded once to
-// fp32), 0 for fp16 tiles.
+// scale s (rint(fl32(x / s)): every x lies inside the tile's maximum, so |code| <= L without a
+// clamp), or the fp16 values.  kv selects the stage order.  With want_err, returns the largest
+// |x - code * s| of these elements (fma: the exact difference rounded once to fp32); else 0.
 template <int D, int BITS, int CPT, int NV>
-__device__ __forceinline__ float stage_row(int8_t* stage, const u32x4_t (&x)[NV], float s, int kv, int t, int c0) {
+__device__ __forceinline__ float stage_row(int8_t* stage, const u32x4_t (&x)[NV], float s, int kv, int t, int c0,
+                                           bool want_err) {
   using TS = TileStage<D, BITS>;
   if constexpr (BITS == 0) {
     if (kv == 0) {
@@ -72,7 +76,6 @@ __device__ __forceinline__ float stage_row(int8_t* stage, const u32x4_t (&x)[NV]
     return 0.f;
   } else {
     const float rs = quant_recip(s);
-    float err = 0.f;
     uint32_t q[CPT / 4];
 #pragma unroll
     for (int i = 0; i < CPT / 4; ++i) {
@@ -81,12 +84,19 @@ __device__ __forceinline__ float stage_row(int8_t* stage, const u32x4_t (&x)[NV]
       for (int k = 0; k < 4; ++k) {
         const int e = 4 * i + k;
         const uint32_t wd = x[e / 8][(e % 8) / 2];
-        const float xv = (e & 1) ? half_hi(wd) : half_lo(wd);
-        const float qv = quant_code<Fmt<BITS>::kLimit>(xv, s, rs);
-        err = fmaxf(err, __builtin_fabsf(fmaf(-qv, s, xv)));
-        cb[k] = static_cast<uint32_t>(static_cast<int>(qv));
+        cb[k] = code_bits(quant_quotient((e & 1) ? half_hi(wd) : half_lo(wd), s, rs));
       }
       q[i] = pack_low_bytes(cb[0], cb[1], cb[2], cb[3]);
+    }
+    float err = 0.f;
+    if (want_err) {
+#pragma unroll
+      for (int e = 0; e < CPT; ++e) {
+        const uint32_t wd = x[e / 8][(e % 8) / 2];
+        const float xv = (e & 1) ? half_hi(wd) : half_lo(wd);
+        const float qv = static_cast<float>(static_cast<int8_t>(q[e / 4] >> (8 * (e % 4))));
+        err = fmaxf(err, __builtin_fabsf(fmaf(-qv, s, xv)));
+      }
     }
     if (kv == 0) {
       uint32_t* dst = reinterpret_cast<uint32_t*>(stage + t * TS::KROW + c0);
@@ -155,6 +165,8 @@ __device__ __forceinline__ float tile_scale(float m) {
   else return m / static_cast<float>(Fmt<BITS>::kLimit);
 }
 
+// One workgroup per (sequence, touched block, kv-head, K|V): one tile, so that the K and V tiles of a
+// block are coded side by side rather than one after the other.
 template <int D, int BITS>
 __global__ __launch_bounds__(kThreads) void append_quant_kernel(AppendParams p) {
   constexpr int S = kBlockSize;
@@ -168,7 +180,8 @@ __global__ __launch_bounds__(kThreads) void append_quant_kernel(AppendParams p) 
 
   const CacheView& c = p.c;
   const int H = c.H, T = c.T;
-  const int wg = blockIdx.x;
+  const int kv = blockIdx.x & 1;
+  const int wg = blockIdx.x >> 1;
   const int h = wg % H;
   const int rest = wg / H;
   const int jj = rest % p.touched_max;
@@ -177,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void append_quant_kernel(AppendParams p) 
   const int b = p.b0 + bl;
   const int nn = p.n_new[bl];
   if (nn <= 0) return;
-  const int n0 = c.seq_len[b];
+  const int n0 = p.n0[bl];  // the host mirror: no load before the rows are requested
   const int n1 = n0 + nn;
   const int cold0 = n0 > T ? n0 - T : 0;
   const int cold1 = n1 > T ? n1 - T : 0;
@@ -185,8 +198,7 @@ __global__ __launch_bounds__(kThreads) void append_quant_kernel(AppendParams p) 
   const int j = cold0 / S + jj;
   if (j * S >= cold1 || j >= c.max_blocks) return;
   hkv_block_header* hdr = c.headers + static_cast<size_t>(b) * c.max_blocks + j;
-  const int phys = hdr->phys_block;
-  if (phys < 0 || phys >= c.num_phys) return;
+  const int ph_lane = hdr->phys_block;  // resolved only before the writes (its wait would hold the row loads)
   const int valid = min(S, cold1 - j * S);
 
   const int tid = threadIdx.x;
@@ -194,51 +206,73 @@ __global__ __launch_bounds__(kThreads) void append_quant_kernel(AppendParams p) 
   const int part = tid % TPT;           // channel slice
   const int pos = j * S + t;
 
-  for (int kv = 0; kv < 2; ++kv) {
-    // ---- gather the FP16 row slice of token t
-    const _Float16* row = nullptr;
-    if (t < valid) {
-      if (pos < cold0) {
-        row = c.tail + ((static_cast<size_t>(b) * H + h) * 2 + kv) * S * D + static_cast<size_t>(t) * D;
-      } else if (pos < n0) {
-        row = c.hot + (((static_cast<size_t>(b) * H + h) * T + (pos % T)) * 2 + kv) * D;
-      } else {
-        const _Float16* src = kv ? p.v_new : p.k_new;
-        row = src + ((static_cast<size_t>(b) * p.max_n_new + (pos - n0)) * H + h) * D;
-      }
+  // ---- the FP16 row slice of token t: the tail shadow (rows of a partial block already cached),
+  // the hot ring (rows leaving it) or the new tokens
+  const _Float16* row = nullptr;
+  if (t < valid) {
+    if (pos < cold0) {
+      row = c.tail + ((static_cast<size_t>(b) * H + h) * 2 + kv) * S * D + static_cast<size_t>(t) * D;
+    } else if (pos < n0) {
+      row = c.hot + (((static_cast<size_t>(b) * H + h) * T + (pos % T)) * 2 + kv) * D;
+    } else {
+      const _Float16* src = kv ? p.v_new : p.k_new;
+      row = src + ((static_cast<size_t>(b) * p.max_n_new + (pos - n0)) * H + h) * D;
     }
-    u32x4_t x[NV];
+  }
+  u32x4_t x[NV];
 #pragma unroll
-    for (int v = 0; v < NV; ++v)
-      x[v] = row ? reinterpret_cast<const u32x4_t*>(row + part * CPT)[v] : u32x4_t{0u, 0u, 0u, 0u};
-    // ---- m = max |x| over the block (exact: every candidate is an fp16 value)
-    float m = 0.f;
+  for (int v = 0; v < NV; ++v)
+    x[v] = row ? reinterpret_cast<const u32x4_t*>(row + part * CPT)[v] : u32x4_t{0u, 0u, 0u, 0u};
+  const int phys = __builtin_amdgcn_readfirstlane(ph_lane);
+  const bool write = phys >= 0 && phys < c.num_phys;  // (workgroup-uniform; out-of-range ids are skipped)
+
+  // ---- m = max |x| over the tile (exact: every candidate is an fp16 value)
+  float m = 0.f;
 #pragma unroll
-    for (int v = 0; v < NV; ++v)
+  for (int v = 0; v < NV; ++v)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(half_lo(x[v][i])), fabsf(half_hi(x[v][i]))));
-    m = wave_max(m);
-    if ((tid & 63) == 0) red[tid >> 6] = m;
-    __syncthreads();
-    m = red[0];
+    for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(half_lo(x[v][i])), fabsf(half_hi(x[v][i]))));
+  m = wave_max(m);
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  m = red[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) m = fmaxf(m, red[w]);
-    // ---- s = fl32(m / L) (IEEE fp32 division), codes = clamp(rint(fl32(x / s)), -L, L)
-    const float s = tile_scale<BITS>(m);
-    const float err = stage_row<D, BITS, CPT, NV>(stage, x, s, kv, t, part * CPT);
-    const float tile_err = c.quant_err ? block_max(err, rerr) : 0.f;  // (also the stage barrier)
-    __syncthreads();
-    // ---- write the tile in its streaming layout
+  for (int w = 1; w < kWaves; ++w) m = fmaxf(m, red[w]);
+  // ---- s = fl32(m / L) (IEEE fp32 division), codes = clamp(rint(fl32(x / s)), -L, L)
+  const float s = tile_scale<BITS>(m);
+  const float err = stage_row<D, BITS, CPT, NV>(stage, x, s, kv, t, part * CPT, c.quant_err != nullptr);
+  const float tile_err = c.quant_err ? block_max(err, rerr) : 0.f;  // (also the stage barrier)
+  __syncthreads();
+  // ---- write the tile in its streaming layout
+  if (write) {
     write_tile<D, BITS>(c.cold + tile_offset(phys, h, kv, H, TB), stage, kv, tid);
     if (tid == 0) c.scales[(static_cast<size_t>(phys) * H + h) * 2 + kv] = s;
     if (tid == 0 && c.quant_err) c.quant_err[(static_cast<size_t>(phys) * H + h) * 2 + kv] = tile_err;
-    __syncthreads();  // stage and red are reused by the V pass
+    if (h == 0 && kv == 0 && tid == 0) {
+      hdr->n_valid = valid;
+      hdr->logical_block = j;
+      hdr->flags = 0u;
+    }
   }
-  if (h == 0 && tid == 0) {
-    hdr->n_valid = valid;
-    hdr->logical_block = j;
-    hdr->flags = 0u;
-  }
+}
+
+// One workgroup per (sequence, kv-head): the tail shadow of the new partial block, then the hot ring.
+// Each copy moves 16-byte vectors, item = (row, K|V, vector), kRingBatch per thread at a time: a
+// round's loads are all issued before its stores (a store between them would make every load wait).
+constexpr int kRingBatch = 8;
+
+struct RingCopy {
+  const _Float16* hot;     // this (sequence, kv-head)'s ring: [T][2][D]
+  const _Float16* k_new;   // this (sequence, kv-head)'s first new token row (stride H*D per token)
+  const _Float16* v_new;
+  int n0, T, D, HD;
+};
+
+// Source of vector v of row (pos, kv): the ring slot (pos < n0) or the new token.
+__device__ __forceinline__ const u32x4_t* ring_src(const RingCopy& r, int pos, int kv, int v) {
+  const _Float16* row = pos < r.n0 ? r.hot + ((pos % r.T) * 2 + kv) * r.D
+                                   : (kv ? r.v_new : r.k_new) + static_cast<size_t>(pos - r.n0) * r.HD;
+  return reinterpret_cast<const u32x4_t*>(row) + v;
 }
 
 template <int D>
@@ -247,58 +281,65 @@ __global__ __launch_bounds__(kThreads) void append_ring_kernel(AppendParams p) {
   constexpr int VPR = D / 8;            // 16-byte vectors per (token, head, K|V) row
   const CacheView& c = p.c;
   const int H = c.H, T = c.T;
-  const int bl = blockIdx.x;
+  const int h = blockIdx.x % H;
+  const int bl = blockIdx.x / H;
   if (bl >= p.n_seq) return;
   const int b = p.b0 + bl;
   const int nn = p.n_new[bl];
   if (nn <= 0) return;
-  const int n0 = c.seq_len[b];
+  const int n0 = p.n0[bl];  // the host mirror: this launch never reads seq_len, which it publishes
   const int n1 = n0 + nn;
   const int cold0 = n0 > T ? n0 - T : 0;
   const int cold1 = n1 > T ? n1 - T : 0;
+  const size_t bh = static_cast<size_t>(b) * H + h;
+  const size_t new0 = (static_cast<size_t>(b) * p.max_n_new * H + h) * D;
+  const RingCopy r{c.hot + bh * T * 2 * D, p.k_new + new0, p.v_new + new0, n0, T, D, H * D};
   const int tid = threadIdx.x;
 
   // (1) FP16 shadow of the new partial last block (rows already there stay)
   const int jf = cold1 / S;
   if ((cold1 % S) != 0 && jf < c.max_blocks) {
-    const int lo = max(jf * S, cold0), hi = cold1;
-    const int items = (hi - lo) * H * 2 * VPR;
-    for (int it = tid; it < items; it += kThreads) {
-      const int v = it % VPR;
-      int r = it / VPR;
-      const int kv = r % 2;
-      r /= 2;
-      const int h = r % H;
-      const int pos = lo + r / H;
-      const _Float16* src;
-      if (pos < n0) {
-        src = c.hot + (((static_cast<size_t>(b) * H + h) * T + (pos % T)) * 2 + kv) * D;
-      } else {
-        src = (kv ? p.v_new : p.k_new) + ((static_cast<size_t>(b) * p.max_n_new + (pos - n0)) * H + h) * D;
+    const int lo = max(jf * S, cold0);
+    const int items = (cold1 - lo) * 2 * VPR;
+    _Float16* tail = c.tail + bh * 2 * S * D;
+    for (int base = 0; base < items; base += kRingBatch * kThreads) {
+      u32x4_t buf[kRingBatch];
+#pragma unroll
+      for (int k = 0; k < kRingBatch; ++k) {
+        const int it = min(base + k * kThreads + tid, items - 1);  // (clamped: every load is in range)
+        buf[k] = *ring_src(r, lo + it / (2 * VPR), (it / VPR) % 2, it % VPR);
       }
-      _Float16* dst = c.tail + ((static_cast<size_t>(b) * H + h) * 2 + kv) * S * D + static_cast<size_t>(pos - jf * S) * D;
-      reinterpret_cast<uint4*>(dst)[v] = reinterpret_cast<const uint4*>(src)[v];
+#pragma unroll
+      for (int k = 0; k < kRingBatch; ++k) {
+        const int it = base + k * kThreads + tid;
+        const int pos = lo + it / (2 * VPR), kv = (it / VPR) % 2;
+        if (it < items) reinterpret_cast<u32x4_t*>(tail + (kv * S + (pos - jf * S)) * D)[it % VPR] = buf[k];
+      }
     }
   }
   __syncthreads();  // ring slots read above are overwritten below
   // (2) new tokens that remain hot go to ring slot pos mod T
   {
-    const int lo = max(n0, n1 - T), hi = n1;
-    const int items = (hi - lo) * H * 2 * VPR;
-    for (int it = tid; it < items; it += kThreads) {
-      const int v = it % VPR;
-      int r = it / VPR;
-      const int kv = r % 2;
-      r /= 2;
-      const int h = r % H;
-      const int pos = lo + r / H;
-      const _Float16* src = (kv ? p.v_new : p.k_new) + ((static_cast<size_t>(b) * p.max_n_new + (pos - n0)) * H + h) * D;
-      _Float16* dst = c.hot + (((static_cast<size_t>(b) * H + h) * T + (pos % T)) * 2 + kv) * D;
-      reinterpret_cast<uint4*>(dst)[v] = reinterpret_cast<const uint4*>(src)[v];
+    const int lo = max(n0, n1 - T);
+    const int items = (n1 - lo) * 2 * VPR;
+    _Float16* ring = c.hot + bh * T * 2 * D;
+    for (int base = 0; base < items; base += kRingBatch * kThreads) {
+      u32x4_t buf[kRingBatch];
+#pragma unroll
+      for (int k = 0; k < kRingBatch; ++k) {
+        const int it = min(base + k * kThreads + tid, items - 1);  // (clamped: every load is in range)
+        buf[k] = *ring_src(r, lo + it / (2 * VPR), (it / VPR) % 2, it % VPR);
+      }
+#pragma unroll
+      for (int k = 0; k < kRingBatch; ++k) {
+        const int it = base + k * kThreads + tid;
+        const int pos = lo + it / (2 * VPR), kv = (it / VPR) % 2;
+        if (it < items) reinterpret_cast<u32x4_t*>(ring + ((pos % T) * 2 + kv) * D)[it % VPR] = buf[k];
+      }
     }
   }
-  __syncthreads();
-  if (tid == 0) c.seq_len[b] = n1;
+  // the new length, once per sequence (no workgroup of this launch reads it)
+  if (h == 0 && tid == 0) c.seq_len[b] = n1;
 }
 
 // Single-pass append, one workgroup per (sequence, kv-head), for appends that
@@ -505,7 +546,7 @@ __global__ __launch_bounds__(kThreads) void append_step_kernel(AppendParams p) {
       u32x4_t xs[NV];
 #pragma unroll
       for (int v = 0; v < NV; ++v) xs[v] = t < vo ? xo[kv][v] : xn[q][kv][v];  // element-wise: no indexed arrays
-      const float err = stage_row<D, BITS, CPT, NV>(stage, xs, s, kv, t, part * CPT);
+      const float err = stage_row<D, BITS, CPT, NV>(stage, xs, s, kv, t, part * CPT, c.quant_err != nullptr);
       const float tile_err = c.quant_err ? block_max(err, rerr) : 0.f;
       __syncthreads();
       write_tile<D, BITS>(tile, stage, kv, tid);
@@ -580,9 +621,9 @@ hipError_t launch_grid(K kernel, dim3 grid, const AppendParams& p, const LaunchC
 template <int D, int BITS>
 hipError_t launch_append_db(const AppendParams& p, const LaunchCtx& quant_ctx, const LaunchCtx& ring_ctx) {
   if (p.single_pass) return launch_grid(append_step_kernel<D, BITS>, dim3(p.c.H, p.n_seq), p, quant_ctx);
-  const int qgrid = p.touched_max > 0 ? p.n_seq * p.touched_max * p.c.H : 0;
+  const int qgrid = p.touched_max > 0 ? p.n_seq * p.touched_max * p.c.H * 2 : 0;
   const hipError_t e = launch1(append_quant_kernel<D, BITS>, qgrid, p, quant_ctx);
-  return e == hipSuccess ? launch1(append_ring_kernel<D>, p.n_seq, p, ring_ctx) : e;
+  return e == hipSuccess ? launch1(append_ring_kernel<D>, p.n_seq * p.c.H, p, ring_ctx) : e;
 }
 
 template <int D>
