@@ -110,6 +110,52 @@ __device__ __forceinline__ float stage_row(int8_t* stage, const u32x4_t (&x)[NV]
   }
 }
 
+// Stage a V tile's elements held as NV tokens (tg NV + r, r < NV) x 8 channels [c0, c0 + 8): the
+// tile is channel-major, so each channel's NV codes (or fp16 values) are adjacent in the stage and
+// leave in one store.  Codes, the error and want_err as in stage_row.
+template <int D, int BITS, int NV>
+__device__ __forceinline__ float stage_cols(int8_t* stage, const u32x4_t (&x)[NV], float s, int tg, int c0,
+                                            bool want_err) {
+  using TS = TileStage<D, BITS>;
+  static_assert(NV == 2 || NV == 4, "2 or 4 tokens per thread");
+  if constexpr (BITS == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint32_t hv[NV];
+#pragma unroll
+      for (int r = 0; r < NV; ++r) hv[r] = (e & 1) ? (x[r][e / 2] >> 16) : (x[r][e / 2] & 0xffffu);
+      int8_t* dst = stage + (c0 + e) * TS::VROW + tg * NV * 2;
+      if constexpr (NV == 4) {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+      } else {
+        *reinterpret_cast<uint32_t*>(dst) = hv[0] | (hv[1] << 16);
+      }
+    }
+    return 0.f;
+  } else {
+    const float rs = quant_recip(s);
+    float err = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {  // channel c0 + e: its NV codes, packed and stored together
+      uint32_t cb[NV];
+#pragma unroll
+      for (int r = 0; r < NV; ++r) {
+        const uint32_t wd = x[r][e / 2];
+        const float xv = (e & 1) ? half_hi(wd) : half_lo(wd);
+        cb[r] = code_bits(quant_quotient(xv, s, rs));
+        if (want_err) err = fmaxf(err, __builtin_fabsf(fmaf(-static_cast<float>(static_cast<int8_t>(cb[r])), s, xv)));
+      }
+      int8_t* dst = stage + (c0 + e) * TS::VROW + tg * NV;
+      if constexpr (NV == 4) {
+        *reinterpret_cast<uint32_t*>(dst) = pack_low_bytes(cb[0], cb[1], cb[2], cb[3]);
+      } else {
+        *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>((cb[0] & 0xffu) | ((cb[1] & 0xffu) << 8));
+      }
+    }
+    return err;
+  }
+}
+
 // Largest value of v over the workgroup (every thread calls it; red holds kWaves floats).
 __device__ __forceinline__ float block_max(float v, float* red) {
   v = wave_max_dpp(v);
@@ -202,27 +248,37 @@ __global__ __launch_bounds__(kThreads) void append_quant_kernel(AppendParams p) 
   const int valid = min(S, cold1 - j * S);
 
   const int tid = threadIdx.x;
-  const int t = tid / TPT;              // token row inside the block
-  const int part = tid % TPT;           // channel slice
-  const int pos = j * S + t;
+  // K tiles (token-major): thread = (token t, channel slice part), NV vectors of 8 channels of token
+  // t.  V tiles (channel-major): thread = (token group tg, channel group cg), vector r = 8 channels of
+  // token tg NV + r, so that the stage takes each channel's NV codes in one store.
+  constexpr int NTG = S / NV;           // token groups of a V tile
+  static_assert(NTG * (D / 8) == kThreads, "a V tile is NV tokens x 8 channels per thread");
+  const int t = tid / TPT;              // (K) token row inside the block
+  const int part = tid % TPT;           // (K) channel slice
+  const int tg = tid % NTG;             // (V) token group
+  const int cg = tid / NTG;             // (V) channel group
 
-  // ---- the FP16 row slice of token t: the tail shadow (rows of a partial block already cached),
-  // the hot ring (rows leaving it) or the new tokens
-  const _Float16* row = nullptr;
-  if (t < valid) {
-    if (pos < cold0) {
-      row = c.tail + ((static_cast<size_t>(b) * H + h) * 2 + kv) * S * D + static_cast<size_t>(t) * D;
-    } else if (pos < n0) {
-      row = c.hot + (((static_cast<size_t>(b) * H + h) * T + (pos % T)) * 2 + kv) * D;
-    } else {
-      const _Float16* src = kv ? p.v_new : p.k_new;
-      row = src + ((static_cast<size_t>(b) * p.max_n_new + (pos - n0)) * H + h) * D;
-    }
-  }
+  // ---- the FP16 row slices: the tail shadow (rows of a partial block already cached), the hot
+  // ring (rows leaving it) or the new tokens
   u32x4_t x[NV];
 #pragma unroll
-  for (int v = 0; v < NV; ++v)
-    x[v] = row ? reinterpret_cast<const u32x4_t*>(row + part * CPT)[v] : u32x4_t{0u, 0u, 0u, 0u};
+  for (int v = 0; v < NV; ++v) {
+    const int tok = kv ? tg * NV + v : t;
+    const int col = kv ? cg * 8 : part * CPT + 8 * v;
+    const int pos = j * S + tok;
+    const _Float16* row = nullptr;
+    if (tok < valid) {
+      if (pos < cold0) {
+        row = c.tail + ((static_cast<size_t>(b) * H + h) * 2 + kv) * S * D + static_cast<size_t>(tok) * D;
+      } else if (pos < n0) {
+        row = c.hot + (((static_cast<size_t>(b) * H + h) * T + (pos % T)) * 2 + kv) * D;
+      } else {
+        const _Float16* src = kv ? p.v_new : p.k_new;
+        row = src + ((static_cast<size_t>(b) * p.max_n_new + (pos - n0)) * H + h) * D;
+      }
+    }
+    x[v] = row ? *reinterpret_cast<const u32x4_t*>(row + col) : u32x4_t{0u, 0u, 0u, 0u};
+  }
   const int phys = __builtin_amdgcn_readfirstlane(ph_lane);
   const bool write = phys >= 0 && phys < c.num_phys;  // (workgroup-uniform; out-of-range ids are skipped)
 
@@ -240,7 +296,12 @@ __global__ __launch_bounds__(kThreads) void append_quant_kernel(AppendParams p) 
   for (int w = 1; w < kWaves; ++w) m = fmaxf(m, red[w]);
   // ---- s = fl32(m / L) (IEEE fp32 division), codes = clamp(rint(fl32(x / s)), -L, L)
   const float s = tile_scale<BITS>(m);
-  const float err = stage_row<D, BITS, CPT, NV>(stage, x, s, kv, t, part * CPT, c.quant_err != nullptr);
+  float err;
+  if (kv) {
+    err = stage_cols<D, BITS, NV>(stage, x, s, tg, cg * 8, c.quant_err != nullptr);
+  } else {
+    err = stage_row<D, BITS, CPT, NV>(stage, x, s, 0, t, part * CPT, c.quant_err != nullptr);
+  }
   const float tile_err = c.quant_err ? block_max(err, rerr) : 0.f;  // (also the stage barrier)
   __syncthreads();
   // ---- write the tile in its streaming layout
