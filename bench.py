@@ -54,12 +54,14 @@ OUT_MAX_ABS, OUT_MEAN_ABS = 4e-3, 5e-4
 # of its leg (TRAFFIC_SOURCES) as they were when it was taken: it is reported as null once their code
 # changes (the hash skips comments and blank lines).
 COUNTER_TRAFFIC = {
-    "sources_sha256": {"llama8b": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "long": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "llama8b_b4": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "long_b4": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "llama8b_b0": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "long_b0": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "sparse_decode": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "store_decode": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "compact": "309892a2957f1162f4cc9fd38f16e916f346bed68dfd667b08dd4cdac4f49fcb", "ragged": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897"},
-    "bytes_per_launch": {"llama8b": 36969045, "long": 1084465875, "llama8b_b4": 20720522, "long_b4": 550185679, "llama8b_b0": 69422932, "long_b0": 2157503970, "sparse_decode": 190046256, "store_decode": 21981706, "compact": 197185588, "ragged": 615006679},
+    "sources_sha256": {"llama8b": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "long": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "llama8b_b4": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "long_b4": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "llama8b_b0": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "long_b0": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "topk": "534261211f52f58f2d73383954ff1c33bf147c2793f3c6e556f6eb451c93210f", "sparse_decode": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "store_decode": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "compact": "309892a2957f1162f4cc9fd38f16e916f346bed68dfd667b08dd4cdac4f49fcb", "ragged": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "prefill_llama8b_2048": "1849120482a7a5e0327f945a629f056c8cdca38fce2eeef8dd067598123355ac", "prefill_topk_8192": "1849120482a7a5e0327f945a629f056c8cdca38fce2eeef8dd067598123355ac"},
+    "bytes_per_launch": {"llama8b": 36969045, "long": 1084465875, "llama8b_b4": 20720522, "long_b4": 550185679, "llama8b_b0": 69422932, "long_b0": 2157503970, "topk": 564694298, "sparse_decode": 190047706, "store_decode": 21981749, "compact": 197186063, "ragged": 615006679, "prefill_llama8b_2048": 104263610, "prefill_topk_8192": 813428879},
 }
 DECODE_SOURCES = ("decode_impl.h", "decode_inst.hip", "hkv_device.h", "hkv_internal.h")
 TRAFFIC_SOURCES = {"topk": ("topk.hip", "hkv_device.h", "hkv_internal.h"),
-                   "compact": ("compact.hip", "hkv_device.h", "hkv_internal.h")}  # every other leg: the decode's
+                   "compact": ("compact.hip", "hkv_device.h", "hkv_internal.h"),
+                   "prefill_llama8b_2048": ("append.hip", "hkv_device.h", "hkv_internal.h"),
+                   "prefill_topk_8192": ("append.hip", "hkv_device.h", "hkv_internal.h")}  # every other leg: the decode's
 
 
 def leg_sources(leg: str):
