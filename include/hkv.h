@@ -298,7 +298,11 @@ hkv_status hkv_decode_attn_noalloc(hkv_handle h, const hkv_cache_desc* c, const 
  *                 (position seq_len[b]) of every sequence.
  *   q, n_q_heads, out, lse, workspace, ws_bytes  as for hkv_decode_attn
  *                 (dense).
- * seq_len_dev and seq_len_host are incremented by one.
+ * seq_len_dev and seq_len_host are incremented by one.  With at most 256
+ * sequences the launch takes the lengths before the append from seq_len_host
+ * (copied into its arguments) and only writes seq_len_dev; with more it reads
+ * seq_len_dev.  Either way the two must hold the same lengths, as after every
+ * call of this library.
  *   HKV_ERR_CAPACITY: a sequence would need more than max_blocks_per_seq
  *     cold blocks.  HKV_ERR_INVALID_VALUE: n_q_heads not a multiple of
  *     n_kv_heads or a negative seq_len_host entry.  HKV_ERR_UNSUPPORTED: a

@@ -793,7 +793,8 @@ __device__ __forceinline__ int splits_of_pair(const DecodeParams& p, int units) 
 
 // ---- cold split: stream its units, merge the 4 waves, write the partial
 template <int D, int G, int BITS, int MODE, bool FUSED, bool CLAIM, bool STATS>
-__device__ __forceinline__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, int h, int bh, int split) {
+__device__ __forceinline__ void cold_split(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, int h, int bh, int split,
+                                           int n_host) {
   using C = Cfg<D, G>;
   constexpr int S = kBlockSize;
   constexpr int NG = C::NG;
@@ -817,8 +818,8 @@ __device__ __forceinline__ void cold_split(const DecodeParams& p, DecodeSmem<D, 
     qv[k] = ok ? v : u32x4_t{0u, 0u, 0u, 0u};
   }
   // needed only after the barrier: kept in a vector register, waited for there (issued before the
-  // tiles, so that wait does not include them)
-  const int n_seq_lane = c.seq_len[opaque_index(b)];
+  // tiles, so that wait does not include them); a fused step's length from the launch arguments
+  const int n_seq_lane = n_host >= 0 ? n_host : c.seq_len[opaque_index(b)];
   Tiles<D, BITS> t0;
   float2 sc0 = make_float2(0.f, 0.f);
   int phys0 = -1, hb = -1;
@@ -1146,7 +1147,7 @@ struct AppendSmem {
 };
 
 template <int D, int G, int BITS, bool STATS>
-__device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>& am, int b, int h, int bh) {
+__device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>& am, int b, int h, int bh, int n_host) {
   __builtin_amdgcn_s_setprio(3);  // the append's coding and its block's attention sit on the step's critical path
   using C = Cfg<D, G>;
   using F = Fmt<BITS>;
@@ -1168,7 +1169,8 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
   const int T = c.T, H = c.H;
   const int t = tid / TPT, part = tid % TPT;
   const size_t bhs = static_cast<size_t>(bh);
-  const int n0 = __builtin_amdgcn_readfirstlane(c.seq_len[b]);  // length before the append
+  // length before the append: from the launch arguments, else from seq_len
+  const int n0 = n_host >= 0 ? n_host : __builtin_amdgcn_readfirstlane(c.seq_len[b]);
   const bool spill = n0 >= T;
   const int ps = n0 - T;                   // the spilled token's position
   const int jt = spill ? ps / S : 0;
@@ -1480,7 +1482,7 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
 // whose loads are all in flight together; thread i owns two adjacent output columns of one query
 // head.
 template <int D, int G, int BITS, int MODE, bool FUSED, bool CLAIM, bool STATS>
-__device__ __forceinline__ void decode_body(const DecodeParams& p, const WgCoord wg) {
+__device__ __forceinline__ void decode_body(const DecodeParams& p, const WgCoord wg, const int32_t* n0h = nullptr) {
   using AppendPart = typename std::conditional<FUSED, AppendSmem<D, G, BITS>, DecodeSmem<D, G>>::type;
   __shared__ union Smem {
     DecodeSmem<D, G> cold;
@@ -1494,20 +1496,22 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, const WgCoord
   const int b = wg.z;
   const int bh = b * c.H + h;
   const int tid = threadIdx.x;
+  // a fused step's length before the append, from the launch arguments (-1: read seq_len)
+  const int n_host = FUSED && n0h != nullptr ? n0h[b] : -1;
   // phase timestamps: this workgroup's 8 slots, when asked for and inside the buffer
   const size_t stamp_wg = static_cast<size_t>(bh) * grid_parts(p) + split;
   unsigned long long* const st = p.stamps && stamp_wg < static_cast<size_t>(p.stamp_wgs) ? p.stamps + stamp_wg * 8 : nullptr;
   const unsigned long long t_start = st ? __builtin_amdgcn_s_memrealtime() : 0ull;
   if (split < p.nsplit) {
-    cold_split<D, G, BITS, MODE, FUSED, CLAIM, STATS>(p, sm.cold, b, h, bh, split);
+    cold_split<D, G, BITS, MODE, FUSED, CLAIM, STATS>(p, sm.cold, b, h, bh, split, n_host);
   } else if constexpr (FUSED) {
-    append_unit_split<D, G, BITS, STATS>(p, sm.app, b, h, bh);  // the hot window, then the append
+    append_unit_split<D, G, BITS, STATS>(p, sm.app, b, h, bh, n_host);  // the hot window, then the append
   } else {
     hot_split<D, G>(p, sm.hot, b, h, bh);
   }
   // this (sequence, kv-head)'s unit count, for the number of its cold splits (loaded with the wait
   // for the partial stores)
-  const int n_seq_lane = c.seq_len[opaque_index(b)];
+  const int n_seq_lane = n_host >= 0 ? n_host : c.seq_len[opaque_index(b)];
   const int count_lane = MODE == kModeStore ? p.store_counts[opaque_index(bh)] : 0;
   // ---- arrival: wait until this workgroup's partial stores are complete, count, and let the
   // last workgroup merge
@@ -1595,11 +1599,14 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, const WgCoord
                                   __HIP_MEMORY_SCOPE_AGENT);
   }
   if constexpr (FUSED) {
-    // every workgroup of (b, h) has read seq_len[b] before this merge; the last of the H merges
-    // of sequence b publishes the new length (and resets the counter)
-    if (tid == 0 &&
-        __hip_atomic_fetch_add(&p.seq_counters[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-            static_cast<unsigned>(c.H - 1)) {
+    if (n_host >= 0) {
+      // no workgroup of this launch reads seq_len: the kv-head 0 merge stores the new length
+      if (h == 0 && tid == 0) __hip_atomic_store(&c.seq_len[b], n_host + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else if (tid == 0 &&
+               __hip_atomic_fetch_add(&p.seq_counters[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   static_cast<unsigned>(c.H - 1)) {
+      // every workgroup of (b, h) has read seq_len[b] before this merge; the last of the H merges
+      // of sequence b publishes the new length (and resets the counter)
       __hip_atomic_store(&c.seq_len[b], c.seq_len[b] + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&p.seq_counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -1622,11 +1629,20 @@ constexpr int decode_waves() { return (G > 4 || BITS == 0) ? 2 : 4; }
 
 // STATS: the variant that also carries the entropy statistic (launched only when the cache view
 // asks for it, with a static plan); the others hold no register for it.
+// A fused step's launch arguments carry the lengths before the append (DecodeParamsFused).
+__device__ __forceinline__ const DecodeParams& params_of(const DecodeParams& p) { return p; }
+__device__ __forceinline__ const DecodeParams& params_of(const DecodeParamsFused& p) { return p.p; }
+__device__ __forceinline__ const int32_t* host_lens_of(const DecodeParams&) { return nullptr; }
+__device__ __forceinline__ const int32_t* host_lens_of(const DecodeParamsFused& p) {
+  return p.p.host_lens ? p.n0 : nullptr;
+}
+
 template <int D, int G, int BITS, int MODE, bool FUSED, bool CLAIM, bool STATS = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves<G, BITS>()))) void decode_kernel(
-    DecodeParams p) {
+    typename std::conditional<FUSED, DecodeParamsFused, DecodeParams>::type po) {
+  const DecodeParams& p = params_of(po);
   consume_args(p);
-  decode_body<D, G, BITS, MODE, FUSED, CLAIM, STATS>(p, wg_coord(p.wg_order));
+  decode_body<D, G, BITS, MODE, FUSED, CLAIM, STATS>(p, wg_coord(p.wg_order), host_lens_of(po));
 }
 
 // Batch plans: the same grid read in the host-built order of the table (see wg_coord_table); a kernel
@@ -1635,7 +1651,17 @@ template <int D, int G, int BITS, bool FUSED, bool CLAIM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves<G, BITS>()))) void
 decode_kernel_ordered(DecodeParamsOrdered po) {
   consume_args(po.p);
-  decode_body<D, G, BITS, kModeDense, FUSED, CLAIM, false>(po.p, wg_coord_table(po.order));
+  decode_body<D, G, BITS, kModeDense, FUSED, CLAIM, false>(po.p, wg_coord_table(po.order),
+                                                           FUSED && po.p.host_lens ? po.n0 : nullptr);
+}
+
+// The fused step's arguments: the parameters and, with p.host_lens, the host mirror's lengths.
+inline DecodeParamsFused fused_args(const DecodeParams& p) {
+  DecodeParamsFused f;
+  f.p = p;
+  std::memset(f.n0, 0, sizeof(f.n0));
+  if (p.host_lens) std::memcpy(f.n0, p.n0_host, sizeof(int32_t) * static_cast<size_t>(p.c.B));
+  return f;
 }
 
 template <typename K, typename P>
@@ -1652,9 +1678,11 @@ hipError_t launch_k(K kernel, dim3 grid, int block, const P& p, const LaunchCtx&
 template <int D, int G, int BITS>
 hipError_t launch_dg(const DecodeParams& p, const LaunchCtx& ctx, const uint16_t* order) {
   const dim3 grid(grid_parts(p), p.c.H, p.c.B);  // (split, kv-head, sequence)
+  if (p.host_lens && (p.c.B > kFusedLenMax || !p.n0_host || !p.k_new)) return hipErrorInvalidValue;
   if (p.c.entropy) {  // statistics: static plans in plain order only
     if (order || p.work || p.wg_order != kOrderPlain) return hipErrorInvalidValue;
-    if (p.k_new) return launch_k(decode_kernel<D, G, BITS, kModeDense, true, false, true>, grid, kThreads, p, ctx);
+    if (p.k_new)
+      return launch_k(decode_kernel<D, G, BITS, kModeDense, true, false, true>, grid, kThreads, fused_args(p), ctx);
     if (p.store_units_base)
       return launch_k(decode_kernel<D, G, BITS, kModeStore, false, false, true>, grid, kThreads, p, ctx);
     if (p.sel) return launch_k(decode_kernel<D, G, BITS, kModeGather, false, false, true>, grid, kThreads, p, ctx);
@@ -1666,6 +1694,8 @@ hipError_t launch_dg(const DecodeParams& p, const LaunchCtx& ctx, const uint16_t
     DecodeParamsOrdered po;
     po.p = p;
     std::memcpy(po.order, order, sizeof(po.order));
+    std::memset(po.n0, 0, sizeof(po.n0));
+    if (p.host_lens) std::memcpy(po.n0, p.n0_host, sizeof(int32_t) * static_cast<size_t>(p.c.B));
     if (p.work)
       return p.k_new ? launch_k(decode_kernel_ordered<D, G, BITS, true, true>, tgrid, kThreads, po, ctx)
                      : launch_k(decode_kernel_ordered<D, G, BITS, false, true>, tgrid, kThreads, po, ctx);
@@ -1673,8 +1703,8 @@ hipError_t launch_dg(const DecodeParams& p, const LaunchCtx& ctx, const uint16_t
                    : launch_k(decode_kernel_ordered<D, G, BITS, false, false>, tgrid, kThreads, po, ctx);
   }
   if (p.k_new)
-    return p.work ? launch_k(decode_kernel<D, G, BITS, kModeDense, true, true>, grid, kThreads, p, ctx)
-                  : launch_k(decode_kernel<D, G, BITS, kModeDense, true, false>, grid, kThreads, p, ctx);
+    return p.work ? launch_k(decode_kernel<D, G, BITS, kModeDense, true, true>, grid, kThreads, fused_args(p), ctx)
+                  : launch_k(decode_kernel<D, G, BITS, kModeDense, true, false>, grid, kThreads, fused_args(p), ctx);
   if (p.store_units_base) return launch_k(decode_kernel<D, G, BITS, kModeStore, false, false>, grid, kThreads, p, ctx);
   if (p.sel) return launch_k(decode_kernel<D, G, BITS, kModeGather, false, false>, grid, kThreads, p, ctx);
   return p.work ? launch_k(decode_kernel<D, G, BITS, kModeDense, false, true>, grid, kThreads, p, ctx)

@@ -674,6 +674,9 @@ hkv_status hkv_append_decode(hkv_handle h, const hkv_cache_desc* c, const void* 
     p.work = sp.claim ? claim_counters(workspace, c, h->H) : nullptr;
     p.k_new = static_cast<const _Float16*>(k_new);  // (before the order table: it counts the workgroups from them)
     p.v_new = static_cast<const _Float16*>(v_new);
+    // lengths before the append from the host mirror, in the launch arguments (up to kFusedLenMax sequences)
+    p.host_lens = c->batch <= hkv::kFusedLenMax ? 1 : 0;
+    p.n0_host = c->seq_len_host;
     uint16_t order[hkv::kOrderTableMax];
     const bool ordered = sp.batch && order_by_work(p, units, sp.per_split, order);
     if (ordered) p.wg_order = hkv::kOrderTable;

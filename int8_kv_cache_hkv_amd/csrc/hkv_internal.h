@@ -84,6 +84,12 @@ struct DecodeParams {
   const _Float16* k_new;   // [B][H][D]
   const _Float16* v_new;   // [B][H][D]
   unsigned* seq_counters;  // [B] merged-head counters, zero between calls
+  // fused step of at most kFusedLenMax sequences: the lengths before the append travel in the launch
+  // arguments (DecodeParamsFused::n0, DecodeParamsOrdered::n0), so no workgroup reads seq_len and
+  // one plain store per sequence publishes the new length.  0: seq_len is read, and the last of the
+  // H merges of a sequence publishes it (seq_counters).
+  int host_lens;
+  const int32_t* n0_host;  // host side only: the host mirror the launch copies into n0 (never read on the GPU)
   // decode over a compacted sparse store (CompactParams layout); store_units_base nullptr otherwise
   const int8_t* store_units_base;
   const float2* store_scales;
@@ -110,11 +116,21 @@ struct CompactParams {
 // append + decode's last workgroup attends the hot window and the tail block, two records.
 __host__ __device__ inline int grid_parts(const DecodeParams& p) { return p.nparts - (p.k_new ? 1 : 0); }
 
+// Sequences whose lengths a fused step takes from its launch arguments (see DecodeParams::host_lens).
+constexpr int kFusedLenMax = 256;
+
+// Arguments of the fused one-token append + decode in the plain, split-major and claim orders.
+struct DecodeParamsFused {
+  DecodeParams p;
+  int32_t n0[kFusedLenMax];  // the cached length of each sequence before the append (p.host_lens)
+};
+
 // Arguments of the table-ordered decode launch (batch plans): the (sequence << 7 | part) groups
-// of the grid in dispatch order, [B * grid_parts] entries used.
+// of the grid in dispatch order, [B * grid_parts] entries used; and, for a fused step, the lengths.
 struct DecodeParamsOrdered {
   DecodeParams p;
   uint16_t order[kOrderTableMax];
+  int32_t n0[kFusedLenMax];  // the cached length of each sequence before the append (p.host_lens)
 };
 
 // Cold splits of one (sequence, kv-head) in a table-ordered launch: enough splits of units_per_split

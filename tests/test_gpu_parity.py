@@ -229,6 +229,33 @@ def test_append_decode_ragged_steps():
         gh.compare_out(out[seqs], o_ref, f"fused ragged step {step}")
 
 
+@pytest.mark.parametrize("batch", [256, 260])
+def test_append_decode_length_protocols(batch):
+    """Fused steps over 256 sequences (lengths from the launch arguments, one store per sequence
+    publishes the new length) and over 260 (more than the launch arguments hold: seq_len read on the
+    device, the last of the H merges of a sequence publishes it).  Three steps; after each, every
+    device length is the host mirror's, and sampled sequences' outputs and cache state equal the
+    oracle's."""
+    import dataclasses
+    w = dataclasses.replace(wl.WORKLOADS["tiny"], batch=batch)
+    lens = [20 + (37 * b) % 380 for b in range(batch)]
+    cache = gh.make_cache(w, 460, batch=batch)
+    gh.fill(cache, w, lens)
+    watch = [0, 1, batch // 2, batch - 1]
+    for step in range(3):
+        cur = [n + step for n in lens]
+        q = wl.queries(w, step=step)
+        out, lse = _append_decode(cache, w, cur, q)
+        assert cache.seq_len.cpu().numpy().tolist() == [n + 1 for n in cur]
+        assert cache.seq_len_host.tolist() == [n + 1 for n in cur]
+        st = _oracle_states(w, [cur[b] + 1 for b in watch], watch)
+        gh.check_state(cache, st, watch)
+        for b, s in zip(watch, st):
+            o_ref, l_ref = orc.decode(q[b], s)
+            gh.compare_out(out[b], o_ref, f"fused batch {batch} step {step} seq {b}")
+            gh.compare_lse(lse[b], l_ref, f"fused batch {batch} step {step} seq {b}")
+
+
 def test_append_decode_equals_separate_calls():
     """The fused step leaves the same cache bytes as hkv_append + hkv_decode_attn, and the outputs
     agree (different split plans: equal to the tolerance, not bitwise)."""
