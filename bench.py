@@ -54,8 +54,8 @@ OUT_MAX_ABS, OUT_MEAN_ABS = 4e-3, 5e-4
 # of its leg (TRAFFIC_SOURCES) as they were when it was taken: it is reported as null once their code
 # changes (the hash skips comments and blank lines).
 COUNTER_TRAFFIC = {
-    "sources_sha256": {"llama8b": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "long": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "llama8b_b4": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "long_b4": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "llama8b_b0": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "long_b0": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "topk": "534261211f52f58f2d73383954ff1c33bf147c2793f3c6e556f6eb451c93210f", "sparse_decode": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "store_decode": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "compact": "309892a2957f1162f4cc9fd38f16e916f346bed68dfd667b08dd4cdac4f49fcb", "ragged": "6909d421f448412c9b9bc76aba239b9ea2cbce69677fc410a08b2b4e86119897", "prefill_llama8b_2048": "1849120482a7a5e0327f945a629f056c8cdca38fce2eeef8dd067598123355ac", "prefill_topk_8192": "1849120482a7a5e0327f945a629f056c8cdca38fce2eeef8dd067598123355ac"},
-    "bytes_per_launch": {"llama8b": 36969045, "long": 1084465875, "llama8b_b4": 20720522, "long_b4": 550185679, "llama8b_b0": 69422932, "long_b0": 2157503970, "topk": 564694298, "sparse_decode": 190047706, "store_decode": 21981749, "compact": 197186063, "ragged": 615006679, "prefill_llama8b_2048": 104263610, "prefill_topk_8192": 813428879},
+    "sources_sha256": {"llama8b": "4f4d7bc6d7bc6cb87d429b5619e9333fe9740c551d48b195be6460fd3fa5e984", "long": "4f4d7bc6d7bc6cb87d429b5619e9333fe9740c551d48b195be6460fd3fa5e984", "llama8b_b4": "4f4d7bc6d7bc6cb87d429b5619e9333fe9740c551d48b195be6460fd3fa5e984", "long_b4": "4f4d7bc6d7bc6cb87d429b5619e9333fe9740c551d48b195be6460fd3fa5e984", "llama8b_b0": "4f4d7bc6d7bc6cb87d429b5619e9333fe9740c551d48b195be6460fd3fa5e984", "long_b0": "4f4d7bc6d7bc6cb87d429b5619e9333fe9740c551d48b195be6460fd3fa5e984", "topk": "02a61cec163e2924c36c95405f44d8d011479325de142a67de5bfff98cb20fe4", "sparse_decode": "4f4d7bc6d7bc6cb87d429b5619e9333fe9740c551d48b195be6460fd3fa5e984", "store_decode": "4f4d7bc6d7bc6cb87d429b5619e9333fe9740c551d48b195be6460fd3fa5e984", "compact": "2b84f9ff4339ac7ae62a6bda8aea558587932f6f19226f25379245c179982a66", "ragged": "4f4d7bc6d7bc6cb87d429b5619e9333fe9740c551d48b195be6460fd3fa5e984", "prefill_llama8b_2048": "3de7b2224ac5f3057f86e618740833cc1d89ee79847b06a46e2232fad843bdc8", "prefill_topk_8192": "3de7b2224ac5f3057f86e618740833cc1d89ee79847b06a46e2232fad843bdc8"},
+    "bytes_per_launch": {"llama8b": 36966804, "long": 1084457679, "llama8b_b4": 20706527, "long_b4": 550214090, "llama8b_b0": 69419797, "long_b0": 2157515261, "topk": 564696698, "sparse_decode": 190053162, "store_decode": 21981691, "compact": 197185451, "ragged": 614997043, "prefill_llama8b_2048": 104263610, "prefill_topk_8192": 813428879},
 }
 DECODE_SOURCES = ("decode_impl.h", "decode_inst.hip", "hkv_device.h", "hkv_internal.h")
 TRAFFIC_SOURCES = {"topk": ("topk.hip", "hkv_device.h", "hkv_internal.h"),
