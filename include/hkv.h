@@ -99,9 +99,11 @@ typedef struct {
  *            (k*S + t)*16.  V tiles: chunk (v, c) = tokens E*v .. E*v+E-1 of
  *            channel c, at byte (v*d + c)*16.  Element e of a chunk is byte e
  *            (8-bit code + 128, so code -127..127 is stored 1..255 and code 0
- *            as 0x80), the half-byte e%2 (low first) of byte e/2 (4-bit code
- *            + 8, so code -7..7 is stored 1..15) or the fp16 at bytes 2e,
- *            2e+1.  Rows t >= n_valid hold code 0 (value 0).
+ *            as 0x80), a half-byte (4-bit code + 8, so code -7..7 is stored
+ *            1..15; each 32-bit word of a chunk holds elements 8j..8j+3 in
+ *            the low half-bytes of its bytes 0..3 and 8j+4..8j+7 in the high
+ *            ones) or the fp16 at bytes 2e, 2e+1.  Rows t >= n_valid hold
+ *            code 0 (value 0).
  *   scales   fp32 [P][H][2]  (K scale, V scale).
  *   headers  hkv_block_header [batch][max_blocks_per_seq].
  *   seq_len_dev   int32 [batch] device: tokens cached per sequence.

@@ -404,10 +404,11 @@ class HybridKVCache:
         if self.quant_bits == 0:
             return raw.view(np.float16)
         u = raw.view(np.uint8)
-        out = np.empty(u.shape[:-1] + (u.shape[-1] * 2,), dtype=np.int8)
-        out[..., 0::2] = (u & 0x0F).astype(np.int8) - 8   # offset binary: element 2i in the low nibble
-        out[..., 1::2] = (u >> 4).astype(np.int8) - 8
-        return out
+        w = u.reshape(u.shape[:-1] + (u.shape[-1] // 4, 4))  # 32-bit words of four bytes
+        out = np.empty(w.shape[:-1] + (8,), dtype=np.int8)
+        out[..., :4] = (w & 0x0F).astype(np.int8) - 8  # offset binary, planar: elements 8j..8j+3 low nibbles
+        out[..., 4:] = (w >> 4).astype(np.int8) - 8    # elements 8j+4..8j+7: the high nibbles
+        return out.reshape(u.shape[:-1] + (u.shape[-1] * 2,))
 
     def _tiles_to_rows(self, tiles: np.ndarray) -> np.ndarray:
         """[N, 2, TB] tile bytes of (block, kv-head) pairs -> [N, 2, S, D] codes (token, channel order)."""

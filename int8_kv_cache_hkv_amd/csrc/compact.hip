@@ -141,11 +141,11 @@ __global__ __launch_bounds__(kCompactThreads) void sparse_compact_kernel(Compact
       if (ph >= 0) {
         const int8_t* vt = c.cold + tile_offset(ph, h, 1, H, TB) + ((t / E) * D + ch) * 16;
         if constexpr (BITS == 8) x = static_cast<uint8_t>(vt[t % E]);
-        else if constexpr (BITS == 4) x = (static_cast<uint8_t>(vt[(t % E) / 2]) >> (4 * (t & 1))) & 0xFu;
+        else if constexpr (BITS == 4) x = (static_cast<uint8_t>(vt[nib_byte(t % E)]) >> nib_shift(t % E)) & 0xFu;
         else x = *reinterpret_cast<const uint16_t*>(vt + (t % E) * 2);
       }
       if constexpr (BITS == 8) w[e / 4] |= x << (8 * (e % 4));
-      else if constexpr (BITS == 4) w[e / 8] |= x << (4 * (e % 8));
+      else if constexpr (BITS == 4) w[e / 8] |= x << (8 * (e & 3) + nib_shift(e));  // planar word (nib_byte)
       else w[e / 2] |= x << (16 * (e % 2));
     }
     reinterpret_cast<uint4*>(dst + TB)[vi] = make_uint4(w[0], w[1], w[2], w[3]);

@@ -602,12 +602,12 @@ __device__ __forceinline__ uint32_t v_element(__amdgpu_buffer_rsrc_t r, int tt, 
   constexpr int E = F::kElems;
   const int chunk = TB + ((tt / E) * D + c) * 16;
   if constexpr (BITS == 8) return __builtin_amdgcn_raw_buffer_load_b8(r, chunk + tt % E, 0, 0);
-  else if constexpr (BITS == 4) return __builtin_amdgcn_raw_buffer_load_b8(r, chunk + (tt % E) / 2, 0, 0);
+  else if constexpr (BITS == 4) return __builtin_amdgcn_raw_buffer_load_b8(r, chunk + nib_byte(tt % E), 0, 0);
   else return __builtin_amdgcn_raw_buffer_load_b16(r, chunk + (tt % E) * 2, 0, 0);
 }
 
 // Exact PV operand of four gathered tokens from their value elements (v_element of each, and for
-// 4-bit tiles the token index, whose parity names the nibble).
+// 4-bit tiles the token index, which names the nibble of the loaded byte).
 template <int BITS>
 __device__ __forceinline__ half4_t gathered_operand(const uint32_t (&e)[4], const int (&tt)[4]) {
   if constexpr (BITS == 8) {
@@ -615,7 +615,7 @@ __device__ __forceinline__ half4_t gathered_operand(const uint32_t (&e)[4], cons
   } else if constexpr (BITS == 4) {
     uint32_t n[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) n[i] = (e[i] >> (4 * (tt[i] & 1))) & 0xFu;
+    for (int i = 0; i < 4; ++i) n[i] = (e[i] >> nib_shift(tt[i] % Fmt<4>::kElems)) & 0xFu;
     const half2_t off = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
     const half2_t a = __builtin_bit_cast(half2_t, 0x64006400u | n[0] | (n[1] << 16)) - off;
     const half2_t b = __builtin_bit_cast(half2_t, 0x64006400u | n[2] | (n[3] << 16)) - off;
@@ -1326,7 +1326,7 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
       if (!whole[kv]) {
         if constexpr (BITS != 8) {
           // only row ts changes: its K chunks, and per channel the V bytes that hold it (4-bit: the
-          // byte shared with row ts ^ 1, rewritten from the stage)
+          // byte it shares with row ts + 4 or ts - 4 of its chunk word, rewritten from the stage)
           if (kv == 0) {
             if (tid < D / E)
               reinterpret_cast<uint4*>(tile)[tid * S + ts] = chunk_from_stage<BITS>(am.stage.k + ts * KROW + tid * E * EB);
@@ -1334,8 +1334,9 @@ __device__ void append_unit_split(const DecodeParams& p, AppendSmem<D, G, BITS>&
             const int8_t* col = am.stage.v + tid * VROW;
             int8_t* chunk = tile + ((ts / E) * D + tid) * 16;
             if constexpr (BITS == 4) {
-              const int t2 = ts & ~1;
-              chunk[(ts % E) / 2] = static_cast<int8_t>(((col[t2] & 0xF) ^ 8) | (((col[t2 + 1] & 0xF) ^ 8) << 4));
+              const int r = ts % E;
+              const int lo = ts - r + (r >> 3) * 8 + (r & 3);  // the byte's low-nibble row; its high one is lo + 4
+              chunk[nib_byte(r)] = static_cast<int8_t>(((col[lo] & 0xF) ^ 8) | (((col[lo + 4] & 0xF) ^ 8) << 4));
             } else {
               *reinterpret_cast<uint16_t*>(chunk + (ts % E) * 2) = *reinterpret_cast<const uint16_t*>(col + 2 * ts);
             }

@@ -329,8 +329,8 @@ constexpr float kCodeBias = 1152.0f;
 // wave load gives every lane its MFMA operand:
 //   K tile: chunk (kc, t) at byte (kc * S + t) * 16 holds channels [kc * E, kc * E + E) of token t;
 //   V tile: chunk (vc, c) at byte (vc * D + c) * 16 holds tokens [vc * E, vc * E + E) of channel c;
-// E = elements per chunk (16, 32 or 8).  Element e of a chunk is byte e (8-bit, two's complement),
-// the nibble e % 2 (0 = low) of byte e / 2 holding code + 8 (4-bit, offset binary: code 0 is 8), or
+// E = elements per chunk (16, 32 or 8).  Element e of a chunk is byte e (8-bit, offset binary), a
+// nibble holding code + 8 (4-bit, offset binary, code 0 is 8; planar per word: see nib_byte), or
 // bytes 2e, 2e + 1 (fp16).  An FP16 tile's scale is stored as 1.
 template <int BITS>
 struct Fmt {
@@ -347,14 +347,11 @@ struct Fmt {
   static constexpr int tile_bytes() { return BITS == 0 ? 64 * D * 2 : 64 * D * BITS / 8; }
 };
 
-// 4-bit codes: elements 2i and 2i + 1 of a word (offset-binary nibbles) as the fp16 pair
-// (1024 + nibble): the nibbles are split into byte lanes, a byte permute places one of each under
-// the exponent of 1024.  Every step is exact.
-__device__ __forceinline__ uint32_t nib_pair(uint32_t lo, uint32_t hi, int i) {
-  // lo = even elements (bytes 0..3), hi = odd elements; selector bytes: lo.b_i, 0, hi.b_i, 0
-  const uint32_t sel = 0x0C000C00u | (static_cast<uint32_t>(4 + i) << 16) | static_cast<uint32_t>(i);
-  return __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u;
-}
+// 4-bit chunks are planar per 32-bit word: word j holds elements 8j..8j+3 in the low nibbles of its
+// bytes 0..3 and elements 8j+4..8j+7 in the high nibbles (offset binary, code + 8).  Byte and shift of
+// element r of a chunk:
+__device__ __forceinline__ int nib_byte(int r) { return (r >> 3) * 4 + (r & 3); }
+__device__ __forceinline__ int nib_shift(int r) { return ((r >> 2) & 1) * 4; }
 
 // MFMA operand `step` (4 consecutive elements) of a 16-byte chunk, as fp16 values: biased
 // (code + kBias, the QK operand) or exact (the code itself, the PV operand).  fp16 tiles give the
@@ -364,11 +361,12 @@ __device__ __forceinline__ half4_t chunk_operand(const uint4& ck, int step) {
   if constexpr (BITS == 8) {
     return BIASED ? codes_to_biased_half4(word_of(ck, step)) : codes_to_half4(word_of(ck, step));
   } else if constexpr (BITS == 4) {
+    // the step's four nibbles, one per byte (the low half of its word, or the high half), each
+    // placed under the fp16 exponent of 1024 by one byte permute: 1024 + nibble, exact
     const uint32_t w = word_of(ck, step >> 1);
-    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-    const int p = (step & 1) * 2;  // element pairs 2p, 2p + 1 of the word
-    half2_t a = __builtin_bit_cast(half2_t, nib_pair(lo, hi, p));
-    half2_t b = __builtin_bit_cast(half2_t, nib_pair(lo, hi, p + 1));
+    const uint32_t n = ((step & 1) ? (w >> 4) : w) & 0x0F0F0F0Fu;
+    half2_t a = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, n, 0x04010400u));
+    half2_t b = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, n, 0x04030402u));
     if (!BIASED) {
       const half2_t off = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
       a = a - off;
@@ -385,14 +383,12 @@ __device__ __forceinline__ float4_t mfma_qk(half4_t a, half4_t b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c, 0, 0, 0);
 }
 
-// 4-bit tiles: eight int8 codes (x0: elements 0..3, x1: 4..7) as one word of offset-binary nibbles
-// (element e in nibble e).  (c & 15) ^ 8 = c + 8 for c in [-7, 7].
+// 4-bit tiles: eight int8 codes (x0: elements 0..3, x1: 4..7) as one planar word of offset-binary
+// nibbles (elements 0..3 low, 4..7 high).  (c & 15) ^ 8 = c + 8 for c in [-7, 7].
 __device__ __forceinline__ uint32_t pack_nib8(uint32_t x0, uint32_t x1) {
-  uint32_t a = (x0 & 0x0F0F0F0Fu) ^ 0x08080808u;
-  uint32_t b = (x1 & 0x0F0F0F0Fu) ^ 0x08080808u;
-  a |= a >> 4;  // byte 0 = e0 | e1 << 4, byte 2 = e2 | e3 << 4
-  b |= b >> 4;
-  return __builtin_amdgcn_perm(b, a, 0x06040200u);
+  const uint32_t a = (x0 & 0x0F0F0F0Fu) ^ 0x08080808u;
+  const uint32_t b = (x1 & 0x0F0F0F0Fu) ^ 0x08080808u;
+  return a | (b << 4);
 }
 
 // A 16-byte tile chunk from 16 bytes of stage (8-bit codes or fp16 values), or from 32 code bytes
