@@ -54,8 +54,8 @@ OUT_MAX_ABS, OUT_MEAN_ABS = 4e-3, 5e-4
 # of its leg (TRAFFIC_SOURCES) as they were when it was taken: it is reported as null once their code
 # changes (the hash skips comments and blank lines).
 COUNTER_TRAFFIC = {
-    "sources_sha256": {"llama8b": "4f4d7bc6d7bc6cb87d429b5619e9333fe9740c551d48b195be6460fd3fa5e984", "long": "4f4d7bc6d7bc6cb87d429b5619e9333fe9740c551d48b195be6460fd3fa5e984", "llama8b_b4": "4f4d7bc6d7bc6cb87d429b5619e9333fe9740c551d48b195be6460fd3fa5e984", "long_b4": "4f4d7bc6d7bc6cb87d429b5619e9333fe9740c551d48b195be6460fd3fa5e984", "llama8b_b0": "4f4d7bc6d7bc6cb87d429b5619e9333fe9740c551d48b195be6460fd3fa5e984", "long_b0": "4f4d7bc6d7bc6cb87d429b5619e9333fe9740c551d48b195be6460fd3fa5e984", "topk": "02a61cec163e2924c36c95405f44d8d011479325de142a67de5bfff98cb20fe4", "sparse_decode": "4f4d7bc6d7bc6cb87d429b5619e9333fe9740c551d48b195be6460fd3fa5e984", "store_decode": "4f4d7bc6d7bc6cb87d429b5619e9333fe9740c551d48b195be6460fd3fa5e984", "compact": "2b84f9ff4339ac7ae62a6bda8aea558587932f6f19226f25379245c179982a66", "ragged": "4f4d7bc6d7bc6cb87d429b5619e9333fe9740c551d48b195be6460fd3fa5e984", "prefill_llama8b_2048": "3de7b2224ac5f3057f86e618740833cc1d89ee79847b06a46e2232fad843bdc8", "prefill_topk_8192": "3de7b2224ac5f3057f86e618740833cc1d89ee79847b06a46e2232fad843bdc8"},
-    "bytes_per_launch": {"llama8b": 36966804, "long": 1084457679, "llama8b_b4": 20706527, "long_b4": 550214090, "llama8b_b0": 69419797, "long_b0": 2157515261, "topk": 564696698, "sparse_decode": 190053162, "store_decode": 21981691, "compact": 197185451, "ragged": 614997043, "prefill_llama8b_2048": 104263610, "prefill_topk_8192": 813428879},
+    "sources_sha256": {"llama8b": "df1d5fd6934c5805b1f1ad65777e7953bc9a2b2798f937bb2d5a7558113c95e4", "long": "df1d5fd6934c5805b1f1ad65777e7953bc9a2b2798f937bb2d5a7558113c95e4", "llama8b_b4": "df1d5fd6934c5805b1f1ad65777e7953bc9a2b2798f937bb2d5a7558113c95e4", "long_b4": "df1d5fd6934c5805b1f1ad65777e7953bc9a2b2798f937bb2d5a7558113c95e4", "llama8b_b0": "df1d5fd6934c5805b1f1ad65777e7953bc9a2b2798f937bb2d5a7558113c95e4", "long_b0": "df1d5fd6934c5805b1f1ad65777e7953bc9a2b2798f937bb2d5a7558113c95e4", "topk": "62eb10d33fdf6c96b429254db587551a5e91998f27246dd46b3cd2ac50126a01", "sparse_decode": "df1d5fd6934c5805b1f1ad65777e7953bc9a2b2798f937bb2d5a7558113c95e4", "store_decode": "df1d5fd6934c5805b1f1ad65777e7953bc9a2b2798f937bb2d5a7558113c95e4", "compact": "007daedc824d3cb9f0c303032b422ca46b003c982428164f9ac3431f9372d8dd", "ragged": "df1d5fd6934c5805b1f1ad65777e7953bc9a2b2798f937bb2d5a7558113c95e4", "prefill_llama8b_2048": "2c996c5f09aca7d5a41e5a7a45a55369573911e03a0fa14df5aee485f255e499", "prefill_topk_8192": "2c996c5f09aca7d5a41e5a7a45a55369573911e03a0fa14df5aee485f255e499"},
+    "bytes_per_launch": {"llama8b": 36967184, "long": 1084456822, "llama8b_b4": 20697970, "long_b4": 550093287, "llama8b_b0": 69420240, "long_b0": 2157511408, "topk": 564698199, "sparse_decode": 190047974, "store_decode": 21981710, "compact": 197185700, "ragged": 614997161, "prefill_llama8b_2048": 104263619, "prefill_topk_8192": 813428927},
 }
 DECODE_SOURCES = ("decode_impl.h", "decode_inst.hip", "hkv_device.h", "hkv_internal.h")
 TRAFFIC_SOURCES = {"topk": ("topk.hip", "hkv_device.h", "hkv_internal.h"),
