@@ -315,8 +315,8 @@ unsigned* claim_counters(void* workspace, const hkv_cache_desc* c, int H) {
 }
 
 // Top-K workspace after the counters: window probabilities [B][H][max_blocks * S] fp32, window tops
-// [B][H][max_blocks] (32 bytes each) and their lanes [B][H][max_blocks] (8 bytes each), every area
-// 256-byte aligned.
+// [B][H][max_blocks] (kWinTop keys of 4 bytes) and their lanes [B][H][max_blocks] (one byte per
+// top), every area 256-byte aligned.
 struct TopkLayout {
   size_t wtop_off, wlane_off, bytes;  // offsets from the start of the probabilities
 };
@@ -325,8 +325,8 @@ TopkLayout topk_layout(const hkv_ctx* h, const hkv_cache_desc* c) {
   const size_t mb = static_cast<size_t>(std::max(0, c->max_blocks_per_seq));
   TopkLayout l;
   l.wtop_off = align_up(bh * mb * h->S * sizeof(float), 256);
-  l.wlane_off = l.wtop_off + align_up(bh * mb * 32, 256);
-  l.bytes = l.wlane_off + bh * mb * 8;
+  l.wlane_off = l.wtop_off + align_up(bh * mb * 4 * hkv::kWinTop, 256);
+  l.bytes = l.wlane_off + bh * mb * hkv::kWinTop;
   return l;
 }
 size_t topk_bytes(const hkv_ctx* h, const hkv_cache_desc* c) { return topk_layout(h, c).bytes; }
@@ -813,7 +813,7 @@ hkv_status hkv_topk_select(hkv_handle h, const hkv_cache_desc* c, const void* q,
     char* const area = static_cast<char*>(workspace) + align_up(counters_bytes(c, h->H), 256);
     p.prob = reinterpret_cast<float*>(area);
     p.wtop = reinterpret_cast<uint4*>(area + tl.wtop_off);
-    p.wlane = reinterpret_cast<uint2*>(area + tl.wlane_off);
+    p.wlane = reinterpret_cast<uint32_t*>(area + tl.wlane_off);
     // the score kernel holds at most 64 VGPRs per lane (D = 128, G <= 4), so 8 of its workgroups fit a
     // CU: twice the decode's grid; its claim plans take 4 per CU (32768-token workload, measured:
     // static splits 98.6 us, claims on 512 / 1024 / 2048 workgroups 98.5 / 91.3 / 92.7 us)

@@ -144,7 +144,7 @@ __host__ __device__ inline int table_splits(int nsplit, int units_per_split, int
 // Top-K selection (topk.hip): the score kernel keeps the kWinTop largest keys of every window and
 // their lanes; one kSelThreads-thread workgroup per row selects from those (rows of up to
 // kTopsWindows windows), staging at most kFinalKeys candidates.
-constexpr int kWinTop = 8;
+constexpr int kWinTop = 4;
 constexpr int kSelThreads = 512;
 constexpr int kFinalKeys = 4096;
 constexpr int kDirectKeys = 8192;    // rows of at most this many keys are selected from the row itself
@@ -155,9 +155,9 @@ struct TopkParams {
   int G;
   const _Float16* q;       // [B][H*G][D]
   float* prob;             // [B][H][max_blocks*S] window probabilities
-  uint4* wtop;             // [B][H][max_blocks][2] each window's kWinTop largest keys, in lane order
+  uint4* wtop;             // [B][H][max_blocks] each window's kWinTop largest keys, in lane order
                            //   (fp32 bits + 1; 0 = none)
-  uint2* wlane;            // [B][H][max_blocks] their lanes in the window, 8 bits each
+  uint32_t* wlane;         // [B][H][max_blocks] their lanes in the window, 8 bits each
   int nsplit;
   int units_per_split;
   int wg_order;            // kOrderPlain / kOrderSplitMajor / kOrderTable (see wg_coord)

@@ -131,32 +131,32 @@ __device__ __forceinline__ unsigned wave_max_u32(unsigned x) {
   return max(max(a, b), max(c, d));
 }
 struct WinTop {
-  uint4 k0, k1;  // keys of the 8 lanes, in lane order
-  uint2 lanes;   // those lanes, 8 bits apiece (lanes of k0 in .x, of k1 in .y)
+  uint4 k;         // keys of the kWinTop lanes, in lane order
+  uint32_t lanes;  // those lanes, 8 bits apiece
 };
-__device__ __forceinline__ WinTop wave_top8(unsigned key, int lane) {
-  static_assert(kWinTop == 8, "eight keys per window");
+__device__ __forceinline__ WinTop wave_top(unsigned key, int lane) {
+  static_assert(kWinTop == 4, "four keys per window");
   const unsigned orig = key;
   bool taken = false;
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
+  for (int r = 0; r < kWinTop; ++r) {
     const unsigned m = wave_max_u32(key);
-    const uint64_t hit = __ballot(key == m && !taken);  // never empty: 64 > 8 lanes
+    const uint64_t hit = __ballot(key == m && !taken);  // never empty: 64 > kWinTop lanes
     if (lane == static_cast<int>(__builtin_ctzll(hit))) {
       key = 0u;
       taken = true;
     }
   }
-  uint64_t mask = __ballot(taken);  // exactly 8 lanes
-  unsigned t[8], ln[2] = {0u, 0u};
+  uint64_t mask = __ballot(taken);  // exactly kWinTop lanes
+  unsigned t[kWinTop], ln = 0u;
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
+  for (int r = 0; r < kWinTop; ++r) {
     const int l = static_cast<int>(__builtin_ctzll(mask));
     mask &= mask - 1;
     t[r] = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(orig), l));
-    ln[r / 4] |= static_cast<unsigned>(l) << (8 * (r % 4));
+    ln |= static_cast<unsigned>(l) << (8 * r);
   }
-  return {make_uint4(t[0], t[1], t[2], t[3]), make_uint4(t[4], t[5], t[6], t[7]), make_uint2(ln[0], ln[1])};
+  return {make_uint4(t[0], t[1], t[2], t[3]), ln};
 }
 
 // Grid (split, kv-head, sequence).  Each wave walks its cold blocks (the same
@@ -173,9 +173,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BITS =
   __shared__ float qinv[4 * NQ];           // 1 / |q_g| (0 for a zero query or a padding row)
   __shared__ float pstage[CLAIM ? kWaves : 1][CLAIM ? kStage : 1][64];  // claim walk: staged window probabilities
   __shared__ int ustage[CLAIM ? kWaves : 1][CLAIM ? kStage : 1];
-  // claim walk: staged window tops, 40 bytes apiece (8 keys, 8 lanes), so that four workgroups
-  // still fit a CU's LDS
-  __shared__ uint2 tstage[CLAIM ? kWaves : 1][CLAIM ? kStage : 1][5];
+  // claim walk: staged window tops, 20 bytes apiece (kWinTop keys and their lanes), so that four
+  // workgroups still fit a CU's LDS
+  __shared__ uint4 tstage[CLAIM ? kWaves : 1][CLAIM ? kStage : 1];     // ... their window tops
+  __shared__ uint32_t lstage[CLAIM ? kWaves : 1][CLAIM ? kStage : 1];  // ... and those tops' lanes
   asm volatile("" ::"s"(p.c.H), "s"(p.c.T), "s"(p.c.max_blocks), "s"(p.c.num_phys), "s"(p.c.cold),
                "s"(p.c.headers), "s"(p.c.seq_len), "s"(p.q), "s"(p.prob), "s"(p.nsplit), "s"(p.units_per_split),
                "s"(p.wg_order), "s"(p.work));
@@ -227,8 +228,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BITS =
   const int units = min(sg.n_blk, c.max_blocks);
   const size_t cap = static_cast<size_t>(c.max_blocks) * S;
   float* prob = p.prob + static_cast<size_t>(bh) * cap;
-  uint4* wtop = p.wtop + static_cast<size_t>(bh) * c.max_blocks * 2;  // per window: its kWinTop largest keys + 1
-  uint2* wlane = p.wlane + static_cast<size_t>(bh) * c.max_blocks;     // ... and their lanes
+  uint4* wtop = p.wtop + static_cast<size_t>(bh) * c.max_blocks;         // per window: its kWinTop largest keys + 1
+  uint32_t* wlane = p.wlane + static_cast<size_t>(bh) * c.max_blocks;    // ... and their lanes
   if constexpr (CLAIM) {
     // Claim walk (see the decode's): the first unit is split * 4 + w, then units nsplit * 4 + claim.
     // A unit's chain is claim -> header -> tiles, each given a whole unit of time: at the start of
@@ -252,10 +253,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BITS =
       for (int k = 0; k < nst; ++k) {
         prob[static_cast<size_t>(ustage[w][k]) * S + lane] = pstage[w][k][lane];
         if (lane == 0) {
-          const uint2* t8 = tstage[w][k];
-          wtop[2 * ustage[w][k]] = make_uint4(t8[0].x, t8[0].y, t8[1].x, t8[1].y);
-          wtop[2 * ustage[w][k] + 1] = make_uint4(t8[2].x, t8[2].y, t8[3].x, t8[3].y);
-          wlane[ustage[w][k]] = t8[4];
+          wtop[ustage[w][k]] = tstage[w][k];
+          wlane[ustage[w][k]] = lstage[w][k];
         }
       }
       nst = 0;
@@ -273,14 +272,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BITS =
       // attended); lanes past the last cold token write row entries the selection never reads
       const float pv = phys >= 0 && lane < nv ? pr : 0.f;
       pstage[w][nst][lane] = pv;
-      const WinTop t8 = wave_top8(lane < nv ? __builtin_bit_cast(unsigned, pv) + 1u : 0u, lane);
+      const WinTop tt = wave_top(lane < nv ? __builtin_bit_cast(unsigned, pv) + 1u : 0u, lane);
       if (lane == 0) {
         ustage[w][nst] = u;
-        tstage[w][nst][0] = make_uint2(t8.k0.x, t8.k0.y);
-        tstage[w][nst][1] = make_uint2(t8.k0.z, t8.k0.w);
-        tstage[w][nst][2] = make_uint2(t8.k1.x, t8.k1.y);
-        tstage[w][nst][3] = make_uint2(t8.k1.z, t8.k1.w);
-        tstage[w][nst][4] = t8.lanes;
+        tstage[w][nst] = tt.k;
+        lstage[w][nst] = tt.lanes;
       }
       if (++nst == kStage) {
         wave_lds_sync();
@@ -315,11 +311,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BITS =
     // a block without a valid physical id contributes probability 0 (its tokens are never attended)
     const float pv = phys >= 0 ? pr : 0.f;
     if (lane < nv) prob[static_cast<size_t>(u) * S + lane] = pv;
-    const WinTop t8 = wave_top8(lane < nv ? __builtin_bit_cast(unsigned, pv) + 1u : 0u, lane);
+    const WinTop tt = wave_top(lane < nv ? __builtin_bit_cast(unsigned, pv) + 1u : 0u, lane);
     if (lane == 0) {
-      wtop[2 * u] = t8.k0;
-      wtop[2 * u + 1] = t8.k1;
-      wlane[u] = t8.lanes;
+      wtop[u] = tt.k;
+      wlane[u] = tt.lanes;
     }
     u = un;
     phys = phys_n;
@@ -703,22 +698,23 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkParams p) 
   }
   // ---- 1. the floor.  Thread t holds windows t + 512 v (v < kTopsWPT), so every thread has work in
   // the first round and the later rounds are skipped as a whole when the row is short.
-  const uint4* tops = p.wtop + static_cast<size_t>(bh) * c.max_blocks * 2;
-  const uint2* lanes = p.wlane + static_cast<size_t>(bh) * c.max_blocks;
+  const uint4* tops = p.wtop + static_cast<size_t>(bh) * c.max_blocks;
+  const uint32_t* lanes = p.wlane + static_cast<size_t>(bh) * c.max_blocks;
   constexpr int WT = kWinTop;
   const int rounds = cdiv(nw, kSelThreads);  // (workgroup-uniform)
   unsigned tk[WT * kTopsWPT];
-  uint2 tl[kTopsWPT];
+  uint32_t tl[kTopsWPT];
+  static_assert(WT == 4, "a window's tops are one 16-byte vector");
 #pragma unroll
   for (int v = 0; v < kTopsWPT; ++v) {
     const int wi = v * kSelThreads + tid;
     const bool ok = v < rounds && wi < nw;
-    const uint4 a0 = ok ? tops[2 * wi] : make_uint4(0u, 0u, 0u, 0u);
-    const uint4 a1 = ok ? tops[2 * wi + 1] : make_uint4(0u, 0u, 0u, 0u);
-    tl[v] = ok ? lanes[wi] : make_uint2(0u, 0u);
-    const unsigned t8[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-#pragma unroll
-    for (int r = 0; r < WT; ++r) tk[WT * v + r] = t8[r];
+    const uint4 a = ok ? tops[wi] : make_uint4(0u, 0u, 0u, 0u);
+    tl[v] = ok ? lanes[wi] : 0u;
+    tk[WT * v + 0] = a.x;
+    tk[WT * v + 1] = a.y;
+    tk[WT * v + 2] = a.z;
+    tk[WT * v + 3] = a.w;
   }
   unsigned tmin = ~0u, tmax = 0u, tcnt = 0u;
 #pragma unroll
@@ -754,7 +750,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkParams p) 
       for (int u = 0; u < kTopsWPT; ++u) kv[r] = u == v ? tk[WT * u + r] : kv[r];
       tmn = min(tmn, kv[r]);
     }
-    uint2 lv = tl[0];
+    uint32_t lv = tl[0];
 #pragma unroll
     for (int u = 1; u < kTopsWPT; ++u) lv = u == v ? tl[u] : lv;
     const bool whole = wi < nw && tmn >= lo;  // every top >= lo: more keys may be
@@ -789,7 +785,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkParams p) 
     if (!whole) {
 #pragma unroll
       for (int r = 0; r < WT; ++r) {
-        const unsigned ln = ((r < 4 ? lv.x : lv.y) >> (8 * (r % 4))) & 63u;
+        const unsigned ln = (lv >> (8 * r)) & 63u;
         if (kv[r] >= lo)  // (a window past the row has no keys: its tops are 0)
           stage[pos++] = static_cast<uint64_t>(kv[r]) |
                          (static_cast<uint64_t>(static_cast<uint32_t>(wi * S + static_cast<int>(ln))) << 32);
