@@ -54,8 +54,8 @@ OUT_MAX_ABS, OUT_MEAN_ABS = 4e-3, 5e-4
 # of its leg (TRAFFIC_SOURCES) as they were when it was taken: it is reported as null once their code
 # changes (the hash skips comments and blank lines).
 COUNTER_TRAFFIC = {
-    "sources_sha256": {"llama8b": "df1d5fd6934c5805b1f1ad65777e7953bc9a2b2798f937bb2d5a7558113c95e4", "long": "df1d5fd6934c5805b1f1ad65777e7953bc9a2b2798f937bb2d5a7558113c95e4", "llama8b_b4": "df1d5fd6934c5805b1f1ad65777e7953bc9a2b2798f937bb2d5a7558113c95e4", "long_b4": "df1d5fd6934c5805b1f1ad65777e7953bc9a2b2798f937bb2d5a7558113c95e4", "llama8b_b0": "df1d5fd6934c5805b1f1ad65777e7953bc9a2b2798f937bb2d5a7558113c95e4", "long_b0": "df1d5fd6934c5805b1f1ad65777e7953bc9a2b2798f937bb2d5a7558113c95e4", "topk": "62eb10d33fdf6c96b429254db587551a5e91998f27246dd46b3cd2ac50126a01", "sparse_decode": "df1d5fd6934c5805b1f1ad65777e7953bc9a2b2798f937bb2d5a7558113c95e4", "store_decode": "df1d5fd6934c5805b1f1ad65777e7953bc9a2b2798f937bb2d5a7558113c95e4", "compact": "007daedc824d3cb9f0c303032b422ca46b003c982428164f9ac3431f9372d8dd", "ragged": "df1d5fd6934c5805b1f1ad65777e7953bc9a2b2798f937bb2d5a7558113c95e4", "prefill_llama8b_2048": "2c996c5f09aca7d5a41e5a7a45a55369573911e03a0fa14df5aee485f255e499", "prefill_topk_8192": "2c996c5f09aca7d5a41e5a7a45a55369573911e03a0fa14df5aee485f255e499"},
-    "bytes_per_launch": {"llama8b": 36967184, "long": 1084456822, "llama8b_b4": 20697970, "long_b4": 550093287, "llama8b_b0": 69420240, "long_b0": 2157511408, "topk": 564698199, "sparse_decode": 190047974, "store_decode": 21981710, "compact": 197185700, "ragged": 614997161, "prefill_llama8b_2048": 104263619, "prefill_topk_8192": 813428927},
+    "sources_sha256": {"llama8b": "ce513c169f5d26665ef634db6d2cfcab71d71aeaf13ee1decc28b485084381cf", "long": "ce513c169f5d26665ef634db6d2cfcab71d71aeaf13ee1decc28b485084381cf", "llama8b_b4": "ce513c169f5d26665ef634db6d2cfcab71d71aeaf13ee1decc28b485084381cf", "long_b4": "ce513c169f5d26665ef634db6d2cfcab71d71aeaf13ee1decc28b485084381cf", "llama8b_b0": "ce513c169f5d26665ef634db6d2cfcab71d71aeaf13ee1decc28b485084381cf", "long_b0": "ce513c169f5d26665ef634db6d2cfcab71d71aeaf13ee1decc28b485084381cf", "topk": "50c5488395d960e412301b4c1437395ed0ad831d7515fe9742b634d8447e46ba", "sparse_decode": "ce513c169f5d26665ef634db6d2cfcab71d71aeaf13ee1decc28b485084381cf", "store_decode": "ce513c169f5d26665ef634db6d2cfcab71d71aeaf13ee1decc28b485084381cf", "compact": "686c662f52804052b365258c44024bfc6152993b907378f690db7ca034320f82", "ragged": "ce513c169f5d26665ef634db6d2cfcab71d71aeaf13ee1decc28b485084381cf", "prefill_llama8b_2048": "111c6b7ed0010d05675ad083b3e02f035479898bf9d2db802e381cb06d306165", "prefill_topk_8192": "111c6b7ed0010d05675ad083b3e02f035479898bf9d2db802e381cb06d306165"},
+    "bytes_per_launch": {"llama8b": 36966974, "long": 1084441620, "llama8b_b4": 20697825, "long_b4": 550152559, "llama8b_b0": 69420191, "long_b0": 2157510913, "topk": 562830430, "sparse_decode": 190040815, "store_decode": 21981696, "compact": 197185291, "ragged": 614999738, "prefill_llama8b_2048": 104263607, "prefill_topk_8192": 813429376},
 }
 DECODE_SOURCES = ("decode_impl.h", "decode_inst.hip", "hkv_device.h", "hkv_internal.h")
 TRAFFIC_SOURCES = {"topk": ("topk.hip", "hkv_device.h", "hkv_internal.h"),
