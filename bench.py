@@ -55,7 +55,7 @@ OUT_MAX_ABS, OUT_MEAN_ABS = 4e-3, 5e-4
 # changes (the hash skips comments and blank lines).
 COUNTER_TRAFFIC = {
     "sources_sha256": {"llama8b": "ce513c169f5d26665ef634db6d2cfcab71d71aeaf13ee1decc28b485084381cf", "long": "ce513c169f5d26665ef634db6d2cfcab71d71aeaf13ee1decc28b485084381cf", "llama8b_b4": "ce513c169f5d26665ef634db6d2cfcab71d71aeaf13ee1decc28b485084381cf", "long_b4": "ce513c169f5d26665ef634db6d2cfcab71d71aeaf13ee1decc28b485084381cf", "llama8b_b0": "ce513c169f5d26665ef634db6d2cfcab71d71aeaf13ee1decc28b485084381cf", "long_b0": "ce513c169f5d26665ef634db6d2cfcab71d71aeaf13ee1decc28b485084381cf", "topk": "50c5488395d960e412301b4c1437395ed0ad831d7515fe9742b634d8447e46ba", "sparse_decode": "ce513c169f5d26665ef634db6d2cfcab71d71aeaf13ee1decc28b485084381cf", "store_decode": "ce513c169f5d26665ef634db6d2cfcab71d71aeaf13ee1decc28b485084381cf", "compact": "686c662f52804052b365258c44024bfc6152993b907378f690db7ca034320f82", "ragged": "ce513c169f5d26665ef634db6d2cfcab71d71aeaf13ee1decc28b485084381cf", "prefill_llama8b_2048": "111c6b7ed0010d05675ad083b3e02f035479898bf9d2db802e381cb06d306165", "prefill_topk_8192": "111c6b7ed0010d05675ad083b3e02f035479898bf9d2db802e381cb06d306165"},
-    "bytes_per_launch": {"llama8b": 36966974, "long": 1084441620, "llama8b_b4": 20697825, "long_b4": 550152559, "llama8b_b0": 69420191, "long_b0": 2157510913, "topk": 562830430, "sparse_decode": 190040815, "store_decode": 21981696, "compact": 197185291, "ragged": 614999738, "prefill_llama8b_2048": 104263607, "prefill_topk_8192": 813429376},
+    "bytes_per_launch": {"llama8b": 36966974, "long": 1084441620, "llama8b_b4": 20697825, "long_b4": 550152559, "llama8b_b0": 69420191, "long_b0": 2157510913, "topk": 562830430, "sparse_decode": 190040815, "store_decode": 21981696, "compact": 197185291, "ragged": 614900311, "prefill_llama8b_2048": 104263607, "prefill_topk_8192": 813429376},
 }
 DECODE_SOURCES = ("decode_impl.h", "decode_inst.hip", "hkv_device.h", "hkv_internal.h")
 TRAFFIC_SOURCES = {"topk": ("topk.hip", "hkv_device.h", "hkv_internal.h"),

@@ -199,11 +199,16 @@ int max_splits(int64_t bh, int64_t units_cap) {
 // fill the resident slots once: placed first, their latency-bound workgroups held every slot at
 // the start (ragged fused step, measured: short groups first 133 us, after 64 / 96 / 128 / 160 /
 // 192 cold groups 128 / 128 / 124 / 124 / 127 us, last 130 us; sequence order 141 us).
+// After the resident slots' first fill, the hot-zone groups are ordered among the remaining cold
+// groups as if each were kHotGroupUnits blocks long (a fused step's append workgroup takes 14-17 us
+// under load; ragged fused step, measured: weight 4 / 8 / 12 / 16 / 20 -> 107.9 / 106.7 / 106.2 /
+// 106.5 / 107.1 us, all after the cold groups 107.0 us).
 // units[b]: the blocks of sequence b this launch attends.  Returns false (plain order kept) when
 // the table cannot hold the groups.
 // Only the cold splits a sequence takes part with are listed (hkv::table_splits of its unit count;
 // the kernel derives the same count), so a sequence's merge never waits for a split that would only
 // have found its units taken.  Sets p.order_groups.
+constexpr int64_t kHotGroupUnits = 12;
 bool order_by_work(hkv::DecodeParams& p, const std::vector<int64_t>& units, int64_t per, uint16_t* order) {
   const int B = static_cast<int>(units.size());
   // entries are (sequence << 7 | part) in 16 bits
@@ -218,9 +223,13 @@ bool order_by_work(hkv::DecodeParams& p, const std::vector<int64_t>& units, int6
   const size_t at = std::min<size_t>(kTargetWorkgroups / p.c.H, v.size());
   size_t i = 0;
   for (size_t k = 0; k < at; ++k) order[i++] = static_cast<uint16_t>(v[k].second);
+  // the hot-zone (and append) groups join the remaining cold groups in the same longest-first order,
+  // weighted as kHotGroupUnits blocks each
+  std::vector<std::pair<int64_t, int>> rest(v.begin() + at, v.end());
   for (int b = 0; b < B; ++b)
-    for (int s = p.nsplit; s < parts; ++s) order[i++] = static_cast<uint16_t>((b << 7) | s);
-  for (size_t k = at; k < v.size(); ++k) order[i++] = static_cast<uint16_t>(v[k].second);
+    for (int s = p.nsplit; s < parts; ++s) rest.push_back({-kHotGroupUnits, (b << 7) | s});
+  std::stable_sort(rest.begin(), rest.end(), [](const auto& x, const auto& y) { return x.first < y.first; });
+  for (const auto& e : rest) order[i++] = static_cast<uint16_t>(e.second);
   p.order_groups = static_cast<int>(i);
   return true;
 }
