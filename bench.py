@@ -334,11 +334,20 @@ def leg_separate(hkv, torch, args):
             "pct_hbm_peak": 100 * r["gbs"] / HBM_PEAK_GBS}
 
 
+def long_steps(args):
+    """Steps per trial (and untimed warm-up steps) of the 131072-token legs: 4x --steps, 16 to 64.
+    A host-clock trial starts from an idle GPU (synchronize), so its first launches run before the
+    clock has settled; 64 steps (7 to 21 ms) keep that ramp to a small part of the trial.  The 4-bit
+    step, bound by its instruction stream, shows it most: 16-step trials of 106 to 145 us against
+    102 us back-to-back."""
+    return max(16, min(4 * args.steps, 64))
+
+
 def leg_long(hkv, torch, args):
     import workloads as wl
     w = wl.WORKLOADS["long"]
-    steps = max(8, min(args.steps, 16))
-    r = decode_step_leg(hkv, torch, w, w.context - 1, steps, 3, args.trials, 2, "long", oracle_check=False)
+    steps = long_steps(args)
+    r = decode_step_leg(hkv, torch, w, w.context - 1, steps, steps, args.trials, 2, "long", oracle_check=False)
     return {"workload": "long: B=4, 131072 tokens, 32/8 heads, d=128, step = fused append 1 token + decode",
             "steps": steps, "ms_per_step": r["ms_per_step"], "trials_ms": r["trials_ms"], "gbs": r["gbs"],
             "pct_hbm_peak": 100 * r["gbs"] / HBM_PEAK_GBS,
@@ -352,7 +361,7 @@ def leg_width(hkv, torch, args, name, bits):
     import workloads as wl
     w = wl.WORKLOADS[name]
     if name == "long":
-        steps, warmup, R, check = max(8, min(args.steps, 16)), 3, 2, False
+        steps, warmup, R, check = long_steps(args), long_steps(args), 2, False
     else:
         steps, warmup, R, check = args.steps, args.warmup, args.instances, True
     label = f"{name} {'fp16' if bits == 0 else str(bits) + '-bit'} cold"
